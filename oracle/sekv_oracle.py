@@ -1,0 +1,363 @@
+"""Plain, slow CPU oracle of SeKV's build step and decode-time attention.
+
+TEST INFRASTRUCTURE.  Only the test suite, the graft entry's smoke check and the
+bench's CPU-baseline leg may import or call this module.  The HIP library never
+does, and this module imports nothing from it: the two share no code.
+
+Everything is computed in float64 with numpy, in the order the method states
+its steps, one span and one head at a time.  Stored quantities the method keeps
+in a narrower type (means and summaries in the key/value storage type) are
+rounded once, to nearest even, exactly where the method stores them; every
+later step reads the rounded value widened back to float64.
+
+Sources (SeKV: Resolution-Adaptive KV Cache with Hierarchical Semantic Memory
+for Long-Context LLM Inference, arXiv 2606.31145, and its Chinese-language
+summary page).  Most inline symbols are lost in the extracted text; each
+function names the passage it follows and the reading taken where the text is
+silent.  The readings are:
+
+  * statistics: population mean and std of the surprisal over the whole
+    sequence, in float64, two passes; threshold mean + alpha * std (Sec. 3.1;
+    summary page sec. 2 gives alpha = 1.0);
+  * boundary: strictly greater than the threshold ("exceeds", summary sec. 2);
+  * the last ``window`` positions are the local window (summary sec. 2: the
+    most recent 512 tokens stay at full resolution) and are never anchors or
+    span members;
+  * spans are the maximal runs of non-anchor positions before the window,
+    including a leading and a trailing run (Sec. 3.3: no span is dropped);
+  * spans shorter than ``min_span_len`` stay at full resolution (Sec. 3.2 low-
+    rank paragraph; the length symbol is lost, 8 is taken);
+  * span-local weights w_t = s_t / sum of s over the span, 1/n if that sum is
+    zero (Sec. 3.2 summary paragraph: normalized, surprisal-weighted);
+  * summary s_{h,j} = W_h kbar_j, which equals the weighted average of the
+    projected keys by linearity (Sec. 3.2);
+  * gate p = sigmoid(q~ . s + gamma ln n), q~ = P q, no 1/sqrt(d_r) scale,
+    natural log; zoom iff p > tau strictly (Sec. 3.2, Sec. 3.3 Eq. 9);
+  * factors: exact SVD, hard gates (keep the top r_j components,
+    r_j = min(requested rank, n_j, d, R), at least 1), same r_j for K and V
+    (Sec. 3.2 low-rank paragraph, Eq. 8 with 0/1 gates);
+  * attention: one softmax over dense tokens (window, anchors, short-span
+    tokens), one coarse entry per non-zoomed span with + ln n_j added to its
+    scaled score, and the rank-r reconstruction of every zoomed span's tokens;
+    score scale 1/sqrt(d) (Sec. 3.3; summary sec. 3).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+F64 = np.float64
+
+
+# ---------------------------------------------------------------------------
+# storage rounding
+# ---------------------------------------------------------------------------
+
+def round_bf16(x) -> np.ndarray:
+    """Round float64 values once, to nearest even, onto the bfloat16 grid
+    (8 significant bits), returned as float64.  Valid for zero and for
+    magnitudes in the bfloat16 normal range, which is all this method stores."""
+    x = np.asarray(x, dtype=F64)
+    m, e = np.frexp(x)                 # x = m * 2**e, 0.5 <= |m| < 1
+    r = np.rint(m * 256.0)             # numpy rint rounds half to even
+    out = np.ldexp(r, e - 8)
+    nz = x != 0
+    if np.any(nz):
+        ax = np.abs(x[nz])
+        if ax.min() < 2.0 ** -126 or ax.max() >= 2.0 ** 128:
+            raise ValueError("value outside the bfloat16 normal range")
+    return out
+
+
+def round_store(x, dtype: str) -> np.ndarray:
+    """Round to the storage type ("bf16" or "f32") and widen back to float64."""
+    if dtype == "bf16":
+        return round_bf16(x)
+    if dtype == "f32":
+        return np.asarray(x, dtype=F64).astype(np.float32).astype(F64)
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------
+# segmentation (Sec. 3.1; summary page sec. 2)
+# ---------------------------------------------------------------------------
+
+def surprisal_threshold(s, alpha: float) -> Tuple[float, float, float]:
+    """Mean, population std and boundary threshold mean + alpha * std of the
+    surprisal over the whole sequence, all in float64 (two passes)."""
+    s = np.asarray(s, dtype=F64)
+    n = s.size
+    if n == 0:
+        raise ValueError("empty sequence")
+    total = 0.0
+    for v in s:
+        total += float(v)
+    mu = total / n
+    ss = 0.0
+    for v in s:
+        ss += (float(v) - mu) ** 2
+    sigma = math.sqrt(ss / n)
+    return mu, sigma, mu + float(alpha) * sigma
+
+
+@dataclasses.dataclass
+class Segmentation:
+    n_tokens: int
+    window: int
+    mu: float
+    sigma: float
+    threshold: float
+    anchors: np.ndarray        # ascending anchor positions, int64
+    span_start: np.ndarray     # every span, ascending, int64
+    span_len: np.ndarray
+    kind: np.ndarray           # 0 = compressed (summary + factors), 1 = short (full resolution)
+    cspan: np.ndarray          # indices (into span_*) of the compressed spans, ascending
+    dense_pos: np.ndarray      # ascending positions kept at full resolution
+
+    @property
+    def n_compressed(self) -> int:
+        return int(self.cspan.size)
+
+
+def segment(s, window: int, alpha: float, min_span_len: int) -> Segmentation:
+    """Anchors are positions before the window whose surprisal exceeds the
+    threshold; spans are the maximal runs of other positions before the window;
+    spans of at least ``min_span_len`` tokens are compressed, shorter ones join
+    the full-resolution set together with the anchors and the window."""
+    s = np.asarray(s, dtype=F64)
+    n = s.size
+    mu, sigma, thr = surprisal_threshold(s, alpha)
+    limit = max(n - int(window), 0)
+    is_anchor = [float(s[t]) > thr for t in range(limit)]
+    anchors = [t for t in range(limit) if is_anchor[t]]
+    starts: List[int] = []
+    lens: List[int] = []
+    t = 0
+    while t < limit:
+        if is_anchor[t]:
+            t += 1
+            continue
+        begin = t
+        while t < limit and not is_anchor[t]:
+            t += 1
+        starts.append(begin)
+        lens.append(t - begin)
+    kind = [0 if ln >= min_span_len else 1 for ln in lens]
+    dense = set(anchors)
+    for b, ln, k in zip(starts, lens, kind):
+        if k == 1:
+            dense.update(range(b, b + ln))
+    dense.update(range(limit, n))
+    return Segmentation(
+        n_tokens=n, window=int(window), mu=mu, sigma=sigma, threshold=thr,
+        anchors=np.array(anchors, dtype=np.int64),
+        span_start=np.array(starts, dtype=np.int64),
+        span_len=np.array(lens, dtype=np.int64),
+        kind=np.array(kind, dtype=np.int64),
+        cspan=np.array([i for i, k in enumerate(kind) if k == 0], dtype=np.int64),
+        dense_pos=np.array(sorted(dense), dtype=np.int64),
+    )
+
+
+# ---------------------------------------------------------------------------
+# span representations (Sec. 3.2)
+# ---------------------------------------------------------------------------
+
+def span_weights(s_span) -> np.ndarray:
+    """Normalized span-local surprisal weights: w_t = s_t / sum_span s."""
+    s_span = np.asarray(s_span, dtype=F64)
+    total = float(np.sum(s_span))
+    if total == 0.0:
+        return np.full(s_span.size, 1.0 / s_span.size)
+    return s_span / total
+
+
+def weighted_mean(w, x) -> np.ndarray:
+    """sum_t w_t x_t over the span's token rows (float64)."""
+    return np.asarray(w, dtype=F64) @ np.asarray(x, dtype=F64)
+
+
+def span_rank(requested: int, n: int, d: int, rank_cap: int) -> int:
+    """Retained rank: the request capped by span length, head dim and the rank
+    cap R, and at least one component."""
+    return int(max(1, min(int(requested), n, d, rank_cap)))
+
+
+@dataclasses.dataclass
+class Factors:
+    u: np.ndarray      # [n][r] left singular vectors
+    sigma: np.ndarray  # [r]    singular values, descending
+    vt: np.ndarray     # [r][d] right singular vectors (rows)
+    tail2: float       # sum of the discarded sigma^2
+
+    def reconstruct(self) -> np.ndarray:
+        return (self.u * self.sigma) @ self.vt
+
+
+def truncated_svd(x, r: int) -> Factors:
+    """Exact SVD of the span's [n][d] token matrix, keeping the top r
+    components (hard gates in the gated reconstruction, Eq. 8)."""
+    x = np.asarray(x, dtype=F64)
+    u, sig, vt = np.linalg.svd(x, full_matrices=False)
+    return Factors(u=u[:, :r].copy(), sigma=sig[:r].copy(), vt=vt[:r].copy(),
+                   tail2=float(np.sum(sig[r:] ** 2)))
+
+
+@dataclasses.dataclass
+class GroupCache:
+    """What one (layer, KV head) keeps: the full-resolution rows, each
+    compressed span's coarse mean key/value (rounded to storage), the routing
+    summaries of every query head in the group (rounded to storage), and the
+    span factors of keys and values."""
+    dense_k: np.ndarray              # [D][d]
+    dense_v: np.ndarray
+    kbar: np.ndarray                 # [S_c][d], rounded to storage
+    vbar: np.ndarray
+    summary: Dict[int, np.ndarray]   # query head -> [S_c][d_r], rounded to storage
+    kfac: List[Factors]
+    vfac: List[Factors]
+    rank: np.ndarray                 # [S_c]
+
+
+def build_group(seg: Segmentation, s, k, v, w_route: Dict[int, np.ndarray], ranks_by_pos,
+                kv_dtype: str, rank_cap: int, with_factors: bool = True) -> GroupCache:
+    """Build the cache of one (layer, KV head) from its keys and values
+    ``k``, ``v`` [N][d] (stored values widened to float64), the surprisal ``s``,
+    each of its query heads' summary projection W_h [d_r][d], and the
+    requested rank of the span that starts at each position."""
+    s = np.asarray(s, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    d = k.shape[1]
+    kbar, vbar, ranks, kfac, vfac = [], [], [], [], []
+    summ = {h: [] for h in w_route}
+    for j in seg.cspan:
+        b, n = int(seg.span_start[j]), int(seg.span_len[j])
+        w = span_weights(s[b:b + n])
+        km = weighted_mean(w, k[b:b + n])
+        vm = weighted_mean(w, v[b:b + n])
+        kbar.append(round_store(km, kv_dtype))
+        vbar.append(round_store(vm, kv_dtype))
+        for h, wh in w_route.items():
+            summ[h].append(round_store(np.asarray(wh, dtype=F64) @ km, kv_dtype))
+        r = span_rank(int(ranks_by_pos[b]), n, d, rank_cap)
+        ranks.append(r)
+        if with_factors:
+            kfac.append(truncated_svd(k[b:b + n], r))
+            vfac.append(truncated_svd(v[b:b + n], r))
+    sc = len(kbar)
+    dr = next(iter(w_route.values())).shape[0] if w_route else 0
+    return GroupCache(
+        dense_k=k[seg.dense_pos], dense_v=v[seg.dense_pos],
+        kbar=np.array(kbar).reshape(sc, d), vbar=np.array(vbar).reshape(sc, d),
+        summary={h: np.array(x).reshape(sc, dr) for h, x in summ.items()},
+        kfac=kfac, vfac=vfac, rank=np.array(ranks, dtype=np.int64))
+
+
+# ---------------------------------------------------------------------------
+# decode: routing (Sec. 3.2 gate, Sec. 3.3 Eq. 9)
+# ---------------------------------------------------------------------------
+
+def span_log_len(seg: Segmentation) -> np.ndarray:
+    """ln n_j of every compressed span, float64."""
+    return np.log(seg.span_len[seg.cspan].astype(F64))
+
+
+def route_head(q, p_proj, summary, log_len, gamma: float, tau: float):
+    """Gate and zoom decision of every compressed span for one query head.
+
+    q~ = P q; x_j = q~ . s_j + gamma ln n_j; p_j = 1 / (1 + e^-x_j);
+    zoom iff p_j > tau.  Returns (p [S_c] float64, zoom [S_c] bool)."""
+    qt = np.asarray(p_proj, dtype=F64) @ np.asarray(q, dtype=F64)
+    x = np.asarray(summary, dtype=F64) @ qt + float(gamma) * np.asarray(log_len, dtype=F64)
+    p = 1.0 / (1.0 + np.exp(-x))
+    return p, p > float(tau)
+
+
+def compact(mask) -> np.ndarray:
+    """Ascending ids of the set entries."""
+    return np.array([j for j, z in enumerate(mask) if z], dtype=np.int64)
+
+
+def union_lists(masks: Sequence[np.ndarray]) -> np.ndarray:
+    """Ascending ids zoomed by at least one head of a group."""
+    if not masks:
+        return np.zeros(0, dtype=np.int64)
+    return compact(np.logical_or.reduce([np.asarray(m, dtype=bool) for m in masks]))
+
+
+# ---------------------------------------------------------------------------
+# decode: mixed-resolution attention (Sec. 3.3; summary sec. 3)
+# ---------------------------------------------------------------------------
+
+def mixed_attention(q, gc: GroupCache, seg: Segmentation, zoom) -> np.ndarray:
+    """One softmax over every entry the head sees: full-resolution rows; one
+    coarse entry (kbar_j, vbar_j) with + ln n_j for each non-zoomed span; the
+    rank-r_j reconstructed rows of each zoomed span.  Returns o [d] float64."""
+    q = np.asarray(q, dtype=F64)
+    d = q.size
+    scale = 1.0 / math.sqrt(d)
+    log_len = span_log_len(seg)
+    keys = [gc.dense_k]
+    vals = [gc.dense_v]
+    bias = [np.zeros(gc.dense_k.shape[0])]
+    for i in range(seg.n_compressed):
+        if zoom[i]:
+            kr = gc.kfac[i].reconstruct()
+            keys.append(kr)
+            vals.append(gc.vfac[i].reconstruct())
+            bias.append(np.zeros(kr.shape[0]))
+        else:
+            keys.append(gc.kbar[i:i + 1])
+            vals.append(gc.vbar[i:i + 1])
+            bias.append(np.array([log_len[i]]))
+    kk = np.concatenate(keys, axis=0)
+    vv = np.concatenate(vals, axis=0)
+    e = scale * (kk @ q) + np.concatenate(bias)
+    m = np.max(e)
+    a = np.exp(e - m)
+    return (a @ vv) / np.sum(a)
+
+
+# ---------------------------------------------------------------------------
+# one decode step of one layer
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class LayerRoute:
+    prob: np.ndarray      # [Hq][S_c] float64
+    mask: np.ndarray      # [Hq][S_c] bool
+    lists: List[np.ndarray]
+    unions: List[np.ndarray]
+
+
+def route_layer(q, p_proj, tau, summaries: Dict[int, np.ndarray], seg: Segmentation,
+                gamma: float, n_kv_heads: int) -> LayerRoute:
+    """Route every query head of a layer and form the per-group unions.
+    ``summaries`` maps each query head to its [S_c][d_r] summaries."""
+    hq = len(q)
+    group = hq // n_kv_heads
+    ll = span_log_len(seg)
+    probs, masks = [], []
+    for h in range(hq):
+        p, z = route_head(q[h], p_proj[h], summaries[h], ll, gamma, float(tau[h]))
+        probs.append(p)
+        masks.append(z)
+    lists = [compact(z) for z in masks]
+    unions = [union_lists(masks[g * group:(g + 1) * group]) for g in range(n_kv_heads)]
+    sc = seg.n_compressed
+    return LayerRoute(prob=np.array(probs).reshape(hq, sc), mask=np.array(masks).reshape(hq, sc),
+                      lists=lists, unions=unions)
+
+
+def decode_layer(q, route: LayerRoute, groups: Dict[int, GroupCache], seg: Segmentation,
+                 heads: Optional[Sequence[int]] = None, n_kv_heads: int = 1) -> Dict[int, np.ndarray]:
+    """Attention output of the given query heads of one layer (all by default);
+    ``groups`` maps KV head -> GroupCache."""
+    hq = len(q)
+    group = hq // n_kv_heads
+    heads = range(hq) if heads is None else heads
+    return {h: mixed_attention(q[h], groups[h // group], seg, route.mask[h]) for h in heads}

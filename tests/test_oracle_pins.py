@@ -1,0 +1,393 @@
+"""Pins of the CPU oracle against what the SeKV pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values
+derived by hand from the definitions (tests/golden), closed forms, invariants,
+special cases that reduce to a textbook routine (torch's scaled-dot-product
+attention, numpy's std, LAPACK eigenvalues), or brute force on tiny inputs.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# segmentation
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", _golden("segmentation_tiny.json")["cases"], ids=lambda c: c["name"])
+def test_segmentation_golden(case):
+    seg = O.segment(np.array(case["surprisal"], float), case["window"], case["alpha"],
+                    case["min_span_len"])
+    assert seg.mu == pytest.approx(case["mu"], abs=1e-15)
+    assert seg.sigma == pytest.approx(case["sigma"], rel=1e-14)
+    assert seg.anchors.tolist() == case["anchors"]
+    assert seg.span_start.tolist() == case["span_start"]
+    assert seg.span_len.tolist() == case["span_len"]
+    assert seg.kind.tolist() == case["kind"]
+    assert seg.dense_pos.tolist() == case["dense_pos"]
+
+
+def _numpy_segmentation(s, window, alpha, min_len):
+    """Brute force through different routines: numpy's std, flatnonzero and
+    diff of a padded indicator."""
+    s = np.asarray(s, float)
+    thr = np.mean(s) + alpha * np.std(s)
+    limit = max(s.size - window, 0)
+    anch = np.flatnonzero(s[:limit] > thr)
+    inside = np.ones(limit + 2, dtype=np.int8)
+    inside[1:limit + 1] = (s[:limit] > thr).astype(np.int8)  # 1 = anchor / outside
+    edges = np.diff(inside)
+    starts = np.flatnonzero(edges == -1)
+    ends = np.flatnonzero(edges == 1)
+    lens = ends - starts
+    return anch, starts, lens, (lens < min_len).astype(int)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_segmentation_brute_force_random(seed):
+    r = np.random.default_rng(seed)
+    n = int(r.integers(1, 40))
+    s = r.gamma(2.0, 1.5, n).astype(np.float32).astype(float)
+    s[r.random(n) < 0.1] += 6
+    window = int(r.integers(0, 6))
+    min_len = int(r.integers(1, 5))
+    seg = O.segment(s, window, 1.0, min_len)
+    anch, starts, lens, kind = _numpy_segmentation(s, window, 1.0, min_len)
+    # the two thresholds differ only by summation order; skip razor-thin ties
+    if np.any(np.abs(s - seg.threshold) < 1e-12 * max(1.0, abs(seg.threshold))):
+        pytest.skip("tie at the threshold")
+    assert seg.anchors.tolist() == anch.tolist()
+    assert seg.span_start.tolist() == starts.tolist()
+    assert seg.span_len.tolist() == lens.tolist()
+    assert seg.kind.tolist() == kind.tolist()
+
+
+def test_segmentation_closed_forms():
+    # constant sequence: std 0, nothing exceeds the mean
+    seg = O.segment(np.full(1000, 0.1, dtype=np.float32), 100, 1.0, 8)
+    assert seg.sigma == 0.0 and seg.anchors.size == 0
+    assert seg.span_start.tolist() == [0] and seg.span_len.tolist() == [900]
+    # a single spike in a constant sequence is the single anchor
+    s = np.full(300, 2.0)
+    s[77] = 9.0
+    seg = O.segment(s, 50, 1.0, 8)
+    assert seg.anchors.tolist() == [77]
+    assert seg.span_start.tolist() == [0, 78] and seg.span_len.tolist() == [77, 172]
+    # fewer tokens than the window: no spans, everything dense
+    seg = O.segment(np.arange(10.0), 512, 1.0, 8)
+    assert seg.span_start.size == 0 and seg.dense_pos.tolist() == list(range(10))
+
+
+def test_segmentation_partition():
+    r = np.random.default_rng(5)
+    s = r.gamma(2.0, 1.5, 5000)
+    s[r.random(5000) < 0.02] += 6
+    seg = O.segment(s, 512, 1.0, 8)
+    covered = np.zeros(5000, int)
+    covered[seg.anchors] += 1
+    for b, n in zip(seg.span_start, seg.span_len):
+        covered[b:b + n] += 1
+    covered[5000 - 512:] += 1
+    assert np.all(covered == 1)
+    assert seg.anchors.size + seg.span_len.sum() + 512 == 5000
+    # anchor share close to P(s > T) of the sample itself
+    assert seg.anchors.size == int(np.sum(s[:-512] > seg.threshold))
+
+
+# ---------------------------------------------------------------------------
+# storage rounding
+# ---------------------------------------------------------------------------
+
+def test_round_bf16_matches_torch_on_float32_values():
+    r = np.random.default_rng(0)
+    x = (r.standard_normal(20000) * np.exp(r.uniform(-20, 20, 20000))).astype(np.float32)
+    mine = O.round_bf16(x.astype(float))
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(mine, ref)
+
+
+def test_round_bf16_single_rounding_from_float64():
+    # halfway cases go to even; a float64 value just above a halfway point must
+    # round up, which rounding through float32 first would get wrong
+    assert O.round_bf16(1 + 2.0 ** -8) == 1.0
+    assert O.round_bf16(1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6
+    assert O.round_bf16(1 + 2.0 ** -8 + 2.0 ** -40) == 1 + 2.0 ** -7
+    assert O.round_bf16(-(1 + 2.0 ** -8 + 2.0 ** -40)) == -(1 + 2.0 ** -7)
+    assert O.round_bf16(255.5) == 256.0
+    assert O.round_store(1 + 2.0 ** -30, "f32") == 1.0
+
+
+# ---------------------------------------------------------------------------
+# weights, means, summaries
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", _golden("span_summary_tiny.json")["cases"], ids=lambda c: c["name"])
+def test_summary_golden(case):
+    w = O.span_weights(case["surprisal"])
+    assert np.allclose(w, case["weights"], atol=1e-15)
+    km = O.weighted_mean(w, case["keys"])
+    vm = O.weighted_mean(w, case["values"])
+    assert np.allclose(km, case["kbar"], atol=1e-14)
+    assert np.allclose(vm, case["vbar"], atol=1e-14)
+    assert np.allclose(np.array(case["w_route"], float) @ km, case["summary"], atol=1e-14)
+
+
+def test_build_group_means_and_summaries_follow_span_table():
+    # a hand-built sequence: anchor at 2, spans [0,2) and [3,7), window 1
+    s = np.array([1.0, 3.0, 50.0, 2.0, 2.0, 4.0, 0.0, 1.0])
+    seg = O.segment(s, 1, 1.0, 2)
+    assert seg.anchors.tolist() == [2]
+    assert seg.span_start.tolist() == [0, 3] and seg.span_len.tolist() == [2, 4]
+    k = np.arange(16, dtype=float).reshape(8, 2)
+    v = -k
+    wh = {0: np.array([[1.0, 0.0]]), 1: np.array([[0.0, 2.0]])}
+    gc = O.build_group(seg, s, k, v, wh, np.full(8, 32), "f32", 32)
+    # span 0: weights [.25, .75] over rows [0,1],[2,3] -> [1.5, 2.5]
+    assert np.allclose(gc.kbar[0], [1.5, 2.5])
+    # span 1: weights [.25,.25,.5,0] over rows 3..6 -> [8.5, 9.5]
+    assert np.allclose(gc.kbar[1], [8.5, 9.5])
+    assert np.allclose(gc.vbar, -gc.kbar)
+    assert np.allclose(gc.summary[0][:, 0], gc.kbar[:, 0])
+    assert np.allclose(gc.summary[1][:, 0], 2 * gc.kbar[:, 1])
+    assert gc.dense_k.tolist() == k[[2, 7]].tolist()
+
+
+def test_summary_linearity_and_constant_span():
+    r = np.random.default_rng(3)
+    n, d, dr = 37, 128, 32
+    x = r.standard_normal((n, d))
+    sp = r.gamma(2, 1.0, n)
+    w = O.span_weights(sp)
+    wh = r.standard_normal((dr, d))
+    # W applied to the weighted mean == weighted mean of the projected keys
+    per_token = np.array([wh @ x[t] for t in range(n)])
+    assert np.allclose(wh @ O.weighted_mean(w, x), (w[:, None] * per_token).sum(0), atol=1e-12)
+    assert abs(w.sum() - 1) < 1e-15
+    # identical tokens: the mean is the token, whatever the weights
+    row = O.round_bf16(r.standard_normal(d))
+    assert np.array_equal(O.round_bf16(O.weighted_mean(w, np.tile(row, (n, 1)))), row)
+    assert O.span_weights([7.0]).tolist() == [1.0]
+
+
+# ---------------------------------------------------------------------------
+# truncated SVD
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,r", [(5, 3), (40, 8), (128, 32), (300, 17), (9, 9)])
+def test_svd_identities(n, r):
+    rng = np.random.default_rng(n * 7 + r)
+    d = 128
+    x = rng.standard_normal((n, 6)) @ rng.standard_normal((6, d)) + 0.05 * rng.standard_normal((n, d))
+    full = O.truncated_svd(x, min(n, d))
+    assert np.linalg.norm(x - full.reconstruct()) <= 1e-12 * np.linalg.norm(x)
+    f = O.truncated_svd(x, r)
+    err2 = np.linalg.norm(x - f.reconstruct()) ** 2
+    # Eckart-Young: the error of the rank-r truncation is the discarded energy
+    assert err2 == pytest.approx(f.tail2, rel=1e-10, abs=1e-20)
+    assert np.allclose(f.u.T @ f.u, np.eye(r), atol=1e-12)
+    assert np.allclose(f.vt @ f.vt.T, np.eye(r), atol=1e-12)
+    # singular values against a different LAPACK routine (symmetric eigensolver)
+    ev = np.sort(np.linalg.eigvalsh(x @ x.T if n <= d else x.T @ x))[::-1]
+    assert np.allclose(f.sigma ** 2, ev[:r], rtol=1e-9, atol=1e-9)
+    assert np.all(np.diff(f.sigma) <= 0)
+
+
+def test_svd_planted_rank():
+    rng = np.random.default_rng(11)
+    n, d, k = 90, 128, 5
+    x = rng.standard_normal((n, k)) @ rng.standard_normal((k, d)) + 1e-3 * rng.standard_normal((n, d))
+    f = O.truncated_svd(x, 32)
+    assert f.sigma[k - 1] > 1.0 and f.sigma[k] < 0.03
+    assert O.span_rank(40, 6, 128, 32) == 6 and O.span_rank(0, 50, 128, 32) == 1
+    assert O.span_rank(20, 50, 128, 32) == 20 and O.span_rank(99, 500, 128, 32) == 32
+
+
+# ---------------------------------------------------------------------------
+# router
+# ---------------------------------------------------------------------------
+
+def test_route_golden():
+    c = _golden("route_attention_tiny.json")["route"]
+    for tau, want in c["zoom_at_tau"].items():
+        p, z = O.route_head(c["q"], c["p_proj"], c["summary"], c["log_len"], c["gamma"], float(tau))
+        assert np.allclose(p, c["p"], rtol=0, atol=1e-16)
+        assert z.tolist() == want
+
+
+def test_route_special_cases():
+    r = np.random.default_rng(2)
+    sc, dr, d = 50, 32, 128
+    summ = O.round_bf16(r.standard_normal((sc, dr)) * 0.3)
+    ll = np.log(r.integers(8, 600, sc).astype(float))
+    q = r.standard_normal(d)
+    pp = r.standard_normal((dr, d)) / math.sqrt(d)
+    # strict threshold: p <= 1 never exceeds 1; p > 0 always exceeds -1
+    assert not O.route_head(q, pp, summ, ll, 0.1, 1.0)[1].any()
+    assert O.route_head(q, pp, summ, ll, 0.1, -1.0)[1].all()
+    # sets grow as the threshold falls
+    prev = np.zeros(sc, bool)
+    for tau in np.linspace(0.99, 0.01, 30):
+        z = O.route_head(q, pp, summ, ll, 0.1, tau)[1]
+        assert np.all(z >= prev)
+        prev = z
+    # zero summaries: the gate is the size prior alone (scipy's expit)
+    from scipy.special import expit
+    p, _ = O.route_head(q, pp, np.zeros((sc, dr)), ll, 0.37, 0.5)
+    assert np.allclose(p, expit(0.37 * ll), rtol=1e-15, atol=0)
+    # zero size prior and a one-hot projection: x is one summary coordinate times q_0
+    e0 = np.zeros((dr, d))
+    e0[3, 0] = 1.0
+    p, _ = O.route_head(np.eye(d)[0] * 2.0, e0, summ, ll, 0.0, 0.5)
+    assert np.allclose(p, expit(2.0 * summ[:, 3]), rtol=1e-15, atol=0)
+
+
+def test_compaction_and_union():
+    r = np.random.default_rng(9)
+    m = r.random((4, 200)) < 0.1
+    for h in range(4):
+        assert O.compact(m[h]).tolist() == np.flatnonzero(m[h]).tolist()
+    assert O.union_lists(list(m)).tolist() == np.flatnonzero(m.any(0)).tolist()
+    assert O.union_lists([]).size == 0
+
+
+# ---------------------------------------------------------------------------
+# mixed-resolution attention
+# ---------------------------------------------------------------------------
+
+def test_attention_golden():
+    c = _golden("route_attention_tiny.json")["attention"]
+    seg = O.Segmentation(n_tokens=3, window=1, mu=0, sigma=0, threshold=0,
+                         anchors=np.zeros(0, np.int64), span_start=np.array([0]),
+                         span_len=np.array(c["span_len"]), kind=np.array([0]),
+                         cspan=np.array([0]), dense_pos=np.array([2]))
+    gc = O.GroupCache(dense_k=np.array(c["dense_k"], float), dense_v=np.array(c["dense_v"], float),
+                      kbar=np.array(c["kbar"], float), vbar=np.array(c["vbar"], float),
+                      summary={}, kfac=[None], vfac=[None], rank=np.array([1]))
+    o = O.mixed_attention(c["q"], gc, seg, [False])
+    assert np.allclose(o, c["o"], atol=1e-15)
+
+
+def _problem(seed, n=1500, hq=4, hkv=2, window=128, min_len=8, constant_spans=False,
+             kv_dtype="f32", rank_cap=32):
+    r = np.random.default_rng(seed)
+    d, dr = 128, 32
+    s = r.gamma(2.0, 0.05, n)
+    s[r.random(n) < 1 / 40] += 6.0
+    seg = O.segment(s, window, 1.0, min_len)
+    k = r.standard_normal((hkv, n, d))
+    v = r.standard_normal((hkv, n, d))
+    if constant_spans:
+        for b, ln in zip(seg.span_start, seg.span_len):
+            k[:, b:b + ln] = k[:, b:b + 1]
+            v[:, b:b + ln] = v[:, b:b + 1]
+    k = O.round_store(k, kv_dtype)
+    v = O.round_store(v, kv_dtype)
+    w = r.standard_normal((hq, dr, d)) / math.sqrt(d)
+    p = r.standard_normal((hq, dr, d)) / math.sqrt(d)
+    q = r.standard_normal((hq, d))
+    g = hq // hkv
+    groups = {kh: O.build_group(seg, s, k[kh], v[kh], {h: w[h] for h in range(kh * g, kh * g + g)},
+                                np.full(n, 999), kv_dtype, rank_cap) for kh in range(hkv)}
+    summ = {h: groups[h // g].summary[h] for h in range(hq)}
+    return seg, k, v, q, p, summ, groups, s
+
+
+def _sdpa(q, k, v, bias=None):
+    """Textbook attention through torch (CPU, float64); grouped-query layout
+    by repeating each KV head over its query heads."""
+    hq, hkv = q.shape[0], k.shape[0]
+    kt = torch.from_numpy(np.repeat(k, hq // hkv, axis=0))
+    vt = torch.from_numpy(np.repeat(v, hq // hkv, axis=0))
+    qt = torch.from_numpy(q)[:, None, :]
+    mask = None if bias is None else torch.from_numpy(bias)[:, None, :]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+    return o[:, 0, :].numpy()
+
+
+def test_all_zoomed_at_full_rank_is_dense_attention():
+    seg, k, v, q, p, summ, groups, _ = _problem(21, rank_cap=128)
+    route = O.route_layer(q, p, np.full(4, -1.0), summ, seg, 0.1, 2)
+    assert route.mask.all()
+    out = O.decode_layer(q, route, groups, seg, n_kv_heads=2)
+    ref = _sdpa(q, k, v)
+    for h in range(4):
+        assert np.allclose(out[h], ref[h], rtol=1e-10, atol=1e-12)
+
+
+def test_none_zoomed_with_constant_spans_is_dense_attention():
+    # a span of identical tokens weighs n e^{q.k/sqrt d}: the coarse entry with
+    # + ln n carries exactly that mass
+    seg, k, v, q, p, summ, groups, _ = _problem(22, constant_spans=True)
+    route = O.route_layer(q, p, np.full(4, 1.0), summ, seg, 0.1, 2)
+    assert not route.mask.any()
+    out = O.decode_layer(q, route, groups, seg, n_kv_heads=2)
+    ref = _sdpa(q, k, v)
+    for h in range(4):
+        assert np.allclose(out[h], ref[h], rtol=1e-10, atol=1e-12)
+
+
+def test_mixed_zoom_matches_explicit_entry_list():
+    """Some spans zoomed at full rank, the rest coarse: the same as textbook
+    attention over an explicit entry list built from the raw rows (dense rows,
+    zoomed spans' exact rows, one mean row per other span with an additive
+    ln n bias)."""
+    seg, k, v, q, p, summ, groups, s = _problem(23, kv_dtype="bf16", rank_cap=128)
+    tau = np.array([0.45, 0.55, 0.5, 0.6])
+    route = O.route_layer(q, p, tau, summ, seg, 0.1, 2)
+    assert 0 < route.mask.sum() < route.mask.size
+    out = O.decode_layer(q, route, groups, seg, n_kv_heads=2)
+    for h in range(4):
+        kh = h // 2
+        rows_k, rows_v, bias = [k[kh, seg.dense_pos]], [v[kh, seg.dense_pos]], [np.zeros(seg.dense_pos.size)]
+        for i, j in enumerate(seg.cspan):
+            b, n = seg.span_start[j], seg.span_len[j]
+            if route.mask[h, i]:
+                rows_k.append(k[kh, b:b + n])
+                rows_v.append(v[kh, b:b + n])
+                bias.append(np.zeros(n))
+            else:
+                rows_k.append(groups[kh].kbar[i:i + 1])
+                rows_v.append(groups[kh].vbar[i:i + 1])
+                bias.append(np.array([math.log(n)]))
+        ref = _sdpa(q[h:h + 1], np.concatenate(rows_k)[None], np.concatenate(rows_v)[None],
+                    np.concatenate(bias)[None])
+        assert np.allclose(out[h], ref[0], rtol=1e-9, atol=1e-11)
+    # the union of a group is the OR of its heads' masks
+    for g in range(2):
+        assert route.unions[g].tolist() == np.flatnonzero(route.mask[2 * g:2 * g + 2].any(0)).tolist()
+
+
+def test_short_context_is_dense_attention_over_window():
+    seg, k, v, q, p, summ, groups, _ = _problem(24, n=300, window=512)
+    assert seg.span_start.size == 0
+    route = O.route_layer(q, p, np.full(4, 0.5), summ, seg, 0.1, 2)
+    out = O.decode_layer(q, route, groups, seg, n_kv_heads=2)
+    ref = _sdpa(q, k, v)
+    for h in range(4):
+        assert np.allclose(out[h], ref[h], rtol=1e-10, atol=1e-12)
+
+
+def test_truncation_moves_output_by_bounded_amount():
+    """Rank-r zoom vs full-rank zoom: the output changes, and by less as r grows."""
+    errs = []
+    for cap in (4, 16, 64, 128):
+        seg, k, v, q, p, summ, groups, _ = _problem(25, n=800, rank_cap=cap)
+        route = O.route_layer(q, p, np.full(4, -1.0), summ, seg, 0.1, 2)
+        out = O.decode_layer(q, route, groups, seg, n_kv_heads=2)
+        ref = _sdpa(q, k, v)
+        errs.append(max(np.abs(out[h] - ref[h]).max() for h in range(4)))
+    assert errs[-1] < 1e-10
+    assert errs[0] > errs[1] > errs[2] > errs[3]
