@@ -1,0 +1,307 @@
+"""SeKV decode-time attention on AMD Instinct MI355X: Python binding.
+
+A thin ctypes layer over ``libsekv.so`` (the C ABI of include/sekv.h).  The
+functions here marshal torch tensors into device pointers and streams and call
+the library; every step of the build and of the decode step runs in the HIP
+kernels behind that ABI.  There is no fallback: if the library is missing or a
+call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "SekvError", "SekvConfig", "SekvCacheInfo", "SekvRouteOut", "lib", "library_path",
+    "make_config", "Cache", "RouteBuffers", "sekv_segment", "sekv_build_spans", "sekv_route",
+    "sekv_decode_attn", "sekv_decode_workspace_bytes", "EXPORTED_SYMBOLS",
+    "SEKV_F32", "SEKV_BF16", "SEKV_TIER_DEVICE", "SEKV_TIER_HOST_PINNED",
+]
+
+SEKV_OK, SEKV_ERR_INVALID, SEKV_ERR_NOMEM, SEKV_ERR_HIP, SEKV_ERR_UNSUPPORTED = range(5)
+SEKV_F32, SEKV_BF16 = 0, 1
+SEKV_TIER_DEVICE, SEKV_TIER_HOST_PINNED = 0, 1
+
+EXPORTED_SYMBOLS = (
+    "sekv_segment", "sekv_build_spans", "sekv_cache_info_get", "sekv_cache_copy_spans",
+    "sekv_cache_copy_group", "sekv_cache_copy_factors", "sekv_route",
+    "sekv_decode_workspace_bytes", "sekv_decode_attn", "sekv_cache_destroy", "sekv_last_error",
+)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.environ.get("SEKV_LIBRARY", os.path.join(_HERE, "libsekv.so"))
+
+
+class SekvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"sekv status {status}: {msg}")
+        self.status = status
+
+
+class SekvConfig(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("route_dim", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("max_rank", ctypes.c_int32), ("min_span_len", ctypes.c_int32),
+        ("alpha", ctypes.c_double), ("gamma", ctypes.c_double),
+        ("kv_dtype", ctypes.c_int32), ("factor_tier", ctypes.c_int32),
+        ("host_pool_cap_bytes", ctypes.c_uint64),
+    ]
+
+
+class SekvCacheInfo(ctypes.Structure):
+    _fields_ = [
+        ("n_tokens", ctypes.c_int32), ("n_anchors", ctypes.c_int32),
+        ("n_spans", ctypes.c_int32), ("n_compressed", ctypes.c_int32),
+        ("n_dense", ctypes.c_int32), ("factor_tier", ctypes.c_int32),
+        ("mu", ctypes.c_double), ("sigma", ctypes.c_double), ("threshold", ctypes.c_double),
+        ("resident_bytes", ctypes.c_uint64), ("factor_bytes", ctypes.c_uint64),
+        ("factor_pool_bytes", ctypes.c_uint64),
+    ]
+
+
+class SekvRouteOut(ctypes.Structure):
+    _fields_ = [
+        ("mask", ctypes.c_void_p), ("list", ctypes.c_void_p), ("count", ctypes.c_void_p),
+        ("union_list", ctypes.c_void_p), ("union_count", ctypes.c_void_p),
+        ("prob", ctypes.c_void_p),
+    ]
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsekv.so (once) and declare its signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"SeKV HIP library not found at {path}; build it with "
+                          "`python -m compressed_kv_attention_sekv_amd.build`")
+    L = ctypes.CDLL(path)
+    P, I32, U64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
+    I32P = ctypes.POINTER(ctypes.c_int32)
+    sig = {
+        "sekv_segment": (I32, [ctypes.POINTER(SekvConfig), I32, P, I32P, I32P, I32P, P]),
+        "sekv_build_spans": (I32, [ctypes.POINTER(SekvConfig), I32, P, P, P, P, P, P,
+                                   ctypes.POINTER(P)]),
+        "sekv_cache_info_get": (I32, [P, ctypes.POINTER(SekvCacheInfo)]),
+        "sekv_cache_copy_spans": (I32, [P, P, P, P, P, P, P]),
+        "sekv_cache_copy_group": (I32, [P, I32, I32, P, P, P, P]),
+        "sekv_cache_copy_factors": (I32, [P, I32, I32, I32, I32, P, P, P]),
+        "sekv_route": (I32, [P, I32, P, P, P, ctypes.POINTER(SekvRouteOut), P]),
+        "sekv_decode_workspace_bytes": (SZ, [P]),
+        "sekv_decode_attn": (I32, [P, I32, P, ctypes.POINTER(SekvRouteOut), P, P, SZ, P, P]),
+        "sekv_cache_destroy": (None, [P]),
+        "sekv_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    del U64
+    _LIB = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != SEKV_OK:
+        raise SekvError(status, lib().sekv_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, device=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def make_config(n_layers: int, n_q_heads: int, n_kv_heads: int, *, head_dim: int = 128,
+                route_dim: int = 32, window: int = 512, max_rank: int = 32,
+                min_span_len: int = 8, alpha: float = 1.0, gamma: float = 0.1,
+                kv_dtype: str = "bf16", factor_tier: str = "device",
+                host_pool_cap_bytes: int = 0) -> SekvConfig:
+    return SekvConfig(n_layers, n_q_heads, n_kv_heads, head_dim, route_dim, window, max_rank,
+                      min_span_len, float(alpha), float(gamma),
+                      SEKV_BF16 if kv_dtype == "bf16" else SEKV_F32,
+                      SEKV_TIER_HOST_PINNED if factor_tier == "host" else SEKV_TIER_DEVICE,
+                      int(host_pool_cap_bytes))
+
+
+def sekv_segment(cfg: SekvConfig, surprisal: torch.Tensor, stream=None):
+    """(n_anchors, n_spans, n_compressed) of a surprisal sequence."""
+    _need(surprisal, "surprisal", torch.float32)
+    a, s, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().sekv_segment(ctypes.byref(cfg), surprisal.numel(), _ptr(surprisal),
+                              ctypes.byref(a), ctypes.byref(s), ctypes.byref(c), _stream(stream)))
+    return a.value, s.value, c.value
+
+
+@dataclasses.dataclass
+class RouteBuffers:
+    """Device buffers of one layer's route output, allocated with torch."""
+    mask: torch.Tensor
+    list: torch.Tensor
+    count: torch.Tensor
+    union_list: torch.Tensor
+    union_count: torch.Tensor
+    prob: Optional[torch.Tensor]
+
+    @classmethod
+    def allocate(cls, cache: "Cache", with_prob: bool = False, device="cuda"):
+        hq, hkv, sc = cache.cfg.n_q_heads, cache.cfg.n_kv_heads, max(cache.info.n_compressed, 1)
+        return cls(
+            mask=torch.zeros(hq, sc, dtype=torch.uint8, device=device),
+            list=torch.zeros(hq, sc, dtype=torch.int32, device=device),
+            count=torch.zeros(hq, dtype=torch.int32, device=device),
+            union_list=torch.zeros(hkv, sc, dtype=torch.int32, device=device),
+            union_count=torch.zeros(hkv, dtype=torch.int32, device=device),
+            prob=torch.zeros(hq, sc, dtype=torch.float64, device=device) if with_prob else None)
+
+    def struct(self) -> SekvRouteOut:
+        return SekvRouteOut(self.mask.data_ptr(), self.list.data_ptr(), self.count.data_ptr(),
+                            self.union_list.data_ptr(), self.union_count.data_ptr(),
+                            self.prob.data_ptr() if self.prob is not None else None)
+
+
+class Cache:
+    """Owns an sekv_cache handle; destroyed with the object."""
+
+    def __init__(self, handle: ctypes.c_void_p, cfg: SekvConfig):
+        self.handle = handle
+        self.cfg = cfg
+        info = SekvCacheInfo()
+        _check(lib().sekv_cache_info_get(handle, ctypes.byref(info)))
+        self.info = info
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and _LIB is not None:
+            _LIB.sekv_cache_destroy(h)
+            self.handle = None
+
+    @property
+    def group(self) -> int:
+        return self.cfg.n_q_heads // self.cfg.n_kv_heads
+
+    def spans(self):
+        """Span table as CPU int tensors."""
+        i = self.info
+        t = {k: torch.zeros(max(n, 1), dtype=torch.int32) for k, n in (
+            ("anchors", i.n_anchors), ("span_start", i.n_spans), ("span_len", i.n_spans),
+            ("cspan", i.n_compressed), ("dense_pos", i.n_dense))}
+        kind = torch.zeros(max(i.n_spans, 1), dtype=torch.uint8)
+        _check(lib().sekv_cache_copy_spans(self.handle, _ptr(t["anchors"]), _ptr(t["span_start"]),
+                                           _ptr(t["span_len"]), _ptr(kind), _ptr(t["cspan"]),
+                                           _ptr(t["dense_pos"])))
+        out = {"anchors": t["anchors"][:i.n_anchors], "span_start": t["span_start"][:i.n_spans],
+               "span_len": t["span_len"][:i.n_spans], "kind": kind[:i.n_spans],
+               "cspan": t["cspan"][:i.n_compressed], "dense_pos": t["dense_pos"][:i.n_dense]}
+        return out
+
+    def group_data(self, layer: int, kv_head: int):
+        """(kbar, vbar, summaries [G][S_c][dr], ranks) of one (layer, KV head), CPU tensors."""
+        sc, d, dr, g = self.info.n_compressed, self.cfg.head_dim, self.cfg.route_dim, self.group
+        dt = torch.bfloat16 if self.cfg.kv_dtype == SEKV_BF16 else torch.float32
+        kb = torch.zeros(max(sc, 1), d, dtype=dt)
+        vb = torch.zeros(max(sc, 1), d, dtype=dt)
+        sm = torch.zeros(g, max(sc, 1), dr, dtype=dt)
+        rk = torch.zeros(max(sc, 1), dtype=torch.int32)
+        _check(lib().sekv_cache_copy_group(self.handle, layer, kv_head, _ptr(kb), _ptr(vb),
+                                           _ptr(sm), _ptr(rk)))
+        return kb[:sc], vb[:sc], sm[:, :sc].contiguous() if sc else sm[:, :0], rk[:sc]
+
+    def factors(self, layer: int, kv_head: int, span: int, kv: int, rank: int, n: int):
+        u = torch.zeros(n, rank, dtype=torch.float32)
+        s = torch.zeros(rank, dtype=torch.float32)
+        vt = torch.zeros(rank, self.cfg.head_dim, dtype=torch.float32)
+        _check(lib().sekv_cache_copy_factors(self.handle, layer, kv_head, span, kv, _ptr(u),
+                                             _ptr(s), _ptr(vt)))
+        return u, s, vt
+
+    def workspace_bytes(self) -> int:
+        return int(lib().sekv_decode_workspace_bytes(self.handle))
+
+
+def sekv_build_spans(cfg: SekvConfig, surprisal: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     w_route: torch.Tensor, rank_by_pos: Optional[torch.Tensor] = None,
+                     stream=None) -> Cache:
+    """Build the cache; shapes as in include/sekv.h."""
+    _need(surprisal, "surprisal", torch.float32)
+    kv_dt = torch.bfloat16 if cfg.kv_dtype == SEKV_BF16 else torch.float32
+    _need(k, "k", kv_dt)
+    _need(v, "v", kv_dt)
+    _need(w_route, "w_route", torch.float32)
+    n = surprisal.numel()
+    shape = (cfg.n_layers, cfg.n_kv_heads, n, cfg.head_dim)
+    if tuple(k.shape) != shape or tuple(v.shape) != shape:
+        raise ValueError(f"k and v must be {shape}")
+    if tuple(w_route.shape) != (cfg.n_layers, cfg.n_q_heads, cfg.route_dim, cfg.head_dim):
+        raise ValueError("w_route must be [L][Hq][dr][d]")
+    if rank_by_pos is not None:
+        _need(rank_by_pos, "rank_by_pos", torch.int32)
+        if tuple(rank_by_pos.shape) != (cfg.n_layers, cfg.n_kv_heads, n):
+            raise ValueError("rank_by_pos must be [L][Hkv][N]")
+    h = ctypes.c_void_p()
+    _check(lib().sekv_build_spans(ctypes.byref(cfg), n, _ptr(surprisal), _ptr(k), _ptr(v),
+                                  _ptr(w_route), _ptr(rank_by_pos), _stream(stream),
+                                  ctypes.byref(h)))
+    return Cache(h, cfg)
+
+
+def sekv_route(cache: Cache, layer: int, q: torch.Tensor, proj: torch.Tensor, tau: torch.Tensor,
+               out: RouteBuffers, stream=None) -> None:
+    _need(q, "q", torch.float32)
+    _need(proj, "proj", torch.float32)
+    _need(tau, "tau", torch.float32)
+    c = cache.cfg
+    if tuple(q.shape) != (c.n_q_heads, c.head_dim) or tuple(tau.shape) != (c.n_q_heads,) or \
+            tuple(proj.shape) != (c.n_q_heads, c.route_dim, c.head_dim):
+        raise ValueError("q [Hq][d], proj [Hq][dr][d], tau [Hq] expected")
+    st = out.struct()
+    _check(lib().sekv_route(cache.handle, layer, _ptr(q), _ptr(proj), _ptr(tau),
+                            ctypes.byref(st), _stream(stream)))
+
+
+def sekv_decode_workspace_bytes(cache: Cache) -> int:
+    return cache.workspace_bytes()
+
+
+def sekv_decode_attn(cache: Cache, layer: int, q: torch.Tensor, route: RouteBuffers,
+                     o: torch.Tensor, workspace: torch.Tensor, stream=None,
+                     fetch_stream=None) -> None:
+    _need(q, "q", torch.float32)
+    _need(o, "o", torch.float32)
+    _need(workspace, "workspace")
+    c = cache.cfg
+    if tuple(q.shape) != (c.n_q_heads, c.head_dim) or tuple(o.shape) != (c.n_q_heads, c.head_dim):
+        raise ValueError("q and o must be [Hq][d]")
+    st = route.struct()
+    fst = None if fetch_stream is None else _stream(fetch_stream)
+    _check(lib().sekv_decode_attn(cache.handle, layer, _ptr(q), ctypes.byref(st), _ptr(o),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream), fst))

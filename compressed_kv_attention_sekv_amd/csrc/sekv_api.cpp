@@ -1,0 +1,557 @@
+// Host runtime and C ABI of the SeKV library: argument validation, the cache
+// handle (device tables, full-resolution rows, means, summaries, factor pool
+// in HBM or pinned host memory), and the launch sequence of the build and of
+// each decode step.  See include/sekv.h for the contract of every call.
+#include "sekv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "sekv_internal.h"
+
+using namespace sekv;
+
+namespace {
+
+thread_local std::string g_err;
+
+sekv_status fail(sekv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define SEKV_HIP(expr)                                                                        \
+  do {                                                                                        \
+    hipError_t e_ = (expr);                                                                   \
+    if (e_ != hipSuccess)                                                                     \
+      return fail(SEKV_ERR_HIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_),        \
+                  __FILE__, __LINE__);                                                        \
+  } while (0)
+
+#define SEKV_ALLOC(ptr, bytes)                                                                \
+  do {                                                                                        \
+    size_t b_ = (bytes);                                                                      \
+    if (b_ == 0) b_ = 256;                                                                    \
+    hipError_t e_ = hipMalloc((void**)&(ptr), b_);                                            \
+    if (e_ != hipSuccess)                                                                     \
+      return fail(SEKV_ERR_NOMEM, "hipMalloc(%zu) for %s failed: %s", b_, #ptr,               \
+                  hipGetErrorString(e_));                                                     \
+  } while (0)
+
+sekv_status check_config(const sekv_config* c) {
+  if (!c) return fail(SEKV_ERR_INVALID, "config is NULL");
+  if (c->n_layers < 1) return fail(SEKV_ERR_INVALID, "n_layers must be >= 1");
+  if (c->n_kv_heads < 1 || c->n_q_heads < 1 || c->n_q_heads % c->n_kv_heads != 0)
+    return fail(SEKV_ERR_INVALID, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                c->n_q_heads, c->n_kv_heads);
+  if (c->n_q_heads / c->n_kv_heads > kMaxGroup)
+    return fail(SEKV_ERR_INVALID, "at most %d query heads per KV head", kMaxGroup);
+  if (c->head_dim != kHeadDim) return fail(SEKV_ERR_INVALID, "head_dim must be %d", kHeadDim);
+  if (c->route_dim < 1 || c->route_dim > kMaxRouteDim)
+    return fail(SEKV_ERR_INVALID, "route_dim must be in [1, %d]", kMaxRouteDim);
+  if (c->window < 0) return fail(SEKV_ERR_INVALID, "window must be >= 0");
+  if (c->max_rank < 1 || c->max_rank > kHeadDim)
+    return fail(SEKV_ERR_INVALID, "max_rank must be in [1, %d]", kHeadDim);
+  if (c->min_span_len < 1) return fail(SEKV_ERR_INVALID, "min_span_len must be >= 1");
+  if (!std::isfinite(c->alpha) || !std::isfinite(c->gamma))
+    return fail(SEKV_ERR_INVALID, "alpha and gamma must be finite");
+  if (c->kv_dtype != SEKV_F32 && c->kv_dtype != SEKV_BF16)
+    return fail(SEKV_ERR_INVALID, "kv_dtype must be SEKV_F32 or SEKV_BF16");
+  if (c->factor_tier != SEKV_TIER_DEVICE && c->factor_tier != SEKV_TIER_HOST_PINNED)
+    return fail(SEKV_ERR_INVALID, "factor_tier must be SEKV_TIER_DEVICE or SEKV_TIER_HOST_PINNED");
+  return SEKV_OK;
+}
+
+struct DevFree {
+  void operator()(void* p) const {
+    if (p) (void)hipFree(p);
+  }
+};
+
+// device buffers owned by a scope; freed on every exit path
+struct Scratch {
+  std::vector<void*> ptrs;
+  ~Scratch() {
+    for (void* p : ptrs) (void)hipFree(p);
+  }
+  template <typename T>
+  sekv_status alloc(T** out, size_t bytes, const char* what) {
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, bytes ? bytes : 256);
+    if (e != hipSuccess)
+      return fail(SEKV_ERR_NOMEM, "hipMalloc(%zu) for %s failed: %s", bytes, what,
+                  hipGetErrorString(e));
+    ptrs.push_back(p);
+    *out = (T*)p;
+    return SEKV_OK;
+  }
+  void release(void* p) {
+    ptrs.erase(std::remove(ptrs.begin(), ptrs.end(), p), ptrs.end());
+  }
+};
+
+size_t elem_bytes(int dtype) { return dtype == SEKV_BF16 ? 2 : 4; }
+
+sekv_status run_segment(const sekv_config* cfg, int n, const float* s, Scratch& sc, SegOut& o,
+                        int32_t counts[4], double stats[3], hipStream_t st) {
+  sekv_status r;
+  if ((r = sc.alloc(&o.stats, 3 * sizeof(double), "stats"))) return r;
+  if ((r = sc.alloc(&o.counts, 4 * sizeof(int32_t), "counts"))) return r;
+  if ((r = sc.alloc(&o.anchors, (size_t)n * 4, "anchors"))) return r;
+  if ((r = sc.alloc(&o.span_start, (size_t)n * 4, "span_start"))) return r;
+  if ((r = sc.alloc(&o.span_len, (size_t)n * 4, "span_len"))) return r;
+  if ((r = sc.alloc(&o.kind, (size_t)n, "kind"))) return r;
+  if ((r = sc.alloc(&o.cspan, (size_t)n * 4, "cspan"))) return r;
+  if ((r = sc.alloc(&o.cstart, (size_t)n * 4, "cstart"))) return r;
+  if ((r = sc.alloc(&o.clen, (size_t)n * 4, "clen"))) return r;
+  if ((r = sc.alloc(&o.dense_pos, (size_t)n * 4, "dense_pos"))) return r;
+  if ((r = sc.alloc(&o.flag, (size_t)n, "flag"))) return r;
+  SEKV_HIP(launch_segment(s, n, cfg->window, cfg->alpha, cfg->min_span_len, o, st));
+  SEKV_HIP(hipMemcpyAsync(counts, o.counts, 4 * sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  SEKV_HIP(hipMemcpyAsync(stats, o.stats, 3 * sizeof(double), hipMemcpyDeviceToHost, st));
+  SEKV_HIP(hipStreamSynchronize(st));
+  return SEKV_OK;
+}
+
+}  // namespace
+
+struct sekv_cache {
+  sekv_config cfg{};
+  int n_tokens = 0, n_anchors = 0, n_spans = 0, sc = 0, n_dense = 0;
+  int group = 1;
+  double stats[3] = {0, 0, 0};
+  std::vector<void*> dev;  // every device allocation, freed on destroy
+  // span tables (device)
+  int32_t *anchors = nullptr, *span_start = nullptr, *span_len = nullptr, *cspan = nullptr;
+  int32_t *cstart = nullptr, *clen = nullptr, *dense_pos = nullptr;
+  uint8_t* kind = nullptr;
+  double* lnn64 = nullptr;
+  float* lnn32 = nullptr;
+  // representations (device)
+  void *dense_k = nullptr, *dense_v = nullptr, *kbar = nullptr, *vbar = nullptr, *summ = nullptr;
+  int32_t* rank = nullptr;        // [L][Hkv][Sc]
+  uint64_t* fac_off = nullptr;    // [L][Hkv][Sc] float offset of each block
+  std::vector<int32_t> h_rank;
+  std::vector<int32_t> h_clen;
+  std::vector<uint64_t> h_fac_off;
+  std::vector<uint64_t> layer_base;  // [L + 1] first float of each layer's blocks
+  uint64_t factor_bytes = 0, pool_floats = 0;
+  float* pool_dev = nullptr;      // device tier
+  float* pool_host = nullptr;     // host tier (pinned, mapped)
+  float* pool_host_dev = nullptr; // device view of pool_host
+  float* stage = nullptr;         // host tier: device staging for one layer
+  uint64_t stage_floats = 0;
+  // routing scratch
+  int32_t* route_scratch = nullptr;
+  uint32_t* tickets = nullptr;
+  DecodeGeom geom{};
+  hipEvent_t ev_route = nullptr, ev_fetch = nullptr;
+
+  ~sekv_cache() {
+    for (void* p : dev) (void)hipFree(p);
+    if (pool_host) (void)hipHostFree(pool_host);
+    if (ev_route) (void)hipEventDestroy(ev_route);
+    if (ev_fetch) (void)hipEventDestroy(ev_fetch);
+  }
+  template <typename T>
+  sekv_status alloc(T** out, size_t bytes, const char* what) {
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, bytes ? bytes : 256);
+    if (e != hipSuccess)
+      return fail(SEKV_ERR_NOMEM, "hipMalloc(%zu) for %s failed: %s", bytes, what,
+                  hipGetErrorString(e));
+    dev.push_back(p);
+    *out = (T*)p;
+    return SEKV_OK;
+  }
+  size_t kv_elem() const { return elem_bytes(cfg.kv_dtype); }
+  int bf16() const { return cfg.kv_dtype == SEKV_BF16; }
+};
+
+extern "C" {
+
+const char* sekv_last_error(void) { return g_err.c_str(); }
+
+sekv_status sekv_segment(const sekv_config* cfg, int32_t n_tokens, const float* surprisal_dev,
+                         int32_t* n_anchors, int32_t* n_spans, int32_t* n_compressed,
+                         hipStream_t stream) {
+  sekv_status r = check_config(cfg);
+  if (r) return r;
+  if (n_tokens < 1) return fail(SEKV_ERR_INVALID, "n_tokens must be >= 1");
+  if (!surprisal_dev) return fail(SEKV_ERR_INVALID, "surprisal_dev is NULL");
+  Scratch scr;
+  SegOut o{};
+  int32_t counts[4];
+  double stats[3];
+  if ((r = run_segment(cfg, n_tokens, surprisal_dev, scr, o, counts, stats, stream))) return r;
+  if (n_anchors) *n_anchors = counts[0];
+  if (n_spans) *n_spans = counts[1];
+  if (n_compressed) *n_compressed = counts[2];
+  return SEKV_OK;
+}
+
+static sekv_status build_impl(const sekv_config* cfg, int32_t n_tokens, const float* s,
+                              const void* k_dev, const void* v_dev, const float* w_route,
+                              const int32_t* rank_by_pos, hipStream_t st,
+                              std::unique_ptr<sekv_cache>& out) {
+  auto c = std::make_unique<sekv_cache>();
+  c->cfg = *cfg;
+  c->n_tokens = n_tokens;
+  c->group = cfg->n_q_heads / cfg->n_kv_heads;
+  const int L = cfg->n_layers, Hkv = cfg->n_kv_heads, Hq = cfg->n_q_heads, dr = cfg->route_dim;
+  const int n_lg = L * Hkv;
+  sekv_status r;
+
+  // ---- segmentation: tables stay in the cache (capacity n_tokens) ---------
+  Scratch scr;
+  SegOut o{};
+  int32_t counts[4];
+  if ((r = run_segment(cfg, n_tokens, s, scr, o, counts, c->stats, st))) return r;
+  for (void* p : {(void*)o.anchors, (void*)o.span_start, (void*)o.span_len, (void*)o.kind,
+                  (void*)o.cspan, (void*)o.cstart, (void*)o.clen, (void*)o.dense_pos}) {
+    scr.release(p);
+    c->dev.push_back(p);
+  }
+  c->anchors = o.anchors;
+  c->span_start = o.span_start;
+  c->span_len = o.span_len;
+  c->kind = o.kind;
+  c->cspan = o.cspan;
+  c->cstart = o.cstart;
+  c->clen = o.clen;
+  c->dense_pos = o.dense_pos;
+  c->n_anchors = counts[0];
+  c->n_spans = counts[1];
+  c->sc = counts[2];
+  c->n_dense = counts[3];
+  const int sc = c->sc, D = c->n_dense;
+  const size_t eb = c->kv_elem();
+
+  if ((r = c->alloc(&c->lnn64, (size_t)sc * 8, "lnn64"))) return r;
+  if ((r = c->alloc(&c->lnn32, (size_t)sc * 4, "lnn32"))) return r;
+  SEKV_HIP(launch_log_len(c->clen, sc, c->lnn64, c->lnn32, st));
+  if ((r = c->alloc(&c->rank, (size_t)n_lg * sc * 4, "rank"))) return r;
+  SEKV_HIP(launch_span_rank(rank_by_pos, c->cstart, c->clen, n_tokens, sc, n_lg, cfg->max_rank,
+                            c->rank, st));
+
+  // ---- full-resolution rows ------------------------------------------------
+  if ((r = c->alloc(&c->dense_k, (size_t)n_lg * D * kHeadDim * eb, "dense_k"))) return r;
+  if ((r = c->alloc(&c->dense_v, (size_t)n_lg * D * kHeadDim * eb, "dense_v"))) return r;
+  SEKV_HIP(launch_gather_dense(c->bf16(), k_dev, n_tokens, c->dense_pos, D, n_lg, c->dense_k, st));
+  SEKV_HIP(launch_gather_dense(c->bf16(), v_dev, n_tokens, c->dense_pos, D, n_lg, c->dense_v, st));
+
+  // ---- means and summaries -------------------------------------------------
+  if ((r = c->alloc(&c->kbar, (size_t)n_lg * sc * kHeadDim * eb, "kbar"))) return r;
+  if ((r = c->alloc(&c->vbar, (size_t)n_lg * sc * kHeadDim * eb, "vbar"))) return r;
+  if ((r = c->alloc(&c->summ, (size_t)L * Hq * sc * dr * eb, "summaries"))) return r;
+  SEKV_HIP(launch_span_summarize(c->bf16(), s, k_dev, v_dev, w_route, n_tokens, c->cstart,
+                                 c->clen, sc, L, Hkv, c->group, dr, c->kbar, c->vbar, c->summ, st));
+
+  // ---- factor pool layout (host) ---------------------------------------------
+  c->h_rank.resize((size_t)n_lg * sc);
+  c->h_clen.resize(sc);
+  if (sc) {
+    SEKV_HIP(hipMemcpyAsync(c->h_rank.data(), c->rank, c->h_rank.size() * 4,
+                            hipMemcpyDeviceToHost, st));
+    SEKV_HIP(hipMemcpyAsync(c->h_clen.data(), c->clen, (size_t)sc * 4, hipMemcpyDeviceToHost, st));
+  }
+  SEKV_HIP(hipStreamSynchronize(st));
+  c->h_fac_off.resize((size_t)n_lg * sc);
+  c->layer_base.assign(L + 1, 0);
+  uint64_t off = 0, fbytes = 0, stage_max = 0;
+  for (int l = 0; l < L; ++l) {
+    c->layer_base[l] = off;
+    for (int g = 0; g < Hkv; ++g)
+      for (int j = 0; j < sc; ++j) {
+        const size_t idx = ((size_t)l * Hkv + g) * sc + j;
+        const int rr = c->h_rank[idx], nn = c->h_clen[j];
+        c->h_fac_off[idx] = off;
+        off += FactorView(rr, nn).block_floats();
+        fbytes += 8ull * rr * (uint64_t)(nn + kHeadDim + 1);
+      }
+    stage_max = std::max(stage_max, off - c->layer_base[l]);
+  }
+  c->layer_base[L] = off;
+  c->pool_floats = off;
+  c->factor_bytes = fbytes;
+  if ((r = c->alloc(&c->fac_off, c->h_fac_off.size() * 8, "fac_off"))) return r;
+  if (!c->h_fac_off.empty())
+    SEKV_HIP(hipMemcpyAsync(c->fac_off, c->h_fac_off.data(), c->h_fac_off.size() * 8,
+                            hipMemcpyHostToDevice, st));
+
+  // ---- per-span SVD, spans bucketed by Gram size m = min(n, d) --------------
+  float* pool_build = nullptr;
+  const size_t pool_bytes = (size_t)c->pool_floats * 4;
+  if (cfg->factor_tier == SEKV_TIER_HOST_PINNED && cfg->host_pool_cap_bytes &&
+      pool_bytes > cfg->host_pool_cap_bytes)
+    return fail(SEKV_ERR_NOMEM, "factor pool needs %zu bytes, host pool cap is %llu", pool_bytes,
+                (unsigned long long)cfg->host_pool_cap_bytes);
+  if (cfg->factor_tier == SEKV_TIER_DEVICE) {
+    if ((r = c->alloc(&c->pool_dev, pool_bytes, "factor pool"))) return r;
+    pool_build = c->pool_dev;
+  } else {
+    if ((r = scr.alloc(&pool_build, pool_bytes, "factor build buffer"))) return r;
+  }
+  {
+    std::vector<int32_t> ids[3];
+    for (int j = 0; j < sc; ++j) {
+      const int m = std::min(c->h_clen[j], kHeadDim);
+      ids[m <= 32 ? 0 : (m <= 64 ? 1 : 2)].push_back(j);
+    }
+    const int max_m[3] = {32, 64, 128};
+    for (int b = 0; b < 3; ++b) {
+      if (ids[b].empty()) continue;
+      int32_t* d_ids = nullptr;
+      if ((r = scr.alloc(&d_ids, ids[b].size() * 4, "svd span ids"))) return r;
+      SEKV_HIP(hipMemcpyAsync(d_ids, ids[b].data(), ids[b].size() * 4, hipMemcpyHostToDevice, st));
+      for (int which = 0; which < 2; ++which)
+        SEKV_HIP(launch_span_svd(c->bf16(), which ? v_dev : k_dev, n_tokens, c->cstart, c->clen,
+                                 d_ids, (int)ids[b].size(), sc, n_lg, c->rank, c->fac_off,
+                                 pool_build, which, max_m[b], st));
+    }
+  }
+  if (cfg->factor_tier == SEKV_TIER_HOST_PINNED) {
+    hipError_t e = hipHostMalloc((void**)&c->pool_host, pool_bytes ? pool_bytes : 256,
+                                 hipHostMallocMapped | hipHostMallocPortable);
+    if (e != hipSuccess) {
+      c->pool_host = nullptr;
+      return fail(SEKV_ERR_NOMEM, "hipHostMalloc(%zu) for the factor pool failed: %s",
+                  pool_bytes, hipGetErrorString(e));
+    }
+    SEKV_HIP(hipHostGetDevicePointer((void**)&c->pool_host_dev, c->pool_host, 0));
+    if (pool_bytes)
+      SEKV_HIP(hipMemcpyAsync(c->pool_host, pool_build, pool_bytes, hipMemcpyDeviceToHost, st));
+    c->stage_floats = stage_max;
+    if ((r = c->alloc(&c->stage, (size_t)stage_max * 4, "fetch staging"))) return r;
+  }
+
+  // ---- decode geometry and routing scratch ----------------------------------
+  DecodeGeom& g = c->geom;
+  g.n_q_heads = Hq;
+  g.n_kv_heads = Hkv;
+  g.group = c->group;
+  g.route_dim = dr;
+  g.n_dense = D;
+  g.n_compressed = sc;
+  g.dense_tiles = (D + 255) / 256;
+  g.coarse_tiles = (sc + 255) / 256;
+  g.zoom_slots = sc ? 64 : 0;
+  g.n_slots = g.dense_tiles + g.coarse_tiles + g.zoom_slots;
+  const int nchunks = (sc + 255) / 256;
+  const size_t scr_ints = (size_t)Hkv * (c->group + 1) * ((size_t)nchunks * 256 + nchunks);
+  if ((r = c->alloc(&c->route_scratch, scr_ints * 4, "route scratch"))) return r;
+  if ((r = c->alloc(&c->tickets, (size_t)Hkv * 4, "route tickets"))) return r;
+  SEKV_HIP(hipMemsetAsync(c->tickets, 0, (size_t)Hkv * 4, st));
+  SEKV_HIP(hipEventCreateWithFlags(&c->ev_route, hipEventDisableTiming));
+  SEKV_HIP(hipEventCreateWithFlags(&c->ev_fetch, hipEventDisableTiming));
+  SEKV_HIP(hipStreamSynchronize(st));
+  out = std::move(c);
+  return SEKV_OK;
+}
+
+sekv_status sekv_build_spans(const sekv_config* cfg, int32_t n_tokens, const float* surprisal_dev,
+                             const void* k_dev, const void* v_dev, const float* w_route_dev,
+                             const int32_t* rank_by_pos_dev, hipStream_t stream,
+                             sekv_cache** out) {
+  if (!out) return fail(SEKV_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  sekv_status r = check_config(cfg);
+  if (r) return r;
+  if (n_tokens < 1) return fail(SEKV_ERR_INVALID, "n_tokens must be >= 1");
+  if (!surprisal_dev || !k_dev || !v_dev || !w_route_dev)
+    return fail(SEKV_ERR_INVALID, "surprisal, keys, values and w_route must be non-NULL");
+  std::unique_ptr<sekv_cache> c;
+  r = build_impl(cfg, n_tokens, surprisal_dev, k_dev, v_dev, w_route_dev, rank_by_pos_dev, stream,
+                 c);
+  if (r) {
+    (void)hipStreamSynchronize(stream);  // nothing queued may outlive the freed buffers
+    return r;
+  }
+  *out = c.release();
+  return SEKV_OK;
+}
+
+sekv_status sekv_cache_info_get(const sekv_cache* c, sekv_cache_info* out) {
+  if (!c || !out) return fail(SEKV_ERR_INVALID, "cache and out must be non-NULL");
+  const int L = c->cfg.n_layers, Hkv = c->cfg.n_kv_heads, Hq = c->cfg.n_q_heads;
+  const size_t eb = c->kv_elem();
+  out->n_tokens = c->n_tokens;
+  out->n_anchors = c->n_anchors;
+  out->n_spans = c->n_spans;
+  out->n_compressed = c->sc;
+  out->n_dense = c->n_dense;
+  out->factor_tier = c->cfg.factor_tier;
+  out->mu = c->stats[0];
+  out->sigma = c->stats[1];
+  out->threshold = c->stats[2];
+  out->resident_bytes = (uint64_t)L * Hkv * ((uint64_t)c->n_dense * 2 + (uint64_t)c->sc * 2) *
+                            kHeadDim * eb +
+                        (uint64_t)L * Hq * c->sc * c->cfg.route_dim * eb;
+  out->factor_bytes = c->factor_bytes;
+  out->factor_pool_bytes = (uint64_t)c->pool_floats * 4;
+  return SEKV_OK;
+}
+
+sekv_status sekv_cache_copy_spans(const sekv_cache* c, int32_t* anchors, int32_t* span_start,
+                                  int32_t* span_len, uint8_t* kind, int32_t* cspan,
+                                  int32_t* dense_pos) {
+  if (!c) return fail(SEKV_ERR_INVALID, "cache is NULL");
+  if (anchors && c->n_anchors)
+    SEKV_HIP(hipMemcpy(anchors, c->anchors, (size_t)c->n_anchors * 4, hipMemcpyDeviceToHost));
+  if (span_start && c->n_spans)
+    SEKV_HIP(hipMemcpy(span_start, c->span_start, (size_t)c->n_spans * 4, hipMemcpyDeviceToHost));
+  if (span_len && c->n_spans)
+    SEKV_HIP(hipMemcpy(span_len, c->span_len, (size_t)c->n_spans * 4, hipMemcpyDeviceToHost));
+  if (kind && c->n_spans)
+    SEKV_HIP(hipMemcpy(kind, c->kind, (size_t)c->n_spans, hipMemcpyDeviceToHost));
+  if (cspan && c->sc)
+    SEKV_HIP(hipMemcpy(cspan, c->cspan, (size_t)c->sc * 4, hipMemcpyDeviceToHost));
+  if (dense_pos && c->n_dense)
+    SEKV_HIP(hipMemcpy(dense_pos, c->dense_pos, (size_t)c->n_dense * 4, hipMemcpyDeviceToHost));
+  return SEKV_OK;
+}
+
+sekv_status sekv_cache_copy_group(const sekv_cache* c, int32_t layer, int32_t kv_head, void* kbar,
+                                  void* vbar, void* summary, int32_t* rank) {
+  if (!c) return fail(SEKV_ERR_INVALID, "cache is NULL");
+  if (layer < 0 || layer >= c->cfg.n_layers || kv_head < 0 || kv_head >= c->cfg.n_kv_heads)
+    return fail(SEKV_ERR_INVALID, "layer %d / kv_head %d out of range", layer, kv_head);
+  const size_t eb = c->kv_elem();
+  const int sc = c->sc, G = c->group, dr = c->cfg.route_dim;
+  const size_t lg = (size_t)layer * c->cfg.n_kv_heads + kv_head;
+  if (!sc) return SEKV_OK;
+  if (kbar)
+    SEKV_HIP(hipMemcpy(kbar, (const char*)c->kbar + lg * sc * kHeadDim * eb, (size_t)sc * kHeadDim * eb,
+                       hipMemcpyDeviceToHost));
+  if (vbar)
+    SEKV_HIP(hipMemcpy(vbar, (const char*)c->vbar + lg * sc * kHeadDim * eb, (size_t)sc * kHeadDim * eb,
+                       hipMemcpyDeviceToHost));
+  if (summary) {
+    const size_t h0 = (size_t)layer * c->cfg.n_q_heads + (size_t)kv_head * G;
+    SEKV_HIP(hipMemcpy(summary, (const char*)c->summ + h0 * sc * dr * eb, (size_t)G * sc * dr * eb,
+                       hipMemcpyDeviceToHost));
+  }
+  if (rank) std::memcpy(rank, c->h_rank.data() + lg * sc, (size_t)sc * 4);
+  return SEKV_OK;
+}
+
+sekv_status sekv_cache_copy_factors(const sekv_cache* c, int32_t layer, int32_t kv_head,
+                                    int32_t span, int32_t kv, float* u, float* sigma, float* vt) {
+  if (!c) return fail(SEKV_ERR_INVALID, "cache is NULL");
+  if (layer < 0 || layer >= c->cfg.n_layers || kv_head < 0 || kv_head >= c->cfg.n_kv_heads ||
+      span < 0 || span >= c->sc || (kv != 0 && kv != 1))
+    return fail(SEKV_ERR_INVALID, "layer/kv_head/span/kv out of range");
+  const size_t idx = ((size_t)layer * c->cfg.n_kv_heads + kv_head) * c->sc + span;
+  const int r = c->h_rank[idx], n = c->h_clen[span];
+  const FactorView fv(r, n);
+  std::vector<float> blk(fv.block_floats());
+  const float* src = (c->cfg.factor_tier == SEKV_TIER_DEVICE ? c->pool_dev : c->pool_host) +
+                     c->h_fac_off[idx];
+  if (c->cfg.factor_tier == SEKV_TIER_DEVICE)
+    SEKV_HIP(hipMemcpy(blk.data(), src, blk.size() * 4, hipMemcpyDeviceToHost));
+  else
+    std::memcpy(blk.data(), src, blk.size() * 4);
+  if (u)
+    for (int t = 0; t < n; ++t)
+      for (int i = 0; i < r; ++i) u[(size_t)t * r + i] = blk[fv.u(kv) + (size_t)i * fv.n4 + t];
+  if (sigma)
+    for (int i = 0; i < r; ++i) sigma[i] = blk[fv.sigma(kv) + i];
+  if (vt) std::memcpy(vt, blk.data() + fv.vt(kv), (size_t)r * kHeadDim * 4);
+  return SEKV_OK;
+}
+
+sekv_status sekv_route(const sekv_cache* c, int32_t layer, const float* q_dev,
+                       const float* proj_dev, const float* tau_dev, const sekv_route_out* out,
+                       hipStream_t stream) {
+  if (!c) return fail(SEKV_ERR_INVALID, "cache is NULL");
+  if (layer < 0 || layer >= c->cfg.n_layers)
+    return fail(SEKV_ERR_INVALID, "layer %d out of range [0, %d)", layer, c->cfg.n_layers);
+  if (!q_dev || !proj_dev || !tau_dev || !out)
+    return fail(SEKV_ERR_INVALID, "q, proj, tau and out must be non-NULL");
+  if (!out->mask || !out->list || !out->count || !out->union_list || !out->union_count)
+    return fail(SEKV_ERR_INVALID, "route output buffers must be non-NULL (prob may be NULL)");
+  const int Hq = c->cfg.n_q_heads, Hkv = c->cfg.n_kv_heads;
+  if (c->sc == 0) {
+    SEKV_HIP(hipMemsetAsync(out->count, 0, (size_t)Hq * 4, stream));
+    SEKV_HIP(hipMemsetAsync(out->union_count, 0, (size_t)Hkv * 4, stream));
+    return SEKV_OK;
+  }
+  const size_t eb = c->kv_elem();
+  const void* summ = (const char*)c->summ + (size_t)layer * Hq * c->sc * c->cfg.route_dim * eb;
+  SEKV_HIP(launch_route(c->bf16(), c->geom, q_dev, proj_dev, tau_dev, summ, c->lnn64,
+                        c->cfg.gamma, out->mask, out->prob, out->list, out->count,
+                        out->union_list, out->union_count, c->route_scratch, c->tickets, stream));
+  return SEKV_OK;
+}
+
+size_t sekv_decode_workspace_bytes(const sekv_cache* c) {
+  if (!c) return 0;
+  const size_t b = (size_t)c->cfg.n_q_heads * c->geom.n_slots * 132 * 4;
+  return (b + 255) & ~(size_t)255;
+}
+
+sekv_status sekv_decode_attn(const sekv_cache* c, int32_t layer, const float* q_dev,
+                             const sekv_route_out* route, float* o_dev, void* ws_dev,
+                             size_t ws_bytes, hipStream_t stream, hipStream_t fetch_stream) {
+  if (!c) return fail(SEKV_ERR_INVALID, "cache is NULL");
+  if (layer < 0 || layer >= c->cfg.n_layers)
+    return fail(SEKV_ERR_INVALID, "layer %d out of range [0, %d)", layer, c->cfg.n_layers);
+  if (!q_dev || !route || !o_dev || !ws_dev)
+    return fail(SEKV_ERR_INVALID, "q, route, o and workspace must be non-NULL");
+  if (!route->mask || !route->union_list || !route->union_count)
+    return fail(SEKV_ERR_INVALID, "route mask and union lists must be non-NULL");
+  if (ws_bytes < sekv_decode_workspace_bytes(c))
+    return fail(SEKV_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
+                sekv_decode_workspace_bytes(c));
+  const DecodeGeom& g = c->geom;
+  const int Hkv = c->cfg.n_kv_heads, sc = c->sc, D = c->n_dense;
+  const size_t eb = c->kv_elem();
+  const size_t lg0 = (size_t)layer * Hkv;
+  float* part = (float*)ws_dev;
+  const void* dk = (const char*)c->dense_k + lg0 * D * kHeadDim * eb;
+  const void* dv = (const char*)c->dense_v + lg0 * D * kHeadDim * eb;
+  const void* kb = (const char*)c->kbar + lg0 * sc * kHeadDim * eb;
+  const void* vb = (const char*)c->vbar + lg0 * sc * kHeadDim * eb;
+  const int32_t* rk = c->rank + lg0 * sc;
+  const uint64_t* fo = c->fac_off + lg0 * sc;
+  const bool host_tier = c->cfg.factor_tier == SEKV_TIER_HOST_PINNED;
+  hipStream_t fst = fetch_stream ? fetch_stream : stream;
+  if (host_tier && sc) {
+    // the fetch waits for this layer's router (queued earlier on `stream`)
+    if (fst != stream) {
+      SEKV_HIP(hipEventRecord(c->ev_route, stream));
+      SEKV_HIP(hipStreamWaitEvent(fst, c->ev_route, 0));
+    }
+    SEKV_HIP(launch_fetch_gather(g, route->union_list, route->union_count, c->clen, rk, fo,
+                                 c->layer_base[layer], c->pool_host_dev, c->stage, fst));
+    if (fst != stream) SEKV_HIP(hipEventRecord(c->ev_fetch, fst));
+  }
+  SEKV_HIP(launch_attn_tiles(c->bf16(), g, q_dev, dk, dv, kb, vb, c->lnn32, route->mask, part,
+                             stream));
+  if (sc) {
+    if (host_tier && fst != stream) SEKV_HIP(hipStreamWaitEvent(stream, c->ev_fetch, 0));
+    const float* pool = host_tier ? c->stage : c->pool_dev;
+    const uint64_t base = host_tier ? c->layer_base[layer] : 0;
+    SEKV_HIP(launch_attn_zoom(g, q_dev, route->mask, route->union_list, route->union_count,
+                              c->clen, rk, fo, pool, base, part, stream));
+  }
+  SEKV_HIP(launch_attn_merge(g, part, o_dev, stream));
+  return SEKV_OK;
+}
+
+void sekv_cache_destroy(sekv_cache* c) { delete c; }
+
+}  // extern "C"

@@ -1,0 +1,194 @@
+/*
+ * sekv.h - C ABI of the SeKV decode path on AMD Instinct MI355X (gfx950).
+ *
+ * SeKV keeps a long prompt as a resolution-adaptive cache (SeKV paper,
+ * Sec. 3): surprisal-guided spans, each with a small routing summary and a
+ * coarse mean key/value on the GPU and low-rank SVD factors of its keys and
+ * values in a second tier; anchor tokens and a local window stay at full
+ * resolution.  Each decode step routes the query against the summaries and
+ * runs one softmax over anchors, window, zoomed spans rebuilt from their
+ * factors, and the coarse entries of every other span.
+ *
+ * Conventions for every call:
+ *   - Pointers marked "device" are HIP device pointers the caller owns; they
+ *     must stay valid until the work queued on the given stream(s) completes.
+ *     Host pointers are read or written before the call returns.
+ *   - The library owns an sekv_cache and everything reachable from it
+ *     (device buffers, the factor pool, staging); sekv_cache_destroy frees it.
+ *   - Errors: argument errors are found on the host before any HIP call and
+ *     return SEKV_ERR_INVALID; failed allocations or a full host pool return
+ *     SEKV_ERR_NOMEM; a failing HIP call returns SEKV_ERR_HIP.  Faults inside
+ *     queued kernels surface at the caller's next synchronisation.  Every
+ *     failing call leaves a message for sekv_last_error() on the calling
+ *     thread, and a failing build leaves *out == NULL.
+ *   - A cache may be used by one host thread and one stream order at a time;
+ *     distinct caches are independent.
+ *   - Layouts are row-major C arrays; [a][b] means b varies fastest.
+ *     L = n_layers, Hq = n_q_heads, Hkv = n_kv_heads, G = Hq / Hkv (query
+ *     heads per KV head; query head h reads KV head h / G), d = head_dim,
+ *     dr = route_dim, N = tokens, S_c = compressed spans of the cache.
+ */
+#ifndef SEKV_H
+#define SEKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SEKV_OK = 0,
+  SEKV_ERR_INVALID = 1,
+  SEKV_ERR_NOMEM = 2,
+  SEKV_ERR_HIP = 3,
+  SEKV_ERR_UNSUPPORTED = 4
+} sekv_status;
+
+/* storage type of keys, values, coarse means and summaries */
+typedef enum { SEKV_F32 = 0, SEKV_BF16 = 1 } sekv_dtype;
+
+/* where the span factors live: device HBM, or pinned host memory fetched per
+ * step for the zoomed spans only (SeKV paper Sec. 3.2: bases on the CPU,
+ * fetched asynchronously for selected spans) */
+typedef enum { SEKV_TIER_DEVICE = 0, SEKV_TIER_HOST_PINNED = 1 } sekv_tier;
+
+typedef struct {
+  int32_t n_layers;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;     /* must divide n_q_heads; at most 8 query heads per KV head */
+  int32_t head_dim;       /* d; must be 128 */
+  int32_t route_dim;      /* dr; 1..64 (the paper uses 32) */
+  int32_t window;         /* most recent tokens kept at full resolution (paper: 512) */
+  int32_t max_rank;       /* rank cap R, 1..head_dim (paper: 32) */
+  int32_t min_span_len;   /* spans shorter than this stay at full resolution (>= 1) */
+  double alpha;           /* boundary sensitivity: anchor iff s_t > mean + alpha * std (paper: 1.0) */
+  double gamma;           /* size-prior coefficient of the gate, p = sigmoid(q~.s + gamma ln n) */
+  int32_t kv_dtype;       /* sekv_dtype */
+  int32_t factor_tier;    /* sekv_tier */
+  uint64_t host_pool_cap_bytes;  /* host tier: refuse a pool larger than this (0 = no cap) */
+} sekv_config;
+
+typedef struct {
+  int32_t n_tokens;
+  int32_t n_anchors;
+  int32_t n_spans;        /* all spans, compressed and short */
+  int32_t n_compressed;   /* S_c */
+  int32_t n_dense;        /* window + anchors + short-span tokens */
+  int32_t factor_tier;
+  double mu, sigma, threshold;   /* surprisal statistics of the build */
+  uint64_t resident_bytes;       /* dense rows, means, summaries, tables on the device */
+  uint64_t factor_bytes;         /* sum over (layer, KV head, span) of 8 r (n + d + 1) */
+  uint64_t factor_pool_bytes;    /* bytes allocated for the pool, padding included */
+} sekv_cache_info;
+
+/* Output of sekv_route for one layer; every buffer is device memory the
+ * caller allocates with the sizes below (S_c from sekv_cache_info). */
+typedef struct {
+  uint8_t* mask;         /* [Hq][S_c]  1 iff head h zooms span j */
+  int32_t* list;         /* [Hq][S_c]  zoomed span ids of head h, ascending; first count[h] valid */
+  int32_t* count;        /* [Hq] */
+  int32_t* union_list;   /* [Hkv][S_c] ids zoomed by any head of the group, ascending */
+  int32_t* union_count;  /* [Hkv] */
+  double* prob;          /* [Hq][S_c] gate values p, or NULL to skip */
+} sekv_route_out;
+
+typedef struct sekv_cache sekv_cache;
+
+/* Segmentation alone (SeKV paper Sec. 3.1): mean and population standard
+ * deviation of the surprisal over all n_tokens positions (float64), anchors
+ * are positions before the last `window` ones whose surprisal exceeds
+ * mean + alpha * std, spans are the maximal runs of other positions before
+ * the window, and spans of at least min_span_len tokens are compressed.
+ * surprisal_dev: device float32 [n_tokens].  Writes the counts (host
+ * pointers, any may be NULL); synchronises `stream`. */
+sekv_status sekv_segment(const sekv_config* cfg, int32_t n_tokens, const float* surprisal_dev,
+                         int32_t* n_anchors, int32_t* n_spans, int32_t* n_compressed,
+                         hipStream_t stream);
+
+/* Build the cache from a prefilled prompt (SeKV paper Sec. 3.1-3.2):
+ * segmentation as in sekv_segment; for every (layer, KV head) and compressed
+ * span j: normalised surprisal weights w_t = s_t / sum_j s (1/n if the sum is
+ * 0), coarse mean key and value sum_t w_t k_t and sum_t w_t v_t, and for every
+ * query head h of the group the routing summary W_h kbar_j, all accumulated in
+ * float64 and rounded once, to nearest even, to kv_dtype; the truncated SVD of
+ * the span's key matrix and of its value matrix, keeping
+ * r_j = min(max(rank, 1), n_j, d, max_rank) components (hard gates on Eq. 8),
+ * stored as float32 factors in the configured tier.  Anchors, the window and
+ * short-span tokens are copied to a contiguous full-resolution set.
+ *   k_dev, v_dev:  device [L][Hkv][N][d] in kv_dtype
+ *   w_route_dev:   device float32 [L][Hq][dr][d]  (summary projections W_h)
+ *   rank_by_pos_dev: device int32 [L][Hkv][N]: requested rank of the span that
+ *                  starts at each position; NULL requests max_rank everywhere.
+ * Inputs are only read during the call (it synchronises `stream`); the cache
+ * holds no pointer to them afterwards. */
+sekv_status sekv_build_spans(const sekv_config* cfg, int32_t n_tokens, const float* surprisal_dev,
+                             const void* k_dev, const void* v_dev, const float* w_route_dev,
+                             const int32_t* rank_by_pos_dev, hipStream_t stream, sekv_cache** out);
+
+sekv_status sekv_cache_info_get(const sekv_cache* cache, sekv_cache_info* out);
+
+/* Copy the span table to host arrays sized from sekv_cache_info (any may be
+ * NULL): anchors [n_anchors], span_start/span_len/kind [n_spans] (kind 0 =
+ * compressed, 1 = short), cspan [n_compressed] (index into the span arrays of
+ * each compressed span), dense_pos [n_dense] (ascending). */
+sekv_status sekv_cache_copy_spans(const sekv_cache* cache, int32_t* anchors, int32_t* span_start,
+                                  int32_t* span_len, uint8_t* kind, int32_t* cspan,
+                                  int32_t* dense_pos);
+
+/* Copy one (layer, KV head) of the cache's stored representation to host
+ * memory (any pointer may be NULL), for inspection and tests:
+ *   kbar, vbar [S_c][d] and summary [G][S_c][dr], in kv_dtype;
+ *   rank [S_c] int32 (retained rank r_j);
+ *   factors of compressed span j, if j >= 0: kv = 0 keys, 1 values;
+ *   u [n_j][r_j], sigma [r_j], vt [r_j][d], all float32. */
+sekv_status sekv_cache_copy_group(const sekv_cache* cache, int32_t layer, int32_t kv_head,
+                                  void* kbar, void* vbar, void* summary, int32_t* rank);
+sekv_status sekv_cache_copy_factors(const sekv_cache* cache, int32_t layer, int32_t kv_head,
+                                    int32_t span, int32_t kv, float* u, float* sigma, float* vt);
+
+/* Route one layer (SeKV paper Sec. 3.2 gate and Sec. 3.3 Eq. 9), float64
+ * throughout: q~_h = P_h q_h; x_j = q~_h . s_{h,j} + gamma ln n_j;
+ * p_j = 1 / (1 + e^-x_j); span j is zoomed by head h iff p_j > tau_h.
+ * Fills `out`: per-head mask and ascending list, per-group ascending union.
+ *   q_dev:    device float32 [Hq][d]
+ *   proj_dev: device float32 [Hq][dr][d]  (query projections P_h of this layer)
+ *   tau_dev:  device float32 [Hq]
+ * Asynchronous on `stream`. */
+sekv_status sekv_route(const sekv_cache* cache, int32_t layer, const float* q_dev,
+                       const float* proj_dev, const float* tau_dev, const sekv_route_out* out,
+                       hipStream_t stream);
+
+/* Bytes of device workspace sekv_decode_attn needs (256-byte aligned). */
+size_t sekv_decode_workspace_bytes(const sekv_cache* cache);
+
+/* Attention of one layer over the mixed-resolution memory (SeKV paper
+ * Sec. 3.3): one softmax, scale 1/sqrt(d), over every full-resolution row of
+ * the group, one coarse entry (kbar_j, vbar_j) with ln n_j added to its scaled
+ * score for every compressed span the head did not zoom, and the n_j rows
+ * U_j diag(sigma_j) V_j^T of every span it zoomed, for keys and values alike.
+ * Accumulates in float32.
+ *   q_dev: device float32 [Hq][d]; route: the output of sekv_route for this
+ *   layer and query (its mask and union lists are read); o_dev: device float32
+ *   [Hq][d]; ws_dev: device workspace of at least
+ *   sekv_decode_workspace_bytes(cache) bytes.
+ * Runs on `stream`.  With host-tier factors, the zoomed spans' factors are
+ * copied into device staging on `fetch_stream` (NULL = `stream`) while the
+ * full-resolution and coarse entries are processed on `stream`. */
+sekv_status sekv_decode_attn(const sekv_cache* cache, int32_t layer, const float* q_dev,
+                             const sekv_route_out* route, float* o_dev, void* ws_dev,
+                             size_t ws_bytes, hipStream_t stream, hipStream_t fetch_stream);
+
+void sekv_cache_destroy(sekv_cache* cache);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* sekv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEKV_H */

@@ -1,0 +1,104 @@
+"""The C ABI library loads on a machine without a GPU, exports every function
+include/sekv.h declares, and rejects invalid arguments on the host before any
+HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compressed_kv_attention_sekv_amd as S
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "sekv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sekv_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(S.library_path()):
+        pytest.skip("libsekv.so not built")
+    return S.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(S.EXPORTED_SYMBOLS)
+
+
+def test_config_struct_layout_matches_header():
+    # int32 x8, double x2, int32 x2, uint64 -> 64 bytes with natural alignment
+    assert ctypes.sizeof(S.SekvConfig) == 64
+    assert ctypes.sizeof(S.SekvRouteOut) == 48
+
+
+def _cfg(**kw):
+    c = S.make_config(2, 8, 2)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("field,value,msg", [
+    ("head_dim", 64, "head_dim"),
+    ("n_q_heads", 7, "multiple"),
+    ("n_kv_heads", 0, "multiple"),
+    ("route_dim", 0, "route_dim"),
+    ("route_dim", 65, "route_dim"),
+    ("max_rank", 0, "max_rank"),
+    ("max_rank", 129, "max_rank"),
+    ("min_span_len", 0, "min_span_len"),
+    ("window", -1, "window"),
+    ("n_layers", 0, "n_layers"),
+    ("kv_dtype", 7, "kv_dtype"),
+    ("factor_tier", 3, "factor_tier"),
+    ("alpha", float("nan"), "finite"),
+])
+def test_build_rejects_bad_config(L, field, value, msg):
+    cfg = _cfg(**{field: value})
+    out = ctypes.c_void_p(123)
+    st = L.sekv_build_spans(ctypes.byref(cfg), 100, ctypes.c_void_p(8), ctypes.c_void_p(8),
+                            ctypes.c_void_p(8), ctypes.c_void_p(8), None, None, ctypes.byref(out))
+    assert st == S.SEKV_ERR_INVALID
+    assert msg in L.sekv_last_error().decode()
+    assert out.value is None
+
+
+def test_build_rejects_null_inputs_and_sizes(L):
+    cfg = _cfg()
+    out = ctypes.c_void_p()
+    assert L.sekv_build_spans(ctypes.byref(cfg), 100, None, ctypes.c_void_p(8), ctypes.c_void_p(8),
+                              ctypes.c_void_p(8), None, None, ctypes.byref(out)) == S.SEKV_ERR_INVALID
+    assert L.sekv_build_spans(ctypes.byref(cfg), 0, ctypes.c_void_p(8), ctypes.c_void_p(8),
+                              ctypes.c_void_p(8), ctypes.c_void_p(8), None, None,
+                              ctypes.byref(out)) == S.SEKV_ERR_INVALID
+    assert L.sekv_build_spans(ctypes.byref(cfg), 10, ctypes.c_void_p(8), ctypes.c_void_p(8),
+                              ctypes.c_void_p(8), ctypes.c_void_p(8), None, None,
+                              None) == S.SEKV_ERR_INVALID
+    assert L.sekv_segment(None, 10, ctypes.c_void_p(8), None, None, None, None) == S.SEKV_ERR_INVALID
+
+
+def test_calls_on_null_cache_are_rejected(L):
+    ro = S.SekvRouteOut()
+    assert L.sekv_route(None, 0, None, None, None, ctypes.byref(ro), None) == S.SEKV_ERR_INVALID
+    assert L.sekv_decode_attn(None, 0, None, ctypes.byref(ro), None, None, 0, None,
+                              None) == S.SEKV_ERR_INVALID
+    assert L.sekv_decode_workspace_bytes(None) == 0
+    info = S.SekvCacheInfo()
+    assert L.sekv_cache_info_get(None, ctypes.byref(info)) == S.SEKV_ERR_INVALID
+    L.sekv_cache_destroy(None)  # no-op
+
+
+def test_binding_checks_tensor_arguments():
+    import torch
+    cfg = S.make_config(1, 4, 1, kv_dtype="f32")
+    with pytest.raises(ValueError, match="device tensor"):
+        S.sekv_build_spans(cfg, torch.zeros(10), torch.zeros(1, 1, 10, 128),
+                           torch.zeros(1, 1, 10, 128), torch.zeros(1, 4, 32, 128))

@@ -1,0 +1,205 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the same
+seeded inputs: span table bit-exact, means and summaries bit-exact up to
+float64 rounding-order ties at the storage rounding point, factors by
+reconstruction and singular values, zoom masks and lists bit-exact outside the
+|p - tau| < 1e-5 band, attention within 1e-5 (float32 K/V) or 2e-3 (bf16 K/V)
+norm-wise relative error."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.conftest import gpu_available
+from tests.parity import (Inputs, OracleSide, calibrate_tau, compare_group, compare_route,
+                          compare_spans, log, make_cfg, rel_err, tied_heads, to64)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+
+@pytest.fixture(scope="module")
+def S():
+    import compressed_kv_attention_sekv_amd as S
+    S.lib()
+    return S
+
+
+def run_gpu_layer(S, cache, layer, q, p, tau, with_prob=True):
+    rb = S.RouteBuffers.allocate(cache, with_prob=with_prob)
+    S.sekv_route(cache, layer, q.contiguous(), p.contiguous(), tau.contiguous(), rb)
+    o = torch.zeros(cache.cfg.n_q_heads, cache.cfg.head_dim, device="cuda")
+    ws = torch.empty(cache.workspace_bytes(), dtype=torch.uint8, device="cuda")
+    S.sekv_decode_attn(cache, layer, q.contiguous(), rb, o, ws)
+    torch.cuda.synchronize()
+    return rb, o
+
+
+def check_layer(S, cache, orc, inp, layer, q, tau, gamma, tol):
+    p = inp.p[layer]
+    rb, o = run_gpu_layer(S, cache, layer, q, p, tau)
+    route = orc.route(layer, to64(q), to64(p), to64(tau), gamma)
+    n_tie = compare_route(rb, route, to64(tau), inp.wl)
+    skip = set(tied_heads(route, to64(tau)))
+    ref = orc.decode(layer, to64(q), route)
+    og = to64(o)
+    worst = 0.0
+    for h in range(inp.wl.n_q_heads):
+        if h in skip:
+            continue
+        e = rel_err(og[h], ref[h])
+        worst = max(worst, e)
+    assert worst <= tol, f"attention error {worst} > {tol}"
+    return n_tie, worst, route
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3, 4])
+def test_tiny_workload_full_parity(S, seed):
+    wl = synth.workload("tiny")
+    log(f"[parity] tiny seed={seed} N={wl.n_tokens}")
+    inp = Inputs(wl, seed)
+    cache = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    orc = OracleSide(inp, [0], wl.max_rank)
+    compare_spans(cache, orc)
+    compare_group(cache, orc, 0, 0, n_factor_checks=1000)
+    tau = synth.tau_uniform(wl, seed, device="cuda")
+    n_tie, worst, route = check_layer(S, cache, orc, inp, 0, inp.query(0)[0], tau[0], wl.gamma,
+                                      TOL["f32"])
+    log(f"[parity] tiny seed={seed} spans={cache.info.n_compressed} zoomed={int(route.mask.sum())} "
+        f"ties={n_tie} err={worst:.2e}")
+
+
+def _reduced(name, **kw):
+    return synth.workload(name, **kw)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("llama3_8b_128k", dict(n_layers=2, n_tokens=16384 + 77)),
+    ("llama32_3b_32k", dict(n_layers=1, n_tokens=8192 + 5)),
+    ("qwen25_14b_128k_b4", dict(n_layers=1, n_tokens=6000, batch=1)),
+])
+def test_bf16_reduced_shapes(S, name, kw):
+    wl = _reduced(name, **kw)
+    seed = synth.default_seed(wl)
+    log(f"[parity] {name} {kw}")
+    inp = Inputs(wl, seed)
+    cache = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    layers = list(range(wl.n_layers))
+    orc = OracleSide(inp, layers, wl.max_rank)
+    compare_spans(cache, orc)
+    for layer in layers:
+        for kh in range(wl.n_kv_heads):
+            compare_group(cache, orc, layer, kh, n_factor_checks=6)
+    tau = calibrate_tau(orc, inp, layers, synth.zoom_targets(wl, seed), wl.gamma).cuda()
+    for step in range(2):
+        q = inp.query(step)
+        for layer in layers:
+            n_tie, worst, route = check_layer(S, cache, orc, inp, layer, q[layer], tau[layer],
+                                              wl.gamma, TOL["bf16"])
+            log(f"[parity] {name} step={step} layer={layer} zoom={route.mask.mean():.3f} "
+                f"ties={n_tie} err={worst:.2e}")
+
+
+def _sdpa(q, k, v):
+    hq, hkv = q.shape[0], k.shape[0]
+    kt = torch.from_numpy(np.repeat(k, hq // hkv, axis=0))
+    vt = torch.from_numpy(np.repeat(v, hq // hkv, axis=0))
+    o = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q)[:, None, :], kt, vt)
+    return o[:, 0, :].numpy()
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", dict()),
+    ("llama3_8b_128k", dict(n_layers=1, n_tokens=6000, n_q_heads=8, n_kv_heads=2)),
+])
+def test_all_zoomed_full_rank_is_dense_attention(S, name, kw):
+    """Every span zoomed with every component kept: textbook attention over
+    all N rows (torch SDPA on the CPU in float64), any gamma."""
+    wl = synth.workload(name, **kw)
+    log(f"[parity] dense check {name} {kw}")
+    inp = Inputs(wl, 5)
+    cache = S.sekv_build_spans(make_cfg(S, wl, max_rank=128), inp.s, inp.k, inp.v, inp.w,
+                               torch.full_like(inp.ranks, 128))
+    q = inp.query(0)[0]
+    tau = torch.full((wl.n_q_heads,), -1.0, device="cuda")
+    rb, o = run_gpu_layer(S, cache, 0, q, inp.p[0], tau)
+    assert int(rb.mask.sum()) == wl.n_q_heads * cache.info.n_compressed
+    ref = _sdpa(to64(q), to64(inp.k[0]), to64(inp.v[0]))
+    err = max(rel_err(to64(o)[h], ref[h]) for h in range(wl.n_q_heads))
+    log(f"[parity] dense check err={err:.2e}")
+    assert err <= TOL[wl.kv_dtype]
+
+
+@pytest.mark.parametrize("case", ["none_zoomed", "short_context", "constant_surprisal",
+                                  "ragged_small"])
+def test_edge_cases(S, case):
+    wl = synth.workload("tiny")
+    tau_val = None
+    surprisal = None
+    if case == "none_zoomed":
+        tau_val = 1.0
+    elif case == "short_context":
+        wl = wl.with_(n_tokens=300)
+    elif case == "constant_surprisal":
+        surprisal = torch.full((wl.n_tokens,), 0.75)
+    elif case == "ragged_small":
+        wl = wl.with_(n_tokens=777, window=100, min_span_len=3)
+    log(f"[parity] edge case {case} N={wl.n_tokens}")
+    inp = Inputs(wl, 11, surprisal=surprisal)
+    cache = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    orc = OracleSide(inp, [0], wl.max_rank)
+    compare_spans(cache, orc)
+    if cache.info.n_compressed:
+        compare_group(cache, orc, 0, 0, n_factor_checks=50)
+    tau = synth.tau_uniform(wl, 11, device="cuda")[0]
+    if tau_val is not None:
+        tau = torch.full_like(tau, tau_val)
+    n_tie, worst, route = check_layer(S, cache, orc, inp, 0, inp.query(0)[0], tau, wl.gamma,
+                                      TOL["f32"])
+    if case == "none_zoomed":
+        assert not route.mask.any()
+    if case == "constant_surprisal":
+        assert cache.info.n_anchors == 0 and cache.info.n_compressed == 1
+    log(f"[parity] edge case {case} spans={cache.info.n_compressed} err={worst:.2e}")
+
+
+def test_repeat_runs_are_bit_identical(S):
+    wl = synth.workload("llama3_8b_128k", n_layers=1, n_tokens=9000)
+    log("[parity] determinism")
+    inp = Inputs(wl, 3)
+    cache = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    q = inp.query(0)[0]
+    tau = torch.full((wl.n_q_heads,), 0.6, device="cuda")
+    rb1, o1 = run_gpu_layer(S, cache, 0, q, inp.p[0], tau)
+    rb2, o2 = run_gpu_layer(S, cache, 0, q, inp.p[0], tau)
+    assert torch.equal(o1, o2)
+    assert torch.equal(rb1.mask, rb2.mask) and torch.equal(rb1.union_list, rb2.union_list)
+    assert torch.equal(rb1.list, rb2.list) and torch.equal(rb1.count, rb2.count)
+    cache2 = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    _, o3 = run_gpu_layer(S, cache2, 0, q, inp.p[0], tau)
+    assert torch.equal(o1, o3)
+
+
+def test_host_tier_matches_device_tier(S):
+    wl = synth.workload("llama3_8b_128k", n_layers=2, n_tokens=9000)
+    log("[parity] host tier")
+    inp = Inputs(wl, 4)
+    dev = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    host = S.sekv_build_spans(make_cfg(S, wl, tier="host"), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    tau = torch.full((wl.n_q_heads,), 0.7, device="cuda")
+    side = torch.cuda.Stream()
+    for layer in range(2):
+        q = inp.query(1)[layer]
+        _, od = run_gpu_layer(S, dev, layer, q, inp.p[layer], tau)
+        rb = S.RouteBuffers.allocate(host)
+        S.sekv_route(host, layer, q, inp.p[layer].contiguous(), tau, rb)
+        oh = torch.zeros_like(od)
+        ws = torch.empty(host.workspace_bytes(), dtype=torch.uint8, device="cuda")
+        S.sekv_decode_attn(host, layer, q, rb, oh, ws, fetch_stream=side)
+        torch.cuda.synchronize()
+        assert int(rb.union_count.sum()) > 0
+        assert torch.equal(od, oh)
