@@ -1,0 +1,384 @@
+"""Decode-step benchmark of the SeKV HIP library on one MI355X.
+
+One step = for every layer, in order: route (gate + zoom lists) and the
+mixed-resolution attention over anchors, window, zoomed spans (factored) and
+coarse entries.  Inputs are seeded synthetic tensors with the shapes of the
+Llama-3-8B workload at 128K context (32 layers, 32 query / 8 KV heads, d 128,
+bf16 K/V, spans of ~80 tokens, rank cap 32, window 512, 10% of heads zoom ~20%
+of spans and the rest ~1%), resident in HBM before timing starts.
+
+Prints ONE JSON line.  ``value`` is decode steps/s of the whole job.
+``roofline`` covers the attention launch of one layer (the dominant kernel):
+algorithmic bytes per launch / average launch time from HIP events recorded on
+the launch stream.  ``cpu_baseline`` times the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attn steps/s at 128K ctx (Llama-3-8B shape); achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+PCIE_GBS = 64.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3_8b_128k")
+    ap.add_argument("--tier", choices=["device", "host"], default="device")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=3)
+    ap.add_argument("--n-layers", type=int, default=None, help="override layer count (testing)")
+    ap.add_argument("--n-tokens", type=int, default=None, help="override context (testing)")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "compressed_kv_attention_sekv_amd", "csrc"))):
+        with open(os.path.join(ROOT, "compressed_kv_attention_sekv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM traffic per attention launch from committed rocprofv3 --pmc
+    summaries, only if they were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_attn_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this path runs on a "
+              "single MI355X; see the sharding notes in the design document)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import compressed_kv_attention_sekv_amd as S
+    import synth
+
+    S.lib()
+    dev = "cuda"
+    over = {}
+    if args.n_layers:
+        over["n_layers"] = args.n_layers
+    if args.n_tokens:
+        over["n_tokens"] = args.n_tokens
+    wl = synth.workload(args.workload, **over)
+    if wl.batch != 1:
+        wl = wl.with_(batch=1)
+    seed = synth.default_seed(wl)
+    L, Hq, Hkv, d, G = wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.group
+
+    # ---- inputs, resident in HBM -------------------------------------------------
+    t0 = time.time()
+    s, spike = synth.surprisal(wl, seed, device=dev)
+    k, v, ranks = synth.kv_cache(wl, seed, spike, device=dev)
+    w, p = synth.route_weights(wl, seed, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs drawn in {time.time() - t0:.1f}s: K/V {2 * k.numel() * k.element_size() / 1e9:.1f} GB")
+
+    cfg = S.make_config(L, Hq, Hkv, head_dim=d, route_dim=wl.route_dim, window=wl.window,
+                        max_rank=wl.max_rank, min_span_len=wl.min_span_len, alpha=wl.alpha,
+                        gamma=wl.gamma, kv_dtype=wl.kv_dtype, factor_tier=args.tier)
+    torch.cuda.synchronize()
+    t0 = time.time()
+    cache = S.sekv_build_spans(cfg, s, k, v, w, ranks)
+    torch.cuda.synchronize()
+    build_s = time.time() - t0
+    info = cache.info
+    log(f"build {build_s:.2f}s: spans {info.n_spans} compressed {info.n_compressed} anchors "
+        f"{info.n_anchors} dense {info.n_dense} factor pool {info.factor_pool_bytes / 1e9:.2f} GB")
+    sc = info.n_compressed
+    # the K/V inputs are not needed by the decode step
+    del k, v
+    torch.cuda.empty_cache()
+
+    # ---- thresholds: calibrated on the library's own gate values ---------------
+    targets = synth.zoom_targets(wl, seed) if wl.tau_mode != "uniform" else None
+    if targets is None:
+        tau = synth.tau_uniform(wl, seed, device=dev)
+    else:
+        cq = synth.calibration_queries(wl, seed, 16, device=dev)
+        tau = torch.empty(L, Hq, dtype=torch.float32, device=dev)
+        rb = S.RouteBuffers.allocate(cache, with_prob=True)
+        big = torch.full((Hq,), 2.0, device=dev)
+        for layer in range(L):
+            probs = []
+            for i in range(cq.shape[0]):
+                S.sekv_route(cache, layer, cq[i, layer].contiguous(), p[layer].contiguous(), big, rb)
+                probs.append(rb.prob.clone())
+            allp = torch.cat(probs, dim=1)
+            tau[layer] = torch.stack([torch.quantile(allp[h], 1.0 - float(targets[layer, h]))
+                                      for h in range(Hq)]).float()
+        torch.cuda.synchronize()
+
+    # ---- per-step buffers ----------------------------------------------------------
+    n_q = args.steps + args.warmup
+    qs = torch.stack([synth.queries(wl, seed, i, device=dev) for i in range(n_q)])  # [T][L][Hq][d]
+    q_cur = torch.empty(L, Hq, d, device=dev)
+    p_c = [p[l].contiguous() for l in range(L)]
+    tau_c = [tau[l].contiguous() for l in range(L)]
+    routes = [S.RouteBuffers.allocate(cache) for _ in range(L)]
+    outs = torch.zeros(L, Hq, d, device=dev)
+    ws = torch.empty(cache.workspace_bytes(), dtype=torch.uint8, device=dev)
+    side = torch.cuda.Stream() if args.tier == "host" else None
+
+    def step():
+        for layer in range(L):
+            S.sekv_route(cache, layer, q_cur[layer], p_c[layer], tau_c[layer], routes[layer])
+            S.sekv_decode_attn(cache, layer, q_cur[layer], routes[layer], outs[layer], ws,
+                               fetch_stream=side)
+
+    graph = None
+    if not args.no_graph and args.tier == "device":
+        q_cur.copy_(qs[0])
+        step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+
+    def run(i):
+        q_cur.copy_(qs[i])
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region ----------------------------------------------------------
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.time()
+    ev0.record()
+    for i in range(args.warmup, n_q):
+        run(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.time() - wall0
+    total_ms = ev0.elapsed_time(ev1)
+    ms_per_step = total_ms / args.steps
+    log(f"{args.steps} steps in {total_ms:.1f} ms (wall {wall * 1e3:.1f} ms): {ms_per_step:.4f} ms/step")
+
+    # ---- algorithmic bytes of the timed steps ----------------------------------
+    eb = 2 if wl.kv_dtype == "bf16" else 4
+    clen = torch.tensor([0], dtype=torch.int64)
+    sp = cache.spans()
+    clen = sp["span_len"][sp["cspan"].long()].to(torch.float64)
+    rank_tab = torch.stack([torch.stack([cache.group_data(l, g)[3] for g in range(Hkv)])
+                            for l in range(L)]).to(torch.float64)  # [L][Hkv][Sc]
+    span_bytes = (8.0 * rank_tab * (clen + d + 1)).to(dev)      # factor bytes per (l, g, j)
+    D = info.n_dense
+    resident_layer = (Hkv * (2 * d * eb * D + 2 * d * eb * sc) + Hq * wl.route_dim * eb * sc +
+                      Hq * (wl.route_dim * d + d + 1) * 4 + Hq * d * 4 + 4 * sc)
+    attn_resident_layer = Hkv * (2 * d * eb * D + 2 * d * eb * sc) + Hq * d * 4 * 2 + Hq * sc
+    zoom_bytes = torch.zeros(args.steps, L, dtype=torch.float64, device=dev)
+    zoom_frac = torch.zeros(L, Hq, dtype=torch.float64, device=dev)
+    union_frac = torch.zeros(L, Hkv, dtype=torch.float64, device=dev)
+    ar = torch.arange(max(sc, 1), device=dev)
+    for si, i in enumerate(range(args.warmup, n_q)):
+        q_cur.copy_(qs[i])
+        for layer in range(L):
+            rb = routes[layer]
+            S.sekv_route(cache, layer, q_cur[layer], p_c[layer], tau_c[layer], rb)
+            valid = ar.unsqueeze(0) < rb.union_count.unsqueeze(1)               # [Hkv][Sc]
+            ids = torch.where(valid, rb.union_list.long(), torch.zeros_like(rb.union_list.long()))
+            zb = torch.gather(span_bytes[layer], 1, ids) * valid
+            zoom_bytes[si, layer] = zb.sum()
+            zoom_frac[layer] += rb.count.double() / max(sc, 1)
+            union_frac[layer] += rb.union_count.double() / max(sc, 1)
+    torch.cuda.synchronize()
+    zoom_frac /= args.steps
+    union_frac /= args.steps
+    zb_step = zoom_bytes.sum(1)                       # [steps]
+    bytes_step = float(zb_step.mean()) + L * resident_layer
+    attn_bytes_launch = float(zb_step.mean()) / L + attn_resident_layer
+    step_gbs = bytes_step / (ms_per_step * 1e-3) / 1e9
+    log(f"bytes/step {bytes_step / 1e9:.3f} GB (zoom {float(zb_step.mean()) / 1e9:.3f} GB): "
+        f"{step_gbs:.0f} GB/s = {step_gbs / HBM_PEAK_GBS:.3f} of peak")
+
+    # ---- live per-launch timing of the attention kernel ------------------------
+    n_meas = min(8, args.steps)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(L)] for _ in range(n_meas)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)   # keep the GPU busy while every launch below is queued
+    for m in range(n_meas):
+        i = args.warmup + m
+        q_cur.copy_(qs[i])
+        for layer in range(L):
+            S.sekv_route(cache, layer, q_cur[layer], p_c[layer], tau_c[layer], routes[layer])
+            evs[m][layer][0].record()
+            S.sekv_decode_attn(cache, layer, q_cur[layer], routes[layer], outs[layer], ws,
+                               fetch_stream=side)
+            evs[m][layer][1].record()
+    torch.cuda.synchronize()
+    attn_us = [a.elapsed_time(b) * 1e3 for row in evs for (a, b) in row]
+    attn_us_mean = float(np.mean(attn_us))
+    attn_bytes_meas = float(zoom_bytes[:n_meas].mean()) / L + attn_resident_layer
+    attn_gbs = attn_bytes_meas / (attn_us_mean * 1e-6) / 1e9
+    log(f"attention launch: {attn_us_mean:.2f} us avg, {attn_bytes_meas / 1e6:.2f} MB algorithmic "
+        f"-> {attn_gbs:.0f} GB/s")
+
+    # ---- reference probes: device copy and pinned host->device copy ------------
+    x = torch.empty(512 * 1024 * 1024, dtype=torch.float32, device=dev)   # 2 GiB
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x, y
+    hpin = torch.empty(64 * 1024 * 1024, dtype=torch.float32, pin_memory=True)   # 256 MiB
+    hd = torch.empty(hpin.shape, dtype=torch.float32, device=dev)
+    hd.copy_(hpin, non_blocking=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(4):
+        hd.copy_(hpin, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    h2d_gbs = 4 * hpin.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del hpin, hd
+    log(f"probes: device copy {copy_gbs:.0f} GB/s (read+write), pinned H2D {h2d_gbs:.1f} GB/s")
+
+    host_link = None
+    if args.tier == "host":
+        link_gbs = float(zb_step.mean()) / (ms_per_step * 1e-3) / 1e9
+        host_link = {"gbs": link_gbs, "frac_of_measured_h2d": link_gbs / h2d_gbs,
+                     "frac_of_pcie5_x16": link_gbs / PCIE_GBS}
+
+    # ---- CPU oracle baseline on a bounded sample --------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, seed, s, spike, w, p, tau, qs, args, ranks)
+
+    traffic = read_traffic(wl.name)
+    result = {
+        "metric": METRIC,
+        "value": 1e3 / ms_per_step,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.kv_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "n_layers": L, "n_q_heads": Hq, "n_kv_heads": Hkv,
+            "head_dim": d, "context": wl.n_tokens, "batch": 1, "kv_dtype": wl.kv_dtype,
+            "factor_dtype": "f32", "factor_tier": args.tier, "window": wl.window,
+            "max_rank": wl.max_rank, "route_dim": wl.route_dim, "graph": graph is not None,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": attn_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": attn_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel": "sekv_decode_attn (one layer)",
+            "algorithmic_bytes_per_launch": attn_bytes_meas,
+            "avg_launch_us": attn_us_mean,
+        },
+        "cpu_baseline": cpu,
+        "step_hbm": {"bytes_per_step": bytes_step, "gbs": step_gbs, "frac": step_gbs / HBM_PEAK_GBS,
+                     "measured_copy_gbs": copy_gbs},
+        "host_link": host_link,
+        "measured_h2d_gbs": h2d_gbs,
+        "cache": {"n_spans": info.n_spans, "n_compressed": sc, "n_anchors": info.n_anchors,
+                  "n_dense": info.n_dense, "factor_pool_gb": info.factor_pool_bytes / 1e9,
+                  "resident_gb": info.resident_bytes / 1e9, "build_s": build_s,
+                  "zoom_frac_per_head_mean": float(zoom_frac.mean()),
+                  "union_frac_per_group_mean": float(union_frac.mean()),
+                  "zoom_bytes_per_step_gb": float(zb_step.mean()) / 1e9},
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, seed, s, spike, w, p, tau, qs, args, ranks):
+    """The oracle as it stands, on one core: build the oracle's cache for a
+    few layers (untimed), then time its decode (route + attention, every
+    query head) of those layers for one step and scale to a full step."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    import synth
+
+    layers = list(range(max(0, wl.n_layers - args.cpu_layers), wl.n_layers))
+    f64 = lambda t: t.detach().cpu().double().numpy()  # noqa: E731
+    with threadpool_limits(limits=1):
+        t0 = time.time()
+        sv = f64(s)
+        seg = O.segment(sv, wl.window, wl.alpha, wl.min_span_len)
+        g = wl.group
+        groups = {}
+        for layer in layers:
+            kk, vv, rk = synth.kv_cache(wl, seed, spike, device=s.device, layers=[layer])
+            wl_ = f64(w[layer])
+            groups[layer] = {kh: O.build_group(seg, sv, f64(kk[0, kh]), f64(vv[0, kh]),
+                                               {h: wl_[h] for h in range(kh * g, kh * g + g)},
+                                               rk[0, kh].cpu().numpy(), wl.kv_dtype, wl.max_rank)
+                             for kh in range(wl.n_kv_heads)}
+            del kk, vv
+        build_s = time.time() - t0
+        q = f64(qs[args.warmup])
+        t0 = time.time()
+        for layer in layers:
+            summ = {h: groups[layer][h // g].summary[h] for h in range(wl.n_q_heads)}
+            route = O.route_layer(q[layer], f64(p[layer]), f64(tau[layer]), summ, seg, wl.gamma,
+                                  wl.n_kv_heads)
+            O.decode_layer(q[layer], route, groups[layer], seg, n_kv_heads=wl.n_kv_heads)
+        dt = time.time() - t0
+    per_step = dt / len(layers) * wl.n_layers
+    log(f"cpu oracle: {len(layers)} layers decoded in {dt:.2f}s (build {build_s:.1f}s) -> "
+        f"{per_step:.2f} s/step")
+    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"one decode step of layers {layers[0]}-{layers[-1]} ({len(layers)} of "
+                      f"{wl.n_layers}), all {wl.n_q_heads} query heads, route + attention, float64 "
+                      f"numpy on one thread; scaled by {wl.n_layers}/{len(layers)}",
+            "host_threads_available": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

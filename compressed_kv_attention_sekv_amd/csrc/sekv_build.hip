@@ -85,18 +85,22 @@ __global__ __launch_bounds__(kSegThreads) void segment_kernel(const float* __res
   auto anchor = [&](int t) -> bool { return t < limit && (double)s[t] > thr; };
 
   // anchors, run starts and run ends, each ascending
-  int na = 0, ns = 0;
+  // a run may start in one thread's chunk and end in another's, so starts
+  // and ends get separate offsets
+  int na = 0, ns = 0, ne = 0;
   for (int t = t0; t < t1; ++t) {
     if (t >= limit) break;
     const bool a = anchor(t);
     na += a;
     if (!a && (t == 0 || anchor(t - 1))) ns++;
+    if (!a && (t == limit - 1 || anchor(t + 1))) ne++;
   }
-  int tot_a, tot_s;
+  int tot_a, tot_s, tot_e;
   const int off_a = block_exclusive_scan<kSegThreads>(na, &tot_a, scan_lds);
   const int off_s = block_exclusive_scan<kSegThreads>(ns, &tot_s, scan_lds);
+  const int off_e = block_exclusive_scan<kSegThreads>(ne, &tot_e, scan_lds);
   {
-    int ia = off_a, is = off_s, ie = off_s;
+    int ia = off_a, is = off_s, ie = off_e;
     for (int t = t0; t < t1; ++t) {
       if (t >= limit) break;
       const bool a = anchor(t);

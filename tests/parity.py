@@ -176,7 +176,7 @@ def compare_route(rb, route: O.LayerRoute, tau: np.ndarray, wl) -> int:
     mask = mask[:, :sc]
     tie = np.abs(route.prob - tau[:, None].astype(np.float64)) < TIE_BAND
     assert np.array_equal(mask[~tie], route.mask[~tie])
-    if rb.prob is not None:
+    if rb.prob is not None and sc:
         gp = rb.prob.cpu().numpy()[:, :sc]
         assert np.max(np.abs(gp - route.prob)) <= 1e-12
     n_tie = int(tie.sum())
