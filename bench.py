@@ -8,9 +8,10 @@ bf16 K/V, spans of ~80 tokens, rank cap 32, window 512, 10% of heads zoom ~20%
 of spans and the rest ~1%), resident in HBM before timing starts.
 
 Prints ONE JSON line.  ``value`` is decode steps/s of the whole job.
-``roofline`` covers the attention launch of one layer (the dominant kernel):
-algorithmic bytes per launch / average launch time from HIP events recorded on
-the launch stream.  ``cpu_baseline`` times the CPU oracle on a bounded sample.
+``roofline`` covers the layer kernel (one launch per layer routes and attends;
+it is the step's only kernel): algorithmic bytes per launch / average launch
+time from HIP events recorded on the launch stream.  ``cpu_baseline`` times the
+CPU oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -149,11 +150,13 @@ def main():
     ws = torch.empty(cache.workspace_bytes(), dtype=torch.uint8, device=dev)
     side = torch.cuda.Stream() if args.tier == "host" else None
 
+    def layer_call(layer):
+        S.sekv_route_attn(cache, layer, q_cur[layer], p_c[layer], tau_c[layer], routes[layer],
+                          outs[layer], ws, fetch_stream=side)
+
     def step():
         for layer in range(L):
-            S.sekv_route(cache, layer, q_cur[layer], p_c[layer], tau_c[layer], routes[layer])
-            S.sekv_decode_attn(cache, layer, q_cur[layer], routes[layer], outs[layer], ws,
-                               fetch_stream=side)
+            layer_call(layer)
 
     graph = None
     if not args.no_graph and args.tier == "device":
@@ -202,7 +205,7 @@ def main():
     D = info.n_dense
     resident_layer = (Hkv * (2 * d * eb * D + 2 * d * eb * sc) + Hq * wl.route_dim * eb * sc +
                       Hq * (wl.route_dim * d + d + 1) * 4 + Hq * d * 4 + 4 * sc)
-    attn_resident_layer = Hkv * (2 * d * eb * D + 2 * d * eb * sc) + Hq * d * 4 * 2 + Hq * sc
+
     zoom_bytes = torch.zeros(args.steps, L, dtype=torch.float64, device=dev)
     zoom_frac = torch.zeros(L, Hq, dtype=torch.float64, device=dev)
     union_frac = torch.zeros(L, Hkv, dtype=torch.float64, device=dev)
@@ -211,7 +214,7 @@ def main():
         q_cur.copy_(qs[i])
         for layer in range(L):
             rb = routes[layer]
-            S.sekv_route(cache, layer, q_cur[layer], p_c[layer], tau_c[layer], rb)
+            layer_call(layer)
             valid = ar.unsqueeze(0) < rb.union_count.unsqueeze(1)               # [Hkv][Sc]
             ids = torch.where(valid, rb.union_list.long(), torch.zeros_like(rb.union_list.long()))
             zb = torch.gather(span_bytes[layer], 1, ids) * valid
@@ -223,7 +226,6 @@ def main():
     union_frac /= args.steps
     zb_step = zoom_bytes.sum(1)                       # [steps]
     bytes_step = float(zb_step.mean()) + L * resident_layer
-    attn_bytes_launch = float(zb_step.mean()) / L + attn_resident_layer
     step_gbs = bytes_step / (ms_per_step * 1e-3) / 1e9
     log(f"bytes/step {bytes_step / 1e9:.3f} GB (zoom {float(zb_step.mean()) / 1e9:.3f} GB): "
         f"{step_gbs:.0f} GB/s = {step_gbs / HBM_PEAK_GBS:.3f} of peak")
@@ -238,17 +240,15 @@ def main():
         i = args.warmup + m
         q_cur.copy_(qs[i])
         for layer in range(L):
-            S.sekv_route(cache, layer, q_cur[layer], p_c[layer], tau_c[layer], routes[layer])
             evs[m][layer][0].record()
-            S.sekv_decode_attn(cache, layer, q_cur[layer], routes[layer], outs[layer], ws,
-                               fetch_stream=side)
+            layer_call(layer)
             evs[m][layer][1].record()
     torch.cuda.synchronize()
     attn_us = [a.elapsed_time(b) * 1e3 for row in evs for (a, b) in row]
     attn_us_mean = float(np.mean(attn_us))
-    attn_bytes_meas = float(zoom_bytes[:n_meas].mean()) / L + attn_resident_layer
+    attn_bytes_meas = float(zoom_bytes[:n_meas].mean()) / L + resident_layer
     attn_gbs = attn_bytes_meas / (attn_us_mean * 1e-6) / 1e9
-    log(f"attention launch: {attn_us_mean:.2f} us avg, {attn_bytes_meas / 1e6:.2f} MB algorithmic "
+    log(f"layer launch: {attn_us_mean:.2f} us avg, {attn_bytes_meas / 1e6:.2f} MB algorithmic "
         f"-> {attn_gbs:.0f} GB/s")
 
     # ---- reference probes: device copy and pinned host->device copy ------------
@@ -315,7 +315,7 @@ def main():
             "unit": "GB/s",
             "frac": attn_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": "sekv_decode_attn (one layer)",
+            "kernel": "sekv::layer_kernel (sekv_route_attn, one layer: route + attention)",
             "algorithmic_bytes_per_launch": attn_bytes_meas,
             "avg_launch_us": attn_us_mean,
         },
@@ -335,9 +335,10 @@ def main():
 
 
 def cpu_baseline(wl, seed, s, spike, w, p, tau, qs, args, ranks):
-    """The oracle as it stands, on one core: build the oracle's cache for a
-    few layers (untimed), then time its decode (route + attention, every
-    query head) of those layers for one step and scale to a full step."""
+    """The oracle as it stands, on one thread: build the oracle's cache for a
+    few layers spread over the depth (untimed), then time its decode (route +
+    attention, every query head) of those layers over fresh step queries until
+    about 10 s of CPU work, and scale to a full step."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -345,7 +346,8 @@ def cpu_baseline(wl, seed, s, spike, w, p, tau, qs, args, ranks):
     import oracle as O
     import synth
 
-    layers = list(range(max(0, wl.n_layers - args.cpu_layers), wl.n_layers))
+    L = wl.n_layers
+    layers = sorted({0, L // 2, L - 1}) if args.cpu_layers >= 3 else list(range(args.cpu_layers))
     f64 = lambda t: t.detach().cpu().double().numpy()  # noqa: E731
     with threadpool_limits(limits=1):
         t0 = time.time()
@@ -362,21 +364,27 @@ def cpu_baseline(wl, seed, s, spike, w, p, tau, qs, args, ranks):
                              for kh in range(wl.n_kv_heads)}
             del kk, vv
         build_s = time.time() - t0
-        q = f64(qs[args.warmup])
-        t0 = time.time()
-        for layer in layers:
-            summ = {h: groups[layer][h // g].summary[h] for h in range(wl.n_q_heads)}
-            route = O.route_layer(q[layer], f64(p[layer]), f64(tau[layer]), summ, seg, wl.gamma,
-                                  wl.n_kv_heads)
-            O.decode_layer(q[layer], route, groups[layer], seg, n_kv_heads=wl.n_kv_heads)
-        dt = time.time() - t0
-    per_step = dt / len(layers) * wl.n_layers
-    log(f"cpu oracle: {len(layers)} layers decoded in {dt:.2f}s (build {build_s:.1f}s) -> "
-        f"{per_step:.2f} s/step")
+        pr = {layer: f64(p[layer]) for layer in layers}
+        ta = {layer: f64(tau[layer]) for layer in layers}
+        summ = {layer: {h: groups[layer][h // g].summary[h] for h in range(wl.n_q_heads)}
+                for layer in layers}
+        n_steps, dt = 0, 0.0
+        while dt < 10.0 and n_steps < min(40, qs.shape[0]):
+            q = f64(qs[n_steps])
+            t0 = time.time()
+            for layer in layers:
+                route = O.route_layer(q[layer], pr[layer], ta[layer], summ[layer], seg, wl.gamma,
+                                      wl.n_kv_heads)
+                O.decode_layer(q[layer], route, groups[layer], seg, n_kv_heads=wl.n_kv_heads)
+            dt += time.time() - t0
+            n_steps += 1
+    per_step = dt / (n_steps * len(layers)) * L
+    log(f"cpu oracle: layers {layers} x {n_steps} steps decoded in {dt:.2f}s (build {build_s:.1f}s) "
+        f"-> {per_step:.2f} s/step")
     return {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"one decode step of layers {layers[0]}-{layers[-1]} ({len(layers)} of "
-                      f"{wl.n_layers}), all {wl.n_q_heads} query heads, route + attention, float64 "
-                      f"numpy on one thread; scaled by {wl.n_layers}/{len(layers)}",
+            "sample": f"{n_steps} decode steps of layers {layers} ({len(layers)} of {L}), all "
+                      f"{wl.n_q_heads} query heads, route + attention, float64 numpy on one "
+                      f"thread ({dt:.1f} s); time per layer scaled by {L}",
             "host_threads_available": os.cpu_count()}
 
 

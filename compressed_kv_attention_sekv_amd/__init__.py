@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "SekvError", "SekvConfig", "SekvCacheInfo", "SekvRouteOut", "lib", "library_path",
     "make_config", "Cache", "RouteBuffers", "sekv_segment", "sekv_build_spans", "sekv_route",
-    "sekv_decode_attn", "sekv_decode_workspace_bytes", "EXPORTED_SYMBOLS",
+    "sekv_decode_attn", "sekv_route_attn", "sekv_decode_workspace_bytes", "EXPORTED_SYMBOLS",
     "SEKV_F32", "SEKV_BF16", "SEKV_TIER_DEVICE", "SEKV_TIER_HOST_PINNED",
 ]
 
@@ -29,7 +29,8 @@ SEKV_TIER_DEVICE, SEKV_TIER_HOST_PINNED = 0, 1
 EXPORTED_SYMBOLS = (
     "sekv_segment", "sekv_build_spans", "sekv_cache_info_get", "sekv_cache_copy_spans",
     "sekv_cache_copy_group", "sekv_cache_copy_factors", "sekv_route",
-    "sekv_decode_workspace_bytes", "sekv_decode_attn", "sekv_cache_destroy", "sekv_last_error",
+    "sekv_decode_workspace_bytes", "sekv_decode_attn", "sekv_route_attn", "sekv_cache_destroy",
+    "sekv_last_error",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -102,6 +103,8 @@ def lib() -> ctypes.CDLL:
         "sekv_route": (I32, [P, I32, P, P, P, ctypes.POINTER(SekvRouteOut), P]),
         "sekv_decode_workspace_bytes": (SZ, [P]),
         "sekv_decode_attn": (I32, [P, I32, P, ctypes.POINTER(SekvRouteOut), P, P, SZ, P, P]),
+        "sekv_route_attn": (I32, [P, I32, P, P, P, ctypes.POINTER(SekvRouteOut), P, P, SZ, P,
+                                  P]),
         "sekv_cache_destroy": (None, [P]),
         "sekv_last_error": (ctypes.c_char_p, []),
     }
@@ -305,3 +308,26 @@ def sekv_decode_attn(cache: Cache, layer: int, q: torch.Tensor, route: RouteBuff
     _check(lib().sekv_decode_attn(cache.handle, layer, _ptr(q), ctypes.byref(st), _ptr(o),
                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   _stream(stream), fst))
+
+
+def sekv_route_attn(cache: Cache, layer: int, q: torch.Tensor, proj: torch.Tensor,
+                    tau: torch.Tensor, route: RouteBuffers, o: torch.Tensor,
+                    workspace: torch.Tensor, stream=None, fetch_stream=None) -> None:
+    """Route and attend one layer in one call (one launch with device-tier factors)."""
+    _need(q, "q", torch.float32)
+    _need(proj, "proj", torch.float32)
+    _need(tau, "tau", torch.float32)
+    _need(o, "o", torch.float32)
+    _need(workspace, "workspace")
+    c = cache.cfg
+    if tuple(q.shape) != (c.n_q_heads, c.head_dim) or tuple(o.shape) != (c.n_q_heads, c.head_dim):
+        raise ValueError("q and o must be [Hq][d]")
+    if tuple(tau.shape) != (c.n_q_heads,) or \
+            tuple(proj.shape) != (c.n_q_heads, c.route_dim, c.head_dim):
+        raise ValueError("proj [Hq][dr][d] and tau [Hq] expected")
+    st = route.struct()
+    fst = None if fetch_stream is None else _stream(fetch_stream)
+    _check(lib().sekv_route_attn(cache.handle, layer, _ptr(q), _ptr(proj), _ptr(tau),
+                                 ctypes.byref(st), _ptr(o), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream),
+                                 fst))

@@ -41,16 +41,6 @@ sekv_status fail(sekv_status st, const char* fmt, ...) {
                   __FILE__, __LINE__);                                                        \
   } while (0)
 
-#define SEKV_ALLOC(ptr, bytes)                                                                \
-  do {                                                                                        \
-    size_t b_ = (bytes);                                                                      \
-    if (b_ == 0) b_ = 256;                                                                    \
-    hipError_t e_ = hipMalloc((void**)&(ptr), b_);                                            \
-    if (e_ != hipSuccess)                                                                     \
-      return fail(SEKV_ERR_NOMEM, "hipMalloc(%zu) for %s failed: %s", b_, #ptr,               \
-                  hipGetErrorString(e_));                                                     \
-  } while (0)
-
 sekv_status check_config(const sekv_config* c) {
   if (!c) return fail(SEKV_ERR_INVALID, "config is NULL");
   if (c->n_layers < 1) return fail(SEKV_ERR_INVALID, "n_layers must be >= 1");
@@ -74,12 +64,6 @@ sekv_status check_config(const sekv_config* c) {
     return fail(SEKV_ERR_INVALID, "factor_tier must be SEKV_TIER_DEVICE or SEKV_TIER_HOST_PINNED");
   return SEKV_OK;
 }
-
-struct DevFree {
-  void operator()(void* p) const {
-    if (p) (void)hipFree(p);
-  }
-};
 
 // device buffers owned by a scope; freed on every exit path
 struct Scratch {
@@ -154,10 +138,10 @@ struct sekv_cache {
   float* pool_host_dev = nullptr; // device view of pool_host
   float* stage = nullptr;         // host tier: device staging for one layer
   uint64_t stage_floats = 0;
-  // routing scratch
-  int32_t* route_scratch = nullptr;
+  // decode: per-KV-head tickets of the layer kernel (zero between launches)
   uint32_t* tickets = nullptr;
-  DecodeGeom geom{};
+  uint32_t* chunk_bits = nullptr;  // [Hkv][n_work][kListWords] zoom bit masks of each chunk
+  LayerGeom geom{};
   hipEvent_t ev_route = nullptr, ev_fetch = nullptr;
 
   ~sekv_cache() {
@@ -338,23 +322,12 @@ static sekv_status build_impl(const sekv_config* cfg, int32_t n_tokens, const fl
     if ((r = c->alloc(&c->stage, (size_t)stage_max * 4, "fetch staging"))) return r;
   }
 
-  // ---- decode geometry and routing scratch ----------------------------------
-  DecodeGeom& g = c->geom;
-  g.n_q_heads = Hq;
-  g.n_kv_heads = Hkv;
-  g.group = c->group;
-  g.route_dim = dr;
-  g.n_dense = D;
-  g.n_compressed = sc;
-  g.dense_tiles = (D + 255) / 256;
-  g.coarse_tiles = (sc + 255) / 256;
-  g.zoom_slots = sc ? 64 : 0;
-  g.n_slots = g.dense_tiles + g.coarse_tiles + g.zoom_slots;
-  const int nchunks = (sc + 255) / 256;
-  const size_t scr_ints = (size_t)Hkv * (c->group + 1) * ((size_t)nchunks * 256 + nchunks);
-  if ((r = c->alloc(&c->route_scratch, scr_ints * 4, "route scratch"))) return r;
-  if ((r = c->alloc(&c->tickets, (size_t)Hkv * 4, "route tickets"))) return r;
+  // ---- decode geometry, tickets and chunk bit masks ---------------------------
+  c->geom = make_layer_geom(Hq, Hkv, dr, D, sc);
+  if ((r = c->alloc(&c->tickets, (size_t)Hkv * 4, "layer tickets"))) return r;
   SEKV_HIP(hipMemsetAsync(c->tickets, 0, (size_t)Hkv * 4, st));
+  if ((r = c->alloc(&c->chunk_bits, (size_t)Hkv * c->geom.n_work * kListWords * 4, "chunk bits")))
+    return r;
   SEKV_HIP(hipEventCreateWithFlags(&c->ev_route, hipEventDisableTiming));
   SEKV_HIP(hipEventCreateWithFlags(&c->ev_fetch, hipEventDisableTiming));
   SEKV_HIP(hipStreamSynchronize(st));
@@ -466,89 +439,160 @@ sekv_status sekv_cache_copy_factors(const sekv_cache* c, int32_t layer, int32_t 
     std::memcpy(blk.data(), src, blk.size() * 4);
   if (u)
     for (int t = 0; t < n; ++t)
-      for (int i = 0; i < r; ++i) u[(size_t)t * r + i] = blk[fv.u(kv) + (size_t)i * fv.n4 + t];
+      for (int i = 0; i < r; ++i) u[(size_t)t * r + i] = blk[fv.u(kv) + (size_t)t * fv.r4 + i];
   if (sigma)
     for (int i = 0; i < r; ++i) sigma[i] = blk[fv.sigma(kv) + i];
   if (vt) std::memcpy(vt, blk.data() + fv.vt(kv), (size_t)r * kHeadDim * 4);
   return SEKV_OK;
 }
 
-sekv_status sekv_route(const sekv_cache* c, int32_t layer, const float* q_dev,
-                       const float* proj_dev, const float* tau_dev, const sekv_route_out* out,
-                       hipStream_t stream) {
+namespace {
+
+sekv_status check_layer_call(const sekv_cache* c, int32_t layer) {
   if (!c) return fail(SEKV_ERR_INVALID, "cache is NULL");
   if (layer < 0 || layer >= c->cfg.n_layers)
     return fail(SEKV_ERR_INVALID, "layer %d out of range [0, %d)", layer, c->cfg.n_layers);
-  if (!q_dev || !proj_dev || !tau_dev || !out)
-    return fail(SEKV_ERR_INVALID, "q, proj, tau and out must be non-NULL");
+  return SEKV_OK;
+}
+
+sekv_status check_route_out(const sekv_route_out* out) {
+  if (!out) return fail(SEKV_ERR_INVALID, "route output is NULL");
   if (!out->mask || !out->list || !out->count || !out->union_list || !out->union_count)
     return fail(SEKV_ERR_INVALID, "route output buffers must be non-NULL (prob may be NULL)");
-  const int Hq = c->cfg.n_q_heads, Hkv = c->cfg.n_kv_heads;
+  return SEKV_OK;
+}
+
+// layer slices of the cache, in the layout the layer kernel reads
+LayerArgs layer_args(const sekv_cache* c, int32_t layer, const float* q, const float* proj,
+                     const float* tau, const sekv_route_out* ro, float* o, void* ws) {
+  const int Hq = c->cfg.n_q_heads, Hkv = c->cfg.n_kv_heads, sc = c->sc, D = c->n_dense;
+  const size_t eb = c->kv_elem();
+  const size_t lg0 = (size_t)layer * Hkv;
+  const bool host_tier = c->cfg.factor_tier == SEKV_TIER_HOST_PINNED;
+  LayerArgs a{};
+  a.q = q;
+  a.proj = proj;
+  a.tau = tau;
+  a.summ = (const char*)c->summ + (size_t)layer * Hq * sc * c->cfg.route_dim * eb;
+  a.lnn64 = c->lnn64;
+  a.lnn32 = c->lnn32;
+  a.gamma = c->cfg.gamma;
+  a.dense_k = (const char*)c->dense_k + lg0 * D * kHeadDim * eb;
+  a.dense_v = (const char*)c->dense_v + lg0 * D * kHeadDim * eb;
+  a.kbar = (const char*)c->kbar + lg0 * sc * kHeadDim * eb;
+  a.vbar = (const char*)c->vbar + lg0 * sc * kHeadDim * eb;
+  a.clen = c->clen;
+  a.rank = c->rank + lg0 * sc;
+  a.fac_off = c->fac_off + lg0 * sc;
+  a.pool = host_tier ? c->stage : c->pool_dev;
+  a.off_base = host_tier ? c->layer_base[layer] : 0;
+  if (ro) {
+    a.mask = ro->mask;
+    a.prob = ro->prob;
+    a.list = ro->list;
+    a.count = ro->count;
+    a.ulist = ro->union_list;
+    a.ucount = ro->union_count;
+  }
+  a.o = o;
+  a.part = (float*)ws;
+  a.tickets = c->tickets;
+  a.chunk_bits = c->chunk_bits;
+  return a;
+}
+
+}  // namespace
+
+sekv_status sekv_route(const sekv_cache* c, int32_t layer, const float* q_dev,
+                       const float* proj_dev, const float* tau_dev, const sekv_route_out* out,
+                       hipStream_t stream) {
+  sekv_status r;
+  if ((r = check_layer_call(c, layer))) return r;
+  if (!q_dev || !proj_dev || !tau_dev)
+    return fail(SEKV_ERR_INVALID, "q, proj and tau must be non-NULL");
+  if ((r = check_route_out(out))) return r;
   if (c->sc == 0) {
-    SEKV_HIP(hipMemsetAsync(out->count, 0, (size_t)Hq * 4, stream));
-    SEKV_HIP(hipMemsetAsync(out->union_count, 0, (size_t)Hkv * 4, stream));
+    SEKV_HIP(launch_fill_i32(out->count, c->cfg.n_q_heads, 0, stream));
+    SEKV_HIP(launch_fill_i32(out->union_count, c->cfg.n_kv_heads, 0, stream));
     return SEKV_OK;
   }
-  const size_t eb = c->kv_elem();
-  const void* summ = (const char*)c->summ + (size_t)layer * Hq * c->sc * c->cfg.route_dim * eb;
-  SEKV_HIP(launch_route(c->bf16(), c->geom, q_dev, proj_dev, tau_dev, summ, c->lnn64,
-                        c->cfg.gamma, out->mask, out->prob, out->list, out->count,
-                        out->union_list, out->union_count, c->route_scratch, c->tickets, stream));
+  const LayerArgs a = layer_args(c, layer, q_dev, proj_dev, tau_dev, out, nullptr, nullptr);
+  SEKV_HIP(launch_layer(c->bf16(), kRoute | kLists, c->geom, a, stream));
   return SEKV_OK;
 }
 
 size_t sekv_decode_workspace_bytes(const sekv_cache* c) {
   if (!c) return 0;
-  const size_t b = (size_t)c->cfg.n_q_heads * c->geom.n_slots * 132 * 4;
+  const size_t b =
+      (size_t)c->cfg.n_kv_heads * c->geom.n_slots() * c->group * kPartStride * sizeof(float);
   return (b + 255) & ~(size_t)255;
+}
+
+static sekv_status attn_impl(const sekv_cache* c, int32_t layer, const float* q_dev,
+                             const sekv_route_out* route, float* o_dev, void* ws_dev,
+                             hipStream_t stream, hipStream_t fetch_stream) {
+  const LayerArgs a = layer_args(c, layer, q_dev, nullptr, nullptr, route, o_dev, ws_dev);
+  const int sc = c->sc;
+  if (c->cfg.factor_tier == SEKV_TIER_DEVICE || sc == 0) {
+    SEKV_HIP(launch_layer(c->bf16(), kDense | kZoom | kMerge, c->geom, a, stream));
+    return SEKV_OK;
+  }
+  // host tier: the zoomed spans' factors are gathered into device staging on
+  // the fetch stream while full-resolution rows and coarse entries are
+  // attended on `stream`; the zoomed spans and the merge follow the fetch
+  const size_t lg0 = (size_t)layer * c->cfg.n_kv_heads;
+  hipStream_t fst = fetch_stream ? fetch_stream : stream;
+  if (fst != stream) {
+    SEKV_HIP(hipEventRecord(c->ev_route, stream));
+    SEKV_HIP(hipStreamWaitEvent(fst, c->ev_route, 0));
+  }
+  SEKV_HIP(launch_fetch_gather(c->geom, route->union_list, route->union_count, c->clen,
+                               c->rank + lg0 * sc, c->fac_off + lg0 * sc, c->layer_base[layer],
+                               c->pool_host_dev, c->stage, fst));
+  if (fst != stream) SEKV_HIP(hipEventRecord(c->ev_fetch, fst));
+  SEKV_HIP(launch_layer(c->bf16(), kDense, c->geom, a, stream));
+  if (fst != stream) SEKV_HIP(hipStreamWaitEvent(stream, c->ev_fetch, 0));
+  SEKV_HIP(launch_layer(c->bf16(), kZoom | kZoomSplit | kMerge, c->geom, a, stream));
+  return SEKV_OK;
+}
+
+static sekv_status check_workspace(const sekv_cache* c, const void* ws_dev, size_t ws_bytes) {
+  if (!ws_dev) return fail(SEKV_ERR_INVALID, "workspace is NULL");
+  if (ws_bytes < sekv_decode_workspace_bytes(c))
+    return fail(SEKV_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
+                sekv_decode_workspace_bytes(c));
+  return SEKV_OK;
 }
 
 sekv_status sekv_decode_attn(const sekv_cache* c, int32_t layer, const float* q_dev,
                              const sekv_route_out* route, float* o_dev, void* ws_dev,
                              size_t ws_bytes, hipStream_t stream, hipStream_t fetch_stream) {
-  if (!c) return fail(SEKV_ERR_INVALID, "cache is NULL");
-  if (layer < 0 || layer >= c->cfg.n_layers)
-    return fail(SEKV_ERR_INVALID, "layer %d out of range [0, %d)", layer, c->cfg.n_layers);
-  if (!q_dev || !route || !o_dev || !ws_dev)
-    return fail(SEKV_ERR_INVALID, "q, route, o and workspace must be non-NULL");
+  sekv_status r;
+  if ((r = check_layer_call(c, layer))) return r;
+  if (!q_dev || !route || !o_dev)
+    return fail(SEKV_ERR_INVALID, "q, route and o must be non-NULL");
   if (!route->mask || !route->union_list || !route->union_count)
     return fail(SEKV_ERR_INVALID, "route mask and union lists must be non-NULL");
-  if (ws_bytes < sekv_decode_workspace_bytes(c))
-    return fail(SEKV_ERR_INVALID, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes,
-                sekv_decode_workspace_bytes(c));
-  const DecodeGeom& g = c->geom;
-  const int Hkv = c->cfg.n_kv_heads, sc = c->sc, D = c->n_dense;
-  const size_t eb = c->kv_elem();
-  const size_t lg0 = (size_t)layer * Hkv;
-  float* part = (float*)ws_dev;
-  const void* dk = (const char*)c->dense_k + lg0 * D * kHeadDim * eb;
-  const void* dv = (const char*)c->dense_v + lg0 * D * kHeadDim * eb;
-  const void* kb = (const char*)c->kbar + lg0 * sc * kHeadDim * eb;
-  const void* vb = (const char*)c->vbar + lg0 * sc * kHeadDim * eb;
-  const int32_t* rk = c->rank + lg0 * sc;
-  const uint64_t* fo = c->fac_off + lg0 * sc;
-  const bool host_tier = c->cfg.factor_tier == SEKV_TIER_HOST_PINNED;
-  hipStream_t fst = fetch_stream ? fetch_stream : stream;
-  if (host_tier && sc) {
-    // the fetch waits for this layer's router (queued earlier on `stream`)
-    if (fst != stream) {
-      SEKV_HIP(hipEventRecord(c->ev_route, stream));
-      SEKV_HIP(hipStreamWaitEvent(fst, c->ev_route, 0));
-    }
-    SEKV_HIP(launch_fetch_gather(g, route->union_list, route->union_count, c->clen, rk, fo,
-                                 c->layer_base[layer], c->pool_host_dev, c->stage, fst));
-    if (fst != stream) SEKV_HIP(hipEventRecord(c->ev_fetch, fst));
+  if ((r = check_workspace(c, ws_dev, ws_bytes))) return r;
+  return attn_impl(c, layer, q_dev, route, o_dev, ws_dev, stream, fetch_stream);
+}
+
+sekv_status sekv_route_attn(const sekv_cache* c, int32_t layer, const float* q_dev,
+                            const float* proj_dev, const float* tau_dev,
+                            const sekv_route_out* route, float* o_dev, void* ws_dev,
+                            size_t ws_bytes, hipStream_t stream, hipStream_t fetch_stream) {
+  sekv_status r;
+  if ((r = check_layer_call(c, layer))) return r;
+  if (!q_dev || !proj_dev || !tau_dev || !o_dev)
+    return fail(SEKV_ERR_INVALID, "q, proj, tau and o must be non-NULL");
+  if ((r = check_route_out(route))) return r;
+  if ((r = check_workspace(c, ws_dev, ws_bytes))) return r;
+  if (c->cfg.factor_tier == SEKV_TIER_HOST_PINNED || c->sc == 0) {
+    if ((r = sekv_route(c, layer, q_dev, proj_dev, tau_dev, route, stream))) return r;
+    return attn_impl(c, layer, q_dev, route, o_dev, ws_dev, stream, fetch_stream);
   }
-  SEKV_HIP(launch_attn_tiles(c->bf16(), g, q_dev, dk, dv, kb, vb, c->lnn32, route->mask, part,
-                             stream));
-  if (sc) {
-    if (host_tier && fst != stream) SEKV_HIP(hipStreamWaitEvent(stream, c->ev_fetch, 0));
-    const float* pool = host_tier ? c->stage : c->pool_dev;
-    const uint64_t base = host_tier ? c->layer_base[layer] : 0;
-    SEKV_HIP(launch_attn_zoom(g, q_dev, route->mask, route->union_list, route->union_count,
-                              c->clen, rk, fo, pool, base, part, stream));
-  }
-  SEKV_HIP(launch_attn_merge(g, part, o_dev, stream));
+  const LayerArgs a = layer_args(c, layer, q_dev, proj_dev, tau_dev, route, o_dev, ws_dev);
+  SEKV_HIP(launch_layer(c->bf16(), kRoute | kDense | kZoom | kMerge | kLists, c->geom, a, stream));
   return SEKV_OK;
 }
 

@@ -492,10 +492,10 @@ __global__ __launch_bounds__(kSvdThreads) void span_svd_kernel(
     sg[i] = (i < r && live(i)) ? (float)sqrt(nrm[order[i]]) : 0.f;
   if (small) {
     // u_i = A[:,p] / lambda (token space); v_i = X^T u_i / sigma
-    for (int idx = tid; idx < r * fv.n4; idx += kSvdThreads) {
-      const int i = idx / fv.n4, t = idx % fv.n4;
+    for (int idx = tid; idx < n * fv.r4; idx += kSvdThreads) {
+      const int t = idx / fv.r4, i = idx % fv.r4;
       float val = 0.f;
-      if (t < n && live(i)) val = (float)(A[(size_t)order[i] * ld + t] / nrm[order[i]]);
+      if (i < r && live(i)) val = (float)(A[(size_t)order[i] * ld + t] / nrm[order[i]]);
       u[idx] = val;
     }
     for (int idx = tid; idx < r * kHeadDim; idx += kSvdThreads) {
@@ -518,10 +518,10 @@ __global__ __launch_bounds__(kSvdThreads) void span_svd_kernel(
       if (live(i)) val = (float)(A[(size_t)order[i] * ld + c] / nrm[order[i]]);
       vt[idx] = val;
     }
-    for (int idx = tid; idx < r * fv.n4; idx += kSvdThreads) {
-      const int i = idx / fv.n4, t = idx % fv.n4;
+    for (int idx = tid; idx < n * fv.r4; idx += kSvdThreads) {
+      const int t = idx / fv.r4, i = idx % fv.r4;
       float val = 0.f;
-      if (t < n && live(i)) {
+      if (i < r && live(i)) {
         const double lam = nrm[order[i]];
         const double* ac = A + (size_t)order[i] * ld;
         const T* xr = X + (size_t)t * kHeadDim;

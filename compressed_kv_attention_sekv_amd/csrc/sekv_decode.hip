@@ -1,10 +1,27 @@
-// Decode-step kernels of the SeKV cache (gfx950): router with ordered
-// compaction, split-K attention over full-resolution rows and coarse span
-// entries, factored attention over zoomed spans, and the log-sum-exp merge.
+// Decode-step kernel of the SeKV cache (gfx950): one launch per layer routes
+// every compressed span, attends over the four sources of the mixed-resolution
+// memory and merges the partial softmax states.
 //
-// SeKV paper Sec. 3.2 (gate) and Sec. 3.3 (Eq. 9 zoom decision; one softmax
-// over anchors, window, reconstructed zoomed tokens and coarse entries with a
-// length correction).
+// SeKV paper Sec. 3.2 (query projected into the routing space; independent
+// sigmoid gate with a gamma ln n size prior) and Sec. 3.3 (Eq. 9 zoom decision
+// per head; one softmax over anchors, window, tokens of zoomed spans rebuilt
+// from their low-rank factors (Eq. 8 with hard gates), and one coarse entry per
+// other span whose scaled score gets + ln n_j).
+//
+// Work split, per KV head g: n_work workgroups of 4 waves.  Workgroup w
+//   - projects the group's queries into routing space (float64), gates the
+//     compressed spans [32 w, 32 w + 32) and writes their zoom mask;
+//   - streams its slice of the full-resolution rows (window, anchors,
+//     short-span tokens) with 16-byte loads shared by the G query heads;
+//   - attends the coarse entries of its spans that a head did not zoom;
+//   - attends each zoomed span straight from its factors, one wave per span:
+//       b_h = sigma_K * (V_K^T q_h) / sqrt(d);  e_{h,t} = U_K[t] . b_h;
+//       c_h = U_V^T p_h;  acc_h += V_V^T (sigma_V * c_h)
+//     so the factors are read once for all heads and no token row is formed.
+// Each workgroup writes one partial (m, l, acc) per head.  The last one of a
+// KV head to finish (an atomic ticket, reset by that workgroup) merges them
+// into o and writes the ascending zoom lists from per-chunk bit masks.  No
+// workgroup ever waits on another, and every launch leaves the tickets at zero.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -12,136 +29,64 @@
 
 namespace sekv {
 
-constexpr int kPartStride = 132;  // per (head, slot): m, l, -, -, acc[128]
-constexpr int kTileRows = 256;    // rows (or coarse entries) per attention tile
-
 // ---------------------------------------------------------------------------
-// Router.  Grid (chunks of 256 spans, KV heads); each workgroup projects the
-// queries of its group's heads (float64), gates its chunk of spans, and
-// compacts each head's zoom set and the group union in chunk order into
-// scratch.  The last workgroup of a group to finish (ticket counter) copies
-// the chunk lists into the ascending output lists and resets the ticket, so
-// no launch leaves state behind and no workgroup ever waits.
+// small helpers
 // ---------------------------------------------------------------------------
-constexpr int kRouteChunk = 256;
+// Cross-lane moves inside a row of 16 lanes go through DPP (an ALU operand
+// modifier); only moves between rows use the LDS permute unit.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)__double2loint(x), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)__double2hiint(x), CTRL, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within 8
+constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within 16
+constexpr int kDppRor8 = 0x128;       // lane i <- (i + 8) mod 16 (= i xor 8)
 
-template <typename T>
-__global__ __launch_bounds__(kRouteChunk) void route_kernel(
-    const float* __restrict__ q, const float* __restrict__ proj, const float* __restrict__ tau,
-    const T* __restrict__ summ, const double* __restrict__ lnn64, double gamma, int sc,
-    int group, int dr, int nchunks, uint8_t* __restrict__ mask, double* __restrict__ prob,
-    int32_t* __restrict__ list, int32_t* __restrict__ count, int32_t* __restrict__ ulist,
-    int32_t* __restrict__ ucount, int32_t* __restrict__ scratch, uint32_t* __restrict__ tickets) {
-  __shared__ double qt[kMaxGroup * kMaxRouteDim];
-  __shared__ int wcnt[kMaxGroup + 1][kRouteChunk / 64];
-  __shared__ int sh_last;
-  const int c = blockIdx.x, g = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int nl = group + 1;  // lists per group: heads, then the union
-  int32_t* scr_list = scratch + (size_t)g * nl * (nchunks * kRouteChunk + nchunks);
-  int32_t* scr_cnt = scr_list + (size_t)nl * nchunks * kRouteChunk;
-
-  for (int o = wid; o < group * dr; o += kRouteChunk / 64) {
-    const int hl = o / dr, i = o % dr, h = g * group + hl;
-    const float* pr = proj + ((size_t)h * dr + i) * kHeadDim;
-    const float* qr = q + (size_t)h * kHeadDim;
-    double a = (double)pr[lane] * (double)qr[lane] + (double)pr[lane + 64] * (double)qr[lane + 64];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) a += __shfl_xor(a, off, 64);
-    if (lane == 0) qt[hl * dr + i] = a;
-  }
-  __syncthreads();
-
-  const int j = c * kRouteChunk + tid;
-  unsigned bits = 0;
-  if (j < sc) {
-    const double prior = gamma * lnn64[j];
-    for (int hl = 0; hl < group; ++hl) {
-      const int h = g * group + hl;
-      const T* sr = summ + ((size_t)h * sc + j) * dr;
-      double x = 0.0;
-      for (int i = 0; i < dr; ++i) x += qt[hl * dr + i] * (double)Store<T>::load(sr + i);
-      x += prior;
-      const double p = 1.0 / (1.0 + exp(-x));
-      const bool z = p > (double)tau[h];
-      bits |= (unsigned)z << hl;
-      mask[(size_t)h * sc + j] = (uint8_t)z;
-      if (prob) prob[(size_t)h * sc + j] = p;
-    }
-  }
-  for (int li = 0; li < nl; ++li) {
-    const bool z = (j < sc) && (li < group ? ((bits >> li) & 1u) != 0 : bits != 0);
-    const unsigned long long bal = __ballot(z);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wcnt[li][wid] = __popcll(bal);
-    __syncthreads();
-    int base = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kRouteChunk / 64; ++w) {
-      base += (w < wid) ? wcnt[li][w] : 0;
-      total += wcnt[li][w];
-    }
-    if (z) scr_list[((size_t)li * nchunks + c) * kRouteChunk + base + before] = j;
-    if (tid == 0) scr_cnt[c * nl + li] = total;
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev =
-        __hip_atomic_fetch_add(&tickets[g], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    sh_last = (prev == (unsigned)(nchunks - 1));
-  }
-  __syncthreads();
-  if (!sh_last) return;
-  __threadfence();
-  for (int li = 0; li < nl; ++li) {
-    int32_t* dst = li < group ? list + (size_t)(g * group + li) * sc : ulist + (size_t)g * sc;
-    int base = 0;
-    for (int cc = 0; cc < nchunks; ++cc) {
-      const int cnt = __hip_atomic_load(&scr_cnt[cc * nl + li], __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-      const int32_t* src = scr_list + ((size_t)li * nchunks + cc) * kRouteChunk;
-      for (int k = tid; k < cnt; k += kRouteChunk) dst[base + k] = src[k];
-      base += cnt;
-    }
-    if (tid == 0) {
-      if (li < group) count[g * group + li] = base;
-      else ucount[g] = base;
-    }
-  }
-  if (tid == 0) __hip_atomic_store(&tickets[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// sum over aligned groups of N lanes (N = 4, 8, 16, 32, 64); every lane of a
+// group receives the group's total
+template <int N, typename F>
+__device__ __forceinline__ F group_sum(F x) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  if (N >= 8) x += dpp<kDppHalfMirror>(x);
+  if (N >= 16) x += dpp<kDppMirror>(x);
+  if (N >= 32) x += __shfl_xor(x, 16, 64);
+  if (N >= 64) x += __shfl_xor(x, 32, 64);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppMirror>(x));
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
+// weights of two online-softmax states under their common max; -inf = empty
+__device__ __forceinline__ float merge_w(float m1, float m2, float& w1, float& w2) {
+  const float M = fmaxf(m1, m2);
+  w1 = (m1 == -INFINITY) ? 0.f : __expf(m1 - M);
+  w2 = (m2 == -INFINITY) ? 0.f : __expf(m2 - M);
+  return M;
 }
 
-hipError_t launch_route(int bf16, const DecodeGeom& g, const float* q, const float* proj,
-                        const float* tau, const void* summ, const double* lnn64, double gamma,
-                        uint8_t* mask, double* prob, int32_t* list, int32_t* count,
-                        int32_t* ulist, int32_t* ucount, int32_t* scratch, uint32_t* tickets,
-                        hipStream_t st) {
-  const int nchunks = (g.n_compressed + kRouteChunk - 1) / kRouteChunk;
-  if (nchunks == 0) return hipSuccess;
-  dim3 grid(nchunks, g.n_kv_heads);
-  if (bf16)
-    hipLaunchKernelGGL(route_kernel<uint16_t>, grid, dim3(kRouteChunk), 0, st, q, proj, tau,
-                       (const uint16_t*)summ, lnn64, gamma, g.n_compressed, g.group, g.route_dim,
-                       nchunks, mask, prob, list, count, ulist, ucount, scratch, tickets);
-  else
-    hipLaunchKernelGGL(route_kernel<float>, grid, dim3(kRouteChunk), 0, st, q, proj, tau,
-                       (const float*)summ, lnn64, gamma, g.n_compressed, g.group, g.route_dim,
-                       nchunks, mask, prob, list, count, ulist, ucount, scratch, tickets);
-  return hipGetLastError();
-}
+template <typename T> struct Lanes {
+  static constexpr int EPL = 16 / sizeof(T);        // elements per 16-byte lane load
+  static constexpr int LPR = kHeadDim / EPL;        // lanes per row
+  static constexpr int RPW = 64 / LPR;              // rows per wave load
+};
 
-// ---------------------------------------------------------------------------
-// Full-resolution rows and coarse entries.  Grid (tiles, KV heads).  Each
-// 16-byte lane load carries EPL elements of one row; LPR lanes cover a row,
-// so one wave instruction reads RPW whole rows (1 KB, coalesced).  All G query
-// heads of the group share every K/V load.  Each row slot keeps its own
-// online-softmax state; slots are combined through LDS at the end.
-// ---------------------------------------------------------------------------
-template <typename T>
-__device__ __forceinline__ void unpack16(const uint4& raw, float* out);
-template <>
-__device__ __forceinline__ void unpack16<uint16_t>(const uint4& raw, float* out) {
+__device__ __forceinline__ void unpack16(const uint4& raw, float* out, uint16_t) {
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -149,448 +94,1014 @@ __device__ __forceinline__ void unpack16<uint16_t>(const uint4& raw, float* out)
     out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
   }
 }
-template <>
-__device__ __forceinline__ void unpack16<float>(const uint4& raw, float* out) {
+__device__ __forceinline__ void unpack16(const uint4& raw, float* out, float) {
   out[0] = __uint_as_float(raw.x);
   out[1] = __uint_as_float(raw.y);
   out[2] = __uint_as_float(raw.z);
   out[3] = __uint_as_float(raw.w);
 }
 
+// ---------------------------------------------------------------------------
+// shared memory of the layer kernel
+// ---------------------------------------------------------------------------
+template <int G>
+struct alignas(16) WaveScratch {
+  union {
+    struct {                       // one zoomed span at a time
+      float bsh[G][kMaxRank];      // b_h
+      float csh[G][kMaxRank];      // c_h
+      float psh[64][G];            // p of the current 64 tokens
+    } z;
+    struct {                       // the wave's zoomed-span state, once its spans are done
+      float acc[G][kHeadDim];
+      float m[G];
+      float l[G];
+    } st;
+  };
+};
+
+template <int G>
+struct alignas(16) Smem {
+  float qs[G][kHeadDim];           // query * 1/sqrt(d)
+  float qu[G][kHeadDim];           // query as given (routing)
+  double qt[G][kMaxRouteDim];      // P_h q_h
+  uint64_t m_off[kChunk];          // factor block of span j0 + i, relative to the pool
+  int m_n[kChunk], m_r[kChunk];    // its length and retained rank
+  int bits[kChunk];                // heads of the group that zoom span j0 + i
+  int zl[kChunk];                  // chunk-local ids of zoomed spans
+  int nz;
+  int last;
+  int wc[kListWords][kWaves];      // list compaction: per-wave counts
+  float rows_acc[kWaves][G][kHeadDim];   // each wave's state over rows and coarse entries
+  float rows_m[kWaves][G], rows_l[kWaves][G];
+  WaveScratch<G> w[kWaves];
+};
+
+// ---------------------------------------------------------------------------
+// Rows of K/V (full-resolution rows, or a chunk's coarse entries), one wave:
+// LOADS wave-wide 16-byte loads of K and of V, RPW rows each.  Each row slot
+// (LPR lanes) keeps its own online state across calls; rows_finish combines
+// the slots, after which every lane holds the wave's state for its EPL dims.
+// ---------------------------------------------------------------------------
 template <typename T, int G>
-__global__ __launch_bounds__(256) void attn_tiles_kernel(
-    const float* __restrict__ q, const T* __restrict__ dense_k, const T* __restrict__ dense_v,
-    const T* __restrict__ kbar, const T* __restrict__ vbar, const float* __restrict__ lnn32,
-    const uint8_t* __restrict__ mask, int n_dense, int sc, int dense_tiles, int n_slots,
-    float* __restrict__ part) {
-  constexpr int EPL = 16 / sizeof(T);
-  constexpr int LPR = kHeadDim / EPL;
-  constexpr int RPW = 64 / LPR;
-  constexpr int UNR = 4;
-  constexpr int NSLOT = 4 * RPW;
-  __shared__ float red[G][NSLOT][kPartStride];
-
-  const int tile = blockIdx.x, g = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int sub = lane / LPR, sl = lane % LPR;
-  const bool coarse = tile >= dense_tiles;
-  int r0, r1;
-  const T* K;
-  const T* V;
-  if (!coarse) {
-    r0 = tile * kTileRows;
-    r1 = min(n_dense, r0 + kTileRows);
-    K = dense_k + (size_t)g * n_dense * kHeadDim;
-    V = dense_v + (size_t)g * n_dense * kHeadDim;
-  } else {
-    r0 = (tile - dense_tiles) * kTileRows;
-    r1 = min(sc, r0 + kTileRows);
-    K = kbar + (size_t)g * sc * kHeadDim;
-    V = vbar + (size_t)g * sc * kHeadDim;
-  }
-  const float scale = rsqrtf((float)kHeadDim);
-  float qv[G][EPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qv[h][e] = q[(size_t)(g * G + h) * kHeadDim + sl * EPL + e] * scale;
-  float m[G], l[G], acc[G][EPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  }
-
-  for (int base = r0 + wid * RPW; base < r1; base += 4 * RPW * UNR) {
-    uint4 kr[UNR], vr[UNR];
-    int row[UNR];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      row[u] = base + u * 4 * RPW + sub;
-      const int rr = row[u] < r1 ? row[u] : r0;
-      kr[u] = *(const uint4*)(K + (size_t)rr * kHeadDim + sl * EPL);
-      vr[u] = *(const uint4*)(V + (size_t)rr * kHeadDim + sl * EPL);
-    }
-    float s[UNR][G];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      float kf[EPL];
-      unpack16<T>(kr[u], kf);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) d += qv[h][e] * kf[e];
-#pragma unroll
-        for (int o = 1; o < LPR; o <<= 1) d += __shfl_xor(d, o, 64);
-        s[u][h] = d;
-      }
-      const bool valid = row[u] < r1;
-      float bias = 0.f;
-      if (coarse && valid) bias = lnn32[row[u]];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        bool keep = valid;
-        if (coarse && valid) keep = mask[(size_t)(g * G + h) * sc + row[u]] == 0;
-        s[u][h] = keep ? s[u][h] + bias : -INFINITY;
-      }
-    }
+struct RowState {
+  float m[G], l[G], acc[G][Lanes<T>::EPL];
+  __device__ void init() {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float bm = s[0][h];
+      m[h] = -INFINITY;
+      l[h] = 0.f;
 #pragma unroll
-      for (int u = 1; u < UNR; ++u) bm = fmaxf(bm, s[u][h]);
-      const float mn = fmaxf(m[h], bm);
-      if (mn == -INFINITY) continue;
-      const float corr = __expf(m[h] - mn);
-      l[h] *= corr;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= corr;
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const float p = __expf(s[u][h] - mn);
-        float vf[EPL];
-        unpack16<T>(vr[u], vf);
-        l[h] += p;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] += p * vf[e];
-      }
-      m[h] = mn;
+      for (int e = 0; e < Lanes<T>::EPL; ++e) acc[h][e] = 0.f;
     }
   }
+};
 
-  const int slot = wid * RPW + sub;
+template <typename T, int LOADS>
+__device__ __forceinline__ void rows_load(const T* __restrict__ K, const T* __restrict__ V, int r0,
+                                          int r1, uint4 (&kr)[LOADS], uint4 (&vr)[LOADS]) {
+  using Ln = Lanes<T>;
+  const int lane = threadIdx.x & 63, sub = lane / Ln::LPR, sl = lane % Ln::LPR;
+  if (r1 > r0) {
+    // rows past the range load row r1 - 1 (always valid) and are masked later
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int row = min(r0 + u * Ln::RPW + sub, r1 - 1);
+      kr[u] = *(const uint4*)(K + (size_t)row * kHeadDim + sl * Ln::EPL);
+      vr[u] = *(const uint4*)(V + (size_t)row * kHeadDim + sl * Ln::EPL);
+    }
+  } else {   // nothing for this wave (uniform)
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      kr[u] = make_uint4(0, 0, 0, 0);
+      vr[u] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// Coarse entries add lnn[row - bias0] to their scaled score and are skipped by
+// the heads whose bit is set in skip[row - bias0]; full-resolution rows pass
+// lnn = NULL.
+template <typename T, int G, int LOADS>
+__device__ __forceinline__ void rows_accumulate(const uint4 (&kr)[LOADS], const uint4 (&vr)[LOADS],
+                                                int r0, int r1, const float (*qs)[kHeadDim],
+                                                const float* lnn, const int* skip, int bias0,
+                                                RowState<T, G>& s) {
+  using Ln = Lanes<T>;
+  constexpr int EPL = Ln::EPL;
+  const int lane = threadIdx.x & 63, sub = lane / Ln::LPR, sl = lane % Ln::LPR;
+  float sc[LOADS][G];
+#pragma unroll
+  for (int u = 0; u < LOADS; ++u) {
+    float kf[EPL];
+    unpack16(kr[u], kf, T());
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) d += qs[h][sl * EPL + e] * kf[e];
+      sc[u][h] = group_sum<Ln::LPR>(d);
+    }
+    const int row = r0 + u * Ln::RPW + sub;
+    const bool valid = row < r1;
+    float bias = 0.f;
+    int sk = 0;
+    if (lnn != nullptr && valid) {
+      bias = lnn[row - bias0];
+      sk = skip[row - bias0];
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      sc[u][h] = (valid && !((sk >> h) & 1)) ? sc[u][h] + bias : -INFINITY;
+  }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
+    float mx = sc[0][h];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) red[h][slot][4 + sl * EPL + e] = acc[h][e];
-    if (sl == 0) {
-      red[h][slot][0] = m[h];
-      red[h][slot][1] = l[h];
+    for (int u = 1; u < LOADS; ++u) mx = fmaxf(mx, sc[u][h]);
+    if (mx == -INFINITY) continue;
+    const float M = fmaxf(s.m[h], mx);
+    const float wo = (s.m[h] == -INFINITY) ? 0.f : __expf(s.m[h] - M);
+    s.l[h] *= wo;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s.acc[h][e] *= wo;
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const float p = (sc[u][h] == -INFINITY) ? 0.f : __expf(sc[u][h] - M);
+      float vf[EPL];
+      unpack16(vr[u], vf, T());
+      s.l[h] += p;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s.acc[h][e] += p * vf[e];
     }
+    s.m[h] = M;
   }
-  __syncthreads();
-  for (int o = tid; o < G * kHeadDim; o += 256) {
-    const int h = o / kHeadDim, dim = o % kHeadDim;
-    float M = -INFINITY;
+}
+
+template <typename T, int G>
+__device__ __forceinline__ void rows_finish(RowState<T, G>& s) {
+  using Ln = Lanes<T>;
 #pragma unroll
-    for (int sidx = 0; sidx < NSLOT; ++sidx) M = fmaxf(M, red[h][sidx][0]);
-    float L = 0.f, A = 0.f;
-    if (M != -INFINITY) {
+  for (int off = Ln::LPR; off < 64; off <<= 1) {
 #pragma unroll
-      for (int sidx = 0; sidx < NSLOT; ++sidx) {
-        const float ms = red[h][sidx][0];
-        const float w = ms == -INFINITY ? 0.f : __expf(ms - M);
-        L += red[h][sidx][1] * w;
-        A += red[h][sidx][4 + dim] * w;
+    for (int h = 0; h < G; ++h) {
+      const float mo = __shfl_xor(s.m[h], off, 64);
+      const float lo = __shfl_xor(s.l[h], off, 64);
+      float w1, w2;
+      const float M = merge_w(s.m[h], mo, w1, w2);
+      s.l[h] = s.l[h] * w1 + lo * w2;
+#pragma unroll
+      for (int e = 0; e < Ln::EPL; ++e) {
+        const float ao = __shfl_xor(s.acc[h][e], off, 64);
+        s.acc[h][e] = s.acc[h][e] * w1 + ao * w2;
       }
-    }
-    float* dst = part + ((size_t)(g * G + h) * n_slots + tile) * kPartStride;
-    dst[4 + dim] = A;
-    if (dim == 0) {
-      dst[0] = M;
-      dst[1] = L;
+      s.m[h] = M;
     }
   }
 }
 
-template <typename T>
-static hipError_t launch_tiles_t(const DecodeGeom& g, const float* q, const T* dk, const T* dv,
-                                 const T* kb, const T* vb, const float* lnn32,
-                                 const uint8_t* mask, float* part, hipStream_t st) {
-  const int tiles = g.dense_tiles + g.coarse_tiles;
-  if (tiles == 0) return hipSuccess;
-  dim3 grid(tiles, g.n_kv_heads);
-#define SEKV_TILES(GG)                                                                        \
-  case GG:                                                                                    \
-    hipLaunchKernelGGL((attn_tiles_kernel<T, GG>), grid, dim3(256), 0, st, q, dk, dv, kb, vb, \
-                       lnn32, mask, g.n_dense, g.n_compressed, g.dense_tiles, g.n_slots,      \
-                       part);                                                                 \
-    break;
-  switch (g.group) {
-    SEKV_TILES(1) SEKV_TILES(2) SEKV_TILES(3) SEKV_TILES(4) SEKV_TILES(5) SEKV_TILES(6)
-    SEKV_TILES(7) SEKV_TILES(8)
-    default: return hipErrorInvalidValue;
+template <typename T, int G>
+__device__ __forceinline__ void rows_store(const RowState<T, G>& s, float (*acc)[kHeadDim],
+                                           float* m, float* l) {
+  using Ln = Lanes<T>;
+  const int lane = threadIdx.x & 63, sub = lane / Ln::LPR, sl = lane % Ln::LPR;
+  if (sub == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < Ln::EPL; ++e) acc[h][sl * Ln::EPL + e] = s.acc[h][e];
   }
-#undef SEKV_TILES
-  return hipGetLastError();
-}
-
-hipError_t launch_attn_tiles(int bf16, const DecodeGeom& g, const float* q, const void* dense_k,
-                             const void* dense_v, const void* kbar, const void* vbar,
-                             const float* lnn32, const uint8_t* mask, float* part,
-                             hipStream_t st) {
-  if (bf16)
-    return launch_tiles_t<uint16_t>(g, q, (const uint16_t*)dense_k, (const uint16_t*)dense_v,
-                                    (const uint16_t*)kbar, (const uint16_t*)vbar, lnn32, mask,
-                                    part, st);
-  return launch_tiles_t<float>(g, q, (const float*)dense_k, (const float*)dense_v,
-                               (const float*)kbar, (const float*)vbar, lnn32, mask, part, st);
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = s.m[h];
+      l[h] = s.l[h];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Zoomed spans, factored (Eq. 8 with hard gates).  Grid (zoom slots, KV
-// heads); slot z of group g takes union entries z, z + slots, ...  For a span
-// with factors U, sigma, V of keys and of values and the heads H that zoomed
-// it:  b_h = sigma_K * (V_K^T q_h) / sqrt(d);  e_{h,t} = U_K[t] . b_h;
-// p = exp(e - m);  c_h = U_V^T p;  acc_h += V_V (sigma_V * c_h).
-// Reconstructed rows are never formed: per head the work is 2 r (n + d)
-// multiply-adds against 8 r (n + d + 1) bytes of factors read once for all
-// heads of the group.
+// One zoomed span, one wave: factored attention of the heads in `hm`, merged
+// into the wave's running state (zm, zl, za: lane holds dims 2 lane, 2 lane+1).
 // ---------------------------------------------------------------------------
 template <int G>
-__device__ __forceinline__ void block_max_sum(float* v, bool is_max, float (*red)[G]) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float x = v[h];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float y = __shfl_xor(x, o, 64);
-      x = is_max ? fmaxf(x, y) : x + y;
-    }
-    if (lane == 0) red[wid][h] = x;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float x = red[0][h];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) x = is_max ? fmaxf(x, red[w][h]) : x + red[w][h];
-    v[h] = x;
-  }
-  __syncthreads();
-}
+__device__ void zoom_span(const float* __restrict__ blk, int n, int r, unsigned hm,
+                          const float (*qs)[kHeadDim], WaveScratch<G>& ws, float* zm, float* zl,
+                          float (*za)[2]) {
+  const int lane = threadIdx.x & 63;
+  const FactorView fv(r, n);
+  const int r4 = fv.r4;
+  const float* vk = blk + fv.vt(0);
+  const float* uk = blk + fv.u(0);
+  const float* sk = blk + fv.sigma(0);
+  const float* vv = blk + fv.vt(1);
+  const float* uv = blk + fv.u(1);
+  const float* sv = blk + fv.sigma(1);
 
-template <int G>
-__global__ __launch_bounds__(256) void attn_zoom_kernel(
-    const float* __restrict__ q, const uint8_t* __restrict__ mask,
-    const int32_t* __restrict__ ulist, const int32_t* __restrict__ ucount,
-    const int32_t* __restrict__ clen, const int32_t* __restrict__ rank,
-    const uint64_t* __restrict__ fac_off, uint64_t off_base, const float* __restrict__ pool,
-    int sc, int slot0, int n_slots, int zslots, float* __restrict__ part) {
-  constexpr int HPT = (G + 1) / 2;  // output heads per thread
-  __shared__ float qs[G][kHeadDim];
-  __shared__ float bsh[G][kHeadDim];
-  __shared__ float csh[G][kHeadDim];
-  __shared__ float psh[G][256];
-  __shared__ float red[4][G];
-  const int zs = blockIdx.x, g = blockIdx.y;
-  const int tid = threadIdx.x;
-  const float scale = rsqrtf((float)kHeadDim);
-  for (int o = tid; o < G * kHeadDim; o += 256)
-    qs[o / kHeadDim][o % kHeadDim] = q[(size_t)g * G * kHeadDim + o] * scale;
-  const int dim = tid & (kHeadDim - 1), hsel = tid >> 7;
-  float m_run[G], l_run[G], acc_run[HPT];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m_run[h] = -INFINITY;
-    l_run[h] = 0.f;
-  }
-#pragma unroll
-  for (int k = 0; k < HPT; ++k) acc_run[k] = 0.f;
-  __syncthreads();
-
-  const int nu = ucount[g];
-  const int rsub = tid >> 3, part8 = tid & 7;
-  for (int u = zs; u < nu; u += zslots) {
-    const int j = ulist[(size_t)g * sc + u];
-    unsigned hm = 0;
-#pragma unroll
-    for (int h = 0; h < G; ++h) hm |= (unsigned)(mask[(size_t)(g * G + h) * sc + j] != 0) << h;
-    const int n = clen[j];
-    const int r = rank[(size_t)g * sc + j];
-    const FactorView fv(r, n);
-    const float* blk = pool + (fac_off[(size_t)g * sc + j] - off_base);
-    const float* vk = blk + fv.vt(0);
-    const float* uk = blk + fv.u(0);
-    const float* sk = blk + fv.sigma(0);
-    const float* vv = blk + fv.vt(1);
-    const float* uv = blk + fv.u(1);
-    const float* sv = blk + fv.sigma(1);
-
-    // b_h = sigma_K * (V_K^T q_h), scale folded into q
-    for (int i0 = 0; i0 < r; i0 += 32) {
-      const int i = i0 + rsub;
+  // (A) b_h[i] = sigma_K[i] * (V_K^T q_h)[i]: 8 lanes per component, 16 dims per lane
+  {
+    const int part = lane & 7, ci = lane >> 3;
+    for (int i0 = 0; i0 < r; i0 += 8) {
+      const int i = i0 + ci;
       float pa[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) pa[h] = 0.f;
       if (i < r) {
-        const float4* row = (const float4*)(vk + (size_t)i * kHeadDim + part8 * 16);
+        const float4* row = (const float4*)(vk + (size_t)i * kHeadDim + part * 16);
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
           const float4 x = row[c4];
-          const int d0 = part8 * 16 + c4 * 4;
+          const int d0 = part * 16 + c4 * 4;
 #pragma unroll
           for (int h = 0; h < G; ++h)
-            pa[h] += x.x * qs[h][d0] + x.y * qs[h][d0 + 1] + x.z * qs[h][d0 + 2] + x.w * qs[h][d0 + 3];
+            pa[h] += x.x * qs[h][d0] + x.y * qs[h][d0 + 1] + x.z * qs[h][d0 + 2] +
+                     x.w * qs[h][d0 + 3];
         }
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        pa[h] += __shfl_xor(pa[h], 1, 64);
-        pa[h] += __shfl_xor(pa[h], 2, 64);
-        pa[h] += __shfl_xor(pa[h], 4, 64);
+        pa[h] = group_sum<8>(pa[h]);
       }
-      if (part8 == 0 && i < r) {
+      if (part == 0 && i < r) {
         const float sg = sk[i];
 #pragma unroll
-        for (int h = 0; h < G; ++h) bsh[h][i] = pa[h] * sg;
+        for (int h = 0; h < G; ++h) ws.z.bsh[h][i] = pa[h] * sg;
       }
     }
-    for (int o = tid; o < G * kHeadDim; o += 256) csh[o / kHeadDim][o % kHeadDim] = 0.f;
-    __syncthreads();
+    // padding components and the value-side coefficients start at zero
+    for (int idx = lane; idx < G * r4; idx += 64) {
+      const int h = idx / r4, i = idx % r4;
+      if (i >= r) ws.z.bsh[h][i] = 0.f;
+      ws.z.csh[h][i] = 0.f;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
 
-    float ms[G], ls[G];
+  // (B, C) 64 tokens at a time: scores, online softmax, c_h += U_V^T p_h
+  float ms[G], ls[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    ms[h] = -INFINITY;
+    ls[h] = 0.f;
+  }
+  for (int t0 = 0; t0 < n; t0 += 64) {
+    const int t = t0 + lane;
+    float e[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) e[h] = 0.f;
+    if (t < n) {
+      const float4* ur = (const float4*)(uk + (size_t)t * r4);
+      for (int i4 = 0; i4 < r4 / 4; ++i4) {
+        const float4 u = ur[i4];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float4 b = *(const float4*)&ws.z.bsh[h][4 * i4];
+          e[h] += u.x * b.x + u.y * b.y + u.z * b.z + u.w * b.w;
+        }
+      }
+    }
+    float corr[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      ms[h] = -INFINITY;
-      ls[h] = 0.f;
+      if (t >= n || !((hm >> h) & 1u)) e[h] = -INFINITY;
+      const float mx = wave_max(e[h]);
+      const float mn = fmaxf(ms[h], mx);
+      corr[h] = (ms[h] == -INFINITY) ? 0.f : __expf(ms[h] - mn);
+      const float p = (e[h] == -INFINITY) ? 0.f : __expf(e[h] - mn);
+      ls[h] = ls[h] * corr[h] + wave_sum(p);
+      ms[h] = mn;
+      ws.z.psh[lane][h] = p;
     }
-    for (int t0 = 0; t0 < n; t0 += 256) {
-      const int t = t0 + tid;
-      float e[G];
+    __builtin_amdgcn_wave_barrier();
+    const int tn = min(64, n - t0);
+    const int i4 = lane & 7, ts = lane >> 3;
+    for (int cb = 0; cb < r4; cb += 32) {
+      const int i = cb + 4 * i4;
+      float c4[G][4];
 #pragma unroll
-      for (int h = 0; h < G; ++h) e[h] = 0.f;
-      if (t < n) {
-        for (int i = 0; i < r; ++i) {
-          const float x = uk[(size_t)i * fv.n4 + t];
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int h = 0; h < G; ++h) e[h] += x * bsh[h][i];
+        for (int q = 0; q < 4; ++q) c4[h][q] = 0.f;
+      if (i < r4) {
+        for (int k = ts; k < tn; k += 8) {
+          const float4 u = *(const float4*)(uv + (size_t)(t0 + k) * r4 + i);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float p = ws.z.psh[k][h];
+            c4[h][0] += p * u.x;
+            c4[h][1] += p * u.y;
+            c4[h][2] += p * u.z;
+            c4[h][3] += p * u.w;
+          }
         }
       }
 #pragma unroll
       for (int h = 0; h < G; ++h)
-        if (t >= n || !((hm >> h) & 1u)) e[h] = -INFINITY;
-      float cm[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) cm[h] = e[h];
-      block_max_sum<G>(cm, true, red);
-      float corr[G], p[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float mn = fmaxf(ms[h], cm[h]);
-        corr[h] = (ms[h] == -INFINITY) ? 0.f : __expf(ms[h] - mn);
-        p[h] = (e[h] == -INFINITY) ? 0.f : __expf(e[h] - mn);
-        psh[h][tid] = p[h];
-        ms[h] = mn;
-      }
-      block_max_sum<G>(p, false, red);  // also orders the psh writes before use
-#pragma unroll
-      for (int h = 0; h < G; ++h) ls[h] = ls[h] * corr[h] + p[h];
-      const int tn = min(256, n - t0);
-      for (int i0 = 0; i0 < r; i0 += 32) {
-        const int i = i0 + rsub;
-        float pc[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) pc[h] = 0.f;
-        if (i < r) {
-          const float* ur = uv + (size_t)i * fv.n4 + t0;
-          for (int k = part8; k < tn; k += 8) {
-            const float x = ur[k];
-#pragma unroll
-            for (int h = 0; h < G; ++h) pc[h] += psh[h][k] * x;
-          }
+        for (int q = 0; q < 4; ++q) {
+          c4[h][q] += dpp<kDppRor8>(c4[h][q]);
+          c4[h][q] += __shfl_xor(c4[h][q], 16, 64);
+          c4[h][q] += __shfl_xor(c4[h][q], 32, 64);
         }
+      if (ts == 0 && i < r4) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) ws.z.csh[h][i + q] = ws.z.csh[h][i + q] * corr[h] + c4[h][q];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // (D) a_h[dim] = sum_i V_V[i][dim] sigma_V[i] c_h[i]; merge into the running state
+  float a[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) a[h][0] = a[h][1] = 0.f;
+  for (int i = 0; i < r; ++i) {
+    const float2 x = *(const float2*)(vv + (size_t)i * kHeadDim + 2 * lane);
+    const float sg = sv[i];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float w = sg * ws.z.csh[h][i];
+      a[h][0] += w * x.x;
+      a[h][1] += w * x.y;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if (!((hm >> h) & 1u)) continue;
+    float w1, w2;
+    const float M = merge_w(zm[h], ms[h], w1, w2);
+    za[h][0] = za[h][0] * w1 + a[h][0] * w2;
+    za[h][1] = za[h][1] * w1 + a[h][1] * w2;
+    zl[h] = zl[h] * w1 + ls[h] * w2;
+    zm[h] = M;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// ---------------------------------------------------------------------------
+// The same for r <= 32, with the span's loads issued ahead of their use and
+// at most ~96 registers of them in flight: V_K and the first 64 rows of U_K
+// together; U_V and the first half of V_V before the scores are formed; the
+// next 64 tokens' rows while the current ones are consumed; the second half
+// of V_V before the reduction of c.  Every load reads a clamped, valid
+// address; values past the span's rank or length are zeroed.
+// ---------------------------------------------------------------------------
+template <int G>
+__device__ void zoom_span32(const float* __restrict__ blk, int n, int r, unsigned hm,
+                            const float (*qs)[kHeadDim], WaveScratch<G>& ws, float* zm, float* zl,
+                            float (*za)[2]) {
+  const int lane = threadIdx.x & 63;
+  const FactorView fv(r, n);
+  const int r4 = fv.r4, nq = r4 / 4;
+  const float* vk = blk + fv.vt(0);
+  const float* uk = blk + fv.u(0);
+  const float* sk = blk + fv.sigma(0);
+  const float* vv = blk + fv.vt(1);
+  const float* uv = blk + fv.u(1);
+  const float* sv = blk + fv.sigma(1);
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int part = lane & 7, ci = lane >> 3;   // (A): component ci + 8 p, dims 16 part ..
+  const int i4 = lane & 7, ts = lane >> 3;     // (C): components 4 i4 .., tokens ts + 8 m
+  const int ic = min(4 * i4, r4 - 4);
+
+  float4 va[4][4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int i = min(ci + 8 * p, r - 1);
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4)
+      va[p][c4] = *(const float4*)(vk + (size_t)i * kHeadDim + part * 16 + c4 * 4);
+  }
+  const int lr = min(lane, r - 1);
+  float skl = sk[lr], svl = sv[lr];
+  float4 ub[8];
+  {
+    const int tl = min(lane, n - 1);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) ub[q] = *(const float4*)(uk + (size_t)tl * r4 + 4 * min(q, nq - 1));
+  }
+  if (lane >= r) skl = svl = 0.f;
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+    if (ci + 8 * p >= r)
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) va[p][c4] = z4;
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    if (lane >= n || q >= nq) ub[q] = z4;
+
+  // (A) b_h[i] = sigma_K[i] (V_K^T q_h)[i]; components r..31 get 0
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int i = ci + 8 * p;
+    float pa[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float acc = 0.f;
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const float4 qv = *(const float4*)&qs[h][part * 16 + c4 * 4];
+        acc += va[p][c4].x * qv.x + va[p][c4].y * qv.y + va[p][c4].z * qv.z + va[p][c4].w * qv.w;
+      }
+      pa[h] = group_sum<8>(acc);
+    }
+    const float sg = __shfl(skl, i, 64);
+    if (part == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) ws.z.bsh[h][i] = pa[h] * sg;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  int tn = min(64, n);
+  float4 uc[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) uc[m] = *(const float4*)(uv + (size_t)min(ts + 8 * m, tn - 1) * r4 + ic);
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+    if (ts + 8 * m >= tn || 4 * i4 >= r4) uc[m] = z4;
+  float2 vd[32];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) vd[i] = *(const float2*)(vv + (size_t)min(i, r - 1) * kHeadDim + 2 * lane);
+
+  float ms[G], ls[G], cacc[G][4];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    ms[h] = -INFINITY;
+    ls[h] = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) cacc[h][q] = 0.f;
+  }
+  for (int t0 = 0; t0 < n; t0 += 64) {
+    tn = min(64, n - t0);
+    // (B) scores of tokens t0 + lane
+    float e[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float acc = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (q < nq) {
+          const float4 b = *(const float4*)&ws.z.bsh[h][4 * q];
+          acc += ub[q].x * b.x + ub[q].y * b.y + ub[q].z * b.z + ub[q].w * b.w;
+        }
+      }
+      e[h] = (lane < tn && ((hm >> h) & 1u)) ? acc : -INFINITY;
+    }
+    const int t1 = t0 + 64;
+    if (t1 < n) {
+      const int tl1 = min(t1 + lane, n - 1);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) ub[q] = *(const float4*)(uk + (size_t)tl1 * r4 + 4 * min(q, nq - 1));
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (t1 + lane >= n || q >= nq) ub[q] = z4;
+    }
+    float corr[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mx = wave_max(e[h]);
+      const float mn = fmaxf(ms[h], mx);
+      corr[h] = (ms[h] == -INFINITY) ? 0.f : __expf(ms[h] - mn);
+      const float p = (e[h] == -INFINITY) ? 0.f : __expf(e[h] - mn);
+      ls[h] = ls[h] * corr[h] + wave_sum(p);
+      ms[h] = mn;
+      ws.z.psh[lane][h] = p;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // (C) c_h[4 i4 ..] += sum over this lane's tokens of p_h U_V
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cacc[h][q] *= corr[h];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int k = ts + 8 * m;
+      if (k < tn) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          pc[h] += __shfl_xor(pc[h], 1, 64);
-          pc[h] += __shfl_xor(pc[h], 2, 64);
-          pc[h] += __shfl_xor(pc[h], 4, 64);
+          const float p = ws.z.psh[k][h];
+          cacc[h][0] += p * uc[m].x;
+          cacc[h][1] += p * uc[m].y;
+          cacc[h][2] += p * uc[m].z;
+          cacc[h][3] += p * uc[m].w;
         }
-        if (part8 == 0 && i < r) {
+      }
+    }
+    if (t1 < n) {
+      const int tn1 = min(64, n - t1);
 #pragma unroll
-          for (int h = 0; h < G; ++h) csh[h][i] = csh[h][i] * corr[h] + pc[h];
+      for (int m = 0; m < 8; ++m)
+        uc[m] = *(const float4*)(uv + (size_t)(t1 + min(ts + 8 * m, tn1 - 1)) * r4 + ic);
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        if (ts + 8 * m >= tn1 || 4 * i4 >= r4) uc[m] = z4;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (r > 16) {   // the other rows of V_V
+#pragma unroll
+    for (int i = 16; i < 32; ++i)
+      vd[i] = *(const float2*)(vv + (size_t)min(i, r - 1) * kHeadDim + 2 * lane);
+  }
+  // reduce c over the 8 token lanes; sigma_V folded in
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      cacc[h][q] += dpp<kDppRor8>(cacc[h][q]);
+      cacc[h][q] += __shfl_xor(cacc[h][q], 16, 64);
+      cacc[h][q] += __shfl_xor(cacc[h][q], 32, 64);
+    }
+  float sgv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sgv[q] = __shfl(svl, 4 * i4 + q, 64);
+  if (ts == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      *(float4*)&ws.z.csh[h][4 * i4] = make_float4(cacc[h][0] * sgv[0], cacc[h][1] * sgv[1],
+                                                   cacc[h][2] * sgv[2], cacc[h][3] * sgv[3]);
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // (D) a_h[dim] = sum_i V_V[i][dim] (sigma_V c_h)[i]; rows past r hold a
+  // clamped copy of row r - 1 (or were never loaded) and are skipped
+  float a[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) a[h][0] = a[h][1] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    if (i < r) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float w = ws.z.csh[h][i];
+        a[h][0] += w * vd[i].x;
+        a[h][1] += w * vd[i].y;
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if (!((hm >> h) & 1u)) continue;
+    float w1, w2;
+    const float M = merge_w(zm[h], ms[h], w1, w2);
+    za[h][0] = za[h][0] * w1 + a[h][0] * w2;
+    za[h][1] = za[h][1] * w1 + a[h][1] * w2;
+    zl[h] = zl[h] * w1 + ls[h] * w2;
+    zm[h] = M;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// ---------------------------------------------------------------------------
+// the layer kernel
+// ---------------------------------------------------------------------------
+static_assert(kChunk * kMaxGroup <= kThreads, "one gate per thread");
+static_assert(kChunk <= 64, "a chunk's zoom sets are one wave ballot");
+
+template <typename T, int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
+  using Ln = Lanes<T>;
+  constexpr int CLOADS = (kChunk / kWaves) / Ln::RPW;     // coarse entries: loads per wave
+  constexpr int DLOADS = kRowBlock / Ln::RPW;             // full-resolution rows: loads per pass
+  __shared__ Smem<G> s;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int W = geo.n_work;
+  const int g = blockIdx.x / W, w = blockIdx.x % W;
+  const int sc = geo.n_compressed, D = geo.n_dense, dr = geo.route_dim;
+  const int h0 = g * G;
+  const int j0 = w * kChunk, nj = w < geo.n_chunks ? min(kChunk, sc - j0) : 0;
+  const int d0 = w * geo.dense_rows, d1 = min(D, d0 + geo.dense_rows);
+  const bool route = (mode & kRoute) != 0, dense = (mode & kDense) != 0;
+  const bool zoom = (mode & kZoom) != 0, attn = dense || zoom;
+  const float scale = rsqrtf((float)kHeadDim);
+
+  // ---- everything this workgroup reads before its zoom decisions, issued up
+  // front: query, span metadata, routing projections, summaries, ln n,
+  // thresholds, then the full-resolution rows (first pass) and coarse entries
+  // (loads complete in issue order, so routing never waits for the rows)
+  for (int o = tid; o < G * kHeadDim; o += kThreads) {
+    const float x = a.q[(size_t)h0 * kHeadDim + o];
+    s.qu[o / kHeadDim][o % kHeadDim] = x;
+    s.qs[o / kHeadDim][o % kHeadDim] = x * scale;
+  }
+  if (tid < kChunk) s.bits[tid] = 0;
+  if (zoom && tid < nj) {
+    const size_t gj = (size_t)g * sc + j0 + tid;
+    s.m_off[tid] = a.fac_off[gj] - a.off_base;
+    s.m_n[tid] = a.clen[j0 + tid];
+    s.m_r[tid] = a.rank[gj];
+  }
+  const int nout = G * dr, part = tid & 7, orow = tid >> 3;
+  float4 pv[4][4];
+  constexpr int kSumVec = 4;                       // up to 64 bytes of summary per (span, head)
+  const int svec = (dr * (int)sizeof(T)) % 16 == 0 ? dr * (int)sizeof(T) / 16 : 0;
+  const bool sfast = svec > 0 && svec <= kSumVec;
+  uint4 sum[kSumVec];
+  const int jl_g = tid / G, hl_g = tid % G;        // this thread's (span, head) of the gate
+  const bool gate = route && tid < nj * G;
+  double lnn_j = 0.0;   // used only after the barrier, so no wait is forced here
+  float tau_f = 0.f;
+  if (route && nj > 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int o = min(orow + 32 * k, nout - 1);   // rows past nout are never used
+      const float4* pr = (const float4*)(a.proj + ((size_t)h0 * dr + o) * kHeadDim + part * 16);
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) pv[k][c4] = pr[c4];
+    }
+    if (gate) {
+      const int j = j0 + jl_g, h = h0 + hl_g;
+      const uint4* sr = (const uint4*)((const T*)a.summ + ((size_t)h * sc + j) * dr);
+      if (sfast) {
+#pragma unroll
+        for (int v = 0; v < kSumVec; ++v) sum[v] = sr[min(v, svec - 1)];
+      }
+      lnn_j = a.lnn64[j];
+      tau_f = a.tau[h];
+    }
+  }
+  const T* DK = (const T*)a.dense_k + (size_t)g * D * kHeadDim;
+  const T* DV = (const T*)a.dense_v + (size_t)g * D * kHeadDim;
+  uint4 dk[DLOADS], dv[DLOADS];
+  const int dr0 = d0 + wid * kRowBlock;
+  if (dense) rows_load<T, DLOADS>(DK, DV, dr0, min(d1, dr0 + kRowBlock), dk, dv);
+  const int cr0 = j0 + wid * (kChunk / kWaves);
+  const int cr1 = min(j0 + nj, cr0 + kChunk / kWaves);
+  uint4 kr[CLOADS], vr[CLOADS];
+  if (dense && nj > 0) {
+    const T* K = (const T*)a.kbar + (size_t)g * sc * kHeadDim;
+    const T* V = (const T*)a.vbar + (size_t)g * sc * kHeadDim;
+    rows_load<T, CLOADS>(K, V, cr0, cr1, kr, vr);
+  }
+  __syncthreads();
+
+  // ---- routing ------------------------------------------------------------
+  if (route && nj > 0) {
+    // q~_h = P_h q_h (float64): 8 lanes per output, 16 dims per lane
+    for (int k0 = 0; k0 < nout; k0 += 128) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int o = k0 + orow + 32 * k;
+        if (k0 > 0 && o < nout) {
+          const float4* pr = (const float4*)(a.proj + ((size_t)h0 * dr + o) * kHeadDim + part * 16);
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) pv[k][c4] = pr[c4];
         }
+        double acc = 0.0;
+        if (o < nout) {
+          const float* qh = &s.qu[o / dr][part * 16];
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) {
+            const float4 x = pv[k][c4];
+            acc += (double)x.x * (double)qh[4 * c4] + (double)x.y * (double)qh[4 * c4 + 1] +
+                   (double)x.z * (double)qh[4 * c4 + 2] + (double)x.w * (double)qh[4 * c4 + 3];
+          }
+        }
+        acc = group_sum<8>(acc);
+        if (part == 0 && o < nout) s.qt[o / dr][o % dr] = acc;
+      }
+    }
+    __syncthreads();
+    // gate: x = q~ . s_j + gamma ln n_j; p = sigmoid(x); zoom iff p > tau_h
+    if (gate) {
+      const int jl = jl_g, hl = hl_g, j = j0 + jl, h = h0 + hl;
+      double x = 0.0;
+      if (sfast) {
+#pragma unroll
+        for (int v = 0; v < kSumVec; ++v) {
+          if (v < svec) {
+            float f[Ln::EPL];
+            unpack16(sum[v], f, T());
+#pragma unroll
+            for (int e = 0; e < Ln::EPL; ++e) x += s.qt[hl][v * Ln::EPL + e] * (double)f[e];
+          }
+        }
+      } else {
+        const T* sr = (const T*)a.summ + ((size_t)h * sc + j) * dr;
+        for (int i = 0; i < dr; ++i) x += s.qt[hl][i] * (double)Store<T>::load(sr + i);
+      }
+      x += a.gamma * lnn_j;
+      const double p = 1.0 / (1.0 + exp(-x));
+      const bool z = p > (double)tau_f;
+      a.mask[(size_t)h * sc + j] = (uint8_t)z;
+      if (a.prob) a.prob[(size_t)h * sc + j] = p;
+      if (z) atomicOr(&s.bits[jl], 1 << hl);
+    }
+  } else if (attn && nj > 0) {
+    for (int idx = tid; idx < nj * G; idx += kThreads) {
+      const int jl = idx / G, hl = idx % G;
+      if (a.mask[(size_t)(h0 + hl) * sc + j0 + jl]) atomicOr(&s.bits[jl], 1 << hl);
+    }
+  }
+  __syncthreads();
+
+  // ---- zoom sets of the chunk: one wave ballot per list ---------------------
+  if (wid == 0 && nj > 0) {
+    const int b = lane < nj ? s.bits[lane] : 0;
+    if (route) {
+#pragma unroll
+      for (int li = 0; li <= G; ++li) {
+        const bool z = li < G ? ((b >> li) & 1) != 0 : b != 0;
+        const unsigned long long bal = __ballot(z);
+        if (lane == 0) a.chunk_bits[((size_t)g * W + w) * kListWords + li] = (uint32_t)bal;
+      }
+    }
+    if (zoom) {
+      const bool z = b != 0;
+      const unsigned long long bal = __ballot(z);
+      if (z) s.zl[__popcll(bal & ((1ull << lane) - 1ull))] = lane;
+      if (lane == 0) s.nz = __popcll(bal);
+    }
+  }
+
+  // ---- full-resolution rows and coarse entries; the state goes to LDS -------
+  if (dense) {
+    RowState<T, G> rs;
+    rs.init();
+    rows_accumulate<T, G, DLOADS>(dk, dv, dr0, min(d1, dr0 + kRowBlock), s.qs, nullptr, nullptr,
+                                  0, rs);
+    for (int p0 = d0 + kWaves * kRowBlock; p0 < d1; p0 += kWaves * kRowBlock) {
+      const int r0 = p0 + wid * kRowBlock, r1 = min(d1, r0 + kRowBlock);
+      rows_load<T, DLOADS>(DK, DV, r0, r1, dk, dv);
+      rows_accumulate<T, G, DLOADS>(dk, dv, r0, r1, s.qs, nullptr, nullptr, 0, rs);
+    }
+    if (nj > 0)
+      rows_accumulate<T, G, CLOADS>(kr, vr, cr0, cr1, s.qs, a.lnn32 + j0, s.bits, j0, rs);
+    rows_finish<T, G>(rs);
+    rows_store<T, G>(rs, s.rows_acc[wid], s.rows_m[wid], s.rows_l[wid]);
+  } else if (lane < G) {
+    s.rows_m[wid][lane] = -INFINITY;
+    s.rows_l[wid][lane] = 0.f;
+  }
+  __syncthreads();
+
+  // ---- zoomed spans: one wave per span ---------------------------------------
+  float zm[G], zl[G], za[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    zm[h] = -INFINITY;
+    zl[h] = 0.f;
+    za[h][0] = za[h][1] = 0.f;
+  }
+  if (zoom && nj > 0) {
+    const int nz = s.nz;
+    for (int u = wid; u < nz; u += kWaves) {
+      const int jl = s.zl[u];
+      const float* blk = a.pool + s.m_off[jl];
+      const int n = s.m_n[jl], r = s.m_r[jl];
+      if (r <= 32)
+        zoom_span32<G>(blk, n, r, (unsigned)s.bits[jl], s.qs, s.w[wid], zm, zl, za);
+      else
+        zoom_span<G>(blk, n, r, (unsigned)s.bits[jl], s.qs, s.w[wid], zm, zl, za);
+    }
+  }
+
+  // ---- the wave's zoomed-span state over its (dead) zoom scratch ------------
+  if (attn) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s.w[wid].st.acc[h][2 * lane] = za[h][0];
+      s.w[wid].st.acc[h][2 * lane + 1] = za[h][1];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        s.w[wid].st.m[h] = zm[h];
+        s.w[wid].st.l[h] = zl[h];
+      }
+    }
+    __syncthreads();
+    // ---- this workgroup's partial --------------------------------------------
+    const int slot = (mode & kZoomSplit) ? W + w : w;
+    float* dst = a.part + ((size_t)g * geo.n_slots() + slot) * G * kPartStride;
+    for (int o = tid; o < G * kHeadDim; o += kThreads) {
+      const int h = o / kHeadDim, d = o % kHeadDim;
+      float M = -INFINITY;
+#pragma unroll
+      for (int wv = 0; wv < kWaves; ++wv)
+        M = fmaxf(M, fmaxf(s.rows_m[wv][h], s.w[wv].st.m[h]));
+      float L = 0.f, A = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int wv = 0; wv < kWaves; ++wv) {
+          const float m0 = s.rows_m[wv][h], m1 = s.w[wv].st.m[h];
+          if (m0 != -INFINITY) {
+            const float wt = __expf(m0 - M);
+            L += s.rows_l[wv][h] * wt;
+            A += s.rows_acc[wv][h][d] * wt;
+          }
+          if (m1 != -INFINITY) {
+            const float wt = __expf(m1 - M);
+            L += s.w[wv].st.l[h] * wt;
+            A += s.w[wv].st.acc[h][d] * wt;
+          }
+        }
+      }
+      dst[(size_t)h * kPartStride + 4 + d] = A;
+      if (d == 0) {
+        dst[(size_t)h * kPartStride] = M;
+        dst[(size_t)h * kPartStride + 1] = L;
+      }
+    }
+  }
+
+  // ---- the last workgroup of this KV head ----------------------------------
+  if (!(mode & (kMerge | kLists))) return;
+  // every wave waits until its stores have reached the L2; then one agent-
+  // scope release (an L2 write-back) publishes them all before the ticket
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const unsigned prev =
+        __hip_atomic_fetch_add(&a.tickets[g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s.last = prev == (unsigned)(W - 1);
+  }
+  __syncthreads();
+  if (!s.last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+  if (mode & kMerge) {
+    // thread = (head, 4 dims, stripe of slots): an online pass over its slots,
+    // 8 slots' loads in flight at a time; stripes are combined through LDS
+    const int ns = (mode & kZoomSplit) ? 2 * W : W;
+    const float* pg = a.part + (size_t)g * geo.n_slots() * G * kPartStride;
+    constexpr int QUADS = G * (kHeadDim / 4);
+    constexpr int STRIPES = (kThreads / QUADS) > 0 ? (kThreads / QUADS) : 1;
+    constexpr int B = 8;
+    const int quad = tid % QUADS, stripe = tid / QUADS;
+    const int hl = quad / (kHeadDim / 4), dq = quad % (kHeadDim / 4);
+    float M = -INFINITY, Ls = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (stripe < STRIPES) {
+      for (int sl0 = stripe; sl0 < ns; sl0 += B * STRIPES) {
+        float m[B], l[B];
+        float4 x[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+          const float* p = pg + ((size_t)min(sl0 + u * STRIPES, ns - 1) * G + hl) * kPartStride;
+          m[u] = p[0];
+          l[u] = p[1];
+          x[u] = *(const float4*)(p + 4 + 4 * dq);
+        }
+#pragma unroll
+        for (int u = 0; u < B; ++u)
+          if (sl0 + u * STRIPES >= ns) m[u] = -INFINITY;   // a clamped duplicate: weight 0
+        float bm = m[0];
+#pragma unroll
+        for (int u = 1; u < B; ++u) bm = fmaxf(bm, m[u]);
+        if (bm == -INFINITY) continue;
+        const float Mn = fmaxf(M, bm);
+        const float wo = (M == -INFINITY) ? 0.f : __expf(M - Mn);
+        acc.x *= wo;
+        acc.y *= wo;
+        acc.z *= wo;
+        acc.w *= wo;
+        Ls *= wo;
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+          const float wt = (m[u] == -INFINITY) ? 0.f : __expf(m[u] - Mn);
+          acc.x += wt * x[u].x;
+          acc.y += wt * x[u].y;
+          acc.z += wt * x[u].z;
+          acc.w += wt * x[u].w;
+          Ls += wt * l[u];
+        }
+        M = Mn;
+      }
+    }
+    // the wave scratch is free again
+    float4* red = (float4*)&s.w[0];
+    float* red_m = (float*)(red + STRIPES * QUADS);
+    float* red_l = red_m + STRIPES * G;
+    if (stripe < STRIPES) {
+      red[stripe * QUADS + quad] = acc;
+      if (dq == 0) {
+        red_m[stripe * G + hl] = M;
+        red_l[stripe * G + hl] = Ls;
+      }
+    }
+    __syncthreads();
+    if (tid < QUADS) {
+      float Mx = -INFINITY;
+      for (int st = 0; st < STRIPES; ++st) Mx = fmaxf(Mx, red_m[st * G + hl]);
+      float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+      float L = 0.f;
+      if (Mx != -INFINITY) {
+        for (int st = 0; st < STRIPES; ++st) {
+          const float ms_ = red_m[st * G + hl];
+          if (ms_ == -INFINITY) continue;
+          const float wt = __expf(ms_ - Mx);
+          const float4 y = red[st * QUADS + tid];
+          t.x += wt * y.x;
+          t.y += wt * y.y;
+          t.z += wt * y.z;
+          t.w += wt * y.w;
+          L += wt * red_l[st * G + hl];
+        }
+      }
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      *(float4*)(a.o + (size_t)(h0 + hl) * kHeadDim + 4 * dq) =
+          make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+    }
+  }
+
+  if (mode & kLists) {
+    // ascending per-head lists and the group union, from the chunks' zoom bit
+    // masks: one load per (chunk, list), a block scan of the popcounts, and
+    // each thread writes its chunk's ids
+    const int nc = geo.n_chunks;
+    int base[kListWords];
+#pragma unroll
+    for (int li = 0; li < kListWords; ++li) base[li] = 0;
+    for (int c0 = 0; c0 < nc; c0 += kThreads) {
+      const int c = c0 + tid;
+      uint32_t word[kListWords];
+      int incl[kListWords];
+#pragma unroll
+      for (int li = 0; li <= G; ++li)
+        word[li] = c < nc ? a.chunk_bits[((size_t)g * W + c) * kListWords + li] : 0u;
+#pragma unroll
+      for (int li = 0; li <= G; ++li) {
+        const int cnt = __popc(word[li]);
+        int x = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(x, o, 64);
+          if (lane >= o) x += y;
+        }
+        incl[li] = x;
+        if (lane == 63) s.wc[li][wid] = x;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int li = 0; li <= G; ++li) {
+        int off = base[li], tot = 0;
+#pragma unroll
+        for (int wv = 0; wv < kWaves; ++wv) {
+          off += (wv < wid) ? s.wc[li][wv] : 0;
+          tot += s.wc[li][wv];
+        }
+        off += incl[li] - __popc(word[li]);
+        int32_t* dst = li < G ? a.list + (size_t)(h0 + li) * sc : a.ulist + (size_t)g * sc;
+        uint32_t bits = word[li];
+        while (bits) {
+          const int b = __ffs(bits) - 1;
+          bits &= bits - 1;
+          dst[off++] = c * kChunk + b;
+        }
+        base[li] += tot;
       }
       __syncthreads();
     }
-
-    // acc_h[dim] += sum_i V_V[i][dim] sigma_V[i] c_h[i], merged into the running state
+    if (tid <= G) {
+      int v = 0;
 #pragma unroll
-    for (int k = 0; k < HPT; ++k) {
-      const int h = hsel + 2 * k;
-      if (h >= G || !((hm >> h) & 1u)) continue;
-      float a = 0.f;
-      for (int i = 0; i < r; ++i) a += vv[(size_t)i * kHeadDim + dim] * sv[i] * csh[h][i];
-      const float M = fmaxf(m_run[h], ms[h]);
-      const float wr = (m_run[h] == -INFINITY) ? 0.f : __expf(m_run[h] - M);
-      const float wsp = __expf(ms[h] - M);
-      acc_run[k] = acc_run[k] * wr + a * wsp;
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (!((hm >> h) & 1u)) continue;
-      const float M = fmaxf(m_run[h], ms[h]);
-      const float wr = (m_run[h] == -INFINITY) ? 0.f : __expf(m_run[h] - M);
-      l_run[h] = l_run[h] * wr + ls[h] * __expf(ms[h] - M);
-      m_run[h] = M;
-    }
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int k = 0; k < HPT; ++k) {
-    const int h = hsel + 2 * k;
-    if (h >= G) continue;
-    float* dst = part + ((size_t)(g * G + h) * n_slots + slot0 + zs) * kPartStride;
-    dst[4 + dim] = acc_run[k];
-    if (dim == 0) {
-      dst[0] = m_run[h];
-      dst[1] = l_run[h];
+      for (int li = 0; li <= G; ++li)
+        if (li == tid) v = base[li];
+      if (tid < G) a.count[h0 + tid] = v;
+      else a.ucount[g] = v;
     }
   }
+  if (tid == 0) __hip_atomic_store(&a.tickets[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-hipError_t launch_attn_zoom(const DecodeGeom& g, const float* q, const uint8_t* mask,
-                            const int32_t* ulist, const int32_t* ucount, const int32_t* clen,
-                            const int32_t* rank, const uint64_t* fac_off, const float* pool,
-                            uint64_t off_base, float* part, hipStream_t st) {
-  if (g.zoom_slots == 0) return hipSuccess;
-  dim3 grid(g.zoom_slots, g.n_kv_heads);
-  const int slot0 = g.dense_tiles + g.coarse_tiles;
-#define SEKV_ZOOM(GG)                                                                           \
-  case GG:                                                                                      \
-    hipLaunchKernelGGL((attn_zoom_kernel<GG>), grid, dim3(256), 0, st, q, mask, ulist, ucount,  \
-                       clen, rank, fac_off, off_base, pool, g.n_compressed, slot0, g.n_slots,   \
-                       g.zoom_slots, part);                                                     \
+hipError_t launch_layer(int bf16, int mode, const LayerGeom& g, const LayerArgs& a,
+                        hipStream_t st) {
+  dim3 grid(g.n_work * g.n_kv_heads);
+#define SEKV_LAYER(GG)                                                                      \
+  case GG:                                                                                  \
+    if (bf16)                                                                               \
+      hipLaunchKernelGGL((layer_kernel<uint16_t, GG>), grid, dim3(kThreads), 0, st, g, a,   \
+                         mode);                                                             \
+    else                                                                                    \
+      hipLaunchKernelGGL((layer_kernel<float, GG>), grid, dim3(kThreads), 0, st, g, a, mode); \
     break;
   switch (g.group) {
-    SEKV_ZOOM(1) SEKV_ZOOM(2) SEKV_ZOOM(3) SEKV_ZOOM(4) SEKV_ZOOM(5) SEKV_ZOOM(6) SEKV_ZOOM(7)
-    SEKV_ZOOM(8)
+    SEKV_LAYER(1) SEKV_LAYER(2) SEKV_LAYER(3) SEKV_LAYER(4) SEKV_LAYER(5) SEKV_LAYER(6)
+    SEKV_LAYER(7) SEKV_LAYER(8)
     default: return hipErrorInvalidValue;
   }
-#undef SEKV_ZOOM
+#undef SEKV_LAYER
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the split-K partials: o = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s
+// small fill (used instead of a memset so the calls can be graph-captured)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kHeadDim) void attn_merge_kernel(const float* __restrict__ part,
-                                                              int n_slots, float* __restrict__ o) {
-  const int h = blockIdx.x, dim = threadIdx.x;
-  const float* ph = part + (size_t)h * n_slots * kPartStride;
-  float M = -INFINITY;
-  for (int s = 0; s < n_slots; ++s) M = fmaxf(M, ph[(size_t)s * kPartStride]);
-  float L = 0.f, A = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < n_slots; ++s) {
-      const float ms = ph[(size_t)s * kPartStride];
-      if (ms == -INFINITY) continue;
-      const float w = __expf(ms - M);
-      L += ph[(size_t)s * kPartStride + 1] * w;
-      A += ph[(size_t)s * kPartStride + 4 + dim] * w;
-    }
-  }
-  o[(size_t)h * kHeadDim + dim] = L > 0.f ? A / L : 0.f;
+__global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
 }
 
-hipError_t launch_attn_merge(const DecodeGeom& g, const float* part, float* o, hipStream_t st) {
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(g.n_q_heads), dim3(kHeadDim), 0, st, part,
-                     g.n_slots, o);
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, p, n, v);
   return hipGetLastError();
 }
 
@@ -599,14 +1110,16 @@ hipError_t launch_attn_merge(const DecodeGeom& g, const float* part, float* o, h
 // pinned host memory into device staging at the same layer-relative offsets
 // (16-byte loads over the host link).
 // ---------------------------------------------------------------------------
+constexpr int kFetchSlots = 64;
+
 __global__ __launch_bounds__(256) void fetch_gather_kernel(
     const int32_t* __restrict__ ulist, const int32_t* __restrict__ ucount,
     const int32_t* __restrict__ clen, const int32_t* __restrict__ rank,
-    const uint64_t* __restrict__ fac_off, uint64_t layer_base, int sc, int zslots,
+    const uint64_t* __restrict__ fac_off, uint64_t layer_base, int sc,
     const float* __restrict__ host, float* __restrict__ stage) {
   const int zs = blockIdx.x, g = blockIdx.y;
   const int nu = ucount[g];
-  for (int u = zs; u < nu; u += zslots) {
+  for (int u = zs; u < nu; u += kFetchSlots) {
     const int j = ulist[(size_t)g * sc + u];
     const FactorView fv(rank[(size_t)g * sc + j], clen[j]);
     const uint64_t off = fac_off[(size_t)g * sc + j];
@@ -617,14 +1130,14 @@ __global__ __launch_bounds__(256) void fetch_gather_kernel(
   }
 }
 
-hipError_t launch_fetch_gather(const DecodeGeom& g, const int32_t* ulist, const int32_t* ucount,
+hipError_t launch_fetch_gather(const LayerGeom& g, const int32_t* ulist, const int32_t* ucount,
                                const int32_t* clen, const int32_t* rank,
                                const uint64_t* fac_off, uint64_t layer_base,
                                const float* host_pool_mapped, float* stage, hipStream_t st) {
-  if (g.zoom_slots == 0) return hipSuccess;
-  hipLaunchKernelGGL(fetch_gather_kernel, dim3(g.zoom_slots, g.n_kv_heads), dim3(256), 0, st,
+  if (g.n_compressed == 0) return hipSuccess;
+  hipLaunchKernelGGL(fetch_gather_kernel, dim3(kFetchSlots, g.n_kv_heads), dim3(256), 0, st,
                      ulist, ucount, clen, rank, fac_off, layer_base, g.n_compressed,
-                     g.zoom_slots, host_pool_mapped, stage);
+                     host_pool_mapped, stage);
   return hipGetLastError();
 }
 

@@ -13,23 +13,24 @@ constexpr int kMaxRouteDim = 64;  // dr
 
 // ---------------------------------------------------------------------------
 // Factor block of one (layer, KV head, compressed span), float32, in the pool:
-//   [ VKt r x d | UK r x n4 | sK r4 | VVt r x d | UV r x n4 | sV r4 ]
-// VKt/VVt hold the right singular vectors as rows, UK/UV the left singular
-// vectors component-major (entry [i][t] is token t of component i, so a wave
-// reading one component over consecutive tokens is coalesced), sK/sV the
-// singular values.  n4 = n rounded up to 4, r4 = r rounded up to 4, so every
-// sub-array starts on a 16-byte boundary; padding entries are zero.  Blocks
-// start on 256-byte boundaries.  Algorithmic size: 8 r (n + d + 1) bytes.
+//   [ VKt r x d | UK n x r4 | sK r4 | VVt r x d | UV n x r4 | sV r4 ]
+// VKt/VVt hold the right singular vectors as rows; UK/UV hold the left
+// singular vectors token-major (row t is token t's r coefficients, padded to
+// r4 = r rounded up to 4), so one lane reads a token's whole row with 16-byte
+// loads and the rows of consecutive tokens are contiguous; sK/sV hold the
+// singular values.  Every sub-array starts on a 16-byte boundary and padding
+// entries are zero.  Blocks start on 256-byte boundaries.  Algorithmic size:
+// 8 r (n + d + 1) bytes.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int round4(int x) { return (x + 3) & ~3; }
 
 struct FactorView {
-  int r, n, n4, r4;
-  __host__ __device__ FactorView(int r_, int n_) : r(r_), n(n_), n4(round4(n_)), r4(round4(r_)) {}
-  __host__ __device__ int half() const { return r * kHeadDim + r * n4 + r4; }
+  int r, n, r4;
+  __host__ __device__ FactorView(int r_, int n_) : r(r_), n(n_), r4(round4(r_)) {}
+  __host__ __device__ int half() const { return r * kHeadDim + n * r4 + r4; }
   __host__ __device__ int vt(int kv) const { return kv * half(); }
   __host__ __device__ int u(int kv) const { return kv * half() + r * kHeadDim; }
-  __host__ __device__ int sigma(int kv) const { return kv * half() + r * kHeadDim + r * n4; }
+  __host__ __device__ int sigma(int kv) const { return kv * half() + r * kHeadDim + n * r4; }
   __host__ __device__ uint64_t block_floats() const {
     return (uint64_t)((2 * half() + 63) & ~63);
   }
@@ -92,10 +93,91 @@ struct SegOut {          // all device, capacity N unless noted
   uint8_t* flag;         // scratch [N]
 };
 
-struct DecodeGeom {
+// ---------------------------------------------------------------------------
+// Decode geometry of a cache.  Per KV head the layer kernel runs n_work
+// workgroups; workgroup w owns
+//   compressed spans [kChunk w, kChunk (w + 1)) (routing, coarse entries and
+//   the zoomed spans among them), and
+//   full-resolution rows [dense_rows w, dense_rows (w + 1)).
+// Partial softmax states live in the workspace as
+//   part[Hkv][2 n_work][G][kPartStride] floats: m, l, -, -, acc[d]
+// slot w holds workgroup w's rows, coarse entries and zoomed spans, or, when
+// the zoomed spans run in a launch of their own, slot n_work + w holds those.
+// ---------------------------------------------------------------------------
+constexpr int kWaves = 4;                 // waves per workgroup of the layer kernel
+constexpr int kThreads = kWaves * 64;
+constexpr int kChunk = 32;                // compressed spans per workgroup
+constexpr int kRowBlock = 16;             // full-resolution rows per wave per pass
+constexpr int kMaxDenseRows = 256;        // full-resolution rows per workgroup, at most
+constexpr int kPartStride = kHeadDim + 4;
+constexpr int kMaxRank = kHeadDim;
+constexpr int kListWords = kMaxGroup + 1; // zoom bit masks per chunk: heads, then union
+
+struct LayerGeom {
   int n_q_heads, n_kv_heads, group, route_dim;
   int n_dense, n_compressed;
-  int dense_tiles, coarse_tiles, zoom_slots, n_slots;
+  int n_chunks;      // ceil(S_c / kChunk)
+  int n_work;        // workgroups per KV head: max(1, n_chunks, ceil(D / kMaxDenseRows))
+  int dense_rows;    // full-resolution rows per workgroup, a multiple of kWaves * kRowBlock
+  __host__ __device__ int n_slots() const { return 2 * n_work; }
+};
+
+__host__ inline LayerGeom make_layer_geom(int hq, int hkv, int dr, int n_dense, int sc) {
+  LayerGeom g{};
+  g.n_q_heads = hq;
+  g.n_kv_heads = hkv;
+  g.group = hq / hkv;
+  g.route_dim = dr;
+  g.n_dense = n_dense;
+  g.n_compressed = sc;
+  g.n_chunks = (sc + kChunk - 1) / kChunk;
+  int w = (n_dense + kMaxDenseRows - 1) / kMaxDenseRows;
+  if (w < g.n_chunks) w = g.n_chunks;
+  if (w < 1) w = 1;
+  g.n_work = w;
+  const int unit = kWaves * kRowBlock;
+  const int rows = (n_dense + w - 1) / w;
+  g.dense_rows = (rows + unit - 1) / unit * unit;
+  return g;
+}
+
+// What one launch of the layer kernel does (bit set).
+enum LayerMode : int {
+  kRoute = 1,      // gate the chunk's spans: mask (+ prob) and the chunk's zoom bit masks
+  kDense = 2,      // attend the workgroup's full-resolution rows and coarse entries
+  kZoom = 4,       // attend the chunk's zoomed spans from their factors
+  kZoomSplit = 8,  // zoomed-span partials go to their own slots (separate launch)
+  kMerge = 16,     // the last workgroup of a KV head merges the partials into o
+  kLists = 32,     // the last workgroup of a KV head writes the ascending zoom lists
+};
+
+struct LayerArgs {
+  const float* q;          // [Hq][d]
+  const float* proj;       // [Hq][dr][d]
+  const float* tau;        // [Hq]
+  const void* summ;        // [Hq][S_c][dr] storage type
+  const double* lnn64;     // [S_c]
+  const float* lnn32;      // [S_c]
+  double gamma;
+  const void* dense_k;     // [Hkv][D][d]
+  const void* dense_v;
+  const void* kbar;        // [Hkv][S_c][d]
+  const void* vbar;
+  const int32_t* clen;     // [S_c]
+  const int32_t* rank;     // [Hkv][S_c]
+  const uint64_t* fac_off; // [Hkv][S_c] float offsets
+  const float* pool;       // factor blocks, addressed as pool + (fac_off - off_base)
+  uint64_t off_base;
+  uint8_t* mask;           // [Hq][S_c] (written with kRoute, read otherwise)
+  double* prob;            // [Hq][S_c] or NULL
+  int32_t* list;           // [Hq][S_c]
+  int32_t* count;          // [Hq]
+  int32_t* ulist;          // [Hkv][S_c]
+  int32_t* ucount;         // [Hkv]
+  float* o;                // [Hq][d]
+  float* part;             // workspace
+  uint32_t* tickets;       // [Hkv], zero between launches
+  uint32_t* chunk_bits;    // [Hkv][n_work][kListWords] zoom bit masks of each chunk
 };
 
 // launchers (return hipError_t of the launch)
@@ -117,21 +199,10 @@ hipError_t launch_span_svd(int bf16, const void* x, int n_tokens, const int32_t*
                            int n_lg, const int32_t* rank, const uint64_t* fac_off, float* pool,
                            int which, int max_m, hipStream_t st);
 
-hipError_t launch_route(int bf16, const DecodeGeom& g, const float* q, const float* proj,
-                        const float* tau, const void* summ, const double* lnn64, double gamma,
-                        uint8_t* mask, double* prob, int32_t* list, int32_t* count,
-                        int32_t* ulist, int32_t* ucount, int32_t* scratch, uint32_t* tickets,
+hipError_t launch_layer(int bf16, int mode, const LayerGeom& g, const LayerArgs& a,
                         hipStream_t st);
-hipError_t launch_attn_tiles(int bf16, const DecodeGeom& g, const float* q, const void* dense_k,
-                             const void* dense_v, const void* kbar, const void* vbar,
-                             const float* lnn32, const uint8_t* mask, float* part,
-                             hipStream_t st);
-hipError_t launch_attn_zoom(const DecodeGeom& g, const float* q, const uint8_t* mask,
-                            const int32_t* ulist, const int32_t* ucount, const int32_t* clen,
-                            const int32_t* rank, const uint64_t* fac_off, const float* pool,
-                            uint64_t off_base, float* part, hipStream_t st);
-hipError_t launch_attn_merge(const DecodeGeom& g, const float* part, float* o, hipStream_t st);
-hipError_t launch_fetch_gather(const DecodeGeom& g, const int32_t* ulist, const int32_t* ucount,
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st);
+hipError_t launch_fetch_gather(const LayerGeom& g, const int32_t* ulist, const int32_t* ucount,
                                const int32_t* clen, const int32_t* rank,
                                const uint64_t* fac_off, uint64_t layer_base,
                                const float* host_pool_mapped, float* stage, hipStream_t st);

@@ -21,8 +21,9 @@
  *     queued kernels surface at the caller's next synchronisation.  Every
  *     failing call leaves a message for sekv_last_error() on the calling
  *     thread, and a failing build leaves *out == NULL.
- *   - A cache may be used by one host thread and one stream order at a time;
- *     distinct caches are independent.
+ *   - A cache may be used by one host thread and one stream order at a time
+ *     (its decode calls share per-cache counters that each launch leaves at
+ *     zero); distinct caches are independent.
  *   - Layouts are row-major C arrays; [a][b] means b varies fastest.
  *     L = n_layers, Hq = n_q_heads, Hkv = n_kv_heads, G = Hq / Hkv (query
  *     heads per KV head; query head h reads KV head h / G), d = head_dim,
@@ -162,7 +163,8 @@ sekv_status sekv_route(const sekv_cache* cache, int32_t layer, const float* q_de
                        const float* proj_dev, const float* tau_dev, const sekv_route_out* out,
                        hipStream_t stream);
 
-/* Bytes of device workspace sekv_decode_attn needs (256-byte aligned). */
+/* Bytes of device workspace sekv_decode_attn and sekv_route_attn need
+ * (256-byte aligned): one partial softmax state per head and work item. */
 size_t sekv_decode_workspace_bytes(const sekv_cache* cache);
 
 /* Attention of one layer over the mixed-resolution memory (SeKV paper
@@ -181,6 +183,18 @@ size_t sekv_decode_workspace_bytes(const sekv_cache* cache);
 sekv_status sekv_decode_attn(const sekv_cache* cache, int32_t layer, const float* q_dev,
                              const sekv_route_out* route, float* o_dev, void* ws_dev,
                              size_t ws_bytes, hipStream_t stream, hipStream_t fetch_stream);
+
+/* Route and attend one layer in one call (SeKV paper Sec. 3.2 gate, Sec. 3.3
+ * Eq. 9 and the mixed-resolution softmax): the result is the same as
+ * sekv_route followed by sekv_decode_attn with the same arguments, and `route`
+ * receives the same mask, lists and counts (and prob, if non-NULL).  With
+ * device-tier factors the whole layer is one kernel launch on `stream`; with
+ * host-tier factors it runs as sekv_route then sekv_decode_attn (fetch on
+ * `fetch_stream`).  Arguments as for those two calls. */
+sekv_status sekv_route_attn(const sekv_cache* cache, int32_t layer, const float* q_dev,
+                            const float* proj_dev, const float* tau_dev,
+                            const sekv_route_out* route, float* o_dev, void* ws_dev,
+                            size_t ws_bytes, hipStream_t stream, hipStream_t fetch_stream);
 
 void sekv_cache_destroy(sekv_cache* cache);
 

@@ -29,19 +29,42 @@ def S():
     return S
 
 
-def run_gpu_layer(S, cache, layer, q, p, tau, with_prob=True):
+def run_gpu_layer(S, cache, layer, q, p, tau, with_prob=True, fused=False):
+    """One layer through the C ABI: sekv_route + sekv_decode_attn, or the
+    single-launch sekv_route_attn."""
     rb = S.RouteBuffers.allocate(cache, with_prob=with_prob)
-    S.sekv_route(cache, layer, q.contiguous(), p.contiguous(), tau.contiguous(), rb)
     o = torch.zeros(cache.cfg.n_q_heads, cache.cfg.head_dim, device="cuda")
     ws = torch.empty(cache.workspace_bytes(), dtype=torch.uint8, device="cuda")
-    S.sekv_decode_attn(cache, layer, q.contiguous(), rb, o, ws)
+    if fused:
+        S.sekv_route_attn(cache, layer, q.contiguous(), p.contiguous(), tau.contiguous(), rb, o, ws)
+    else:
+        S.sekv_route(cache, layer, q.contiguous(), p.contiguous(), tau.contiguous(), rb)
+        S.sekv_decode_attn(cache, layer, q.contiguous(), rb, o, ws)
     torch.cuda.synchronize()
     return rb, o
 
 
+def assert_same_route(a, b):
+    assert torch.equal(a.mask, b.mask)
+    assert torch.equal(a.count, b.count) and torch.equal(a.union_count, b.union_count)
+    for h in range(a.count.numel()):
+        n = int(a.count[h])
+        assert torch.equal(a.list[h, :n], b.list[h, :n])
+    for g in range(a.union_count.numel()):
+        n = int(a.union_count[g])
+        assert torch.equal(a.union_list[g, :n], b.union_list[g, :n])
+    if a.prob is not None and b.prob is not None:
+        assert torch.equal(a.prob, b.prob)
+
+
 def check_layer(S, cache, orc, inp, layer, q, tau, gamma, tol):
+    """Both call paths against the oracle; the single-launch path must give
+    bit-identical routes and outputs to the two-call path."""
     p = inp.p[layer]
     rb, o = run_gpu_layer(S, cache, layer, q, p, tau)
+    rbf, of = run_gpu_layer(S, cache, layer, q, p, tau, fused=True)
+    assert_same_route(rb, rbf)
+    assert torch.equal(o, of)
     route = orc.route(layer, to64(q), to64(p), to64(tau), gamma)
     n_tie = compare_route(rb, route, to64(tau), inp.wl)
     skip = set(tied_heads(route, to64(tau)))
@@ -127,6 +150,8 @@ def test_all_zoomed_full_rank_is_dense_attention(S, name, kw):
     q = inp.query(0)[0]
     tau = torch.full((wl.n_q_heads,), -1.0, device="cuda")
     rb, o = run_gpu_layer(S, cache, 0, q, inp.p[0], tau)
+    rbf, of = run_gpu_layer(S, cache, 0, q, inp.p[0], tau, fused=True)
+    assert torch.equal(o, of)
     assert int(rb.mask.sum()) == wl.n_q_heads * cache.info.n_compressed
     ref = _sdpa(to64(q), to64(inp.k[0]), to64(inp.v[0]))
     err = max(rel_err(to64(o)[h], ref[h]) for h in range(wl.n_q_heads))
@@ -177,6 +202,10 @@ def test_repeat_runs_are_bit_identical(S):
     rb1, o1 = run_gpu_layer(S, cache, 0, q, inp.p[0], tau)
     rb2, o2 = run_gpu_layer(S, cache, 0, q, inp.p[0], tau)
     assert torch.equal(o1, o2)
+    for _ in range(3):
+        rbf, of = run_gpu_layer(S, cache, 0, q, inp.p[0], tau, fused=True)
+        assert torch.equal(o1, of)
+        assert_same_route(rb1, rbf)
     assert torch.equal(rb1.mask, rb2.mask) and torch.equal(rb1.union_list, rb2.union_list)
     assert torch.equal(rb1.list, rb2.list) and torch.equal(rb1.count, rb2.count)
     cache2 = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
@@ -185,21 +214,33 @@ def test_repeat_runs_are_bit_identical(S):
 
 
 def test_host_tier_matches_device_tier(S):
+    """Factors in pinned host memory, fetched per layer for the union of the
+    zoomed spans: same routes as the device tier, outputs equal up to the
+    order of the float32 merge (the zoomed spans form their own partials)."""
     wl = synth.workload("llama3_8b_128k", n_layers=2, n_tokens=9000)
     log("[parity] host tier")
     inp = Inputs(wl, 4)
     dev = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
     host = S.sekv_build_spans(make_cfg(S, wl, tier="host"), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    assert host.info.factor_pool_bytes == dev.info.factor_pool_bytes
     tau = torch.full((wl.n_q_heads,), 0.7, device="cuda")
     side = torch.cuda.Stream()
     for layer in range(2):
         q = inp.query(1)[layer]
-        _, od = run_gpu_layer(S, dev, layer, q, inp.p[layer], tau)
-        rb = S.RouteBuffers.allocate(host)
-        S.sekv_route(host, layer, q, inp.p[layer].contiguous(), tau, rb)
-        oh = torch.zeros_like(od)
-        ws = torch.empty(host.workspace_bytes(), dtype=torch.uint8, device="cuda")
-        S.sekv_decode_attn(host, layer, q, rb, oh, ws, fetch_stream=side)
-        torch.cuda.synchronize()
-        assert int(rb.union_count.sum()) > 0
-        assert torch.equal(od, oh)
+        rbd, od = run_gpu_layer(S, dev, layer, q, inp.p[layer], tau)
+        for fused in (False, True):
+            rb = S.RouteBuffers.allocate(host)
+            oh = torch.zeros_like(od)
+            ws = torch.empty(host.workspace_bytes(), dtype=torch.uint8, device="cuda")
+            if fused:
+                S.sekv_route_attn(host, layer, q, inp.p[layer].contiguous(), tau, rb, oh, ws,
+                                  fetch_stream=side)
+            else:
+                S.sekv_route(host, layer, q, inp.p[layer].contiguous(), tau, rb)
+                S.sekv_decode_attn(host, layer, q, rb, oh, ws, fetch_stream=side)
+            torch.cuda.synchronize()
+            assert int(rb.union_count.sum()) > 0
+            assert torch.equal(rb.mask, rbd.mask) and torch.equal(rb.union_count, rbd.union_count)
+            err = float((oh - od).abs().max() / od.abs().max())
+            log(f"[parity] host tier layer={layer} fused={fused} rel diff vs device={err:.2e}")
+            assert err <= 1e-6
