@@ -182,14 +182,34 @@ __device__ __forceinline__ void rows_load(const T* __restrict__ K, const T* __re
 // Coarse entries add lnn[row - bias0] to their scaled score and are skipped by
 // the heads whose bit is set in skip[row - bias0]; full-resolution rows pass
 // lnn = NULL.
+// this lane's EPL query dims of every head of the group, in registers
+template <typename T, int G>
+struct QSlice {
+  float v[G][Lanes<T>::EPL];
+  __device__ void load(const float (*qs)[kHeadDim]) {
+    using Ln = Lanes<T>;
+    const int sl = (threadIdx.x & 63) % Ln::LPR;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < Ln::EPL; e += 4) {
+        const float4 x = *(const float4*)&qs[h][sl * Ln::EPL + e];
+        v[h][e] = x.x;
+        v[h][e + 1] = x.y;
+        v[h][e + 2] = x.z;
+        v[h][e + 3] = x.w;
+      }
+  }
+};
+
 template <typename T, int G, int LOADS>
 __device__ __forceinline__ void rows_accumulate(const uint4 (&kr)[LOADS], const uint4 (&vr)[LOADS],
-                                                int r0, int r1, const float (*qs)[kHeadDim],
+                                                int r0, int r1, const QSlice<T, G>& q,
                                                 const float* lnn, const int* skip, int bias0,
                                                 RowState<T, G>& s) {
   using Ln = Lanes<T>;
   constexpr int EPL = Ln::EPL;
-  const int lane = threadIdx.x & 63, sub = lane / Ln::LPR, sl = lane % Ln::LPR;
+  const int lane = threadIdx.x & 63, sub = lane / Ln::LPR;
   float sc[LOADS][G];
 #pragma unroll
   for (int u = 0; u < LOADS; ++u) {
@@ -199,7 +219,7 @@ __device__ __forceinline__ void rows_accumulate(const uint4 (&kr)[LOADS], const 
     for (int h = 0; h < G; ++h) {
       float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) d += qs[h][sl * EPL + e] * kf[e];
+      for (int e = 0; e < EPL; ++e) d += q.v[h][e] * kf[e];
       sc[u][h] = group_sum<Ln::LPR>(d);
     }
     const int row = r0 + u * Ln::RPW + sub;
@@ -446,7 +466,8 @@ __device__ void zoom_span(const float* __restrict__ blk, int n, int r, unsigned 
 // together; U_V and the first half of V_V before the scores are formed; the
 // next 64 tokens' rows while the current ones are consumed; the second half
 // of V_V before the reduction of c.  Every load reads a clamped, valid
-// address; values past the span's rank or length are zeroed.
+// address; values past the span's rank or length are left in place and
+// excluded where they are used (an overwrite would wait for the load).
 // ---------------------------------------------------------------------------
 template <int G>
 __device__ void zoom_span32(const float* __restrict__ blk, int n, int r, unsigned hm,
@@ -461,7 +482,6 @@ __device__ void zoom_span32(const float* __restrict__ blk, int n, int r, unsigne
   const float* vv = blk + fv.vt(1);
   const float* uv = blk + fv.u(1);
   const float* sv = blk + fv.sigma(1);
-  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
   const int part = lane & 7, ci = lane >> 3;   // (A): component ci + 8 p, dims 16 part ..
   const int i4 = lane & 7, ts = lane >> 3;     // (C): components 4 i4 .., tokens ts + 8 m
   const int ic = min(4 * i4, r4 - 4);
@@ -475,42 +495,41 @@ __device__ void zoom_span32(const float* __restrict__ blk, int n, int r, unsigne
       va[p][c4] = *(const float4*)(vk + (size_t)i * kHeadDim + part * 16 + c4 * 4);
   }
   const int lr = min(lane, r - 1);
-  float skl = sk[lr], svl = sv[lr];
+  const float skl = sk[lr], svl = sv[lr];
   float4 ub[8];
   {
     const int tl = min(lane, n - 1);
 #pragma unroll
     for (int q = 0; q < 8; ++q) ub[q] = *(const float4*)(uk + (size_t)tl * r4 + 4 * min(q, nq - 1));
   }
-  if (lane >= r) skl = svl = 0.f;
-#pragma unroll
-  for (int p = 0; p < 4; ++p)
-    if (ci + 8 * p >= r)
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) va[p][c4] = z4;
-#pragma unroll
-  for (int q = 0; q < 8; ++q)
-    if (lane >= n || q >= nq) ub[q] = z4;
+  // No loaded value is overwritten here (that would make the wave wait for
+  // the load at once): clamped duplicates are excluded where they are used,
+  // by the rank or length guards below.
 
-  // (A) b_h[i] = sigma_K[i] (V_K^T q_h)[i]; components r..31 get 0
+  // (A) b_h[i] = sigma_K[i] (V_K^T q_h)[i] for the heads that zoomed the span
+  // (branches on hm are uniform over the wave); components r..31 get 0
+  float sg[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int i = ci + 8 * p;
-    float pa[G];
+    const float sgl = __shfl(skl, i, 64);
+    sg[p] = i < r ? sgl : 0.f;
+  }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+  for (int h = 0; h < G; ++h) {
+    if (!((hm >> h) & 1u)) continue;
+    float4 qv[4];
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) qv[c4] = *(const float4*)&qs[h][part * 16 + c4 * 4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
       float acc = 0.f;
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const float4 qv = *(const float4*)&qs[h][part * 16 + c4 * 4];
-        acc += va[p][c4].x * qv.x + va[p][c4].y * qv.y + va[p][c4].z * qv.z + va[p][c4].w * qv.w;
-      }
-      pa[h] = group_sum<8>(acc);
-    }
-    const float sg = __shfl(skl, i, 64);
-    if (part == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) ws.z.bsh[h][i] = pa[h] * sg;
+      for (int c4 = 0; c4 < 4; ++c4)
+        acc += va[p][c4].x * qv[c4].x + va[p][c4].y * qv[c4].y + va[p][c4].z * qv[c4].z +
+               va[p][c4].w * qv[c4].w;
+      acc = group_sum<8>(acc);
+      if (part == 0) ws.z.bsh[h][ci + 8 * p] = acc * sg[p];
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -519,9 +538,6 @@ __device__ void zoom_span32(const float* __restrict__ blk, int n, int r, unsigne
   float4 uc[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) uc[m] = *(const float4*)(uv + (size_t)min(ts + 8 * m, tn - 1) * r4 + ic);
-#pragma unroll
-  for (int m = 0; m < 8; ++m)
-    if (ts + 8 * m >= tn || 4 * i4 >= r4) uc[m] = z4;
   float2 vd[32];
 #pragma unroll
   for (int i = 0; i < 16; ++i) vd[i] = *(const float2*)(vv + (size_t)min(i, r - 1) * kHeadDim + 2 * lane);
@@ -540,6 +556,8 @@ __device__ void zoom_span32(const float* __restrict__ blk, int n, int r, unsigne
     float e[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+      e[h] = -INFINITY;
+      if (!((hm >> h) & 1u)) continue;
       float acc = 0.f;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -548,40 +566,36 @@ __device__ void zoom_span32(const float* __restrict__ blk, int n, int r, unsigne
           acc += ub[q].x * b.x + ub[q].y * b.y + ub[q].z * b.z + ub[q].w * b.w;
         }
       }
-      e[h] = (lane < tn && ((hm >> h) & 1u)) ? acc : -INFINITY;
+      if (lane < tn) e[h] = acc;
     }
     const int t1 = t0 + 64;
     if (t1 < n) {
       const int tl1 = min(t1 + lane, n - 1);
 #pragma unroll
       for (int q = 0; q < 8; ++q) ub[q] = *(const float4*)(uk + (size_t)tl1 * r4 + 4 * min(q, nq - 1));
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (t1 + lane >= n || q >= nq) ub[q] = z4;
     }
-    float corr[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+      if (!((hm >> h) & 1u)) continue;
       const float mx = wave_max(e[h]);
       const float mn = fmaxf(ms[h], mx);
-      corr[h] = (ms[h] == -INFINITY) ? 0.f : __expf(ms[h] - mn);
+      const float corr = (ms[h] == -INFINITY) ? 0.f : __expf(ms[h] - mn);
       const float p = (e[h] == -INFINITY) ? 0.f : __expf(e[h] - mn);
-      ls[h] = ls[h] * corr[h] + wave_sum(p);
+      ls[h] = ls[h] * corr + wave_sum(p);
       ms[h] = mn;
       ws.z.psh[lane][h] = p;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cacc[h][q] *= corr;
     }
     __builtin_amdgcn_wave_barrier();
     // (C) c_h[4 i4 ..] += sum over this lane's tokens of p_h U_V
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h) {
+      if (!((hm >> h) & 1u)) continue;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) cacc[h][q] *= corr[h];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int k = ts + 8 * m;
-      if (k < tn) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
+      for (int m = 0; m < 8; ++m) {
+        const int k = ts + 8 * m;
+        if (k < tn) {
           const float p = ws.z.psh[k][h];
           cacc[h][0] += p * uc[m].x;
           cacc[h][1] += p * uc[m].y;
@@ -595,9 +609,6 @@ __device__ void zoom_span32(const float* __restrict__ blk, int n, int r, unsigne
 #pragma unroll
       for (int m = 0; m < 8; ++m)
         uc[m] = *(const float4*)(uv + (size_t)(t1 + min(ts + 8 * m, tn1 - 1)) * r4 + ic);
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-        if (ts + 8 * m >= tn1 || 4 * i4 >= r4) uc[m] = z4;
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -606,21 +617,21 @@ __device__ void zoom_span32(const float* __restrict__ blk, int n, int r, unsigne
     for (int i = 16; i < 32; ++i)
       vd[i] = *(const float2*)(vv + (size_t)min(i, r - 1) * kHeadDim + 2 * lane);
   }
-  // reduce c over the 8 token lanes; sigma_V folded in
+  // reduce c over the 8 token lanes; sigma_V folded in (components at or past
+  // r hold values of clamped loads, never read by (D))
+  float sgv[4];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int q = 0; q < 4; ++q) sgv[q] = __shfl(svl, 4 * i4 + q, 64);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if (!((hm >> h) & 1u)) continue;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       cacc[h][q] += dpp<kDppRor8>(cacc[h][q]);
       cacc[h][q] += __shfl_xor(cacc[h][q], 16, 64);
       cacc[h][q] += __shfl_xor(cacc[h][q], 32, 64);
     }
-  float sgv[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) sgv[q] = __shfl(svl, 4 * i4 + q, 64);
-  if (ts == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
+    if (ts == 0)
       *(float4*)&ws.z.csh[h][4 * i4] = make_float4(cacc[h][0] * sgv[0], cacc[h][1] * sgv[1],
                                                    cacc[h][2] * sgv[2], cacc[h][3] * sgv[3]);
   }
@@ -632,10 +643,11 @@ __device__ void zoom_span32(const float* __restrict__ blk, int n, int r, unsigne
 #pragma unroll
   for (int h = 0; h < G; ++h) a[h][0] = a[h][1] = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    if (i < r) {
+  for (int h = 0; h < G; ++h) {
+    if (!((hm >> h) & 1u)) continue;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
+    for (int i = 0; i < 32; ++i) {
+      if (i < r) {
         const float w = ws.z.csh[h][i];
         a[h][0] += w * vd[i].x;
         a[h][1] += w * vd[i].y;
@@ -821,17 +833,18 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
 
   // ---- full-resolution rows and coarse entries; the state goes to LDS -------
   if (dense) {
+    QSlice<T, G> qv;
+    qv.load(s.qs);
     RowState<T, G> rs;
     rs.init();
-    rows_accumulate<T, G, DLOADS>(dk, dv, dr0, min(d1, dr0 + kRowBlock), s.qs, nullptr, nullptr,
-                                  0, rs);
+    rows_accumulate<T, G, DLOADS>(dk, dv, dr0, min(d1, dr0 + kRowBlock), qv, nullptr, nullptr, 0,
+                                  rs);
     for (int p0 = d0 + kWaves * kRowBlock; p0 < d1; p0 += kWaves * kRowBlock) {
       const int r0 = p0 + wid * kRowBlock, r1 = min(d1, r0 + kRowBlock);
       rows_load<T, DLOADS>(DK, DV, r0, r1, dk, dv);
-      rows_accumulate<T, G, DLOADS>(dk, dv, r0, r1, s.qs, nullptr, nullptr, 0, rs);
+      rows_accumulate<T, G, DLOADS>(dk, dv, r0, r1, qv, nullptr, nullptr, 0, rs);
     }
-    if (nj > 0)
-      rows_accumulate<T, G, CLOADS>(kr, vr, cr0, cr1, s.qs, a.lnn32 + j0, s.bits, j0, rs);
+    if (nj > 0) rows_accumulate<T, G, CLOADS>(kr, vr, cr0, cr1, qv, a.lnn32 + j0, s.bits, j0, rs);
     rows_finish<T, G>(rs);
     rows_store<T, G>(rs, s.rows_acc[wid], s.rows_m[wid], s.rows_l[wid]);
   } else if (lane < G) {
