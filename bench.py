@@ -61,7 +61,7 @@ def kernel_source_hash() -> str:
 def read_traffic(workload: str):
     """HBM traffic per attention launch from committed rocprofv3 --pmc
     summaries, only if they were taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_attn_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_layer_kernel_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -246,7 +246,9 @@ def main():
     torch.cuda.synchronize()
     attn_us = [a.elapsed_time(b) * 1e3 for row in evs for (a, b) in row]
     attn_us_mean = float(np.mean(attn_us))
-    attn_bytes_meas = float(zoom_bytes[:n_meas].mean()) / L + resident_layer
+    # zoom_bytes[step, layer] is per launch already: its mean over the
+    # measured steps' launches plus the resident bytes every launch reads
+    attn_bytes_meas = float(zoom_bytes[:n_meas].mean()) + resident_layer
     attn_gbs = attn_bytes_meas / (attn_us_mean * 1e-6) / 1e9
     log(f"layer launch: {attn_us_mean:.2f} us avg, {attn_bytes_meas / 1e6:.2f} MB algorithmic "
         f"-> {attn_gbs:.0f} GB/s")

@@ -244,3 +244,68 @@ def test_host_tier_matches_device_tier(S):
             err = float((oh - od).abs().max() / od.abs().max())
             log(f"[parity] host tier layer={layer} fused={fused} rel diff vs device={err:.2e}")
             assert err <= 1e-6
+
+
+@pytest.mark.parametrize("layer,kv_head", [(0, 3), (31, 6)])
+def test_full_size_sampled_parity(S, layer, kv_head):
+    """The Llama-3-8B-shape workload at full size (32 layers, 131072 tokens,
+    bf16), through the single-launch call the bench times: the whole span
+    table bit-exact, and for one sampled (layer, KV head) the oracle rebuilds
+    that group from the same inputs and checks its means, summaries, sampled
+    factors, the zoom masks and lists of its query heads and their outputs."""
+    wl = synth.workload("llama3_8b_128k")
+    seed = synth.default_seed(wl)
+    log(f"[parity] full size layer={layer} kv_head={kv_head}")
+    inp = Inputs(wl, seed)
+    cache = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    s64 = to64(inp.s)
+    seg = O.segment(s64, wl.window, wl.alpha, wl.min_span_len)
+
+    class One:  # the oracle side for a single group
+        pass
+    orc = One()
+    orc.wl, orc.seg = wl, seg
+    g = wl.group
+    w = to64(inp.w[layer])
+    gc = O.build_group(seg, s64, to64(inp.k[layer, kv_head]), to64(inp.v[layer, kv_head]),
+                       {h: w[h] for h in range(kv_head * g, kv_head * g + g)},
+                       inp.ranks[layer, kv_head].cpu().numpy(), wl.kv_dtype, wl.max_rank)
+    orc.groups = {layer: {kv_head: gc}}
+    compare_spans(cache, orc)
+    nmis, worst = compare_group(cache, orc, layer, kv_head, n_factor_checks=12)
+    log(f"[parity] full size: storage mismatches {nmis}, factor rel err {worst:.2e}")
+
+    # thresholds: the group's first head zooms ~20% of spans, the others ~1%
+    # (quantiles of the oracle's gate), every other head of the layer 0.5
+    q = inp.query(7)[layer]
+    heads = list(range(kv_head * g, kv_head * g + g))
+    pr = to64(inp.p[layer])
+    ll = O.span_log_len(seg)
+    tau = torch.full((wl.n_q_heads,), 0.5)
+    for i, h in enumerate(heads):
+        p, _ = O.route_head(to64(q[h]), pr[h], gc.summary[h], ll, wl.gamma, 2.0)
+        tau[h] = float(np.quantile(p, 0.8 if i == 0 else 0.99))
+    tau = tau.cuda()
+    rb, o = run_gpu_layer(S, cache, layer, q, inp.p[layer], tau, fused=True)
+    qn, tn = to64(q), to64(tau)
+    route = O.route_layer(qn[heads[0]:heads[-1] + 1], pr[heads[0]:heads[-1] + 1], tn[heads[0]:heads[-1] + 1],
+                          {i: gc.summary[h] for i, h in enumerate(heads)}, seg, wl.gamma, 1)
+    mask = rb.mask.cpu().numpy().astype(bool)[heads[0]:heads[-1] + 1, :seg.n_compressed]
+    tie = np.abs(route.prob - tn[heads[0]:heads[-1] + 1, None]) < 1e-5
+    assert np.array_equal(mask[~tie], route.mask[~tie])
+    if not tie.any():
+        cnt, lst = rb.count.cpu().numpy(), rb.list.cpu().numpy()
+        for i, h in enumerate(heads):
+            assert lst[h, :cnt[h]].tolist() == route.lists[i].tolist()
+        uc, ul = rb.union_count.cpu().numpy(), rb.union_list.cpu().numpy()
+        assert ul[kv_head, :uc[kv_head]].tolist() == route.unions[0].tolist()
+    og = to64(o)
+    worst = 0.0
+    for i, h in enumerate(heads):
+        if tie[i].any():
+            continue
+        ref = O.mixed_attention(qn[h], gc, seg, route.mask[i])
+        worst = max(worst, rel_err(og[h], ref))
+    log(f"[parity] full size: zoom {route.mask.mean(axis=1).round(3).tolist()} ties {int(tie.sum())} "
+        f"attention err {worst:.2e}")
+    assert worst <= TOL["bf16"]
