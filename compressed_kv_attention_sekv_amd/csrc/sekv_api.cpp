@@ -141,6 +141,7 @@ struct sekv_cache {
   // decode: per-KV-head tickets of the layer kernel (zero between launches)
   uint32_t* tickets = nullptr;
   uint32_t* chunk_bits = nullptr;  // [Hkv][n_work][kListWords] zoom bit masks of each chunk
+  float* zero_block = nullptr;     // kZeroBlockFloats zeros: a valid source for idle prefetches
   LayerGeom geom{};
   hipEvent_t ev_route = nullptr, ev_fetch = nullptr;
 
@@ -328,6 +329,8 @@ static sekv_status build_impl(const sekv_config* cfg, int32_t n_tokens, const fl
   SEKV_HIP(hipMemsetAsync(c->tickets, 0, (size_t)Hkv * 4, st));
   if ((r = c->alloc(&c->chunk_bits, (size_t)Hkv * c->geom.n_work * kListWords * 4, "chunk bits")))
     return r;
+  if ((r = c->alloc(&c->zero_block, (size_t)kZeroBlockFloats * 4, "zero block"))) return r;
+  SEKV_HIP(hipMemsetAsync(c->zero_block, 0, (size_t)kZeroBlockFloats * 4, st));
   SEKV_HIP(hipEventCreateWithFlags(&c->ev_route, hipEventDisableTiming));
   SEKV_HIP(hipEventCreateWithFlags(&c->ev_fetch, hipEventDisableTiming));
   SEKV_HIP(hipStreamSynchronize(st));
@@ -498,6 +501,7 @@ LayerArgs layer_args(const sekv_cache* c, int32_t layer, const float* q, const f
   a.part = (float*)ws;
   a.tickets = c->tickets;
   a.chunk_bits = c->chunk_bits;
+  a.zero_block = c->zero_block;
   return a;
 }
 

@@ -33,7 +33,8 @@ namespace sekv {
 // small helpers
 // ---------------------------------------------------------------------------
 // Cross-lane moves inside a row of 16 lanes go through DPP (an ALU operand
-// modifier); only moves between rows use the LDS permute unit.
+// modifier), moves between rows through the gfx950 permlane swaps; neither
+// touches the LDS permute unit.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
@@ -50,6 +51,26 @@ constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within 8
 constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within 16
 constexpr int kDppRor8 = 0x128;       // lane i <- (i + 8) mod 16 (= i xor 8)
 
+// The values of a lane and of its partner 16 (or 32) lanes away, in a fixed
+// order: lo from the lower row (half), hi from the upper one, the same on
+// both lanes.  v_permlane16_swap exchanges the odd rows of one operand with
+// the even rows of the other; applied to one value twice it yields rows
+// (x0, x0, x2, x2) and (x1, x1, x3, x3).  v_permlane32_swap does the same
+// with the two halves of the wave.  No LDS access is involved.
+struct Pair { float lo, hi; };
+template <int OFF>
+__device__ __forceinline__ Pair pair_xor(float x) {
+  static_assert(OFF == 16 || OFF == 32, "row or half exchange");
+  const uint32_t u = __float_as_uint(x);
+  const auto r = OFF == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                           : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float xor16_sum(float x) { const Pair p = pair_xor<16>(x); return p.lo + p.hi; }
+__device__ __forceinline__ float xor32_sum(float x) { const Pair p = pair_xor<32>(x); return p.lo + p.hi; }
+__device__ __forceinline__ double xor16_sum(double x) { return x + __shfl_xor(x, 16, 64); }
+__device__ __forceinline__ double xor32_sum(double x) { return x + __shfl_xor(x, 32, 64); }
+
 // sum over aligned groups of N lanes (N = 4, 8, 16, 32, 64); every lane of a
 // group receives the group's total
 template <int N, typename F>
@@ -59,17 +80,29 @@ __device__ __forceinline__ F group_sum(F x) {
   x += dpp<kDppXor2>(x);
   if (N >= 8) x += dpp<kDppHalfMirror>(x);
   if (N >= 16) x += dpp<kDppMirror>(x);
-  if (N >= 32) x += __shfl_xor(x, 16, 64);
-  if (N >= 64) x += __shfl_xor(x, 32, 64);
+  if (N >= 32) x = xor16_sum(x);
+  if (N >= 64) x = xor32_sum(x);
   return x;
 }
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float readlane(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+// wave-wide max / sum, the total on every lane
 __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp<kDppXor1>(x));
   x = fmaxf(x, dpp<kDppXor2>(x));
   x = fmaxf(x, dpp<kDppHalfMirror>(x));
   x = fmaxf(x, dpp<kDppMirror>(x));
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  return fmaxf(x, __shfl_xor(x, 32, 64));
+  Pair p = pair_xor<16>(x);
+  x = fmaxf(p.lo, p.hi);
+  p = pair_xor<32>(x);
+  return fmaxf(p.lo, p.hi);
 }
 __device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
 // weights of two online-softmax states under their common max; -inf = empty
@@ -104,27 +137,32 @@ __device__ __forceinline__ void unpack16(const uint4& raw, float* out, float) {
 // ---------------------------------------------------------------------------
 // shared memory of the layer kernel
 // ---------------------------------------------------------------------------
+// scratch of one zoomed span of any rank
+template <int G> struct ZoomScratchAny {
+  float bsh[G][kMaxRank];
+  float csh[G][kMaxRank];
+  float psh[64][G];
+};
+// an online softmax state of G heads: (m, l, acc[d]) per head
+template <int G> struct WaveState {
+  float acc[G][kHeadDim];
+  float m[G];
+  float l[G];
+};
 template <int G>
 struct alignas(16) WaveScratch {
-  union {
-    struct {                       // one zoomed span at a time
-      float bsh[G][kMaxRank];      // b_h
-      float csh[G][kMaxRank];      // c_h
-      float psh[64][G];            // p of the current 64 tokens
-    } z;
-    struct {                       // the wave's zoomed-span state, once its spans are done
-      float acc[G][kHeadDim];
-      float m[G];
-      float l[G];
-    } st;
-  };
+  WaveState<G> st;                 // the wave's state before and after its spans
 };
+
+// Rows of V_K a wave can stage in LDS for its next zoomed span: all 32 while
+// two workgroups still fit in a CU's 160 KB, fewer for large groups.
+template <int G> constexpr int stage_rows() { return G <= 5 ? 32 : 24; }
+// a stage: SR rows of V_K, then 64 floats of sigma_K and 64 of sigma_V
+template <int SR> constexpr int stage_floats() { return SR * kHeadDim + 128; }
 
 template <int G>
 struct alignas(16) Smem {
   float qs[G][kHeadDim];           // query * 1/sqrt(d)
-  float qu[G][kHeadDim];           // query as given (routing)
-  double qt[G][kMaxRouteDim];      // P_h q_h
   uint64_t m_off[kChunk];          // factor block of span j0 + i, relative to the pool
   int m_n[kChunk], m_r[kChunk];    // its length and retained rank
   int bits[kChunk];                // heads of the group that zoom span j0 + i
@@ -132,9 +170,20 @@ struct alignas(16) Smem {
   int nz;
   int last;
   int wc[kListWords][kWaves];      // list compaction: per-wave counts
-  float rows_acc[kWaves][G][kHeadDim];   // each wave's state over rows and coarse entries
-  float rows_m[kWaves][G], rows_l[kWaves][G];
-  WaveScratch<G> w[kWaves];
+  union {
+    struct {                       // routing (dead once the gates are taken)
+      float qu[G][kHeadDim];       // query as given
+      double qt[G][kMaxRouteDim];  // P_h q_h
+    } rt;
+    WaveScratch<G> w[kWaves];      // written from the rows phase on
+  };
+};
+// Per wave: V_K of its next zoomed span, written by LDS DMA while the current
+// span is processed, or the scratch of a span of rank > 32.  An array of its
+// own, so the compiler can tell the DMA's LDS writes from every other LDS
+// access and waits for them only where the stage is read.
+template <int G> struct alignas(16) Stage {
+  float v[kWaves][stage_floats<stage_rows<G>()>()];
 };
 
 // ---------------------------------------------------------------------------
@@ -205,8 +254,8 @@ struct QSlice {
 template <typename T, int G, int LOADS>
 __device__ __forceinline__ void rows_accumulate(const uint4 (&kr)[LOADS], const uint4 (&vr)[LOADS],
                                                 int r0, int r1, const QSlice<T, G>& q,
-                                                const float* lnn, const int* skip, int bias0,
-                                                RowState<T, G>& s) {
+                                                const float (&bias)[LOADS], const int* skip,
+                                                int skip0, RowState<T, G>& s) {
   using Ln = Lanes<T>;
   constexpr int EPL = Ln::EPL;
   const int lane = threadIdx.x & 63, sub = lane / Ln::LPR;
@@ -224,15 +273,10 @@ __device__ __forceinline__ void rows_accumulate(const uint4 (&kr)[LOADS], const 
     }
     const int row = r0 + u * Ln::RPW + sub;
     const bool valid = row < r1;
-    float bias = 0.f;
-    int sk = 0;
-    if (lnn != nullptr && valid) {
-      bias = lnn[row - bias0];
-      sk = skip[row - bias0];
-    }
+    const int sk = (skip != nullptr && valid) ? skip[row - skip0] : 0;
 #pragma unroll
     for (int h = 0; h < G; ++h)
-      sc[u][h] = (valid && !((sk >> h) & 1)) ? sc[u][h] + bias : -INFINITY;
+      sc[u][h] = (valid && !((sk >> h) & 1)) ? sc[u][h] + bias[u] : -INFINITY;
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -258,26 +302,31 @@ __device__ __forceinline__ void rows_accumulate(const uint4 (&kr)[LOADS], const 
   }
 }
 
-template <typename T, int G>
-__device__ __forceinline__ void rows_finish(RowState<T, G>& s) {
+// merge the states of lanes OFF apart (both lanes end with the same state)
+template <int OFF, typename T, int G>
+__device__ __forceinline__ void rows_merge_xor(RowState<T, G>& s) {
   using Ln = Lanes<T>;
 #pragma unroll
-  for (int off = Ln::LPR; off < 64; off <<= 1) {
+  for (int h = 0; h < G; ++h) {
+    const Pair m = pair_xor<OFF>(s.m[h]);
+    const Pair l = pair_xor<OFF>(s.l[h]);
+    float w1, w2;
+    const float M = merge_w(m.lo, m.hi, w1, w2);
+    s.l[h] = l.lo * w1 + l.hi * w2;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(s.m[h], off, 64);
-      const float lo = __shfl_xor(s.l[h], off, 64);
-      float w1, w2;
-      const float M = merge_w(s.m[h], mo, w1, w2);
-      s.l[h] = s.l[h] * w1 + lo * w2;
-#pragma unroll
-      for (int e = 0; e < Ln::EPL; ++e) {
-        const float ao = __shfl_xor(s.acc[h][e], off, 64);
-        s.acc[h][e] = s.acc[h][e] * w1 + ao * w2;
-      }
-      s.m[h] = M;
+    for (int e = 0; e < Ln::EPL; ++e) {
+      const Pair x = pair_xor<OFF>(s.acc[h][e]);
+      s.acc[h][e] = x.lo * w1 + x.hi * w2;
     }
+    s.m[h] = M;
   }
+}
+
+template <typename T, int G>
+__device__ __forceinline__ void rows_finish(RowState<T, G>& s) {
+  static_assert(Lanes<T>::LPR == 16 || Lanes<T>::LPR == 32, "row slots are 16 or 32 lanes apart");
+  if (Lanes<T>::LPR == 16) rows_merge_xor<16>(s);
+  rows_merge_xor<32>(s);
 }
 
 template <typename T, int G>
@@ -306,7 +355,7 @@ __device__ __forceinline__ void rows_store(const RowState<T, G>& s, float (*acc)
 // ---------------------------------------------------------------------------
 template <int G>
 __device__ void zoom_span(const float* __restrict__ blk, int n, int r, unsigned hm,
-                          const float (*qs)[kHeadDim], WaveScratch<G>& ws, float* zm, float* zl,
+                          const float (*qs)[kHeadDim], ZoomScratchAny<G>& zs, float* zm, float* zl,
                           float (*za)[2]) {
   const int lane = threadIdx.x & 63;
   const FactorView fv(r, n);
@@ -345,14 +394,14 @@ __device__ void zoom_span(const float* __restrict__ blk, int n, int r, unsigned 
       if (part == 0 && i < r) {
         const float sg = sk[i];
 #pragma unroll
-        for (int h = 0; h < G; ++h) ws.z.bsh[h][i] = pa[h] * sg;
+        for (int h = 0; h < G; ++h) zs.bsh[h][i] = pa[h] * sg;
       }
     }
     // padding components and the value-side coefficients start at zero
     for (int idx = lane; idx < G * r4; idx += 64) {
       const int h = idx / r4, i = idx % r4;
-      if (i >= r) ws.z.bsh[h][i] = 0.f;
-      ws.z.csh[h][i] = 0.f;
+      if (i >= r) zs.bsh[h][i] = 0.f;
+      zs.csh[h][i] = 0.f;
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -375,7 +424,7 @@ __device__ void zoom_span(const float* __restrict__ blk, int n, int r, unsigned 
         const float4 u = ur[i4];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const float4 b = *(const float4*)&ws.z.bsh[h][4 * i4];
+          const float4 b = *(const float4*)&zs.bsh[h][4 * i4];
           e[h] += u.x * b.x + u.y * b.y + u.z * b.z + u.w * b.w;
         }
       }
@@ -390,7 +439,7 @@ __device__ void zoom_span(const float* __restrict__ blk, int n, int r, unsigned 
       const float p = (e[h] == -INFINITY) ? 0.f : __expf(e[h] - mn);
       ls[h] = ls[h] * corr[h] + wave_sum(p);
       ms[h] = mn;
-      ws.z.psh[lane][h] = p;
+      zs.psh[lane][h] = p;
     }
     __builtin_amdgcn_wave_barrier();
     const int tn = min(64, n - t0);
@@ -407,7 +456,7 @@ __device__ void zoom_span(const float* __restrict__ blk, int n, int r, unsigned 
           const float4 u = *(const float4*)(uv + (size_t)(t0 + k) * r4 + i);
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            const float p = ws.z.psh[k][h];
+            const float p = zs.psh[k][h];
             c4[h][0] += p * u.x;
             c4[h][1] += p * u.y;
             c4[h][2] += p * u.z;
@@ -420,14 +469,13 @@ __device__ void zoom_span(const float* __restrict__ blk, int n, int r, unsigned 
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           c4[h][q] += dpp<kDppRor8>(c4[h][q]);
-          c4[h][q] += __shfl_xor(c4[h][q], 16, 64);
-          c4[h][q] += __shfl_xor(c4[h][q], 32, 64);
+          c4[h][q] = xor32_sum(xor16_sum(c4[h][q]));
         }
       if (ts == 0 && i < r4) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) ws.z.csh[h][i + q] = ws.z.csh[h][i + q] * corr[h] + c4[h][q];
+          for (int q = 0; q < 4; ++q) zs.csh[h][i + q] = zs.csh[h][i + q] * corr[h] + c4[h][q];
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -442,7 +490,7 @@ __device__ void zoom_span(const float* __restrict__ blk, int n, int r, unsigned 
     const float sg = sv[i];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float w = sg * ws.z.csh[h][i];
+      const float w = sg * zs.csh[h][i];
       a[h][0] += w * x.x;
       a[h][1] += w * x.y;
     }
@@ -461,86 +509,273 @@ __device__ void zoom_span(const float* __restrict__ blk, int n, int r, unsigned 
 }
 
 // ---------------------------------------------------------------------------
-// The same for r <= 32, with the span's loads issued ahead of their use and
-// at most ~96 registers of them in flight: V_K and the first 64 rows of U_K
-// together; U_V and the first half of V_V before the scores are formed; the
-// next 64 tokens' rows while the current ones are consumed; the second half
-// of V_V before the reduction of c.  Every load reads a clamped, valid
-// address; values past the span's rank or length are left in place and
-// excluded where they are used (an overwrite would wait for the load).
+// Zoomed spans of rank <= 32, processed by one wave as a pipeline over its
+// list of spans.  While span i is processed, the loads of span i + 1 are in
+// flight: its V_K by LDS DMA into the wave's stage (issued once phase (A) of
+// span i has read the stage), its first 64 rows of U_K into the registers ub
+// (issued once span i's last rows there are consumed).  Span i's own U_V and
+// V_V, needed last, are loaded at its start, ahead of all of these.
+//
+// Loads complete in issue order and the wait for one load is a count of the
+// loads issued after it, so every wave issues the same loads whatever it has
+// to prefetch: a wave with no next span prefetches its current one again, or
+// the cache's zero block.  The compiler then counts exactly, and no wait for
+// a span's own data also waits for the next span's.  Every load reads a
+// clamped, valid address; values past a span's rank or length are left in
+// place and excluded where they are used (an overwrite would wait for the load).
 // ---------------------------------------------------------------------------
+struct SpanRef {        // a zoomed span, the same on every lane of the wave
+  const float* blk;     // its factor block
+  int n, r;
+  unsigned hm;          // heads of the group that zoom it
+};
+
 template <int G>
-__device__ void zoom_span32(const float* __restrict__ blk, int n, int r, unsigned hm,
-                            const float (*qs)[kHeadDim], WaveScratch<G>& ws, float* zm, float* zl,
-                            float (*za)[2]) {
+__device__ __forceinline__ SpanRef span_ref(const Smem<G>& s, const float* pool, int jl) {
+  SpanRef sp;
+  jl = uniform(jl);
+  sp.blk = pool + uniform64(s.m_off[jl]);
+  sp.n = uniform(s.m_n[jl]);
+  sp.r = uniform(s.m_r[jl]);
+  sp.hm = (unsigned)uniform(s.bits[jl]);
+  return sp;
+}
+
+// A span's V_K (r rows of d floats at the start of its block) and its sigma_K
+// and sigma_V into a stage: SR rows, then 64 floats of sigma_K and 64 of
+// sigma_V (entry i holds sigma[min(i, r4 - 1)]; entries r .. r4 - 1 are the
+// block's zero padding).  Each row instruction moves 1 KB (two rows) straight
+// from memory to LDS, lane l writing bytes [16 l, 16 l + 16) of it; always
+// SR / 2 of them, those past the span's rows copying its last two rows again
+// (an odd r also moves the 512 bytes after V_K, still inside the block).
+//
+// The DMA instructions are written as inline assembly.  The compiler then
+// does not count them among the wave's outstanding loads: its own waits for
+// registers loaded before a DMA stay exact (with the DMA counted, every such
+// wait becomes a wait for all loads, the DMA of the next span included), and
+// a DMA it does not see only makes those waits stricter, never too weak.  The
+// waits for the DMA itself are explicit: wait_lds() before a stage is
+// overwritten, wait_vm<48>() before it is read.  M0 holds the LDS address of
+// each instruction and is restored after it.
+// the LDS address of p, in a scalar register (p is the same on every lane)
+__device__ __forceinline__ uint32_t lds_addr(const float* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float*)p);
+}
+__device__ __forceinline__ void dma_x4(const float* g, const float* lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr(lds)), "v"(g)
+      : "memory");
+}
+__device__ __forceinline__ void dma_x1(const float* g, const float* lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr(lds)), "v"(g)
+      : "memory");
+}
+template <int SR>
+__device__ __forceinline__ void stage_vk(const SpanRef& sp, float* stage) {
   const int lane = threadIdx.x & 63;
+  const int nk = (sp.r + 1) >> 1;
+  const FactorView fv(sp.r, sp.n);
+#pragma unroll
+  for (int k = 0; k < SR / 2; ++k) dma_x4(sp.blk + min(k, nk - 1) * 256 + lane * 4, stage + k * 256);
+  const int si = min(lane, fv.r4 - 1);
+  dma_x1(sp.blk + fv.sigma(0) + si, stage + SR * kHeadDim);
+  dma_x1(sp.blk + fv.sigma(1) + si, stage + SR * kHeadDim + 64);
+}
+
+// LDS reads of this wave complete before the stage is overwritten by DMA
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// token rows t0 .. t0 + 63 of U (n rows of r4 floats), lane = token: 8
+// 16-byte loads of components 4 q .. 4 q + 3 (clamped to valid rows and
+// components)
+template <int NQ, int M>
+__device__ __forceinline__ void load_u_tile(const float* u, int n, int r4, int t0, float4 (&x)[M]) {
+  static_assert(NQ <= M, "tile registers");
+  const int lane = threadIdx.x & 63;
+  const int nq = r4 / 4, tl = min(t0 + lane, n - 1);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) x[q] = *(const float4*)(u + (size_t)tl * r4 + 4 * min(q, nq - 1));
+}
+// what a wave prefetches of its next span into registers: the first rows of
+// U_K (always 8 loads, so the waits that count them stay exact)
+__device__ __forceinline__ void prefetch_span(const SpanRef& sp, float4 (&ub)[8]) {
+  const FactorView fv(sp.r, sp.n);
+  load_u_tile<8>(sp.blk + fv.u(0), sp.n, fv.r4, 0, ub);
+}
+
+// Keep the loads issued so far ahead of everything after (the waits below
+// count loads in issue order).
+__device__ __forceinline__ void issue_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Wait until at most N of this wave's vector memory operations (loads, and
+// LDS DMA) are outstanding.  Operations complete in issue order, so this
+// waits for everything issued before the last N.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Sum over the 64 lanes of p * u[i] for the RC components i of u (u[q] holds
+// components 4 q .. 4 q + 3 of the lane's row), left as components 4 g + k
+// (k < 4) in out[k] of the lanes GL g .. GL g + GL - 1, GL = 256 / RC: the
+// halves of the wave swap RC / 2 components, rows RC / 4, then (RC 32) lanes
+// 8 apart 4 and each group of 8 lanes sums, or (RC 16) each row sums.
+template <int RC>
+__device__ __forceinline__ void reduce_scatter(float p, const float4 (&u)[RC / 4], float (&out)[4]) {
+  static_assert(RC == 16 || RC == 32, "rank class");
+  constexpr int H = RC / 2;
+  const int lane = threadIdx.x & 63;
+  // lanes 0..31 keep the first RC / 2 components, lanes 32..63 the others
+  // (each product formed where it is swapped)
+  float y[H];
+#pragma unroll
+  for (int q = 0; q < RC / 8; ++q) {
+    const float lo[4] = {p * u[q].x, p * u[q].y, p * u[q].z, p * u[q].w};
+    const float4 uh = u[q + RC / 8];
+    const float hi[4] = {p * uh.x, p * uh.y, p * uh.z, p * uh.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo[k]), __float_as_uint(hi[k]),
+                                                      false, false);
+      y[4 * q + k] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    }
+  }
+  // even rows keep the first half of theirs, odd rows the second
+  float z[H / 2];
+#pragma unroll
+  for (int i = 0; i < H / 2; ++i) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(y[i]),
+                                                    __float_as_uint(y[i + H / 2]), false, false);
+    z[i] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  }
+  if constexpr (RC == 32) {
+    // lanes 0..7 of a row keep the first 4 of their 8, lanes 8..15 the last 4
+    const bool hi8 = (lane & 8) != 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float keep = hi8 ? z[k + 4] : z[k];
+      const float send = hi8 ? z[k] : z[k + 4];
+      out[k] = group_sum<8>(keep + dpp<kDppRor8>(send));
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out[k] = group_sum<16>(z[k]);
+  }
+}
+
+// One span of the pipeline, for ranks up to RC (16 or 32): loads are sized
+// to RC (U rows of RC / 4 16-byte pieces, V_V in RC / 2 16-byte loads of two
+// rows each).  On entry ub holds the span's first rows of U_K and, if
+// r <= SR, the stage holds (or is receiving) its V_K; on return ub holds the
+// first rows of U_K of `nxp` (8 loads, whatever its rank) and the stage
+// receives the V_K of `nxs` (the next span, or a stand-in when it has none of
+// the kind).
+//
+//  (A) b_h[i] = sigma_K[i] (V_K q_h)[i]: lane (part, ci) sums 16 dims of rows
+//      ci + 8 p; b goes to the wave's scratch scr[h][0..32), which (B) reads
+//      broadcast.
+//  (B) e[t] = U_K[t] . b_h with lane = token t, then the online softmax.
+//  (C) c_h[i] = sum_t p_h[t] U_V[t][i]: each lane multiplies its token's row,
+//      and a reduce-scatter over the 64 lanes leaves components 4 g .. 4 g + 3
+//      in lanes GL g .. GL g + GL - 1.
+//  (D) a_h = V_V^T (sigma_V c_h) with sigma_V c_h read out as scalars; lane
+//      (half, dq) sums rows 2 k + half of dims 4 dq .. 4 dq + 3, the two
+//      halves of the wave are added, and scr[h] turns the result into the
+//      state's layout (dims 2 lane, 2 lane + 1).
+template <int G, int SR, int RC>
+__device__ void zoom_span32(const SpanRef& cu, const SpanRef& nxp, const SpanRef& nxs,
+                            float4 (&ub)[8], float* stage, float (*scr)[kHeadDim],
+                            const float (*qs)[kHeadDim], float* zm, float* zl, float (*za)[2]) {
+  static_assert(RC == 16 || RC == 32, "rank class");
+  constexpr int UQ = RC / 4;          // 16-byte pieces of a U row
+  constexpr int VK = RC / 2;          // 16-byte loads of V_V
+  constexpr int GL = 64 / (RC / 4);   // lanes holding each 4 components of c
+  const int lane = threadIdx.x & 63;
+  const int n = cu.n, r = cu.r;
+  const unsigned hm = cu.hm;
   const FactorView fv(r, n);
   const int r4 = fv.r4, nq = r4 / 4;
-  const float* vk = blk + fv.vt(0);
-  const float* uk = blk + fv.u(0);
-  const float* sk = blk + fv.sigma(0);
-  const float* vv = blk + fv.vt(1);
-  const float* uv = blk + fv.u(1);
-  const float* sv = blk + fv.sigma(1);
+  const float* vk = cu.blk + fv.vt(0);
+  const float* vv = cu.blk + fv.vt(1);
   const int part = lane & 7, ci = lane >> 3;   // (A): component ci + 8 p, dims 16 part ..
-  const int i4 = lane & 7, ts = lane >> 3;     // (C): components 4 i4 .., tokens ts + 8 m
-  const int ic = min(4 * i4, r4 - 4);
+  const int half = lane >> 5, dq = lane & 31;  // (D): rows 2 k + half, dims 4 dq ..
+  const int cg = lane / GL;                    // after (C): components 4 cg ..
+  const bool staged = SR >= 32 || r <= SR;     // always, when the stage holds 32 rows
 
-  float4 va[4][4];
+  // this span's own loads, needed last: the first rows of U_V, all of V_V
+  float4 uc[UQ];
+  load_u_tile<UQ>(cu.blk + fv.u(1), n, r4, 0, uc);
+  float4 vd[VK];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int i = min(ci + 8 * p, r - 1);
+  for (int k = 0; k < VK; ++k)
+    vd[k] = *(const float4*)(vv + (size_t)min(2 * k + half, r - 1) * kHeadDim + 4 * dq);
+  float4 va[4][4];   // V_K from memory, only when it is not staged
+  if (!staged) {
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4)
-      va[p][c4] = *(const float4*)(vk + (size_t)i * kHeadDim + part * 16 + c4 * 4);
+    for (int p = 0; p < 4; ++p) {
+      const int i = min(ci + 8 * p, r - 1);
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4)
+        va[p][c4] = *(const float4*)(vk + (size_t)i * kHeadDim + part * 16 + c4 * 4);
+    }
   }
-  const int lr = min(lane, r - 1);
-  const float skl = sk[lr], svl = sv[lr];
-  float4 ub[8];
-  {
-    const int tl = min(lane, n - 1);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) ub[q] = *(const float4*)(uk + (size_t)tl * r4 + 4 * min(q, nq - 1));
-  }
-  // No loaded value is overwritten here (that would make the wave wait for
-  // the load at once): clamped duplicates are excluded where they are used,
-  // by the rank or length guards below.
 
-  // (A) b_h[i] = sigma_K[i] (V_K^T q_h)[i] for the heads that zoomed the span
-  // (branches on hm are uniform over the wave); components r..31 get 0
+  // sigma_K of the lane's components in (A) (ci + 8 p) and sigma_V of its
+  // components after (C) (4 cg ..), from the stage.  Its DMA was followed by
+  // the 8 loads of U_K rows prefetched for this span and the UQ + VK above,
+  // so once at most that many are outstanding the DMA has landed.
+  issue_fence();
+  wait_vm<8 + UQ + VK>();
   float sg[4];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int i = ci + 8 * p;
-    const float sgl = __shfl(skl, i, 64);
-    sg[p] = i < r ? sgl : 0.f;
-  }
+  for (int p = 0; p < 4; ++p) sg[p] = stage[SR * kHeadDim + ci + 8 * p];
+  const float4 svg = *(const float4*)(stage + SR * kHeadDim + 64 + 4 * cg);
+
+  // (A) components at or past r get exactly 0 (a stage row past r may hold
+  // anything)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     if (!((hm >> h) & 1u)) continue;
-    float4 qv[4];
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) qv[c4] = *(const float4*)&qs[h][part * 16 + c4 * 4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < RC / 8; ++p) {
+      const int i = ci + 8 * p;
       float acc = 0.f;
+      if (8 * p < r) {
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4)
-        acc += va[p][c4].x * qv[c4].x + va[p][c4].y * qv[c4].y + va[p][c4].z * qv[c4].z +
-               va[p][c4].w * qv[c4].w;
-      acc = group_sum<8>(acc);
-      if (part == 0) ws.z.bsh[h][ci + 8 * p] = acc * sg[p];
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const float4 x =
+              staged ? *(const float4*)(stage + i * kHeadDim + part * 16 + c4 * 4) : va[p][c4];
+          const float4 qv = *(const float4*)&qs[h][part * 16 + c4 * 4];
+          acc += x.x * qv.x + x.y * qv.y + x.z * qv.z + x.w * qv.w;
+        }
+        acc = group_sum<8>(acc);
+      }
+      if (part == 0) scr[h][i] = i < r ? acc * sg[p] : 0.f;
     }
   }
+  // the stage is free: the next span's V_K goes in while this one proceeds
+  wait_lds();
+  issue_fence();
+  stage_vk<SR>(nxs, stage);
+  issue_fence();
   __builtin_amdgcn_wave_barrier();
-
-  int tn = min(64, n);
-  float4 uc[8];
-#pragma unroll
-  for (int m = 0; m < 8; ++m) uc[m] = *(const float4*)(uv + (size_t)min(ts + 8 * m, tn - 1) * r4 + ic);
-  float2 vd[32];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) vd[i] = *(const float2*)(vv + (size_t)min(i, r - 1) * kHeadDim + 2 * lane);
 
   float ms[G], ls[G], cacc[G][4];
 #pragma unroll
@@ -548,32 +783,26 @@ __device__ void zoom_span32(const float* __restrict__ blk, int n, int r, unsigne
     ms[h] = -INFINITY;
     ls[h] = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) cacc[h][q] = 0.f;
+    for (int k = 0; k < 4; ++k) cacc[h][k] = 0.f;
   }
-  for (int t0 = 0; t0 < n; t0 += 64) {
-    tn = min(64, n - t0);
-    // (B) scores of tokens t0 + lane
-    float e[G];
+  // (B) scores of tokens t0 + lane from the rows in ub
+  auto scores = [&](int t0, float (&e)[G]) {
+    const int tn = min(64, n - t0);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       e[h] = -INFINITY;
       if (!((hm >> h) & 1u)) continue;
       float acc = 0.f;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (q < nq) {
-          const float4 b = *(const float4*)&ws.z.bsh[h][4 * q];
-          acc += ub[q].x * b.x + ub[q].y * b.y + ub[q].z * b.z + ub[q].w * b.w;
-        }
+      for (int q = 0; q < UQ; ++q) {
+        const float4 b = *(const float4*)&scr[h][4 * q];   // the same address on every lane
+        if (q < nq) acc += ub[q].x * b.x + ub[q].y * b.y + ub[q].z * b.z + ub[q].w * b.w;
       }
       if (lane < tn) e[h] = acc;
     }
-    const int t1 = t0 + 64;
-    if (t1 < n) {
-      const int tl1 = min(t1 + lane, n - 1);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) ub[q] = *(const float4*)(uk + (size_t)tl1 * r4 + 4 * min(q, nq - 1));
-    }
+  };
+  // online softmax and (C) from the rows in uc
+  auto accumulate = [&](const float (&e)[G]) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       if (!((hm >> h) & 1u)) continue;
@@ -583,84 +812,69 @@ __device__ void zoom_span32(const float* __restrict__ blk, int n, int r, unsigne
       const float p = (e[h] == -INFINITY) ? 0.f : __expf(e[h] - mn);
       ls[h] = ls[h] * corr + wave_sum(p);
       ms[h] = mn;
-      ws.z.psh[lane][h] = p;
+      float c4[4];
+      reduce_scatter<RC>(p, uc, c4);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) cacc[h][q] *= corr;
+      for (int k = 0; k < 4; ++k) cacc[h][k] = cacc[h][k] * corr + c4[k];
     }
-    __builtin_amdgcn_wave_barrier();
-    // (C) c_h[4 i4 ..] += sum over this lane's tokens of p_h U_V
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (!((hm >> h) & 1u)) continue;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int k = ts + 8 * m;
-        if (k < tn) {
-          const float p = ws.z.psh[k][h];
-          cacc[h][0] += p * uc[m].x;
-          cacc[h][1] += p * uc[m].y;
-          cacc[h][2] += p * uc[m].z;
-          cacc[h][3] += p * uc[m].w;
-        }
-      }
-    }
-    if (t1 < n) {
-      const int tn1 = min(64, n - t1);
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-        uc[m] = *(const float4*)(uv + (size_t)(t1 + min(ts + 8 * m, tn1 - 1)) * r4 + ic);
-    }
-    __builtin_amdgcn_wave_barrier();
+  };
+  // every 64 tokens but the last: the next 64 rows of U_K and U_V follow
+  // (the same loads on every pass, so the compiler's waits stay exact)
+  int t0 = 0;
+  for (; t0 + 64 < n; t0 += 64) {
+    float e[G];
+    scores(t0, e);
+    issue_fence();
+    load_u_tile<UQ>(cu.blk + fv.u(0), n, r4, t0 + 64, ub);
+    issue_fence();
+    accumulate(e);
+    issue_fence();
+    load_u_tile<UQ>(cu.blk + fv.u(1), n, r4, t0 + 64, uc);
+    issue_fence();
   }
-  if (r > 16) {   // the other rows of V_V
-#pragma unroll
-    for (int i = 16; i < 32; ++i)
-      vd[i] = *(const float2*)(vv + (size_t)min(i, r - 1) * kHeadDim + 2 * lane);
+  // the last 64: then what the next span needs first
+  {
+    float e[G];
+    scores(t0, e);
+    issue_fence();
+    prefetch_span(nxp, ub);
+    issue_fence();
+    accumulate(e);
   }
-  // reduce c over the 8 token lanes; sigma_V folded in (components at or past
-  // r hold values of clamped loads, never read by (D))
-  float sgv[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) sgv[q] = __shfl(svl, 4 * i4 + q, 64);
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    if (!((hm >> h) & 1u)) continue;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      cacc[h][q] += dpp<kDppRor8>(cacc[h][q]);
-      cacc[h][q] += __shfl_xor(cacc[h][q], 16, 64);
-      cacc[h][q] += __shfl_xor(cacc[h][q], 32, 64);
-    }
-    if (ts == 0)
-      *(float4*)&ws.z.csh[h][4 * i4] = make_float4(cacc[h][0] * sgv[0], cacc[h][1] * sgv[1],
-                                                   cacc[h][2] * sgv[2], cacc[h][3] * sgv[3]);
-  }
-  __builtin_amdgcn_wave_barrier();
 
   // (D) a_h[dim] = sum_i V_V[i][dim] (sigma_V c_h)[i]; rows past r hold a
-  // clamped copy of row r - 1 (or were never loaded) and are skipped
-  float a[G][2];
-#pragma unroll
-  for (int h = 0; h < G; ++h) a[h][0] = a[h][1] = 0.f;
+  // clamped copy of row r - 1 and get weight 0
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     if (!((hm >> h) & 1u)) continue;
+    const float cs[4] = {cacc[h][0] * svg.x, cacc[h][1] * svg.y, cacc[h][2] * svg.z,
+                         cacc[h][3] * svg.w};
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (i < r) {
-        const float w = ws.z.csh[h][i];
-        a[h][0] += w * vd[i].x;
-        a[h][1] += w * vd[i].y;
-      }
+    for (int k = 0; k < VK; ++k) {
+      const int i0 = 2 * k, i1 = 2 * k + 1;
+      if (i0 >= r) continue;
+      const float w0 = readlane(cs[i0 & 3], GL * (i0 >> 2));
+      const float w1 = i1 < r ? readlane(cs[i1 & 3], GL * (i1 >> 2)) : 0.f;
+      const float w = half ? w1 : w0;
+      a[0] += w * vd[k].x;
+      a[1] += w * vd[k].y;
+      a[2] += w * vd[k].z;
+      a[3] += w * vd[k].w;
     }
+    // the swaps read the other half of the wave: every lane runs them
+    const float4 sum = make_float4(xor32_sum(a[0]), xor32_sum(a[1]), xor32_sum(a[2]), xor32_sum(a[3]));
+    if (half == 0) *(float4*)&scr[h][4 * dq] = sum;
   }
+  __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     if (!((hm >> h) & 1u)) continue;
+    const float2 ah = *(const float2*)&scr[h][2 * lane];
     float w1, w2;
     const float M = merge_w(zm[h], ms[h], w1, w2);
-    za[h][0] = za[h][0] * w1 + a[h][0] * w2;
-    za[h][1] = za[h][1] * w1 + a[h][1] * w2;
+    za[h][0] = za[h][0] * w1 + ah.x * w2;
+    za[h][1] = za[h][1] * w1 + ah.y * w2;
     zl[h] = zl[h] * w1 + ls[h] * w2;
     zm[h] = M;
   }
@@ -671,6 +885,15 @@ __device__ void zoom_span32(const float* __restrict__ blk, int n, int r, unsigne
 // the layer kernel
 // ---------------------------------------------------------------------------
 static_assert(kChunk * kMaxGroup <= kThreads, "one gate per thread");
+template <int G> constexpr bool smem_fits() {
+  return sizeof(Smem<G>) + sizeof(Stage<G>) <= 80 * 1024 &&   // two workgroups per CU (160 KB)
+         sizeof(Smem<G>::rt) <= sizeof(Smem<G>::w) &&
+         sizeof(ZoomScratchAny<G>) <= sizeof(float) * stage_floats<stage_rows<G>()>() &&
+         stage_rows<G>() % 2 == 0 && stage_rows<G>() <= 32;
+}
+static_assert(smem_fits<1>() && smem_fits<2>() && smem_fits<3>() && smem_fits<4>() &&
+              smem_fits<5>() && smem_fits<6>() && smem_fits<7>() && smem_fits<8>(),
+              "LDS layout of the layer kernel");
 static_assert(kChunk <= 64, "a chunk's zoom sets are one wave ballot");
 
 template <typename T, int G>
@@ -680,8 +903,10 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
   constexpr int CLOADS = (kChunk / kWaves) / Ln::RPW;     // coarse entries: loads per wave
   constexpr int DLOADS = kRowBlock / Ln::RPW;             // full-resolution rows: loads per pass
   __shared__ Smem<G> s;
+  __shared__ Stage<G> stg;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  float* const stage = stg.v[uniform(wid)];   // this wave's stage, a scalar LDS address
   const int W = geo.n_work;
   const int g = blockIdx.x / W, w = blockIdx.x % W;
   const int sc = geo.n_compressed, D = geo.n_dense, dr = geo.route_dim;
@@ -698,7 +923,7 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
   // (loads complete in issue order, so routing never waits for the rows)
   for (int o = tid; o < G * kHeadDim; o += kThreads) {
     const float x = a.q[(size_t)h0 * kHeadDim + o];
-    s.qu[o / kHeadDim][o % kHeadDim] = x;
+    s.rt.qu[o / kHeadDim][o % kHeadDim] = x;
     s.qs[o / kHeadDim][o % kHeadDim] = x * scale;
   }
   if (tid < kChunk) s.bits[tid] = 0;
@@ -745,10 +970,14 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
   const int cr0 = j0 + wid * (kChunk / kWaves);
   const int cr1 = min(j0 + nj, cr0 + kChunk / kWaves);
   uint4 kr[CLOADS], vr[CLOADS];
+  float cbias[CLOADS];   // ln n of each coarse entry (loaded with it)
   if (dense && nj > 0) {
     const T* K = (const T*)a.kbar + (size_t)g * sc * kHeadDim;
     const T* V = (const T*)a.vbar + (size_t)g * sc * kHeadDim;
     rows_load<T, CLOADS>(K, V, cr0, cr1, kr, vr);
+#pragma unroll
+    for (int u = 0; u < CLOADS; ++u)
+      cbias[u] = a.lnn32[min(cr0 + u * Ln::RPW + lane / Ln::LPR, j0 + nj - 1)];
   }
   __syncthreads();
 
@@ -766,7 +995,7 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
         }
         double acc = 0.0;
         if (o < nout) {
-          const float* qh = &s.qu[o / dr][part * 16];
+          const float* qh = &s.rt.qu[o / dr][part * 16];
 #pragma unroll
           for (int c4 = 0; c4 < 4; ++c4) {
             const float4 x = pv[k][c4];
@@ -775,7 +1004,7 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
           }
         }
         acc = group_sum<8>(acc);
-        if (part == 0 && o < nout) s.qt[o / dr][o % dr] = acc;
+        if (part == 0 && o < nout) s.rt.qt[o / dr][o % dr] = acc;
       }
     }
     __syncthreads();
@@ -790,12 +1019,12 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
             float f[Ln::EPL];
             unpack16(sum[v], f, T());
 #pragma unroll
-            for (int e = 0; e < Ln::EPL; ++e) x += s.qt[hl][v * Ln::EPL + e] * (double)f[e];
+            for (int e = 0; e < Ln::EPL; ++e) x += s.rt.qt[hl][v * Ln::EPL + e] * (double)f[e];
           }
         }
       } else {
         const T* sr = (const T*)a.summ + ((size_t)h * sc + j) * dr;
-        for (int i = 0; i < dr; ++i) x += s.qt[hl][i] * (double)Store<T>::load(sr + i);
+        for (int i = 0; i < dr; ++i) x += s.rt.qt[hl][i] * (double)Store<T>::load(sr + i);
       }
       x += a.gamma * lnn_j;
       const double p = 1.0 / (1.0 + exp(-x));
@@ -831,46 +1060,99 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
     }
   }
 
-  // ---- full-resolution rows and coarse entries; the state goes to LDS -------
+  // ---- each wave's first zoomed span (the wid-th of the chunk): its V_K
+  // moves into the wave's stage under the rest of the rows phase (issued once
+  // the first rows have arrived, so no wait for them also waits for it) ------
+  constexpr int SR = stage_rows<G>();
+  const SpanRef zero{a.zero_block, 1, 1, 0u};
+  SpanRef first = zero;   // the wave's first zoomed span of rank <= 32
+  if (zoom && nj > 0) {
+    unsigned zb = (unsigned)__ballot(lane < nj && s.bits[lane] != 0);
+    for (int k = 0; k < wid; ++k) zb &= zb - 1u;   // the wid-th zoomed span on
+    while (zb != 0u) {
+      const int jl = __ffs(zb) - 1;
+      if (s.m_r[jl] <= 32) {
+        first = span_ref(s, a.pool, jl);
+        break;
+      }
+      for (int k = 0; k < kWaves; ++k) zb &= zb - 1u;   // the wave's next one
+    }
+  }
+  if (first.r > SR) first = zero;
+
+  // ---- full-resolution rows and coarse entries: each wave's state ----------
   if (dense) {
     QSlice<T, G> qv;
     qv.load(s.qs);
     RowState<T, G> rs;
     rs.init();
-    rows_accumulate<T, G, DLOADS>(dk, dv, dr0, min(d1, dr0 + kRowBlock), qv, nullptr, nullptr, 0,
-                                  rs);
+    const float nob[DLOADS] = {};
+    rows_accumulate<T, G, DLOADS>(dk, dv, dr0, min(d1, dr0 + kRowBlock), qv, nob, nullptr, 0, rs);
+    stage_vk<SR>(first, stage);
     for (int p0 = d0 + kWaves * kRowBlock; p0 < d1; p0 += kWaves * kRowBlock) {
       const int r0 = p0 + wid * kRowBlock, r1 = min(d1, r0 + kRowBlock);
       rows_load<T, DLOADS>(DK, DV, r0, r1, dk, dv);
-      rows_accumulate<T, G, DLOADS>(dk, dv, r0, r1, qv, nullptr, nullptr, 0, rs);
+      rows_accumulate<T, G, DLOADS>(dk, dv, r0, r1, qv, nob, nullptr, 0, rs);
     }
-    if (nj > 0) rows_accumulate<T, G, CLOADS>(kr, vr, cr0, cr1, qv, a.lnn32 + j0, s.bits, j0, rs);
+    if (nj > 0) rows_accumulate<T, G, CLOADS>(kr, vr, cr0, cr1, qv, cbias, s.bits, j0, rs);
     rows_finish<T, G>(rs);
-    rows_store<T, G>(rs, s.rows_acc[wid], s.rows_m[wid], s.rows_l[wid]);
-  } else if (lane < G) {
-    s.rows_m[wid][lane] = -INFINITY;
-    s.rows_l[wid][lane] = 0.f;
+    rows_store<T, G>(rs, s.w[wid].st.acc, s.w[wid].st.m, s.w[wid].st.l);
+  } else {
+    stage_vk<SR>(first, stage);
   }
   __syncthreads();
 
-  // ---- zoomed spans: one wave per span ---------------------------------------
+  // ---- zoomed spans: the wave's running state starts from its rows and
+  // coarse entries; spans u = wid, wid + kWaves, ... of the chunk's list ------
+  // (lane holds dims 2 lane, 2 lane + 1)
   float zm[G], zl[G], za[G][2];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    zm[h] = -INFINITY;
-    zl[h] = 0.f;
-    za[h][0] = za[h][1] = 0.f;
+    zm[h] = dense ? s.w[wid].st.m[h] : -INFINITY;
+    zl[h] = dense ? s.w[wid].st.l[h] : 0.f;
+    za[h][0] = dense ? s.w[wid].st.acc[h][2 * lane] : 0.f;
+    za[h][1] = dense ? s.w[wid].st.acc[h][2 * lane + 1] : 0.f;
   }
+  __builtin_amdgcn_wave_barrier();
   if (zoom && nj > 0) {
     const int nz = s.nz;
-    for (int u = wid; u < nz; u += kWaves) {
-      const int jl = s.zl[u];
-      const float* blk = a.pool + s.m_off[jl];
-      const int n = s.m_n[jl], r = s.m_r[jl];
-      if (r <= 32)
-        zoom_span32<G>(blk, n, r, (unsigned)s.bits[jl], s.qs, s.w[wid], zm, zl, za);
-      else
-        zoom_span<G>(blk, n, r, (unsigned)s.bits[jl], s.qs, s.w[wid], zm, zl, za);
+    // the wave's spans u = wid, wid + kWaves, ... of rank <= 32, pipelined
+    auto next_small = [&](int u) {
+      while (u < nz && s.m_r[s.zl[u]] > 32) u += kWaves;
+      return uniform(u);
+    };
+    int u = next_small(wid);
+    if (u < nz) {
+      SpanRef cu = span_ref(s, a.pool, s.zl[u]);
+      float4 ub[8];
+      prefetch_span(cu, ub);
+      for (;;) {
+        const int un = next_small(u + kWaves);
+        const bool has_nx = un < nz;
+        const SpanRef nx = span_ref(s, a.pool, s.zl[min(un, nz - 1)]);
+        // stand-ins when there is no next span: this one again (its V_K only
+        // if it is staged, else the zeros)
+        const SpanRef nxp = has_nx ? nx : cu;
+        const SpanRef nxs = has_nx && nx.r <= SR ? nx : (cu.r <= SR ? cu : zero);
+        // the span's scratch: the wave's state area (idle while its spans run)
+        float (*scr)[kHeadDim] = s.w[wid].st.acc;
+        if (cu.r <= 16)
+          zoom_span32<G, SR, 16>(cu, nxp, nxs, ub, stage, scr, s.qs, zm, zl, za);
+        else
+          zoom_span32<G, SR, 32>(cu, nxp, nxs, ub, stage, scr, s.qs, zm, zl, za);
+        if (!has_nx) break;
+        cu = nx;
+        u = un;
+      }
+    }
+    // then those of rank > 32, with the stage as scratch once its DMA is done
+    for (u = wid; u < nz; u += kWaves) {
+      const int jl = uniform(s.zl[u]);
+      if (s.m_r[jl] <= 32) continue;
+      const SpanRef sp = span_ref(s, a.pool, jl);
+      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+      zoom_span<G>(sp.blk, sp.n, sp.r, sp.hm, s.qs,
+                   *reinterpret_cast<ZoomScratchAny<G>*>(stage), zm, zl, za);
     }
   }
 
@@ -896,18 +1178,12 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
       const int h = o / kHeadDim, d = o % kHeadDim;
       float M = -INFINITY;
 #pragma unroll
-      for (int wv = 0; wv < kWaves; ++wv)
-        M = fmaxf(M, fmaxf(s.rows_m[wv][h], s.w[wv].st.m[h]));
+      for (int wv = 0; wv < kWaves; ++wv) M = fmaxf(M, s.w[wv].st.m[h]);
       float L = 0.f, A = 0.f;
       if (M != -INFINITY) {
 #pragma unroll
         for (int wv = 0; wv < kWaves; ++wv) {
-          const float m0 = s.rows_m[wv][h], m1 = s.w[wv].st.m[h];
-          if (m0 != -INFINITY) {
-            const float wt = __expf(m0 - M);
-            L += s.rows_l[wv][h] * wt;
-            A += s.rows_acc[wv][h][d] * wt;
-          }
+          const float m1 = s.w[wv].st.m[h];
           if (m1 != -INFINITY) {
             const float wt = __expf(m1 - M);
             L += s.w[wv].st.l[h] * wt;

@@ -112,6 +112,11 @@ constexpr int kMaxDenseRows = 256;        // full-resolution rows per workgroup,
 constexpr int kPartStride = kHeadDim + 4;
 constexpr int kMaxRank = kHeadDim;
 constexpr int kListWords = kMaxGroup + 1; // zoom bit masks per chunk: heads, then union
+// A block of zeros each cache owns: the source of the layer kernel's prefetches
+// when a wave has nothing to prefetch, so that every wave issues the same
+// loads and the compiler counts outstanding loads exactly.  It holds a factor
+// block of one token at rank 1 and a full V_K stage (32 rows of d floats).
+constexpr int kZeroBlockFloats = 32 * kHeadDim;
 
 struct LayerGeom {
   int n_q_heads, n_kv_heads, group, route_dim;
@@ -178,6 +183,7 @@ struct LayerArgs {
   float* part;             // workspace
   uint32_t* tickets;       // [Hkv], zero between launches
   uint32_t* chunk_bits;    // [Hkv][n_work][kListWords] zoom bit masks of each chunk
+  const float* zero_block; // kZeroBlockFloats zeros
 };
 
 // launchers (return hipError_t of the launch)
