@@ -230,25 +230,15 @@ def main():
     log(f"bytes/step {bytes_step / 1e9:.3f} GB (zoom {float(zb_step.mean()) / 1e9:.3f} GB): "
         f"{step_gbs:.0f} GB/s = {step_gbs / HBM_PEAK_GBS:.3f} of peak")
 
-    # ---- live per-launch timing of the attention kernel ------------------------
-    n_meas = min(8, args.steps)
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(L)] for _ in range(n_meas)]
-    torch.cuda.synchronize()
-    torch.cuda._sleep(50_000_000)   # keep the GPU busy while every launch below is queued
-    for m in range(n_meas):
-        i = args.warmup + m
-        q_cur.copy_(qs[i])
-        for layer in range(L):
-            evs[m][layer][0].record()
-            layer_call(layer)
-            evs[m][layer][1].record()
-    torch.cuda.synchronize()
-    attn_us = [a.elapsed_time(b) * 1e3 for row in evs for (a, b) in row]
-    attn_us_mean = float(np.mean(attn_us))
-    # zoom_bytes[step, layer] is per launch already: its mean over the
-    # measured steps' launches plus the resident bytes every launch reads
-    attn_bytes_meas = float(zoom_bytes[:n_meas].mean()) + resident_layer
+    # ---- mean launch of the layer kernel, live, from the timed region ----------
+    # The graph replays launch the 32 layer kernels back to back on one stream
+    # (no host gaps: in a kernel trace the step's span equals the sum of its
+    # launches), so the HIP events around the timed region over its steps x L
+    # launches give the kernel's mean duration (plus one small query copy per
+    # step).  Algorithmic bytes: the timed steps' zoomed-span factors per launch
+    # plus the resident bytes every launch reads.
+    attn_us_mean = total_ms * 1e3 / (args.steps * L)
+    attn_bytes_meas = float(zoom_bytes.mean()) + resident_layer
     attn_gbs = attn_bytes_meas / (attn_us_mean * 1e-6) / 1e9
     log(f"layer launch: {attn_us_mean:.2f} us avg, {attn_bytes_meas / 1e6:.2f} MB algorithmic "
         f"-> {attn_gbs:.0f} GB/s")
@@ -320,6 +310,7 @@ def main():
             "kernel": "sekv::layer_kernel (sekv_route_attn, one layer: route + attention)",
             "algorithmic_bytes_per_launch": attn_bytes_meas,
             "avg_launch_us": attn_us_mean,
+            "avg_launch_from": "HIP events around the timed region / (steps x layers)",
         },
         "cpu_baseline": cpu,
         "step_hbm": {"bytes_per_step": bytes_step, "gbs": step_gbs, "frac": step_gbs / HBM_PEAK_GBS,

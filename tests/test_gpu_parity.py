@@ -213,6 +213,43 @@ def test_repeat_runs_are_bit_identical(S):
     assert torch.equal(o1, o3)
 
 
+def test_uneven_zoom_parity_and_repeat(S):
+    """Zoom concentrated on a few KV heads (three zoom ~75% of their spans,
+    two have one head at ~40%, three zoom nothing), so a few workgroups attend
+    many spans while most attend none: against the oracle, and bit-identical
+    over repeated launches of both call paths."""
+    wl = synth.workload("llama3_8b_128k", n_layers=1, n_tokens=20000)
+    log("[parity] uneven zoom")
+    inp = Inputs(wl, 6)
+    cache = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    orc = OracleSide(inp, [0], wl.max_rank)
+    q = inp.query(0)[0]
+    q64, p64 = to64(q), to64(inp.p[0])
+    prob = orc.route(0, q64, p64, np.full(wl.n_q_heads, 2.0), wl.gamma).prob
+    frac = np.zeros(wl.n_q_heads)
+    for h in range(wl.n_q_heads):
+        kh, i = divmod(h, wl.group)
+        frac[h] = 0.75 if kh < 3 else (0.4 if kh < 5 and i == 0 else 0.0)
+    tau = torch.tensor([float(np.quantile(prob[h], 1.0 - frac[h])) if frac[h] > 0 else 1.0
+                        for h in range(wl.n_q_heads)], dtype=torch.float32).cuda()
+    n_tie, worst, route = check_layer(S, cache, orc, inp, 0, q, tau, wl.gamma, TOL["bf16"])
+    heavy = 0   # 32-span chunks with more than 8 zoomed spans (two per wave)
+    for kh in range(wl.n_kv_heads):
+        ids = np.asarray(route.unions[kh])
+        if ids.size:
+            heavy += int((np.bincount(ids // 32) > 8).sum())
+    log(f"[parity] uneven zoom: chunks with >8 zoomed {heavy} ties={n_tie} err={worst:.2e}")
+    assert heavy >= 10
+    assert all(len(route.unions[kh]) == 0 for kh in range(5, wl.n_kv_heads))
+    rb0, o0 = run_gpu_layer(S, cache, 0, q, inp.p[0], tau, fused=True)
+    for _ in range(4):
+        rb1, o1 = run_gpu_layer(S, cache, 0, q, inp.p[0], tau, fused=True)
+        assert torch.equal(o0, o1)
+        assert_same_route(rb0, rb1)
+        rb2, o2 = run_gpu_layer(S, cache, 0, q, inp.p[0], tau)
+        assert torch.equal(o0, o2)
+
+
 def test_host_tier_matches_device_tier(S):
     """Factors in pinned host memory, fetched per layer for the union of the
     zoomed spans: same routes as the device tier, outputs equal up to the
