@@ -354,7 +354,7 @@ __device__ __forceinline__ void rows_store(const RowState<T, G>& s, float (*acc)
 // into the wave's running state (zm, zl, za: lane holds dims 2 lane, 2 lane+1).
 // ---------------------------------------------------------------------------
 template <int G>
-__device__ void zoom_span(const float* __restrict__ blk, int n, int r, unsigned hm,
+__device__ __attribute__((always_inline)) void zoom_span(const float* __restrict__ blk, int n, int r, unsigned hm,
                           const float (*qs)[kHeadDim], ZoomScratchAny<G>& zs, float* zm, float* zl,
                           float (*za)[2]) {
   const int lane = threadIdx.x & 63;
@@ -700,7 +700,7 @@ __device__ __forceinline__ void reduce_scatter(float p, const float4 (&u)[RC / 4
 //      halves of the wave are added, and scr[h] turns the result into the
 //      state's layout (dims 2 lane, 2 lane + 1).
 template <int G, int SR, int RC>
-__device__ void zoom_span32(const SpanRef& cu, const SpanRef& nxp, const SpanRef& nxs,
+__device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, const SpanRef& nxp, const SpanRef& nxs,
                             float4 (&ub)[8], float* stage, float (*scr)[kHeadDim],
                             const float (*qs)[kHeadDim], float* zm, float* zl, float (*za)[2]) {
   static_assert(RC == 16 || RC == 32, "rank class");
@@ -1215,14 +1215,25 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
   if (!s.last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
+  // The lists' chunk masks (first kThreads chunks) and the merge's slots are
+  // all requested before either is used: one round trip for both.
+  const int nc = geo.n_chunks;
+  uint32_t word0[kListWords];
+#pragma unroll
+  for (int li = 0; li < kListWords; ++li)
+    word0[li] = ((mode & kLists) && li <= G && tid < nc)
+                    ? a.chunk_bits[((size_t)g * W + tid) * kListWords + li]
+                    : 0u;
+
   if (mode & kMerge) {
     // thread = (head, 4 dims, stripe of slots): an online pass over its slots,
-    // 8 slots' loads in flight at a time; stripes are combined through LDS
+    // B slots' loads in flight at a time (all of them up to B * STRIPES slots);
+    // stripes are combined through LDS
     const int ns = (mode & kZoomSplit) ? 2 * W : W;
     const float* pg = a.part + (size_t)g * geo.n_slots() * G * kPartStride;
     constexpr int QUADS = G * (kHeadDim / 4);
     constexpr int STRIPES = (kThreads / QUADS) > 0 ? (kThreads / QUADS) : 1;
-    constexpr int B = 8;
+    constexpr int B = 24;
     const int quad = tid % QUADS, stripe = tid / QUADS;
     const int hl = quad / (kHeadDim / 4), dq = quad % (kHeadDim / 4);
     float M = -INFINITY, Ls = 0.f;
@@ -1234,8 +1245,9 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
 #pragma unroll
         for (int u = 0; u < B; ++u) {
           const float* p = pg + ((size_t)min(sl0 + u * STRIPES, ns - 1) * G + hl) * kPartStride;
-          m[u] = p[0];
-          l[u] = p[1];
+          const float2 ml = *(const float2*)p;
+          m[u] = ml.x;
+          l[u] = ml.y;
           x[u] = *(const float4*)(p + 4 + 4 * dq);
         }
 #pragma unroll
@@ -1304,7 +1316,6 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
     // ascending per-head lists and the group union, from the chunks' zoom bit
     // masks: one load per (chunk, list), a block scan of the popcounts, and
     // each thread writes its chunk's ids
-    const int nc = geo.n_chunks;
     int base[kListWords];
 #pragma unroll
     for (int li = 0; li < kListWords; ++li) base[li] = 0;
@@ -1314,7 +1325,8 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
       int incl[kListWords];
 #pragma unroll
       for (int li = 0; li <= G; ++li)
-        word[li] = c < nc ? a.chunk_bits[((size_t)g * W + c) * kListWords + li] : 0u;
+        word[li] = c0 == 0 ? word0[li]
+                           : (c < nc ? a.chunk_bits[((size_t)g * W + c) * kListWords + li] : 0u);
 #pragma unroll
       for (int li = 0; li <= G; ++li) {
         const int cnt = __popc(word[li]);
