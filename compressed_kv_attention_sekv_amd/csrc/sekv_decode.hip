@@ -919,19 +919,23 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
 
   // ---- everything this workgroup reads before its zoom decisions, issued up
   // front: query, span metadata, routing projections, summaries, ln n,
-  // thresholds, then the full-resolution rows (first pass) and coarse entries
-  // (loads complete in issue order, so routing never waits for the rows)
-  for (int o = tid; o < G * kHeadDim; o += kThreads) {
-    const float x = a.q[(size_t)h0 * kHeadDim + o];
-    s.rt.qu[o / kHeadDim][o % kHeadDim] = x;
-    s.qs[o / kHeadDim][o % kHeadDim] = x * scale;
+  // thresholds, then the full-resolution rows (first pass) and coarse entries.
+  // Query and metadata go to LDS only after every load is out, so no wait for
+  // them holds back the rest: the whole prologue is one round trip.
+  constexpr int QPT = (G * kHeadDim + kThreads - 1) / kThreads;   // query floats per thread
+  float qx[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int o = tid + i * kThreads;
+    qx[i] = o < G * kHeadDim ? a.q[(size_t)h0 * kHeadDim + o] : 0.f;
   }
-  if (tid < kChunk) s.bits[tid] = 0;
+  unsigned long long m_off = 0;
+  int m_n = 0, m_r = 0;
   if (zoom && tid < nj) {
     const size_t gj = (size_t)g * sc + j0 + tid;
-    s.m_off[tid] = a.fac_off[gj] - a.off_base;
-    s.m_n[tid] = a.clen[j0 + tid];
-    s.m_r[tid] = a.rank[gj];
+    m_off = a.fac_off[gj];
+    m_n = a.clen[j0 + tid];
+    m_r = a.rank[gj];
   }
   const int nout = G * dr, part = tid & 7, orow = tid >> 3;
   float4 pv[4][4];
@@ -978,6 +982,23 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
 #pragma unroll
     for (int u = 0; u < CLOADS; ++u)
       cbias[u] = a.lnn32[min(cr0 + u * Ln::RPW + lane / Ln::LPR, j0 + nj - 1)];
+  }
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int o = tid + i * kThreads;
+    if (o < G * kHeadDim) {
+      s.rt.qu[o / kHeadDim][o % kHeadDim] = qx[i];
+      s.qs[o / kHeadDim][o % kHeadDim] = qx[i] * scale;
+    }
+  }
+  if (tid < kChunk) s.bits[tid] = 0;
+  if (zoom && tid < nj) {
+    // (an empty asm keeps the compiler from moving this arithmetic, and the
+    // wait for its load, up next to the load)
+    asm volatile("" : "+v"(m_off));
+    s.m_off[tid] = m_off - a.off_base;
+    s.m_n[tid] = m_n;
+    s.m_r[tid] = m_r;
   }
   __syncthreads();
 
@@ -1028,6 +1049,7 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
       }
       x += a.gamma * lnn_j;
       const double p = 1.0 / (1.0 + exp(-x));
+      asm volatile("" : "+v"(tau_f));   // its widening stays here, not next to its load
       const bool z = p > (double)tau_f;
       a.mask[(size_t)h * sc + j] = (uint8_t)z;
       if (a.prob) a.prob[(size_t)h * sc + j] = p;
