@@ -11,26 +11,28 @@ from __future__ import annotations
 import ctypes
 import dataclasses
 import os
-from typing import Optional
+from typing import Optional, Sequence
 
 import torch
 
 __all__ = [
     "SekvError", "SekvConfig", "SekvCacheInfo", "SekvRouteOut", "lib", "library_path",
     "make_config", "Cache", "RouteBuffers", "sekv_segment", "sekv_build_spans", "sekv_route",
-    "sekv_decode_attn", "sekv_route_attn", "sekv_decode_workspace_bytes", "EXPORTED_SYMBOLS",
+    "sekv_decode_attn", "sekv_route_attn", "sekv_decode_attn_batch", "sekv_route_attn_batch",
+    "sekv_decode_workspace_bytes", "EXPORTED_SYMBOLS", "SEKV_MAX_BATCH",
     "SEKV_F32", "SEKV_BF16", "SEKV_TIER_DEVICE", "SEKV_TIER_HOST_PINNED",
 ]
 
 SEKV_OK, SEKV_ERR_INVALID, SEKV_ERR_NOMEM, SEKV_ERR_HIP, SEKV_ERR_UNSUPPORTED = range(5)
 SEKV_F32, SEKV_BF16 = 0, 1
 SEKV_TIER_DEVICE, SEKV_TIER_HOST_PINNED = 0, 1
+SEKV_MAX_BATCH = 8
 
 EXPORTED_SYMBOLS = (
     "sekv_segment", "sekv_build_spans", "sekv_cache_info_get", "sekv_cache_copy_spans",
     "sekv_cache_copy_group", "sekv_cache_copy_factors", "sekv_route",
-    "sekv_decode_workspace_bytes", "sekv_decode_attn", "sekv_route_attn", "sekv_cache_destroy",
-    "sekv_last_error",
+    "sekv_decode_workspace_bytes", "sekv_decode_attn", "sekv_route_attn",
+    "sekv_decode_attn_batch", "sekv_route_attn_batch", "sekv_cache_destroy", "sekv_last_error",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -105,6 +107,12 @@ def lib() -> ctypes.CDLL:
         "sekv_decode_attn": (I32, [P, I32, P, ctypes.POINTER(SekvRouteOut), P, P, SZ, P, P]),
         "sekv_route_attn": (I32, [P, I32, P, P, P, ctypes.POINTER(SekvRouteOut), P, P, SZ, P,
                                   P]),
+        "sekv_route_attn_batch": (I32, [ctypes.POINTER(P), I32, I32, ctypes.POINTER(P), P, P,
+                                        ctypes.POINTER(SekvRouteOut), ctypes.POINTER(P),
+                                        ctypes.POINTER(P), ctypes.POINTER(SZ), P]),
+        "sekv_decode_attn_batch": (I32, [ctypes.POINTER(P), I32, I32, ctypes.POINTER(P),
+                                         ctypes.POINTER(SekvRouteOut), ctypes.POINTER(P),
+                                         ctypes.POINTER(P), ctypes.POINTER(SZ), P]),
         "sekv_cache_destroy": (None, [P]),
         "sekv_last_error": (ctypes.c_char_p, []),
     }
@@ -331,3 +339,42 @@ def sekv_route_attn(cache: Cache, layer: int, q: torch.Tensor, proj: torch.Tenso
                                  ctypes.byref(st), _ptr(o), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream),
                                  fst))
+
+
+def _batch_arrays(caches, qs, routes, os_, workspaces):
+    n = len(caches)
+    if not (len(qs) == len(routes) == len(os_) == len(workspaces) == n):
+        raise ValueError("caches, q, routes, o and workspaces must have one entry per sequence")
+    for c, q, o, w in zip(caches, qs, os_, workspaces):
+        _need(q, "q", torch.float32)
+        _need(o, "o", torch.float32)
+        _need(w, "workspace")
+        shape = (c.cfg.n_q_heads, c.cfg.head_dim)
+        if tuple(q.shape) != shape or tuple(o.shape) != shape:
+            raise ValueError("q and o must be [Hq][d]")
+    P = ctypes.c_void_p
+    return ((P * n)(*[c.handle for c in caches]), (P * n)(*[_ptr(q) for q in qs]),
+            (SekvRouteOut * n)(*[r.struct() for r in routes]), (P * n)(*[_ptr(o) for o in os_]),
+            (P * n)(*[_ptr(w) for w in workspaces]),
+            (ctypes.c_size_t * n)(*[w.numel() * w.element_size() for w in workspaces]))
+
+
+def sekv_route_attn_batch(caches: Sequence[Cache], layer: int, qs: Sequence[torch.Tensor],
+                          proj: torch.Tensor, tau: torch.Tensor, routes: Sequence[RouteBuffers],
+                          os_: Sequence[torch.Tensor], workspaces: Sequence[torch.Tensor],
+                          stream=None) -> None:
+    """Route and attend one layer of several sequences (one cache each) in one launch."""
+    _need(proj, "proj", torch.float32)
+    _need(tau, "tau", torch.float32)
+    cs, qp, rs, op, wp, wb = _batch_arrays(caches, qs, routes, os_, workspaces)
+    _check(lib().sekv_route_attn_batch(cs, len(caches), layer, qp, _ptr(proj), _ptr(tau), rs, op,
+                                       wp, wb, _stream(stream)))
+
+
+def sekv_decode_attn_batch(caches: Sequence[Cache], layer: int, qs: Sequence[torch.Tensor],
+                           routes: Sequence[RouteBuffers], os_: Sequence[torch.Tensor],
+                           workspaces: Sequence[torch.Tensor], stream=None) -> None:
+    """Attend one layer of several sequences (routes given) in one launch."""
+    cs, qp, rs, op, wp, wb = _batch_arrays(caches, qs, routes, os_, workspaces)
+    _check(lib().sekv_decode_attn_batch(cs, len(caches), layer, qp, rs, op, wp, wb,
+                                        _stream(stream)))

@@ -600,6 +600,87 @@ sekv_status sekv_route_attn(const sekv_cache* c, int32_t layer, const float* q_d
   return SEKV_OK;
 }
 
+// ---- batches of sequences -------------------------------------------------------
+static_assert(kMaxBatch == SEKV_MAX_BATCH, "one batch limit");
+
+static sekv_status batch_impl(const sekv_cache* const* caches, int32_t batch, int32_t layer,
+                              const float* const* q_devs, const float* proj_dev,
+                              const float* tau_dev, const sekv_route_out* routes,
+                              float* const* o_devs, void* const* ws_devs, const size_t* ws_bytes,
+                              hipStream_t stream, bool with_route) {
+  if (!caches || !q_devs || !routes || !o_devs || !ws_devs || !ws_bytes)
+    return fail(SEKV_ERR_INVALID, "caches, q, routes, o, workspace arrays must be non-NULL");
+  if (batch < 1 || batch > SEKV_MAX_BATCH)
+    return fail(SEKV_ERR_INVALID, "batch %d outside [1, %d]", batch, SEKV_MAX_BATCH);
+  if (with_route && (!proj_dev || !tau_dev))
+    return fail(SEKV_ERR_INVALID, "proj and tau must be non-NULL");
+  sekv_status r;
+  for (int i = 0; i < batch; ++i) {
+    const sekv_cache* c = caches[i];
+    if ((r = check_layer_call(c, layer))) return r;
+    const sekv_config& a = c->cfg;
+    const sekv_config& b = caches[0]->cfg;
+    if (a.n_layers != b.n_layers || a.n_q_heads != b.n_q_heads || a.n_kv_heads != b.n_kv_heads ||
+        a.head_dim != b.head_dim || a.route_dim != b.route_dim || a.kv_dtype != b.kv_dtype)
+      return fail(SEKV_ERR_INVALID, "cache %d has another model shape than cache 0", i);
+    for (int k = 0; k < i; ++k)
+      if (caches[k] == c)
+        return fail(SEKV_ERR_INVALID, "cache %d appears twice in the batch (slots %d and %d)", i,
+                    k, i);
+    if (!q_devs[i] || !o_devs[i])
+      return fail(SEKV_ERR_INVALID, "q and o of sequence %d must be non-NULL", i);
+    if (with_route) {
+      if ((r = check_route_out(&routes[i]))) return r;
+    } else if (!routes[i].mask || !routes[i].union_list || !routes[i].union_count) {
+      return fail(SEKV_ERR_INVALID, "route mask and union lists of sequence %d must be non-NULL",
+                  i);
+    }
+    if ((r = check_workspace(c, ws_devs[i], ws_bytes[i]))) return r;
+  }
+  // every device-tier sequence with compressed spans goes into the one launch;
+  // the others take the single-sequence path (also on `stream`)
+  BatchLayerArgs b{};
+  int nb = 0;
+  for (int i = 0; i < batch; ++i) {
+    const sekv_cache* c = caches[i];
+    if (c->cfg.factor_tier == SEKV_TIER_HOST_PINNED || c->sc == 0) {
+      r = with_route ? sekv_route_attn(c, layer, q_devs[i], proj_dev, tau_dev, &routes[i],
+                                       o_devs[i], ws_devs[i], ws_bytes[i], stream, stream)
+                     : sekv_decode_attn(c, layer, q_devs[i], &routes[i], o_devs[i], ws_devs[i],
+                                        ws_bytes[i], stream, stream);
+      if (r) return r;
+      continue;
+    }
+    b.geo[nb] = c->geom;
+    b.arg[nb] = layer_args(c, layer, q_devs[i], with_route ? proj_dev : nullptr,
+                           with_route ? tau_dev : nullptr, &routes[i], o_devs[i], ws_devs[i]);
+    ++nb;
+  }
+  if (nb > 0) {
+    const int mode = with_route ? (kRoute | kDense | kZoom | kMerge | kLists)
+                                : (kDense | kZoom | kMerge);
+    SEKV_HIP(launch_layer_batch(caches[0]->bf16(), mode, caches[0]->geom.group, b, nb, stream));
+  }
+  return SEKV_OK;
+}
+
+sekv_status sekv_route_attn_batch(const sekv_cache* const* caches, int32_t batch, int32_t layer,
+                                  const float* const* q_devs, const float* proj_dev,
+                                  const float* tau_dev, const sekv_route_out* routes,
+                                  float* const* o_devs, void* const* ws_devs,
+                                  const size_t* ws_bytes, hipStream_t stream) {
+  return batch_impl(caches, batch, layer, q_devs, proj_dev, tau_dev, routes, o_devs, ws_devs,
+                    ws_bytes, stream, true);
+}
+
+sekv_status sekv_decode_attn_batch(const sekv_cache* const* caches, int32_t batch, int32_t layer,
+                                   const float* const* q_devs, const sekv_route_out* routes,
+                                   float* const* o_devs, void* const* ws_devs,
+                                   const size_t* ws_bytes, hipStream_t stream) {
+  return batch_impl(caches, batch, layer, q_devs, nullptr, nullptr, routes, o_devs, ws_devs,
+                    ws_bytes, stream, false);
+}
+
 void sekv_cache_destroy(sekv_cache* c) { delete c; }
 
 }  // extern "C"

@@ -896,9 +896,11 @@ static_assert(smem_fits<1>() && smem_fits<2>() && smem_fits<3>() && smem_fits<4>
               "LDS layout of the layer kernel");
 static_assert(kChunk <= 64, "a chunk's zoom sets are one wave ballot");
 
+// One layer of one sequence: workgroup `block` of its Hkv x n_work grid.
 template <typename T, int G>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
+__device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
+                                                          const LayerArgs& a, int mode,
+                                                          int block) {
   using Ln = Lanes<T>;
   constexpr int CLOADS = (kChunk / kWaves) / Ln::RPW;     // coarse entries: loads per wave
   constexpr int DLOADS = kRowBlock / Ln::RPW;             // full-resolution rows: loads per pass
@@ -908,7 +910,7 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   float* const stage = stg.v[uniform(wid)];   // this wave's stage, a scalar LDS address
   const int W = geo.n_work;
-  const int g = blockIdx.x / W, w = blockIdx.x % W;
+  const int g = block / W, w = block % W;
   const int sc = geo.n_compressed, D = geo.n_dense, dr = geo.route_dim;
   const int h0 = g * G;
   const int j0 = w * kChunk, nj = w < geo.n_chunks ? min(kChunk, sc - j0) : 0;
@@ -1392,6 +1394,46 @@ void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
     }
   }
   if (tid == 0) __hip_atomic_store(&a.tickets[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T, int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
+  layer_body<T, G>(geo, a, mode, blockIdx.x);
+}
+
+// A batch of sequences, one cache each: blockIdx.y is the sequence; each runs
+// its own Hkv x n_work workgroups and the rest of grid.x returns at once.
+template <typename T, int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void layer_batch_kernel(BatchLayerArgs b, int mode) {
+  const int i = blockIdx.y;
+  if ((int)blockIdx.x >= b.geo[i].n_kv_heads * b.geo[i].n_work) return;
+  layer_body<T, G>(b.geo[i], b.arg[i], mode, blockIdx.x);
+}
+
+hipError_t launch_layer_batch(int bf16, int mode, int group, const BatchLayerArgs& b, int batch,
+                              hipStream_t st) {
+  if (batch < 1 || batch > kMaxBatch) return hipErrorInvalidValue;
+  int nx = 0;
+  for (int i = 0; i < batch; ++i) nx = max(nx, b.geo[i].n_kv_heads * b.geo[i].n_work);
+  const dim3 grid(nx, batch);
+#define SEKV_LAYER(GG)                                                                       \
+  case GG:                                                                                   \
+    if (bf16)                                                                                \
+      hipLaunchKernelGGL((layer_batch_kernel<uint16_t, GG>), grid, dim3(kThreads), 0, st, b, \
+                         mode);                                                              \
+    else                                                                                     \
+      hipLaunchKernelGGL((layer_batch_kernel<float, GG>), grid, dim3(kThreads), 0, st, b,    \
+                         mode);                                                              \
+    break;
+  switch (group) {
+    SEKV_LAYER(1) SEKV_LAYER(2) SEKV_LAYER(3) SEKV_LAYER(4) SEKV_LAYER(5) SEKV_LAYER(6)
+    SEKV_LAYER(7) SEKV_LAYER(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef SEKV_LAYER
+  return hipGetLastError();
 }
 
 hipError_t launch_layer(int bf16, int mode, const LayerGeom& g, const LayerArgs& a,

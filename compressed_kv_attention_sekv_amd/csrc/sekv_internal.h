@@ -186,6 +186,16 @@ struct LayerArgs {
   const float* zero_block; // kZeroBlockFloats zeros
 };
 
+// A batch of independent sequences (one cache each, same model shape) through
+// one launch per layer: every sequence's geometry and pointers travel in the
+// kernel arguments.
+constexpr int kMaxBatch = 8;
+struct BatchLayerArgs {
+  LayerGeom geo[kMaxBatch];
+  LayerArgs arg[kMaxBatch];
+};
+static_assert(sizeof(BatchLayerArgs) + 16 <= 4096, "kernel arguments fit 4 KB");
+
 // launchers (return hipError_t of the launch)
 hipError_t launch_segment(const float* s, int n, int window, double alpha, int min_len,
                           const SegOut& o, hipStream_t st);
@@ -207,6 +217,8 @@ hipError_t launch_span_svd(int bf16, const void* x, int n_tokens, const int32_t*
 
 hipError_t launch_layer(int bf16, int mode, const LayerGeom& g, const LayerArgs& a,
                         hipStream_t st);
+hipError_t launch_layer_batch(int bf16, int mode, int group, const BatchLayerArgs& b, int batch,
+                              hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st);
 hipError_t launch_fetch_gather(const LayerGeom& g, const int32_t* ulist, const int32_t* ucount,
                                const int32_t* clen, const int32_t* rank,

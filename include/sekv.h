@@ -196,6 +196,33 @@ sekv_status sekv_route_attn(const sekv_cache* cache, int32_t layer, const float*
                             const sekv_route_out* route, float* o_dev, void* ws_dev,
                             size_t ws_bytes, hipStream_t stream, hipStream_t fetch_stream);
 
+/* Batched decode: the same layer of `batch` independent sequences
+ * (1 <= batch <= SEKV_MAX_BATCH), one cache each, in one kernel launch (the
+ * per-sequence computation of sekv_route_attn / sekv_decode_attn; batch-4
+ * serving).  The caches must share n_layers, n_q_heads, n_kv_heads,
+ * head_dim, route_dim and kv_dtype, and must be distinct (each holds its own
+ * completion counters); their context lengths may differ.  For sequence i the
+ * arguments are those of the single-sequence call: q_devs[i], routes[i],
+ * o_devs[i], and ws_devs[i] with ws_bytes[i] bytes (at least
+ * sekv_decode_workspace_bytes(caches[i])).  proj_dev and tau_dev are one
+ * model layer's, shared by the batch.  Outputs equal those of the
+ * single-sequence calls bit for bit.  Sequences whose factors are host-tier,
+ * or that have no compressed span, run through the single-sequence path on
+ * `stream` (fetch included).  The pointer arrays are host memory, read during
+ * the call.  Errors: SEKV_ERR_INVALID for a NULL array or pointer, a batch size
+ * outside the range, mixed model shapes, a repeated cache or a short
+ * workspace, checked before anything is launched. */
+#define SEKV_MAX_BATCH 8
+sekv_status sekv_route_attn_batch(const sekv_cache* const* caches, int32_t batch, int32_t layer,
+                                  const float* const* q_devs, const float* proj_dev,
+                                  const float* tau_dev, const sekv_route_out* routes,
+                                  float* const* o_devs, void* const* ws_devs,
+                                  const size_t* ws_bytes, hipStream_t stream);
+sekv_status sekv_decode_attn_batch(const sekv_cache* const* caches, int32_t batch, int32_t layer,
+                                   const float* const* q_devs, const sekv_route_out* routes,
+                                   float* const* o_devs, void* const* ws_devs,
+                                   const size_t* ws_bytes, hipStream_t stream);
+
 void sekv_cache_destroy(sekv_cache* cache);
 
 /* Message of the last failing call on this thread ("" if none). */

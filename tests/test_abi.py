@@ -96,6 +96,25 @@ def test_calls_on_null_cache_are_rejected(L):
     L.sekv_cache_destroy(None)  # no-op
 
 
+def test_batch_calls_reject_bad_arguments(L):
+    P, SZ = ctypes.c_void_p, ctypes.c_size_t
+    n = 2
+    nulls = (P * n)()
+    ros = (S.SekvRouteOut * n)()
+    sizes = (SZ * n)()
+    for fn, extra in ((L.sekv_route_attn_batch, (P(8), P(8))), (L.sekv_decode_attn_batch, ())):
+        def call(caches, batch):
+            return fn(caches, batch, 0, nulls, *extra, ros, nulls, nulls, sizes, None)
+        assert call(None, n) == S.SEKV_ERR_INVALID              # no cache array
+        for batch in (0, -1, S.SEKV_MAX_BATCH + 1):             # batch size out of range
+            assert call(nulls, batch) == S.SEKV_ERR_INVALID
+            assert b"batch" in L.sekv_last_error()
+        assert call(nulls, n) == S.SEKV_ERR_INVALID             # NULL caches in the array
+    # the shared projection and thresholds are required by the routing variant
+    assert L.sekv_route_attn_batch(nulls, n, 0, nulls, None, None, ros, nulls, nulls, sizes,
+                                   None) == S.SEKV_ERR_INVALID
+
+
 def test_binding_checks_tensor_arguments():
     import torch
     cfg = S.make_config(1, 4, 1, kv_dtype="f32")

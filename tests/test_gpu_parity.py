@@ -250,6 +250,58 @@ def test_uneven_zoom_parity_and_repeat(S):
         assert torch.equal(o0, o2)
 
 
+def test_batched_layer_matches_single_calls(S):
+    """Sequences of one model shape (Qwen2.5-14B heads, G = 5), each with its own
+    cache and context length, one of them shorter than the window (no compressed
+    span), through the batched calls (one launch for the rest): routes and
+    outputs bit-identical to the single-sequence calls, and one sequence against
+    the oracle."""
+    base = synth.workload("qwen25_14b_128k_b4", n_layers=1, n_tokens=4096)
+    seed = synth.default_seed(base)
+    lens = [6000, 4096, 300, 9000]
+    log(f"[parity] batched layer, contexts {lens}")
+    inps, caches = [], []
+    for i, n in enumerate(lens):
+        wl = base.with_(n_tokens=n)
+        inp = Inputs(wl, seed, seq=i)
+        inps.append(inp)
+        caches.append(S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks))
+    assert caches[2].info.n_compressed == 0 and caches[0].info.n_compressed > 0
+    Hq, d = base.n_q_heads, base.head_dim
+    p = inps[0].p[0].contiguous()   # one model layer's projections, shared by the batch
+    qs = [inp.query(i)[0].contiguous() for i, inp in enumerate(inps)]
+    orc = OracleSide(inps[0], [0], base.max_rank)
+    prob = orc.route(0, to64(qs[0]), to64(p), np.full(Hq, 2.0), base.gamma).prob
+    tau = torch.tensor([float(np.quantile(prob[h], 0.9)) for h in range(Hq)],
+                       dtype=torch.float32).cuda()   # ~10% zoom per head
+
+    def fresh():
+        return ([S.RouteBuffers.allocate(c, with_prob=True) for c in caches],
+                [torch.zeros(Hq, d, device="cuda") for _ in caches],
+                [torch.empty(c.workspace_bytes(), dtype=torch.uint8, device="cuda") for c in caches])
+    rbs, outs, wss = fresh()
+    S.sekv_route_attn_batch(caches, 0, qs, p, tau, rbs, outs, wss)
+    torch.cuda.synchronize()
+    assert sum(int(r.union_count.sum()) for r in rbs) > 0
+    for i, c in enumerate(caches):
+        rb, o = run_gpu_layer(S, c, 0, qs[i], p, tau, fused=True)
+        assert_same_route(rb, rbs[i])
+        assert torch.equal(o, outs[i]), f"sequence {i}"
+    _, outs_d, wss_d = fresh()
+    S.sekv_decode_attn_batch(caches, 0, qs, rbs, outs_d, wss_d)
+    torch.cuda.synchronize()
+    for i, c in enumerate(caches):
+        _, o = run_gpu_layer(S, c, 0, qs[i], p, tau)
+        assert torch.equal(o, outs_d[i]), f"sequence {i}"
+    route = orc.route(0, to64(qs[0]), to64(p), to64(tau), base.gamma)
+    n_tie = compare_route(rbs[0], route, to64(tau), inps[0].wl)
+    skip = set(tied_heads(route, to64(tau)))
+    ref = orc.decode(0, to64(qs[0]), route)
+    worst = max(rel_err(to64(outs[0])[h], ref[h]) for h in range(Hq) if h not in skip)
+    log(f"[parity] batched layer: ties={n_tie} err={worst:.2e}")
+    assert worst <= TOL["bf16"]
+
+
 def test_host_tier_matches_device_tier(S):
     """Factors in pinned host memory, fetched per layer for the union of the
     zoomed spans: same routes as the device tier, outputs equal up to the
