@@ -881,6 +881,20 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
   __builtin_amdgcn_wave_barrier();
 }
 
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele within each row of 16
+// lanes by DPP row shifts (lanes shifted in from outside the row add 0), then
+// the totals of the rows below each row.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  const int t0 = __builtin_amdgcn_readlane(x, 15), t1 = __builtin_amdgcn_readlane(x, 31),
+            t2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row > 0 ? t0 : 0) + (row > 1 ? t1 : 0) + (row > 2 ? t2 : 0);
+}
+
 // ---------------------------------------------------------------------------
 // the layer kernel
 // ---------------------------------------------------------------------------
@@ -1249,55 +1263,124 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
                     ? a.chunk_bits[((size_t)g * W + tid) * kListWords + li]
                     : 0u;
 
-  if (mode & kMerge) {
-    // thread = (head, 4 dims, stripe of slots): an online pass over its slots,
-    // B slots' loads in flight at a time (all of them up to B * STRIPES slots);
-    // stripes are combined through LDS
-    const int ns = (mode & kZoomSplit) ? 2 * W : W;
-    const float* pg = a.part + (size_t)g * geo.n_slots() * G * kPartStride;
-    constexpr int QUADS = G * (kHeadDim / 4);
-    constexpr int STRIPES = (kThreads / QUADS) > 0 ? (kThreads / QUADS) : 1;
-    constexpr int B = 24;
-    const int quad = tid % QUADS, stripe = tid / QUADS;
-    const int hl = quad / (kHeadDim / 4), dq = quad % (kHeadDim / 4);
-    float M = -INFINITY, Ls = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (stripe < STRIPES) {
-      for (int sl0 = stripe; sl0 < ns; sl0 += B * STRIPES) {
-        float m[B], l[B];
-        float4 x[B];
+  // Merge: thread = (head, 4 dims, stripe of slots), an online pass over its
+  // slots, B slots' loads in flight at a time (all of them up to B * STRIPES
+  // slots); stripes are combined through LDS.  The lists are built while the
+  // first batch of slot loads is in flight.
+  const bool merge = (mode & kMerge) != 0;
+  const int ns = (mode & kZoomSplit) ? 2 * W : W;
+  const float* pg = a.part + (size_t)g * geo.n_slots() * G * kPartStride;
+  constexpr int QUADS = G * (kHeadDim / 4);
+  constexpr int STRIPES = (kThreads / QUADS) > 0 ? (kThreads / QUADS) : 1;
+  constexpr int B = 24;
+  const int quad = tid % QUADS, stripe = tid / QUADS;
+  const int hl = quad / (kHeadDim / 4), dq = quad % (kHeadDim / 4);
+  const bool active = merge && stripe < STRIPES;
+  float M = -INFINITY, Ls = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float m[B], l[B];
+  float4 x[B];
+  auto load_batch = [&](int sl0) {
 #pragma unroll
-        for (int u = 0; u < B; ++u) {
-          const float* p = pg + ((size_t)min(sl0 + u * STRIPES, ns - 1) * G + hl) * kPartStride;
-          const float2 ml = *(const float2*)p;
-          m[u] = ml.x;
-          l[u] = ml.y;
-          x[u] = *(const float4*)(p + 4 + 4 * dq);
-        }
+    for (int u = 0; u < B; ++u) {
+      const float* p = pg + ((size_t)min(sl0 + u * STRIPES, ns - 1) * G + hl) * kPartStride;
+      const float2 ml = *(const float2*)p;
+      m[u] = ml.x;
+      l[u] = ml.y;
+      x[u] = *(const float4*)(p + 4 + 4 * dq);
+    }
+  };
+  auto add_batch = [&](int sl0) {
 #pragma unroll
-        for (int u = 0; u < B; ++u)
-          if (sl0 + u * STRIPES >= ns) m[u] = -INFINITY;   // a clamped duplicate: weight 0
-        float bm = m[0];
+    for (int u = 0; u < B; ++u)
+      if (sl0 + u * STRIPES >= ns) m[u] = -INFINITY;   // a clamped duplicate: weight 0
+    float bm = m[0];
 #pragma unroll
-        for (int u = 1; u < B; ++u) bm = fmaxf(bm, m[u]);
-        if (bm == -INFINITY) continue;
-        const float Mn = fmaxf(M, bm);
-        const float wo = (M == -INFINITY) ? 0.f : __expf(M - Mn);
-        acc.x *= wo;
-        acc.y *= wo;
-        acc.z *= wo;
-        acc.w *= wo;
-        Ls *= wo;
+    for (int u = 1; u < B; ++u) bm = fmaxf(bm, m[u]);
+    if (bm == -INFINITY) return;
+    const float Mn = fmaxf(M, bm);
+    const float wo = (M == -INFINITY) ? 0.f : __expf(M - Mn);
+    acc.x *= wo;
+    acc.y *= wo;
+    acc.z *= wo;
+    acc.w *= wo;
+    Ls *= wo;
 #pragma unroll
-        for (int u = 0; u < B; ++u) {
-          const float wt = (m[u] == -INFINITY) ? 0.f : __expf(m[u] - Mn);
-          acc.x += wt * x[u].x;
-          acc.y += wt * x[u].y;
-          acc.z += wt * x[u].z;
-          acc.w += wt * x[u].w;
-          Ls += wt * l[u];
-        }
-        M = Mn;
+    for (int u = 0; u < B; ++u) {
+      const float wt = (m[u] == -INFINITY) ? 0.f : __expf(m[u] - Mn);
+      acc.x += wt * x[u].x;
+      acc.y += wt * x[u].y;
+      acc.z += wt * x[u].z;
+      acc.w += wt * x[u].w;
+      Ls += wt * l[u];
+    }
+    M = Mn;
+  };
+  // Ascending per-head lists and the group union, from the chunks' zoom bit
+  // masks: a block scan of the popcounts, and each thread writes its chunk's
+  // ids.  The first pass (chunks 0 .. kThreads - 1) uses the masks loaded up
+  // front.
+  auto list_pass = [&](int c, const uint32_t (&word)[kListWords], int (&base)[kListWords]) {
+    int incl[kListWords];
+#pragma unroll
+    for (int li = 0; li <= G; ++li) {
+      incl[li] = wave_incl_scan(__popc(word[li]));
+      if (lane == 63) s.wc[li][wid] = incl[li];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int li = 0; li <= G; ++li) {
+      int off = base[li], tot = 0;
+#pragma unroll
+      for (int wv = 0; wv < kWaves; ++wv) {
+        off += (wv < wid) ? s.wc[li][wv] : 0;
+        tot += s.wc[li][wv];
+      }
+      off += incl[li] - __popc(word[li]);
+      int32_t* dst = li < G ? a.list + (size_t)(h0 + li) * sc : a.ulist + (size_t)g * sc;
+      uint32_t bits = word[li];
+      while (bits) {
+        const int bb = __ffs(bits) - 1;
+        bits &= bits - 1;
+        dst[off++] = c * kChunk + bb;
+      }
+      base[li] += tot;
+    }
+    __syncthreads();
+  };
+  auto lists_all = [&]() {
+    int base[kListWords];
+#pragma unroll
+    for (int li = 0; li < kListWords; ++li) base[li] = 0;
+    list_pass(tid, word0, base);
+    for (int c0 = kThreads; c0 < nc; c0 += kThreads) {
+      const int c = c0 + tid;
+      uint32_t word[kListWords];
+#pragma unroll
+      for (int li = 0; li < kListWords; ++li)
+        word[li] = (li <= G && c < nc) ? a.chunk_bits[((size_t)g * W + c) * kListWords + li] : 0u;
+      list_pass(c, word, base);
+    }
+    if (tid <= G) {
+      int v = 0;
+#pragma unroll
+      for (int li = 0; li <= G; ++li)
+        if (li == tid) v = base[li];
+      if (tid < G) a.count[h0 + tid] = v;
+      else a.ucount[g] = v;
+    }
+  };
+  if (merge) {
+    // every thread issues the first batch (spare threads a copy of stripe
+    // STRIPES - 1's), so the loads are unconditional and the lists' wait for
+    // their masks counts past them
+    load_batch(min(stripe, STRIPES - 1));
+    if (mode & kLists) lists_all();
+    if (active) {
+      add_batch(stripe);
+      for (int sl0 = stripe + B * STRIPES; sl0 < ns; sl0 += B * STRIPES) {
+        load_batch(sl0);
+        add_batch(sl0);
       }
     }
     // the wave scratch is free again
@@ -1334,64 +1417,8 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
       *(float4*)(a.o + (size_t)(h0 + hl) * kHeadDim + 4 * dq) =
           make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
     }
-  }
-
-  if (mode & kLists) {
-    // ascending per-head lists and the group union, from the chunks' zoom bit
-    // masks: one load per (chunk, list), a block scan of the popcounts, and
-    // each thread writes its chunk's ids
-    int base[kListWords];
-#pragma unroll
-    for (int li = 0; li < kListWords; ++li) base[li] = 0;
-    for (int c0 = 0; c0 < nc; c0 += kThreads) {
-      const int c = c0 + tid;
-      uint32_t word[kListWords];
-      int incl[kListWords];
-#pragma unroll
-      for (int li = 0; li <= G; ++li)
-        word[li] = c0 == 0 ? word0[li]
-                           : (c < nc ? a.chunk_bits[((size_t)g * W + c) * kListWords + li] : 0u);
-#pragma unroll
-      for (int li = 0; li <= G; ++li) {
-        const int cnt = __popc(word[li]);
-        int x = cnt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(x, o, 64);
-          if (lane >= o) x += y;
-        }
-        incl[li] = x;
-        if (lane == 63) s.wc[li][wid] = x;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int li = 0; li <= G; ++li) {
-        int off = base[li], tot = 0;
-#pragma unroll
-        for (int wv = 0; wv < kWaves; ++wv) {
-          off += (wv < wid) ? s.wc[li][wv] : 0;
-          tot += s.wc[li][wv];
-        }
-        off += incl[li] - __popc(word[li]);
-        int32_t* dst = li < G ? a.list + (size_t)(h0 + li) * sc : a.ulist + (size_t)g * sc;
-        uint32_t bits = word[li];
-        while (bits) {
-          const int b = __ffs(bits) - 1;
-          bits &= bits - 1;
-          dst[off++] = c * kChunk + b;
-        }
-        base[li] += tot;
-      }
-      __syncthreads();
-    }
-    if (tid <= G) {
-      int v = 0;
-#pragma unroll
-      for (int li = 0; li <= G; ++li)
-        if (li == tid) v = base[li];
-      if (tid < G) a.count[h0 + tid] = v;
-      else a.ucount[g] = v;
-    }
+  } else if (mode & kLists) {
+    lists_all();
   }
   if (tid == 0) __hip_atomic_store(&a.tickets[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
