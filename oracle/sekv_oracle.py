@@ -39,7 +39,11 @@ silent.  The readings are:
   * attention: one softmax over dense tokens (window, anchors, short-span
     tokens), one coarse entry per non-zoomed span with + ln n_j added to its
     scaled score, and the rank-r reconstruction of every zoomed span's tokens;
-    score scale 1/sqrt(d) (Sec. 3.3; summary sec. 3).
+    score scale 1/sqrt(d) (Sec. 3.3; summary sec. 3);
+  * budget cap (optional): per layer and KV head, the reconstructed spans'
+    total length is capped; spans are kept by decreasing gate value (the
+    largest over the group's heads that selected them), ties by lower id,
+    as long as the total fits (Sec. 3.3, the matched-budget paragraph).
 """
 from __future__ import annotations
 
@@ -351,6 +355,43 @@ def route_layer(q, p_proj, tau, summaries: Dict[int, np.ndarray], seg: Segmentat
     sc = seg.n_compressed
     return LayerRoute(prob=np.array(probs).reshape(hq, sc), mask=np.array(masks).reshape(hq, sc),
                       lists=lists, unions=unions)
+
+
+def cap_budget(route: LayerRoute, seg: Segmentation, n_kv_heads: int, budget: int) -> LayerRoute:
+    """The matched-budget cap of the zoom decisions (Sec. 3.3, zoom-in decoding:
+    when the selected spans exceed the budget, spans are kept in decreasing
+    order of their gate value until the budget is filled).
+
+    Reading taken: the budget counts the tokens a KV head reconstructs in one
+    layer, i.e. the lengths n_j of the spans in its union; a span's order key is
+    the largest gate value among the group's heads that selected it, ties going
+    to the lower span id; the kept spans are the longest prefix of that order
+    whose total length is at most ``budget``.  A kept span stays zoomed for the
+    heads that selected it; a dropped one reverts to its coarse entry for all."""
+    hq = route.mask.shape[0]
+    group = hq // n_kv_heads
+    n = seg.span_len[seg.cspan].astype(np.int64)
+    mask = route.mask.copy()
+    for g in range(n_kv_heads):
+        heads = range(g * group, (g + 1) * group)
+        cand = union_lists([route.mask[h] for h in heads])
+        if cand.size == 0:
+            continue
+        key = np.array([max(route.prob[h, j] for h in heads if route.mask[h, j]) for j in cand])
+        order = sorted(range(cand.size), key=lambda i: (-key[i], cand[i]))
+        kept = np.zeros(seg.n_compressed, dtype=bool)
+        total = 0
+        for i in order:
+            j = cand[i]
+            if total + n[j] > budget:
+                break
+            total += n[j]
+            kept[j] = True
+        for h in heads:
+            mask[h] &= kept
+    lists = [compact(z) for z in mask]
+    unions = [union_lists(list(mask[g * group:(g + 1) * group])) for g in range(n_kv_heads)]
+    return LayerRoute(prob=route.prob, mask=mask, lists=lists, unions=unions)
 
 
 def decode_layer(q, route: LayerRoute, groups: Dict[int, GroupCache], seg: Segmentation,

@@ -8,6 +8,7 @@ attention, numpy's std, LAPACK eigenvalues), or brute force on tiny inputs.
 import json
 import math
 import os
+import types
 
 import numpy as np
 import pytest
@@ -391,3 +392,71 @@ def test_truncation_moves_output_by_bounded_amount():
         errs.append(max(np.abs(out[h] - ref[h]).max() for h in range(4)))
     assert errs[-1] < 1e-10
     assert errs[0] > errs[1] > errs[2] > errs[3]
+
+
+# ---------------------------------------------------------------------------
+# budget cap (Sec. 3.3, matched-budget paragraph)
+# ---------------------------------------------------------------------------
+
+def _route_of(prob, tau):
+    prob = np.asarray(prob, dtype=np.float64)
+    mask = prob > tau
+    return O.LayerRoute(prob=prob, mask=mask, lists=[O.compact(z) for z in mask], unions=[])
+
+
+def _seg_of(span_len):
+    n = np.asarray(span_len, dtype=np.int64)
+    return types.SimpleNamespace(span_len=n, cspan=np.arange(n.size), n_compressed=n.size)
+
+
+@pytest.mark.parametrize("case", _golden("budget_cap_tiny.json")["cases"], ids=lambda c: str(c["budget"]))
+def test_budget_cap_golden(case):
+    gold = _golden("budget_cap_tiny.json")
+    route = _route_of(gold["prob"], gold["tau"])
+    capped = O.cap_budget(route, _seg_of(gold["span_len"]), gold["n_kv_heads"], case["budget"])
+    assert capped.mask.astype(int).tolist() == case["mask"]
+    assert [u.tolist() for u in capped.unions] == case["unions"]
+    assert [l.tolist() for l in capped.lists] == [list(np.flatnonzero(m)) for m in case["mask"]]
+
+
+def test_budget_cap_properties():
+    """On random routes: the kept spans of each group are a prefix of the
+    order (key descending, id ascending) whose total fits and whose next span
+    would not; the cap only removes zooms; it is monotone in the budget and
+    leaves a route unchanged once the budget covers the whole union."""
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        hkv, grp, sc = int(rng.integers(1, 4)), int(rng.integers(1, 5)), int(rng.integers(1, 40))
+        hq = hkv * grp
+        prob = rng.random((hq, sc))
+        if trial % 3 == 0:
+            prob = np.round(prob, 1)   # many ties
+        n = rng.integers(1, 60, sc)
+        route = _route_of(prob, rng.random())
+        seg = _seg_of(n)
+        full = [int(n[O.union_lists(list(route.mask[g * grp:(g + 1) * grp]))].sum()) for g in range(hkv)]
+        prev = None
+        for budget in sorted(int(b) for b in rng.integers(0, max(full) + 2, 5)):
+            capped = O.cap_budget(route, seg, hkv, budget)
+            assert not (capped.mask & ~route.mask).any()
+            for g in range(hkv):
+                hs = slice(g * grp, (g + 1) * grp)
+                cand = O.union_lists(list(route.mask[hs]))
+                kept = set(O.union_lists(list(capped.mask[hs])).tolist())
+                assert sum(n[j] for j in kept) <= budget
+                if not cand.size:
+                    continue
+                key = {j: prob[hs][route.mask[hs][:, j], j].max() for j in cand}
+                order = sorted(cand, key=lambda j: (-key[j], j))
+                k = len(kept)
+                assert set(order[:k]) == kept
+                if k < len(order):
+                    assert sum(n[j] for j in order[:k + 1]) > budget
+                # a kept span stays zoomed for exactly the heads that chose it
+                for j in kept:
+                    assert (capped.mask[hs][:, j] == route.mask[hs][:, j]).all()
+            if prev is not None:
+                assert not (prev & ~capped.mask).any()
+            prev = capped.mask
+        big = O.cap_budget(route, seg, hkv, max(full))
+        assert (big.mask == route.mask).all()
