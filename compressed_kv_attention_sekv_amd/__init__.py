@@ -19,7 +19,7 @@ __all__ = [
     "SekvError", "SekvConfig", "SekvCacheInfo", "SekvRouteOut", "lib", "library_path",
     "make_config", "Cache", "RouteBuffers", "sekv_segment", "sekv_build_spans", "sekv_route",
     "sekv_decode_attn", "sekv_route_attn", "sekv_decode_attn_batch", "sekv_route_attn_batch",
-    "sekv_decode_workspace_bytes", "EXPORTED_SYMBOLS", "SEKV_MAX_BATCH",
+    "sekv_cap_budget", "sekv_decode_workspace_bytes", "EXPORTED_SYMBOLS", "SEKV_MAX_BATCH",
     "SEKV_F32", "SEKV_BF16", "SEKV_TIER_DEVICE", "SEKV_TIER_HOST_PINNED",
 ]
 
@@ -32,7 +32,8 @@ EXPORTED_SYMBOLS = (
     "sekv_segment", "sekv_build_spans", "sekv_cache_info_get", "sekv_cache_copy_spans",
     "sekv_cache_copy_group", "sekv_cache_copy_factors", "sekv_route",
     "sekv_decode_workspace_bytes", "sekv_decode_attn", "sekv_route_attn",
-    "sekv_decode_attn_batch", "sekv_route_attn_batch", "sekv_cache_destroy", "sekv_last_error",
+    "sekv_decode_attn_batch", "sekv_route_attn_batch", "sekv_cap_budget", "sekv_cache_destroy",
+    "sekv_last_error",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -113,6 +114,7 @@ def lib() -> ctypes.CDLL:
         "sekv_decode_attn_batch": (I32, [ctypes.POINTER(P), I32, I32, ctypes.POINTER(P),
                                          ctypes.POINTER(SekvRouteOut), ctypes.POINTER(P),
                                          ctypes.POINTER(P), ctypes.POINTER(SZ), P]),
+        "sekv_cap_budget": (I32, [P, ctypes.POINTER(SekvRouteOut), ctypes.c_int64, P]),
         "sekv_cache_destroy": (None, [P]),
         "sekv_last_error": (ctypes.c_char_p, []),
     }
@@ -339,6 +341,16 @@ def sekv_route_attn(cache: Cache, layer: int, q: torch.Tensor, proj: torch.Tenso
                                  ctypes.byref(st), _ptr(o), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream),
                                  fst))
+
+
+def sekv_cap_budget(cache: Cache, route: RouteBuffers, budget_tokens: int, stream=None) -> None:
+    """Cap one layer's zoom decisions to ``budget_tokens`` reconstructed tokens
+    per KV head, in place (``route`` must carry gate values)."""
+    if route.prob is None:
+        raise ValueError("the budget cap needs the route's gate values: allocate with_prob=True")
+    st = route.struct()
+    _check(lib().sekv_cap_budget(cache.handle, ctypes.byref(st), int(budget_tokens),
+                                 _stream(stream)))
 
 
 def _batch_arrays(caches, qs, routes, os_, workspaces):

@@ -600,6 +600,26 @@ sekv_status sekv_route_attn(const sekv_cache* c, int32_t layer, const float* q_d
   return SEKV_OK;
 }
 
+sekv_status sekv_cap_budget(const sekv_cache* c, const sekv_route_out* route,
+                            int64_t budget_tokens, hipStream_t stream) {
+  sekv_status r;
+  if (!c) return fail(SEKV_ERR_INVALID, "cache is NULL");
+  if ((r = check_route_out(route))) return r;
+  if (!route->prob)
+    return fail(SEKV_ERR_INVALID, "the budget cap orders spans by gate value: route prob is NULL");
+  if (budget_tokens < 0)
+    return fail(SEKV_ERR_INVALID, "budget_tokens must be >= 0 (got %lld)",
+                (long long)budget_tokens);
+  if (c->sc > kCapMaxSpans)
+    return fail(SEKV_ERR_UNSUPPORTED, "the budget cap handles at most %d compressed spans (cache "
+                "has %d)", kCapMaxSpans, c->sc);
+  if (c->sc == 0) return SEKV_OK;
+  SEKV_HIP(launch_cap_budget(c->sc, c->cfg.n_kv_heads, c->group, (long long)budget_tokens,
+                             c->clen, route->prob, route->mask, route->list, route->count,
+                             route->union_list, route->union_count, stream));
+  return SEKV_OK;
+}
+
 // ---- batches of sequences -------------------------------------------------------
 static_assert(kMaxBatch == SEKV_MAX_BATCH, "one batch limit");
 

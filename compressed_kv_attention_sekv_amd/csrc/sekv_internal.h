@@ -220,6 +220,13 @@ hipError_t launch_layer(int bf16, int mode, const LayerGeom& g, const LayerArgs&
 hipError_t launch_layer_batch(int bf16, int mode, int group, const BatchLayerArgs& b, int batch,
                               hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st);
+// matched-budget cap of one layer's route output (in place); the kernel keeps
+// one bit per union entry in LDS, so S_c is limited to kCapMaxSpans
+constexpr int kCapMaxSpans = 1 << 19;
+size_t cap_budget_lds_bytes(int sc);
+hipError_t launch_cap_budget(int sc, int hkv, int group, long long budget, const int32_t* clen,
+                             const double* prob, uint8_t* mask, int32_t* list, int32_t* count,
+                             int32_t* ulist, int32_t* ucount, hipStream_t st);
 hipError_t launch_fetch_gather(const LayerGeom& g, const int32_t* ulist, const int32_t* ucount,
                                const int32_t* clen, const int32_t* rank,
                                const uint64_t* fac_off, uint64_t layer_base,

@@ -196,6 +196,29 @@ sekv_status sekv_route_attn(const sekv_cache* cache, int32_t layer, const float*
                             const sekv_route_out* route, float* o_dev, void* ws_dev,
                             size_t ws_bytes, hipStream_t stream, hipStream_t fetch_stream);
 
+/* Matched-budget cap of one layer's zoom decisions (SeKV paper Sec. 3.3,
+ * zoom-in decoding: past the GPU KV budget, spans are kept in decreasing order
+ * of their gate value until the budget is filled).  Per KV head g, the
+ * candidates are the spans of route->union_list[g]; a candidate's key is the
+ * largest gate value p among the heads of g that zoomed it, ties going to the
+ * lower span id; the kept candidates are the longest prefix of that order
+ * whose total length sum n_j is at most budget_tokens (the budget counts the
+ * tokens one KV head reconstructs in this layer).  A kept span stays zoomed
+ * for the heads that selected it; a dropped one leaves the mask of every head
+ * of g and reverts to its coarse entry.
+ *   route: the output of sekv_route or sekv_route_attn for this cache, made
+ *          with prob != NULL; its mask, list, count, union_list and
+ *          union_count are rewritten in place (lists stay ascending), prob is
+ *          only read.  Pass the result to sekv_decode_attn.
+ *   budget_tokens >= 0; 0 zooms nothing, a budget at least the union's total
+ *          length changes nothing.
+ * Asynchronous on `stream`; the route buffers must not be in use by other
+ * work until it completes.  Errors: SEKV_ERR_INVALID for a NULL cache, route
+ * buffer or prob, or a negative budget; SEKV_ERR_UNSUPPORTED for caches of
+ * more than 2^19 compressed spans. */
+sekv_status sekv_cap_budget(const sekv_cache* cache, const sekv_route_out* route,
+                            int64_t budget_tokens, hipStream_t stream);
+
 /* Batched decode: the same layer of `batch` independent sequences
  * (1 <= batch <= SEKV_MAX_BATCH), one cache each, in one kernel launch (the
  * per-sequence computation of sekv_route_attn / sekv_decode_attn; batch-4
