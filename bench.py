@@ -47,6 +47,12 @@ def parse():
     ap.add_argument("--cpu-layers", type=int, default=3)
     ap.add_argument("--n-layers", type=int, default=None, help="override layer count (testing)")
     ap.add_argument("--n-tokens", type=int, default=None, help="override context (testing)")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="sequences per step (default: the workload's); above 1 each layer runs "
+                         "through the batched call, one launch for all sequences")
+    ap.add_argument("--zoom-frac", type=float, default=None,
+                    help="share of spans every query head zooms (workloads with one share for "
+                         "all heads, e.g. the batch-4 sweep)")
     return ap.parse_args()
 
 
@@ -90,38 +96,57 @@ def main():
         over["n_layers"] = args.n_layers
     if args.n_tokens:
         over["n_tokens"] = args.n_tokens
+    if args.batch is not None:
+        over["batch"] = args.batch
     wl = synth.workload(args.workload, **over)
-    if wl.batch != 1:
-        wl = wl.with_(batch=1)
+    B = wl.batch
+    if not 1 <= B <= S.SEKV_MAX_BATCH:
+        print(f"--batch must be in [1, {S.SEKV_MAX_BATCH}]", file=sys.stderr)
+        sys.exit(2)
+    if B > 1 and args.tier != "device":
+        print("batched steps run with device-tier factors only", file=sys.stderr)
+        sys.exit(2)
     seed = synth.default_seed(wl)
     L, Hq, Hkv, d, G = wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.group
 
-    # ---- inputs, resident in HBM -------------------------------------------------
-    t0 = time.time()
-    s, spike = synth.surprisal(wl, seed, device=dev)
-    k, v, ranks = synth.kv_cache(wl, seed, spike, device=dev)
+    # ---- inputs, resident in HBM, and one cache per sequence ---------------------
     w, p = synth.route_weights(wl, seed, device=dev)
-    torch.cuda.synchronize()
-    log(f"inputs drawn in {time.time() - t0:.1f}s: K/V {2 * k.numel() * k.element_size() / 1e9:.1f} GB")
-
     cfg = S.make_config(L, Hq, Hkv, head_dim=d, route_dim=wl.route_dim, window=wl.window,
                         max_rank=wl.max_rank, min_span_len=wl.min_span_len, alpha=wl.alpha,
                         gamma=wl.gamma, kv_dtype=wl.kv_dtype, factor_tier=args.tier)
-    torch.cuda.synchronize()
-    t0 = time.time()
-    cache = S.sekv_build_spans(cfg, s, k, v, w, ranks)
-    torch.cuda.synchronize()
-    build_s = time.time() - t0
+    caches, build_s = [], 0.0
+    for b in range(B):
+        t0 = time.time()
+        s_b, spike_b = synth.surprisal(wl, seed, seq=b, device=dev)
+        k, v, ranks_b = synth.kv_cache(wl, seed, spike_b, seq=b, device=dev)
+        torch.cuda.synchronize()
+        log(f"sequence {b}: inputs drawn in {time.time() - t0:.1f}s: K/V "
+            f"{2 * k.numel() * k.element_size() / 1e9:.1f} GB")
+        t0 = time.time()
+        c = S.sekv_build_spans(cfg, s_b, k, v, w, ranks_b)
+        torch.cuda.synchronize()
+        dt = time.time() - t0
+        build_s += dt
+        i_ = c.info
+        log(f"sequence {b}: build {dt:.2f}s: spans {i_.n_spans} compressed {i_.n_compressed} "
+            f"anchors {i_.n_anchors} dense {i_.n_dense} factor pool "
+            f"{i_.factor_pool_bytes / 1e9:.2f} GB")
+        caches.append(c)
+        if b == 0:
+            s, spike, ranks = s_b, spike_b, ranks_b   # the CPU baseline's sample
+        # the K/V inputs are not needed by the decode step
+        del k, v
+        torch.cuda.empty_cache()
+    cache = caches[0]
     info = cache.info
-    log(f"build {build_s:.2f}s: spans {info.n_spans} compressed {info.n_compressed} anchors "
-        f"{info.n_anchors} dense {info.n_dense} factor pool {info.factor_pool_bytes / 1e9:.2f} GB")
     sc = info.n_compressed
-    # the K/V inputs are not needed by the decode step
-    del k, v
-    torch.cuda.empty_cache()
 
-    # ---- thresholds: calibrated on the library's own gate values ---------------
-    targets = synth.zoom_targets(wl, seed) if wl.tau_mode != "uniform" else None
+    # ---- thresholds: calibrated on the library's own gate values (sequence 0;
+    # thresholds belong to the model, so every sequence uses them) -------------
+    if wl.tau_mode == "uniform":
+        targets = None
+    else:
+        targets = synth.zoom_targets(wl, seed, frac=args.zoom_frac)
     if targets is None:
         tau = synth.tau_uniform(wl, seed, device=dev)
     else:
@@ -135,24 +160,34 @@ def main():
                 S.sekv_route(cache, layer, cq[i, layer].contiguous(), p[layer].contiguous(), big, rb)
                 probs.append(rb.prob.clone())
             allp = torch.cat(probs, dim=1)
-            tau[layer] = torch.stack([torch.quantile(allp[h], 1.0 - float(targets[layer, h]))
-                                      for h in range(Hq)]).float()
+            # a share of 0 zooms nothing (p <= 1 is never above 1), 1 zooms all
+            tau[layer] = torch.stack([
+                torch.tensor(1.0, device=dev) if float(targets[layer, h]) <= 0.0 else
+                torch.tensor(-1.0, device=dev) if float(targets[layer, h]) >= 1.0 else
+                torch.quantile(allp[h], 1.0 - float(targets[layer, h])).float()
+                for h in range(Hq)]).float()
         torch.cuda.synchronize()
 
     # ---- per-step buffers ----------------------------------------------------------
     n_q = args.steps + args.warmup
-    qs = torch.stack([synth.queries(wl, seed, i, device=dev) for i in range(n_q)])  # [T][L][Hq][d]
-    q_cur = torch.empty(L, Hq, d, device=dev)
+    qs = torch.stack([torch.stack([synth.queries(wl, seed, i, seq=b, device=dev)
+                                   for b in range(B)]) for i in range(n_q)])  # [T][B][L][Hq][d]
+    q_cur = torch.empty(B, L, Hq, d, device=dev)
     p_c = [p[l].contiguous() for l in range(L)]
     tau_c = [tau[l].contiguous() for l in range(L)]
-    routes = [S.RouteBuffers.allocate(cache) for _ in range(L)]
-    outs = torch.zeros(L, Hq, d, device=dev)
-    ws = torch.empty(cache.workspace_bytes(), dtype=torch.uint8, device=dev)
+    routes = [[S.RouteBuffers.allocate(c) for _ in range(L)] for c in caches]   # [B][L]
+    outs = torch.zeros(B, L, Hq, d, device=dev)
+    wss = [torch.empty(c.workspace_bytes(), dtype=torch.uint8, device=dev) for c in caches]
     side = torch.cuda.Stream() if args.tier == "host" else None
 
     def layer_call(layer):
-        S.sekv_route_attn(cache, layer, q_cur[layer], p_c[layer], tau_c[layer], routes[layer],
-                          outs[layer], ws, fetch_stream=side)
+        if B == 1:
+            S.sekv_route_attn(cache, layer, q_cur[0, layer], p_c[layer], tau_c[layer],
+                              routes[0][layer], outs[0, layer], wss[0], fetch_stream=side)
+        else:
+            S.sekv_route_attn_batch(caches, layer, [q_cur[b, layer] for b in range(B)],
+                                    p_c[layer], tau_c[layer], [r[layer] for r in routes],
+                                    [outs[b, layer] for b in range(B)], wss)
 
     def step():
         for layer in range(L):
@@ -195,32 +230,41 @@ def main():
     log(f"{args.steps} steps in {total_ms:.1f} ms (wall {wall * 1e3:.1f} ms): {ms_per_step:.4f} ms/step")
 
     # ---- algorithmic bytes of the timed steps ----------------------------------
+    # per sequence: the resident bytes every layer launch reads, and the factor
+    # bytes 8 r (n + d + 1) of each (layer, KV head, span) for the zoom part
     eb = 2 if wl.kv_dtype == "bf16" else 4
-    clen = torch.tensor([0], dtype=torch.int64)
-    sp = cache.spans()
-    clen = sp["span_len"][sp["cspan"].long()].to(torch.float64)
-    rank_tab = torch.stack([torch.stack([cache.group_data(l, g)[3] for g in range(Hkv)])
-                            for l in range(L)]).to(torch.float64)  # [L][Hkv][Sc]
-    span_bytes = (8.0 * rank_tab * (clen + d + 1)).to(dev)      # factor bytes per (l, g, j)
-    D = info.n_dense
-    resident_layer = (Hkv * (2 * d * eb * D + 2 * d * eb * sc) + Hq * wl.route_dim * eb * sc +
-                      Hq * (wl.route_dim * d + d + 1) * 4 + Hq * d * 4 + 4 * sc)
+    span_bytes, resident_layer = [], 0
+    for c in caches:
+        sp = c.spans()
+        clen = sp["span_len"][sp["cspan"].long()].to(torch.float64)
+        rank_tab = torch.stack([torch.stack([c.group_data(l, g)[3] for g in range(Hkv)])
+                                for l in range(L)]).to(torch.float64)  # [L][Hkv][Sc]
+        span_bytes.append((8.0 * rank_tab * (clen + d + 1)).to(dev))
+        D_b, sc_b = c.info.n_dense, c.info.n_compressed
+        resident_layer += (Hkv * (2 * d * eb * D_b + 2 * d * eb * sc_b) +
+                           Hq * wl.route_dim * eb * sc_b + Hq * (wl.route_dim * d + d + 1) * 4 +
+                           Hq * d * 4 + 4 * sc_b)
 
     zoom_bytes = torch.zeros(args.steps, L, dtype=torch.float64, device=dev)
     zoom_frac = torch.zeros(L, Hq, dtype=torch.float64, device=dev)
     union_frac = torch.zeros(L, Hkv, dtype=torch.float64, device=dev)
-    ar = torch.arange(max(sc, 1), device=dev)
     for si, i in enumerate(range(args.warmup, n_q)):
         q_cur.copy_(qs[i])
         for layer in range(L):
-            rb = routes[layer]
             layer_call(layer)
-            valid = ar.unsqueeze(0) < rb.union_count.unsqueeze(1)               # [Hkv][Sc]
-            ids = torch.where(valid, rb.union_list.long(), torch.zeros_like(rb.union_list.long()))
-            zb = torch.gather(span_bytes[layer], 1, ids) * valid
-            zoom_bytes[si, layer] = zb.sum()
-            zoom_frac[layer] += rb.count.double() / max(sc, 1)
-            union_frac[layer] += rb.union_count.double() / max(sc, 1)
+            for b, c in enumerate(caches):
+                rb = routes[b][layer]
+                sc_b = c.info.n_compressed
+                if sc_b == 0:
+                    continue
+                ar = torch.arange(sc_b, device=dev)
+                valid = ar.unsqueeze(0) < rb.union_count.unsqueeze(1)           # [Hkv][Sc]
+                ids = torch.where(valid, rb.union_list.long(),
+                                  torch.zeros_like(rb.union_list.long()))
+                zb = torch.gather(span_bytes[b][layer], 1, ids) * valid
+                zoom_bytes[si, layer] += zb.sum()
+                zoom_frac[layer] += rb.count.double() / (sc_b * B)
+                union_frac[layer] += rb.union_count.double() / (sc_b * B)
     torch.cuda.synchronize()
     zoom_frac /= args.steps
     union_frac /= args.steps
@@ -278,7 +322,7 @@ def main():
     # ---- CPU oracle baseline on a bounded sample --------------------------------
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, seed, s, spike, w, p, tau, qs, args, ranks)
+        cpu = cpu_baseline(wl, seed, s, spike, w, p, tau, qs[:, 0], args, ranks, B)
 
     traffic = read_traffic(wl.name)
     result = {
@@ -296,9 +340,12 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": wl.name, "n_layers": L, "n_q_heads": Hq, "n_kv_heads": Hkv,
-            "head_dim": d, "context": wl.n_tokens, "batch": 1, "kv_dtype": wl.kv_dtype,
+            "head_dim": d, "context": wl.n_tokens, "batch": B, "kv_dtype": wl.kv_dtype,
             "factor_dtype": "f32", "factor_tier": args.tier, "window": wl.window,
             "max_rank": wl.max_rank, "route_dim": wl.route_dim, "graph": graph is not None,
+            "zoom": ("skewed" if wl.tau_mode == "skewed" else
+                     (f"{float(targets[0, 0]):g} per head" if targets is not None
+                      else "uniform tau")),
         },
         "roofline": {
             "bound": "hbm",
@@ -307,7 +354,10 @@ def main():
             "unit": "GB/s",
             "frac": attn_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": "sekv::layer_kernel (sekv_route_attn, one layer: route + attention)",
+            "kernel": ("sekv::layer_kernel (sekv_route_attn, one layer: route + attention)"
+                       if B == 1 else
+                       f"sekv::layer_batch_kernel (sekv_route_attn_batch, one layer of {B} "
+                       "sequences: route + attention)"),
             "algorithmic_bytes_per_launch": attn_bytes_meas,
             "avg_launch_us": attn_us_mean,
             "avg_launch_from": "HIP events around the timed region / (steps x layers)",
@@ -322,16 +372,18 @@ def main():
                   "resident_gb": info.resident_bytes / 1e9, "build_s": build_s,
                   "zoom_frac_per_head_mean": float(zoom_frac.mean()),
                   "union_frac_per_group_mean": float(union_frac.mean()),
-                  "zoom_bytes_per_step_gb": float(zb_step.mean()) / 1e9},
+                  "zoom_bytes_per_step_gb": float(zb_step.mean()) / 1e9,
+                  "tokens_per_s": B * 1e3 / ms_per_step},
     }
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(wl, seed, s, spike, w, p, tau, qs, args, ranks):
+def cpu_baseline(wl, seed, s, spike, w, p, tau, qs, args, ranks, batch=1):
     """The oracle as it stands, on one thread: build the oracle's cache for a
     few layers spread over the depth (untimed), then time its decode (route +
     attention, every query head) of those layers over fresh step queries until
-    about 10 s of CPU work, and scale to a full step."""
+    about 10 s of CPU work, and scale to a full step (of sequence 0; a step of
+    a batch is ``batch`` such sequences)."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -371,13 +423,14 @@ def cpu_baseline(wl, seed, s, spike, w, p, tau, qs, args, ranks):
                 O.decode_layer(q[layer], route, groups[layer], seg, n_kv_heads=wl.n_kv_heads)
             dt += time.time() - t0
             n_steps += 1
-    per_step = dt / (n_steps * len(layers)) * L
+    per_step = dt / (n_steps * len(layers)) * L * batch
     log(f"cpu oracle: layers {layers} x {n_steps} steps decoded in {dt:.2f}s (build {build_s:.1f}s) "
         f"-> {per_step:.2f} s/step")
     return {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
             "sample": f"{n_steps} decode steps of layers {layers} ({len(layers)} of {L}), all "
                       f"{wl.n_q_heads} query heads, route + attention, float64 numpy on one "
-                      f"thread ({dt:.1f} s); time per layer scaled by {L}",
+                      f"thread ({dt:.1f} s); time per layer scaled by {L}" +
+                      (f" and by {batch} sequences" if batch > 1 else ""),
             "host_threads_available": os.cpu_count()}
 
 
