@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--batch", type=int, default=None,
                     help="sequences per step (default: the workload's); above 1 each layer runs "
                          "through the batched call, one launch for all sequences")
+    ap.add_argument("--budget", type=int, default=None,
+                    help="matched-budget cap in tokens per KV head and layer: each layer runs "
+                         "sekv_route (gate values kept), sekv_cap_budget, sekv_decode_attn")
     ap.add_argument("--zoom-frac", type=float, default=None,
                     help="share of spans every query head zooms (workloads with one share for "
                          "all heads, e.g. the batch-4 sweep)")
@@ -105,6 +108,9 @@ def main():
         sys.exit(2)
     if B > 1 and args.tier != "device":
         print("batched steps run with device-tier factors only", file=sys.stderr)
+        sys.exit(2)
+    if args.budget is not None and (B > 1 or args.budget < 0):
+        print("--budget takes a count >= 0 and one sequence", file=sys.stderr)
         sys.exit(2)
     seed = synth.default_seed(wl)
     L, Hq, Hkv, d, G = wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.group
@@ -175,13 +181,20 @@ def main():
     q_cur = torch.empty(B, L, Hq, d, device=dev)
     p_c = [p[l].contiguous() for l in range(L)]
     tau_c = [tau[l].contiguous() for l in range(L)]
-    routes = [[S.RouteBuffers.allocate(c) for _ in range(L)] for c in caches]   # [B][L]
+    capped = args.budget is not None
+    routes = [[S.RouteBuffers.allocate(c, with_prob=capped) for _ in range(L)]
+              for c in caches]   # [B][L]
     outs = torch.zeros(B, L, Hq, d, device=dev)
     wss = [torch.empty(c.workspace_bytes(), dtype=torch.uint8, device=dev) for c in caches]
     side = torch.cuda.Stream() if args.tier == "host" else None
 
     def layer_call(layer):
-        if B == 1:
+        if capped:
+            S.sekv_route(cache, layer, q_cur[0, layer], p_c[layer], tau_c[layer], routes[0][layer])
+            S.sekv_cap_budget(cache, routes[0][layer], args.budget)
+            S.sekv_decode_attn(cache, layer, q_cur[0, layer], routes[0][layer], outs[0, layer],
+                               wss[0], fetch_stream=side)
+        elif B == 1:
             S.sekv_route_attn(cache, layer, q_cur[0, layer], p_c[layer], tau_c[layer],
                               routes[0][layer], outs[0, layer], wss[0], fetch_stream=side)
         else:
@@ -281,7 +294,7 @@ def main():
     # launches give the kernel's mean duration (plus one small query copy per
     # step).  Algorithmic bytes: the timed steps' zoomed-span factors per launch
     # plus the resident bytes every launch reads.
-    attn_us_mean = total_ms * 1e3 / (args.steps * L)
+    attn_us_mean = total_ms * 1e3 / (args.steps * L)   # with --budget: the layer's 3 launches
     attn_bytes_meas = float(zoom_bytes.mean()) + resident_layer
     attn_gbs = attn_bytes_meas / (attn_us_mean * 1e-6) / 1e9
     log(f"layer launch: {attn_us_mean:.2f} us avg, {attn_bytes_meas / 1e6:.2f} MB algorithmic "
@@ -343,6 +356,7 @@ def main():
             "head_dim": d, "context": wl.n_tokens, "batch": B, "kv_dtype": wl.kv_dtype,
             "factor_dtype": "f32", "factor_tier": args.tier, "window": wl.window,
             "max_rank": wl.max_rank, "route_dim": wl.route_dim, "graph": graph is not None,
+            "budget_tokens": args.budget,
             "zoom": ("skewed" if wl.tau_mode == "skewed" else
                      (f"{float(targets[0, 0]):g} per head" if targets is not None
                       else "uniform tau")),
@@ -354,7 +368,9 @@ def main():
             "unit": "GB/s",
             "frac": attn_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": ("sekv::layer_kernel (sekv_route_attn, one layer: route + attention)"
+            "kernel": ("sekv::layer_kernel x2 + sekv::cap_budget_kernel (sekv_route, "
+                       "sekv_cap_budget, sekv_decode_attn: one layer, capped)" if capped else
+                       "sekv::layer_kernel (sekv_route_attn, one layer: route + attention)"
                        if B == 1 else
                        f"sekv::layer_batch_kernel (sekv_route_attn_batch, one layer of {B} "
                        "sequences: route + attention)"),

@@ -10,11 +10,14 @@
 // kept set is the longest prefix that fits).  A dropped span reverts to its
 // coarse entry for every head of the group.
 //
-// One workgroup of 1024 threads per KV head.  The order is never materialised:
+// One workgroup of 512 threads per KV head.  The order is never materialised:
 // each candidate's inclusive prefix length is a sum over the candidates that
 // precede it, counted against LDS tiles of (key, id, length), so the decisions
-// do not depend on any sort and are deterministic.  Masks, the per-head lists
-// and the union are then compacted in place, stably, with ballot scans.
+// do not depend on any sort and are deterministic.  Then one pass over the
+// union clears the dropped spans from the masks and compacts the union and
+// every head's list at once (a head's new list is the kept union filtered by
+// its mask bit), in place and stably, with ballot scans.  Every gather is
+// issued without waiting on another, so each phase is one or two round trips.
 #include <hip/hip_runtime.h>
 
 #include "sekv_internal.h"
@@ -22,50 +25,74 @@
 namespace sekv {
 namespace {
 
-constexpr int kCapThreads = 1024;
+constexpr int kCapThreads = 512;
 constexpr int kCapWaves = kCapThreads / 64;
 constexpr int kCapTile = 2048;
 
 // largest gate value among the heads [h0, h0 + G) that zoomed span j (gate
-// values are probabilities, so -1 marks "none")
+// values are probabilities, so -1 marks "none"); all 2 G loads go out at once
+template <int G>
 __device__ __forceinline__ double cap_key(const uint8_t* __restrict__ mask,
-                                          const double* __restrict__ prob, int sc, int h0, int G,
+                                          const double* __restrict__ prob, int sc, int h0,
                                           int j) {
-  double k = -1.0;
+  uint8_t mb[G];
+  double pb[G];
+#pragma unroll
   for (int hl = 0; hl < G; ++hl) {
     const size_t o = (size_t)(h0 + hl) * sc + j;
-    if (mask[o] && prob[o] > k) k = prob[o];
+    mb[hl] = mask[o];
+    pb[hl] = prob[o];
   }
+  double k = -1.0;
+#pragma unroll
+  for (int hl = 0; hl < G; ++hl)
+    if (mb[hl] && pb[hl] > k) k = pb[hl];
   return k;
 }
 
-// exclusive prefix count of `flag` over the workgroup, in thread order;
-// *total receives the workgroup's count.  Every thread must call it.
-__device__ __forceinline__ int cap_scan(int flag, int* s_wave, int* total) {
+// exclusive prefix counts of NF flags at once over the workgroup, in thread
+// order; tot[f] receives the workgroup's count of flag f.  Every thread must
+// call it.
+template <int NF>
+__device__ __forceinline__ void cap_scan(const int (&flag)[NF], int (&pos)[NF], int (&tot)[NF],
+                                         int (*s_wave)[kCapWaves]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const unsigned long long b = __ballot(flag);
-  const int before = __popcll(b & ((1ull << lane) - 1ull));
-  if (lane == 0) s_wave[wave] = __popcll(b);
-  __syncthreads();
-  int base = 0, tot = 0;
-  for (int w = 0; w < kCapWaves; ++w) {
-    const int c = s_wave[w];
-    base += w < wave ? c : 0;
-    tot += c;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int before[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const unsigned long long b = __ballot(flag[f]);
+    before[f] = __popcll(b & below);
+    if (lane == 0) s_wave[f][wave] = __popcll(b);
   }
   __syncthreads();
-  *total = tot;
-  return base + before;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    int base = 0, t = 0;
+    for (int w = 0; w < kCapWaves; ++w) {
+      const int c = s_wave[f][w];
+      base += w < wave ? c : 0;
+      t += c;
+    }
+    pos[f] = base + before[f];
+    tot[f] = t;
+  }
+  __syncthreads();
 }
 
+// one candidate in LDS: a single 16-byte read per comparison
+struct alignas(16) CapEnt {
+  double key;
+  int id;
+  int len;
+};
+
+template <int G>
 __global__ __launch_bounds__(kCapThreads) void cap_budget_kernel(
-    int sc, int G, long long budget, const int32_t* __restrict__ clen,
-    const double* __restrict__ prob, uint8_t* mask, int32_t* list, int32_t* count,
-    int32_t* ulist, int32_t* ucount) {
-  __shared__ double s_key[kCapTile];
-  __shared__ int s_id[kCapTile];
-  __shared__ int s_len[kCapTile];
-  __shared__ int s_wave[kCapWaves];
+    int sc, long long budget, const int32_t* __restrict__ clen, const double* __restrict__ prob,
+    uint8_t* mask, int32_t* list, int32_t* count, int32_t* ulist, int32_t* ucount) {
+  __shared__ CapEnt s_ent[kCapTile];
+  __shared__ int s_wave[G + 1][kCapWaves];
   extern __shared__ uint32_t s_drop[];  // one bit per union position
 
   const int g = blockIdx.x, tid = threadIdx.x;
@@ -74,15 +101,17 @@ __global__ __launch_bounds__(kCapThreads) void cap_budget_kernel(
   const int U = ucount[g];
   for (int w = tid; w < (U + 31) / 32; w += kCapThreads) s_drop[w] = 0u;
 
-  // 1. inclusive prefix length of every candidate in (key desc, id asc) order
+  // 1. inclusive prefix length of every candidate in (key desc, id asc) order;
+  //    with a single tile (U <= kCapTile) a candidate's own key comes from it
+  const bool one_tile = U <= kCapTile;
   for (int base = 0; base < U; base += kCapThreads) {
     const int i = base + tid;
     const bool have = i < U;
     int ji = 0;
     double ki = 0.0;
-    if (have) {
+    if (have && !one_tile) {
       ji = ul[i];
-      ki = cap_key(mask, prob, sc, h0, G, ji);
+      ki = cap_key<G>(mask, prob, sc, h0, ji);
     }
     long long S = 0;
     for (int t0 = 0; t0 < U; t0 += kCapTile) {
@@ -90,15 +119,26 @@ __global__ __launch_bounds__(kCapThreads) void cap_budget_kernel(
       __syncthreads();
       for (int k = tid; k < tn; k += kCapThreads) {
         const int j = ul[t0 + k];
-        s_id[k] = j;
-        s_len[k] = clen[j];
-        s_key[k] = cap_key(mask, prob, sc, h0, G, j);
+        CapEnt e;
+        e.key = cap_key<G>(mask, prob, sc, h0, j);
+        e.id = j;
+        e.len = clen[j];
+        s_ent[k] = e;
       }
       __syncthreads();
       if (have) {
+        if (one_tile) {
+          ki = s_ent[i].key;
+          ji = s_ent[i].id;
+        }
+        // branch-free: every entry is read (one broadcast 16-byte LDS read)
+        // and counted with a select, so the reads of an unrolled group are
+        // all in flight together
+#pragma unroll 8
         for (int k = 0; k < tn; ++k) {
-          const double kk = s_key[k];
-          if (kk > ki || (kk == ki && s_id[k] <= ji)) S += s_len[k];
+          const CapEnt e = s_ent[k];
+          const bool before = (e.key > ki) | ((e.key == ki) & (e.id <= ji));
+          S += before ? e.len : 0;
         }
       }
     }
@@ -106,54 +146,48 @@ __global__ __launch_bounds__(kCapThreads) void cap_budget_kernel(
   }
   __syncthreads();
 
-  // 2. a dropped span leaves the mask of every head of the group
-  for (int i = tid; i < U; i += kCapThreads) {
-    if ((s_drop[i >> 5] >> (i & 31)) & 1u) {
-      const int j = ul[i];
-      for (int hl = 0; hl < G; ++hl) mask[(size_t)(h0 + hl) * sc + j] = 0;
-    }
-  }
-  __syncthreads();
-
-  // 3. the union keeps its kept candidates, in ascending order (in place:
-  //    every tile is read before any of its entries is written, and writes
-  //    never pass the position being read)
-  int out = 0;
+  // 2. one pass over the union: a dropped span leaves every head's mask; the
+  //    union keeps its kept spans and head h's list the kept spans in h's mask,
+  //    ascending.  In place: each block of positions is read before any of it
+  //    is written, and writes never pass the position being read.
+  int out[G + 1];
+#pragma unroll
+  for (int f = 0; f <= G; ++f) out[f] = 0;
   for (int base = 0; base < U; base += kCapThreads) {
     const int i = base + tid;
-    int j = 0, keep = 0;
+    int flag[G + 1];
+    int j = 0;
+    uint8_t mb[G];
+#pragma unroll
+    for (int f = 0; f <= G; ++f) flag[f] = 0;
     if (i < U) {
       j = ul[i];
-      keep = !((s_drop[i >> 5] >> (i & 31)) & 1u);
-    }
-    int tot;
-    const int pos = cap_scan(keep, s_wave, &tot);
-    if (keep) ul[out + pos] = j;
-    out += tot;
-  }
-  if (tid == 0) ucount[g] = out;
-
-  // 4. each head's ascending list keeps the spans still in its mask
-  for (int hl = 0; hl < G; ++hl) {
-    const int h = h0 + hl;
-    int32_t* lst = list + (size_t)h * sc;
-    const uint8_t* m = mask + (size_t)h * sc;
-    const int n = count[h];
-    int o = 0;
-    for (int base = 0; base < n; base += kCapThreads) {
-      const int i = base + tid;
-      int j = 0, keep = 0;
-      if (i < n) {
-        j = lst[i];
-        keep = m[j] != 0;
+#pragma unroll
+      for (int hl = 0; hl < G; ++hl) mb[hl] = mask[(size_t)(h0 + hl) * sc + j];
+      const bool keep = !((s_drop[i >> 5] >> (i & 31)) & 1u);
+#pragma unroll
+      for (int hl = 0; hl < G; ++hl) {
+        flag[hl] = keep && mb[hl] != 0;
+        if (!keep && mb[hl]) mask[(size_t)(h0 + hl) * sc + j] = 0;
       }
-      int tot;
-      const int pos = cap_scan(keep, s_wave, &tot);
-      if (keep) lst[o + pos] = j;
-      o += tot;
+      flag[G] = keep;
     }
-    if (tid == 0) count[h] = o;
+    int pos[G + 1], tot[G + 1];
+    cap_scan<G + 1>(flag, pos, tot, s_wave);
+#pragma unroll
+    for (int hl = 0; hl < G; ++hl)
+      if (flag[hl]) list[(size_t)(h0 + hl) * sc + out[hl] + pos[hl]] = j;
+    if (flag[G]) ul[out[G] + pos[G]] = j;
+#pragma unroll
+    for (int f = 0; f <= G; ++f) out[f] += tot[f];
   }
+  if (tid < G) {
+    int v = 0;
+#pragma unroll
+    for (int hl = 0; hl < G; ++hl) v = hl == tid ? out[hl] : v;
+    count[h0 + tid] = v;
+  }
+  if (tid == G) ucount[g] = out[G];
 }
 
 }  // namespace
@@ -164,8 +198,18 @@ hipError_t launch_cap_budget(int sc, int hkv, int group, long long budget, const
                              const double* prob, uint8_t* mask, int32_t* list, int32_t* count,
                              int32_t* ulist, int32_t* ucount, hipStream_t st) {
   if (sc <= 0 || hkv <= 0) return hipSuccess;
-  hipLaunchKernelGGL(cap_budget_kernel, dim3(hkv), dim3(kCapThreads), cap_budget_lds_bytes(sc),
-                     st, sc, group, budget, clen, prob, mask, list, count, ulist, ucount);
+  const size_t lds = cap_budget_lds_bytes(sc);
+#define SEKV_CAP(GG)                                                                           \
+  case GG:                                                                                     \
+    hipLaunchKernelGGL(cap_budget_kernel<GG>, dim3(hkv), dim3(kCapThreads), lds, st, sc,       \
+                       budget, clen, prob, mask, list, count, ulist, ucount);                  \
+    break;
+  switch (group) {
+    SEKV_CAP(1) SEKV_CAP(2) SEKV_CAP(3) SEKV_CAP(4) SEKV_CAP(5) SEKV_CAP(6) SEKV_CAP(7)
+    SEKV_CAP(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef SEKV_CAP
   return hipGetLastError();
 }
 
