@@ -53,6 +53,11 @@ def parse():
     ap.add_argument("--budget", type=int, default=None,
                     help="matched-budget cap in tokens per KV head and layer: each layer runs "
                          "sekv_route (gate values kept), sekv_cap_budget, sekv_decode_attn")
+    ap.add_argument("--residency-gb", type=float, default=0.0,
+                    help="host tier: HBM residency cache of factor blocks, in GB (0 = none)")
+    ap.add_argument("--slot-kb", type=int, default=64, help="residency cache slot size, KiB")
+    ap.add_argument("--query-corr", type=float, default=0.0,
+                    help="AR(1) correlation of consecutive step queries (0 = independent)")
     ap.add_argument("--zoom-frac", type=float, default=None,
                     help="share of spans every query head zooms (workloads with one share for "
                          "all heads, e.g. the batch-4 sweep)")
@@ -108,6 +113,9 @@ def main():
         sys.exit(2)
     if B > 1 and args.tier != "device":
         print("batched steps run with device-tier factors only", file=sys.stderr)
+        sys.exit(2)
+    if args.residency_gb > 0 and args.tier != "host":
+        print("--residency-gb applies to host-tier factors (--tier host)", file=sys.stderr)
         sys.exit(2)
     if args.budget is not None and (B > 1 or args.budget < 0):
         print("--budget takes a count >= 0 and one sequence", file=sys.stderr)
@@ -176,8 +184,15 @@ def main():
 
     # ---- per-step buffers ----------------------------------------------------------
     n_q = args.steps + args.warmup
-    qs = torch.stack([torch.stack([synth.queries(wl, seed, i, seq=b, device=dev)
-                                   for b in range(B)]) for i in range(n_q)])  # [T][B][L][Hq][d]
+    if args.query_corr:
+        qs = torch.stack([synth.correlated_queries(wl, seed, n_q, args.query_corr, seq=b,
+                                                   device=dev) for b in range(B)], dim=1)
+    else:
+        qs = torch.stack([torch.stack([synth.queries(wl, seed, i, seq=b, device=dev)
+                                       for b in range(B)]) for i in range(n_q)])
+    # qs: [T][B][L][Hq][d]
+    if args.residency_gb > 0:
+        cache.set_residency(int(args.residency_gb * 1e9), args.slot_kb * 1024)
     q_cur = torch.empty(B, L, Hq, d, device=dev)
     p_c = [p[l].contiguous() for l in range(L)]
     tau_c = [tau[l].contiguous() for l in range(L)]
@@ -228,6 +243,8 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed region ----------------------------------------------------------
+    if args.residency_gb > 0:
+        cache.residency_stats(reset=True)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -241,6 +258,10 @@ def main():
     total_ms = ev0.elapsed_time(ev1)
     ms_per_step = total_ms / args.steps
     log(f"{args.steps} steps in {total_ms:.1f} ms (wall {wall * 1e3:.1f} ms): {ms_per_step:.4f} ms/step")
+    res_stats = cache.residency_stats(reset=True) if args.residency_gb > 0 else None
+    if res_stats:
+        log(f"residency: {res_stats['hit_blocks']} blocks from HBM, {res_stats['fetched_blocks']} "
+            f"over the host link ({res_stats['fetched_bytes'] / args.steps / 1e9:.3f} GB/step)")
 
     # ---- algorithmic bytes of the timed steps ----------------------------------
     # per sequence: the resident bytes every layer launch reads, and the factor
@@ -328,9 +349,21 @@ def main():
 
     host_link = None
     if args.tier == "host":
-        link_gbs = float(zb_step.mean()) / (ms_per_step * 1e-3) / 1e9
-        host_link = {"gbs": link_gbs, "frac_of_measured_h2d": link_gbs / h2d_gbs,
+        # bytes that crossed the link: every union block, or with the residency
+        # cache only the blocks it did not hold
+        link_bytes = (res_stats["fetched_bytes"] / args.steps if res_stats
+                      else float(zb_step.mean()))
+        link_gbs = link_bytes / (ms_per_step * 1e-3) / 1e9
+        host_link = {"gbs": link_gbs, "bytes_per_step": link_bytes,
+                     "frac_of_measured_h2d": link_gbs / h2d_gbs,
                      "frac_of_pcie5_x16": link_gbs / PCIE_GBS}
+        if res_stats:
+            tot = res_stats["hit_blocks"] + res_stats["fetched_blocks"]
+            host_link["residency"] = {
+                "capacity_gb": args.residency_gb, "slot_bytes": res_stats["slot_bytes"],
+                "sets": res_stats["sets"],
+                "hit_rate_blocks": res_stats["hit_blocks"] / tot if tot else None,
+                "hit_bytes_per_step": res_stats["hit_bytes"] / args.steps}
 
     # ---- CPU oracle baseline on a bounded sample --------------------------------
     cpu = None
@@ -356,7 +389,7 @@ def main():
             "head_dim": d, "context": wl.n_tokens, "batch": B, "kv_dtype": wl.kv_dtype,
             "factor_dtype": "f32", "factor_tier": args.tier, "window": wl.window,
             "max_rank": wl.max_rank, "route_dim": wl.route_dim, "graph": graph is not None,
-            "budget_tokens": args.budget,
+            "budget_tokens": args.budget, "query_corr": args.query_corr,
             "zoom": ("skewed" if wl.tau_mode == "skewed" else
                      (f"{float(targets[0, 0]):g} per head" if targets is not None
                       else "uniform tau")),

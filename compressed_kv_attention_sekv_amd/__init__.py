@@ -19,7 +19,8 @@ __all__ = [
     "SekvError", "SekvConfig", "SekvCacheInfo", "SekvRouteOut", "lib", "library_path",
     "make_config", "Cache", "RouteBuffers", "sekv_segment", "sekv_build_spans", "sekv_route",
     "sekv_decode_attn", "sekv_route_attn", "sekv_decode_attn_batch", "sekv_route_attn_batch",
-    "sekv_cap_budget", "sekv_decode_workspace_bytes", "EXPORTED_SYMBOLS", "SEKV_MAX_BATCH",
+    "sekv_cap_budget", "sekv_decode_workspace_bytes", "EXPORTED_SYMBOLS",
+    "sekv_set_residency", "sekv_residency_stats", "SEKV_MAX_BATCH",
     "SEKV_F32", "SEKV_BF16", "SEKV_TIER_DEVICE", "SEKV_TIER_HOST_PINNED",
 ]
 
@@ -32,8 +33,8 @@ EXPORTED_SYMBOLS = (
     "sekv_segment", "sekv_build_spans", "sekv_cache_info_get", "sekv_cache_copy_spans",
     "sekv_cache_copy_group", "sekv_cache_copy_factors", "sekv_route",
     "sekv_decode_workspace_bytes", "sekv_decode_attn", "sekv_route_attn",
-    "sekv_decode_attn_batch", "sekv_route_attn_batch", "sekv_cap_budget", "sekv_cache_destroy",
-    "sekv_last_error",
+    "sekv_decode_attn_batch", "sekv_route_attn_batch", "sekv_cap_budget", "sekv_set_residency",
+    "sekv_residency_stats", "sekv_cache_destroy", "sekv_last_error",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -115,6 +116,8 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(SekvRouteOut), ctypes.POINTER(P),
                                          ctypes.POINTER(P), ctypes.POINTER(SZ), P]),
         "sekv_cap_budget": (I32, [P, ctypes.POINTER(SekvRouteOut), ctypes.c_int64, P]),
+        "sekv_set_residency": (I32, [P, U64, U64]),
+        "sekv_residency_stats": (I32, [P, ctypes.POINTER(U64), I32]),
         "sekv_cache_destroy": (None, [P]),
         "sekv_last_error": (ctypes.c_char_p, []),
     }
@@ -258,6 +261,17 @@ class Cache:
 
     def workspace_bytes(self) -> int:
         return int(lib().sekv_decode_workspace_bytes(self.handle))
+
+    def set_residency(self, capacity_bytes: int, slot_bytes: int = 64 * 1024) -> None:
+        """Enable (capacity > 0) or disable the HBM residency cache of a
+        host-tier cache's factor blocks."""
+        _check(lib().sekv_set_residency(self.handle, int(capacity_bytes), int(slot_bytes)))
+
+    def residency_stats(self, reset: bool = False) -> dict:
+        out = (ctypes.c_uint64 * 6)()
+        _check(lib().sekv_residency_stats(self.handle, out, 1 if reset else 0))
+        return {"hit_blocks": out[0], "fetched_blocks": out[1], "hit_bytes": out[2],
+                "fetched_bytes": out[3], "sets": out[4], "slot_bytes": out[5]}
 
 
 def sekv_build_spans(cfg: SekvConfig, surprisal: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

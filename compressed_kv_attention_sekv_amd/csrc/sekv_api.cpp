@@ -144,8 +144,21 @@ struct sekv_cache {
   float* zero_block = nullptr;     // kZeroBlockFloats zeros: a valid source for idle prefetches
   LayerGeom geom{};
   hipEvent_t ev_route = nullptr, ev_fetch = nullptr;
+  // host tier: HBM residency cache of factor blocks (sekv_set_residency)
+  std::vector<void*> res_dev;
+  ResidencyView res{};
+  bool res_on = false;
+  uint64_t res_epoch = 0;
 
+  void residency_free() {
+    for (void* p : res_dev) (void)hipFree(p);
+    res_dev.clear();
+    res = ResidencyView{};
+    res_on = false;
+    res_epoch = 0;
+  }
   ~sekv_cache() {
+    residency_free();
     for (void* p : dev) (void)hipFree(p);
     if (pool_host) (void)hipHostFree(pool_host);
     if (ev_route) (void)hipEventDestroy(ev_route);
@@ -550,13 +563,31 @@ static sekv_status attn_impl(const sekv_cache* c, int32_t layer, const float* q_
     SEKV_HIP(hipEventRecord(c->ev_route, stream));
     SEKV_HIP(hipStreamWaitEvent(fst, c->ev_route, 0));
   }
-  SEKV_HIP(launch_fetch_gather(c->geom, route->union_list, route->union_count, c->clen,
-                               c->rank + lg0 * sc, c->fac_off + lg0 * sc, c->layer_base[layer],
-                               c->pool_host_dev, c->stage, fst));
+  // with the residency cache the zoomed spans read their blocks through the
+  // offset table the fetch writes (cache slots or the arena's staging)
+  LayerArgs az = a;
+  if (c->res_on) {
+    sekv_cache* cm = const_cast<sekv_cache*>(c);   // per-cache call counter
+    if (++cm->res_epoch > kResMaxEpoch) {
+      SEKV_HIP(hipMemsetAsync(c->res.claim, 0, c->res.n_sets * 8, fst));
+      cm->res_epoch = 1;
+    }
+    SEKV_HIP(launch_resident_fetch(c->geom, layer, route->union_list, route->union_count,
+                                   c->clen, c->rank + lg0 * sc, c->fac_off + lg0 * sc,
+                                   c->layer_base[layer], c->pool_host_dev, c->res, c->res_epoch,
+                                   fst));
+    az.pool = c->res.arena;
+    az.fac_off = c->res.off;
+    az.off_base = 0;
+  } else {
+    SEKV_HIP(launch_fetch_gather(c->geom, route->union_list, route->union_count, c->clen,
+                                 c->rank + lg0 * sc, c->fac_off + lg0 * sc, c->layer_base[layer],
+                                 c->pool_host_dev, c->stage, fst));
+  }
   if (fst != stream) SEKV_HIP(hipEventRecord(c->ev_fetch, fst));
   SEKV_HIP(launch_layer(c->bf16(), kDense, c->geom, a, stream));
   if (fst != stream) SEKV_HIP(hipStreamWaitEvent(stream, c->ev_fetch, 0));
-  SEKV_HIP(launch_layer(c->bf16(), kZoom | kZoomSplit | kMerge, c->geom, a, stream));
+  SEKV_HIP(launch_layer(c->bf16(), kZoom | kZoomSplit | kMerge, c->geom, az, stream));
   return SEKV_OK;
 }
 
@@ -617,6 +648,75 @@ sekv_status sekv_cap_budget(const sekv_cache* c, const sekv_route_out* route,
   SEKV_HIP(launch_cap_budget(c->sc, c->cfg.n_kv_heads, c->group, (long long)budget_tokens,
                              c->clen, route->prob, route->mask, route->list, route->count,
                              route->union_list, route->union_count, stream));
+  return SEKV_OK;
+}
+
+sekv_status sekv_set_residency(sekv_cache* c, uint64_t capacity_bytes, uint64_t slot_bytes) {
+  if (!c) return fail(SEKV_ERR_INVALID, "cache is NULL");
+  if (c->cfg.factor_tier != SEKV_TIER_HOST_PINNED)
+    return fail(SEKV_ERR_INVALID, "the residency cache holds host-tier factors; this cache keeps "
+                "its factors in HBM");
+  const uint64_t keys = (uint64_t)c->cfg.n_layers * c->cfg.n_kv_heads * (uint64_t)c->sc;
+  if (keys > kResKeyMask)
+    return fail(SEKV_ERR_UNSUPPORTED, "too many (layer, KV head, span) blocks for the cache keys");
+  uint64_t slot_floats = 0, n_sets = 0;
+  if (capacity_bytes) {
+    if (slot_bytes == 0) return fail(SEKV_ERR_INVALID, "slot_bytes must be > 0");
+    slot_floats = ((slot_bytes + 255) / 256) * 64;
+    n_sets = capacity_bytes / (slot_floats * 4);
+    if (n_sets == 0)
+      return fail(SEKV_ERR_INVALID, "capacity of %llu bytes is below one slot of %llu bytes",
+                  (unsigned long long)capacity_bytes, (unsigned long long)(slot_floats * 4));
+  }
+  // nothing queued may still use the old tables
+  SEKV_HIP(hipDeviceSynchronize());
+  c->residency_free();
+  if (!capacity_bytes) return SEKV_OK;
+  const uint64_t slots_off = (c->stage_floats + 63) / 64 * 64;
+  const size_t n_off = std::max<size_t>((size_t)c->cfg.n_kv_heads * c->sc, 1);
+  struct Buf { void** p; size_t bytes; const char* what; } bufs[] = {
+      {(void**)&c->res.arena, (size_t)(slots_off + n_sets * slot_floats) * 4, "residency arena"},
+      {(void**)&c->res.claim, (size_t)n_sets * 8, "residency claims"},
+      {(void**)&c->res.tag, (size_t)n_sets * 8, "residency tags"},
+      {(void**)&c->res.off, n_off * 8, "residency offsets"},
+      {(void**)&c->res.stats, 4 * 8, "residency counters"}};
+  for (const Buf& b : bufs) {
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, b.bytes);
+    if (e != hipSuccess) {
+      c->residency_free();
+      return fail(SEKV_ERR_NOMEM, "hipMalloc(%zu) for %s failed: %s", b.bytes, b.what,
+                  hipGetErrorString(e));
+    }
+    c->res_dev.push_back(p);
+    *b.p = p;
+  }
+  c->res.slots_off = slots_off;
+  c->res.slot_floats = slot_floats;
+  c->res.n_sets = n_sets;
+  hipError_t e = hipMemset(c->res.claim, 0, n_sets * 8);
+  if (e == hipSuccess) e = hipMemset(c->res.tag, 0xff, n_sets * 8);
+  if (e == hipSuccess) e = hipMemset(c->res.stats, 0, 4 * 8);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    c->residency_free();
+    return fail(SEKV_ERR_HIP, "clearing the residency tables failed: %s", hipGetErrorString(e));
+  }
+  c->res_on = true;
+  return SEKV_OK;
+}
+
+sekv_status sekv_residency_stats(const sekv_cache* c, uint64_t* out, int32_t reset) {
+  if (!c || !out) return fail(SEKV_ERR_INVALID, "cache and out must be non-NULL");
+  if (!c->res_on) return fail(SEKV_ERR_INVALID, "the residency cache is not enabled");
+  SEKV_HIP(hipDeviceSynchronize());
+  SEKV_HIP(hipMemcpy(out, c->res.stats, 4 * 8, hipMemcpyDeviceToHost));
+  out[4] = c->res.n_sets;
+  out[5] = c->res.slot_floats * 4;
+  if (reset) {
+    SEKV_HIP(hipMemset(c->res.stats, 0, 4 * 8));
+    SEKV_HIP(hipDeviceSynchronize());
+  }
   return SEKV_OK;
 }
 

@@ -227,6 +227,27 @@ size_t cap_budget_lds_bytes(int sc);
 hipError_t launch_cap_budget(int sc, int hkv, int group, long long budget, const int32_t* clen,
                              const double* prob, uint8_t* mask, int32_t* list, int32_t* count,
                              int32_t* ulist, int32_t* ucount, hipStream_t st);
+// HBM residency cache of host-tier factor blocks (direct-mapped, one slot per
+// set).  A block's key is (layer * Hkv + g) * S_c + j, below 2^kResKeyBits; a
+// set's claim is (epoch << kResKeyBits) | (kResKeyMask - key) of its winner.
+constexpr int kResKeyBits = 40;
+constexpr uint64_t kResKeyMask = (1ull << kResKeyBits) - 1;
+constexpr uint64_t kResMaxEpoch = (1ull << (64 - kResKeyBits)) - 1;
+struct ResidencyView {
+  float* arena;                // [staging of one layer | n_sets slots]
+  uint64_t slots_off;          // first float of slot 0
+  uint64_t slot_floats;        // multiple of 64
+  uint64_t n_sets;
+  unsigned long long* claim;   // [n_sets]
+  long long* tag;              // [n_sets], -1 = empty
+  uint64_t* off;               // [Hkv][S_c] arena offset of each union block, this call
+  unsigned long long* stats;   // hit blocks, fetched blocks, hit bytes, fetched bytes
+};
+hipError_t launch_resident_fetch(const LayerGeom& g, int layer, const int32_t* ulist,
+                                 const int32_t* ucount, const int32_t* clen, const int32_t* rank,
+                                 const uint64_t* fac_off, uint64_t layer_base,
+                                 const float* host_pool_mapped, const ResidencyView& rv,
+                                 uint64_t epoch, hipStream_t st);
 hipError_t launch_fetch_gather(const LayerGeom& g, const int32_t* ulist, const int32_t* ucount,
                                const int32_t* clen, const int32_t* rank,
                                const uint64_t* fac_off, uint64_t layer_base,

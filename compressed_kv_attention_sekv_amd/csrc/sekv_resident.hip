@@ -1,0 +1,133 @@
+// HBM residency cache of host-tier span factors (gfx950).
+//
+// With factors in pinned host memory, every zoomed span's block crosses the
+// host link each time it is zoomed (SeKV paper Sec. 3.2: bases on the CPU,
+// fetched for the selected spans; the paper's limitation section names that
+// transfer as the cost of the CPU tier).  Decoding tends to zoom the same
+// spans again, so blocks stay in an HBM cache between calls.
+//
+// The cache is direct-mapped: block (layer, KV head, span) may live only in
+// set hash(key) mod n_sets, one fixed-size slot per set, with the set's tag
+// naming the block it holds.  One call (one layer) runs two kernels on the
+// fetch stream:
+//   claim: every union span whose block fits a slot bids for its set with a
+//          64-bit atomicMax of (epoch, inverted key), so within a call the
+//          lowest key wins each set, and bids of older calls always lose
+//          (no reset pass);
+//   fetch: a winner whose set's tag already names it is a hit (no copy);
+//          any other winner copies its block from host memory into the slot
+//          and takes the tag; losers and oversize blocks are copied into the
+//          layer's staging area at their layer-relative offsets, as without
+//          the cache.  Each union span's block offset goes to an offset table
+//          that the attention reads instead of the pool's own offsets.
+// Each set is written by at most one span per call, so the blocks a call
+// reads are never overwritten during it; results do not depend on where a
+// block was read from.
+#include <hip/hip_runtime.h>
+
+#include "sekv_internal.h"
+
+namespace sekv {
+namespace {
+
+constexpr int kResSlotsPerHead = 64;   // workgroups per KV head in the fetch
+
+__device__ __forceinline__ uint64_t res_mix(uint64_t x) {
+  // splitmix64 finalizer (Steele, Lea and Flood, 2014)
+  x ^= x >> 30;
+  x *= 0xbf58476d1ce4e5b9ull;
+  x ^= x >> 27;
+  x *= 0x94d049bb133111ebull;
+  x ^= x >> 31;
+  return x;
+}
+
+__device__ __forceinline__ uint64_t res_bid(uint64_t epoch, uint64_t key) {
+  return (epoch << kResKeyBits) | (kResKeyMask - key);
+}
+
+__global__ __launch_bounds__(256) void res_claim_kernel(
+    const int32_t* __restrict__ ulist, const int32_t* __restrict__ ucount,
+    const int32_t* __restrict__ clen, const int32_t* __restrict__ rank, int sc, int layer,
+    int hkv, uint64_t slot_floats, uint64_t n_sets, uint64_t epoch,
+    unsigned long long* __restrict__ claim) {
+  const int g = blockIdx.y;
+  const int nu = ucount[g];
+  for (int u = blockIdx.x * 256 + threadIdx.x; u < nu; u += gridDim.x * 256) {
+    const int j = ulist[(size_t)g * sc + u];
+    const FactorView fv(rank[(size_t)g * sc + j], clen[j]);
+    if (fv.block_floats() > slot_floats) continue;
+    const uint64_t key = ((uint64_t)layer * hkv + g) * (uint64_t)sc + j;
+    atomicMax(&claim[res_mix(key) % n_sets], (unsigned long long)res_bid(epoch, key));
+  }
+}
+
+__global__ __launch_bounds__(256) void res_fetch_kernel(
+    const int32_t* __restrict__ ulist, const int32_t* __restrict__ ucount,
+    const int32_t* __restrict__ clen, const int32_t* __restrict__ rank,
+    const uint64_t* __restrict__ fac_off, uint64_t layer_base, int sc, int layer, int hkv,
+    uint64_t slot_floats, uint64_t n_sets, uint64_t epoch,
+    const unsigned long long* __restrict__ claim, long long* __restrict__ tag,
+    const float* __restrict__ host, float* __restrict__ arena, uint64_t slots_off,
+    uint64_t* __restrict__ off_out, unsigned long long* __restrict__ stats) {
+  const int g = blockIdx.y;
+  const int nu = ucount[g];
+  for (int u = blockIdx.x; u < nu; u += kResSlotsPerHead) {
+    const int j = ulist[(size_t)g * sc + u];
+    const FactorView fv(rank[(size_t)g * sc + j], clen[j]);
+    const uint64_t nfl = fv.block_floats();
+    const uint64_t hoff = fac_off[(size_t)g * sc + j];
+    const uint64_t key = ((uint64_t)layer * hkv + g) * (uint64_t)sc + j;
+    uint64_t dst_off = hoff - layer_base;   // the layer's staging (arena start)
+    bool copy = true, hit = false, cached = false;
+    if (nfl <= slot_floats) {
+      const uint64_t set = res_mix(key) % n_sets;
+      if (claim[set] == res_bid(epoch, key)) {
+        cached = true;
+        dst_off = slots_off + set * slot_floats;
+        hit = tag[set] == (long long)key;
+        copy = !hit;
+      }
+    }
+    if (copy) {
+      const uint4* src = (const uint4*)(host + hoff);
+      uint4* dst = (uint4*)(arena + dst_off);
+      const int nvec = (int)(nfl / 4);
+      for (int k = threadIdx.x; k < nvec; k += 256) dst[k] = src[k];
+    }
+    // every lane has read the tag before it changes
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      off_out[(size_t)g * sc + j] = dst_off;
+      if (cached && !hit) tag[res_mix(key) % n_sets] = (long long)key;
+      const unsigned long long bytes = 8ull * (unsigned long long)fv.r *
+                                       (unsigned long long)(fv.n + kHeadDim + 1);
+      atomicAdd(&stats[hit ? 0 : 1], 1ull);
+      atomicAdd(&stats[hit ? 2 : 3], bytes);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_resident_fetch(const LayerGeom& g, int layer, const int32_t* ulist,
+                                 const int32_t* ucount, const int32_t* clen, const int32_t* rank,
+                                 const uint64_t* fac_off, uint64_t layer_base,
+                                 const float* host_pool_mapped, const ResidencyView& rv,
+                                 uint64_t epoch, hipStream_t st) {
+  if (g.n_compressed == 0) return hipSuccess;
+  const int sc = g.n_compressed, hkv = g.n_kv_heads;
+  const int cx = (sc + 255) / 256;
+  hipLaunchKernelGGL(res_claim_kernel, dim3(cx < 64 ? cx : 64, hkv), dim3(256), 0, st, ulist,
+                     ucount, clen, rank, sc, layer, hkv, rv.slot_floats, rv.n_sets, epoch,
+                     rv.claim);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(res_fetch_kernel, dim3(kResSlotsPerHead, hkv), dim3(256), 0, st, ulist,
+                     ucount, clen, rank, fac_off, layer_base, sc, layer, hkv, rv.slot_floats,
+                     rv.n_sets, epoch, rv.claim, rv.tag, host_pool_mapped, rv.arena,
+                     rv.slots_off, rv.off, rv.stats);
+  return hipGetLastError();
+}
+
+}  // namespace sekv

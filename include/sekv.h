@@ -219,6 +219,34 @@ sekv_status sekv_route_attn(const sekv_cache* cache, int32_t layer, const float*
 sekv_status sekv_cap_budget(const sekv_cache* cache, const sekv_route_out* route,
                             int64_t budget_tokens, hipStream_t stream);
 
+/* HBM residency cache for host-tier factors (SeKV paper Sec. 3.2 keeps the
+ * span bases on the CPU and fetches them for the selected spans; its
+ * limitations name that transfer as the cost of the CPU tier).  Once enabled,
+ * each host-tier sekv_decode_attn / sekv_route_attn keeps the zoomed spans'
+ * factor blocks in HBM, so a span zoomed again in a later call (same layer and
+ * KV head) is read from HBM instead of crossing the host link.  The cache is
+ * direct-mapped: block (layer, KV head, span) may occupy only the set given by
+ * a fixed hash of that key, one slot of slot_bytes (rounded up to 256) per
+ * set, capacity_bytes / slot_bytes sets.  Within one call, spans of the union
+ * that share a set are resolved by the lowest key; the others, and blocks
+ * larger than a slot, are copied to per-layer staging as without the cache.
+ * Outputs do not depend on the cache (a block is the same bytes wherever it is
+ * read from).
+ *   capacity_bytes: 0 disables the cache and frees it.
+ * The call synchronises the device (it frees and allocates device memory and
+ * clears the tables), so no work of this cache may be in flight on another
+ * thread.  Errors: SEKV_ERR_INVALID for a NULL or device-tier cache, a zero
+ * slot size, or a capacity below one slot; SEKV_ERR_NOMEM if the tables do
+ * not fit; on failure the cache is left disabled. */
+sekv_status sekv_set_residency(sekv_cache* cache, uint64_t capacity_bytes, uint64_t slot_bytes);
+
+/* Counters of the residency cache since it was enabled or last reset
+ * (synchronises the device): out[0] blocks read from the cache, out[1] blocks
+ * copied over the host link, out[2] and out[3] their bytes counted as
+ * 8 r (n + d + 1) per block, out[4] sets, out[5] slot bytes.  reset != 0 zeroes
+ * the counters afterwards.  SEKV_ERR_INVALID if the cache is not enabled. */
+sekv_status sekv_residency_stats(const sekv_cache* cache, uint64_t out[6], int32_t reset);
+
 /* Batched decode: the same layer of `batch` independent sequences
  * (1 <= batch <= SEKV_MAX_BATCH), one cache each, in one kernel launch (the
  * per-sequence computation of sekv_route_attn / sekv_decode_attn; batch-4

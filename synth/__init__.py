@@ -31,7 +31,7 @@ import torch
 __all__ = [
     "Workload", "WORKLOADS", "workload", "rng", "surprisal", "planted_segments",
     "span_kv", "kv_cache", "rank_by_pos", "route_weights", "tau_uniform",
-    "zoom_targets", "queries", "calibration_queries",
+    "zoom_targets", "queries", "correlated_queries", "calibration_queries",
 ]
 
 
@@ -284,6 +284,21 @@ def queries(wl: Workload, seed: int, step: int, seq: int = 0, device="cpu") -> t
     """Decode query for one step, [L][Hq][d] float32 ~ N(0, 1)."""
     g = rng(seed, "query", seq, step, device=device)
     return torch.randn(wl.n_layers, wl.n_q_heads, wl.head_dim, generator=g, device=device)
+
+
+def correlated_queries(wl: Workload, seed: int, n: int, rho: float, seq: int = 0,
+                       device="cpu") -> torch.Tensor:
+    """n consecutive decode queries [n][L][Hq][d] from a stationary AR(1)
+    process, q_0 = e_0 and q_t = rho q_{t-1} + sqrt(1 - rho^2) e_t with the
+    e_t those of ``queries``: each q_t ~ N(0, 1), neighbouring steps
+    correlated by rho (real decoding keeps zooming into many of the same
+    spans; independent queries do not).  rho = 0 gives ``queries``."""
+    out = torch.empty(n, wl.n_layers, wl.n_q_heads, wl.head_dim, device=device)
+    c = math.sqrt(max(0.0, 1.0 - rho * rho))
+    for t in range(n):
+        e = queries(wl, seed, t, seq=seq, device=device)
+        out[t] = e if t == 0 else rho * out[t - 1] + c * e
+    return out
 
 
 def calibration_queries(wl: Workload, seed: int, n: int = 16, seq: int = 0, device="cpu"):
