@@ -40,6 +40,9 @@ silent.  The readings are:
     tokens), one coarse entry per non-zoomed span with + ln n_j added to its
     scaled score, and the rank-r reconstruction of every zoomed span's tokens;
     score scale 1/sqrt(d) (Sec. 3.3; summary sec. 3);
+  * soft gates (optional, Eq. 8): each retained component i is scaled by its
+    gate g_i, components with g_i below a threshold are dropped, at least one
+    (the largest gate) is kept; one gate vector per span for keys and values;
   * budget cap (optional): per layer and KV head, the reconstructed spans'
     total length is capped; spans are kept by decreasing gate value (the
     largest over the group's heads that selected them), ties by lower id,
@@ -208,6 +211,37 @@ def truncated_svd(x, r: int) -> Factors:
     u, sig, vt = np.linalg.svd(x, full_matrices=False)
     return Factors(u=u[:, :r].copy(), sigma=sig[:r].copy(), vt=vt[:r].copy(),
                    tail2=float(np.sum(sig[r:] ** 2)))
+
+
+def gate_factors(f: Factors, gates, eps: float) -> Factors:
+    """Gated reconstruction (Eq. 8): component i of the retained factors is
+    scaled by its gate g_i in [0, 1], K^ = U diag(g * sigma) V^T, and
+    components whose gate is negligible (g_i < eps) are dropped from storage.
+
+    Reading taken: gate i belongs to the i-th largest singular value; the kept
+    components keep their order; a span keeps at least one component (as the
+    hard-gate rank is at least one), the one with the largest gate (lowest
+    index on ties), when every gate is negligible.  ``tail2`` of the result is
+    not set (nan): the reconstruction error of soft gates is no longer the
+    discarded energy alone."""
+    r = f.sigma.size
+    g = np.asarray(gates, dtype=F64)[:r]
+    kept = [i for i in range(r) if g[i] >= eps]
+    if not kept:
+        kept = [int(np.argmax(g))]
+    kept = np.array(kept, dtype=np.int64)
+    return Factors(u=f.u[:, kept].copy(), sigma=f.sigma[kept] * g[kept], vt=f.vt[kept].copy(),
+                   tail2=float("nan"))
+
+
+def gate_group(gc: "GroupCache", gates, eps: float) -> "GroupCache":
+    """The group with every span's key and value factors gated (Eq. 8), one
+    gate vector per span shared by keys and values (they keep one rank);
+    ``gates`` is [S_c][R]."""
+    kf = [gate_factors(f, gates[i], eps) for i, f in enumerate(gc.kfac)]
+    vf = [gate_factors(f, gates[i], eps) for i, f in enumerate(gc.vfac)]
+    return dataclasses.replace(gc, kfac=kf, vfac=vf,
+                               rank=np.array([f.sigma.size for f in kf], dtype=np.int64))
 
 
 @dataclasses.dataclass

@@ -217,6 +217,53 @@ def test_svd_planted_rank():
 
 
 # ---------------------------------------------------------------------------
+# soft gates (Eq. 8)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,r", [(40, 8), (128, 32), (300, 17)])
+def test_gate_factors_closed_forms(n, r):
+    rng = np.random.default_rng(n + 3 * r)
+    d = 128
+    x = rng.standard_normal((n, 6)) @ rng.standard_normal((6, d)) + 0.05 * rng.standard_normal((n, d))
+    f = O.truncated_svd(x, r)
+    full = O.truncated_svd(x, min(n, d))
+    # gates of one change nothing
+    g1 = O.gate_factors(f, np.ones(r), 0.5)
+    assert np.array_equal(g1.u, f.u) and np.array_equal(g1.sigma, f.sigma)
+    assert np.array_equal(g1.vt, f.vt)
+    # 0/1 gates on a prefix are the truncation to that prefix (Eckart-Young pins it)
+    k = max(1, r // 2)
+    gp = O.gate_factors(f, np.r_[np.ones(k), np.zeros(r - k)], 0.5)
+    assert gp.sigma.size == k
+    assert np.linalg.norm(gp.reconstruct() - O.truncated_svd(x, k).reconstruct()) <= \
+        1e-12 * np.linalg.norm(x)
+    # soft gates: with orthonormal factors the error splits component by
+    # component, (1 - g_i)^2 sigma_i^2 for a kept one and sigma_i^2 for every
+    # dropped or never-retained one (the full spectrum from LAPACK)
+    g = rng.uniform(0.0, 1.0, r)
+    eps = 0.3
+    gf = O.gate_factors(f, g, eps)
+    kept = g >= eps
+    assert gf.sigma.size == int(kept.sum())
+    s_all = full.sigma
+    want = float(np.sum(((1.0 - g[kept]) * s_all[:r][kept]) ** 2) +
+                 np.sum(s_all[:r][~kept] ** 2) + np.sum(s_all[r:] ** 2))
+    got = float(np.linalg.norm(x - gf.reconstruct()) ** 2)
+    assert got == pytest.approx(want, rel=1e-9)
+
+
+def test_gate_factors_keeps_one_component():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((20, 128))
+    f = O.truncated_svd(x, 6)
+    g = np.array([0.01, 0.05, 0.02, 0.05, 0.0, 0.03])
+    gf = O.gate_factors(f, g, 0.5)
+    assert gf.sigma.size == 1
+    assert gf.sigma[0] == pytest.approx(0.05 * f.sigma[1])   # largest gate, lowest index
+    assert np.array_equal(gf.vt[0], f.vt[1])
+
+
+# ---------------------------------------------------------------------------
 # router
 # ---------------------------------------------------------------------------
 
