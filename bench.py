@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--slot-kb", type=int, default=64, help="residency cache slot size, KiB")
     ap.add_argument("--query-corr", type=float, default=0.0,
                     help="AR(1) correlation of consecutive step queries (0 = independent)")
+    ap.add_argument("--gates", type=float, default=None,
+                    help="soft-gate the factors after the build (Eq. 8) with synthetic gates, "
+                         "dropping components whose gate is below this value")
     ap.add_argument("--zoom-frac", type=float, default=None,
                     help="share of spans every query head zooms (workloads with one share for "
                          "all heads, e.g. the batch-4 sweep)")
@@ -145,6 +148,16 @@ def main():
         log(f"sequence {b}: build {dt:.2f}s: spans {i_.n_spans} compressed {i_.n_compressed} "
             f"anchors {i_.n_anchors} dense {i_.n_dense} factor pool "
             f"{i_.factor_pool_bytes / 1e9:.2f} GB")
+        if args.gates is not None:
+            if args.tier != "device":
+                print("--gates needs device-tier factors", file=sys.stderr)
+                sys.exit(2)
+            fb = c.info.factor_bytes
+            t0 = time.time()
+            S.sekv_apply_gates(c, synth.span_gates(wl, seed, c.info.n_compressed, device=dev),
+                               args.gates)
+            log(f"sequence {b}: gates applied in {time.time() - t0:.2f}s, factor bytes "
+                f"{fb / 1e9:.2f} -> {c.info.factor_bytes / 1e9:.2f} GB")
         caches.append(c)
         if b == 0:
             s, spike, ranks = s_b, spike_b, ranks_b   # the CPU baseline's sample
@@ -390,6 +403,7 @@ def main():
             "factor_dtype": "f32", "factor_tier": args.tier, "window": wl.window,
             "max_rank": wl.max_rank, "route_dim": wl.route_dim, "graph": graph is not None,
             "budget_tokens": args.budget, "query_corr": args.query_corr,
+            "gate_eps": args.gates,
             "zoom": ("skewed" if wl.tau_mode == "skewed" else
                      (f"{float(targets[0, 0]):g} per head" if targets is not None
                       else "uniform tau")),

@@ -20,7 +20,7 @@ __all__ = [
     "make_config", "Cache", "RouteBuffers", "sekv_segment", "sekv_build_spans", "sekv_route",
     "sekv_decode_attn", "sekv_route_attn", "sekv_decode_attn_batch", "sekv_route_attn_batch",
     "sekv_cap_budget", "sekv_decode_workspace_bytes", "EXPORTED_SYMBOLS",
-    "sekv_set_residency", "sekv_residency_stats", "SEKV_MAX_BATCH",
+    "sekv_set_residency", "sekv_residency_stats", "sekv_apply_gates", "SEKV_MAX_BATCH",
     "SEKV_F32", "SEKV_BF16", "SEKV_TIER_DEVICE", "SEKV_TIER_HOST_PINNED",
 ]
 
@@ -34,7 +34,7 @@ EXPORTED_SYMBOLS = (
     "sekv_cache_copy_group", "sekv_cache_copy_factors", "sekv_route",
     "sekv_decode_workspace_bytes", "sekv_decode_attn", "sekv_route_attn",
     "sekv_decode_attn_batch", "sekv_route_attn_batch", "sekv_cap_budget", "sekv_set_residency",
-    "sekv_residency_stats", "sekv_cache_destroy", "sekv_last_error",
+    "sekv_residency_stats", "sekv_apply_gates", "sekv_cache_destroy", "sekv_last_error",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -117,6 +117,7 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(P), ctypes.POINTER(SZ), P]),
         "sekv_cap_budget": (I32, [P, ctypes.POINTER(SekvRouteOut), ctypes.c_int64, P]),
         "sekv_set_residency": (I32, [P, U64, U64]),
+        "sekv_apply_gates": (I32, [P, P, ctypes.c_float, P]),
         "sekv_residency_stats": (I32, [P, ctypes.POINTER(U64), I32]),
         "sekv_cache_destroy": (None, [P]),
         "sekv_last_error": (ctypes.c_char_p, []),
@@ -365,6 +366,20 @@ def sekv_cap_budget(cache: Cache, route: RouteBuffers, budget_tokens: int, strea
     st = route.struct()
     _check(lib().sekv_cap_budget(cache.handle, ctypes.byref(st), int(budget_tokens),
                                  _stream(stream)))
+
+
+def sekv_apply_gates(cache: Cache, gates: torch.Tensor, eps: float, stream=None) -> None:
+    """Soft-gate the cache's factors (Eq. 8); gates [L][Hkv][S_c][max_rank]
+    float32 on the device.  Refreshes ``cache.info``."""
+    _need(gates, "gates", torch.float32)
+    c = cache.cfg
+    shape = (c.n_layers, c.n_kv_heads, cache.info.n_compressed, c.max_rank)
+    if tuple(gates.shape) != shape:
+        raise ValueError(f"gates must be {shape}")
+    _check(lib().sekv_apply_gates(cache.handle, _ptr(gates), float(eps), _stream(stream)))
+    info = SekvCacheInfo()
+    _check(lib().sekv_cache_info_get(cache.handle, ctypes.byref(info)))
+    cache.info = info
 
 
 def _batch_arrays(caches, qs, routes, os_, workspaces):

@@ -651,6 +651,84 @@ sekv_status sekv_cap_budget(const sekv_cache* c, const sekv_route_out* route,
   return SEKV_OK;
 }
 
+sekv_status sekv_apply_gates(sekv_cache* c, const float* gates_dev, float eps,
+                             hipStream_t st) {
+  if (!c || !gates_dev) return fail(SEKV_ERR_INVALID, "cache and gates must be non-NULL");
+  if (!std::isfinite(eps)) return fail(SEKV_ERR_INVALID, "eps must be finite");
+  if (c->cfg.factor_tier != SEKV_TIER_DEVICE)
+    return fail(SEKV_ERR_UNSUPPORTED, "soft gates repack the device factor pool; this cache keeps "
+                "its factors in host memory");
+  const int L = c->cfg.n_layers, Hkv = c->cfg.n_kv_heads, sc = c->sc, R = c->cfg.max_rank;
+  if (sc == 0) return SEKV_OK;
+  const size_t nb = (size_t)L * Hkv * sc;
+  std::vector<float> hg(nb * R);
+  SEKV_HIP(hipMemcpyAsync(hg.data(), gates_dev, hg.size() * 4, hipMemcpyDeviceToHost, st));
+  SEKV_HIP(hipStreamSynchronize(st));
+  // which components stay: gate >= eps, at least one (the largest gate, the
+  // lowest index on ties); the new pool keeps the layout of the old one
+  std::vector<uint8_t> kept(nb * R, 0);
+  std::vector<int32_t> nr(nb);
+  std::vector<uint64_t> noff(nb), nbase(L + 1, 0);
+  uint64_t off = 0, fbytes = 0;
+  for (int l = 0; l < L; ++l) {
+    nbase[l] = off;
+    for (int g = 0; g < Hkv; ++g)
+      for (int j = 0; j < sc; ++j) {
+        const size_t idx = ((size_t)l * Hkv + g) * sc + j;
+        const int r = c->h_rank[idx], n = c->h_clen[j];
+        const float* gg = &hg[idx * R];
+        int k = 0, best = 0;
+        for (int i = 0; i < r; ++i) {
+          if (!(gg[i] >= 0.f && gg[i] <= 1.f))
+            return fail(SEKV_ERR_INVALID, "gate %d of (layer %d, KV head %d, span %d) is %g, "
+                        "outside [0, 1]", i, l, g, j, (double)gg[i]);
+          if (gg[i] >= eps) kept[idx * R + k++] = (uint8_t)i;
+          if (gg[i] > gg[best]) best = i;
+        }
+        if (k == 0) {
+          kept[idx * R] = (uint8_t)best;
+          k = 1;
+        }
+        nr[idx] = k;
+        noff[idx] = off;
+        off += FactorView(k, n).block_floats();
+        fbytes += 8ull * k * (uint64_t)(n + kHeadDim + 1);
+      }
+  }
+  nbase[L] = off;
+  Scratch scr;
+  sekv_status r;
+  uint8_t* d_kept = nullptr;
+  int32_t* d_rank = nullptr;
+  uint64_t* d_off = nullptr;
+  float* npool = nullptr;
+  if ((r = scr.alloc(&d_kept, kept.size(), "gate kept components"))) return r;
+  if ((r = scr.alloc(&d_rank, nb * 4, "gated ranks"))) return r;
+  if ((r = scr.alloc(&d_off, nb * 8, "gated offsets"))) return r;
+  if ((r = scr.alloc(&npool, (size_t)off * 4, "gated factor pool"))) return r;
+  SEKV_HIP(hipMemcpyAsync(d_kept, kept.data(), kept.size(), hipMemcpyHostToDevice, st));
+  SEKV_HIP(hipMemcpyAsync(d_rank, nr.data(), nb * 4, hipMemcpyHostToDevice, st));
+  SEKV_HIP(hipMemcpyAsync(d_off, noff.data(), nb * 8, hipMemcpyHostToDevice, st));
+  SEKV_HIP(hipMemsetAsync(npool, 0, (size_t)off * 4, st));
+  SEKV_HIP(launch_gate_repack(c->pool_dev, c->fac_off, c->rank, npool, d_off, d_rank, d_kept,
+                              gates_dev, c->clen, sc, R, nb, st));
+  SEKV_HIP(hipMemcpyAsync(c->rank, d_rank, nb * 4, hipMemcpyDeviceToDevice, st));
+  SEKV_HIP(hipMemcpyAsync(c->fac_off, d_off, nb * 8, hipMemcpyDeviceToDevice, st));
+  SEKV_HIP(hipStreamSynchronize(st));
+  // the new pool replaces the old one
+  scr.release(npool);
+  c->dev.erase(std::remove(c->dev.begin(), c->dev.end(), (void*)c->pool_dev), c->dev.end());
+  (void)hipFree(c->pool_dev);
+  c->pool_dev = npool;
+  c->dev.push_back(npool);
+  c->h_rank = std::move(nr);
+  c->h_fac_off = std::move(noff);
+  c->layer_base = std::move(nbase);
+  c->pool_floats = off;
+  c->factor_bytes = fbytes;
+  return SEKV_OK;
+}
+
 sekv_status sekv_set_residency(sekv_cache* c, uint64_t capacity_bytes, uint64_t slot_bytes) {
   if (!c) return fail(SEKV_ERR_INVALID, "cache is NULL");
   if (c->cfg.factor_tier != SEKV_TIER_HOST_PINNED)

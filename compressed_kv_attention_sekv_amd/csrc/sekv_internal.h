@@ -248,6 +248,13 @@ hipError_t launch_resident_fetch(const LayerGeom& g, int layer, const int32_t* u
                                  const uint64_t* fac_off, uint64_t layer_base,
                                  const float* host_pool_mapped, const ResidencyView& rv,
                                  uint64_t epoch, hipStream_t st);
+// soft gates: repack every (layer, KV head, span) block of the device pool
+// into a new pool with the kept components (gate-scaled sigma)
+hipError_t launch_gate_repack(const float* old_pool, const uint64_t* old_off,
+                              const int32_t* old_rank, float* new_pool, const uint64_t* new_off,
+                              const int32_t* new_rank, const uint8_t* kept, const float* gates,
+                              const int32_t* clen, int sc, int max_rank, uint64_t n_blocks,
+                              hipStream_t st);
 hipError_t launch_fetch_gather(const LayerGeom& g, const int32_t* ulist, const int32_t* ucount,
                                const int32_t* clen, const int32_t* rank,
                                const uint64_t* fac_off, uint64_t layer_base,

@@ -219,6 +219,28 @@ sekv_status sekv_route_attn(const sekv_cache* cache, int32_t layer, const float*
 sekv_status sekv_cap_budget(const sekv_cache* cache, const sekv_route_out* route,
                             int64_t budget_tokens, hipStream_t stream);
 
+/* Soft-gated reconstruction (SeKV paper Sec. 3.2 low-rank paragraph, Eq. 8:
+ * K^_j = U_j diag(g_j * sigma_j) V_j^T with per-component gates in [0, 1],
+ * components with negligible gates not stored), applied to a built cache.
+ * For every (layer, KV head, compressed span), gate i belongs to the i-th
+ * largest singular value of the stored factors (i < r_j); the components with
+ * gate >= eps stay, in order, with sigma scaled by the gate, for keys and
+ * values alike (one gate vector per span: keys and values keep one rank); a
+ * span keeps at least one component, the one with the largest gate (lowest
+ * index on ties).  The factor pool is repacked to the new ranks, so zoomed
+ * spans then move 8 r' (n + d + 1) bytes.  Calling it again gates the gated
+ * factors.
+ *   gates_dev: device float32 [L][Hkv][S_c][max_rank] (S_c from
+ *              sekv_cache_info; entries i >= r_j are ignored), each used gate
+ *              in [0, 1]; read during the call.
+ * Synchronises `stream`.  Errors: SEKV_ERR_INVALID for NULL arguments, a
+ * non-finite eps or a gate outside [0, 1] (nothing changed);
+ * SEKV_ERR_UNSUPPORTED for host-tier caches; SEKV_ERR_NOMEM if the new pool
+ * does not fit (nothing changed); after SEKV_ERR_HIP the cache must be
+ * destroyed. */
+sekv_status sekv_apply_gates(sekv_cache* cache, const float* gates_dev, float eps,
+                             hipStream_t stream);
+
 /* HBM residency cache for host-tier factors (SeKV paper Sec. 3.2 keeps the
  * span bases on the CPU and fetches them for the selected spans; its
  * limitations name that transfer as the cost of the CPU tier).  Once enabled,

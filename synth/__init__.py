@@ -31,7 +31,7 @@ import torch
 __all__ = [
     "Workload", "WORKLOADS", "workload", "rng", "surprisal", "planted_segments",
     "span_kv", "kv_cache", "rank_by_pos", "route_weights", "tau_uniform",
-    "zoom_targets", "queries", "correlated_queries", "calibration_queries",
+    "zoom_targets", "queries", "correlated_queries", "span_gates", "calibration_queries",
 ]
 
 
@@ -299,6 +299,18 @@ def correlated_queries(wl: Workload, seed: int, n: int, rho: float, seq: int = 0
         e = queries(wl, seed, t, seq=seq, device=device)
         out[t] = e if t == 0 else rho * out[t - 1] + c * e
     return out
+
+
+def span_gates(wl: Workload, seed: int, n_compressed: int, device="cpu") -> torch.Tensor:
+    """Per-component gates of every (layer, KV head, compressed span),
+    [L][Hkv][S_c][max_rank] float32 in (0, 1): g_i = sigmoid(z_i) with
+    z_i ~ N(3 - 6 i / (R - 1), 1), so leading components mostly stay open and
+    trailing ones mostly close (a stand-in for a trained gate predictor)."""
+    R = wl.max_rank
+    g = rng(seed, "span_gates", device=device)
+    mu = 3.0 - 6.0 * torch.arange(R, device=device, dtype=torch.float32) / max(R - 1, 1)
+    z = torch.randn(wl.n_layers, wl.n_kv_heads, n_compressed, R, generator=g, device=device)
+    return torch.sigmoid(z + mu)
 
 
 def calibration_queries(wl: Workload, seed: int, n: int = 16, seq: int = 0, device="cpu"):
