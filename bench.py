@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--slot-kb", type=int, default=64, help="residency cache slot size, KiB")
     ap.add_argument("--query-corr", type=float, default=0.0,
                     help="AR(1) correlation of consecutive step queries (0 = independent)")
+    ap.add_argument("--svd", choices=["exact", "randomized"], default="exact",
+                    help="per-span truncated SVD of the build")
     ap.add_argument("--gates", type=float, default=None,
                     help="soft-gate the factors after the build (Eq. 8) with synthetic gates, "
                          "dropping components whose gate is below this value")
@@ -68,8 +70,9 @@ def parse():
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources the layer kernel is compiled from."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "compressed_kv_attention_sekv_amd", "csrc"))):
+    for f in ("sekv_decode.hip", "sekv_internal.h"):
         with open(os.path.join(ROOT, "compressed_kv_attention_sekv_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -130,7 +133,8 @@ def main():
     w, p = synth.route_weights(wl, seed, device=dev)
     cfg = S.make_config(L, Hq, Hkv, head_dim=d, route_dim=wl.route_dim, window=wl.window,
                         max_rank=wl.max_rank, min_span_len=wl.min_span_len, alpha=wl.alpha,
-                        gamma=wl.gamma, kv_dtype=wl.kv_dtype, factor_tier=args.tier)
+                        gamma=wl.gamma, kv_dtype=wl.kv_dtype, factor_tier=args.tier,
+                        svd=args.svd)
     caches, build_s = [], 0.0
     for b in range(B):
         t0 = time.time()
@@ -403,7 +407,7 @@ def main():
             "factor_dtype": "f32", "factor_tier": args.tier, "window": wl.window,
             "max_rank": wl.max_rank, "route_dim": wl.route_dim, "graph": graph is not None,
             "budget_tokens": args.budget, "query_corr": args.query_corr,
-            "gate_eps": args.gates,
+            "gate_eps": args.gates, "svd": args.svd,
             "zoom": ("skewed" if wl.tau_mode == "skewed" else
                      (f"{float(targets[0, 0]):g} per head" if targets is not None
                       else "uniform tau")),

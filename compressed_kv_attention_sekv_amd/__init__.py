@@ -22,11 +22,13 @@ __all__ = [
     "sekv_cap_budget", "sekv_decode_workspace_bytes", "EXPORTED_SYMBOLS",
     "sekv_set_residency", "sekv_residency_stats", "sekv_apply_gates", "SEKV_MAX_BATCH",
     "SEKV_F32", "SEKV_BF16", "SEKV_TIER_DEVICE", "SEKV_TIER_HOST_PINNED",
+    "SEKV_SVD_EXACT", "SEKV_SVD_RANDOMIZED",
 ]
 
 SEKV_OK, SEKV_ERR_INVALID, SEKV_ERR_NOMEM, SEKV_ERR_HIP, SEKV_ERR_UNSUPPORTED = range(5)
 SEKV_F32, SEKV_BF16 = 0, 1
 SEKV_TIER_DEVICE, SEKV_TIER_HOST_PINNED = 0, 1
+SEKV_SVD_EXACT, SEKV_SVD_RANDOMIZED = 0, 1
 SEKV_MAX_BATCH = 8
 
 EXPORTED_SYMBOLS = (
@@ -59,6 +61,7 @@ class SekvConfig(ctypes.Structure):
         ("alpha", ctypes.c_double), ("gamma", ctypes.c_double),
         ("kv_dtype", ctypes.c_int32), ("factor_tier", ctypes.c_int32),
         ("host_pool_cap_bytes", ctypes.c_uint64),
+        ("svd_mode", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -161,12 +164,13 @@ def make_config(n_layers: int, n_q_heads: int, n_kv_heads: int, *, head_dim: int
                 route_dim: int = 32, window: int = 512, max_rank: int = 32,
                 min_span_len: int = 8, alpha: float = 1.0, gamma: float = 0.1,
                 kv_dtype: str = "bf16", factor_tier: str = "device",
-                host_pool_cap_bytes: int = 0) -> SekvConfig:
+                host_pool_cap_bytes: int = 0, svd: str = "exact") -> SekvConfig:
     return SekvConfig(n_layers, n_q_heads, n_kv_heads, head_dim, route_dim, window, max_rank,
                       min_span_len, float(alpha), float(gamma),
                       SEKV_BF16 if kv_dtype == "bf16" else SEKV_F32,
                       SEKV_TIER_HOST_PINNED if factor_tier == "host" else SEKV_TIER_DEVICE,
-                      int(host_pool_cap_bytes))
+                      int(host_pool_cap_bytes),
+                      SEKV_SVD_RANDOMIZED if svd == "randomized" else SEKV_SVD_EXACT, 0)
 
 
 def sekv_segment(cfg: SekvConfig, surprisal: torch.Tensor, stream=None):

@@ -13,7 +13,7 @@ OUT = os.path.join(HERE, "libsekv.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["sekv_api.cpp", "sekv_build.hip", "sekv_decode.hip", "sekv_cap.hip",
-           "sekv_resident.hip", "sekv_gates.hip"]
+           "sekv_resident.hip", "sekv_gates.hip", "sekv_rsvd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

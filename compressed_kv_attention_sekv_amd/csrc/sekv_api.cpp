@@ -62,6 +62,11 @@ sekv_status check_config(const sekv_config* c) {
     return fail(SEKV_ERR_INVALID, "kv_dtype must be SEKV_F32 or SEKV_BF16");
   if (c->factor_tier != SEKV_TIER_DEVICE && c->factor_tier != SEKV_TIER_HOST_PINNED)
     return fail(SEKV_ERR_INVALID, "factor_tier must be SEKV_TIER_DEVICE or SEKV_TIER_HOST_PINNED");
+  if (c->svd_mode != SEKV_SVD_EXACT && c->svd_mode != SEKV_SVD_RANDOMIZED)
+    return fail(SEKV_ERR_INVALID, "svd_mode must be SEKV_SVD_EXACT or SEKV_SVD_RANDOMIZED");
+  if (c->svd_mode == SEKV_SVD_RANDOMIZED && c->max_rank > kRsvdMaxRank)
+    return fail(SEKV_ERR_INVALID, "the randomized SVD supports max_rank <= %d", kRsvdMaxRank);
+  if (c->reserved != 0) return fail(SEKV_ERR_INVALID, "reserved must be 0");
   return SEKV_OK;
 }
 
@@ -304,10 +309,27 @@ static sekv_status build_impl(const sekv_config* cfg, int32_t n_tokens, const fl
     if ((r = scr.alloc(&pool_build, pool_bytes, "factor build buffer"))) return r;
   }
   {
-    std::vector<int32_t> ids[3];
+    std::vector<int32_t> ids[3], rs_ids[2];
+    const bool rsvd = cfg->svd_mode == SEKV_SVD_RANDOMIZED;
     for (int j = 0; j < sc; ++j) {
-      const int m = std::min(c->h_clen[j], kHeadDim);
+      const int n = c->h_clen[j];
+      if (rsvd && n > kRsvdMinRows && n <= kRsvdMaxRows) {
+        rs_ids[n <= 128 ? 0 : 1].push_back(j);
+        continue;
+      }
+      const int m = std::min(n, kHeadDim);
       ids[m <= 32 ? 0 : (m <= 64 ? 1 : 2)].push_back(j);
+    }
+    for (int b = 0; b < 2; ++b) {
+      if (rs_ids[b].empty()) continue;
+      int32_t* d_ids = nullptr;
+      if ((r = scr.alloc(&d_ids, rs_ids[b].size() * 4, "randomized svd span ids"))) return r;
+      SEKV_HIP(hipMemcpyAsync(d_ids, rs_ids[b].data(), rs_ids[b].size() * 4,
+                              hipMemcpyHostToDevice, st));
+      for (int which = 0; which < 2; ++which)
+        SEKV_HIP(launch_span_rsvd(c->bf16(), which ? v_dev : k_dev, n_tokens, c->cstart, c->clen,
+                                  d_ids, (int)rs_ids[b].size(), sc, n_lg, c->rank, c->fac_off,
+                                  pool_build, which, b ? kRsvdMaxRows : 128, st));
     }
     const int max_m[3] = {32, 64, 128};
     for (int b = 0; b < 3; ++b) {

@@ -215,6 +215,16 @@ hipError_t launch_span_svd(int bf16, const void* x, int n_tokens, const int32_t*
                            int n_lg, const int32_t* rank, const uint64_t* fac_off, float* pool,
                            int which, int max_m, hipStream_t st);
 
+// randomized truncated SVD (build option): spans of kRsvdMinRows < n <=
+// kRsvdMaxRows tokens, ranks up to kRsvdMaxRank; other spans take the exact path
+constexpr int kRsvdMaxRank = 32;
+constexpr int kRsvdMinRows = 40;
+constexpr int kRsvdMaxRows = 256;
+hipError_t launch_span_rsvd(int bf16, const void* x, int n_tokens, const int32_t* cstart,
+                            const int32_t* clen, const int32_t* span_ids, int n_ids, int sc,
+                            int n_lg, const int32_t* rank, const uint64_t* fac_off, float* pool,
+                            int which, int max_rows, hipStream_t st);
+
 hipError_t launch_layer(int bf16, int mode, const LayerGeom& g, const LayerArgs& a,
                         hipStream_t st);
 hipError_t launch_layer_batch(int bf16, int mode, int group, const BatchLayerArgs& b, int batch,

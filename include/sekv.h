@@ -52,6 +52,12 @@ typedef enum {
 /* storage type of keys, values, coarse means and summaries */
 typedef enum { SEKV_F32 = 0, SEKV_BF16 = 1 } sekv_dtype;
 
+/* how the per-span truncated SVD is computed: exactly (Gram matrix and
+ * one-sided Jacobi in float64), or by a randomized range finder with power
+ * iterations (SeKV paper Sec. 3.2 names a randomized SVD) for spans of
+ * 41..256 tokens, the others exactly; the randomized mode needs max_rank <= 32 */
+typedef enum { SEKV_SVD_EXACT = 0, SEKV_SVD_RANDOMIZED = 1 } sekv_svd_mode;
+
 /* where the span factors live: device HBM, or pinned host memory fetched per
  * step for the zoomed spans only (SeKV paper Sec. 3.2: bases on the CPU,
  * fetched asynchronously for selected spans) */
@@ -71,6 +77,8 @@ typedef struct {
   int32_t kv_dtype;       /* sekv_dtype */
   int32_t factor_tier;    /* sekv_tier */
   uint64_t host_pool_cap_bytes;  /* host tier: refuse a pool larger than this (0 = no cap) */
+  int32_t svd_mode;       /* sekv_svd_mode */
+  int32_t reserved;       /* must be 0 */
 } sekv_config;
 
 typedef struct {

@@ -34,8 +34,8 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_config_struct_layout_matches_header():
-    # int32 x8, double x2, int32 x2, uint64 -> 64 bytes with natural alignment
-    assert ctypes.sizeof(S.SekvConfig) == 64
+    # int32 x8, double x2, int32 x2, uint64, int32 x2 -> 72 bytes with natural alignment
+    assert ctypes.sizeof(S.SekvConfig) == 72
     assert ctypes.sizeof(S.SekvRouteOut) == 48
 
 
@@ -60,6 +60,8 @@ def _cfg(**kw):
     ("kv_dtype", 7, "kv_dtype"),
     ("factor_tier", 3, "factor_tier"),
     ("alpha", float("nan"), "finite"),
+    ("svd_mode", 2, "svd_mode"),
+    ("reserved", 1, "reserved"),
 ])
 def test_build_rejects_bad_config(L, field, value, msg):
     cfg = _cfg(**{field: value})
