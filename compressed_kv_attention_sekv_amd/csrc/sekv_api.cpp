@@ -309,18 +309,19 @@ static sekv_status build_impl(const sekv_config* cfg, int32_t n_tokens, const fl
     if ((r = scr.alloc(&pool_build, pool_bytes, "factor build buffer"))) return r;
   }
   {
-    std::vector<int32_t> ids[3], rs_ids[2];
+    std::vector<int32_t> ids[3], rs_ids[3];
+    const int rs_rows[3] = {128, 256, kRsvdMaxRows};
     const bool rsvd = cfg->svd_mode == SEKV_SVD_RANDOMIZED;
     for (int j = 0; j < sc; ++j) {
       const int n = c->h_clen[j];
       if (rsvd && n > kRsvdMinRows && n <= kRsvdMaxRows) {
-        rs_ids[n <= 128 ? 0 : 1].push_back(j);
+        rs_ids[n <= 128 ? 0 : (n <= 256 ? 1 : 2)].push_back(j);
         continue;
       }
       const int m = std::min(n, kHeadDim);
       ids[m <= 32 ? 0 : (m <= 64 ? 1 : 2)].push_back(j);
     }
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < 3; ++b) {
       if (rs_ids[b].empty()) continue;
       int32_t* d_ids = nullptr;
       if ((r = scr.alloc(&d_ids, rs_ids[b].size() * 4, "randomized svd span ids"))) return r;
@@ -329,7 +330,7 @@ static sekv_status build_impl(const sekv_config* cfg, int32_t n_tokens, const fl
       for (int which = 0; which < 2; ++which)
         SEKV_HIP(launch_span_rsvd(c->bf16(), which ? v_dev : k_dev, n_tokens, c->cstart, c->clen,
                                   d_ids, (int)rs_ids[b].size(), sc, n_lg, c->rank, c->fac_off,
-                                  pool_build, which, b ? kRsvdMaxRows : 128, st));
+                                  pool_build, which, rs_rows[b], st));
     }
     const int max_m[3] = {32, 64, 128};
     for (int b = 0; b < 3; ++b) {

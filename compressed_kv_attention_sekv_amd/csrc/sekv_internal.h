@@ -217,9 +217,10 @@ hipError_t launch_span_svd(int bf16, const void* x, int n_tokens, const int32_t*
 
 // randomized truncated SVD (build option): spans of kRsvdMinRows < n <=
 // kRsvdMaxRows tokens, ranks up to kRsvdMaxRank; other spans take the exact path
+// (launches sized for 128, 256 and kRsvdMaxRows rows)
 constexpr int kRsvdMaxRank = 32;
 constexpr int kRsvdMinRows = 40;
-constexpr int kRsvdMaxRows = 256;
+constexpr int kRsvdMaxRows = 640;
 hipError_t launch_span_rsvd(int bf16, const void* x, int n_tokens, const int32_t* cstart,
                             const int32_t* clen, const int32_t* span_ids, int n_ids, int sc,
                             int n_lg, const int32_t* rank, const uint64_t* fac_off, float* pool,

@@ -14,9 +14,9 @@
 // numerically dependent column, which is zeroed and carries no component.
 //
 // One workgroup of 256 threads per (span, layer x KV head), spans of
-// 40 < n <= 256 tokens and ranks up to 32; everything but X sits in LDS, sized
-// for up to 128 or 256 rows (two launches), so that spans of up to 128 tokens
-// fit two workgroups per CU.
+// 40 < n <= 640 tokens and ranks up to 32; everything but X sits in LDS, sized
+// for up to 128, 256 or 640 rows (one launch each), so that spans of up to 128
+// tokens fit two workgroups per CU.
 #include <hip/hip_runtime.h>
 
 #include "sekv_internal.h"
@@ -353,6 +353,7 @@ hipError_t launch_span_rsvd(int bf16, const void* x, int n_tokens, const int32_t
               : launch_rsvd_t<float, ROWS>((const float*)x, n_tokens, cstart, clen, span_ids,   \
                                            n_ids, sc, n_lg, rank, fac_off, pool, which, st)
   if (max_rows <= 128) { SEKV_RSVD(128); }
+  if (max_rows <= 256) { SEKV_RSVD(256); }
   SEKV_RSVD(kRsvdMaxRows);
 #undef SEKV_RSVD
 }

@@ -55,7 +55,7 @@ typedef enum { SEKV_F32 = 0, SEKV_BF16 = 1 } sekv_dtype;
 /* how the per-span truncated SVD is computed: exactly (Gram matrix and
  * one-sided Jacobi in float64), or by a randomized range finder with power
  * iterations (SeKV paper Sec. 3.2 names a randomized SVD) for spans of
- * 41..256 tokens, the others exactly; the randomized mode needs max_rank <= 32 */
+ * 41..640 tokens, the others exactly; the randomized mode needs max_rank <= 32 */
 typedef enum { SEKV_SVD_EXACT = 0, SEKV_SVD_RANDOMIZED = 1 } sekv_svd_mode;
 
 /* where the span factors live: device HBM, or pinned host memory fetched per

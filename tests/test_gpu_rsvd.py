@@ -44,9 +44,12 @@ def test_randomized_svd_bounds_and_attention(S, name, kw):
     orc = OracleSide(inp, layers, wl.max_rank)
     seg = orc.seg
     n_all = seg.span_len[seg.cspan]
-    cand = np.flatnonzero((n_all > 40) & (n_all <= 256))
+    cand = np.flatnonzero((n_all > 40) & (n_all <= 640))
     assert cand.size > 0
-    idx = cand[np.unique(np.linspace(0, cand.size - 1, min(cand.size, 48)).astype(int))]
+    # an even sample, plus every span of the 256- and 640-row launches
+    idx = np.union1d(cand[np.unique(np.linspace(0, cand.size - 1, min(cand.size, 48)).astype(int))],
+                     np.flatnonzero((n_all > 128) & (n_all <= 640)))
+    log(f"[rsvd] spans checked: {idx.size}, longest {int(n_all[idx].max())} tokens")
     worst = {"sigma": 0.0, "excess": 0.0, "rec": 0.0}
     for layer in layers:
         for kh in range(wl.n_kv_heads):
