@@ -160,6 +160,17 @@ template <int G> constexpr int stage_rows() { return G <= 5 ? 32 : 24; }
 // a stage: SR rows of V_K, then 64 floats of sigma_K and 64 of sigma_V
 template <int SR> constexpr int stage_floats() { return SR * kHeadDim + 128; }
 
+// The last workgroup's merge: thread = (head, 4 dims, stripe of slots); the
+// stripes are combined through LDS.
+template <int G> constexpr int merge_quads() { return G * (kHeadDim / 4); }
+template <int G> constexpr int merge_stripes() {
+  return (kThreads / merge_quads<G>()) > 0 ? (kThreads / merge_quads<G>()) : 1;
+}
+template <int G> struct MergeScratch {
+  float4 red[merge_stripes<G>() * merge_quads<G>()];   // each stripe's acc
+  float m[merge_stripes<G>() * G], l[merge_stripes<G>() * G];
+};
+
 template <int G>
 struct alignas(16) Smem {
   float qs[G][kHeadDim];           // query * 1/sqrt(d)
@@ -176,6 +187,7 @@ struct alignas(16) Smem {
       double qt[G][kMaxRouteDim];  // P_h q_h
     } rt;
     WaveScratch<G> w[kWaves];      // written from the rows phase on
+    MergeScratch<G> mg;            // the last workgroup's merge (the wave states are dead)
   };
 };
 // Per wave: V_K of its next zoomed span, written by LDS DMA while the current
@@ -727,6 +739,8 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
   for (int k = 0; k < VK; ++k)
     vd[k] = *(const float4*)(vv + (size_t)min(2 * k + half, r - 1) * kHeadDim + 4 * dq);
   float4 va[4][4];   // V_K from memory, only when it is not staged
+  float sgm[4];      // and then sigma_K and sigma_V too (the stage holds another span's)
+  float4 svm = make_float4(0.f, 0.f, 0.f, 0.f);
   if (!staged) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -735,18 +749,26 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
       for (int c4 = 0; c4 < 4; ++c4)
         va[p][c4] = *(const float4*)(vk + (size_t)i * kHeadDim + part * 16 + c4 * 4);
     }
+    // entries clamped to the block's r4 (as the stage copy is)
+    const float* sk = cu.blk + fv.sigma(0);
+    const float* sv = cu.blk + fv.sigma(1);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) sgm[p] = sk[min(ci + 8 * p, r4 - 1)];
+    svm = make_float4(sv[min(4 * cg, r4 - 1)], sv[min(4 * cg + 1, r4 - 1)],
+                      sv[min(4 * cg + 2, r4 - 1)], sv[min(4 * cg + 3, r4 - 1)]);
   }
 
   // sigma_K of the lane's components in (A) (ci + 8 p) and sigma_V of its
-  // components after (C) (4 cg ..), from the stage.  Its DMA was followed by
+  // components after (C) (4 cg ..), from the stage (for a span too large for
+  // the stage, from its block, loaded above).  The stage's DMA was followed by
   // the 8 loads of U_K rows prefetched for this span and the UQ + VK above,
   // so once at most that many are outstanding the DMA has landed.
   issue_fence();
   wait_vm<8 + UQ + VK>();
   float sg[4];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) sg[p] = stage[SR * kHeadDim + ci + 8 * p];
-  const float4 svg = *(const float4*)(stage + SR * kHeadDim + 64 + 4 * cg);
+  for (int p = 0; p < 4; ++p) sg[p] = staged ? stage[SR * kHeadDim + ci + 8 * p] : sgm[p];
+  const float4 svg = staged ? *(const float4*)(stage + SR * kHeadDim + 64 + 4 * cg) : svm;
 
   // (A) components at or past r get exactly 0 (a stage row past r may hold
   // anything)
@@ -1270,8 +1292,8 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
   const bool merge = (mode & kMerge) != 0;
   const int ns = (mode & kZoomSplit) ? 2 * W : W;
   const float* pg = a.part + (size_t)g * geo.n_slots() * G * kPartStride;
-  constexpr int QUADS = G * (kHeadDim / 4);
-  constexpr int STRIPES = (kThreads / QUADS) > 0 ? (kThreads / QUADS) : 1;
+  constexpr int QUADS = merge_quads<G>();
+  constexpr int STRIPES = merge_stripes<G>();
   constexpr int B = 24;
   const int quad = tid % QUADS, stripe = tid / QUADS;
   const int hl = quad / (kHeadDim / 4), dq = quad % (kHeadDim / 4);
@@ -1383,10 +1405,10 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
         add_batch(sl0);
       }
     }
-    // the wave scratch is free again
-    float4* red = (float4*)&s.w[0];
-    float* red_m = (float*)(red + STRIPES * QUADS);
-    float* red_l = red_m + STRIPES * G;
+    // the wave states are dead: the merge scratch overlays them
+    float4* red = s.mg.red;
+    float* red_m = s.mg.m;
+    float* red_l = s.mg.l;
     if (stripe < STRIPES) {
       red[stripe * QUADS + quad] = acc;
       if (dq == 0) {

@@ -398,3 +398,40 @@ def test_full_size_sampled_parity(S, layer, kv_head):
     log(f"[parity] full size: zoom {route.mask.mean(axis=1).round(3).tolist()} ties {int(tie.sum())} "
         f"attention err {worst:.2e}")
     assert worst <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (6, 2), (12, 2), (16, 2)])
+def test_group_sizes(S, hq, hkv):
+    """Query heads per KV head G = 1, 2, 3, 6 and 8 (the kernels are instantiated
+    for every G up to 8): route and attention against the oracle, both call
+    paths bit-identical, and the budget cap on the same route."""
+    wl = synth.workload("llama3_8b_128k", n_layers=1, n_tokens=5000, n_q_heads=hq, n_kv_heads=hkv)
+    log(f"[parity] group size G={hq // hkv} ({hq}/{hkv} heads)")
+    inp = Inputs(wl, 12)
+    cache = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    orc = OracleSide(inp, [0], wl.max_rank)
+    compare_spans(cache, orc)
+    q = inp.query(0)[0]
+    prob = orc.route(0, to64(q), to64(inp.p[0]), np.full(hq, 2.0), wl.gamma).prob
+    tau = torch.tensor([float(np.quantile(prob[h], 0.75)) for h in range(hq)],
+                       dtype=torch.float32).cuda()
+    n_tie, worst, route = check_layer(S, cache, orc, inp, 0, q, tau, wl.gamma, TOL["bf16"])
+    # the budget cap on the GPU's own route, against the oracle's cap
+    rb, _ = run_gpu_layer(S, cache, 0, q, inp.p[0], tau)
+    gp = rb.prob.cpu().numpy()[:, :cache.info.n_compressed]
+    gm = rb.mask.cpu().numpy().astype(bool)[:, :cache.info.n_compressed]
+    g = hq // hkv
+    uncapped = O.LayerRoute(prob=gp, mask=gm, lists=[O.compact(gm[h]) for h in range(hq)],
+                            unions=[O.union_lists(list(gm[k * g:(k + 1) * g])) for k in range(hkv)])
+    n = orc.seg.span_len[orc.seg.cspan].astype(np.int64)
+    budget = int(np.median([n[u].sum() for u in uncapped.unions]) // 2)
+    S.sekv_cap_budget(cache, rb, budget)
+    torch.cuda.synchronize()
+    ref = O.cap_budget(uncapped, orc.seg, hkv, budget)
+    assert np.array_equal(rb.mask.cpu().numpy().astype(bool)[:, :cache.info.n_compressed], ref.mask)
+    for k in range(hkv):
+        assert rb.union_list[k, :int(rb.union_count[k])].cpu().tolist() == ref.unions[k].tolist()
+    for h in range(hq):
+        assert rb.list[h, :int(rb.count[h])].cpu().tolist() == ref.lists[h].tolist()
+    log(f"[parity] G={g}: zoom={route.mask.mean():.3f} ties={n_tie} err={worst:.2e} "
+        f"budget={budget} capped pairs={int(ref.mask.sum())}")
