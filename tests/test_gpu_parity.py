@@ -400,12 +400,17 @@ def test_full_size_sampled_parity(S, layer, kv_head):
     assert worst <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (6, 2), (12, 2), (16, 2)])
-def test_group_sizes(S, hq, hkv):
-    """Query heads per KV head G = 1, 2, 3, 6 and 8 (the kernels are instantiated
-    for every G up to 8): route and attention against the oracle, both call
-    paths bit-identical, and the budget cap on the same route."""
-    wl = synth.workload("llama3_8b_128k", n_layers=1, n_tokens=5000, n_q_heads=hq, n_kv_heads=hkv)
+@pytest.mark.parametrize("name,hq,hkv", [
+    ("llama3_8b_128k", 4, 4), ("llama3_8b_128k", 8, 4), ("llama3_8b_128k", 6, 2),
+    ("llama3_8b_128k", 12, 2), ("llama3_8b_128k", 16, 2),
+    ("tiny", 2, 2), ("tiny", 4, 2), ("tiny", 8, 1)])
+def test_group_sizes(S, name, hq, hkv):
+    """Query heads per KV head G = 1, 2, 3, 6 and 8 with bf16 K/V and G = 1, 2
+    and 8 with float32 K/V (the kernels are instantiated for every G up to 8
+    and both storage types): route and attention against the oracle, both
+    call paths bit-identical, and the budget cap on the same route."""
+    kw = dict(n_layers=1, n_tokens=5000) if name != "tiny" else {}
+    wl = synth.workload(name, n_q_heads=hq, n_kv_heads=hkv, **kw)
     log(f"[parity] group size G={hq // hkv} ({hq}/{hkv} heads)")
     inp = Inputs(wl, 12)
     cache = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
@@ -415,7 +420,7 @@ def test_group_sizes(S, hq, hkv):
     prob = orc.route(0, to64(q), to64(inp.p[0]), np.full(hq, 2.0), wl.gamma).prob
     tau = torch.tensor([float(np.quantile(prob[h], 0.75)) for h in range(hq)],
                        dtype=torch.float32).cuda()
-    n_tie, worst, route = check_layer(S, cache, orc, inp, 0, q, tau, wl.gamma, TOL["bf16"])
+    n_tie, worst, route = check_layer(S, cache, orc, inp, 0, q, tau, wl.gamma, TOL[wl.kv_dtype])
     # the budget cap on the GPU's own route, against the oracle's cap
     rb, _ = run_gpu_layer(S, cache, 0, q, inp.p[0], tau)
     gp = rb.prob.cpu().numpy()[:, :cache.info.n_compressed]
