@@ -440,6 +440,11 @@ def main():
                   "zoom_frac_per_head_mean": float(zoom_frac.mean()),
                   "union_frac_per_group_mean": float(union_frac.mean()),
                   "zoom_bytes_per_step_gb": float(zb_step.mean()) / 1e9,
+                  # the GPU KV budget of a step: what is resident plus the factors
+                  # of the spans zoomed in it, against the full-resolution K/V
+                  "kv_budget_frac": (sum(c.info.resident_bytes for c in caches) +
+                                     float(zb_step.mean())) /
+                                    (B * L * Hkv * wl.n_tokens * d * 2 * eb),
                   "tokens_per_s": B * 1e3 / ms_per_step},
     }
     print(json.dumps(result), flush=True)
