@@ -238,12 +238,14 @@ size_t cap_budget_lds_bytes(int sc);
 hipError_t launch_cap_budget(int sc, int hkv, int group, long long budget, const int32_t* clen,
                              const double* prob, uint8_t* mask, int32_t* list, int32_t* count,
                              int32_t* ulist, int32_t* ucount, hipStream_t st);
-// HBM residency cache of host-tier factor blocks (direct-mapped, one slot per
-// set).  A block's key is (layer * Hkv + g) * S_c + j, below 2^kResKeyBits; a
-// set's claim is (epoch << kResKeyBits) | (kResKeyMask - key) of its winner.
-constexpr int kResKeyBits = 40;
+// HBM residency cache of host-tier factor blocks (two-choice: a block may sit
+// in either of two hashed sets, one slot per set).  A block's key is
+// (layer * Hkv + g) * S_c + j, below 2^kResKeyBits; a set's claim is
+// (epoch << (kResKeyBits + 1)) | (holds << kResKeyBits) | (kResKeyMask - key)
+// of its winner, holds = 1 if the set already holds that block.
+constexpr int kResKeyBits = 39;
 constexpr uint64_t kResKeyMask = (1ull << kResKeyBits) - 1;
-constexpr uint64_t kResMaxEpoch = (1ull << (64 - kResKeyBits)) - 1;
+constexpr uint64_t kResMaxEpoch = (1ull << (64 - kResKeyBits - 1)) - 1;
 struct ResidencyView {
   float* arena;                // [staging of one layer | n_sets slots]
   uint64_t slots_off;          // first float of slot 0

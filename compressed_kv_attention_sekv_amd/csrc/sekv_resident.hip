@@ -6,23 +6,24 @@
 // transfer as the cost of the CPU tier).  Decoding tends to zoom the same
 // spans again, so blocks stay in an HBM cache between calls.
 //
-// The cache is direct-mapped: block (layer, KV head, span) may live only in
-// set hash(key) mod n_sets, one fixed-size slot per set, with the set's tag
-// naming the block it holds.  One call (one layer) runs two kernels on the
-// fetch stream:
-//   claim: every union span whose block fits a slot bids for its set with a
-//          64-bit atomicMax of (epoch, inverted key), so within a call the
-//          lowest key wins each set, and bids of older calls always lose
-//          (no reset pass);
-//   fetch: a winner whose set's tag already names it is a hit (no copy);
-//          any other winner copies its block from host memory into the slot
-//          and takes the tag; losers and oversize blocks are copied into the
-//          layer's staging area at their layer-relative offsets, as without
-//          the cache.  Each union span's block offset goes to an offset table
-//          that the attention reads instead of the pool's own offsets.
-// Each set is written by at most one span per call, so the blocks a call
-// reads are never overwritten during it; results do not depend on where a
-// block was read from.
+// Placement is two-choice: block (layer, KV head, span) may live in set
+// h1(key) or h2(key) (two hashes mod n_sets), one fixed-size slot per set,
+// each set tagged with the block it holds.  One call (one layer) runs two
+// kernels on the fetch stream:
+//   claim: every union span whose block fits a slot bids for both its sets
+//          with a 64-bit atomicMax of (epoch, holds, inverted key): bids of
+//          older calls always lose (no reset pass), a set's current holder
+//          beats any newcomer, and otherwise the lowest key wins;
+//   fetch: a span reads its block from a set it won that holds it (a hit, no
+//          copy); else it copies the block from host memory into a set it won
+//          (the first) and takes the tag; a span that won neither set, or
+//          whose block is larger than a slot, is copied into the layer's
+//          staging area at its layer-relative offset, as without the cache.
+//          Each union span's block offset goes to an offset table that the
+//          attention reads instead of the pool's own offsets.
+// Each set is written by at most its winner in a call and a span reads only a
+// set it won, so no block a call reads is overwritten during it; results do
+// not depend on where a block was read from.
 #include <hip/hip_runtime.h>
 
 #include "sekv_internal.h"
@@ -42,15 +43,23 @@ __device__ __forceinline__ uint64_t res_mix(uint64_t x) {
   return x;
 }
 
-__device__ __forceinline__ uint64_t res_bid(uint64_t epoch, uint64_t key) {
-  return (epoch << kResKeyBits) | (kResKeyMask - key);
+__device__ __forceinline__ uint64_t res_bid(uint64_t epoch, bool holds, uint64_t key) {
+  return (epoch << (kResKeyBits + 1)) | ((uint64_t)holds << kResKeyBits) | (kResKeyMask - key);
+}
+
+// the two candidate sets of a block (distinct when there are two sets or more)
+__device__ __forceinline__ void res_sets(uint64_t key, uint64_t n_sets, uint64_t& s1,
+                                         uint64_t& s2) {
+  const uint64_t h = res_mix(key);
+  s1 = h % n_sets;
+  s2 = n_sets > 1 ? (s1 + 1 + (res_mix(h) % (n_sets - 1))) % n_sets : s1;
 }
 
 __global__ __launch_bounds__(256) void res_claim_kernel(
     const int32_t* __restrict__ ulist, const int32_t* __restrict__ ucount,
     const int32_t* __restrict__ clen, const int32_t* __restrict__ rank, int sc, int layer,
     int hkv, uint64_t slot_floats, uint64_t n_sets, uint64_t epoch,
-    unsigned long long* __restrict__ claim) {
+    const long long* __restrict__ tag, unsigned long long* __restrict__ claim) {
   const int g = blockIdx.y;
   const int nu = ucount[g];
   for (int u = blockIdx.x * 256 + threadIdx.x; u < nu; u += gridDim.x * 256) {
@@ -58,7 +67,11 @@ __global__ __launch_bounds__(256) void res_claim_kernel(
     const FactorView fv(rank[(size_t)g * sc + j], clen[j]);
     if (fv.block_floats() > slot_floats) continue;
     const uint64_t key = ((uint64_t)layer * hkv + g) * (uint64_t)sc + j;
-    atomicMax(&claim[res_mix(key) % n_sets], (unsigned long long)res_bid(epoch, key));
+    uint64_t s1, s2;
+    res_sets(key, n_sets, s1, s2);
+    atomicMax(&claim[s1], (unsigned long long)res_bid(epoch, tag[s1] == (long long)key, key));
+    if (s2 != s1)
+      atomicMax(&claim[s2], (unsigned long long)res_bid(epoch, tag[s2] == (long long)key, key));
   }
 }
 
@@ -80,12 +93,22 @@ __global__ __launch_bounds__(256) void res_fetch_kernel(
     const uint64_t key = ((uint64_t)layer * hkv + g) * (uint64_t)sc + j;
     uint64_t dst_off = hoff - layer_base;   // the layer's staging (arena start)
     bool copy = true, hit = false, cached = false;
+    uint64_t set = 0;
     if (nfl <= slot_floats) {
-      const uint64_t set = res_mix(key) % n_sets;
-      if (claim[set] == res_bid(epoch, key)) {
+      uint64_t s1, s2;
+      res_sets(key, n_sets, s1, s2);
+      const bool h1 = tag[s1] == (long long)key, h2 = tag[s2] == (long long)key;
+      const bool w1 = claim[s1] == res_bid(epoch, h1, key);
+      const bool w2 = s2 != s1 && claim[s2] == res_bid(epoch, h2, key);
+      if ((w1 && h1) || (w2 && h2)) {
+        set = (w1 && h1) ? s1 : s2;
+        hit = true;
+      } else if (w1 || w2) {
+        set = w1 ? s1 : s2;
+      }
+      if (w1 || w2) {
         cached = true;
         dst_off = slots_off + set * slot_floats;
-        hit = tag[set] == (long long)key;
         copy = !hit;
       }
     }
@@ -99,7 +122,7 @@ __global__ __launch_bounds__(256) void res_fetch_kernel(
     __syncthreads();
     if (threadIdx.x == 0) {
       off_out[(size_t)g * sc + j] = dst_off;
-      if (cached && !hit) tag[res_mix(key) % n_sets] = (long long)key;
+      if (cached && !hit) tag[set] = (long long)key;
       const unsigned long long bytes = 8ull * (unsigned long long)fv.r *
                                        (unsigned long long)(fv.n + kHeadDim + 1);
       atomicAdd(&stats[hit ? 0 : 1], 1ull);
@@ -120,7 +143,7 @@ hipError_t launch_resident_fetch(const LayerGeom& g, int layer, const int32_t* u
   const int cx = (sc + 255) / 256;
   hipLaunchKernelGGL(res_claim_kernel, dim3(cx < 64 ? cx : 64, hkv), dim3(256), 0, st, ulist,
                      ucount, clen, rank, sc, layer, hkv, rv.slot_floats, rv.n_sets, epoch,
-                     rv.claim);
+                     rv.tag, rv.claim);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(res_fetch_kernel, dim3(kResSlotsPerHead, hkv), dim3(256), 0, st, ulist,

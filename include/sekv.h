@@ -254,12 +254,13 @@ sekv_status sekv_apply_gates(sekv_cache* cache, const float* gates_dev, float ep
  * limitations name that transfer as the cost of the CPU tier).  Once enabled,
  * each host-tier sekv_decode_attn / sekv_route_attn keeps the zoomed spans'
  * factor blocks in HBM, so a span zoomed again in a later call (same layer and
- * KV head) is read from HBM instead of crossing the host link.  The cache is
- * direct-mapped: block (layer, KV head, span) may occupy only the set given by
- * a fixed hash of that key, one slot of slot_bytes (rounded up to 256) per
- * set, capacity_bytes / slot_bytes sets.  Within one call, spans of the union
- * that share a set are resolved by the lowest key; the others, and blocks
- * larger than a slot, are copied to per-layer staging as without the cache.
+ * KV head) is read from HBM instead of crossing the host link.  Block
+ * (layer, KV head, span) may occupy either of two sets given by fixed hashes of
+ * that key, one slot of slot_bytes (rounded up to 256) per set,
+ * capacity_bytes / slot_bytes sets.  Within one call, a set goes to the block
+ * it already holds if that block is zoomed, else to the lowest key that wants
+ * it; spans that get neither of their sets, and blocks larger than a slot, are
+ * copied to per-layer staging as without the cache.
  * Outputs do not depend on the cache (a block is the same bytes wherever it is
  * read from).
  *   capacity_bytes: 0 disables the cache and frees it.
