@@ -440,3 +440,43 @@ def test_group_sizes(S, name, hq, hkv):
         assert rb.list[h, :int(rb.count[h])].cpu().tolist() == ref.lists[h].tolist()
     log(f"[parity] G={g}: zoom={route.mask.mean():.3f} ties={n_tie} err={worst:.2e} "
         f"budget={budget} capped pairs={int(ref.mask.sum())}")
+
+
+@pytest.mark.parametrize("case", ["route_dim_7", "route_dim_64_bf16", "no_window_unit_spans",
+                                  "one_past_window", "rank_one"])
+def test_config_edges(S, case):
+    """Configurations off the common path: routing dimensions that take the
+    general summary loads (7 floats, 64 bf16), no local window with every
+    non-anchor run compressed down to one-token spans, a context one token past
+    the window, and rank-1 factors; all against the oracle."""
+    wl = synth.workload("tiny")
+    max_rank = None
+    if case == "route_dim_7":
+        wl = wl.with_(route_dim=7)
+    elif case == "route_dim_64_bf16":
+        wl = synth.workload("llama3_8b_128k", n_layers=1, n_tokens=4000, route_dim=64)
+    elif case == "no_window_unit_spans":
+        wl = wl.with_(n_tokens=1500, window=0, min_span_len=1)
+    elif case == "one_past_window":
+        wl = wl.with_(n_tokens=wl.window + 1)
+    elif case == "rank_one":
+        max_rank = 1
+    log(f"[parity] config edge {case}")
+    inp = Inputs(wl, 21)
+    cache = S.sekv_build_spans(make_cfg(S, wl, max_rank=max_rank), inp.s, inp.k, inp.v, inp.w,
+                               inp.ranks)
+    orc = OracleSide(inp, [0], wl.max_rank if max_rank is None else max_rank)
+    compare_spans(cache, orc)
+    if cache.info.n_compressed:
+        for kh in range(wl.n_kv_heads):
+            compare_group(cache, orc, 0, kh, n_factor_checks=20)
+    q = inp.query(0)[0]
+    if cache.info.n_compressed:
+        prob = orc.route(0, to64(q), to64(inp.p[0]), np.full(wl.n_q_heads, 2.0), wl.gamma).prob
+        tau = torch.tensor([float(np.quantile(prob[h], 0.7)) for h in range(wl.n_q_heads)],
+                           dtype=torch.float32).cuda()
+    else:
+        tau = torch.full((wl.n_q_heads,), 0.5, device="cuda")
+    n_tie, worst, route = check_layer(S, cache, orc, inp, 0, q, tau, wl.gamma, TOL[wl.kv_dtype])
+    log(f"[parity] config edge {case}: spans={cache.info.n_compressed} dense={cache.info.n_dense} "
+        f"zoomed pairs={int(route.mask.sum())} ties={n_tie} err={worst:.2e}")
