@@ -155,3 +155,37 @@ def test_budget_cap_rejects_bad_arguments(S):
     import ctypes
     assert S.lib().sekv_cap_budget(cache.handle, ctypes.byref(st), 5, None) == S.SEKV_ERR_INVALID
     assert b"prob" in S.lib().sekv_last_error()
+
+
+def test_budget_cap_large_union(S):
+    """A union of thousands of spans (short spans, every span zoomed), so the
+    cap runs its multi-tile comparison and multi-block compaction: masks,
+    lists and unions bit-exact against the oracle's cap on the GPU's gates."""
+    wl = synth.workload("tiny", n_tokens=40000, min_span_len=1)
+    hq, hkv = wl.n_q_heads, wl.n_kv_heads
+    inp = Inputs(wl, 4)
+    cache = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    seg = O.segment(to64(inp.s), wl.window, wl.alpha, wl.min_span_len)
+    sc = cache.info.n_compressed
+    assert sc == seg.n_compressed and sc > 4096
+    q = inp.query(0)[0].contiguous()
+    # every span zoomed by head 0, the others above their median gate
+    base = S.RouteBuffers.allocate(cache, with_prob=True)
+    S.sekv_route(cache, 0, q, inp.p[0].contiguous(), torch.full((hq,), 2.0, device="cuda"), base)
+    torch.cuda.synchronize()
+    med = base.prob[:, :sc].median(dim=1).values.float()
+    tau = torch.where(torch.arange(hq, device="cuda") == 0, torch.full_like(med, -1.0), med)
+    S.sekv_route(cache, 0, q, inp.p[0].contiguous(), tau.contiguous(), base)
+    torch.cuda.synchronize()
+    uncapped = gpu_route_as_oracle(base, sc, hq, hkv)
+    assert uncapped.unions[0].size == sc
+    n = seg.span_len[seg.cspan].astype(np.int64)
+    total = int(n.sum())
+    log(f"[budget] large union: {sc} spans, {total} tokens")
+    for budget in (total // 5, total // 2, total - 1):
+        rb = clone_route(S, base)
+        S.sekv_cap_budget(cache, rb, budget)
+        torch.cuda.synchronize()
+        ref = O.cap_budget(uncapped, seg, hkv, budget)
+        assert_route_equals(rb, ref, hq, hkv)
+        log(f"[budget] budget={budget}: kept {ref.unions[0].size} of {sc} spans")
