@@ -350,7 +350,17 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     copy_gbs = 5 * 2 * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del x, y
+    # read-only stream: row sums over the same 2 GiB (4096-float rows; writes
+    # 0.02% of what it reads), the fastest read-only torch op on this GPU
+    acc = x.view(-1, 4096).sum(dim=1)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        acc = x.view(-1, 4096).sum(dim=1)
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbs = 5 * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x, y, acc
     hpin = torch.empty(64 * 1024 * 1024, dtype=torch.float32, pin_memory=True)   # 256 MiB
     hd = torch.empty(hpin.shape, dtype=torch.float32, device=dev)
     hd.copy_(hpin, non_blocking=True)
@@ -362,7 +372,8 @@ def main():
     torch.cuda.synchronize()
     h2d_gbs = 4 * hpin.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del hpin, hd
-    log(f"probes: device copy {copy_gbs:.0f} GB/s (read+write), pinned H2D {h2d_gbs:.1f} GB/s")
+    log(f"probes: device copy {copy_gbs:.0f} GB/s (read+write), read-only {read_gbs:.0f} GB/s, "
+        f"pinned H2D {h2d_gbs:.1f} GB/s")
 
     host_link = None
     if args.tier == "host":
@@ -428,10 +439,11 @@ def main():
             "algorithmic_bytes_per_launch": attn_bytes_meas,
             "avg_launch_us": attn_us_mean,
             "avg_launch_from": "HIP events around the timed region / (steps x layers)",
+            "frac_of_measured_read": attn_gbs / read_gbs,
         },
         "cpu_baseline": cpu,
         "step_hbm": {"bytes_per_step": bytes_step, "gbs": step_gbs, "frac": step_gbs / HBM_PEAK_GBS,
-                     "measured_copy_gbs": copy_gbs},
+                     "measured_copy_gbs": copy_gbs, "measured_read_gbs": read_gbs},
         "host_link": host_link,
         "measured_h2d_gbs": h2d_gbs,
         "cache": {"n_spans": info.n_spans, "n_compressed": sc, "n_anchors": info.n_anchors,
