@@ -70,7 +70,7 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    """Hash of the sources the layer kernel is compiled from."""
+    """Hash of the sources the layer kernels are compiled from."""
     h = hashlib.sha256()
     for f in ("sekv_decode.hip", "sekv_internal.h"):
         with open(os.path.join(ROOT, "compressed_kv_attention_sekv_amd", "csrc", f), "rb") as fh:
@@ -432,13 +432,15 @@ def main():
             "traffic": traffic,
             "kernel": ("sekv::layer_kernel x2 + sekv::cap_budget_kernel (sekv_route, "
                        "sekv_cap_budget, sekv_decode_attn: one layer, capped)" if capped else
-                       "sekv::layer_kernel (sekv_route_attn, one layer: route + attention)"
+                       "sekv::layer_kernel + sekv::layer_tail_kernel (sekv_route_attn, one "
+                       "layer: route + attention, then merge + lists)"
                        if B == 1 else
-                       f"sekv::layer_batch_kernel (sekv_route_attn_batch, one layer of {B} "
-                       "sequences: route + attention)"),
+                       f"sekv::layer_batch_kernel + sekv::layer_tail_batch_kernel "
+                       f"(sekv_route_attn_batch, one layer of {B} sequences)"),
             "algorithmic_bytes_per_launch": attn_bytes_meas,
             "avg_launch_us": attn_us_mean,
-            "avg_launch_from": "HIP events around the timed region / (steps x layers)",
+            "avg_launch_from": "HIP events around the timed region / (steps x layers); "
+                               "a layer is its two launches",
             "frac_of_measured_read": attn_gbs / read_gbs,
         },
         "cpu_baseline": cpu,

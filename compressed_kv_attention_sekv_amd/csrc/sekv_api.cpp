@@ -143,8 +143,6 @@ struct sekv_cache {
   float* pool_host_dev = nullptr; // device view of pool_host
   float* stage = nullptr;         // host tier: device staging for one layer
   uint64_t stage_floats = 0;
-  // decode: per-KV-head tickets of the layer kernel (zero between launches)
-  uint32_t* tickets = nullptr;
   uint32_t* chunk_bits = nullptr;  // [Hkv][n_work][kListWords] zoom bit masks of each chunk
   float* zero_block = nullptr;     // kZeroBlockFloats zeros: a valid source for idle prefetches
   LayerGeom geom{};
@@ -359,10 +357,8 @@ static sekv_status build_impl(const sekv_config* cfg, int32_t n_tokens, const fl
     if ((r = c->alloc(&c->stage, (size_t)stage_max * 4, "fetch staging"))) return r;
   }
 
-  // ---- decode geometry, tickets and chunk bit masks ---------------------------
+  // ---- decode geometry and chunk bit masks --------------------------------------
   c->geom = make_layer_geom(Hq, Hkv, dr, D, sc);
-  if ((r = c->alloc(&c->tickets, (size_t)Hkv * 4, "layer tickets"))) return r;
-  SEKV_HIP(hipMemsetAsync(c->tickets, 0, (size_t)Hkv * 4, st));
   if ((r = c->alloc(&c->chunk_bits, (size_t)Hkv * c->geom.n_work * kListWords * 4, "chunk bits")))
     return r;
   if ((r = c->alloc(&c->zero_block, (size_t)kZeroBlockFloats * 4, "zero block"))) return r;
@@ -535,7 +531,6 @@ LayerArgs layer_args(const sekv_cache* c, int32_t layer, const float* q, const f
   }
   a.o = o;
   a.part = (float*)ws;
-  a.tickets = c->tickets;
   a.chunk_bits = c->chunk_bits;
   a.zero_block = c->zero_block;
   return a;
@@ -557,7 +552,8 @@ sekv_status sekv_route(const sekv_cache* c, int32_t layer, const float* q_dev,
     return SEKV_OK;
   }
   const LayerArgs a = layer_args(c, layer, q_dev, proj_dev, tau_dev, out, nullptr, nullptr);
-  SEKV_HIP(launch_layer(c->bf16(), kRoute | kLists, c->geom, a, stream));
+  SEKV_HIP(launch_layer(c->bf16(), kRoute, c->geom, a, stream));
+  SEKV_HIP(launch_layer_tail(kLists, c->geom, a, stream));
   return SEKV_OK;
 }
 
@@ -574,7 +570,8 @@ static sekv_status attn_impl(const sekv_cache* c, int32_t layer, const float* q_
   const LayerArgs a = layer_args(c, layer, q_dev, nullptr, nullptr, route, o_dev, ws_dev);
   const int sc = c->sc;
   if (c->cfg.factor_tier == SEKV_TIER_DEVICE || sc == 0) {
-    SEKV_HIP(launch_layer(c->bf16(), kDense | kZoom | kMerge, c->geom, a, stream));
+    SEKV_HIP(launch_layer(c->bf16(), kDense | kZoom, c->geom, a, stream));
+    SEKV_HIP(launch_layer_tail(kMerge, c->geom, a, stream));
     return SEKV_OK;
   }
   // host tier: the zoomed spans' factors are gathered into device staging on
@@ -610,7 +607,8 @@ static sekv_status attn_impl(const sekv_cache* c, int32_t layer, const float* q_
   if (fst != stream) SEKV_HIP(hipEventRecord(c->ev_fetch, fst));
   SEKV_HIP(launch_layer(c->bf16(), kDense, c->geom, a, stream));
   if (fst != stream) SEKV_HIP(hipStreamWaitEvent(stream, c->ev_fetch, 0));
-  SEKV_HIP(launch_layer(c->bf16(), kZoom | kZoomSplit | kMerge, c->geom, az, stream));
+  SEKV_HIP(launch_layer(c->bf16(), kZoom | kZoomSplit, c->geom, az, stream));
+  SEKV_HIP(launch_layer_tail(kZoomSplit | kMerge, c->geom, az, stream));
   return SEKV_OK;
 }
 
@@ -650,7 +648,8 @@ sekv_status sekv_route_attn(const sekv_cache* c, int32_t layer, const float* q_d
     return attn_impl(c, layer, q_dev, route, o_dev, ws_dev, stream, fetch_stream);
   }
   const LayerArgs a = layer_args(c, layer, q_dev, proj_dev, tau_dev, route, o_dev, ws_dev);
-  SEKV_HIP(launch_layer(c->bf16(), kRoute | kDense | kZoom | kMerge | kLists, c->geom, a, stream));
+  SEKV_HIP(launch_layer(c->bf16(), kRoute | kDense | kZoom, c->geom, a, stream));
+  SEKV_HIP(launch_layer_tail(kMerge | kLists, c->geom, a, stream));
   return SEKV_OK;
 }
 
@@ -878,9 +877,10 @@ static sekv_status batch_impl(const sekv_cache* const* caches, int32_t batch, in
     ++nb;
   }
   if (nb > 0) {
-    const int mode = with_route ? (kRoute | kDense | kZoom | kMerge | kLists)
-                                : (kDense | kZoom | kMerge);
+    const int mode = with_route ? (kRoute | kDense | kZoom) : (kDense | kZoom);
+    const int tail = with_route ? (kMerge | kLists) : kMerge;
     SEKV_HIP(launch_layer_batch(caches[0]->bf16(), mode, caches[0]->geom.group, b, nb, stream));
+    SEKV_HIP(launch_layer_tail_batch(tail, caches[0]->geom.group, b, nb, stream));
   }
   return SEKV_OK;
 }

@@ -1,6 +1,6 @@
-// Decode-step kernel of the SeKV cache (gfx950): one launch per layer routes
-// every compressed span, attends over the four sources of the mixed-resolution
-// memory and merges the partial softmax states.
+// Decode-step kernels of the SeKV cache (gfx950): one launch per layer routes
+// every compressed span and attends over the four sources of the mixed-
+// resolution memory; a small second launch merges the partial softmax states.
 //
 // SeKV paper Sec. 3.2 (query projected into the routing space; independent
 // sigmoid gate with a gamma ln n size prior) and Sec. 3.3 (Eq. 9 zoom decision
@@ -18,10 +18,13 @@
 //       b_h = sigma_K * (V_K^T q_h) / sqrt(d);  e_{h,t} = U_K[t] . b_h;
 //       c_h = U_V^T p_h;  acc_h += V_V^T (sigma_V * c_h)
 //     so the factors are read once for all heads and no token row is formed.
-// Each workgroup writes one partial (m, l, acc) per head.  The last one of a
-// KV head to finish (an atomic ticket, reset by that workgroup) merges them
-// into o and writes the ascending zoom lists from per-chunk bit masks.  No
-// workgroup ever waits on another, and every launch leaves the tickets at zero.
+// Each workgroup writes one partial (m, l, acc) per head and its chunk's zoom
+// bit masks.  A second, small launch (one workgroup per KV head) merges the
+// partials into o and writes the ascending zoom lists from the bit masks: the
+// kernel boundary between the two makes every workgroup's stores visible, so
+// no workgroup waits on another and no agent-scope fence (an L2 write-back or
+// invalidation, which stalls the other KV heads' workgroups still streaming
+// factors through that L2) sits inside the layer kernel.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -160,8 +163,8 @@ template <int G> constexpr int stage_rows() { return G <= 5 ? 32 : 24; }
 // a stage: SR rows of V_K, then 64 floats of sigma_K and 64 of sigma_V
 template <int SR> constexpr int stage_floats() { return SR * kHeadDim + 128; }
 
-// The last workgroup's merge: thread = (head, 4 dims, stripe of slots); the
-// stripes are combined through LDS.
+// The tail's merge: thread = (head, 4 dims, stripe of slots); the stripes are
+// combined through LDS.
 template <int G> constexpr int merge_quads() { return G * (kHeadDim / 4); }
 template <int G> constexpr int merge_stripes() {
   return (kThreads / merge_quads<G>()) > 0 ? (kThreads / merge_quads<G>()) : 1;
@@ -179,15 +182,12 @@ struct alignas(16) Smem {
   int bits[kChunk];                // heads of the group that zoom span j0 + i
   int zl[kChunk];                  // chunk-local ids of zoomed spans
   int nz;
-  int last;
-  int wc[kListWords][kWaves];      // list compaction: per-wave counts
   union {
     struct {                       // routing (dead once the gates are taken)
       float qu[G][kHeadDim];       // query as given
       double qt[G][kMaxRouteDim];  // P_h q_h
     } rt;
     WaveScratch<G> w[kWaves];      // written from the rows phase on
-    MergeScratch<G> mg;            // the last workgroup's merge (the wave states are dead)
   };
 };
 // Per wave: V_K of its next zoomed span, written by LDS DMA while the current
@@ -932,6 +932,183 @@ static_assert(smem_fits<1>() && smem_fits<2>() && smem_fits<3>() && smem_fits<4>
               "LDS layout of the layer kernel");
 static_assert(kChunk <= 64, "a chunk's zoom sets are one wave ballot");
 
+// The merge of a KV head's partial softmax states into o, and its ascending
+// zoom lists and union, by the KV head's workgroup of the tail launch.
+template <int G>
+__device__ __attribute__((always_inline)) void layer_tail(const LayerGeom& geo, const LayerArgs& a,
+                                                          int mode, int g, int (*wc)[kWaves],
+                                                          MergeScratch<G>& mg) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int W = geo.n_work, sc = geo.n_compressed, h0 = g * G;
+  // The lists' chunk masks (first kThreads chunks) and the merge's slots are
+  // all requested before either is used: one round trip for both.
+  const int nc = geo.n_chunks;
+  uint32_t word0[kListWords];
+#pragma unroll
+  for (int li = 0; li < kListWords; ++li)
+    word0[li] = ((mode & kLists) && li <= G && tid < nc)
+                    ? a.chunk_bits[((size_t)g * W + tid) * kListWords + li]
+                    : 0u;
+
+  // Merge: thread = (head, 4 dims, stripe of slots), an online pass over its
+  // slots, B slots' loads in flight at a time (all of them up to B * STRIPES
+  // slots); stripes are combined through LDS.  The lists are built while the
+  // first batch of slot loads is in flight.
+  const bool merge = (mode & kMerge) != 0;
+  const int ns = (mode & kZoomSplit) ? 2 * W : W;
+  const float* pg = a.part + (size_t)g * geo.n_slots() * G * kPartStride;
+  constexpr int QUADS = merge_quads<G>();
+  constexpr int STRIPES = merge_stripes<G>();
+  constexpr int B = 24;
+  const int quad = tid % QUADS, stripe = tid / QUADS;
+  const int hl = quad / (kHeadDim / 4), dq = quad % (kHeadDim / 4);
+  const bool active = merge && stripe < STRIPES;
+  float M = -INFINITY, Ls = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float m[B], l[B];
+  float4 x[B];
+  auto load_batch = [&](int sl0) {
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const float* p = pg + ((size_t)min(sl0 + u * STRIPES, ns - 1) * G + hl) * kPartStride;
+      const float2 ml = *(const float2*)p;
+      m[u] = ml.x;
+      l[u] = ml.y;
+      x[u] = *(const float4*)(p + 4 + 4 * dq);
+    }
+  };
+  auto add_batch = [&](int sl0) {
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (sl0 + u * STRIPES >= ns) m[u] = -INFINITY;   // a clamped duplicate: weight 0
+    float bm = m[0];
+#pragma unroll
+    for (int u = 1; u < B; ++u) bm = fmaxf(bm, m[u]);
+    if (bm == -INFINITY) return;
+    const float Mn = fmaxf(M, bm);
+    const float wo = (M == -INFINITY) ? 0.f : __expf(M - Mn);
+    acc.x *= wo;
+    acc.y *= wo;
+    acc.z *= wo;
+    acc.w *= wo;
+    Ls *= wo;
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const float wt = (m[u] == -INFINITY) ? 0.f : __expf(m[u] - Mn);
+      acc.x += wt * x[u].x;
+      acc.y += wt * x[u].y;
+      acc.z += wt * x[u].z;
+      acc.w += wt * x[u].w;
+      Ls += wt * l[u];
+    }
+    M = Mn;
+  };
+  // Ascending per-head lists and the group union, from the chunks' zoom bit
+  // masks: a block scan of the popcounts, and each thread writes its chunk's
+  // ids.  The first pass (chunks 0 .. kThreads - 1) uses the masks loaded up
+  // front.
+  auto list_pass = [&](int c, const uint32_t (&word)[kListWords], int (&base)[kListWords]) {
+    int incl[kListWords];
+#pragma unroll
+    for (int li = 0; li <= G; ++li) {
+      incl[li] = wave_incl_scan(__popc(word[li]));
+      if (lane == 63) wc[li][wid] = incl[li];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int li = 0; li <= G; ++li) {
+      int off = base[li], tot = 0;
+#pragma unroll
+      for (int wv = 0; wv < kWaves; ++wv) {
+        off += (wv < wid) ? wc[li][wv] : 0;
+        tot += wc[li][wv];
+      }
+      off += incl[li] - __popc(word[li]);
+      int32_t* dst = li < G ? a.list + (size_t)(h0 + li) * sc : a.ulist + (size_t)g * sc;
+      uint32_t bits = word[li];
+      while (bits) {
+        const int bb = __ffs(bits) - 1;
+        bits &= bits - 1;
+        dst[off++] = c * kChunk + bb;
+      }
+      base[li] += tot;
+    }
+    __syncthreads();
+  };
+  auto lists_all = [&]() {
+    int base[kListWords];
+#pragma unroll
+    for (int li = 0; li < kListWords; ++li) base[li] = 0;
+    list_pass(tid, word0, base);
+    for (int c0 = kThreads; c0 < nc; c0 += kThreads) {
+      const int c = c0 + tid;
+      uint32_t word[kListWords];
+#pragma unroll
+      for (int li = 0; li < kListWords; ++li)
+        word[li] = (li <= G && c < nc) ? a.chunk_bits[((size_t)g * W + c) * kListWords + li] : 0u;
+      list_pass(c, word, base);
+    }
+    if (tid <= G) {
+      int v = 0;
+#pragma unroll
+      for (int li = 0; li <= G; ++li)
+        if (li == tid) v = base[li];
+      if (tid < G) a.count[h0 + tid] = v;
+      else a.ucount[g] = v;
+    }
+  };
+  if (merge) {
+    // every thread issues the first batch (spare threads a copy of stripe
+    // STRIPES - 1's), so the loads are unconditional and the lists' wait for
+    // their masks counts past them
+    load_batch(min(stripe, STRIPES - 1));
+    if (mode & kLists) lists_all();
+    if (active) {
+      add_batch(stripe);
+      for (int sl0 = stripe + B * STRIPES; sl0 < ns; sl0 += B * STRIPES) {
+        load_batch(sl0);
+        add_batch(sl0);
+      }
+    }
+    // the wave states are dead: the merge scratch overlays them
+    float4* red = mg.red;
+    float* red_m = mg.m;
+    float* red_l = mg.l;
+    if (stripe < STRIPES) {
+      red[stripe * QUADS + quad] = acc;
+      if (dq == 0) {
+        red_m[stripe * G + hl] = M;
+        red_l[stripe * G + hl] = Ls;
+      }
+    }
+    __syncthreads();
+    if (tid < QUADS) {
+      float Mx = -INFINITY;
+      for (int st = 0; st < STRIPES; ++st) Mx = fmaxf(Mx, red_m[st * G + hl]);
+      float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+      float L = 0.f;
+      if (Mx != -INFINITY) {
+        for (int st = 0; st < STRIPES; ++st) {
+          const float ms_ = red_m[st * G + hl];
+          if (ms_ == -INFINITY) continue;
+          const float wt = __expf(ms_ - Mx);
+          const float4 y = red[st * QUADS + tid];
+          t.x += wt * y.x;
+          t.y += wt * y.y;
+          t.z += wt * y.z;
+          t.w += wt * y.w;
+          L += wt * red_l[st * G + hl];
+        }
+      }
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      *(float4*)(a.o + (size_t)(h0 + hl) * kHeadDim + 4 * dq) =
+          make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+    }
+  } else if (mode & kLists) {
+    lists_all();
+  }
+}
+
 // One layer of one sequence: workgroup `block` of its Hkv x n_work grid.
 template <typename T, int G>
 __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
@@ -1259,190 +1436,6 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
     }
   }
 
-  // ---- the last workgroup of this KV head ----------------------------------
-  if (!(mode & (kMerge | kLists))) return;
-  // every wave waits until its stores have reached the L2; then one agent-
-  // scope release (an L2 write-back) publishes them all before the ticket
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const unsigned prev =
-        __hip_atomic_fetch_add(&a.tickets[g], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s.last = prev == (unsigned)(W - 1);
-  }
-  __syncthreads();
-  if (!s.last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-
-  // The lists' chunk masks (first kThreads chunks) and the merge's slots are
-  // all requested before either is used: one round trip for both.
-  const int nc = geo.n_chunks;
-  uint32_t word0[kListWords];
-#pragma unroll
-  for (int li = 0; li < kListWords; ++li)
-    word0[li] = ((mode & kLists) && li <= G && tid < nc)
-                    ? a.chunk_bits[((size_t)g * W + tid) * kListWords + li]
-                    : 0u;
-
-  // Merge: thread = (head, 4 dims, stripe of slots), an online pass over its
-  // slots, B slots' loads in flight at a time (all of them up to B * STRIPES
-  // slots); stripes are combined through LDS.  The lists are built while the
-  // first batch of slot loads is in flight.
-  const bool merge = (mode & kMerge) != 0;
-  const int ns = (mode & kZoomSplit) ? 2 * W : W;
-  const float* pg = a.part + (size_t)g * geo.n_slots() * G * kPartStride;
-  constexpr int QUADS = merge_quads<G>();
-  constexpr int STRIPES = merge_stripes<G>();
-  constexpr int B = 24;
-  const int quad = tid % QUADS, stripe = tid / QUADS;
-  const int hl = quad / (kHeadDim / 4), dq = quad % (kHeadDim / 4);
-  const bool active = merge && stripe < STRIPES;
-  float M = -INFINITY, Ls = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float m[B], l[B];
-  float4 x[B];
-  auto load_batch = [&](int sl0) {
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const float* p = pg + ((size_t)min(sl0 + u * STRIPES, ns - 1) * G + hl) * kPartStride;
-      const float2 ml = *(const float2*)p;
-      m[u] = ml.x;
-      l[u] = ml.y;
-      x[u] = *(const float4*)(p + 4 + 4 * dq);
-    }
-  };
-  auto add_batch = [&](int sl0) {
-#pragma unroll
-    for (int u = 0; u < B; ++u)
-      if (sl0 + u * STRIPES >= ns) m[u] = -INFINITY;   // a clamped duplicate: weight 0
-    float bm = m[0];
-#pragma unroll
-    for (int u = 1; u < B; ++u) bm = fmaxf(bm, m[u]);
-    if (bm == -INFINITY) return;
-    const float Mn = fmaxf(M, bm);
-    const float wo = (M == -INFINITY) ? 0.f : __expf(M - Mn);
-    acc.x *= wo;
-    acc.y *= wo;
-    acc.z *= wo;
-    acc.w *= wo;
-    Ls *= wo;
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const float wt = (m[u] == -INFINITY) ? 0.f : __expf(m[u] - Mn);
-      acc.x += wt * x[u].x;
-      acc.y += wt * x[u].y;
-      acc.z += wt * x[u].z;
-      acc.w += wt * x[u].w;
-      Ls += wt * l[u];
-    }
-    M = Mn;
-  };
-  // Ascending per-head lists and the group union, from the chunks' zoom bit
-  // masks: a block scan of the popcounts, and each thread writes its chunk's
-  // ids.  The first pass (chunks 0 .. kThreads - 1) uses the masks loaded up
-  // front.
-  auto list_pass = [&](int c, const uint32_t (&word)[kListWords], int (&base)[kListWords]) {
-    int incl[kListWords];
-#pragma unroll
-    for (int li = 0; li <= G; ++li) {
-      incl[li] = wave_incl_scan(__popc(word[li]));
-      if (lane == 63) s.wc[li][wid] = incl[li];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int li = 0; li <= G; ++li) {
-      int off = base[li], tot = 0;
-#pragma unroll
-      for (int wv = 0; wv < kWaves; ++wv) {
-        off += (wv < wid) ? s.wc[li][wv] : 0;
-        tot += s.wc[li][wv];
-      }
-      off += incl[li] - __popc(word[li]);
-      int32_t* dst = li < G ? a.list + (size_t)(h0 + li) * sc : a.ulist + (size_t)g * sc;
-      uint32_t bits = word[li];
-      while (bits) {
-        const int bb = __ffs(bits) - 1;
-        bits &= bits - 1;
-        dst[off++] = c * kChunk + bb;
-      }
-      base[li] += tot;
-    }
-    __syncthreads();
-  };
-  auto lists_all = [&]() {
-    int base[kListWords];
-#pragma unroll
-    for (int li = 0; li < kListWords; ++li) base[li] = 0;
-    list_pass(tid, word0, base);
-    for (int c0 = kThreads; c0 < nc; c0 += kThreads) {
-      const int c = c0 + tid;
-      uint32_t word[kListWords];
-#pragma unroll
-      for (int li = 0; li < kListWords; ++li)
-        word[li] = (li <= G && c < nc) ? a.chunk_bits[((size_t)g * W + c) * kListWords + li] : 0u;
-      list_pass(c, word, base);
-    }
-    if (tid <= G) {
-      int v = 0;
-#pragma unroll
-      for (int li = 0; li <= G; ++li)
-        if (li == tid) v = base[li];
-      if (tid < G) a.count[h0 + tid] = v;
-      else a.ucount[g] = v;
-    }
-  };
-  if (merge) {
-    // every thread issues the first batch (spare threads a copy of stripe
-    // STRIPES - 1's), so the loads are unconditional and the lists' wait for
-    // their masks counts past them
-    load_batch(min(stripe, STRIPES - 1));
-    if (mode & kLists) lists_all();
-    if (active) {
-      add_batch(stripe);
-      for (int sl0 = stripe + B * STRIPES; sl0 < ns; sl0 += B * STRIPES) {
-        load_batch(sl0);
-        add_batch(sl0);
-      }
-    }
-    // the wave states are dead: the merge scratch overlays them
-    float4* red = s.mg.red;
-    float* red_m = s.mg.m;
-    float* red_l = s.mg.l;
-    if (stripe < STRIPES) {
-      red[stripe * QUADS + quad] = acc;
-      if (dq == 0) {
-        red_m[stripe * G + hl] = M;
-        red_l[stripe * G + hl] = Ls;
-      }
-    }
-    __syncthreads();
-    if (tid < QUADS) {
-      float Mx = -INFINITY;
-      for (int st = 0; st < STRIPES; ++st) Mx = fmaxf(Mx, red_m[st * G + hl]);
-      float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-      float L = 0.f;
-      if (Mx != -INFINITY) {
-        for (int st = 0; st < STRIPES; ++st) {
-          const float ms_ = red_m[st * G + hl];
-          if (ms_ == -INFINITY) continue;
-          const float wt = __expf(ms_ - Mx);
-          const float4 y = red[st * QUADS + tid];
-          t.x += wt * y.x;
-          t.y += wt * y.y;
-          t.z += wt * y.z;
-          t.w += wt * y.w;
-          L += wt * red_l[st * G + hl];
-        }
-      }
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-      *(float4*)(a.o + (size_t)(h0 + hl) * kHeadDim + 4 * dq) =
-          make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
-    }
-  } else if (mode & kLists) {
-    lists_all();
-  }
-  if (tid == 0) __hip_atomic_store(&a.tickets[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T, int G>
@@ -1459,6 +1452,61 @@ void layer_batch_kernel(BatchLayerArgs b, int mode) {
   const int i = blockIdx.y;
   if ((int)blockIdx.x >= b.geo[i].n_kv_heads * b.geo[i].n_work) return;
   layer_body<T, G>(b.geo[i], b.arg[i], mode, blockIdx.x);
+}
+
+// The merge and lists of one layer in a launch of their own, one workgroup
+// per KV head (grid.y: the sequence of a batch).  The layer launch before it
+// wrote the partial states and chunk masks; the kernel boundary makes them
+// visible here, so the layer kernel needs no ticket and no agent-scope fence.
+template <int G>
+__global__ __launch_bounds__(kThreads) void layer_tail_kernel(LayerGeom geo, LayerArgs a,
+                                                              int mode) {
+  __shared__ int wc[kListWords][kWaves];
+  __shared__ MergeScratch<G> mg;
+  layer_tail<G>(geo, a, mode, blockIdx.x, wc, mg);
+}
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void layer_tail_batch_kernel(BatchLayerArgs b, int mode) {
+  __shared__ int wc[kListWords][kWaves];
+  __shared__ MergeScratch<G> mg;
+  const int i = blockIdx.y;
+  if ((int)blockIdx.x >= b.geo[i].n_kv_heads) return;
+  layer_tail<G>(b.geo[i], b.arg[i], mode, blockIdx.x, wc, mg);
+}
+
+hipError_t launch_layer_tail(int mode, const LayerGeom& g, const LayerArgs& a, hipStream_t st) {
+  const dim3 grid(g.n_kv_heads);
+#define SEKV_TAIL(GG)                                                                          \
+  case GG:                                                                                     \
+    hipLaunchKernelGGL((layer_tail_kernel<GG>), grid, dim3(kThreads), 0, st, g, a, mode);     \
+    break;
+  switch (g.group) {
+    SEKV_TAIL(1) SEKV_TAIL(2) SEKV_TAIL(3) SEKV_TAIL(4) SEKV_TAIL(5) SEKV_TAIL(6) SEKV_TAIL(7)
+    SEKV_TAIL(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef SEKV_TAIL
+  return hipGetLastError();
+}
+
+hipError_t launch_layer_tail_batch(int mode, int group, const BatchLayerArgs& b, int batch,
+                                   hipStream_t st) {
+  if (batch < 1 || batch > kMaxBatch) return hipErrorInvalidValue;
+  int nx = 0;
+  for (int i = 0; i < batch; ++i) nx = max(nx, b.geo[i].n_kv_heads);
+  const dim3 grid(nx, batch);
+#define SEKV_TAIL(GG)                                                                          \
+  case GG:                                                                                     \
+    hipLaunchKernelGGL((layer_tail_batch_kernel<GG>), grid, dim3(kThreads), 0, st, b, mode);  \
+    break;
+  switch (group) {
+    SEKV_TAIL(1) SEKV_TAIL(2) SEKV_TAIL(3) SEKV_TAIL(4) SEKV_TAIL(5) SEKV_TAIL(6) SEKV_TAIL(7)
+    SEKV_TAIL(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef SEKV_TAIL
+  return hipGetLastError();
 }
 
 hipError_t launch_layer_batch(int bf16, int mode, int group, const BatchLayerArgs& b, int batch,

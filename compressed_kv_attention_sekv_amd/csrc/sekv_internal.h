@@ -152,8 +152,8 @@ enum LayerMode : int {
   kDense = 2,      // attend the workgroup's full-resolution rows and coarse entries
   kZoom = 4,       // attend the chunk's zoomed spans from their factors
   kZoomSplit = 8,  // zoomed-span partials go to their own slots (separate launch)
-  kMerge = 16,     // the last workgroup of a KV head merges the partials into o
-  kLists = 32,     // the last workgroup of a KV head writes the ascending zoom lists
+  kMerge = 16,     // tail launch: merge a KV head's partials into o
+  kLists = 32,     // tail launch: write the ascending zoom lists and union
 };
 
 struct LayerArgs {
@@ -181,7 +181,6 @@ struct LayerArgs {
   int32_t* ucount;         // [Hkv]
   float* o;                // [Hq][d]
   float* part;             // workspace
-  uint32_t* tickets;       // [Hkv], zero between launches
   uint32_t* chunk_bits;    // [Hkv][n_work][kListWords] zoom bit masks of each chunk
   const float* zero_block; // kZeroBlockFloats zeros
 };
@@ -230,6 +229,11 @@ hipError_t launch_layer(int bf16, int mode, const LayerGeom& g, const LayerArgs&
                         hipStream_t st);
 hipError_t launch_layer_batch(int bf16, int mode, int group, const BatchLayerArgs& b, int batch,
                               hipStream_t st);
+// the merge and lists of a layer (kMerge, kLists, kZoomSplit bits of mode) in a
+// launch of their own, after a layer launch without those bits
+hipError_t launch_layer_tail(int mode, const LayerGeom& g, const LayerArgs& a, hipStream_t st);
+hipError_t launch_layer_tail_batch(int mode, int group, const BatchLayerArgs& b, int batch,
+                                   hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st);
 // matched-budget cap of one layer's route output (in place); the kernel keeps
 // one bit per union entry in LDS, so S_c is limited to kCapMaxSpans

@@ -22,8 +22,9 @@
  *     failing call leaves a message for sekv_last_error() on the calling
  *     thread, and a failing build leaves *out == NULL.
  *   - A cache may be used by one host thread and one stream order at a time
- *     (its decode calls share per-cache counters that each launch leaves at
- *     zero); distinct caches are independent.
+ *     (its decode calls share per-cache scratch: the chunk zoom masks the
+ *     layer launch writes and its tail launch reads); distinct caches are
+ *     independent.
  *   - Layouts are row-major C arrays; [a][b] means b varies fastest.
  *     L = n_layers, Hq = n_q_heads, Hkv = n_kv_heads, G = Hq / Hkv (query
  *     heads per KV head; query head h reads KV head h / G), d = head_dim,
@@ -283,7 +284,7 @@ sekv_status sekv_residency_stats(const sekv_cache* cache, uint64_t out[6], int32
  * per-sequence computation of sekv_route_attn / sekv_decode_attn; batch-4
  * serving).  The caches must share n_layers, n_q_heads, n_kv_heads,
  * head_dim, route_dim and kv_dtype, and must be distinct (each holds its own
- * completion counters); their context lengths may differ.  For sequence i the
+ * chunk zoom masks); their context lengths may differ.  For sequence i the
  * arguments are those of the single-sequence call: q_devs[i], routes[i],
  * o_devs[i], and ws_devs[i] with ws_bytes[i] bytes (at least
  * sekv_decode_workspace_bytes(caches[i])).  proj_dev and tau_dev are one
