@@ -1454,16 +1454,24 @@ void layer_batch_kernel(BatchLayerArgs b, int mode) {
   layer_body<T, G>(b.geo[i], b.arg[i], mode, blockIdx.x);
 }
 
-// The merge and lists of one layer in a launch of their own, one workgroup
-// per KV head (grid.y: the sequence of a batch).  The layer launch before it
-// wrote the partial states and chunk masks; the kernel boundary makes them
-// visible here, so the layer kernel needs no ticket and no agent-scope fence.
+// The merge and lists of one layer in a launch of their own: per KV head one
+// workgroup merges and another writes the lists, on different CUs (grid.x =
+// 2 Hkv; grid.y: the sequence of a batch).  The layer launch before it wrote
+// the partial states and chunk masks; the kernel boundary makes them visible
+// here, so the layer kernel needs no ticket and no agent-scope fence.
+__device__ __forceinline__ int tail_role_mode(int mode, int role) {
+  return role == 0 ? (mode & (kMerge | kZoomSplit)) : (mode & kLists);
+}
+
 template <int G>
 __global__ __launch_bounds__(kThreads) void layer_tail_kernel(LayerGeom geo, LayerArgs a,
                                                               int mode) {
   __shared__ int wc[kListWords][kWaves];
   __shared__ MergeScratch<G> mg;
-  layer_tail<G>(geo, a, mode, blockIdx.x, wc, mg);
+  const int hkv = geo.n_kv_heads;
+  const int m = tail_role_mode(mode, blockIdx.x / hkv);
+  if (!(m & (kMerge | kLists))) return;
+  layer_tail<G>(geo, a, m, blockIdx.x % hkv, wc, mg);
 }
 
 template <int G>
@@ -1471,12 +1479,15 @@ __global__ __launch_bounds__(kThreads) void layer_tail_batch_kernel(BatchLayerAr
   __shared__ int wc[kListWords][kWaves];
   __shared__ MergeScratch<G> mg;
   const int i = blockIdx.y;
-  if ((int)blockIdx.x >= b.geo[i].n_kv_heads) return;
-  layer_tail<G>(b.geo[i], b.arg[i], mode, blockIdx.x, wc, mg);
+  const int hkv = b.geo[i].n_kv_heads;
+  if ((int)blockIdx.x >= 2 * hkv) return;
+  const int m = tail_role_mode(mode, blockIdx.x / hkv);
+  if (!(m & (kMerge | kLists))) return;
+  layer_tail<G>(b.geo[i], b.arg[i], m, blockIdx.x % hkv, wc, mg);
 }
 
 hipError_t launch_layer_tail(int mode, const LayerGeom& g, const LayerArgs& a, hipStream_t st) {
-  const dim3 grid(g.n_kv_heads);
+  const dim3 grid(2 * g.n_kv_heads);
 #define SEKV_TAIL(GG)                                                                          \
   case GG:                                                                                     \
     hipLaunchKernelGGL((layer_tail_kernel<GG>), grid, dim3(kThreads), 0, st, g, a, mode);     \
@@ -1494,7 +1505,7 @@ hipError_t launch_layer_tail_batch(int mode, int group, const BatchLayerArgs& b,
                                    hipStream_t st) {
   if (batch < 1 || batch > kMaxBatch) return hipErrorInvalidValue;
   int nx = 0;
-  for (int i = 0; i < batch; ++i) nx = max(nx, b.geo[i].n_kv_heads);
+  for (int i = 0; i < batch; ++i) nx = max(nx, 2 * b.geo[i].n_kv_heads);
   const dim3 grid(nx, batch);
 #define SEKV_TAIL(GG)                                                                          \
   case GG:                                                                                     \
