@@ -8,9 +8,9 @@ bf16 K/V, spans of ~80 tokens, rank cap 32, window 512, 10% of heads zoom ~20%
 of spans and the rest ~1%), resident in HBM before timing starts.
 
 Prints ONE JSON line.  ``value`` is decode steps/s of the whole job.
-``roofline`` covers the layer kernel (one launch per layer routes and attends;
-it is the step's only kernel): algorithmic bytes per launch / average launch
-time from HIP events recorded on the launch stream.  ``cpu_baseline`` times the
+``roofline`` covers a layer, the step's only work: the layer kernel (route and
+attention) and its tail launch (merge and lists); algorithmic bytes per layer /
+average layer time from HIP events recorded on the launch stream.  ``cpu_baseline`` times the
 CPU oracle on a bounded sample.
 """
 from __future__ import annotations
@@ -49,7 +49,8 @@ def parse():
     ap.add_argument("--n-tokens", type=int, default=None, help="override context (testing)")
     ap.add_argument("--batch", type=int, default=None,
                     help="sequences per step (default: the workload's); above 1 each layer runs "
-                         "through the batched call, one launch for all sequences")
+                         "through the batched calls, one layer launch and one tail launch for "
+                         "all sequences")
     ap.add_argument("--budget", type=int, default=None,
                     help="matched-budget cap in tokens per KV head and layer: each layer runs "
                          "sekv_route (gate values kept), sekv_cap_budget, sekv_decode_attn")

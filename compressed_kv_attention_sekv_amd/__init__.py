@@ -342,7 +342,7 @@ def sekv_decode_attn(cache: Cache, layer: int, q: torch.Tensor, route: RouteBuff
 def sekv_route_attn(cache: Cache, layer: int, q: torch.Tensor, proj: torch.Tensor,
                     tau: torch.Tensor, route: RouteBuffers, o: torch.Tensor,
                     workspace: torch.Tensor, stream=None, fetch_stream=None) -> None:
-    """Route and attend one layer in one call (one launch with device-tier factors)."""
+    """Route and attend one layer in one call (two launches with device-tier factors)."""
     _need(q, "q", torch.float32)
     _need(proj, "proj", torch.float32)
     _need(tau, "tau", torch.float32)
@@ -408,7 +408,8 @@ def sekv_route_attn_batch(caches: Sequence[Cache], layer: int, qs: Sequence[torc
                           proj: torch.Tensor, tau: torch.Tensor, routes: Sequence[RouteBuffers],
                           os_: Sequence[torch.Tensor], workspaces: Sequence[torch.Tensor],
                           stream=None) -> None:
-    """Route and attend one layer of several sequences (one cache each) in one launch."""
+    """Route and attend one layer of several sequences (one cache each): one layer launch
+    and one tail launch for all of them."""
     _need(proj, "proj", torch.float32)
     _need(tau, "tau", torch.float32)
     cs, qp, rs, op, wp, wb = _batch_arrays(caches, qs, routes, os_, workspaces)
@@ -419,7 +420,8 @@ def sekv_route_attn_batch(caches: Sequence[Cache], layer: int, qs: Sequence[torc
 def sekv_decode_attn_batch(caches: Sequence[Cache], layer: int, qs: Sequence[torch.Tensor],
                            routes: Sequence[RouteBuffers], os_: Sequence[torch.Tensor],
                            workspaces: Sequence[torch.Tensor], stream=None) -> None:
-    """Attend one layer of several sequences (routes given) in one launch."""
+    """Attend one layer of several sequences (routes given): one layer launch and one
+    tail launch."""
     cs, qp, rs, op, wp, wb = _batch_arrays(caches, qs, routes, os_, workspaces)
     _check(lib().sekv_decode_attn_batch(cs, len(caches), layer, qp, rs, op, wp, wb,
                                         _stream(stream)))

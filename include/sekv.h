@@ -197,9 +197,10 @@ sekv_status sekv_decode_attn(const sekv_cache* cache, int32_t layer, const float
  * Eq. 9 and the mixed-resolution softmax): the result is the same as
  * sekv_route followed by sekv_decode_attn with the same arguments, and `route`
  * receives the same mask, lists and counts (and prob, if non-NULL).  With
- * device-tier factors the whole layer is one kernel launch on `stream`; with
- * host-tier factors it runs as sekv_route then sekv_decode_attn (fetch on
- * `fetch_stream`).  Arguments as for those two calls. */
+ * device-tier factors the layer is two kernel launches on `stream` (route and
+ * attention in one pass, then the merge and lists); with host-tier factors it
+ * runs as sekv_route then sekv_decode_attn (fetch on `fetch_stream`).
+ * Arguments as for those two calls. */
 sekv_status sekv_route_attn(const sekv_cache* cache, int32_t layer, const float* q_dev,
                             const float* proj_dev, const float* tau_dev,
                             const sekv_route_out* route, float* o_dev, void* ws_dev,
@@ -280,8 +281,9 @@ sekv_status sekv_set_residency(sekv_cache* cache, uint64_t capacity_bytes, uint6
 sekv_status sekv_residency_stats(const sekv_cache* cache, uint64_t out[6], int32_t reset);
 
 /* Batched decode: the same layer of `batch` independent sequences
- * (1 <= batch <= SEKV_MAX_BATCH), one cache each, in one kernel launch (the
- * per-sequence computation of sekv_route_attn / sekv_decode_attn; batch-4
+ * (1 <= batch <= SEKV_MAX_BATCH), one cache each, in one layer launch and one
+ * tail launch (the per-sequence computation of sekv_route_attn /
+ * sekv_decode_attn; batch-4
  * serving).  The caches must share n_layers, n_q_heads, n_kv_heads,
  * head_dim, route_dim and kv_dtype, and must be distinct (each holds its own
  * chunk zoom masks); their context lengths may differ.  For sequence i the
