@@ -163,15 +163,13 @@ template <int G> constexpr int stage_rows() { return G <= 5 ? 32 : 24; }
 // a stage: SR rows of V_K, then 64 floats of sigma_K and 64 of sigma_V
 template <int SR> constexpr int stage_floats() { return SR * kHeadDim + 128; }
 
-// The tail's merge: thread = (head, 4 dims, stripe of slots); the stripes are
-// combined through LDS.
-template <int G> constexpr int merge_quads() { return G * (kHeadDim / 4); }
-template <int G> constexpr int merge_stripes() {
-  return (kThreads / merge_quads<G>()) > 0 ? (kThreads / merge_quads<G>()) : 1;
-}
-template <int G> struct MergeScratch {
-  float4 red[merge_stripes<G>() * merge_quads<G>()];   // each stripe's acc
-  float m[merge_stripes<G>() * G], l[merge_stripes<G>() * G];
+// The tail's merge, one workgroup per query head: thread = (4 dims, stripe of
+// slots); the stripes are combined through LDS.
+constexpr int kMergeQuads = kHeadDim / 4;
+constexpr int kMergeStripes = kThreads / kMergeQuads;
+struct MergeScratch {
+  float4 red[kMergeStripes * kMergeQuads];   // each stripe's acc
+  float m[kMergeStripes], l[kMergeStripes];
 };
 
 template <int G>
@@ -932,81 +930,14 @@ static_assert(smem_fits<1>() && smem_fits<2>() && smem_fits<3>() && smem_fits<4>
               "LDS layout of the layer kernel");
 static_assert(kChunk <= 64, "a chunk's zoom sets are one wave ballot");
 
-// The merge of a KV head's partial softmax states into o, and its ascending
-// zoom lists and union, by the KV head's workgroup of the tail launch.
+// The ascending zoom lists of a KV head's query heads and its union, from the
+// chunks' zoom bit masks: a block scan of the popcounts, and each thread
+// writes its chunk's ids.
 template <int G>
-__device__ __attribute__((always_inline)) void layer_tail(const LayerGeom& geo, const LayerArgs& a,
-                                                          int mode, int g, int (*wc)[kWaves],
-                                                          MergeScratch<G>& mg) {
+__device__ __attribute__((always_inline)) void tail_lists(const LayerGeom& geo, const LayerArgs& a,
+                                                          int g, int (*wc)[kWaves]) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int W = geo.n_work, sc = geo.n_compressed, h0 = g * G;
-  // The lists' chunk masks (first kThreads chunks) and the merge's slots are
-  // all requested before either is used: one round trip for both.
-  const int nc = geo.n_chunks;
-  uint32_t word0[kListWords];
-#pragma unroll
-  for (int li = 0; li < kListWords; ++li)
-    word0[li] = ((mode & kLists) && li <= G && tid < nc)
-                    ? a.chunk_bits[((size_t)g * W + tid) * kListWords + li]
-                    : 0u;
-
-  // Merge: thread = (head, 4 dims, stripe of slots), an online pass over its
-  // slots, B slots' loads in flight at a time (all of them up to B * STRIPES
-  // slots); stripes are combined through LDS.  The lists are built while the
-  // first batch of slot loads is in flight.
-  const bool merge = (mode & kMerge) != 0;
-  const int ns = (mode & kZoomSplit) ? 2 * W : W;
-  const float* pg = a.part + (size_t)g * geo.n_slots() * G * kPartStride;
-  constexpr int QUADS = merge_quads<G>();
-  constexpr int STRIPES = merge_stripes<G>();
-  constexpr int B = 24;
-  const int quad = tid % QUADS, stripe = tid / QUADS;
-  const int hl = quad / (kHeadDim / 4), dq = quad % (kHeadDim / 4);
-  const bool active = merge && stripe < STRIPES;
-  float M = -INFINITY, Ls = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float m[B], l[B];
-  float4 x[B];
-  auto load_batch = [&](int sl0) {
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const float* p = pg + ((size_t)min(sl0 + u * STRIPES, ns - 1) * G + hl) * kPartStride;
-      const float2 ml = *(const float2*)p;
-      m[u] = ml.x;
-      l[u] = ml.y;
-      x[u] = *(const float4*)(p + 4 + 4 * dq);
-    }
-  };
-  auto add_batch = [&](int sl0) {
-#pragma unroll
-    for (int u = 0; u < B; ++u)
-      if (sl0 + u * STRIPES >= ns) m[u] = -INFINITY;   // a clamped duplicate: weight 0
-    float bm = m[0];
-#pragma unroll
-    for (int u = 1; u < B; ++u) bm = fmaxf(bm, m[u]);
-    if (bm == -INFINITY) return;
-    const float Mn = fmaxf(M, bm);
-    const float wo = (M == -INFINITY) ? 0.f : __expf(M - Mn);
-    acc.x *= wo;
-    acc.y *= wo;
-    acc.z *= wo;
-    acc.w *= wo;
-    Ls *= wo;
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const float wt = (m[u] == -INFINITY) ? 0.f : __expf(m[u] - Mn);
-      acc.x += wt * x[u].x;
-      acc.y += wt * x[u].y;
-      acc.z += wt * x[u].z;
-      acc.w += wt * x[u].w;
-      Ls += wt * l[u];
-    }
-    M = Mn;
-  };
-  // Ascending per-head lists and the group union, from the chunks' zoom bit
-  // masks: a block scan of the popcounts, and each thread writes its chunk's
-  // ids.  The first pass (chunks 0 .. kThreads - 1) uses the masks loaded up
-  // front.
+  const int W = geo.n_work, sc = geo.n_compressed, h0 = g * G, nc = geo.n_chunks;
   auto list_pass = [&](int c, const uint32_t (&word)[kListWords], int (&base)[kListWords]) {
     int incl[kListWords];
 #pragma unroll
@@ -1035,77 +966,121 @@ __device__ __attribute__((always_inline)) void layer_tail(const LayerGeom& geo, 
     }
     __syncthreads();
   };
-  auto lists_all = [&]() {
-    int base[kListWords];
+  int base[kListWords];
 #pragma unroll
-    for (int li = 0; li < kListWords; ++li) base[li] = 0;
-    list_pass(tid, word0, base);
-    for (int c0 = kThreads; c0 < nc; c0 += kThreads) {
-      const int c = c0 + tid;
-      uint32_t word[kListWords];
+  for (int li = 0; li < kListWords; ++li) base[li] = 0;
+  for (int c0 = 0; c0 < nc; c0 += kThreads) {
+    const int c = c0 + tid;
+    uint32_t word[kListWords];
 #pragma unroll
-      for (int li = 0; li < kListWords; ++li)
-        word[li] = (li <= G && c < nc) ? a.chunk_bits[((size_t)g * W + c) * kListWords + li] : 0u;
-      list_pass(c, word, base);
-    }
-    if (tid <= G) {
-      int v = 0;
+    for (int li = 0; li < kListWords; ++li)
+      word[li] = (li <= G && c < nc) ? a.chunk_bits[((size_t)g * W + c) * kListWords + li] : 0u;
+    list_pass(c, word, base);
+  }
+  if (tid <= G) {
+    int v = 0;
 #pragma unroll
-      for (int li = 0; li <= G; ++li)
-        if (li == tid) v = base[li];
-      if (tid < G) a.count[h0 + tid] = v;
-      else a.ucount[g] = v;
-    }
-  };
-  if (merge) {
-    // every thread issues the first batch (spare threads a copy of stripe
-    // STRIPES - 1's), so the loads are unconditional and the lists' wait for
-    // their masks counts past them
-    load_batch(min(stripe, STRIPES - 1));
-    if (mode & kLists) lists_all();
-    if (active) {
-      add_batch(stripe);
-      for (int sl0 = stripe + B * STRIPES; sl0 < ns; sl0 += B * STRIPES) {
-        load_batch(sl0);
-        add_batch(sl0);
+    for (int li = 0; li <= G; ++li)
+      if (li == tid) v = base[li];
+    if (tid < G) a.count[h0 + tid] = v;
+    else a.ucount[g] = v;
+  }
+}
+
+// The merge of query head h's partial softmax states (one per slot) into o:
+// an online pass per thread over its stripe of slots, B slots' loads in
+// flight at a time, then the stripes combined by log-sum-exp through LDS.
+template <int G>
+__device__ __attribute__((always_inline)) void tail_merge(const LayerGeom& geo, const LayerArgs& a,
+                                                          int mode, int h, MergeScratch& mg) {
+  const int tid = threadIdx.x;
+  const int g = h / G, hl = h % G;
+  const int ns = (mode & kZoomSplit) ? geo.n_slots() : geo.n_work;
+  const float* pg = a.part + (size_t)g * geo.n_slots() * G * kPartStride;
+  constexpr int B = 16;
+  const int dq = tid % kMergeQuads, stripe = tid / kMergeQuads;
+  float M = -INFINITY, Ls = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sl0 = stripe; sl0 < ns; sl0 += B * kMergeStripes) {
+    float m[B], l[B];
+    float4 x[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int sl = sl0 + u * kMergeStripes;
+      m[u] = -INFINITY;
+      l[u] = 0.f;
+      x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (sl < ns) {
+        const float* p = pg + ((size_t)sl * G + hl) * kPartStride;
+        const float2 ml = *(const float2*)p;
+        m[u] = ml.x;
+        l[u] = ml.y;
+        x[u] = *(const float4*)(p + 4 + 4 * dq);
       }
     }
-    // the wave states are dead: the merge scratch overlays them
-    float4* red = mg.red;
-    float* red_m = mg.m;
-    float* red_l = mg.l;
-    if (stripe < STRIPES) {
-      red[stripe * QUADS + quad] = acc;
-      if (dq == 0) {
-        red_m[stripe * G + hl] = M;
-        red_l[stripe * G + hl] = Ls;
+    float bm = m[0];
+#pragma unroll
+    for (int u = 1; u < B; ++u) bm = fmaxf(bm, m[u]);
+    if (bm == -INFINITY) continue;
+    const float Mn = fmaxf(M, bm);
+    const float wo = (M == -INFINITY) ? 0.f : __expf(M - Mn);
+    acc.x *= wo;
+    acc.y *= wo;
+    acc.z *= wo;
+    acc.w *= wo;
+    Ls *= wo;
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const float wt = (m[u] == -INFINITY) ? 0.f : __expf(m[u] - Mn);
+      acc.x += wt * x[u].x;
+      acc.y += wt * x[u].y;
+      acc.z += wt * x[u].z;
+      acc.w += wt * x[u].w;
+      Ls += wt * l[u];
+    }
+    M = Mn;
+  }
+  mg.red[stripe * kMergeQuads + dq] = acc;
+  if (dq == 0) {
+    mg.m[stripe] = M;
+    mg.l[stripe] = Ls;
+  }
+  __syncthreads();
+  if (tid < kMergeQuads) {
+    float Mx = -INFINITY;
+    for (int st = 0; st < kMergeStripes; ++st) Mx = fmaxf(Mx, mg.m[st]);
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = 0.f;
+    if (Mx != -INFINITY) {
+      for (int st = 0; st < kMergeStripes; ++st) {
+        const float ms_ = mg.m[st];
+        if (ms_ == -INFINITY) continue;
+        const float wt = __expf(ms_ - Mx);
+        const float4 y = mg.red[st * kMergeQuads + tid];
+        t.x += wt * y.x;
+        t.y += wt * y.y;
+        t.z += wt * y.z;
+        t.w += wt * y.w;
+        L += wt * mg.l[st];
       }
     }
-    __syncthreads();
-    if (tid < QUADS) {
-      float Mx = -INFINITY;
-      for (int st = 0; st < STRIPES; ++st) Mx = fmaxf(Mx, red_m[st * G + hl]);
-      float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-      float L = 0.f;
-      if (Mx != -INFINITY) {
-        for (int st = 0; st < STRIPES; ++st) {
-          const float ms_ = red_m[st * G + hl];
-          if (ms_ == -INFINITY) continue;
-          const float wt = __expf(ms_ - Mx);
-          const float4 y = red[st * QUADS + tid];
-          t.x += wt * y.x;
-          t.y += wt * y.y;
-          t.z += wt * y.z;
-          t.w += wt * y.w;
-          L += wt * red_l[st * G + hl];
-        }
-      }
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-      *(float4*)(a.o + (size_t)(h0 + hl) * kHeadDim + 4 * dq) =
-          make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
-    }
-  } else if (mode & kLists) {
-    lists_all();
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    *(float4*)(a.o + (size_t)h * kHeadDim + 4 * dq) =
+        make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+  }
+}
+
+// One workgroup of a tail launch: x < Hq merges query head x, the others
+// write KV head x - Hq's lists.
+template <int G>
+__device__ __attribute__((always_inline)) void layer_tail(const LayerGeom& geo, const LayerArgs& a,
+                                                          int mode, int x, int (*wc)[kWaves],
+                                                          MergeScratch& mg) {
+  const int hq = geo.n_kv_heads * G;
+  if (x < hq) {
+    if (mode & kMerge) tail_merge<G>(geo, a, mode, x, mg);
+  } else if (x < hq + geo.n_kv_heads) {
+    if (mode & kLists) tail_lists<G>(geo, a, x - hq, wc);
   }
 }
 
@@ -1454,40 +1429,29 @@ void layer_batch_kernel(BatchLayerArgs b, int mode) {
   layer_body<T, G>(b.geo[i], b.arg[i], mode, blockIdx.x);
 }
 
-// The merge and lists of one layer in a launch of their own: per KV head one
-// workgroup merges and another writes the lists, on different CUs (grid.x =
-// 2 Hkv; grid.y: the sequence of a batch).  The layer launch before it wrote
-// the partial states and chunk masks; the kernel boundary makes them visible
-// here, so the layer kernel needs no ticket and no agent-scope fence.
-__device__ __forceinline__ int tail_role_mode(int mode, int role) {
-  return role == 0 ? (mode & (kMerge | kZoomSplit)) : (mode & kLists);
-}
-
+// The merge and lists of one layer in a launch of their own: one workgroup
+// per query head merges, one per KV head writes the lists (grid.x =
+// Hkv (G + 1); grid.y: the sequence of a batch).  The layer launch before it
+// wrote the partial states and chunk masks; the kernel boundary makes them
+// visible here, so the layer kernel needs no ticket and no agent-scope fence.
 template <int G>
 __global__ __launch_bounds__(kThreads) void layer_tail_kernel(LayerGeom geo, LayerArgs a,
                                                               int mode) {
   __shared__ int wc[kListWords][kWaves];
-  __shared__ MergeScratch<G> mg;
-  const int hkv = geo.n_kv_heads;
-  const int m = tail_role_mode(mode, blockIdx.x / hkv);
-  if (!(m & (kMerge | kLists))) return;
-  layer_tail<G>(geo, a, m, blockIdx.x % hkv, wc, mg);
+  __shared__ MergeScratch mg;
+  layer_tail<G>(geo, a, mode, blockIdx.x, wc, mg);
 }
 
 template <int G>
 __global__ __launch_bounds__(kThreads) void layer_tail_batch_kernel(BatchLayerArgs b, int mode) {
   __shared__ int wc[kListWords][kWaves];
-  __shared__ MergeScratch<G> mg;
+  __shared__ MergeScratch mg;
   const int i = blockIdx.y;
-  const int hkv = b.geo[i].n_kv_heads;
-  if ((int)blockIdx.x >= 2 * hkv) return;
-  const int m = tail_role_mode(mode, blockIdx.x / hkv);
-  if (!(m & (kMerge | kLists))) return;
-  layer_tail<G>(b.geo[i], b.arg[i], m, blockIdx.x % hkv, wc, mg);
+  layer_tail<G>(b.geo[i], b.arg[i], mode, blockIdx.x, wc, mg);
 }
 
 hipError_t launch_layer_tail(int mode, const LayerGeom& g, const LayerArgs& a, hipStream_t st) {
-  const dim3 grid(2 * g.n_kv_heads);
+  const dim3 grid(g.n_kv_heads * (g.group + 1));
 #define SEKV_TAIL(GG)                                                                          \
   case GG:                                                                                     \
     hipLaunchKernelGGL((layer_tail_kernel<GG>), grid, dim3(kThreads), 0, st, g, a, mode);     \
@@ -1505,7 +1469,7 @@ hipError_t launch_layer_tail_batch(int mode, int group, const BatchLayerArgs& b,
                                    hipStream_t st) {
   if (batch < 1 || batch > kMaxBatch) return hipErrorInvalidValue;
   int nx = 0;
-  for (int i = 0; i < batch; ++i) nx = max(nx, 2 * b.geo[i].n_kv_heads);
+  for (int i = 0; i < batch; ++i) nx = max(nx, b.geo[i].n_kv_heads * (group + 1));
   const dim3 grid(nx, batch);
 #define SEKV_TAIL(GG)                                                                          \
   case GG:                                                                                     \
