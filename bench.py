@@ -79,6 +79,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def counters_apply(args) -> bool:
+    """The committed counter summaries are of the plain step (device tier, every
+    option at its default); a run with any other option moves other bytes."""
+    return (args.tier == "device" and args.budget is None and args.gates is None
+            and args.query_corr == 0.0 and args.svd == "exact" and args.zoom_frac is None
+            and args.batch is None and args.n_layers is None and args.n_tokens is None
+            and args.residency_gb == 0.0)
+
+
 def read_traffic(workload: str):
     """HBM traffic per attention launch from committed rocprofv3 --pmc
     summaries, only if they were taken on the current kernel sources."""
@@ -399,7 +408,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, seed, s, spike, w, p, tau, qs[:, 0], args, ranks, B)
 
-    traffic = read_traffic(wl.name)
+    traffic = read_traffic(wl.name) if counters_apply(args) else None
     result = {
         "metric": METRIC,
         "value": 1e3 / ms_per_step,
@@ -431,8 +440,9 @@ def main():
             "unit": "GB/s",
             "frac": attn_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": ("sekv::layer_kernel x2 + sekv::cap_budget_kernel (sekv_route, "
-                       "sekv_cap_budget, sekv_decode_attn: one layer, capped)" if capped else
+            "kernel": ("sekv::layer_kernel + sekv::layer_tail_kernel, twice, and "
+                       "sekv::cap_budget_kernel (sekv_route, sekv_cap_budget, sekv_decode_attn: "
+                       "one layer, capped)" if capped else
                        "sekv::layer_kernel + sekv::layer_tail_kernel (sekv_route_attn, one "
                        "layer: route + attention, then merge + lists)"
                        if B == 1 else
@@ -441,7 +451,7 @@ def main():
             "algorithmic_bytes_per_launch": attn_bytes_meas,
             "avg_launch_us": attn_us_mean,
             "avg_launch_from": "HIP events around the timed region / (steps x layers); "
-                               "a layer is its two launches",
+                               "a layer is every launch named under kernel",
             "frac_of_measured_read": attn_gbs / read_gbs,
         },
         "cpu_baseline": cpu,

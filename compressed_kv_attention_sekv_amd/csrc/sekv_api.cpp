@@ -589,7 +589,8 @@ static sekv_status attn_impl(const sekv_cache* c, int32_t layer, const float* q_
   if (c->res_on) {
     sekv_cache* cm = const_cast<sekv_cache*>(c);   // per-cache call counter
     if (++cm->res_epoch > kResMaxEpoch) {
-      SEKV_HIP(hipMemsetAsync(c->res.claim, 0, c->res.n_sets * 8, fst));
+      // a fill kernel, not a memset, so that a captured step replays it correctly
+      SEKV_HIP(launch_fill_i32((int32_t*)c->res.claim, (int)(c->res.n_sets * 2), 0, fst));
       cm->res_epoch = 1;
     }
     SEKV_HIP(launch_resident_fetch(c->geom, layer, route->union_list, route->union_count,
@@ -751,6 +752,9 @@ sekv_status sekv_apply_gates(sekv_cache* c, const float* gates_dev, float eps,
   return SEKV_OK;
 }
 
+// sets of one residency cache, at most (the claims are cleared as 32-bit words)
+constexpr uint64_t kResMaxSets = 1ull << 30;
+
 sekv_status sekv_set_residency(sekv_cache* c, uint64_t capacity_bytes, uint64_t slot_bytes) {
   if (!c) return fail(SEKV_ERR_INVALID, "cache is NULL");
   if (c->cfg.factor_tier != SEKV_TIER_HOST_PINNED)
@@ -767,6 +771,9 @@ sekv_status sekv_set_residency(sekv_cache* c, uint64_t capacity_bytes, uint64_t 
     if (n_sets == 0)
       return fail(SEKV_ERR_INVALID, "capacity of %llu bytes is below one slot of %llu bytes",
                   (unsigned long long)capacity_bytes, (unsigned long long)(slot_floats * 4));
+    if (n_sets > kResMaxSets)
+      return fail(SEKV_ERR_UNSUPPORTED, "%llu residency sets; at most %llu are supported",
+                  (unsigned long long)n_sets, (unsigned long long)kResMaxSets);
   }
   // nothing queued may still use the old tables
   SEKV_HIP(hipDeviceSynchronize());

@@ -269,8 +269,10 @@ sekv_status sekv_apply_gates(sekv_cache* cache, const float* gates_dev, float ep
  * The call synchronises the device (it frees and allocates device memory and
  * clears the tables), so no work of this cache may be in flight on another
  * thread.  Errors: SEKV_ERR_INVALID for a NULL or device-tier cache, a zero
- * slot size, or a capacity below one slot; SEKV_ERR_NOMEM if the tables do
- * not fit; on failure the cache is left disabled. */
+ * slot size, or a capacity below one slot; SEKV_ERR_UNSUPPORTED for more
+ * than 2^30 sets or more than 2^39 (layer, KV head, span) blocks;
+ * SEKV_ERR_NOMEM if the tables do not fit; on failure the cache is left
+ * disabled. */
 sekv_status sekv_set_residency(sekv_cache* cache, uint64_t capacity_bytes, uint64_t slot_bytes);
 
 /* Counters of the residency cache since it was enabled or last reset

@@ -61,6 +61,8 @@ def test_residency_rejects_device_tier_and_bad_sizes(S, setup):
         dev.set_residency(1 << 20)
     with pytest.raises(S.SekvError, match="below one slot"):
         res.set_residency(1000, 64 * 1024)
+    with pytest.raises(S.SekvError, match="residency sets"):
+        res.set_residency((1 << 31) * 256, 256)   # 2^31 sets of 256 bytes, before any allocation
     with pytest.raises(S.SekvError, match="not enabled"):
         res.residency_stats()
 
