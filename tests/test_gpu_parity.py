@@ -335,6 +335,37 @@ def test_host_tier_matches_device_tier(S):
             assert err <= 1e-6
 
 
+def test_many_chunks_merge_parity(S):
+    """Thousands of short spans, so a KV head has more than 128 chunks and the
+    tail's merge runs more than one round of slot loads per thread (three with
+    the host tier's separate zoom slots): routes and outputs against the
+    oracle, and the host tier against the device tier."""
+    wl = synth.workload("tiny", n_tokens=40000, min_span_len=1)
+    log("[parity] many chunks: tiny N=40000, min span 1")
+    inp = Inputs(wl, 4)
+    cache = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    assert cache.info.n_compressed > 128 * 32
+    orc = OracleSide(inp, [0], wl.max_rank)
+    tau = synth.tau_uniform(wl, 4, device="cuda")[0].contiguous()
+    q = inp.query(0)[0]
+    n_tie, worst, route = check_layer(S, cache, orc, inp, 0, q, tau, wl.gamma, TOL["f32"])
+    log(f"[parity] many chunks: spans={cache.info.n_compressed} zoomed={int(route.mask.sum())} "
+        f"ties={n_tie} err={worst:.2e}")
+    assert int(route.mask.sum()) > 0
+    host = S.sekv_build_spans(make_cfg(S, wl, tier="host"), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    rbd, od = run_gpu_layer(S, cache, 0, q, inp.p[0], tau)
+    rb = S.RouteBuffers.allocate(host)
+    oh = torch.zeros_like(od)
+    ws = torch.empty(host.workspace_bytes(), dtype=torch.uint8, device="cuda")
+    S.sekv_route_attn(host, 0, q, inp.p[0].contiguous(), tau, rb, oh, ws,
+                      fetch_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert torch.equal(rb.mask, rbd.mask) and torch.equal(rb.union_count, rbd.union_count)
+    err = float((oh - od).abs().max() / od.abs().max())
+    log(f"[parity] many chunks: host tier rel diff vs device={err:.2e}")
+    assert err <= 1e-6
+
+
 @pytest.mark.parametrize("layer,kv_head", [(0, 3), (31, 6)])
 def test_full_size_sampled_parity(S, layer, kv_head):
     """The Llama-3-8B-shape workload at full size (32 layers, 131072 tokens,
