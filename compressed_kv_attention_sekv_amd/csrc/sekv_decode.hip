@@ -19,9 +19,9 @@
 //       c_h = U_V^T p_h;  acc_h += V_V^T (sigma_V * c_h)
 //     so the factors are read once for all heads and no token row is formed.
 // Each workgroup writes one partial (m, l, acc) per head and its chunk's zoom
-// bit masks.  A second, small launch (one workgroup per KV head) merges the
-// partials into o and writes the ascending zoom lists from the bit masks: the
-// kernel boundary between the two makes every workgroup's stores visible, so
+// bit masks.  A second, small launch merges the partials into o (one workgroup
+// per query head) and writes the ascending zoom lists from the bit masks (one
+// per KV head): the kernel boundary between the two makes every workgroup's stores visible, so
 // no workgroup waits on another and no agent-scope fence (an L2 write-back or
 // invalidation, which stalls the other KV heads' workgroups still streaming
 // factors through that L2) sits inside the layer kernel.

@@ -152,7 +152,7 @@ enum LayerMode : int {
   kDense = 2,      // attend the workgroup's full-resolution rows and coarse entries
   kZoom = 4,       // attend the chunk's zoomed spans from their factors
   kZoomSplit = 8,  // zoomed-span partials go to their own slots (separate launch)
-  kMerge = 16,     // tail launch: merge a KV head's partials into o
+  kMerge = 16,     // tail launch: merge each query head's partials into o
   kLists = 32,     // tail launch: write the ascending zoom lists and union
 };
 
