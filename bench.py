@@ -443,6 +443,11 @@ def main():
             "kernel": ("sekv::layer_kernel + sekv::layer_tail_kernel, twice, and "
                        "sekv::cap_budget_kernel (sekv_route, sekv_cap_budget, sekv_decode_attn: "
                        "one layer, capped)" if capped else
+                       "host tier: sekv::layer_kernel + sekv::layer_tail_kernel (route, lists), "
+                       "the factor fetch (fetch_gather_kernel, or res_claim_kernel + "
+                       "res_fetch_kernel with a residency cache), sekv::layer_kernel twice (rows "
+                       "and coarse entries; zoomed spans) and sekv::layer_tail_kernel (merge)"
+                       if args.tier == "host" else
                        "sekv::layer_kernel + sekv::layer_tail_kernel (sekv_route_attn, one "
                        "layer: route + attention, then merge + lists)"
                        if B == 1 else
