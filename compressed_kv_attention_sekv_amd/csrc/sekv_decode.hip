@@ -1141,9 +1141,9 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int o = min(orow + 32 * k, nout - 1);   // rows past nout are never used
-      const float4* pr = (const float4*)(a.proj + ((size_t)h0 * dr + o) * kHeadDim + part * 16);
+      const float* pr = a.proj + ((size_t)h0 * dr + o) * kHeadDim + part * 4;
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) pv[k][c4] = pr[c4];
+      for (int c4 = 0; c4 < 4; ++c4) pv[k][c4] = *(const float4*)(pr + 32 * c4);
     }
     if (gate) {
       const int j = j0 + jl_g, h = h0 + hl_g;
@@ -1194,24 +1194,26 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
 
   // ---- routing ------------------------------------------------------------
   if (route && nj > 0) {
-    // q~_h = P_h q_h (float64): 8 lanes per output, 16 dims per lane
+    // q~_h = P_h q_h (float64): 8 lanes per output, 16 dims per lane, lane
+    // `part` takes dims 32 c + 4 part .. + 3, so each load is a 128-byte run
     for (int k0 = 0; k0 < nout; k0 += 128) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int o = k0 + orow + 32 * k;
         if (k0 > 0 && o < nout) {
-          const float4* pr = (const float4*)(a.proj + ((size_t)h0 * dr + o) * kHeadDim + part * 16);
+          const float* pr = a.proj + ((size_t)h0 * dr + o) * kHeadDim + part * 4;
 #pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) pv[k][c4] = pr[c4];
+          for (int c4 = 0; c4 < 4; ++c4) pv[k][c4] = *(const float4*)(pr + 32 * c4);
         }
         double acc = 0.0;
         if (o < nout) {
-          const float* qh = &s.rt.qu[o / dr][part * 16];
+          const float* qh = &s.rt.qu[o / dr][part * 4];
 #pragma unroll
           for (int c4 = 0; c4 < 4; ++c4) {
             const float4 x = pv[k][c4];
-            acc += (double)x.x * (double)qh[4 * c4] + (double)x.y * (double)qh[4 * c4 + 1] +
-                   (double)x.z * (double)qh[4 * c4 + 2] + (double)x.w * (double)qh[4 * c4 + 3];
+            const float* qc = qh + 32 * c4;
+            acc += (double)x.x * (double)qc[0] + (double)x.y * (double)qc[1] +
+                   (double)x.z * (double)qc[2] + (double)x.w * (double)qc[3];
           }
         }
         acc = group_sum<8>(acc);
