@@ -65,8 +65,8 @@ def parse():
                     help="soft-gate the factors after the build (Eq. 8) with synthetic gates, "
                          "dropping components whose gate is below this value")
     ap.add_argument("--zoom-frac", type=float, default=None,
-                    help="share of spans every query head zooms (workloads with one share for "
-                         "all heads, e.g. the batch-4 sweep)")
+                    help="share of spans every query head zooms, replacing the workload's own "
+                         "shares (0 zooms nothing, 1 zooms every span)")
     return ap.parse_args()
 
 
@@ -184,10 +184,13 @@ def main():
 
     # ---- thresholds: calibrated on the library's own gate values (sequence 0;
     # thresholds belong to the model, so every sequence uses them) -------------
-    if wl.tau_mode == "uniform":
+    if args.zoom_frac is not None:
+        # one share for every (layer, head), whatever the workload's own mode
+        targets = torch.full((L, Hq), float(args.zoom_frac), dtype=torch.float64)
+    elif wl.tau_mode == "uniform":
         targets = None
     else:
-        targets = synth.zoom_targets(wl, seed, frac=args.zoom_frac)
+        targets = synth.zoom_targets(wl, seed)
     if targets is None:
         tau = synth.tau_uniform(wl, seed, device=dev)
     else:
@@ -429,7 +432,7 @@ def main():
             "max_rank": wl.max_rank, "route_dim": wl.route_dim, "graph": graph is not None,
             "budget_tokens": args.budget, "query_corr": args.query_corr,
             "gate_eps": args.gates, "svd": args.svd,
-            "zoom": ("skewed" if wl.tau_mode == "skewed" else
+            "zoom": ("skewed" if wl.tau_mode == "skewed" and args.zoom_frac is None else
                      (f"{float(targets[0, 0]):g} per head" if targets is not None
                       else "uniform tau")),
         },

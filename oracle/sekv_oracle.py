@@ -19,7 +19,8 @@ silent.  The readings are:
   * statistics: population mean and std of the surprisal over the whole
     sequence, in float64, two passes; threshold mean + alpha * std (Sec. 3.1;
     summary page sec. 2 gives alpha = 1.0);
-  * boundary: strictly greater than the threshold ("exceeds", summary sec. 2);
+  * boundary: strictly greater than the threshold (summary sec. 2 says the
+    surprisal must exceed it);
   * the last ``window`` positions are the local window (summary sec. 2: the
     most recent 512 tokens stay at full resolution) and are never anchors or
     span members;
@@ -34,15 +35,20 @@ silent.  The readings are:
   * gate p = sigmoid(q~ . s + gamma ln n), q~ = P q, no 1/sqrt(d_r) scale,
     natural log; zoom iff p > tau strictly (Sec. 3.2, Sec. 3.3 Eq. 9);
   * factors: exact SVD, hard gates (keep the top r_j components,
-    r_j = min(requested rank, n_j, d, R), at least 1), same r_j for K and V
-    (Sec. 3.2 low-rank paragraph, Eq. 8 with 0/1 gates);
+    r_j = min(requested rank, n_j, d, R), at least 1); the build takes one
+    requested rank per span for its keys and its values alike (Sec. 3.2
+    low-rank paragraph, Eq. 8 with 0/1 gates), and soft gates may then leave
+    the two with different ranks;
   * attention: one softmax over dense tokens (window, anchors, short-span
     tokens), one coarse entry per non-zoomed span with + ln n_j added to its
     scaled score, and the rank-r reconstruction of every zoomed span's tokens;
     score scale 1/sqrt(d) (Sec. 3.3; summary sec. 3);
   * soft gates (optional, Eq. 8): each retained component i is scaled by its
     gate g_i, components with g_i below a threshold are dropped, at least one
-    (the largest gate) is kept; one gate vector per span for keys and values;
+    (the largest gate) is kept; the key matrix and the value matrix of a span
+    carry their own gate vectors (Sec. 3.2 low-rank paragraph: the value
+    matrix gets the same gated decomposition with its own gates and factors),
+    so each keeps its own rank;
   * budget cap (optional): per layer and KV head, the reconstructed spans'
     total length is capped; spans are kept by decreasing gate value (the
     largest over the group's heads that selected them), ties by lower id,
@@ -234,14 +240,18 @@ def gate_factors(f: Factors, gates, eps: float) -> Factors:
                    tail2=float("nan"))
 
 
-def gate_group(gc: "GroupCache", gates, eps: float) -> "GroupCache":
-    """The group with every span's key and value factors gated (Eq. 8), one
-    gate vector per span shared by keys and values (they keep one rank);
-    ``gates`` is [S_c][R]."""
-    kf = [gate_factors(f, gates[i], eps) for i, f in enumerate(gc.kfac)]
-    vf = [gate_factors(f, gates[i], eps) for i, f in enumerate(gc.vfac)]
+def gate_group(gc: "GroupCache", key_gates, value_gates, eps: float) -> "GroupCache":
+    """The group with every span's key factors gated by its key gates and its
+    value factors by its value gates (Eq. 8 applied to each matrix, Sec. 3.2:
+    the value matrix has gates and factors of its own).  ``key_gates`` and
+    ``value_gates`` are [S_c][R]; gate i of a span belongs to the i-th largest
+    singular value of that matrix.  Keys and values then keep their own ranks
+    (``rank`` and ``vrank``)."""
+    kf = [gate_factors(f, key_gates[i], eps) for i, f in enumerate(gc.kfac)]
+    vf = [gate_factors(f, value_gates[i], eps) for i, f in enumerate(gc.vfac)]
     return dataclasses.replace(gc, kfac=kf, vfac=vf,
-                               rank=np.array([f.sigma.size for f in kf], dtype=np.int64))
+                               rank=np.array([f.sigma.size for f in kf], dtype=np.int64),
+                               vrank=np.array([f.sigma.size for f in vf], dtype=np.int64))
 
 
 @dataclasses.dataclass
@@ -257,7 +267,8 @@ class GroupCache:
     summary: Dict[int, np.ndarray]   # query head -> [S_c][d_r], rounded to storage
     kfac: List[Factors]
     vfac: List[Factors]
-    rank: np.ndarray                 # [S_c]
+    rank: np.ndarray                 # [S_c] retained rank of the key factors
+    vrank: np.ndarray                # [S_c] retained rank of the value factors
 
 
 def build_group(seg: Segmentation, s, k, v, w_route: Dict[int, np.ndarray], ranks_by_pos,
@@ -292,7 +303,8 @@ def build_group(seg: Segmentation, s, k, v, w_route: Dict[int, np.ndarray], rank
         dense_k=k[seg.dense_pos], dense_v=v[seg.dense_pos],
         kbar=np.array(kbar).reshape(sc, d), vbar=np.array(vbar).reshape(sc, d),
         summary={h: np.array(x).reshape(sc, dr) for h, x in summ.items()},
-        kfac=kfac, vfac=vfac, rank=np.array(ranks, dtype=np.int64))
+        kfac=kfac, vfac=vfac, rank=np.array(ranks, dtype=np.int64),
+        vrank=np.array(ranks, dtype=np.int64))
 
 
 # ---------------------------------------------------------------------------

@@ -323,7 +323,7 @@ def test_attention_golden():
                          cspan=np.array([0]), dense_pos=np.array([2]))
     gc = O.GroupCache(dense_k=np.array(c["dense_k"], float), dense_v=np.array(c["dense_v"], float),
                       kbar=np.array(c["kbar"], float), vbar=np.array(c["vbar"], float),
-                      summary={}, kfac=[None], vfac=[None], rank=np.array([1]))
+                      summary={}, kfac=[None], vfac=[None], rank=np.array([1]), vrank=np.array([1]))
     o = O.mixed_attention(c["q"], gc, seg, [False])
     assert np.allclose(o, c["o"], atol=1e-15)
 
@@ -507,3 +507,92 @@ def test_budget_cap_properties():
             prev = capped.mask
         big = O.cap_budget(route, seg, hkv, max(full))
         assert (big.mask == route.mask).all()
+
+
+def _two_spans(seed, n=60):
+    """A span's key and value matrices with different planted spectra."""
+    rng = np.random.default_rng(seed)
+    d = 128
+    k = rng.standard_normal((n, 7)) @ rng.standard_normal((7, d)) + 0.05 * rng.standard_normal((n, d))
+    v = 3.0 * rng.standard_normal((n, 4)) @ rng.standard_normal((4, d)) + \
+        0.2 * rng.standard_normal((n, d))
+    return k, v
+
+
+def _energy(x):
+    """Squared singular values of x, descending, from LAPACK's symmetric
+    eigensolver (a routine other than the oracle's SVD)."""
+    return np.sort(np.clip(np.linalg.eigvalsh(x.T @ x), 0.0, None))[::-1]
+
+
+def test_gate_group_keys_and_values_have_their_own_gates():
+    """Sec. 3.2 low-rank paragraph: the value matrix gets the gated
+    decomposition with gates and factors of its own.  Value-only gates leave
+    the keys bit-identical; distinct key and value gates give distinct ranks;
+    and each matrix's error is its own closed form sum_kept (1 - g)^2 s^2 +
+    sum_dropped s^2 + sum_beyond_r s^2 (orthonormal factors), so gates applied
+    to the wrong matrix, or one vector for both, fail."""
+    n, r, eps = 60, 12, 0.3
+    k, v = _two_spans(3, n)
+    seg = types.SimpleNamespace()
+    kf, vf = O.truncated_svd(k, r), O.truncated_svd(v, r)
+    gc = O.GroupCache(dense_k=np.zeros((0, 128)), dense_v=np.zeros((0, 128)),
+                      kbar=np.zeros((1, 128)), vbar=np.zeros((1, 128)), summary={},
+                      kfac=[kf], vfac=[vf], rank=np.array([r]), vrank=np.array([r]))
+    ones = np.ones((1, 32))
+    rng = np.random.default_rng(9)
+    gv = np.r_[rng.uniform(0.35, 1.0, 4), rng.uniform(0.0, 0.25, r - 4), np.zeros(32 - r)][None, :]
+    gk = np.r_[rng.uniform(0.35, 1.0, 9), rng.uniform(0.0, 0.25, r - 9), np.zeros(32 - r)][None, :]
+    # value gates only: keys untouched, bit for bit
+    g1 = O.gate_group(gc, ones, gv, eps)
+    assert np.array_equal(g1.kfac[0].u, kf.u) and np.array_equal(g1.kfac[0].sigma, kf.sigma)
+    assert np.array_equal(g1.kfac[0].vt, kf.vt)
+    assert g1.rank.tolist() == [r] and g1.vrank.tolist() == [4]
+    # distinct gates: distinct ranks, each matrix's error its own closed form
+    g2 = O.gate_group(gc, gk, gv, eps)
+    assert g2.rank.tolist() == [9] and g2.vrank.tolist() == [4]
+    for x, fac, g in ((k, g2.kfac[0], gk[0]), (v, g2.vfac[0], gv[0])):
+        s2 = _energy(x)
+        kept = g[:r] >= eps
+        want = float(np.sum((1.0 - g[:r][kept]) ** 2 * s2[:r][kept]) + np.sum(s2[:r][~kept]) +
+                     np.sum(s2[r:]))
+        got = float(np.linalg.norm(x - fac.reconstruct()) ** 2)
+        assert got == pytest.approx(want, rel=1e-8)
+    # the closed forms tell the two matrices apart: the key error under the
+    # value gates is not the key error under the key gates
+    swapped = O.gate_group(gc, gv, gk, eps)
+    ek = float(np.linalg.norm(k - swapped.kfac[0].reconstruct()) ** 2)
+    s2 = _energy(k)
+    kept = gk[0, :r] >= eps
+    want_k = float(np.sum((1.0 - gk[0, :r][kept]) ** 2 * s2[:r][kept]) + np.sum(s2[:r][~kept]) +
+                   np.sum(s2[r:]))
+    assert abs(ek - want_k) > 1e-3 * want_k
+    del seg
+
+
+def test_gated_attention_uses_each_matrix_reconstruction():
+    """A zoomed span with value gates of zero everywhere but one component
+    attends to values rebuilt from that component alone, while its scores
+    still use the ungated keys: checked against torch's SDPA over the rows the
+    two reconstructions give."""
+    n, r = 40, 10
+    k, v = _two_spans(4, n)
+    seg = O.Segmentation(n_tokens=n, window=0, mu=0.0, sigma=0.0, threshold=0.0,
+                         anchors=np.zeros(0, np.int64), span_start=np.array([0]),
+                         span_len=np.array([n]), kind=np.array([0]), cspan=np.array([0]),
+                         dense_pos=np.zeros(0, np.int64))
+    kf, vf = O.truncated_svd(k, r), O.truncated_svd(v, r)
+    gc = O.GroupCache(dense_k=np.zeros((0, 128)), dense_v=np.zeros((0, 128)),
+                      kbar=np.zeros((1, 128)), vbar=np.zeros((1, 128)), summary={},
+                      kfac=[kf], vfac=[vf], rank=np.array([r]), vrank=np.array([r]))
+    gv = np.zeros((1, 32))
+    gv[0, 2] = 0.7
+    gg = O.gate_group(gc, np.ones((1, 32)), gv, 0.5)
+    assert gg.rank.tolist() == [r] and gg.vrank.tolist() == [1]
+    q = np.random.default_rng(5).standard_normal(128)
+    o = O.mixed_attention(q, gg, seg, np.array([True]))
+    kr = (kf.u * kf.sigma) @ kf.vt
+    vr = 0.7 * vf.sigma[2] * np.outer(vf.u[:, 2], vf.vt[2])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, None, :], torch.from_numpy(kr)[None], torch.from_numpy(vr)[None])
+    assert np.allclose(o, ref[0, 0].numpy(), rtol=1e-10, atol=1e-12)
