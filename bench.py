@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=3)
+    ap.add_argument("--cpu-configs", action="store_true",
+                    help="only time the CPU oracle (one pinned core) on every decode workload and "
+                         "print one JSON line; uses no GPU")
     ap.add_argument("--n-layers", type=int, default=None, help="override layer count (testing)")
     ap.add_argument("--n-tokens", type=int, default=None, help="override context (testing)")
     ap.add_argument("--batch", type=int, default=None,
@@ -103,6 +106,9 @@ def read_traffic(workload: str):
 
 def main():
     args = parse()
+    if args.cpu_configs:
+        cpu_configs(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this path runs on a "
               "single MI355X; see the sharding notes in the design document)", file=sys.stderr)
@@ -168,7 +174,8 @@ def main():
                 sys.exit(2)
             fb = c.info.factor_bytes
             t0 = time.time()
-            S.sekv_apply_gates(c, synth.span_gates(wl, seed, c.info.n_compressed, device=dev),
+            S.sekv_apply_gates(c, synth.span_gates(wl, seed, c.info.n_compressed, "k", device=dev),
+                               synth.span_gates(wl, seed, c.info.n_compressed, "v", device=dev),
                                args.gates)
             log(f"sequence {b}: gates applied in {time.time() - t0:.2f}s, factor bytes "
                 f"{fb / 1e9:.2f} -> {c.info.factor_bytes / 1e9:.2f} GB")
@@ -295,15 +302,15 @@ def main():
 
     # ---- algorithmic bytes of the timed steps ----------------------------------
     # per sequence: the resident bytes every layer launch reads, and the factor
-    # bytes 8 r (n + d + 1) of each (layer, KV head, span) for the zoom part
+    # bytes 4 (rK + rV) (n + d + 1) of each (layer, KV head, span) for the zoom part
     eb = 2 if wl.kv_dtype == "bf16" else 4
     span_bytes, resident_layer = [], 0
     for c in caches:
         sp = c.spans()
         clen = sp["span_len"][sp["cspan"].long()].to(torch.float64)
-        rank_tab = torch.stack([torch.stack([c.group_data(l, g)[3] for g in range(Hkv)])
-                                for l in range(L)]).to(torch.float64)  # [L][Hkv][Sc]
-        span_bytes.append((8.0 * rank_tab * (clen + d + 1)).to(dev))
+        rank_tab = torch.stack([torch.stack([sum(c.group_data(l, g)[3:5]) for g in range(Hkv)])
+                                for l in range(L)]).to(torch.float64)  # [L][Hkv][Sc] rK + rV
+        span_bytes.append((4.0 * rank_tab * (clen + d + 1)).to(dev))
         D_b, sc_b = c.info.n_dense, c.info.n_compressed
         resident_layer += (Hkv * (2 * d * eb * D_b + 2 * d * eb * sc_b) +
                            Hq * wl.route_dim * eb * sc_b + Hq * (wl.route_dim * d + d + 1) * 4 +
@@ -483,60 +490,175 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def host_info() -> dict:
+    """CPU model and thread counts of the host the oracle runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "threads_allowed": aff}
+
+
+class one_core:
+    """Pin this process to one core (the first it may run on) and every thread
+    pool to one thread; restore both on exit."""
+
+    def __enter__(self):
+        import torch
+        from threadpoolctl import threadpool_limits
+        self.aff = os.sched_getaffinity(0)
+        self.core = min(self.aff)
+        os.sched_setaffinity(0, {self.core})
+        self.torch_threads = torch.get_num_threads()
+        torch.set_num_threads(1)
+        self.tp = threadpool_limits(limits=1)
+        return self
+
+    def __exit__(self, *exc):
+        import torch
+        self.tp.unregister()
+        torch.set_num_threads(self.torch_threads)
+        os.sched_setaffinity(0, self.aff)
+        return False
+
+
+def oracle_cache(wl, seg, sv, seed, spike, w, layers, device):
+    """The oracle's cache of the given layers (all KV heads), untimed."""
+    import oracle as O
+    import synth
+    f64 = lambda t: t.detach().cpu().double().numpy()  # noqa: E731
+    g = wl.group
+    groups = {}
+    for layer in layers:
+        kk, vv, rk = synth.kv_cache(wl, seed, spike, device=device, layers=[layer])
+        wl_ = f64(w[layer])
+        groups[layer] = {kh: O.build_group(seg, sv, f64(kk[0, kh]), f64(vv[0, kh]),
+                                           {h: wl_[h] for h in range(kh * g, kh * g + g)},
+                                           rk[0, kh].cpu().numpy(), wl.kv_dtype, wl.max_rank)
+                         for kh in range(wl.n_kv_heads)}
+        del kk, vv
+    return groups
+
+
+def time_oracle_decode(wl, seg, groups, p, tau, qs, layers, budget_s=10.0, max_steps=40):
+    """Route + attention of the given layers, every query head, over fresh step
+    queries until about ``budget_s`` of work; returns (seconds per layer, steps)."""
+    import oracle as O
+    f64 = lambda t: t.detach().cpu().double().numpy()  # noqa: E731
+    g = wl.group
+    pr = {layer: f64(p[layer]) for layer in layers}
+    ta = {layer: f64(tau[layer]) for layer in layers}
+    summ = {layer: {h: groups[layer][h // g].summary[h] for h in range(wl.n_q_heads)}
+            for layer in layers}
+    n_steps, dt = 0, 0.0
+    while dt < budget_s and n_steps < min(max_steps, qs.shape[0]):
+        q = f64(qs[n_steps])
+        t0 = time.time()
+        for layer in layers:
+            route = O.route_layer(q[layer], pr[layer], ta[layer], summ[layer], seg, wl.gamma,
+                                  wl.n_kv_heads)
+            O.decode_layer(q[layer], route, groups[layer], seg, n_kv_heads=wl.n_kv_heads)
+        dt += time.time() - t0
+        n_steps += 1
+    return dt / (n_steps * len(layers)), n_steps, dt
+
+
 def cpu_baseline(wl, seed, s, spike, w, p, tau, qs, args, ranks, batch=1):
-    """The oracle as it stands, on one thread: build the oracle's cache for a
-    few layers spread over the depth (untimed), then time its decode (route +
-    attention, every query head) of those layers over fresh step queries until
-    about 10 s of CPU work, and scale to a full step (of sequence 0; a step of
-    a batch is ``batch`` such sequences)."""
+    """The oracle as it stands, pinned to one core with one thread: build the
+    oracle's cache for a few layers spread over the depth (untimed), then time
+    its decode (route + attention, every query head) of those layers over
+    fresh step queries until about 10 s of CPU work, and scale to a full step
+    (of sequence 0; a step of a batch is ``batch`` such sequences)."""
+    import oracle as O
+
+    L = wl.n_layers
+    layers = sorted({0, L // 2, L - 1}) if args.cpu_layers >= 3 else list(range(args.cpu_layers))
+    with one_core() as pin:
+        t0 = time.time()
+        sv = s.detach().cpu().double().numpy()
+        seg = O.segment(sv, wl.window, wl.alpha, wl.min_span_len)
+        groups = oracle_cache(wl, seg, sv, seed, spike, w, layers, s.device)
+        build_s = time.time() - t0
+        per_layer, n_steps, dt = time_oracle_decode(wl, seg, groups, p, tau, qs, layers)
+        core = pin.core
+    per_step = per_layer * L * batch
+    log(f"cpu oracle (core {core}): layers {layers} x {n_steps} steps decoded in {dt:.2f}s "
+        f"(build {build_s:.1f}s) -> {per_step:.2f} s/step")
+    out = {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
+           "sample": f"{n_steps} decode steps of layers {layers} ({len(layers)} of {L}), all "
+                     f"{wl.n_q_heads} query heads, route + attention, float64 numpy pinned to "
+                     f"core {core} with one thread ({dt:.1f} s); time per layer scaled by {L}" +
+                     (f" and by {batch} sequences" if batch > 1 else ""),
+           "pinned_core": core}
+    out.update(host_info())
+    return out
+
+
+def cpu_configs(args):
+    """The oracle on one pinned core for every decode workload (no GPU): the
+    tiny single-layer reference whole, and sampled layers of the 32K, 128K and
+    batch-4 128K shapes, each scaled to a full step.  Inputs are drawn on the
+    CPU; thresholds are calibrated on the oracle's own gate values as the
+    workloads state (the batch-4 shape at its 10% share per head)."""
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_limits
 
     import oracle as O
     import synth
 
-    L = wl.n_layers
-    layers = sorted({0, L // 2, L - 1}) if args.cpu_layers >= 3 else list(range(args.cpu_layers))
-    f64 = lambda t: t.detach().cpu().double().numpy()  # noqa: E731
-    with threadpool_limits(limits=1):
+    results = []
+    for name, n_layers_timed in (("tiny", 1), ("llama32_3b_32k", 3), ("llama3_8b_128k", 3),
+                                 ("qwen25_14b_128k_b4", 3)):
+        wl = synth.workload(name)
+        seed = synth.default_seed(wl)
+        L = wl.n_layers
+        layers = [0] if L == 1 else sorted({0, L // 2, L - 1})[:n_layers_timed]
         t0 = time.time()
-        sv = f64(s)
+        s, spike = synth.surprisal(wl, seed)
+        w, p = synth.route_weights(wl, seed)
+        sv = s.double().numpy()
         seg = O.segment(sv, wl.window, wl.alpha, wl.min_span_len)
+        groups = oracle_cache(wl, seg, sv, seed, spike, w, layers, "cpu")
         g = wl.group
-        groups = {}
-        for layer in layers:
-            kk, vv, rk = synth.kv_cache(wl, seed, spike, device=s.device, layers=[layer])
-            wl_ = f64(w[layer])
-            groups[layer] = {kh: O.build_group(seg, sv, f64(kk[0, kh]), f64(vv[0, kh]),
-                                               {h: wl_[h] for h in range(kh * g, kh * g + g)},
-                                               rk[0, kh].cpu().numpy(), wl.kv_dtype, wl.max_rank)
-                             for kh in range(wl.n_kv_heads)}
-            del kk, vv
-        build_s = time.time() - t0
-        pr = {layer: f64(p[layer]) for layer in layers}
-        ta = {layer: f64(tau[layer]) for layer in layers}
-        summ = {layer: {h: groups[layer][h // g].summary[h] for h in range(wl.n_q_heads)}
-                for layer in layers}
-        n_steps, dt = 0, 0.0
-        while dt < 10.0 and n_steps < min(40, qs.shape[0]):
-            q = f64(qs[n_steps])
-            t0 = time.time()
+        if wl.tau_mode == "uniform":
+            tau = synth.tau_uniform(wl, seed)
+        else:
+            targets = synth.zoom_targets(wl, seed)
+            cq = synth.calibration_queries(wl, seed, 16)
+            tau = torch.ones(L, wl.n_q_heads)
             for layer in layers:
-                route = O.route_layer(q[layer], pr[layer], ta[layer], summ[layer], seg, wl.gamma,
-                                      wl.n_kv_heads)
-                O.decode_layer(q[layer], route, groups[layer], seg, n_kv_heads=wl.n_kv_heads)
-            dt += time.time() - t0
-            n_steps += 1
-    per_step = dt / (n_steps * len(layers)) * L * batch
-    log(f"cpu oracle: layers {layers} x {n_steps} steps decoded in {dt:.2f}s (build {build_s:.1f}s) "
-        f"-> {per_step:.2f} s/step")
-    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_steps} decode steps of layers {layers} ({len(layers)} of {L}), all "
-                      f"{wl.n_q_heads} query heads, route + attention, float64 numpy on one "
-                      f"thread ({dt:.1f} s); time per layer scaled by {L}" +
-                      (f" and by {batch} sequences" if batch > 1 else ""),
-            "host_threads_available": os.cpu_count()}
+                summ = {h: groups[layer][h // g].summary[h] for h in range(wl.n_q_heads)}
+                probs = np.concatenate([O.route_layer(
+                    cq[i, layer].double().numpy(), p[layer].double().numpy(),
+                    np.full(wl.n_q_heads, 2.0), summ, seg, wl.gamma, wl.n_kv_heads).prob
+                    for i in range(cq.shape[0])], axis=1)
+                for h in range(wl.n_q_heads):
+                    f = float(targets[layer, h])
+                    tau[layer, h] = float(np.quantile(probs[h], 1.0 - f)) if f > 0 else 1.0
+        qs = torch.stack([synth.queries(wl, seed, i) for i in range(40)])
+        setup_s = time.time() - t0
+        with one_core() as pin:
+            per_layer, n_steps, dt = time_oracle_decode(wl, seg, groups, p, tau, qs, layers)
+            core = pin.core
+        per_step = per_layer * L * wl.batch
+        log(f"cpu oracle {name}: {n_steps} steps of layers {layers} in {dt:.1f}s "
+            f"(setup {setup_s:.0f}s) -> {per_step:.3f} s/step")
+        results.append({"workload": name, "value": 1.0 / per_step, "unit": "steps/s",
+                        "cores": 1, "pinned_core": core, "kind": "oracle",
+                        "sample": f"{n_steps} decode steps of layers {layers} ({len(layers)} of "
+                                  f"{L}), route + attention of all {wl.n_q_heads} query heads "
+                                  f"({dt:.1f} s); scaled by {L} layers"
+                                  + (f" and {wl.batch} sequences" if wl.batch > 1 else ""),
+                        "context": wl.n_tokens, "n_compressed": seg.n_compressed})
+    out = {"cpu_oracle_configs": results}
+    out.update(host_info())
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -105,7 +105,7 @@ def lib() -> ctypes.CDLL:
                                    ctypes.POINTER(P)]),
         "sekv_cache_info_get": (I32, [P, ctypes.POINTER(SekvCacheInfo)]),
         "sekv_cache_copy_spans": (I32, [P, P, P, P, P, P, P]),
-        "sekv_cache_copy_group": (I32, [P, I32, I32, P, P, P, P]),
+        "sekv_cache_copy_group": (I32, [P, I32, I32, P, P, P, P, P]),
         "sekv_cache_copy_factors": (I32, [P, I32, I32, I32, I32, P, P, P]),
         "sekv_route": (I32, [P, I32, P, P, P, ctypes.POINTER(SekvRouteOut), P]),
         "sekv_decode_workspace_bytes": (SZ, [P]),
@@ -120,7 +120,7 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(P), ctypes.POINTER(SZ), P]),
         "sekv_cap_budget": (I32, [P, ctypes.POINTER(SekvRouteOut), ctypes.c_int64, P]),
         "sekv_set_residency": (I32, [P, U64, U64]),
-        "sekv_apply_gates": (I32, [P, P, ctypes.c_float, P]),
+        "sekv_apply_gates": (I32, [P, P, P, ctypes.c_float, P]),
         "sekv_residency_stats": (I32, [P, ctypes.POINTER(U64), I32]),
         "sekv_cache_destroy": (None, [P]),
         "sekv_last_error": (ctypes.c_char_p, []),
@@ -245,16 +245,18 @@ class Cache:
         return out
 
     def group_data(self, layer: int, kv_head: int):
-        """(kbar, vbar, summaries [G][S_c][dr], ranks) of one (layer, KV head), CPU tensors."""
+        """(kbar, vbar, summaries [G][S_c][dr], key ranks, value ranks) of one
+        (layer, KV head), CPU tensors."""
         sc, d, dr, g = self.info.n_compressed, self.cfg.head_dim, self.cfg.route_dim, self.group
         dt = torch.bfloat16 if self.cfg.kv_dtype == SEKV_BF16 else torch.float32
         kb = torch.zeros(max(sc, 1), d, dtype=dt)
         vb = torch.zeros(max(sc, 1), d, dtype=dt)
         sm = torch.zeros(g, max(sc, 1), dr, dtype=dt)
         rk = torch.zeros(max(sc, 1), dtype=torch.int32)
+        rv = torch.zeros(max(sc, 1), dtype=torch.int32)
         _check(lib().sekv_cache_copy_group(self.handle, layer, kv_head, _ptr(kb), _ptr(vb),
-                                           _ptr(sm), _ptr(rk)))
-        return kb[:sc], vb[:sc], sm[:, :sc].contiguous() if sc else sm[:, :0], rk[:sc]
+                                           _ptr(sm), _ptr(rk), _ptr(rv)))
+        return kb[:sc], vb[:sc], sm[:, :sc].contiguous() if sc else sm[:, :0], rk[:sc], rv[:sc]
 
     def factors(self, layer: int, kv_head: int, span: int, kv: int, rank: int, n: int):
         u = torch.zeros(n, rank, dtype=torch.float32)
@@ -372,15 +374,19 @@ def sekv_cap_budget(cache: Cache, route: RouteBuffers, budget_tokens: int, strea
                                  _stream(stream)))
 
 
-def sekv_apply_gates(cache: Cache, gates: torch.Tensor, eps: float, stream=None) -> None:
-    """Soft-gate the cache's factors (Eq. 8); gates [L][Hkv][S_c][max_rank]
-    float32 on the device.  Refreshes ``cache.info``."""
-    _need(gates, "gates", torch.float32)
+def sekv_apply_gates(cache: Cache, key_gates: torch.Tensor, value_gates: torch.Tensor,
+                     eps: float, stream=None) -> None:
+    """Soft-gate the cache's key factors with ``key_gates`` and its value
+    factors with ``value_gates`` (Eq. 8), each [L][Hkv][S_c][max_rank] float32
+    on the device.  Refreshes ``cache.info``."""
     c = cache.cfg
     shape = (c.n_layers, c.n_kv_heads, cache.info.n_compressed, c.max_rank)
-    if tuple(gates.shape) != shape:
-        raise ValueError(f"gates must be {shape}")
-    _check(lib().sekv_apply_gates(cache.handle, _ptr(gates), float(eps), _stream(stream)))
+    for name, g in (("key_gates", key_gates), ("value_gates", value_gates)):
+        _need(g, name, torch.float32)
+        if tuple(g.shape) != shape:
+            raise ValueError(f"{name} must be {shape}")
+    _check(lib().sekv_apply_gates(cache.handle, _ptr(key_gates), _ptr(value_gates), float(eps),
+                                  _stream(stream)))
     info = SekvCacheInfo()
     _check(lib().sekv_cache_info_get(cache.handle, ctypes.byref(info)))
     cache.info = info

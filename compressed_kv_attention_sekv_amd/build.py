@@ -26,16 +26,29 @@ FLAGS = [
 ]
 
 
+def _jobs() -> int:
+    n = os.environ.get("MAX_JOBS")
+    return max(1, min(len(SOURCES), int(n) if n and n.isdigit() else (os.cpu_count() or 1)))
+
+
 def build(verbose: bool = False) -> str:
+    """Compile every source (in parallel, one hipcc per file) and link."""
+    from concurrent.futures import ThreadPoolExecutor
     os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = []
+    cmds, objs = [], []
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmds.append([HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+
+    def compile_one(cmd):
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
-        objs.append(obj)
+
+    with ThreadPoolExecutor(max_workers=_jobs()) as ex:
+        for f in [ex.submit(compile_one, c) for c in cmds]:
+            f.result()
     tmp = OUT + ".tmp"
     cmd = [HIPCC, "-shared", "--offload-arch=gfx950", "-fPIC", *objs, "-o", tmp]
     if verbose:

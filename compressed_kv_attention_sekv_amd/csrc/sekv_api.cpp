@@ -278,10 +278,10 @@ static sekv_status build_impl(const sekv_config* cfg, int32_t n_tokens, const fl
     for (int g = 0; g < Hkv; ++g)
       for (int j = 0; j < sc; ++j) {
         const size_t idx = ((size_t)l * Hkv + g) * sc + j;
-        const int rr = c->h_rank[idx], nn = c->h_clen[j];
+        const FactorView fv = FactorView::packed(c->h_rank[idx], c->h_clen[j]);
         c->h_fac_off[idx] = off;
-        off += FactorView(rr, nn).block_floats();
-        fbytes += 8ull * rr * (uint64_t)(nn + kHeadDim + 1);
+        off += fv.block_floats();
+        fbytes += fv.alg_bytes();
       }
     stage_max = std::max(stage_max, off - c->layer_base[l]);
   }
@@ -433,7 +433,7 @@ sekv_status sekv_cache_copy_spans(const sekv_cache* c, int32_t* anchors, int32_t
 }
 
 sekv_status sekv_cache_copy_group(const sekv_cache* c, int32_t layer, int32_t kv_head, void* kbar,
-                                  void* vbar, void* summary, int32_t* rank) {
+                                  void* vbar, void* summary, int32_t* rank_k, int32_t* rank_v) {
   if (!c) return fail(SEKV_ERR_INVALID, "cache is NULL");
   if (layer < 0 || layer >= c->cfg.n_layers || kv_head < 0 || kv_head >= c->cfg.n_kv_heads)
     return fail(SEKV_ERR_INVALID, "layer %d / kv_head %d out of range", layer, kv_head);
@@ -452,7 +452,10 @@ sekv_status sekv_cache_copy_group(const sekv_cache* c, int32_t layer, int32_t kv
     SEKV_HIP(hipMemcpy(summary, (const char*)c->summ + h0 * sc * dr * eb, (size_t)G * sc * dr * eb,
                        hipMemcpyDeviceToHost));
   }
-  if (rank) std::memcpy(rank, c->h_rank.data() + lg * sc, (size_t)sc * 4);
+  for (int j = 0; j < sc; ++j) {
+    if (rank_k) rank_k[j] = rank_of(c->h_rank[lg * sc + j], 0);
+    if (rank_v) rank_v[j] = rank_of(c->h_rank[lg * sc + j], 1);
+  }
   return SEKV_OK;
 }
 
@@ -463,8 +466,9 @@ sekv_status sekv_cache_copy_factors(const sekv_cache* c, int32_t layer, int32_t 
       span < 0 || span >= c->sc || (kv != 0 && kv != 1))
     return fail(SEKV_ERR_INVALID, "layer/kv_head/span/kv out of range");
   const size_t idx = ((size_t)layer * c->cfg.n_kv_heads + kv_head) * c->sc + span;
-  const int r = c->h_rank[idx], n = c->h_clen[span];
-  const FactorView fv(r, n);
+  const int n = c->h_clen[span];
+  const FactorView fv = FactorView::packed(c->h_rank[idx], n);
+  const int r = fv.r(kv), r4 = fv.r4(kv);
   std::vector<float> blk(fv.block_floats());
   const float* src = (c->cfg.factor_tier == SEKV_TIER_DEVICE ? c->pool_dev : c->pool_host) +
                      c->h_fac_off[idx];
@@ -474,7 +478,7 @@ sekv_status sekv_cache_copy_factors(const sekv_cache* c, int32_t layer, int32_t 
     std::memcpy(blk.data(), src, blk.size() * 4);
   if (u)
     for (int t = 0; t < n; ++t)
-      for (int i = 0; i < r; ++i) u[(size_t)t * r + i] = blk[fv.u(kv) + (size_t)t * fv.r4 + i];
+      for (int i = 0; i < r; ++i) u[(size_t)t * r + i] = blk[fv.u(kv) + (size_t)t * r4 + i];
   if (sigma)
     for (int i = 0; i < r; ++i) sigma[i] = blk[fv.sigma(kv) + i];
   if (vt) std::memcpy(vt, blk.data() + fv.vt(kv), (size_t)r * kHeadDim * 4);
@@ -674,9 +678,10 @@ sekv_status sekv_cap_budget(const sekv_cache* c, const sekv_route_out* route,
   return SEKV_OK;
 }
 
-sekv_status sekv_apply_gates(sekv_cache* c, const float* gates_dev, float eps,
-                             hipStream_t st) {
-  if (!c || !gates_dev) return fail(SEKV_ERR_INVALID, "cache and gates must be non-NULL");
+sekv_status sekv_apply_gates(sekv_cache* c, const float* key_gates_dev,
+                             const float* value_gates_dev, float eps, hipStream_t st) {
+  if (!c || !key_gates_dev || !value_gates_dev)
+    return fail(SEKV_ERR_INVALID, "cache, key gates and value gates must be non-NULL");
   if (!std::isfinite(eps)) return fail(SEKV_ERR_INVALID, "eps must be finite");
   if (c->cfg.factor_tier != SEKV_TIER_DEVICE)
     return fail(SEKV_ERR_UNSUPPORTED, "soft gates repack the device factor pool; this cache keeps "
@@ -684,12 +689,16 @@ sekv_status sekv_apply_gates(sekv_cache* c, const float* gates_dev, float eps,
   const int L = c->cfg.n_layers, Hkv = c->cfg.n_kv_heads, sc = c->sc, R = c->cfg.max_rank;
   if (sc == 0) return SEKV_OK;
   const size_t nb = (size_t)L * Hkv * sc;
-  std::vector<float> hg(nb * R);
-  SEKV_HIP(hipMemcpyAsync(hg.data(), gates_dev, hg.size() * 4, hipMemcpyDeviceToHost, st));
+  std::vector<float> hg[2];
+  for (int kv = 0; kv < 2; ++kv) {
+    hg[kv].resize(nb * R);
+    SEKV_HIP(hipMemcpyAsync(hg[kv].data(), kv ? value_gates_dev : key_gates_dev,
+                            hg[kv].size() * 4, hipMemcpyDeviceToHost, st));
+  }
   SEKV_HIP(hipStreamSynchronize(st));
-  // which components stay: gate >= eps, at least one (the largest gate, the
-  // lowest index on ties); the new pool keeps the layout of the old one
-  std::vector<uint8_t> kept(nb * R, 0);
+  // which components stay, per matrix: gate >= eps, at least one (the largest
+  // gate, the lowest index on ties); the new pool keeps the layout of the old one
+  std::vector<uint8_t> kept(nb * 2 * R, 0);
   std::vector<int32_t> nr(nb);
   std::vector<uint64_t> noff(nb), nbase(L + 1, 0);
   uint64_t off = 0, fbytes = 0;
@@ -698,24 +707,31 @@ sekv_status sekv_apply_gates(sekv_cache* c, const float* gates_dev, float eps,
     for (int g = 0; g < Hkv; ++g)
       for (int j = 0; j < sc; ++j) {
         const size_t idx = ((size_t)l * Hkv + g) * sc + j;
-        const int r = c->h_rank[idx], n = c->h_clen[j];
-        const float* gg = &hg[idx * R];
-        int k = 0, best = 0;
-        for (int i = 0; i < r; ++i) {
-          if (!(gg[i] >= 0.f && gg[i] <= 1.f))
-            return fail(SEKV_ERR_INVALID, "gate %d of (layer %d, KV head %d, span %d) is %g, "
-                        "outside [0, 1]", i, l, g, j, (double)gg[i]);
-          if (gg[i] >= eps) kept[idx * R + k++] = (uint8_t)i;
-          if (gg[i] > gg[best]) best = i;
+        const int n = c->h_clen[j];
+        int nk[2];
+        for (int kv = 0; kv < 2; ++kv) {
+          const int r = rank_of(c->h_rank[idx], kv);
+          const float* gg = &hg[kv][idx * R];
+          uint8_t* kp = &kept[(idx * 2 + kv) * R];
+          int k = 0, best = 0;
+          for (int i = 0; i < r; ++i) {
+            if (!(gg[i] >= 0.f && gg[i] <= 1.f))
+              return fail(SEKV_ERR_INVALID, "%s gate %d of (layer %d, KV head %d, span %d) is %g, "
+                          "outside [0, 1]", kv ? "value" : "key", i, l, g, j, (double)gg[i]);
+            if (gg[i] >= eps) kp[k++] = (uint8_t)i;
+            if (gg[i] > gg[best]) best = i;
+          }
+          if (k == 0) {
+            kp[0] = (uint8_t)best;
+            k = 1;
+          }
+          nk[kv] = k;
         }
-        if (k == 0) {
-          kept[idx * R] = (uint8_t)best;
-          k = 1;
-        }
-        nr[idx] = k;
+        const FactorView fv(nk[0], nk[1], n);
+        nr[idx] = pack_ranks(nk[0], nk[1]);
         noff[idx] = off;
-        off += FactorView(k, n).block_floats();
-        fbytes += 8ull * k * (uint64_t)(n + kHeadDim + 1);
+        off += fv.block_floats();
+        fbytes += fv.alg_bytes();
       }
   }
   nbase[L] = off;
@@ -734,7 +750,7 @@ sekv_status sekv_apply_gates(sekv_cache* c, const float* gates_dev, float eps,
   SEKV_HIP(hipMemcpyAsync(d_off, noff.data(), nb * 8, hipMemcpyHostToDevice, st));
   SEKV_HIP(hipMemsetAsync(npool, 0, (size_t)off * 4, st));
   SEKV_HIP(launch_gate_repack(c->pool_dev, c->fac_off, c->rank, npool, d_off, d_rank, d_kept,
-                              gates_dev, c->clen, sc, R, nb, st));
+                              key_gates_dev, value_gates_dev, c->clen, sc, R, nb, st));
   SEKV_HIP(hipMemcpyAsync(c->rank, d_rank, nb * 4, hipMemcpyDeviceToDevice, st));
   SEKV_HIP(hipMemcpyAsync(c->fac_off, d_off, nb * 8, hipMemcpyDeviceToDevice, st));
   SEKV_HIP(hipStreamSynchronize(st));

@@ -203,7 +203,7 @@ __global__ void span_rank_kernel(const int32_t* rank_by_pos, const int32_t* csta
   r = min(r, clen[j]);
   r = min(r, kHeadDim);
   r = min(r, max_rank);
-  rank[(size_t)lg * sc + j] = r;
+  rank[(size_t)lg * sc + j] = pack_ranks(r, r);   // keys and values alike
 }
 
 hipError_t launch_span_rank(const int32_t* rank_by_pos, const int32_t* cstart,
@@ -345,7 +345,8 @@ __global__ __launch_bounds__(kSvdThreads) void span_svd_kernel(
   const int j = span_ids[blockIdx.x];
   const int lg = blockIdx.y;
   const int b = cstart[j], n = clen[j];
-  const int r = rank[(size_t)lg * sc + j];
+  const int32_t ranks = rank[(size_t)lg * sc + j];
+  const int r = rank_of(ranks, which);
   const bool small = n <= kHeadDim;
   const int m = small ? n : kHeadDim;
   const int me = m + (m & 1);
@@ -479,7 +480,8 @@ __global__ __launch_bounds__(kSvdThreads) void span_svd_kernel(
   const double lmax = sh_lmax;
 
   // ---- write the factors ---------------------------------------------------
-  const FactorView fv(r, n);
+  const FactorView fv = FactorView::packed(ranks, n);
+  const int r4 = fv.r4(which);
   float* blk = pool + fac_off[(size_t)lg * sc + j];
   float* vt = blk + fv.vt(which);
   float* u = blk + fv.u(which);
@@ -488,12 +490,12 @@ __global__ __launch_bounds__(kSvdThreads) void span_svd_kernel(
     const double lam = nrm[order[i]];
     return lam > 0.0 && lam > lmax * 1e-24;
   };
-  for (int i = tid; i < fv.r4; i += kSvdThreads)
+  for (int i = tid; i < r4; i += kSvdThreads)
     sg[i] = (i < r && live(i)) ? (float)sqrt(nrm[order[i]]) : 0.f;
   if (small) {
     // u_i = A[:,p] / lambda (token space); v_i = X^T u_i / sigma
-    for (int idx = tid; idx < n * fv.r4; idx += kSvdThreads) {
-      const int t = idx / fv.r4, i = idx % fv.r4;
+    for (int idx = tid; idx < n * r4; idx += kSvdThreads) {
+      const int t = idx / r4, i = idx % r4;
       float val = 0.f;
       if (i < r && live(i)) val = (float)(A[(size_t)order[i] * ld + t] / nrm[order[i]]);
       u[idx] = val;
@@ -518,8 +520,8 @@ __global__ __launch_bounds__(kSvdThreads) void span_svd_kernel(
       if (live(i)) val = (float)(A[(size_t)order[i] * ld + c] / nrm[order[i]]);
       vt[idx] = val;
     }
-    for (int idx = tid; idx < n * fv.r4; idx += kSvdThreads) {
-      const int t = idx / fv.r4, i = idx % fv.r4;
+    for (int idx = tid; idx < n * r4; idx += kSvdThreads) {
+      const int t = idx / r4, i = idx % r4;
       float val = 0.f;
       if (i < r && live(i)) {
         const double lam = nrm[order[i]];

@@ -176,7 +176,7 @@ template <int G>
 struct alignas(16) Smem {
   float qs[G][kHeadDim];           // query * 1/sqrt(d)
   uint64_t m_off[kChunk];          // factor block of span j0 + i, relative to the pool
-  int m_n[kChunk], m_r[kChunk];    // its length and retained rank
+  int m_n[kChunk], m_r[kChunk];    // its length and packed key and value ranks
   int bits[kChunk];                // heads of the group that zoom span j0 + i
   int zl[kChunk];                  // chunk-local ids of zoomed spans
   int nz;
@@ -364,12 +364,12 @@ __device__ __forceinline__ void rows_store(const RowState<T, G>& s, float (*acc)
 // into the wave's running state (zm, zl, za: lane holds dims 2 lane, 2 lane+1).
 // ---------------------------------------------------------------------------
 template <int G>
-__device__ __attribute__((always_inline)) void zoom_span(const float* __restrict__ blk, int n, int r, unsigned hm,
+__device__ __attribute__((always_inline)) void zoom_span(const float* __restrict__ blk, int n, int rk, int rv, unsigned hm,
                           const float (*qs)[kHeadDim], ZoomScratchAny<G>& zs, float* zm, float* zl,
                           float (*za)[2]) {
   const int lane = threadIdx.x & 63;
-  const FactorView fv(r, n);
-  const int r4 = fv.r4;
+  const FactorView fv(rk, rv, n);
+  const int rk4 = fv.r4(0), rv4 = fv.r4(1);
   const float* vk = blk + fv.vt(0);
   const float* uk = blk + fv.u(0);
   const float* sk = blk + fv.sigma(0);
@@ -380,12 +380,12 @@ __device__ __attribute__((always_inline)) void zoom_span(const float* __restrict
   // (A) b_h[i] = sigma_K[i] * (V_K^T q_h)[i]: 8 lanes per component, 16 dims per lane
   {
     const int part = lane & 7, ci = lane >> 3;
-    for (int i0 = 0; i0 < r; i0 += 8) {
+    for (int i0 = 0; i0 < rk; i0 += 8) {
       const int i = i0 + ci;
       float pa[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) pa[h] = 0.f;
-      if (i < r) {
+      if (i < rk) {
         const float4* row = (const float4*)(vk + (size_t)i * kHeadDim + part * 16);
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
@@ -401,18 +401,18 @@ __device__ __attribute__((always_inline)) void zoom_span(const float* __restrict
       for (int h = 0; h < G; ++h) {
         pa[h] = group_sum<8>(pa[h]);
       }
-      if (part == 0 && i < r) {
+      if (part == 0 && i < rk) {
         const float sg = sk[i];
 #pragma unroll
         for (int h = 0; h < G; ++h) zs.bsh[h][i] = pa[h] * sg;
       }
     }
     // padding components and the value-side coefficients start at zero
-    for (int idx = lane; idx < G * r4; idx += 64) {
-      const int h = idx / r4, i = idx % r4;
-      if (i >= r) zs.bsh[h][i] = 0.f;
-      zs.csh[h][i] = 0.f;
+    for (int idx = lane; idx < G * rk4; idx += 64) {
+      const int h = idx / rk4, i = idx % rk4;
+      if (i >= rk) zs.bsh[h][i] = 0.f;
     }
+    for (int idx = lane; idx < G * rv4; idx += 64) zs.csh[idx / rv4][idx % rv4] = 0.f;
   }
   __builtin_amdgcn_wave_barrier();
 
@@ -429,8 +429,8 @@ __device__ __attribute__((always_inline)) void zoom_span(const float* __restrict
 #pragma unroll
     for (int h = 0; h < G; ++h) e[h] = 0.f;
     if (t < n) {
-      const float4* ur = (const float4*)(uk + (size_t)t * r4);
-      for (int i4 = 0; i4 < r4 / 4; ++i4) {
+      const float4* ur = (const float4*)(uk + (size_t)t * rk4);
+      for (int i4 = 0; i4 < rk4 / 4; ++i4) {
         const float4 u = ur[i4];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -454,16 +454,16 @@ __device__ __attribute__((always_inline)) void zoom_span(const float* __restrict
     __builtin_amdgcn_wave_barrier();
     const int tn = min(64, n - t0);
     const int i4 = lane & 7, ts = lane >> 3;
-    for (int cb = 0; cb < r4; cb += 32) {
+    for (int cb = 0; cb < rv4; cb += 32) {
       const int i = cb + 4 * i4;
       float c4[G][4];
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int q = 0; q < 4; ++q) c4[h][q] = 0.f;
-      if (i < r4) {
+      if (i < rv4) {
         for (int k = ts; k < tn; k += 8) {
-          const float4 u = *(const float4*)(uv + (size_t)(t0 + k) * r4 + i);
+          const float4 u = *(const float4*)(uv + (size_t)(t0 + k) * rv4 + i);
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             const float p = zs.psh[k][h];
@@ -481,7 +481,7 @@ __device__ __attribute__((always_inline)) void zoom_span(const float* __restrict
           c4[h][q] += dpp<kDppRor8>(c4[h][q]);
           c4[h][q] = xor32_sum(xor16_sum(c4[h][q]));
         }
-      if (ts == 0 && i < r4) {
+      if (ts == 0 && i < rv4) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -495,7 +495,7 @@ __device__ __attribute__((always_inline)) void zoom_span(const float* __restrict
   float a[G][2];
 #pragma unroll
   for (int h = 0; h < G; ++h) a[h][0] = a[h][1] = 0.f;
-  for (int i = 0; i < r; ++i) {
+  for (int i = 0; i < rv; ++i) {
     const float2 x = *(const float2*)(vv + (size_t)i * kHeadDim + 2 * lane);
     const float sg = sv[i];
 #pragma unroll
@@ -536,7 +536,7 @@ __device__ __attribute__((always_inline)) void zoom_span(const float* __restrict
 // ---------------------------------------------------------------------------
 struct SpanRef {        // a zoomed span, the same on every lane of the wave
   const float* blk;     // its factor block
-  int n, r;
+  int n, rk, rv;        // length, ranks of its key and value factors
   unsigned hm;          // heads of the group that zoom it
 };
 
@@ -546,18 +546,22 @@ __device__ __forceinline__ SpanRef span_ref(const Smem<G>& s, const float* pool,
   jl = uniform(jl);
   sp.blk = pool + uniform64(s.m_off[jl]);
   sp.n = uniform(s.m_n[jl]);
-  sp.r = uniform(s.m_r[jl]);
+  const int32_t rr = uniform(s.m_r[jl]);
+  sp.rk = rank_of(rr, 0);
+  sp.rv = rank_of(rr, 1);
   sp.hm = (unsigned)uniform(s.bits[jl]);
   return sp;
 }
 
-// A span's V_K (r rows of d floats at the start of its block) and its sigma_K
-// and sigma_V into a stage: SR rows, then 64 floats of sigma_K and 64 of
-// sigma_V (entry i holds sigma[min(i, r4 - 1)]; entries r .. r4 - 1 are the
-// block's zero padding).  Each row instruction moves 1 KB (two rows) straight
-// from memory to LDS, lane l writing bytes [16 l, 16 l + 16) of it; always
-// SR / 2 of them, those past the span's rows copying its last two rows again
-// (an odd r also moves the 512 bytes after V_K, still inside the block).
+// A span's V_K (rK rows of d floats at the start of its block) and its
+// sigma_K and sigma_V into a stage: SR rows, then 64 floats of sigma_K and 64
+// of sigma_V (entry i holds sigma[min(i, r4 - 1)] with r4 of that matrix;
+// entries r .. r4 - 1 are the block's zero padding).  Each row instruction
+// moves 1 KB (two rows) straight from memory to LDS, lane l writing bytes
+// [16 l, 16 l + 16) of it; always SR / 2 of them, those past the span's rows
+// copying its last two rows again (an odd rK also moves the 512 bytes after
+// V_K, still inside the block: the value half that follows holds at least
+// one row of d floats).
 //
 // The DMA instructions are written as inline assembly.  The compiler then
 // does not count them among the wave's outstanding loads: its own waits for
@@ -599,13 +603,12 @@ __device__ __forceinline__ void dma_x1(const float* g, const float* lds) {
 template <int SR>
 __device__ __forceinline__ void stage_vk(const SpanRef& sp, float* stage) {
   const int lane = threadIdx.x & 63;
-  const int nk = (sp.r + 1) >> 1;
-  const FactorView fv(sp.r, sp.n);
+  const int nk = (sp.rk + 1) >> 1;
+  const FactorView fv(sp.rk, sp.rv, sp.n);
 #pragma unroll
   for (int k = 0; k < SR / 2; ++k) dma_x4(sp.blk + min(k, nk - 1) * 256 + lane * 4, stage + k * 256);
-  const int si = min(lane, fv.r4 - 1);
-  dma_x1(sp.blk + fv.sigma(0) + si, stage + SR * kHeadDim);
-  dma_x1(sp.blk + fv.sigma(1) + si, stage + SR * kHeadDim + 64);
+  dma_x1(sp.blk + fv.sigma(0) + min(lane, fv.r4(0) - 1), stage + SR * kHeadDim);
+  dma_x1(sp.blk + fv.sigma(1) + min(lane, fv.r4(1) - 1), stage + SR * kHeadDim + 64);
 }
 
 // LDS reads of this wave complete before the stage is overwritten by DMA
@@ -625,8 +628,8 @@ __device__ __forceinline__ void load_u_tile(const float* u, int n, int r4, int t
 // what a wave prefetches of its next span into registers: the first rows of
 // U_K (always 8 loads, so the waits that count them stay exact)
 __device__ __forceinline__ void prefetch_span(const SpanRef& sp, float4 (&ub)[8]) {
-  const FactorView fv(sp.r, sp.n);
-  load_u_tile<8>(sp.blk + fv.u(0), sp.n, fv.r4, 0, ub);
+  const FactorView fv(sp.rk, sp.rv, sp.n);
+  load_u_tile<8>(sp.blk + fv.u(0), sp.n, fv.r4(0), 0, ub);
 }
 
 // Keep the loads issued so far ahead of everything after (the waits below
@@ -690,10 +693,11 @@ __device__ __forceinline__ void reduce_scatter(float p, const float4 (&u)[RC / 4
   }
 }
 
-// One span of the pipeline, for ranks up to RC (16 or 32): loads are sized
-// to RC (U rows of RC / 4 16-byte pieces, V_V in RC / 2 16-byte loads of two
-// rows each).  On entry ub holds the span's first rows of U_K and, if
-// r <= SR, the stage holds (or is receiving) its V_K; on return ub holds the
+// One span of the pipeline, for key and value ranks up to RC (16 or 32):
+// loads are sized to RC (U rows of RC / 4 16-byte pieces, V_V in RC / 2
+// 16-byte loads of two rows each), whatever the two ranks below it.  On entry
+// ub holds the span's first rows of U_K and, if rK <= SR, the stage holds (or
+// is receiving) its V_K; on return ub holds the
 // first rows of U_K of `nxp` (8 loads, whatever its rank) and the stage
 // receives the V_K of `nxs` (the next span, or a stand-in when it has none of
 // the kind).
@@ -718,42 +722,42 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
   constexpr int VK = RC / 2;          // 16-byte loads of V_V
   constexpr int GL = 64 / (RC / 4);   // lanes holding each 4 components of c
   const int lane = threadIdx.x & 63;
-  const int n = cu.n, r = cu.r;
+  const int n = cu.n, rk = cu.rk, rv = cu.rv;
   const unsigned hm = cu.hm;
-  const FactorView fv(r, n);
-  const int r4 = fv.r4, nq = r4 / 4;
+  const FactorView fv(rk, rv, n);
+  const int rk4 = fv.r4(0), rv4 = fv.r4(1), nqk = rk4 / 4;
   const float* vk = cu.blk + fv.vt(0);
   const float* vv = cu.blk + fv.vt(1);
   const int part = lane & 7, ci = lane >> 3;   // (A): component ci + 8 p, dims 16 part ..
   const int half = lane >> 5, dq = lane & 31;  // (D): rows 2 k + half, dims 4 dq ..
   const int cg = lane / GL;                    // after (C): components 4 cg ..
-  const bool staged = SR >= 32 || r <= SR;     // always, when the stage holds 32 rows
+  const bool staged = SR >= 32 || rk <= SR;    // always, when the stage holds 32 rows
 
   // this span's own loads, needed last: the first rows of U_V, all of V_V
   float4 uc[UQ];
-  load_u_tile<UQ>(cu.blk + fv.u(1), n, r4, 0, uc);
+  load_u_tile<UQ>(cu.blk + fv.u(1), n, rv4, 0, uc);
   float4 vd[VK];
 #pragma unroll
   for (int k = 0; k < VK; ++k)
-    vd[k] = *(const float4*)(vv + (size_t)min(2 * k + half, r - 1) * kHeadDim + 4 * dq);
+    vd[k] = *(const float4*)(vv + (size_t)min(2 * k + half, rv - 1) * kHeadDim + 4 * dq);
   float4 va[4][4];   // V_K from memory, only when it is not staged
   float sgm[4];      // and then sigma_K and sigma_V too (the stage holds another span's)
   float4 svm = make_float4(0.f, 0.f, 0.f, 0.f);
   if (!staged) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const int i = min(ci + 8 * p, r - 1);
+      const int i = min(ci + 8 * p, rk - 1);
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4)
         va[p][c4] = *(const float4*)(vk + (size_t)i * kHeadDim + part * 16 + c4 * 4);
     }
-    // entries clamped to the block's r4 (as the stage copy is)
+    // entries clamped to each matrix's r4 (as the stage copy is)
     const float* sk = cu.blk + fv.sigma(0);
     const float* sv = cu.blk + fv.sigma(1);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) sgm[p] = sk[min(ci + 8 * p, r4 - 1)];
-    svm = make_float4(sv[min(4 * cg, r4 - 1)], sv[min(4 * cg + 1, r4 - 1)],
-                      sv[min(4 * cg + 2, r4 - 1)], sv[min(4 * cg + 3, r4 - 1)]);
+    for (int p = 0; p < 4; ++p) sgm[p] = sk[min(ci + 8 * p, rk4 - 1)];
+    svm = make_float4(sv[min(4 * cg, rv4 - 1)], sv[min(4 * cg + 1, rv4 - 1)],
+                      sv[min(4 * cg + 2, rv4 - 1)], sv[min(4 * cg + 3, rv4 - 1)]);
   }
 
   // sigma_K of the lane's components in (A) (ci + 8 p) and sigma_V of its
@@ -768,7 +772,7 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
   for (int p = 0; p < 4; ++p) sg[p] = staged ? stage[SR * kHeadDim + ci + 8 * p] : sgm[p];
   const float4 svg = staged ? *(const float4*)(stage + SR * kHeadDim + 64 + 4 * cg) : svm;
 
-  // (A) components at or past r get exactly 0 (a stage row past r may hold
+  // (A) components at or past rK get exactly 0 (a stage row past rK may hold
   // anything)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -777,7 +781,7 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
     for (int p = 0; p < RC / 8; ++p) {
       const int i = ci + 8 * p;
       float acc = 0.f;
-      if (8 * p < r) {
+      if (8 * p < rk) {
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
           const float4 x =
@@ -787,7 +791,7 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
         }
         acc = group_sum<8>(acc);
       }
-      if (part == 0) scr[h][i] = i < r ? acc * sg[p] : 0.f;
+      if (part == 0) scr[h][i] = i < rk ? acc * sg[p] : 0.f;
     }
   }
   // the stage is free: the next span's V_K goes in while this one proceeds
@@ -816,7 +820,7 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
 #pragma unroll
       for (int q = 0; q < UQ; ++q) {
         const float4 b = *(const float4*)&scr[h][4 * q];   // the same address on every lane
-        if (q < nq) acc += ub[q].x * b.x + ub[q].y * b.y + ub[q].z * b.z + ub[q].w * b.w;
+        if (q < nqk) acc += ub[q].x * b.x + ub[q].y * b.y + ub[q].z * b.z + ub[q].w * b.w;
       }
       if (lane < tn) e[h] = acc;
     }
@@ -845,11 +849,11 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
     float e[G];
     scores(t0, e);
     issue_fence();
-    load_u_tile<UQ>(cu.blk + fv.u(0), n, r4, t0 + 64, ub);
+    load_u_tile<UQ>(cu.blk + fv.u(0), n, rk4, t0 + 64, ub);
     issue_fence();
     accumulate(e);
     issue_fence();
-    load_u_tile<UQ>(cu.blk + fv.u(1), n, r4, t0 + 64, uc);
+    load_u_tile<UQ>(cu.blk + fv.u(1), n, rv4, t0 + 64, uc);
     issue_fence();
   }
   // the last 64: then what the next span needs first
@@ -862,8 +866,9 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
     accumulate(e);
   }
 
-  // (D) a_h[dim] = sum_i V_V[i][dim] (sigma_V c_h)[i]; rows past r hold a
-  // clamped copy of row r - 1 and get weight 0
+  // (D) a_h[dim] = sum_i V_V[i][dim] (sigma_V c_h)[i]; rows past rV hold a
+  // clamped copy of row rV - 1 and get weight 0 (so do components of c past
+  // rV, which the clamped U_V pieces leave arbitrary)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     if (!((hm >> h) & 1u)) continue;
@@ -873,9 +878,9 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
 #pragma unroll
     for (int k = 0; k < VK; ++k) {
       const int i0 = 2 * k, i1 = 2 * k + 1;
-      if (i0 >= r) continue;
+      if (i0 >= rv) continue;
       const float w0 = readlane(cs[i0 & 3], GL * (i0 >> 2));
-      const float w1 = i1 < r ? readlane(cs[i1 & 3], GL * (i1 >> 2)) : 0.f;
+      const float w1 = i1 < rv ? readlane(cs[i1 & 3], GL * (i1 >> 2)) : 0.f;
       const float w = half ? w1 : w0;
       a[0] += w * vd[k].x;
       a[1] += w * vd[k].y;
@@ -1278,21 +1283,21 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
   // moves into the wave's stage under the rest of the rows phase (issued once
   // the first rows have arrived, so no wait for them also waits for it) ------
   constexpr int SR = stage_rows<G>();
-  const SpanRef zero{a.zero_block, 1, 1, 0u};
+  const SpanRef zero{a.zero_block, 1, 1, 1, 0u};
   SpanRef first = zero;   // the wave's first zoomed span of rank <= 32
   if (zoom && nj > 0) {
     unsigned zb = (unsigned)__ballot(lane < nj && s.bits[lane] != 0);
     for (int k = 0; k < wid; ++k) zb &= zb - 1u;   // the wid-th zoomed span on
     while (zb != 0u) {
       const int jl = __ffs(zb) - 1;
-      if (s.m_r[jl] <= 32) {
+      if (rank_max(s.m_r[jl]) <= 32) {
         first = span_ref(s, a.pool, jl);
         break;
       }
       for (int k = 0; k < kWaves; ++k) zb &= zb - 1u;   // the wave's next one
     }
   }
-  if (first.r > SR) first = zero;
+  if (first.rk > SR) first = zero;
 
   // ---- full-resolution rows and coarse entries: each wave's state ----------
   if (dense) {
@@ -1332,7 +1337,7 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
     const int nz = s.nz;
     // the wave's spans u = wid, wid + kWaves, ... of rank <= 32, pipelined
     auto next_small = [&](int u) {
-      while (u < nz && s.m_r[s.zl[u]] > 32) u += kWaves;
+      while (u < nz && rank_max(s.m_r[s.zl[u]]) > 32) u += kWaves;
       return uniform(u);
     };
     int u = next_small(wid);
@@ -1347,10 +1352,10 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
         // stand-ins when there is no next span: this one again (its V_K only
         // if it is staged, else the zeros)
         const SpanRef nxp = has_nx ? nx : cu;
-        const SpanRef nxs = has_nx && nx.r <= SR ? nx : (cu.r <= SR ? cu : zero);
+        const SpanRef nxs = has_nx && nx.rk <= SR ? nx : (cu.rk <= SR ? cu : zero);
         // the span's scratch: the wave's state area (idle while its spans run)
         float (*scr)[kHeadDim] = s.w[wid].st.acc;
-        if (cu.r <= 16)
+        if (cu.rk <= 16 && cu.rv <= 16)
           zoom_span32<G, SR, 16>(cu, nxp, nxs, ub, stage, scr, s.qs, zm, zl, za);
         else
           zoom_span32<G, SR, 32>(cu, nxp, nxs, ub, stage, scr, s.qs, zm, zl, za);
@@ -1362,10 +1367,10 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
     // then those of rank > 32, with the stage as scratch once its DMA is done
     for (u = wid; u < nz; u += kWaves) {
       const int jl = uniform(s.zl[u]);
-      if (s.m_r[jl] <= 32) continue;
+      if (rank_max(s.m_r[jl]) <= 32) continue;
       const SpanRef sp = span_ref(s, a.pool, jl);
       __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-      zoom_span<G>(sp.blk, sp.n, sp.r, sp.hm, s.qs,
+      zoom_span<G>(sp.blk, sp.n, sp.rk, sp.rv, sp.hm, s.qs,
                    *reinterpret_cast<ZoomScratchAny<G>*>(stage), zm, zl, za);
     }
   }
@@ -1560,7 +1565,7 @@ __global__ __launch_bounds__(256) void fetch_gather_kernel(
   const int nu = ucount[g];
   for (int u = zs; u < nu; u += kFetchSlots) {
     const int j = ulist[(size_t)g * sc + u];
-    const FactorView fv(rank[(size_t)g * sc + j], clen[j]);
+    const FactorView fv = FactorView::packed(rank[(size_t)g * sc + j], clen[j]);
     const uint64_t off = fac_off[(size_t)g * sc + j];
     const uint4* src = (const uint4*)(host + off);
     uint4* dst = (uint4*)(stage + (off - layer_base));

@@ -13,26 +13,51 @@ constexpr int kMaxRouteDim = 64;  // dr
 
 // ---------------------------------------------------------------------------
 // Factor block of one (layer, KV head, compressed span), float32, in the pool:
-//   [ VKt r x d | UK n x r4 | sK r4 | VVt r x d | UV n x r4 | sV r4 ]
-// VKt/VVt hold the right singular vectors as rows; UK/UV hold the left
-// singular vectors token-major (row t is token t's r coefficients, padded to
-// r4 = r rounded up to 4), so one lane reads a token's whole row with 16-byte
-// loads and the rows of consecutive tokens are contiguous; sK/sV hold the
-// singular values.  Every sub-array starts on a 16-byte boundary and padding
-// entries are zero.  Blocks start on 256-byte boundaries.  Algorithmic size:
-// 8 r (n + d + 1) bytes.
+//   [ VKt rK x d | UK n x rK4 | sK rK4 | VVt rV x d | UV n x rV4 | sV rV4 ]
+// The key and value matrices of a span are factored separately and keep their
+// own ranks rK and rV (equal after the build; soft gates may make them
+// differ).  VKt/VVt hold the right singular vectors as rows; UK/UV hold the
+// left singular vectors token-major (row t is token t's coefficients, padded
+// to r4 = r rounded up to 4), so one lane reads a token's whole row with
+// 16-byte loads and the rows of consecutive tokens are contiguous; sK/sV hold
+// the singular values.  Every sub-array starts on a 16-byte boundary and
+// padding entries are zero.  Blocks start on 256-byte boundaries.
+// Algorithmic size: 4 (rK + rV) (n + d + 1) bytes.
+//
+// The rank table holds one int32 per block: rK in the low 16 bits, rV in the
+// high 16 bits.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int round4(int x) { return (x + 3) & ~3; }
+__host__ __device__ inline int32_t pack_ranks(int rk, int rv) {
+  return (int32_t)((uint32_t)rk | ((uint32_t)rv << 16));
+}
+// rank of the key (kv = 0) or value (kv = 1) factors of a packed entry
+__host__ __device__ inline int rank_of(int32_t packed, int kv) {
+  return kv ? (int)((uint32_t)packed >> 16) : (int)((uint32_t)packed & 0xffffu);
+}
+__host__ __device__ inline int rank_max(int32_t packed) {
+  const int a = rank_of(packed, 0), b = rank_of(packed, 1);
+  return a > b ? a : b;
+}
 
 struct FactorView {
-  int r, n, r4;
-  __host__ __device__ FactorView(int r_, int n_) : r(r_), n(n_), r4(round4(r_)) {}
-  __host__ __device__ int half() const { return r * kHeadDim + n * r4 + r4; }
-  __host__ __device__ int vt(int kv) const { return kv * half(); }
-  __host__ __device__ int u(int kv) const { return kv * half() + r * kHeadDim; }
-  __host__ __device__ int sigma(int kv) const { return kv * half() + r * kHeadDim + n * r4; }
+  int rk, rv, n;
+  __host__ __device__ FactorView(int rk_, int rv_, int n_) : rk(rk_), rv(rv_), n(n_) {}
+  __host__ __device__ static FactorView packed(int32_t ranks, int n_) {
+    return FactorView(rank_of(ranks, 0), rank_of(ranks, 1), n_);
+  }
+  __host__ __device__ int r(int kv) const { return kv ? rv : rk; }
+  __host__ __device__ int r4(int kv) const { return round4(r(kv)); }
+  __host__ __device__ int half(int kv) const { return r(kv) * kHeadDim + n * r4(kv) + r4(kv); }
+  __host__ __device__ int vt(int kv) const { return kv ? half(0) : 0; }
+  __host__ __device__ int u(int kv) const { return vt(kv) + r(kv) * kHeadDim; }
+  __host__ __device__ int sigma(int kv) const { return u(kv) + n * r4(kv); }
   __host__ __device__ uint64_t block_floats() const {
-    return (uint64_t)((2 * half() + 63) & ~63);
+    return (uint64_t)((half(0) + half(1) + 63) & ~63);
+  }
+  // algorithmic bytes of the block: 4 (rK + rV) (n + d + 1)
+  __host__ __device__ uint64_t alg_bytes() const {
+    return 4ull * (uint64_t)(rk + rv) * (uint64_t)(n + kHeadDim + 1);
   }
 };
 
@@ -169,7 +194,7 @@ struct LayerArgs {
   const void* kbar;        // [Hkv][S_c][d]
   const void* vbar;
   const int32_t* clen;     // [S_c]
-  const int32_t* rank;     // [Hkv][S_c]
+  const int32_t* rank;     // [Hkv][S_c] packed key and value ranks
   const uint64_t* fac_off; // [Hkv][S_c] float offsets
   const float* pool;       // factor blocks, addressed as pool + (fac_off - off_base)
   uint64_t off_base;
@@ -266,12 +291,13 @@ hipError_t launch_resident_fetch(const LayerGeom& g, int layer, const int32_t* u
                                  const float* host_pool_mapped, const ResidencyView& rv,
                                  uint64_t epoch, hipStream_t st);
 // soft gates: repack every (layer, KV head, span) block of the device pool
-// into a new pool with the kept components (gate-scaled sigma)
+// into a new pool with the kept components (gate-scaled sigma); kept is
+// [blocks][2][max_rank] (keys, then values), the gates [blocks][max_rank] each
 hipError_t launch_gate_repack(const float* old_pool, const uint64_t* old_off,
                               const int32_t* old_rank, float* new_pool, const uint64_t* new_off,
-                              const int32_t* new_rank, const uint8_t* kept, const float* gates,
-                              const int32_t* clen, int sc, int max_rank, uint64_t n_blocks,
-                              hipStream_t st);
+                              const int32_t* new_rank, const uint8_t* kept, const float* key_gates,
+                              const float* value_gates, const int32_t* clen, int sc, int max_rank,
+                              uint64_t n_blocks, hipStream_t st);
 hipError_t launch_fetch_gather(const LayerGeom& g, const int32_t* ulist, const int32_t* ucount,
                                const int32_t* clen, const int32_t* rank,
                                const uint64_t* fac_off, uint64_t layer_base,

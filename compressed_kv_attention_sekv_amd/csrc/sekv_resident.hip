@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void res_claim_kernel(
   const int nu = ucount[g];
   for (int u = blockIdx.x * 256 + threadIdx.x; u < nu; u += gridDim.x * 256) {
     const int j = ulist[(size_t)g * sc + u];
-    const FactorView fv(rank[(size_t)g * sc + j], clen[j]);
+    const FactorView fv = FactorView::packed(rank[(size_t)g * sc + j], clen[j]);
     if (fv.block_floats() > slot_floats) continue;
     const uint64_t key = ((uint64_t)layer * hkv + g) * (uint64_t)sc + j;
     uint64_t s1, s2;
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void res_fetch_kernel(
   const int nu = ucount[g];
   for (int u = blockIdx.x; u < nu; u += kResSlotsPerHead) {
     const int j = ulist[(size_t)g * sc + u];
-    const FactorView fv(rank[(size_t)g * sc + j], clen[j]);
+    const FactorView fv = FactorView::packed(rank[(size_t)g * sc + j], clen[j]);
     const uint64_t nfl = fv.block_floats();
     const uint64_t hoff = fac_off[(size_t)g * sc + j];
     const uint64_t key = ((uint64_t)layer * hkv + g) * (uint64_t)sc + j;
@@ -123,8 +123,7 @@ __global__ __launch_bounds__(256) void res_fetch_kernel(
     if (threadIdx.x == 0) {
       off_out[(size_t)g * sc + j] = dst_off;
       if (cached && !hit) tag[set] = (long long)key;
-      const unsigned long long bytes = 8ull * (unsigned long long)fv.r *
-                                       (unsigned long long)(fv.n + kHeadDim + 1);
+      const unsigned long long bytes = (unsigned long long)fv.alg_bytes();
       atomicAdd(&stats[hit ? 0 : 1], 1ull);
       atomicAdd(&stats[hit ? 2 : 3], bytes);
     }

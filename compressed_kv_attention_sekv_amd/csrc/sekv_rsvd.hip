@@ -181,7 +181,8 @@ __global__ __launch_bounds__(kRsThreads) void span_rsvd_kernel(
   const int j = span_ids[blockIdx.x];
   const int lg = blockIdx.y;
   const int b = cstart[j], n = clen[j];
-  const int r = rank[(size_t)lg * sc + j];
+  const int32_t ranks = rank[(size_t)lg * sc + j];
+  const int r = rank_of(ranks, which);
   const int k = min(kRsMaxK, (r + 8 + 1) & ~1);
   const T* X = x + ((size_t)lg * n_tokens + b) * kHeadDim;
 
@@ -292,15 +293,16 @@ __global__ __launch_bounds__(kRsThreads) void span_rsvd_kernel(
   };
 
   // ---- factors: sigma, u_i = Q w_i (token-major), v_i = B^T w_i / sigma -----
-  const FactorView fv(r, n);
+  const FactorView fv = FactorView::packed(ranks, n);
+  const int r4 = fv.r4(which);
   float* blk = pool + fac_off[(size_t)lg * sc + j];
   float* vt = blk + fv.vt(which);
   float* u = blk + fv.u(which);
   float* sg = blk + fv.sigma(which);
-  for (int i = tid; i < fv.r4; i += kRsThreads)
+  for (int i = tid; i < r4; i += kRsThreads)
     sg[i] = (i < r && live(i)) ? (float)sqrt(s.nrm[s.order[i]]) : 0.f;
-  for (int idx = tid; idx < n * fv.r4; idx += kRsThreads) {
-    const int t = idx / fv.r4, i = idx % fv.r4;
+  for (int idx = tid; idx < n * r4; idx += kRsThreads) {
+    const int t = idx / r4, i = idx % r4;
     float val = 0.f;
     if (i < r && live(i)) {
       const double* w = s.g[s.order[i]];

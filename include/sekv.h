@@ -91,7 +91,7 @@ typedef struct {
   int32_t factor_tier;
   double mu, sigma, threshold;   /* surprisal statistics of the build */
   uint64_t resident_bytes;       /* dense rows, means, summaries, tables on the device */
-  uint64_t factor_bytes;         /* sum over (layer, KV head, span) of 8 r (n + d + 1) */
+  uint64_t factor_bytes;         /* sum over (layer, KV head, span) of 4 (rK + rV) (n + d + 1) */
   uint64_t factor_pool_bytes;    /* bytes allocated for the pool, padding included */
 } sekv_cache_info;
 
@@ -152,11 +152,14 @@ sekv_status sekv_cache_copy_spans(const sekv_cache* cache, int32_t* anchors, int
 /* Copy one (layer, KV head) of the cache's stored representation to host
  * memory (any pointer may be NULL), for inspection and tests:
  *   kbar, vbar [S_c][d] and summary [G][S_c][dr], in kv_dtype;
- *   rank [S_c] int32 (retained rank r_j);
- *   factors of compressed span j, if j >= 0: kv = 0 keys, 1 values;
- *   u [n_j][r_j], sigma [r_j], vt [r_j][d], all float32. */
+ *   rank_k, rank_v [S_c] int32: retained ranks of each span's key factors and
+ *   of its value factors (equal after the build, see sekv_apply_gates);
+ * sekv_cache_copy_factors copies the factors of compressed span j, kv = 0
+ * keys, 1 values: u [n_j][r], sigma [r], vt [r][d], all float32, with r that
+ * matrix's rank. */
 sekv_status sekv_cache_copy_group(const sekv_cache* cache, int32_t layer, int32_t kv_head,
-                                  void* kbar, void* vbar, void* summary, int32_t* rank);
+                                  void* kbar, void* vbar, void* summary, int32_t* rank_k,
+                                  int32_t* rank_v);
 sekv_status sekv_cache_copy_factors(const sekv_cache* cache, int32_t layer, int32_t kv_head,
                                     int32_t span, int32_t kv, float* u, float* sigma, float* vt);
 
@@ -180,7 +183,8 @@ size_t sekv_decode_workspace_bytes(const sekv_cache* cache);
  * Sec. 3.3): one softmax, scale 1/sqrt(d), over every full-resolution row of
  * the group, one coarse entry (kbar_j, vbar_j) with ln n_j added to its scaled
  * score for every compressed span the head did not zoom, and the n_j rows
- * U_j diag(sigma_j) V_j^T of every span it zoomed, for keys and values alike.
+ * U_j diag(sigma_j) V_j^T of every span it zoomed (keys from the span's key
+ * factors, values from its value factors, each at its own rank).
  * Accumulates in float32.
  *   q_dev: device float32 [Hq][d]; route: the output of sekv_route for this
  *   layer and query (its mask and union lists are read); o_dev: device float32
@@ -232,24 +236,25 @@ sekv_status sekv_cap_budget(const sekv_cache* cache, const sekv_route_out* route
 /* Soft-gated reconstruction (SeKV paper Sec. 3.2 low-rank paragraph, Eq. 8:
  * K^_j = U_j diag(g_j * sigma_j) V_j^T with per-component gates in [0, 1],
  * components with negligible gates not stored), applied to a built cache.
- * For every (layer, KV head, compressed span), gate i belongs to the i-th
- * largest singular value of the stored factors (i < r_j); the components with
- * gate >= eps stay, in order, with sigma scaled by the gate, for keys and
- * values alike (one gate vector per span: keys and values keep one rank); a
- * span keeps at least one component, the one with the largest gate (lowest
- * index on ties).  The factor pool is repacked to the new ranks, so zoomed
- * spans then move 8 r' (n + d + 1) bytes.  Calling it again gates the gated
- * factors.
- *   gates_dev: device float32 [L][Hkv][S_c][max_rank] (S_c from
- *              sekv_cache_info; entries i >= r_j are ignored), each used gate
- *              in [0, 1]; read during the call.
+ * The value matrix of a span has gates of its own (same paragraph), so keys
+ * and values are gated separately and may end with different ranks.  For
+ * every (layer, KV head, compressed span) and each of its two matrices, gate
+ * i belongs to the i-th largest singular value of that matrix's stored
+ * factors (i < its rank); the components with gate >= eps stay, in order,
+ * with sigma scaled by the gate; a matrix keeps at least one component, the
+ * one with the largest gate (lowest index on ties).  The factor pool is
+ * repacked to the new ranks, so zoomed spans then move
+ * 4 (rK' + rV') (n + d + 1) bytes.  Calling it again gates the gated factors.
+ *   key_gates_dev, value_gates_dev: device float32 [L][Hkv][S_c][max_rank]
+ *              each (S_c from sekv_cache_info; entries past a matrix's rank
+ *              are ignored), each used gate in [0, 1]; read during the call.
  * Synchronises `stream`.  Errors: SEKV_ERR_INVALID for NULL arguments, a
  * non-finite eps or a gate outside [0, 1] (nothing changed);
  * SEKV_ERR_UNSUPPORTED for host-tier caches; SEKV_ERR_NOMEM if the new pool
  * does not fit (nothing changed); after SEKV_ERR_HIP the cache must be
  * destroyed. */
-sekv_status sekv_apply_gates(sekv_cache* cache, const float* gates_dev, float eps,
-                             hipStream_t stream);
+sekv_status sekv_apply_gates(sekv_cache* cache, const float* key_gates_dev,
+                             const float* value_gates_dev, float eps, hipStream_t stream);
 
 /* HBM residency cache for host-tier factors (SeKV paper Sec. 3.2 keeps the
  * span bases on the CPU and fetches them for the selected spans; its
@@ -278,7 +283,7 @@ sekv_status sekv_set_residency(sekv_cache* cache, uint64_t capacity_bytes, uint6
 /* Counters of the residency cache since it was enabled or last reset
  * (synchronises the device): out[0] blocks read from the cache, out[1] blocks
  * copied over the host link, out[2] and out[3] their bytes counted as
- * 8 r (n + d + 1) per block, out[4] sets, out[5] slot bytes.  reset != 0 zeroes
+ * 4 (rK + rV) (n + d + 1) per block, out[4] sets, out[5] slot bytes.  reset != 0 zeroes
  * the counters afterwards.  SEKV_ERR_INVALID if the cache is not enabled. */
 sekv_status sekv_residency_stats(const sekv_cache* cache, uint64_t out[6], int32_t reset);
 

@@ -301,13 +301,18 @@ def correlated_queries(wl: Workload, seed: int, n: int, rho: float, seq: int = 0
     return out
 
 
-def span_gates(wl: Workload, seed: int, n_compressed: int, device="cpu") -> torch.Tensor:
-    """Per-component gates of every (layer, KV head, compressed span),
-    [L][Hkv][S_c][max_rank] float32 in (0, 1): g_i = sigmoid(z_i) with
-    z_i ~ N(3 - 6 i / (R - 1), 1), so leading components mostly stay open and
-    trailing ones mostly close (a stand-in for a trained gate predictor)."""
+def span_gates(wl: Workload, seed: int, n_compressed: int, which: str = "k",
+               device="cpu") -> torch.Tensor:
+    """Per-component gates of the key (``which`` "k") or value ("v") factors of
+    every (layer, KV head, compressed span), [L][Hkv][S_c][max_rank] float32
+    in (0, 1): g_i = sigmoid(z_i) with z_i ~ N(3 - 6 i / (R - 1), 1), so
+    leading components mostly stay open and trailing ones mostly close (a
+    stand-in for a trained gate predictor).  Keys and values draw from streams
+    of their own."""
+    if which not in ("k", "v"):
+        raise ValueError(which)
     R = wl.max_rank
-    g = rng(seed, "span_gates", device=device)
+    g = rng(seed, "span_gates", which, device=device)
     mu = 3.0 - 6.0 * torch.arange(R, device=device, dtype=torch.float32) / max(R - 1, 1)
     z = torch.randn(wl.n_layers, wl.n_kv_heads, n_compressed, R, generator=g, device=device)
     return torch.sigmoid(z + mu)

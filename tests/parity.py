@@ -109,6 +109,36 @@ def rel_err(a: np.ndarray, b: np.ndarray) -> float:
     return float(np.max(np.abs(a - b))) / (den if den > 0 else 1.0)
 
 
+ELEM_FLOOR = 0.1
+
+
+def elem_err(a: np.ndarray, b: np.ndarray, floor: float = ELEM_FLOOR) -> float:
+    """Element-wise relative error max_i |a_i - b_i| / max(|b_i|, floor max|b|):
+    each output element against its own magnitude, with an absolute floor of
+    10% of the head's largest element where the reference is near zero."""
+    b = np.asarray(b, dtype=np.float64)
+    den = np.maximum(np.abs(b), floor * float(np.max(np.abs(b))))
+    den = np.where(den > 0, den, 1.0)
+    return float(np.max(np.abs(np.asarray(a, dtype=np.float64) - b) / den))
+
+
+def attn_err(a: np.ndarray, b: np.ndarray) -> float:
+    """The larger of the norm-wise and the floored element-wise error."""
+    return max(rel_err(a, b), elem_err(a, b))
+
+
+def route_from_gpu(rb, prob: np.ndarray, n_kv_heads: int) -> O.LayerRoute:
+    """An oracle route carrying the GPU's zoom mask (lists and unions formed by
+    the oracle's own compaction), so attention parity covers every head: a
+    decision inside the tie band is taken as the GPU took it."""
+    hq, sc = prob.shape
+    mask = rb.mask.cpu().numpy().astype(bool)[:, :sc]
+    g = hq // n_kv_heads
+    return O.LayerRoute(prob=prob, mask=mask, lists=[O.compact(mask[h]) for h in range(hq)],
+                        unions=[O.union_lists(list(mask[k * g:(k + 1) * g]))
+                                for k in range(n_kv_heads)])
+
+
 def compare_spans(cache, orc: OracleSide):
     sp = cache.spans()
     seg = orc.seg
@@ -138,9 +168,10 @@ def storage_mismatch(gpu: np.ndarray, ref: np.ndarray, kv_dtype: str) -> int:
 
 def compare_group(cache, orc: OracleSide, layer: int, kv_head: int, n_factor_checks: int = 24):
     wl = orc.wl
-    kb, vb, sm, rk = cache.group_data(layer, kv_head)
+    kb, vb, sm, rk, rv = cache.group_data(layer, kv_head)
     gc = orc.groups[layer][kv_head]
     assert rk.numpy().tolist() == gc.rank.tolist()
+    assert rv.numpy().tolist() == gc.vrank.tolist()
     nmis = storage_mismatch(to64(kb), gc.kbar, wl.kv_dtype)
     nmis += storage_mismatch(to64(vb), gc.vbar, wl.kv_dtype)
     g = wl.group
@@ -155,14 +186,14 @@ def compare_group(cache, orc: OracleSide, layer: int, kv_head: int, n_factor_che
         idx = np.unique(np.linspace(0, sc - 1, min(sc, n_factor_checks)).astype(int)) if sc else []
         for i in idx:
             n = int(orc.seg.span_len[orc.seg.cspan[i]])
-            r = int(gc.rank[i])
             for kv, fac in ((0, gc.kfac[i]), (1, gc.vfac[i])):
+                r = int(gc.rank[i] if kv == 0 else gc.vrank[i])
                 u, sg, vt = cache.factors(layer, kv_head, int(i), kv, r, n)
                 rec = (u.double() * sg.double()) @ vt.double()
                 ref = fac.reconstruct()
                 e = np.linalg.norm(rec.numpy() - ref) / max(np.linalg.norm(ref), 1e-300)
                 worst = max(worst, e)
-                big = fac.sigma > 1e-6 * fac.sigma[0]
+                big = np.abs(fac.sigma) > 1e-6 * np.max(np.abs(fac.sigma))
                 assert np.allclose(sg.double().numpy()[big], fac.sigma[big], rtol=1e-5, atol=0)
     assert worst <= 1e-4, f"factor reconstruction differs by {worst}"
     return nmis, worst

@@ -94,7 +94,8 @@ def test_calls_on_null_cache_are_rejected(L):
                               None) == S.SEKV_ERR_INVALID
     assert L.sekv_cap_budget(None, ctypes.byref(ro), 0, None) == S.SEKV_ERR_INVALID
     assert L.sekv_set_residency(None, 1 << 20, 1 << 16) == S.SEKV_ERR_INVALID
-    assert L.sekv_apply_gates(None, ctypes.c_void_p(8), 0.5, None) == S.SEKV_ERR_INVALID
+    assert L.sekv_apply_gates(None, ctypes.c_void_p(8), ctypes.c_void_p(8), 0.5,
+                              None) == S.SEKV_ERR_INVALID
     out6 = (ctypes.c_uint64 * 6)()
     assert L.sekv_residency_stats(None, out6, 0) == S.SEKV_ERR_INVALID
     assert L.sekv_decode_workspace_bytes(None) == 0
