@@ -22,7 +22,8 @@ __all__ = [
     "sekv_cap_budget", "sekv_decode_workspace_bytes", "EXPORTED_SYMBOLS",
     "sekv_set_residency", "sekv_residency_stats", "sekv_apply_gates", "SEKV_MAX_BATCH",
     "SEKV_F32", "SEKV_BF16", "SEKV_TIER_DEVICE", "SEKV_TIER_HOST_PINNED",
-    "SEKV_SVD_EXACT", "SEKV_SVD_RANDOMIZED",
+    "SEKV_SVD_EXACT", "SEKV_SVD_RANDOMIZED", "sekv_route_attn_noalloc",
+    "SEKV_NOALLOC_SCRATCH_BYTES",
 ]
 
 SEKV_OK, SEKV_ERR_INVALID, SEKV_ERR_NOMEM, SEKV_ERR_HIP, SEKV_ERR_UNSUPPORTED = range(5)
@@ -30,6 +31,7 @@ SEKV_F32, SEKV_BF16 = 0, 1
 SEKV_TIER_DEVICE, SEKV_TIER_HOST_PINNED = 0, 1
 SEKV_SVD_EXACT, SEKV_SVD_RANDOMIZED = 0, 1
 SEKV_MAX_BATCH = 8
+SEKV_NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024
 
 EXPORTED_SYMBOLS = (
     "sekv_segment", "sekv_build_spans", "sekv_cache_info_get", "sekv_cache_copy_spans",
@@ -37,6 +39,7 @@ EXPORTED_SYMBOLS = (
     "sekv_decode_workspace_bytes", "sekv_decode_attn", "sekv_route_attn",
     "sekv_decode_attn_batch", "sekv_route_attn_batch", "sekv_cap_budget", "sekv_set_residency",
     "sekv_residency_stats", "sekv_apply_gates", "sekv_cache_destroy", "sekv_last_error",
+    "sekv_route_attn_noalloc",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -112,6 +115,8 @@ def lib() -> ctypes.CDLL:
         "sekv_decode_attn": (I32, [P, I32, P, ctypes.POINTER(SekvRouteOut), P, P, SZ, P, P]),
         "sekv_route_attn": (I32, [P, I32, P, P, P, ctypes.POINTER(SekvRouteOut), P, P, SZ, P,
                                   P]),
+        "sekv_route_attn_noalloc": (I32, [P, I32, P, P, P, ctypes.POINTER(SekvRouteOut), P,
+                                          P, P]),
         "sekv_route_attn_batch": (I32, [ctypes.POINTER(P), I32, I32, ctypes.POINTER(P), P, P,
                                         ctypes.POINTER(SekvRouteOut), ctypes.POINTER(P),
                                         ctypes.POINTER(P), ctypes.POINTER(SZ), P]),
@@ -362,6 +367,28 @@ def sekv_route_attn(cache: Cache, layer: int, q: torch.Tensor, proj: torch.Tenso
                                  ctypes.byref(st), _ptr(o), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream),
                                  fst))
+
+
+def sekv_route_attn_noalloc(cache: Cache, layer: int, q: torch.Tensor, proj: torch.Tensor,
+                            tau: torch.Tensor, route: RouteBuffers, o: torch.Tensor, stream=None,
+                            fetch_stream=None) -> None:
+    """sekv_route_attn without a workspace: the partial states go to the
+    library's per-device scratch (no allocation; calls on one device must not
+    overlap)."""
+    _need(q, "q", torch.float32)
+    _need(proj, "proj", torch.float32)
+    _need(tau, "tau", torch.float32)
+    _need(o, "o", torch.float32)
+    c = cache.cfg
+    if tuple(q.shape) != (c.n_q_heads, c.head_dim) or tuple(o.shape) != (c.n_q_heads, c.head_dim):
+        raise ValueError("q and o must be [Hq][d]")
+    if tuple(tau.shape) != (c.n_q_heads,) or \
+            tuple(proj.shape) != (c.n_q_heads, c.route_dim, c.head_dim):
+        raise ValueError("proj [Hq][dr][d] and tau [Hq] expected")
+    st = route.struct()
+    fst = None if fetch_stream is None else _stream(fetch_stream)
+    _check(lib().sekv_route_attn_noalloc(cache.handle, layer, _ptr(q), _ptr(proj), _ptr(tau),
+                                         ctypes.byref(st), _ptr(o), _stream(stream), fst))
 
 
 def sekv_cap_budget(cache: Cache, route: RouteBuffers, budget_tokens: int, stream=None) -> None:

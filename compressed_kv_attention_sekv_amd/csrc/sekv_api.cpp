@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstring>
 #include <memory>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -119,6 +120,7 @@ sekv_status run_segment(const sekv_config* cfg, int n, const float* s, Scratch& 
 
 struct sekv_cache {
   sekv_config cfg{};
+  int device = 0;                  // the device the cache was built on
   int n_tokens = 0, n_anchors = 0, n_spans = 0, sc = 0, n_dense = 0;
   int group = 1;
   double stats[3] = {0, 0, 0};
@@ -210,6 +212,7 @@ static sekv_status build_impl(const sekv_config* cfg, int32_t n_tokens, const fl
                               std::unique_ptr<sekv_cache>& out) {
   auto c = std::make_unique<sekv_cache>();
   c->cfg = *cfg;
+  SEKV_HIP(hipGetDevice(&c->device));
   c->n_tokens = n_tokens;
   c->group = cfg->n_q_heads / cfg->n_kv_heads;
   const int L = cfg->n_layers, Hkv = cfg->n_kv_heads, Hq = cfg->n_q_heads, dr = cfg->route_dim;
@@ -656,6 +659,58 @@ sekv_status sekv_route_attn(const sekv_cache* c, int32_t layer, const float* q_d
   SEKV_HIP(launch_layer(c->bf16(), kRoute | kDense | kZoom, c->geom, a, stream));
   SEKV_HIP(launch_layer_tail(kMerge | kLists, c->geom, a, stream));
   return SEKV_OK;
+}
+
+// ---- the allocation-free route + attention --------------------------------------
+// The partial softmax states of sekv_route_attn_noalloc live in this file-scope
+// device array instead of a caller workspace.  Each device holds its own copy
+// until the process ends.  Host code never uses the array's name as an address:
+// its device address is looked up once per device (with that device current)
+// and kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[SEKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+sekv_status scratch_for_device(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SEKV_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table covers", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    SEKV_HIP(hipGetDevice(&cur));
+    if (cur != dev) SEKV_HIP(hipSetDevice(dev));
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) SEKV_HIP(hipSetDevice(cur));
+    if (e != hipSuccess)
+      return fail(SEKV_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SEKV_OK;
+}
+}  // namespace
+
+sekv_status sekv_route_attn_noalloc(const sekv_cache* c, int32_t layer, const float* q_dev,
+                                    const float* proj_dev, const float* tau_dev,
+                                    const sekv_route_out* route, float* o_dev, hipStream_t stream,
+                                    hipStream_t fetch_stream) {
+  sekv_status r;
+  if ((r = check_layer_call(c, layer))) return r;
+  const size_t need = sekv_decode_workspace_bytes(c);
+  if (need > (size_t)SEKV_NOALLOC_SCRATCH_BYTES)
+    return fail(SEKV_ERR_UNSUPPORTED, "this cache needs %zu bytes of partial states, more than the "
+                "%d-byte scratch of the allocation-free call; use sekv_route_attn with a workspace",
+                need, (int)SEKV_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((r = scratch_for_device(c->device, &ws))) return r;
+  return sekv_route_attn(c, layer, q_dev, proj_dev, tau_dev, route, o_dev, ws,
+                         (size_t)SEKV_NOALLOC_SCRATCH_BYTES, stream, fetch_stream);
 }
 
 sekv_status sekv_cap_budget(const sekv_cache* c, const sekv_route_out* route,

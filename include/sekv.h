@@ -210,6 +210,26 @@ sekv_status sekv_route_attn(const sekv_cache* cache, int32_t layer, const float*
                             const sekv_route_out* route, float* o_dev, void* ws_dev,
                             size_t ws_bytes, hipStream_t stream, hipStream_t fetch_stream);
 
+/* Route and attend one layer like sekv_route_attn, with no workspace
+ * argument and no allocation: for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, hosts that forbid
+ * hipMalloc).  The partial softmax states go to a scratch array of
+ * SEKV_NOALLOC_SCRATCH_BYTES that the library holds on each device until the
+ * process ends (it calls neither hipMalloc nor hipFree, nor any allocating
+ * routine).  Every call on a device shares that device's scratch: calls that
+ * may overlap on one device (other streams, other threads) race and must be
+ * serialised by the caller; each call writes every part of the scratch it
+ * reads, so nothing needs clearing between calls.  Arguments, results and
+ * errors as for sekv_route_attn; SEKV_ERR_UNSUPPORTED if the cache needs more
+ * than SEKV_NOALLOC_SCRATCH_BYTES of partial states
+ * (sekv_decode_workspace_bytes), which holds the 128K-context Llama-3-8B and
+ * Qwen2.5-14B shapes with room to spare. */
+#define SEKV_NOALLOC_SCRATCH_BYTES (8 * 1024 * 1024)
+sekv_status sekv_route_attn_noalloc(const sekv_cache* cache, int32_t layer, const float* q_dev,
+                                    const float* proj_dev, const float* tau_dev,
+                                    const sekv_route_out* route, float* o_dev, hipStream_t stream,
+                                    hipStream_t fetch_stream);
+
 /* Matched-budget cap of one layer's zoom decisions (SeKV paper Sec. 3.3,
  * zoom-in decoding: past the GPU KV budget, spans are kept in decreasing order
  * of their gate value until the budget is filled).  Per KV head g, the
