@@ -49,10 +49,16 @@ silent.  The readings are:
     carry their own gate vectors (Sec. 3.2 low-rank paragraph: the value
     matrix gets the same gated decomposition with its own gates and factors),
     so each keeps its own rank;
-  * budget cap (optional): per layer and KV head, the reconstructed spans'
-    total length is capped; spans are kept by decreasing gate value (the
-    largest over the group's heads that selected them), ties by lower id,
-    as long as the total fits (Sec. 3.3, the matched-budget paragraph).
+  * window append and retire (optional): appended tokens enter the window;
+    a token leaving it is an anchor if its surprisal exceeds the build's
+    threshold, else it joins the open run, which stays at full resolution
+    until the next retired anchor closes it into a span;
+  * budget cap (optional): the reconstructed spans' total length is capped,
+    per KV head or over the whole layer (one order across its KV heads, the
+    step-peak reading of the budget); spans are kept by decreasing gate value
+    (the largest over the group's heads that selected them), ties by lower KV
+    head then lower id, as long as the total fits (Sec. 3.3, the
+    matched-budget paragraph).
 """
 from __future__ import annotations
 
@@ -129,6 +135,8 @@ class Segmentation:
     kind: np.ndarray           # 0 = compressed (summary + factors), 1 = short (full resolution)
     cspan: np.ndarray          # indices (into span_*) of the compressed spans, ascending
     dense_pos: np.ndarray      # ascending positions kept at full resolution
+    open_start: int = 0        # after appends: the open run of retired tokens (not yet a span)
+    open_len: int = 0
 
     @property
     def n_compressed(self) -> int:
@@ -173,6 +181,57 @@ def segment(s, window: int, alpha: float, min_span_len: int) -> Segmentation:
         cspan=np.array([i for i, k in enumerate(kind) if k == 0], dtype=np.int64),
         dense_pos=np.array(sorted(dense), dtype=np.int64),
     )
+
+
+def segment_appended(s, n_build: int, build: Segmentation, min_span_len: int) -> Segmentation:
+    """The segmentation of a cache built over the first ``n_build`` tokens of
+    ``s`` after the remaining tokens were appended one decode step at a time.
+
+    Reading taken (the pages say every decode step attends over the
+    mixed-resolution memory and the most recent ``window`` tokens stay at full
+    resolution, and are silent on how tokens leave the window): an appended
+    token enters the window at full resolution; a token that leaves the window
+    is compared with the build's threshold (the prompt's statistics, which the
+    method computes once): above it, it becomes an anchor; otherwise it joins
+    the open run, the retired non-anchor tokens since the last retired anchor,
+    which stay at full resolution until the next retired anchor closes the run
+    into a span (compressed if at least ``min_span_len`` tokens long, else kept
+    at full resolution like any short span).  What the build made stays as it
+    is."""
+    s = np.asarray(s, dtype=F64)
+    n = s.size
+    w = build.window
+    thr = build.threshold
+    r0, r1 = max(n_build - w, 0), max(n - w, 0)   # positions retired by the appends
+    anchors = list(build.anchors)
+    starts, lens = list(build.span_start), list(build.span_len)
+    run_start, run_len = r0, 0
+    for t in range(r0, r1):
+        if float(s[t]) > thr:
+            if run_len:
+                starts.append(run_start)
+                lens.append(run_len)
+            anchors.append(t)
+            run_start, run_len = t + 1, 0
+        else:
+            if run_len == 0:
+                run_start = t
+            run_len += 1
+    kind = [0 if ln >= min_span_len else 1 for ln in lens]
+    dense = set(anchors)
+    for b, ln, k in zip(starts, lens, kind):
+        if k == 1:
+            dense.update(range(b, b + ln))
+    dense.update(range(run_start, run_start + run_len))
+    dense.update(range(r1, n))
+    return Segmentation(
+        n_tokens=n, window=w, mu=build.mu, sigma=build.sigma, threshold=thr,
+        anchors=np.array(anchors, dtype=np.int64),
+        span_start=np.array(starts, dtype=np.int64), span_len=np.array(lens, dtype=np.int64),
+        kind=np.array(kind, dtype=np.int64),
+        cspan=np.array([i for i, k in enumerate(kind) if k == 0], dtype=np.int64),
+        dense_pos=np.array(sorted(dense), dtype=np.int64),
+        open_start=run_start if run_len else 0, open_len=run_len)
 
 
 # ---------------------------------------------------------------------------
@@ -403,38 +462,52 @@ def route_layer(q, p_proj, tau, summaries: Dict[int, np.ndarray], seg: Segmentat
                       lists=lists, unions=unions)
 
 
-def cap_budget(route: LayerRoute, seg: Segmentation, n_kv_heads: int, budget: int) -> LayerRoute:
+def cap_budget(route: LayerRoute, seg: Segmentation, n_kv_heads: int, budget: int,
+               scope: str = "kv_head") -> LayerRoute:
     """The matched-budget cap of the zoom decisions (Sec. 3.3, zoom-in decoding:
     when the selected spans exceed the budget, spans are kept in decreasing
     order of their gate value until the budget is filled).
 
-    Reading taken: the budget counts the tokens a KV head reconstructs in one
-    layer, i.e. the lengths n_j of the spans in its union; a span's order key is
-    the largest gate value among the group's heads that selected it, ties going
-    to the lower span id; the kept spans are the longest prefix of that order
-    whose total length is at most ``budget``.  A kept span stays zoomed for the
-    heads that selected it; a dropped one reverts to its coarse entry for all."""
+    Reading taken: a candidate is a span in a KV head's union; its order key is
+    the largest gate value among the group's heads that selected it; its cost is
+    its length n_j (the tokens that KV head reconstructs).  With scope
+    "kv_head" each KV head is capped on its own, ties going to the lower span
+    id.  With scope "layer" one order runs over the candidates of every KV head
+    of the layer (ties to the lower KV head, then the lower span id) and the
+    budget bounds their total: Sec. 3.3 defines the budget as the peak
+    GPU-resident KV of a decoding step including the spans reconstructed at
+    that step, and a step reaches its peak inside one layer, whose
+    reconstructed spans are needed only while it attends.  The kept
+    candidates are the longest prefix of the order whose total length is at
+    most ``budget``; a kept span stays zoomed for the heads that selected it,
+    a dropped one reverts to its coarse entry for all of them."""
+    if scope not in ("kv_head", "layer"):
+        raise ValueError(scope)
     hq = route.mask.shape[0]
     group = hq // n_kv_heads
     n = seg.span_len[seg.cspan].astype(np.int64)
     mask = route.mask.copy()
+    cands = []   # (key, g, j)
     for g in range(n_kv_heads):
         heads = range(g * group, (g + 1) * group)
-        cand = union_lists([route.mask[h] for h in heads])
-        if cand.size == 0:
-            continue
-        key = np.array([max(route.prob[h, j] for h in heads if route.mask[h, j]) for j in cand])
-        order = sorted(range(cand.size), key=lambda i: (-key[i], cand[i]))
-        kept = np.zeros(seg.n_compressed, dtype=bool)
+        for j in union_lists([route.mask[h] for h in heads]):
+            key = max(route.prob[h, j] for h in heads if route.mask[h, j])
+            cands.append((float(key), g, int(j)))
+    kept = set()
+    groups = [list(range(n_kv_heads))] if scope == "layer" else [[g] for g in range(n_kv_heads)]
+    for gs in groups:
+        order = sorted((c for c in cands if c[1] in gs), key=lambda c: (-c[0], c[1], c[2]))
         total = 0
-        for i in order:
-            j = cand[i]
+        for key, g, j in order:
             if total + n[j] > budget:
                 break
             total += n[j]
-            kept[j] = True
-        for h in heads:
-            mask[h] &= kept
+            kept.add((g, j))
+    for h in range(hq):
+        g = h // group
+        for j in np.flatnonzero(mask[h]):
+            if (g, int(j)) not in kept:
+                mask[h, j] = False
     lists = [compact(z) for z in mask]
     unions = [union_lists(list(mask[g * group:(g + 1) * group])) for g in range(n_kv_heads)]
     return LayerRoute(prob=route.prob, mask=mask, lists=lists, unions=unions)

@@ -466,6 +466,43 @@ def test_budget_cap_golden(case):
     assert [l.tolist() for l in capped.lists] == [list(np.flatnonzero(m)) for m in case["mask"]]
 
 
+@pytest.mark.parametrize("case", _golden("budget_cap_tiny.json")["layer_scope"]["cases"],
+                         ids=lambda c: f"layer-{c['budget']}")
+def test_budget_cap_layer_scope_golden(case):
+    gold = _golden("budget_cap_tiny.json")
+    route = _route_of(gold["prob"], gold["tau"])
+    capped = O.cap_budget(route, _seg_of(gold["span_len"]), gold["n_kv_heads"], case["budget"],
+                          scope="layer")
+    assert capped.mask.astype(int).tolist() == case["mask"]
+    assert [u.tolist() for u in capped.unions] == case["unions"]
+    assert [l.tolist() for l in capped.lists] == [list(np.flatnonzero(m)) for m in case["mask"]]
+
+
+def test_budget_cap_layer_scope_properties():
+    """Layer scope: one KV head reduces to the per-KV-head cap; the kept total
+    never exceeds the budget and is a prefix (adding the next candidate in
+    key order would exceed it); larger budgets keep supersets."""
+    rng = np.random.default_rng(3)
+    for trial in range(20):
+        hkv, g, sc = int(rng.integers(1, 4)), int(rng.integers(1, 4)), int(rng.integers(5, 40))
+        prob = rng.uniform(0, 1, (hkv * g, sc))
+        lens = rng.integers(1, 50, sc)
+        route = _route_of(prob.tolist(), 0.5)
+        seg = _seg_of(lens.tolist())
+        prev = None
+        for budget in sorted(rng.integers(0, int(lens.sum()) * hkv + 1, 6).tolist()):
+            capped = O.cap_budget(route, seg, hkv, budget, scope="layer")
+            if hkv == 1:
+                same = O.cap_budget(route, seg, hkv, budget)
+                assert np.array_equal(capped.mask, same.mask)
+            total = sum(int(lens[j]) for u in capped.unions for j in u)
+            assert total <= budget
+            assert np.all(capped.mask <= route.mask)
+            if prev is not None:
+                assert np.all(prev <= capped.mask)
+            prev = capped.mask
+
+
 def test_budget_cap_properties():
     """On random routes: the kept spans of each group are a prefix of the
     order (key descending, id ascending) whose total fits and whose next span
@@ -595,4 +632,93 @@ def test_gated_attention_uses_each_matrix_reconstruction():
     vr = 0.7 * vf.sigma[2] * np.outer(vf.u[:, 2], vf.vt[2])
     ref = torch.nn.functional.scaled_dot_product_attention(
         torch.from_numpy(q)[None, None, :], torch.from_numpy(kr)[None], torch.from_numpy(vr)[None])
+    assert np.allclose(o, ref[0, 0].numpy(), rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# window append and retire
+# ---------------------------------------------------------------------------
+
+def _append_case(seed, n_build=300, n_total=420, window=40, min_len=4):
+    rng = np.random.default_rng(seed)
+    s = rng.gamma(2.0, 0.3, n_total)
+    s[rng.choice(n_total, n_total // 12, replace=False)] += 3.0
+    build = O.segment(s[:n_build], window, 1.0, min_len)
+    return s, build
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_append_partition_and_brute_force(seed):
+    """After appends, anchors, every span, the open run and the window
+    partition [0, N); the spans and anchors the appends add equal an
+    independent formulation: in the retired positions, the anchors are those
+    above the build's threshold and the new spans are the maximal runs of
+    other positions that an anchor follows (found with numpy run boundaries)."""
+    n_build, window, min_len = 300, 40, 4
+    s, build = _append_case(seed, n_build=n_build, window=window, min_len=min_len)
+    for n in (n_build, n_build + 1, n_build + 17, s.size):
+        seg = O.segment_appended(s[:n], n_build, build, min_len)
+        covered = np.zeros(n, dtype=int)
+        covered[seg.anchors] += 1
+        for b, ln in zip(seg.span_start, seg.span_len):
+            covered[b:b + ln] += 1
+        covered[seg.open_start:seg.open_start + seg.open_len] += 1
+        covered[max(n - window, 0):] += 1
+        assert np.all(covered == 1)
+        assert seg.anchors.size + int(seg.span_len.sum()) + seg.open_len + min(window, n) == n
+        # brute force over the retired positions
+        r0, r1 = n_build - window, n - window
+        above = s[r0:r1] > build.threshold
+        assert seg.anchors[build.anchors.size:].tolist() == (r0 + np.flatnonzero(above)).tolist()
+        low = np.r_[False, ~above, False].astype(int)
+        edges = np.diff(low)
+        starts, ends = np.flatnonzero(edges == 1), np.flatnonzero(edges == -1)
+        closed = [(r0 + a, b - a) for a, b in zip(starts, ends) if b < r1 - r0]
+        new = list(zip(seg.span_start[build.span_start.size:].tolist(),
+                       seg.span_len[build.span_len.size:].tolist()))
+        assert new == closed
+        tail = [(r0 + a, b - a) for a, b in zip(starts, ends) if b == r1 - r0]
+        assert (seg.open_start, seg.open_len) == (tail[0] if tail else (0, 0))
+        # short new spans stay at full resolution
+        assert set(seg.dense_pos.tolist()) == set(range(n)) - {
+            t for i in seg.cspan for t in range(seg.span_start[i], seg.span_start[i] + seg.span_len[i])}
+
+
+def test_append_closed_forms():
+    """No appended token above the threshold: the spans stay, every retired
+    token sits in the open run; every retired token above it: each becomes an
+    anchor, no span is added; appending nothing returns the build."""
+    n_build, window = 200, 30
+    s, build = _append_case(1, n_build=n_build, n_total=260, window=window)
+    same = O.segment_appended(s[:n_build], n_build, build, 4)
+    for f in ("anchors", "span_start", "span_len", "kind", "cspan", "dense_pos"):
+        assert np.array_equal(getattr(same, f), getattr(build, f))
+    low = s.copy()
+    low[n_build:] = build.threshold - 1.0
+    low[n_build - window:n_build] = np.minimum(low[n_build - window:n_build], build.threshold)
+    seg = O.segment_appended(low, n_build, build, 4)
+    assert np.array_equal(seg.span_start, build.span_start)
+    assert seg.open_len == 60 and seg.open_start == n_build - window
+    high = s.copy()
+    high[n_build - window:] = build.threshold + 1.0
+    seg = O.segment_appended(high, n_build, build, 4)
+    assert seg.anchors.size == build.anchors.size + 60 and seg.open_len == 0
+    assert np.array_equal(seg.span_len, build.span_len)
+
+
+def test_append_full_rank_all_zoomed_is_dense_attention():
+    """Every span of the appended cache zoomed at full rank: textbook attention
+    over all N tokens (torch SDPA), whatever was retired."""
+    n_build, window, min_len = 300, 40, 4
+    s, build = _append_case(3, n_build=n_build, window=window, min_len=min_len)
+    seg = O.segment_appended(s, n_build, build, min_len)
+    assert seg.n_compressed > build.n_compressed
+    rng = np.random.default_rng(8)
+    k = rng.standard_normal((s.size, 128))
+    v = rng.standard_normal((s.size, 128))
+    gc = O.build_group(seg, s, k, v, {}, np.full(s.size, 128), "f32", 128)
+    q = rng.standard_normal(128)
+    o = O.mixed_attention(q, gc, seg, np.ones(seg.n_compressed, dtype=bool))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, None, :], torch.from_numpy(k)[None], torch.from_numpy(v)[None])
     assert np.allclose(o, ref[0, 0].numpy(), rtol=1e-10, atol=1e-12)
