@@ -19,7 +19,9 @@ __all__ = [
     "SekvError", "SekvConfig", "SekvCacheInfo", "SekvRouteOut", "lib", "library_path",
     "make_config", "Cache", "RouteBuffers", "sekv_segment", "sekv_build_spans", "sekv_route",
     "sekv_decode_attn", "sekv_route_attn", "sekv_decode_attn_batch", "sekv_route_attn_batch",
-    "sekv_cap_budget", "sekv_decode_workspace_bytes", "EXPORTED_SYMBOLS",
+    "sekv_cap_budget", "sekv_cap_budget_layer", "sekv_decode_workspace_bytes",
+    "sekv_append_tokens",
+    "EXPORTED_SYMBOLS",
     "sekv_set_residency", "sekv_residency_stats", "sekv_apply_gates", "SEKV_MAX_BATCH",
     "SEKV_F32", "SEKV_BF16", "SEKV_TIER_DEVICE", "SEKV_TIER_HOST_PINNED",
     "SEKV_SVD_EXACT", "SEKV_SVD_RANDOMIZED", "sekv_route_attn_noalloc",
@@ -39,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "sekv_decode_workspace_bytes", "sekv_decode_attn", "sekv_route_attn",
     "sekv_decode_attn_batch", "sekv_route_attn_batch", "sekv_cap_budget", "sekv_set_residency",
     "sekv_residency_stats", "sekv_apply_gates", "sekv_cache_destroy", "sekv_last_error",
-    "sekv_route_attn_noalloc",
+    "sekv_route_attn_noalloc", "sekv_cap_budget_layer", "sekv_append_tokens",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -64,7 +66,7 @@ class SekvConfig(ctypes.Structure):
         ("alpha", ctypes.c_double), ("gamma", ctypes.c_double),
         ("kv_dtype", ctypes.c_int32), ("factor_tier", ctypes.c_int32),
         ("host_pool_cap_bytes", ctypes.c_uint64),
-        ("svd_mode", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("svd_mode", ctypes.c_int32), ("append_capacity", ctypes.c_int32),
     ]
 
 
@@ -76,6 +78,8 @@ class SekvCacheInfo(ctypes.Structure):
         ("mu", ctypes.c_double), ("sigma", ctypes.c_double), ("threshold", ctypes.c_double),
         ("resident_bytes", ctypes.c_uint64), ("factor_bytes", ctypes.c_uint64),
         ("factor_pool_bytes", ctypes.c_uint64),
+        ("open_start", ctypes.c_int32), ("open_len", ctypes.c_int32),
+        ("n_appended", ctypes.c_int32), ("append_capacity", ctypes.c_int32),
     ]
 
 
@@ -124,6 +128,8 @@ def lib() -> ctypes.CDLL:
                                          ctypes.POINTER(SekvRouteOut), ctypes.POINTER(P),
                                          ctypes.POINTER(P), ctypes.POINTER(SZ), P]),
         "sekv_cap_budget": (I32, [P, ctypes.POINTER(SekvRouteOut), ctypes.c_int64, P]),
+        "sekv_cap_budget_layer": (I32, [P, ctypes.POINTER(SekvRouteOut), ctypes.c_int64, P]),
+        "sekv_append_tokens": (I32, [P, I32, P, P, P, P, P, P]),
         "sekv_set_residency": (I32, [P, U64, U64]),
         "sekv_apply_gates": (I32, [P, P, P, ctypes.c_float, P]),
         "sekv_residency_stats": (I32, [P, ctypes.POINTER(U64), I32]),
@@ -169,13 +175,15 @@ def make_config(n_layers: int, n_q_heads: int, n_kv_heads: int, *, head_dim: int
                 route_dim: int = 32, window: int = 512, max_rank: int = 32,
                 min_span_len: int = 8, alpha: float = 1.0, gamma: float = 0.1,
                 kv_dtype: str = "bf16", factor_tier: str = "device",
-                host_pool_cap_bytes: int = 0, svd: str = "exact") -> SekvConfig:
+                host_pool_cap_bytes: int = 0, svd: str = "exact",
+                append_capacity: int = 0) -> SekvConfig:
     return SekvConfig(n_layers, n_q_heads, n_kv_heads, head_dim, route_dim, window, max_rank,
                       min_span_len, float(alpha), float(gamma),
                       SEKV_BF16 if kv_dtype == "bf16" else SEKV_F32,
                       SEKV_TIER_HOST_PINNED if factor_tier == "host" else SEKV_TIER_DEVICE,
                       int(host_pool_cap_bytes),
-                      SEKV_SVD_RANDOMIZED if svd == "randomized" else SEKV_SVD_EXACT, 0)
+                      SEKV_SVD_RANDOMIZED if svd == "randomized" else SEKV_SVD_EXACT,
+                      int(append_capacity))
 
 
 def sekv_segment(cfg: SekvConfig, surprisal: torch.Tensor, stream=None):
@@ -312,6 +320,34 @@ def sekv_build_spans(cfg: SekvConfig, surprisal: torch.Tensor, k: torch.Tensor, 
     return Cache(h, cfg)
 
 
+def sekv_append_tokens(cache: Cache, surprisal: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       w_route: torch.Tensor, rank: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    """Append decode tokens to the window and retire those that leave it
+    (shapes as in include/sekv.h); refreshes ``cache.info``."""
+    c = cache.cfg
+    _need(surprisal, "surprisal", torch.float32)
+    kv_dt = torch.bfloat16 if c.kv_dtype == SEKV_BF16 else torch.float32
+    _need(k, "k", kv_dt)
+    _need(v, "v", kv_dt)
+    _need(w_route, "w_route", torch.float32)
+    n = surprisal.numel()
+    shape = (c.n_layers, c.n_kv_heads, n, c.head_dim)
+    if tuple(k.shape) != shape or tuple(v.shape) != shape:
+        raise ValueError(f"k and v must be {shape}")
+    if tuple(w_route.shape) != (c.n_layers, c.n_q_heads, c.route_dim, c.head_dim):
+        raise ValueError("w_route must be [L][Hq][dr][d]")
+    if rank is not None:
+        _need(rank, "rank", torch.int32)
+        if tuple(rank.shape) != (c.n_layers, c.n_kv_heads, n):
+            raise ValueError("rank must be [L][Hkv][n_new]")
+    _check(lib().sekv_append_tokens(cache.handle, n, _ptr(surprisal), _ptr(k), _ptr(v),
+                                    _ptr(w_route), _ptr(rank), _stream(stream)))
+    info = SekvCacheInfo()
+    _check(lib().sekv_cache_info_get(cache.handle, ctypes.byref(info)))
+    cache.info = info
+
+
 def sekv_route(cache: Cache, layer: int, q: torch.Tensor, proj: torch.Tensor, tau: torch.Tensor,
                out: RouteBuffers, stream=None) -> None:
     _need(q, "q", torch.float32)
@@ -349,7 +385,7 @@ def sekv_decode_attn(cache: Cache, layer: int, q: torch.Tensor, route: RouteBuff
 def sekv_route_attn(cache: Cache, layer: int, q: torch.Tensor, proj: torch.Tensor,
                     tau: torch.Tensor, route: RouteBuffers, o: torch.Tensor,
                     workspace: torch.Tensor, stream=None, fetch_stream=None) -> None:
-    """Route and attend one layer in one call (two launches with device-tier factors)."""
+    """Route and attend one layer in one call (three launches with device-tier factors)."""
     _need(q, "q", torch.float32)
     _need(proj, "proj", torch.float32)
     _need(tau, "tau", torch.float32)
@@ -391,14 +427,18 @@ def sekv_route_attn_noalloc(cache: Cache, layer: int, q: torch.Tensor, proj: tor
                                          ctypes.byref(st), _ptr(o), _stream(stream), fst))
 
 
-def sekv_cap_budget(cache: Cache, route: RouteBuffers, budget_tokens: int, stream=None) -> None:
+def sekv_cap_budget(cache: Cache, route: RouteBuffers, budget_tokens: int, stream=None,
+                    scope: str = "kv_head") -> None:
     """Cap one layer's zoom decisions to ``budget_tokens`` reconstructed tokens
-    per KV head, in place (``route`` must carry gate values)."""
+    per KV head (scope "kv_head") or for the whole layer (scope "layer"), in
+    place (``route`` must carry gate values)."""
     if route.prob is None:
         raise ValueError("the budget cap needs the route's gate values: allocate with_prob=True")
+    if scope not in ("kv_head", "layer"):
+        raise ValueError(f"scope must be 'kv_head' or 'layer', got {scope!r}")
     st = route.struct()
-    _check(lib().sekv_cap_budget(cache.handle, ctypes.byref(st), int(budget_tokens),
-                                 _stream(stream)))
+    fn = lib().sekv_cap_budget_layer if scope == "layer" else lib().sekv_cap_budget
+    _check(fn(cache.handle, ctypes.byref(st), int(budget_tokens), _stream(stream)))
 
 
 def sekv_apply_gates(cache: Cache, key_gates: torch.Tensor, value_gates: torch.Tensor,

@@ -48,6 +48,8 @@ sekv_status check_config(const sekv_config* c) {
   if (c->n_kv_heads < 1 || c->n_q_heads < 1 || c->n_q_heads % c->n_kv_heads != 0)
     return fail(SEKV_ERR_INVALID, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
                 c->n_q_heads, c->n_kv_heads);
+  if (c->n_kv_heads > kMaxKvHeads)
+    return fail(SEKV_ERR_INVALID, "at most %d KV heads", kMaxKvHeads);
   if (c->n_q_heads / c->n_kv_heads > kMaxGroup)
     return fail(SEKV_ERR_INVALID, "at most %d query heads per KV head", kMaxGroup);
   if (c->head_dim != kHeadDim) return fail(SEKV_ERR_INVALID, "head_dim must be %d", kHeadDim);
@@ -67,7 +69,9 @@ sekv_status check_config(const sekv_config* c) {
     return fail(SEKV_ERR_INVALID, "svd_mode must be SEKV_SVD_EXACT or SEKV_SVD_RANDOMIZED");
   if (c->svd_mode == SEKV_SVD_RANDOMIZED && c->max_rank > kRsvdMaxRank)
     return fail(SEKV_ERR_INVALID, "the randomized SVD supports max_rank <= %d", kRsvdMaxRank);
-  if (c->reserved != 0) return fail(SEKV_ERR_INVALID, "reserved must be 0");
+  if (c->append_capacity < 0) return fail(SEKV_ERR_INVALID, "append_capacity must be >= 0");
+  if (c->append_capacity > 0 && c->factor_tier != SEKV_TIER_DEVICE)
+    return fail(SEKV_ERR_UNSUPPORTED, "append_capacity needs device-tier factors");
   return SEKV_OK;
 }
 
@@ -96,8 +100,10 @@ struct Scratch {
 size_t elem_bytes(int dtype) { return dtype == SEKV_BF16 ? 2 : 4; }
 
 sekv_status run_segment(const sekv_config* cfg, int n, const float* s, Scratch& sc, SegOut& o,
-                        int32_t counts[4], double stats[3], hipStream_t st) {
+                        int32_t counts[4], double stats[3], hipStream_t st, int extra = 0) {
   sekv_status r;
+  const int n_tab = n;   // the segmentation kernel's own length
+  n = n + extra;         // table capacity: room for appended tokens
   if ((r = sc.alloc(&o.stats, 3 * sizeof(double), "stats"))) return r;
   if ((r = sc.alloc(&o.counts, 4 * sizeof(int32_t), "counts"))) return r;
   if ((r = sc.alloc(&o.anchors, (size_t)n * 4, "anchors"))) return r;
@@ -109,7 +115,7 @@ sekv_status run_segment(const sekv_config* cfg, int n, const float* s, Scratch& 
   if ((r = sc.alloc(&o.clen, (size_t)n * 4, "clen"))) return r;
   if ((r = sc.alloc(&o.dense_pos, (size_t)n * 4, "dense_pos"))) return r;
   if ((r = sc.alloc(&o.flag, (size_t)n, "flag"))) return r;
-  SEKV_HIP(launch_segment(s, n, cfg->window, cfg->alpha, cfg->min_span_len, o, st));
+  SEKV_HIP(launch_segment(s, n_tab, cfg->window, cfg->alpha, cfg->min_span_len, o, st));
   SEKV_HIP(hipMemcpyAsync(counts, o.counts, 4 * sizeof(int32_t), hipMemcpyDeviceToHost, st));
   SEKV_HIP(hipMemcpyAsync(stats, o.stats, 3 * sizeof(double), hipMemcpyDeviceToHost, st));
   SEKV_HIP(hipStreamSynchronize(st));
@@ -122,6 +128,20 @@ struct sekv_cache {
   sekv_config cfg{};
   int device = 0;                  // the device the cache was built on
   int n_tokens = 0, n_anchors = 0, n_spans = 0, sc = 0, n_dense = 0;
+  // strides of the span arrays ([..][scs]) and of the full-resolution rows
+  // ([..][ds][d]): the counts plus room for appended tokens (window append)
+  int scs = 0, ds = 0;
+  // window append (append_capacity > 0): host copies of what the appends
+  // read and extend, and the device buffers they add
+  int n_appended = 0, open_start = 0, open_len = 0;
+  uint64_t pool_cap_floats = 0;       // pool allocation, in floats (>= pool_floats)
+  std::vector<int32_t> h_dense_pos;   // ascending positions of the full-resolution rows
+  std::vector<float> h_tail_s;        // surprisal of positions tail_base .. n_tokens - 1
+  int tail_base = 0;
+  float* dense_s = nullptr;           // [ds] surprisal of each full-resolution row
+  int32_t* rank_by_dense = nullptr;   // [L][Hkv][ds] rank requested at each row
+  int32_t* app_start = nullptr;       // [scs] first full-resolution row of appended spans
+  int32_t* app_ranges = nullptr;      // [2 capacity] row ranges removed by one append
   int group = 1;
   double stats[3] = {0, 0, 0};
   std::vector<void*> dev;  // every device allocation, freed on destroy
@@ -146,6 +166,8 @@ struct sekv_cache {
   float* stage = nullptr;         // host tier: device staging for one layer
   uint64_t stage_floats = 0;
   uint32_t* chunk_bits = nullptr;  // [Hkv][n_work][kListWords] zoom bit masks of each chunk
+  int32_t* zcount = nullptr;       // [Hkv] zoom workgroups per KV head of the last zoom launch
+  uint8_t* cap_drop = nullptr;     // [Hkv][S_c] decisions of the layer-wide budget cap
   float* zero_block = nullptr;     // kZeroBlockFloats zeros: a valid source for idle prefetches
   LayerGeom geom{};
   hipEvent_t ev_route = nullptr, ev_fetch = nullptr;
@@ -223,7 +245,8 @@ static sekv_status build_impl(const sekv_config* cfg, int32_t n_tokens, const fl
   Scratch scr;
   SegOut o{};
   int32_t counts[4];
-  if ((r = run_segment(cfg, n_tokens, s, scr, o, counts, c->stats, st))) return r;
+  const int cap = cfg->append_capacity;
+  if ((r = run_segment(cfg, n_tokens, s, scr, o, counts, c->stats, st, cap))) return r;
   for (void* p : {(void*)o.anchors, (void*)o.span_start, (void*)o.span_len, (void*)o.kind,
                   (void*)o.cspan, (void*)o.cstart, (void*)o.clen, (void*)o.dense_pos}) {
     scr.release(p);
@@ -243,29 +266,35 @@ static sekv_status build_impl(const sekv_config* cfg, int32_t n_tokens, const fl
   c->n_dense = counts[3];
   const int sc = c->sc, D = c->n_dense;
   const size_t eb = c->kv_elem();
+  c->scs = sc + (cap > 0 ? cap / cfg->min_span_len + 1 : 0);
+  c->ds = D + cap;
+  const int scs = c->scs, ds = c->ds;
 
-  if ((r = c->alloc(&c->lnn64, (size_t)sc * 8, "lnn64"))) return r;
-  if ((r = c->alloc(&c->lnn32, (size_t)sc * 4, "lnn32"))) return r;
+  if ((r = c->alloc(&c->lnn64, (size_t)scs * 8, "lnn64"))) return r;
+  if ((r = c->alloc(&c->lnn32, (size_t)scs * 4, "lnn32"))) return r;
   SEKV_HIP(launch_log_len(c->clen, sc, c->lnn64, c->lnn32, st));
-  if ((r = c->alloc(&c->rank, (size_t)n_lg * sc * 4, "rank"))) return r;
-  SEKV_HIP(launch_span_rank(rank_by_pos, c->cstart, c->clen, n_tokens, sc, n_lg, cfg->max_rank,
-                            c->rank, st));
+  if ((r = c->alloc(&c->rank, (size_t)n_lg * scs * 4, "rank"))) return r;
+  SEKV_HIP(launch_span_rank(rank_by_pos, c->cstart, c->clen, n_tokens, 0, sc, scs, n_lg,
+                            cfg->max_rank, c->rank, st));
 
   // ---- full-resolution rows ------------------------------------------------
-  if ((r = c->alloc(&c->dense_k, (size_t)n_lg * D * kHeadDim * eb, "dense_k"))) return r;
-  if ((r = c->alloc(&c->dense_v, (size_t)n_lg * D * kHeadDim * eb, "dense_v"))) return r;
-  SEKV_HIP(launch_gather_dense(c->bf16(), k_dev, n_tokens, c->dense_pos, D, n_lg, c->dense_k, st));
-  SEKV_HIP(launch_gather_dense(c->bf16(), v_dev, n_tokens, c->dense_pos, D, n_lg, c->dense_v, st));
+  if ((r = c->alloc(&c->dense_k, (size_t)n_lg * ds * kHeadDim * eb, "dense_k"))) return r;
+  if ((r = c->alloc(&c->dense_v, (size_t)n_lg * ds * kHeadDim * eb, "dense_v"))) return r;
+  SEKV_HIP(launch_gather_dense(c->bf16(), k_dev, n_tokens, c->dense_pos, D, ds, n_lg, c->dense_k,
+                               st));
+  SEKV_HIP(launch_gather_dense(c->bf16(), v_dev, n_tokens, c->dense_pos, D, ds, n_lg, c->dense_v,
+                               st));
 
   // ---- means and summaries -------------------------------------------------
-  if ((r = c->alloc(&c->kbar, (size_t)n_lg * sc * kHeadDim * eb, "kbar"))) return r;
-  if ((r = c->alloc(&c->vbar, (size_t)n_lg * sc * kHeadDim * eb, "vbar"))) return r;
-  if ((r = c->alloc(&c->summ, (size_t)L * Hq * sc * dr * eb, "summaries"))) return r;
+  if ((r = c->alloc(&c->kbar, (size_t)n_lg * scs * kHeadDim * eb, "kbar"))) return r;
+  if ((r = c->alloc(&c->vbar, (size_t)n_lg * scs * kHeadDim * eb, "vbar"))) return r;
+  if ((r = c->alloc(&c->summ, (size_t)L * Hq * scs * dr * eb, "summaries"))) return r;
   SEKV_HIP(launch_span_summarize(c->bf16(), s, k_dev, v_dev, w_route, n_tokens, c->cstart,
-                                 c->clen, sc, L, Hkv, c->group, dr, c->kbar, c->vbar, c->summ, st));
+                                 c->clen, 0, sc, scs, L, Hkv, c->group, dr, c->kbar, c->vbar,
+                                 c->summ, st));
 
   // ---- factor pool layout (host) ---------------------------------------------
-  c->h_rank.resize((size_t)n_lg * sc);
+  c->h_rank.assign((size_t)n_lg * scs, 0);
   c->h_clen.resize(sc);
   if (sc) {
     SEKV_HIP(hipMemcpyAsync(c->h_rank.data(), c->rank, c->h_rank.size() * 4,
@@ -273,14 +302,14 @@ static sekv_status build_impl(const sekv_config* cfg, int32_t n_tokens, const fl
     SEKV_HIP(hipMemcpyAsync(c->h_clen.data(), c->clen, (size_t)sc * 4, hipMemcpyDeviceToHost, st));
   }
   SEKV_HIP(hipStreamSynchronize(st));
-  c->h_fac_off.resize((size_t)n_lg * sc);
+  c->h_fac_off.assign((size_t)n_lg * scs, 0);
   c->layer_base.assign(L + 1, 0);
   uint64_t off = 0, fbytes = 0, stage_max = 0;
   for (int l = 0; l < L; ++l) {
     c->layer_base[l] = off;
     for (int g = 0; g < Hkv; ++g)
       for (int j = 0; j < sc; ++j) {
-        const size_t idx = ((size_t)l * Hkv + g) * sc + j;
+        const size_t idx = ((size_t)l * Hkv + g) * scs + j;
         const FactorView fv = FactorView::packed(c->h_rank[idx], c->h_clen[j]);
         c->h_fac_off[idx] = off;
         off += fv.block_floats();
@@ -304,7 +333,17 @@ static sekv_status build_impl(const sekv_config* cfg, int32_t n_tokens, const fl
     return fail(SEKV_ERR_NOMEM, "factor pool needs %zu bytes, host pool cap is %llu", pool_bytes,
                 (unsigned long long)cfg->host_pool_cap_bytes);
   if (cfg->factor_tier == SEKV_TIER_DEVICE) {
-    if ((r = c->alloc(&c->pool_dev, pool_bytes, "factor pool"))) return r;
+    // with append capacity, room for the blocks of every span the appends
+    // can close: at most cap / min_span_len + 1 spans per (layer, KV head),
+    // of at most cap tokens together, each at most at the rank cap
+    c->pool_cap_floats = c->pool_floats;
+    if (cap > 0) {
+      const uint64_t R = (uint64_t)std::min(cfg->max_rank, kHeadDim), R4 = (R + 3) & ~3ull;
+      const uint64_t spans = (uint64_t)cap / cfg->min_span_len + 1;
+      c->pool_cap_floats += (uint64_t)n_lg * (spans * (2 * R * kHeadDim + 2 * R4 + 63) +
+                                              2 * R4 * (uint64_t)cap);
+    }
+    if ((r = c->alloc(&c->pool_dev, (size_t)c->pool_cap_floats * 4, "factor pool"))) return r;
     pool_build = c->pool_dev;
   } else {
     if ((r = scr.alloc(&pool_build, pool_bytes, "factor build buffer"))) return r;
@@ -330,7 +369,7 @@ static sekv_status build_impl(const sekv_config* cfg, int32_t n_tokens, const fl
                               hipMemcpyHostToDevice, st));
       for (int which = 0; which < 2; ++which)
         SEKV_HIP(launch_span_rsvd(c->bf16(), which ? v_dev : k_dev, n_tokens, c->cstart, c->clen,
-                                  d_ids, (int)rs_ids[b].size(), sc, n_lg, c->rank, c->fac_off,
+                                  d_ids, (int)rs_ids[b].size(), scs, n_lg, c->rank, c->fac_off,
                                   pool_build, which, rs_rows[b], st));
     }
     const int max_m[3] = {32, 64, 128};
@@ -341,7 +380,7 @@ static sekv_status build_impl(const sekv_config* cfg, int32_t n_tokens, const fl
       SEKV_HIP(hipMemcpyAsync(d_ids, ids[b].data(), ids[b].size() * 4, hipMemcpyHostToDevice, st));
       for (int which = 0; which < 2; ++which)
         SEKV_HIP(launch_span_svd(c->bf16(), which ? v_dev : k_dev, n_tokens, c->cstart, c->clen,
-                                 d_ids, (int)ids[b].size(), sc, n_lg, c->rank, c->fac_off,
+                                 d_ids, (int)ids[b].size(), scs, n_lg, c->rank, c->fac_off,
                                  pool_build, which, max_m[b], st));
     }
   }
@@ -361,10 +400,42 @@ static sekv_status build_impl(const sekv_config* cfg, int32_t n_tokens, const fl
   }
 
   // ---- decode geometry and chunk bit masks --------------------------------------
-  c->geom = make_layer_geom(Hq, Hkv, dr, D, sc);
-  if ((r = c->alloc(&c->chunk_bits, (size_t)Hkv * c->geom.n_work * kListWords * 4, "chunk bits")))
+  c->geom = make_layer_geom(Hq, Hkv, dr, D, sc, ds, scs);
+  // chunk masks for the geometry at full append capacity (the most workgroups)
+  const int nw_max = make_layer_geom(Hq, Hkv, dr, ds, scs, ds, scs).n_work;
+  if ((r = c->alloc(&c->chunk_bits, (size_t)Hkv * nw_max * kListWords * 4, "chunk bits")))
     return r;
+  if (cap > 0) {
+    // what the appends read: each full-resolution row's surprisal and
+    // requested rank, and on the host the row positions and the surprisal
+    // from the window on
+    if ((r = c->alloc(&c->dense_s, (size_t)ds * 4, "row surprisal"))) return r;
+    if ((r = c->alloc(&c->rank_by_dense, (size_t)n_lg * ds * 4, "row ranks"))) return r;
+    if ((r = c->alloc(&c->app_start, (size_t)scs * 4, "appended span rows"))) return r;
+    if ((r = c->alloc(&c->app_ranges, (size_t)2 * (cap / cfg->min_span_len + 2) * 4,
+                      "removed row ranges")))
+      return r;
+    SEKV_HIP(launch_gather_words((const uint32_t*)s, 0, c->dense_pos, D, ds, 1,
+                                 (uint32_t*)c->dense_s, st));
+    if (rank_by_pos)
+      SEKV_HIP(launch_gather_words((const uint32_t*)rank_by_pos, n_tokens, c->dense_pos, D, ds,
+                                   n_lg, (uint32_t*)c->rank_by_dense, st));
+    else
+      SEKV_HIP(launch_fill_i32(c->rank_by_dense, n_lg * ds, cfg->max_rank, st));
+    c->h_dense_pos.resize(D);
+    if (D)
+      SEKV_HIP(hipMemcpyAsync(c->h_dense_pos.data(), c->dense_pos, (size_t)D * 4,
+                              hipMemcpyDeviceToHost, st));
+    c->tail_base = std::max(n_tokens - cfg->window, 0);
+    c->h_tail_s.resize(n_tokens - c->tail_base);
+    if (!c->h_tail_s.empty())
+      SEKV_HIP(hipMemcpyAsync(c->h_tail_s.data(), s + c->tail_base, c->h_tail_s.size() * 4,
+                              hipMemcpyDeviceToHost, st));
+  }
   if ((r = c->alloc(&c->zero_block, (size_t)kZeroBlockFloats * 4, "zero block"))) return r;
+  if ((r = c->alloc(&c->zcount, (size_t)Hkv * 4, "zoom counts"))) return r;
+  if ((r = c->alloc(&c->cap_drop, (size_t)Hkv * std::max(scs, 1), "budget decisions"))) return r;
+  SEKV_HIP(hipMemsetAsync(c->zcount, 0, (size_t)Hkv * 4, st));
   SEKV_HIP(hipMemsetAsync(c->zero_block, 0, (size_t)kZeroBlockFloats * 4, st));
   SEKV_HIP(hipEventCreateWithFlags(&c->ev_route, hipEventDisableTiming));
   SEKV_HIP(hipEventCreateWithFlags(&c->ev_fetch, hipEventDisableTiming));
@@ -395,6 +466,231 @@ sekv_status sekv_build_spans(const sekv_config* cfg, int32_t n_tokens, const flo
   return SEKV_OK;
 }
 
+// ---- window append ----------------------------------------------------------------
+static sekv_status append_impl(sekv_cache* c, int n_new, const float* s_new, const void* k_new,
+                               const void* v_new, const float* w_route, const int32_t* rank_new,
+                               hipStream_t st) {
+  const sekv_config& cfg = c->cfg;
+  const int L = cfg.n_layers, Hkv = cfg.n_kv_heads, Hq = cfg.n_q_heads, dr = cfg.route_dim;
+  const int n_lg = L * Hkv, W = cfg.window;
+  const size_t eb = c->kv_elem();
+  const int ds = c->ds, scs = c->scs;
+  sekv_status r;
+  // the new tokens' surprisal decides the retirements on the host
+  std::vector<float> sn(n_new);
+  SEKV_HIP(hipMemcpyAsync(sn.data(), s_new, (size_t)n_new * 4, hipMemcpyDeviceToHost, st));
+  SEKV_HIP(hipStreamSynchronize(st));
+  for (int t = 0; t < n_new; ++t)
+    if (!std::isfinite(sn[t]))
+      return fail(SEKV_ERR_INVALID, "surprisal of new token %d is not finite", t);
+
+  // ---- 1. the new tokens join the full-resolution rows (the window) ---------
+  const int D0 = c->n_dense, N0 = c->n_tokens;
+  SEKV_HIP(hipMemcpy2DAsync((char*)c->dense_k + (size_t)D0 * kHeadDim * eb,
+                            (size_t)ds * kHeadDim * eb, k_new, (size_t)n_new * kHeadDim * eb,
+                            (size_t)n_new * kHeadDim * eb, n_lg, hipMemcpyDeviceToDevice, st));
+  SEKV_HIP(hipMemcpy2DAsync((char*)c->dense_v + (size_t)D0 * kHeadDim * eb,
+                            (size_t)ds * kHeadDim * eb, v_new, (size_t)n_new * kHeadDim * eb,
+                            (size_t)n_new * kHeadDim * eb, n_lg, hipMemcpyDeviceToDevice, st));
+  SEKV_HIP(hipMemcpyAsync(c->dense_s + D0, s_new, (size_t)n_new * 4, hipMemcpyDeviceToDevice, st));
+  if (rank_new)
+    SEKV_HIP(hipMemcpy2DAsync(c->rank_by_dense + D0, (size_t)ds * 4, rank_new, (size_t)n_new * 4,
+                              (size_t)n_new * 4, n_lg, hipMemcpyDeviceToDevice, st));
+
+  Scratch scr_rank;
+  if (!rank_new) {   // max_rank for every new token: one fill, then a strided copy
+    int32_t* tmp = nullptr;
+    if ((r = scr_rank.alloc(&tmp, (size_t)n_lg * n_new * 4, "requested ranks"))) return r;
+    SEKV_HIP(launch_fill_i32(tmp, n_lg * n_new, cfg.max_rank, st));
+    SEKV_HIP(hipMemcpy2DAsync(c->rank_by_dense + D0, (size_t)ds * 4, tmp, (size_t)n_new * 4,
+                              (size_t)n_new * 4, n_lg, hipMemcpyDeviceToDevice, st));
+  }
+  // host state changes below are undone if the append fails before the device
+  // copies of the span table change (only the pool room and scratch can fail)
+  const size_t hp0 = c->h_dense_pos.size(), ht0 = c->h_tail_s.size();
+  auto undo = [&](sekv_status e) {
+    c->h_dense_pos.resize(hp0);
+    c->h_tail_s.resize(ht0);
+    return e;
+  };
+  for (int t = 0; t < n_new; ++t) {
+    c->h_dense_pos.push_back(N0 + t);
+    c->h_tail_s.push_back(sn[t]);
+  }
+  int D = D0 + n_new;
+  const int N = N0 + n_new;
+
+  // ---- 2. retire the tokens that leave the window ----------------------------
+  struct NewSpan { int start, len, row; bool compressed; };
+  std::vector<NewSpan> closed;
+  std::vector<int32_t> new_anchors;
+  const double thr = c->stats[2];
+  const int r_old = std::max(N0 - W, 0), r_new = std::max(N - W, 0);
+  // the row of position p among the full-resolution rows (ascending)
+  auto row_of = [&](int p) {
+    return (int)(std::lower_bound(c->h_dense_pos.begin(), c->h_dense_pos.end(), p) -
+                 c->h_dense_pos.begin());
+  };
+  int open_start = c->open_start, open_len = c->open_len;
+  for (int t = r_old; t < r_new; ++t) {
+    const double sv = (double)c->h_tail_s[t - c->tail_base];
+    if (sv > thr) {
+      if (open_len > 0) {
+        closed.push_back(NewSpan{open_start, open_len, row_of(open_start),
+                                 open_len >= cfg.min_span_len});
+        open_len = 0;
+      }
+      new_anchors.push_back(t);
+    } else {
+      if (open_len == 0) open_start = t;
+      ++open_len;
+    }
+  }
+  // spans now stored compressed: ids sc0 .. sc0 + nc - 1, in order
+  const int sc0 = c->sc;
+  std::vector<NewSpan> comp;
+  for (const NewSpan& sp : closed)
+    if (sp.compressed) comp.push_back(sp);
+  const int nc = (int)comp.size();
+  if (nc > 0) {
+    std::vector<int32_t> hstart(nc), hlen(nc);
+    for (int i = 0; i < nc; ++i) {
+      hstart[i] = comp[i].row;
+      hlen[i] = comp[i].len;
+    }
+    SEKV_HIP(hipMemcpyAsync(c->app_start + sc0, hstart.data(), (size_t)nc * 4,
+                            hipMemcpyHostToDevice, st));
+    SEKV_HIP(hipMemcpyAsync(c->clen + sc0, hlen.data(), (size_t)nc * 4, hipMemcpyHostToDevice, st));
+    SEKV_HIP(launch_log_len(c->clen + sc0, nc, c->lnn64 + sc0, c->lnn32 + sc0, st));
+    // retained ranks, then the blocks' place in the pool
+    SEKV_HIP(launch_span_rank(c->rank_by_dense, c->app_start, c->clen, ds, sc0, nc, scs, n_lg,
+                              cfg.max_rank, c->rank, st));
+    std::vector<int32_t> hr((size_t)n_lg * nc);
+    SEKV_HIP(hipMemcpy2DAsync(hr.data(), (size_t)nc * 4, c->rank + sc0, (size_t)scs * 4,
+                              (size_t)nc * 4, n_lg, hipMemcpyDeviceToHost, st));
+    SEKV_HIP(hipStreamSynchronize(st));
+    uint64_t off = c->pool_floats, fbytes = 0;
+    std::vector<uint64_t> hoff((size_t)n_lg * nc);
+    for (int lg = 0; lg < n_lg; ++lg)
+      for (int i = 0; i < nc; ++i) {
+        const FactorView fv = FactorView::packed(hr[(size_t)lg * nc + i], hlen[i]);
+        hoff[(size_t)lg * nc + i] = off;
+        off += fv.block_floats();
+        fbytes += fv.alg_bytes();
+      }
+    if (off > c->pool_cap_floats)
+      return undo(fail(SEKV_ERR_NOMEM, "the factor pool's append room is exhausted"));
+    int32_t* d_ids = nullptr;
+    Scratch scr;
+    if ((r = scr.alloc(&d_ids, (size_t)nc * 4, "appended span ids"))) return undo(r);
+    SEKV_HIP(hipMemcpy2DAsync(c->fac_off + sc0, (size_t)scs * 8, hoff.data(), (size_t)nc * 8,
+                              (size_t)nc * 8, n_lg, hipMemcpyHostToDevice, st));
+    for (int lg = 0; lg < n_lg; ++lg)
+      for (int i = 0; i < nc; ++i) {
+        c->h_rank[(size_t)lg * scs + sc0 + i] = hr[(size_t)lg * nc + i];
+        c->h_fac_off[(size_t)lg * scs + sc0 + i] = hoff[(size_t)lg * nc + i];
+      }
+    for (int i = 0; i < nc; ++i) c->h_clen.push_back(hlen[i]);
+    c->pool_floats = off;
+    c->factor_bytes += fbytes;
+    // means, summaries and factors from the spans' full-resolution rows
+    SEKV_HIP(launch_span_summarize(c->bf16(), c->dense_s, c->dense_k, c->dense_v, w_route, ds,
+                                   c->app_start, c->clen, sc0, nc, scs, L, Hkv, c->group, dr,
+                                   c->kbar, c->vbar, c->summ, st));
+    std::vector<int32_t> ids[3];
+    for (int i = 0; i < nc; ++i) {
+      const int m = std::min(hlen[i], kHeadDim);
+      ids[m <= 32 ? 0 : (m <= 64 ? 1 : 2)].push_back(sc0 + i);
+    }
+    const int max_m[3] = {32, 64, 128};
+    std::vector<int32_t> all_ids;
+    for (int b = 0; b < 3; ++b) all_ids.insert(all_ids.end(), ids[b].begin(), ids[b].end());
+    SEKV_HIP(hipMemcpyAsync(d_ids, all_ids.data(), (size_t)nc * 4, hipMemcpyHostToDevice, st));
+    for (int b = 0, at = 0; b < 3; at += (int)ids[b].size(), ++b) {
+      if (ids[b].empty()) continue;
+      for (int which = 0; which < 2; ++which)
+        SEKV_HIP(launch_span_svd(c->bf16(), which ? c->dense_v : c->dense_k, ds, c->app_start,
+                                 c->clen, d_ids + at, (int)ids[b].size(), scs, n_lg, c->rank,
+                                 c->fac_off, c->pool_dev, which, max_m[b], st));
+    }
+    // the compressed spans' rows leave the full-resolution set
+    std::vector<int32_t> ranges;
+    for (const NewSpan& sp : comp) {
+      ranges.push_back(sp.row);
+      ranges.push_back(sp.len);
+    }
+    SEKV_HIP(hipMemcpyAsync(c->app_ranges, ranges.data(), ranges.size() * 4,
+                            hipMemcpyHostToDevice, st));
+    const int vec = (int)(kHeadDim * eb / 16);
+    SEKV_HIP(launch_compact_rows(c->dense_k, 16, ds, vec, D, n_lg, c->app_ranges, nc, st));
+    SEKV_HIP(launch_compact_rows(c->dense_v, 16, ds, vec, D, n_lg, c->app_ranges, nc, st));
+    SEKV_HIP(launch_compact_rows(c->dense_s, 4, ds, 1, D, 1, c->app_ranges, nc, st));
+    SEKV_HIP(launch_compact_rows(c->rank_by_dense, 4, ds, 1, D, n_lg, c->app_ranges, nc, st));
+    for (int i = nc - 1; i >= 0; --i)
+      c->h_dense_pos.erase(c->h_dense_pos.begin() + comp[i].row,
+                           c->h_dense_pos.begin() + comp[i].row + comp[i].len);
+    for (const NewSpan& sp : comp) D -= sp.len;
+    SEKV_HIP(hipStreamSynchronize(st));  // the host staging vectors of this block end here
+  }
+
+  // ---- 3. the span table, anchors and row positions on the device -----------
+  std::vector<int32_t> hs, hl, hcs;
+  std::vector<uint8_t> hk;
+  for (const NewSpan& sp : closed) {
+    hs.push_back(sp.start);
+    hl.push_back(sp.len);
+    hk.push_back(sp.compressed ? 0 : 1);
+  }
+  for (size_t i = 0; i < closed.size(); ++i)
+    if (closed[i].compressed) hcs.push_back(c->n_spans + (int)i);
+  if (!closed.empty()) {
+    const size_t k = closed.size();
+    SEKV_HIP(hipMemcpyAsync(c->span_start + c->n_spans, hs.data(), k * 4, hipMemcpyHostToDevice, st));
+    SEKV_HIP(hipMemcpyAsync(c->span_len + c->n_spans, hl.data(), k * 4, hipMemcpyHostToDevice, st));
+    SEKV_HIP(hipMemcpyAsync(c->kind + c->n_spans, hk.data(), k, hipMemcpyHostToDevice, st));
+  }
+  if (!hcs.empty()) {
+    SEKV_HIP(hipMemcpyAsync(c->cspan + sc0, hcs.data(), hcs.size() * 4, hipMemcpyHostToDevice, st));
+    std::vector<int32_t> cst(nc);
+    for (int i = 0; i < nc; ++i) cst[i] = comp[i].start;
+    SEKV_HIP(hipMemcpyAsync(c->cstart + sc0, cst.data(), (size_t)nc * 4, hipMemcpyHostToDevice, st));
+  }
+  if (!new_anchors.empty())
+    SEKV_HIP(hipMemcpyAsync(c->anchors + c->n_anchors, new_anchors.data(), new_anchors.size() * 4,
+                            hipMemcpyHostToDevice, st));
+  // the row positions changed from the first removed row (or the new rows) on
+  const int first = nc > 0 ? comp[0].row : D0;
+  if (D > first)
+    SEKV_HIP(hipMemcpyAsync(c->dense_pos + first, c->h_dense_pos.data() + first,
+                            (size_t)(D - first) * 4, hipMemcpyHostToDevice, st));
+  SEKV_HIP(hipStreamSynchronize(st));
+  c->open_start = open_start;
+  c->open_len = open_len;
+  c->n_spans += (int)closed.size();
+  c->n_anchors += (int)new_anchors.size();
+  c->sc += nc;
+  c->n_dense = D;
+  c->n_tokens = N;
+  c->n_appended += n_new;
+  c->geom = make_layer_geom(Hq, Hkv, dr, D, c->sc, ds, scs);
+  return SEKV_OK;
+}
+
+sekv_status sekv_append_tokens(sekv_cache* c, int32_t n_new, const float* surprisal_dev,
+                               const void* k_dev, const void* v_dev, const float* w_route_dev,
+                               const int32_t* rank_dev, hipStream_t stream) {
+  if (!c) return fail(SEKV_ERR_INVALID, "cache is NULL");
+  if (!surprisal_dev || !k_dev || !v_dev || !w_route_dev)
+    return fail(SEKV_ERR_INVALID, "surprisal, keys, values and w_route must be non-NULL");
+  if (n_new < 1) return fail(SEKV_ERR_INVALID, "n_new must be >= 1 (got %d)", n_new);
+  if (c->cfg.append_capacity <= 0)
+    return fail(SEKV_ERR_UNSUPPORTED, "the cache was built without append_capacity");
+  if ((long long)c->n_appended + n_new > c->cfg.append_capacity)
+    return fail(SEKV_ERR_NOMEM, "appending %d tokens exceeds the append capacity (%d of %d used)",
+                n_new, c->n_appended, c->cfg.append_capacity);
+  return append_impl(c, n_new, surprisal_dev, k_dev, v_dev, w_route_dev, rank_dev, stream);
+}
+
 sekv_status sekv_cache_info_get(const sekv_cache* c, sekv_cache_info* out) {
   if (!c || !out) return fail(SEKV_ERR_INVALID, "cache and out must be non-NULL");
   const int L = c->cfg.n_layers, Hkv = c->cfg.n_kv_heads, Hq = c->cfg.n_q_heads;
@@ -413,6 +709,10 @@ sekv_status sekv_cache_info_get(const sekv_cache* c, sekv_cache_info* out) {
                         (uint64_t)L * Hq * c->sc * c->cfg.route_dim * eb;
   out->factor_bytes = c->factor_bytes;
   out->factor_pool_bytes = (uint64_t)c->pool_floats * 4;
+  out->open_start = c->open_start;
+  out->open_len = c->open_len;
+  out->n_appended = c->n_appended;
+  out->append_capacity = c->cfg.append_capacity;
   return SEKV_OK;
 }
 
@@ -443,21 +743,24 @@ sekv_status sekv_cache_copy_group(const sekv_cache* c, int32_t layer, int32_t kv
   const size_t eb = c->kv_elem();
   const int sc = c->sc, G = c->group, dr = c->cfg.route_dim;
   const size_t lg = (size_t)layer * c->cfg.n_kv_heads + kv_head;
+  const size_t scs = c->scs;
   if (!sc) return SEKV_OK;
   if (kbar)
-    SEKV_HIP(hipMemcpy(kbar, (const char*)c->kbar + lg * sc * kHeadDim * eb, (size_t)sc * kHeadDim * eb,
-                       hipMemcpyDeviceToHost));
+    SEKV_HIP(hipMemcpy(kbar, (const char*)c->kbar + lg * scs * kHeadDim * eb,
+                       (size_t)sc * kHeadDim * eb, hipMemcpyDeviceToHost));
   if (vbar)
-    SEKV_HIP(hipMemcpy(vbar, (const char*)c->vbar + lg * sc * kHeadDim * eb, (size_t)sc * kHeadDim * eb,
-                       hipMemcpyDeviceToHost));
+    SEKV_HIP(hipMemcpy(vbar, (const char*)c->vbar + lg * scs * kHeadDim * eb,
+                       (size_t)sc * kHeadDim * eb, hipMemcpyDeviceToHost));
   if (summary) {
     const size_t h0 = (size_t)layer * c->cfg.n_q_heads + (size_t)kv_head * G;
-    SEKV_HIP(hipMemcpy(summary, (const char*)c->summ + h0 * sc * dr * eb, (size_t)G * sc * dr * eb,
-                       hipMemcpyDeviceToHost));
+    for (int hl = 0; hl < G; ++hl)
+      SEKV_HIP(hipMemcpy((char*)summary + (size_t)hl * sc * dr * eb,
+                         (const char*)c->summ + (h0 + hl) * scs * dr * eb, (size_t)sc * dr * eb,
+                         hipMemcpyDeviceToHost));
   }
   for (int j = 0; j < sc; ++j) {
-    if (rank_k) rank_k[j] = rank_of(c->h_rank[lg * sc + j], 0);
-    if (rank_v) rank_v[j] = rank_of(c->h_rank[lg * sc + j], 1);
+    if (rank_k) rank_k[j] = rank_of(c->h_rank[lg * scs + j], 0);
+    if (rank_v) rank_v[j] = rank_of(c->h_rank[lg * scs + j], 1);
   }
   return SEKV_OK;
 }
@@ -468,7 +771,7 @@ sekv_status sekv_cache_copy_factors(const sekv_cache* c, int32_t layer, int32_t 
   if (layer < 0 || layer >= c->cfg.n_layers || kv_head < 0 || kv_head >= c->cfg.n_kv_heads ||
       span < 0 || span >= c->sc || (kv != 0 && kv != 1))
     return fail(SEKV_ERR_INVALID, "layer/kv_head/span/kv out of range");
-  const size_t idx = ((size_t)layer * c->cfg.n_kv_heads + kv_head) * c->sc + span;
+  const size_t idx = ((size_t)layer * c->cfg.n_kv_heads + kv_head) * c->scs + span;
   const int n = c->h_clen[span];
   const FactorView fv = FactorView::packed(c->h_rank[idx], n);
   const int r = fv.r(kv), r4 = fv.r4(kv);
@@ -507,7 +810,7 @@ sekv_status check_route_out(const sekv_route_out* out) {
 // layer slices of the cache, in the layout the layer kernel reads
 LayerArgs layer_args(const sekv_cache* c, int32_t layer, const float* q, const float* proj,
                      const float* tau, const sekv_route_out* ro, float* o, void* ws) {
-  const int Hq = c->cfg.n_q_heads, Hkv = c->cfg.n_kv_heads, sc = c->sc, D = c->n_dense;
+  const int Hq = c->cfg.n_q_heads, Hkv = c->cfg.n_kv_heads;
   const size_t eb = c->kv_elem();
   const size_t lg0 = (size_t)layer * Hkv;
   const bool host_tier = c->cfg.factor_tier == SEKV_TIER_HOST_PINNED;
@@ -515,17 +818,17 @@ LayerArgs layer_args(const sekv_cache* c, int32_t layer, const float* q, const f
   a.q = q;
   a.proj = proj;
   a.tau = tau;
-  a.summ = (const char*)c->summ + (size_t)layer * Hq * sc * c->cfg.route_dim * eb;
+  a.summ = (const char*)c->summ + (size_t)layer * Hq * c->scs * c->cfg.route_dim * eb;
   a.lnn64 = c->lnn64;
   a.lnn32 = c->lnn32;
   a.gamma = c->cfg.gamma;
-  a.dense_k = (const char*)c->dense_k + lg0 * D * kHeadDim * eb;
-  a.dense_v = (const char*)c->dense_v + lg0 * D * kHeadDim * eb;
-  a.kbar = (const char*)c->kbar + lg0 * sc * kHeadDim * eb;
-  a.vbar = (const char*)c->vbar + lg0 * sc * kHeadDim * eb;
+  a.dense_k = (const char*)c->dense_k + lg0 * c->ds * kHeadDim * eb;
+  a.dense_v = (const char*)c->dense_v + lg0 * c->ds * kHeadDim * eb;
+  a.kbar = (const char*)c->kbar + lg0 * c->scs * kHeadDim * eb;
+  a.vbar = (const char*)c->vbar + lg0 * c->scs * kHeadDim * eb;
   a.clen = c->clen;
-  a.rank = c->rank + lg0 * sc;
-  a.fac_off = c->fac_off + lg0 * sc;
+  a.rank = c->rank + lg0 * c->scs;
+  a.fac_off = c->fac_off + lg0 * c->scs;
   a.pool = host_tier ? c->stage : c->pool_dev;
   a.off_base = host_tier ? c->layer_base[layer] : 0;
   if (ro) {
@@ -539,6 +842,7 @@ LayerArgs layer_args(const sekv_cache* c, int32_t layer, const float* q, const f
   a.o = o;
   a.part = (float*)ws;
   a.chunk_bits = c->chunk_bits;
+  a.zcount = c->zcount;
   a.zero_block = c->zero_block;
   return a;
 }
@@ -577,8 +881,9 @@ static sekv_status attn_impl(const sekv_cache* c, int32_t layer, const float* q_
   const LayerArgs a = layer_args(c, layer, q_dev, nullptr, nullptr, route, o_dev, ws_dev);
   const int sc = c->sc;
   if (c->cfg.factor_tier == SEKV_TIER_DEVICE || sc == 0) {
-    SEKV_HIP(launch_layer(c->bf16(), kDense | kZoom, c->geom, a, stream));
-    SEKV_HIP(launch_layer_tail(kMerge, c->geom, a, stream));
+    SEKV_HIP(launch_layer(c->bf16(), kDense, c->geom, a, stream));
+    SEKV_HIP(launch_zoom(c->geom, a, stream));
+    SEKV_HIP(launch_layer_tail(kMerge | (sc ? kZoomSplit : 0), c->geom, a, stream));
     return SEKV_OK;
   }
   // host tier: the zoomed spans' factors are gathered into device staging on
@@ -601,7 +906,7 @@ static sekv_status attn_impl(const sekv_cache* c, int32_t layer, const float* q_
       cm->res_epoch = 1;
     }
     SEKV_HIP(launch_resident_fetch(c->geom, layer, route->union_list, route->union_count,
-                                   c->clen, c->rank + lg0 * sc, c->fac_off + lg0 * sc,
+                                   c->clen, c->rank + lg0 * c->scs, c->fac_off + lg0 * c->scs,
                                    c->layer_base[layer], c->pool_host_dev, c->res, c->res_epoch,
                                    fst));
     az.pool = c->res.arena;
@@ -609,13 +914,14 @@ static sekv_status attn_impl(const sekv_cache* c, int32_t layer, const float* q_
     az.off_base = 0;
   } else {
     SEKV_HIP(launch_fetch_gather(c->geom, route->union_list, route->union_count, c->clen,
-                                 c->rank + lg0 * sc, c->fac_off + lg0 * sc, c->layer_base[layer],
+                                 c->rank + lg0 * c->scs, c->fac_off + lg0 * c->scs,
+                                 c->layer_base[layer],
                                  c->pool_host_dev, c->stage, fst));
   }
   if (fst != stream) SEKV_HIP(hipEventRecord(c->ev_fetch, fst));
   SEKV_HIP(launch_layer(c->bf16(), kDense, c->geom, a, stream));
   if (fst != stream) SEKV_HIP(hipStreamWaitEvent(stream, c->ev_fetch, 0));
-  SEKV_HIP(launch_layer(c->bf16(), kZoom | kZoomSplit, c->geom, az, stream));
+  SEKV_HIP(launch_zoom(c->geom, az, stream));
   SEKV_HIP(launch_layer_tail(kZoomSplit | kMerge, c->geom, az, stream));
   return SEKV_OK;
 }
@@ -656,8 +962,9 @@ sekv_status sekv_route_attn(const sekv_cache* c, int32_t layer, const float* q_d
     return attn_impl(c, layer, q_dev, route, o_dev, ws_dev, stream, fetch_stream);
   }
   const LayerArgs a = layer_args(c, layer, q_dev, proj_dev, tau_dev, route, o_dev, ws_dev);
-  SEKV_HIP(launch_layer(c->bf16(), kRoute | kDense | kZoom, c->geom, a, stream));
-  SEKV_HIP(launch_layer_tail(kMerge | kLists, c->geom, a, stream));
+  SEKV_HIP(launch_layer(c->bf16(), kRoute | kDense, c->geom, a, stream));
+  SEKV_HIP(launch_zoom(c->geom, a, stream));
+  SEKV_HIP(launch_layer_tail(kMerge | kLists | kZoomSplit, c->geom, a, stream));
   return SEKV_OK;
 }
 
@@ -713,8 +1020,8 @@ sekv_status sekv_route_attn_noalloc(const sekv_cache* c, int32_t layer, const fl
                          (size_t)SEKV_NOALLOC_SCRATCH_BYTES, stream, fetch_stream);
 }
 
-sekv_status sekv_cap_budget(const sekv_cache* c, const sekv_route_out* route,
-                            int64_t budget_tokens, hipStream_t stream) {
+static sekv_status cap_impl(const sekv_cache* c, const sekv_route_out* route,
+                            int64_t budget_tokens, hipStream_t stream, bool layer_scope) {
   sekv_status r;
   if (!c) return fail(SEKV_ERR_INVALID, "cache is NULL");
   if ((r = check_route_out(route))) return r;
@@ -729,8 +1036,19 @@ sekv_status sekv_cap_budget(const sekv_cache* c, const sekv_route_out* route,
   if (c->sc == 0) return SEKV_OK;
   SEKV_HIP(launch_cap_budget(c->sc, c->cfg.n_kv_heads, c->group, (long long)budget_tokens,
                              c->clen, route->prob, route->mask, route->list, route->count,
-                             route->union_list, route->union_count, stream));
+                             route->union_list, route->union_count,
+                             layer_scope ? c->cap_drop : nullptr, stream));
   return SEKV_OK;
+}
+
+sekv_status sekv_cap_budget(const sekv_cache* c, const sekv_route_out* route,
+                            int64_t budget_tokens, hipStream_t stream) {
+  return cap_impl(c, route, budget_tokens, stream, false);
+}
+
+sekv_status sekv_cap_budget_layer(const sekv_cache* c, const sekv_route_out* route,
+                                  int64_t budget_tokens, hipStream_t stream) {
+  return cap_impl(c, route, budget_tokens, stream, true);
 }
 
 sekv_status sekv_apply_gates(sekv_cache* c, const float* key_gates_dev,
@@ -743,7 +1061,8 @@ sekv_status sekv_apply_gates(sekv_cache* c, const float* key_gates_dev,
                 "its factors in host memory");
   const int L = c->cfg.n_layers, Hkv = c->cfg.n_kv_heads, sc = c->sc, R = c->cfg.max_rank;
   if (sc == 0) return SEKV_OK;
-  const size_t nb = (size_t)L * Hkv * sc;
+  const size_t nb = (size_t)L * Hkv * sc;      // gate rows [L][Hkv][S_c]
+  const size_t nbs = (size_t)L * Hkv * c->scs;  // table entries [L][Hkv][scs]
   std::vector<float> hg[2];
   for (int kv = 0; kv < 2; ++kv) {
     hg[kv].resize(nb * R);
@@ -753,20 +1072,21 @@ sekv_status sekv_apply_gates(sekv_cache* c, const float* key_gates_dev,
   SEKV_HIP(hipStreamSynchronize(st));
   // which components stay, per matrix: gate >= eps, at least one (the largest
   // gate, the lowest index on ties); the new pool keeps the layout of the old one
-  std::vector<uint8_t> kept(nb * 2 * R, 0);
-  std::vector<int32_t> nr(nb);
-  std::vector<uint64_t> noff(nb), nbase(L + 1, 0);
+  std::vector<uint8_t> kept(nbs * 2 * R, 0);
+  std::vector<int32_t> nr(nbs, 0);
+  std::vector<uint64_t> noff(nbs, 0), nbase(L + 1, 0);
   uint64_t off = 0, fbytes = 0;
   for (int l = 0; l < L; ++l) {
     nbase[l] = off;
     for (int g = 0; g < Hkv; ++g)
       for (int j = 0; j < sc; ++j) {
-        const size_t idx = ((size_t)l * Hkv + g) * sc + j;
+        const size_t idx = ((size_t)l * Hkv + g) * c->scs + j;
+        const size_t gi = ((size_t)l * Hkv + g) * sc + j;
         const int n = c->h_clen[j];
         int nk[2];
         for (int kv = 0; kv < 2; ++kv) {
           const int r = rank_of(c->h_rank[idx], kv);
-          const float* gg = &hg[kv][idx * R];
+          const float* gg = &hg[kv][gi * R];
           uint8_t* kp = &kept[(idx * 2 + kv) * R];
           int k = 0, best = 0;
           for (int i = 0; i < r; ++i) {
@@ -797,17 +1117,19 @@ sekv_status sekv_apply_gates(sekv_cache* c, const float* key_gates_dev,
   uint64_t* d_off = nullptr;
   float* npool = nullptr;
   if ((r = scr.alloc(&d_kept, kept.size(), "gate kept components"))) return r;
-  if ((r = scr.alloc(&d_rank, nb * 4, "gated ranks"))) return r;
-  if ((r = scr.alloc(&d_off, nb * 8, "gated offsets"))) return r;
-  if ((r = scr.alloc(&npool, (size_t)off * 4, "gated factor pool"))) return r;
+  if ((r = scr.alloc(&d_rank, nbs * 4, "gated ranks"))) return r;
+  if ((r = scr.alloc(&d_off, nbs * 8, "gated offsets"))) return r;
+  // the repacked pool keeps the room an append capacity reserved
+  const uint64_t room = c->pool_cap_floats - c->pool_floats;
+  if ((r = scr.alloc(&npool, (size_t)(off + room) * 4, "gated factor pool"))) return r;
   SEKV_HIP(hipMemcpyAsync(d_kept, kept.data(), kept.size(), hipMemcpyHostToDevice, st));
-  SEKV_HIP(hipMemcpyAsync(d_rank, nr.data(), nb * 4, hipMemcpyHostToDevice, st));
-  SEKV_HIP(hipMemcpyAsync(d_off, noff.data(), nb * 8, hipMemcpyHostToDevice, st));
-  SEKV_HIP(hipMemsetAsync(npool, 0, (size_t)off * 4, st));
+  SEKV_HIP(hipMemcpyAsync(d_rank, nr.data(), nbs * 4, hipMemcpyHostToDevice, st));
+  SEKV_HIP(hipMemcpyAsync(d_off, noff.data(), nbs * 8, hipMemcpyHostToDevice, st));
+  SEKV_HIP(hipMemsetAsync(npool, 0, (size_t)(off + room) * 4, st));
   SEKV_HIP(launch_gate_repack(c->pool_dev, c->fac_off, c->rank, npool, d_off, d_rank, d_kept,
-                              key_gates_dev, value_gates_dev, c->clen, sc, R, nb, st));
-  SEKV_HIP(hipMemcpyAsync(c->rank, d_rank, nb * 4, hipMemcpyDeviceToDevice, st));
-  SEKV_HIP(hipMemcpyAsync(c->fac_off, d_off, nb * 8, hipMemcpyDeviceToDevice, st));
+                              key_gates_dev, value_gates_dev, c->clen, sc, c->scs, R, nbs, st));
+  SEKV_HIP(hipMemcpyAsync(c->rank, d_rank, nbs * 4, hipMemcpyDeviceToDevice, st));
+  SEKV_HIP(hipMemcpyAsync(c->fac_off, d_off, nbs * 8, hipMemcpyDeviceToDevice, st));
   SEKV_HIP(hipStreamSynchronize(st));
   // the new pool replaces the old one
   scr.release(npool);
@@ -819,6 +1141,7 @@ sekv_status sekv_apply_gates(sekv_cache* c, const float* key_gates_dev,
   c->h_fac_off = std::move(noff);
   c->layer_base = std::move(nbase);
   c->pool_floats = off;
+  c->pool_cap_floats = off + room;
   c->factor_bytes = fbytes;
   return SEKV_OK;
 }
@@ -851,7 +1174,7 @@ sekv_status sekv_set_residency(sekv_cache* c, uint64_t capacity_bytes, uint64_t 
   c->residency_free();
   if (!capacity_bytes) return SEKV_OK;
   const uint64_t slots_off = (c->stage_floats + 63) / 64 * 64;
-  const size_t n_off = std::max<size_t>((size_t)c->cfg.n_kv_heads * c->sc, 1);
+  const size_t n_off = std::max<size_t>((size_t)c->cfg.n_kv_heads * c->scs, 1);
   struct Buf { void** p; size_t bytes; const char* what; } bufs[] = {
       {(void**)&c->res.arena, (size_t)(slots_off + n_sets * slot_floats) * 4, "residency arena"},
       {(void**)&c->res.claim, (size_t)n_sets * 8, "residency claims"},
@@ -955,9 +1278,10 @@ static sekv_status batch_impl(const sekv_cache* const* caches, int32_t batch, in
     ++nb;
   }
   if (nb > 0) {
-    const int mode = with_route ? (kRoute | kDense | kZoom) : (kDense | kZoom);
-    const int tail = with_route ? (kMerge | kLists) : kMerge;
+    const int mode = with_route ? (kRoute | kDense) : kDense;
+    const int tail = (with_route ? (kMerge | kLists) : kMerge) | kZoomSplit;
     SEKV_HIP(launch_layer_batch(caches[0]->bf16(), mode, caches[0]->geom.group, b, nb, stream));
+    SEKV_HIP(launch_zoom_batch(caches[0]->geom.group, b, nb, stream));
     SEKV_HIP(launch_layer_tail_batch(tail, caches[0]->geom.group, b, nb, stream));
   }
   return SEKV_OK;

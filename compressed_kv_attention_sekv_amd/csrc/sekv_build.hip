@@ -191,27 +191,28 @@ hipError_t launch_log_len(const int32_t* clen, int sc, double* lnn64, float* lnn
   return hipGetLastError();
 }
 
-// retained rank r_j = min(max(requested, 1), n_j, d, R)
+// retained rank r_j = min(max(requested, 1), n_j, d, R) of spans j0 .. j0 + n - 1
+// (the request is that of the span's first row of rank_by_pos)
 __global__ void span_rank_kernel(const int32_t* rank_by_pos, const int32_t* cstart,
-                                 const int32_t* clen, int n_tokens, int sc, int max_rank,
-                                 int32_t* rank) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+                                 const int32_t* clen, int n_tokens, int j0, int n, int stride,
+                                 int max_rank, int32_t* rank) {
+  const int j = j0 + (int)(blockIdx.x * blockDim.x + threadIdx.x);
   const int lg = blockIdx.y;
-  if (j >= sc) return;
+  if (j >= j0 + n) return;
   int r = rank_by_pos ? rank_by_pos[(size_t)lg * n_tokens + cstart[j]] : max_rank;
   r = max(r, 1);
   r = min(r, clen[j]);
   r = min(r, kHeadDim);
   r = min(r, max_rank);
-  rank[(size_t)lg * sc + j] = pack_ranks(r, r);   // keys and values alike
+  rank[(size_t)lg * stride + j] = pack_ranks(r, r);   // keys and values alike
 }
 
 hipError_t launch_span_rank(const int32_t* rank_by_pos, const int32_t* cstart,
-                            const int32_t* clen, int n_tokens, int sc, int n_lg, int max_rank,
-                            int32_t* rank, hipStream_t st) {
-  if (sc == 0) return hipSuccess;
-  hipLaunchKernelGGL(span_rank_kernel, dim3((sc + 255) / 256, n_lg), dim3(256), 0, st,
-                     rank_by_pos, cstart, clen, n_tokens, sc, max_rank, rank);
+                            const int32_t* clen, int n_tokens, int j0, int n, int stride,
+                            int n_lg, int max_rank, int32_t* rank, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(span_rank_kernel, dim3((n + 255) / 256, n_lg), dim3(256), 0, st,
+                     rank_by_pos, cstart, clen, n_tokens, j0, n, stride, max_rank, rank);
   return hipGetLastError();
 }
 
@@ -221,7 +222,8 @@ hipError_t launch_span_rank(const int32_t* rank_by_pos, const int32_t* cstart,
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ src,
                                                           int n_tokens, const int32_t* pos,
-                                                          int n_rows, int vec_per_row,
+                                                          int n_rows, int dst_stride,
+                                                          int vec_per_row,
                                                           uint4* __restrict__ dst) {
   const int lg = blockIdx.y;
   const int rows_per_block = 256 / vec_per_row;
@@ -229,17 +231,17 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restric
   const int c = threadIdx.x % vec_per_row;
   if (r >= n_rows || threadIdx.x >= rows_per_block * vec_per_row) return;
   const size_t s_off = ((size_t)lg * n_tokens + pos[r]) * vec_per_row + c;
-  const size_t d_off = ((size_t)lg * n_rows + r) * vec_per_row + c;
+  const size_t d_off = ((size_t)lg * dst_stride + r) * vec_per_row + c;
   dst[d_off] = src[s_off];
 }
 
 hipError_t launch_gather_dense(int bf16, const void* src, int n_tokens, const int32_t* pos,
-                               int n_dense, int n_lg, void* dst, hipStream_t st) {
+                               int n_dense, int dst_stride, int n_lg, void* dst, hipStream_t st) {
   if (n_dense == 0) return hipSuccess;
   const int vec = bf16 ? kHeadDim * 2 / 16 : kHeadDim * 4 / 16;
   const int rows = 256 / vec;
   hipLaunchKernelGGL(gather_rows_kernel, dim3((n_dense + rows - 1) / rows, n_lg), dim3(256), 0,
-                     st, (const uint4*)src, n_tokens, pos, n_dense, vec, (uint4*)dst);
+                     st, (const uint4*)src, n_tokens, pos, n_dense, dst_stride, vec, (uint4*)dst);
   return hipGetLastError();
 }
 
@@ -252,10 +254,11 @@ template <typename T>
 __global__ __launch_bounds__(kHeadDim) void span_summarize_kernel(
     const float* __restrict__ s, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ w_route, int n_tokens, const int32_t* __restrict__ cstart,
-    const int32_t* __restrict__ clen, int sc, int hkv, int group, int dr, T* __restrict__ kbar,
+    const int32_t* __restrict__ clen, int j0, int sc, int hkv, int group, int dr,
+    T* __restrict__ kbar,
     T* __restrict__ vbar, T* __restrict__ summ) {
   __shared__ double km_sh[kHeadDim];
-  const int j = blockIdx.x, lg = blockIdx.y;
+  const int j = j0 + (int)blockIdx.x, lg = blockIdx.y;
   const int layer = lg / hkv, g = lg % hkv;
   const int dim = threadIdx.x;
   const int b = cstart[j], n = clen[j];
@@ -288,18 +291,103 @@ __global__ __launch_bounds__(kHeadDim) void span_summarize_kernel(
 
 hipError_t launch_span_summarize(int bf16, const float* s, const void* k, const void* v,
                                  const float* w_route, int n_tokens, const int32_t* cstart,
-                                 const int32_t* clen, int sc, int n_layers, int hkv, int group,
-                                 int dr, void* kbar, void* vbar, void* summ, hipStream_t st) {
-  if (sc == 0) return hipSuccess;
-  dim3 grid(sc, n_layers * hkv);
+                                 const int32_t* clen, int j0, int n, int sc, int n_layers,
+                                 int hkv, int group, int dr, void* kbar, void* vbar, void* summ,
+                                 hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  dim3 grid(n, n_layers * hkv);
   if (bf16)
     hipLaunchKernelGGL(span_summarize_kernel<uint16_t>, grid, dim3(kHeadDim), 0, st, s,
                        (const uint16_t*)k, (const uint16_t*)v, w_route, n_tokens, cstart, clen,
-                       sc, hkv, group, dr, (uint16_t*)kbar, (uint16_t*)vbar, (uint16_t*)summ);
+                       j0, sc, hkv, group, dr, (uint16_t*)kbar, (uint16_t*)vbar, (uint16_t*)summ);
   else
     hipLaunchKernelGGL(span_summarize_kernel<float>, grid, dim3(kHeadDim), 0, st, s,
-                       (const float*)k, (const float*)v, w_route, n_tokens, cstart, clen, sc,
-                       hkv, group, dr, (float*)kbar, (float*)vbar, (float*)summ);
+                       (const float*)k, (const float*)v, w_route, n_tokens, cstart, clen, j0,
+                       sc, hkv, group, dr, (float*)kbar, (float*)vbar, (float*)summ);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Window append support.
+//
+// gather_words: dst[lg][r] = src[lg][pos[r]] for 32-bit words (surprisal or
+// requested rank of each full-resolution row).
+// compact_rows: remove sorted, disjoint row ranges [a_i, a_i + n_i) from rows
+// [0, n_rows) of every (layer, KV head) block (one workgroup each), moving the
+// rows after them down.  Rows only move to lower indices, so a workgroup that
+// reads a chunk of rows, waits, then writes it never overwrites a row of a
+// later chunk before reading it.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gather_words_kernel(const uint32_t* __restrict__ src,
+                                                           int src_stride, const int32_t* pos,
+                                                           int n, int dst_stride,
+                                                           uint32_t* __restrict__ dst) {
+  const int lg = blockIdx.y;
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r < n) dst[(size_t)lg * dst_stride + r] = src[(size_t)lg * src_stride + pos[r]];
+}
+
+hipError_t launch_gather_words(const uint32_t* src, int src_stride, const int32_t* pos, int n,
+                               int dst_stride, int n_lg, uint32_t* dst, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_words_kernel, dim3((n + 255) / 256, n_lg), dim3(256), 0, st, src,
+                     src_stride, pos, n, dst_stride, dst);
+  return hipGetLastError();
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void compact_rows_kernel(E* __restrict__ base, int stride,
+                                                           int elems_per_row, int n_rows,
+                                                           const int32_t* __restrict__ ranges,
+                                                           int n_ranges) {
+  constexpr int kUnroll = 4;
+  E* rows = base + (size_t)blockIdx.x * stride * elems_per_row;
+  const int rows_per_pass = 256 / elems_per_row;
+  const int first = ranges[0];
+  for (int r0 = first; r0 < n_rows; r0 += rows_per_pass * kUnroll) {
+    E val[kUnroll];
+    int dst[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int t = threadIdx.x;
+      const int r = r0 + (u * rows_per_pass) + t / elems_per_row;
+      const int e = t % elems_per_row;
+      dst[u] = -1;
+      if (t < rows_per_pass * elems_per_row && r < n_rows) {
+        int removed = 0;
+        bool gone = false;
+        for (int i = 0; i < n_ranges; ++i) {
+          const int a = ranges[2 * i], len = ranges[2 * i + 1];
+          if (r >= a + len) removed += len;
+          else if (r >= a) gone = true;
+        }
+        if (!gone) {
+          val[u] = rows[(size_t)r * elems_per_row + e];
+          dst[u] = (r - removed) * elems_per_row + e;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (dst[u] >= 0) rows[dst[u]] = val[u];
+    __syncthreads();
+  }
+}
+
+hipError_t launch_compact_rows(void* base, int elem_bytes, int stride, int elems_per_row,
+                               int n_rows, int n_lg, const int32_t* ranges, int n_ranges,
+                               hipStream_t st) {
+  if (n_ranges == 0 || n_lg == 0) return hipSuccess;
+  if (elems_per_row < 1 || elems_per_row > 256) return hipErrorInvalidValue;
+  if (elem_bytes == 16)
+    hipLaunchKernelGGL(compact_rows_kernel<uint4>, dim3(n_lg), dim3(256), 0, st, (uint4*)base,
+                       stride, elems_per_row, n_rows, ranges, n_ranges);
+  else if (elem_bytes == 4)
+    hipLaunchKernelGGL(compact_rows_kernel<uint32_t>, dim3(n_lg), dim3(256), 0, st,
+                       (uint32_t*)base, stride, elems_per_row, n_rows, ranges, n_ranges);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -10,6 +10,10 @@
 // kept set is the longest prefix that fits).  A dropped span reverts to its
 // coarse entry for every head of the group.
 //
+// A second reading takes one budget for the whole layer: one order over the
+// candidates of every KV head (ties to the lower KV head, then the lower span
+// id), whose kept prefix bounds the total the layer reconstructs.
+//
 // One workgroup of 512 threads per KV head.  The order is never materialised:
 // each candidate's inclusive prefix length is a sum over the candidates that
 // precede it, counted against LDS tiles of (key, id, length), so the decisions
@@ -87,10 +91,18 @@ struct alignas(16) CapEnt {
   int len;
 };
 
-template <int G>
+// Which phases a launch runs: both, for one KV head's own budget; or, for one
+// budget over the whole layer, the decisions (counted against every KV head's
+// candidates, written as one byte per union position) and then, in a launch
+// of its own, their application (the decisions read other heads' masks and
+// unions, which the application rewrites).
+enum CapPhase : int { kCapBoth = 0, kCapDecide = 1, kCapApply = 2 };
+
+template <int G, int PHASE>
 __global__ __launch_bounds__(kCapThreads) void cap_budget_kernel(
-    int sc, long long budget, const int32_t* __restrict__ clen, const double* __restrict__ prob,
-    uint8_t* mask, int32_t* list, int32_t* count, int32_t* ulist, int32_t* ucount) {
+    int sc, int hkv, long long budget, const int32_t* __restrict__ clen,
+    const double* __restrict__ prob, uint8_t* mask, int32_t* list, int32_t* count, int32_t* ulist,
+    int32_t* ucount, uint8_t* __restrict__ drop) {
   __shared__ CapEnt s_ent[kCapTile];
   __shared__ int s_wave[G + 1][kCapWaves];
   extern __shared__ uint32_t s_drop[];  // one bit per union position
@@ -101,48 +113,69 @@ __global__ __launch_bounds__(kCapThreads) void cap_budget_kernel(
   const int U = ucount[g];
   for (int w = tid; w < (U + 31) / 32; w += kCapThreads) s_drop[w] = 0u;
 
-  // 1. inclusive prefix length of every candidate in (key desc, id asc) order;
-  //    with a single tile (U <= kCapTile) a candidate's own key comes from it
-  const bool one_tile = U <= kCapTile;
-  for (int base = 0; base < U; base += kCapThreads) {
-    const int i = base + tid;
-    const bool have = i < U;
-    int ji = 0;
-    double ki = 0.0;
-    if (have && !one_tile) {
-      ji = ul[i];
-      ki = cap_key<G>(mask, prob, sc, h0, ji);
-    }
-    long long S = 0;
-    for (int t0 = 0; t0 < U; t0 += kCapTile) {
-      const int tn = min(kCapTile, U - t0);
-      __syncthreads();
-      for (int k = tid; k < tn; k += kCapThreads) {
-        const int j = ul[t0 + k];
-        CapEnt e;
-        e.key = cap_key<G>(mask, prob, sc, h0, j);
-        e.id = j;
-        e.len = clen[j];
-        s_ent[k] = e;
+  // 1. inclusive prefix length of every candidate in (key desc, KV head asc,
+  //    id asc) order, over this KV head's candidates or over every KV head's
+  //    (layer scope); with a single tile of its own candidates a candidate's
+  //    own key comes from it
+  if (PHASE != kCapApply) {
+    const int ga = PHASE == kCapDecide ? 0 : g, gb = PHASE == kCapDecide ? hkv : g + 1;
+    const bool one_tile = PHASE == kCapBoth && U <= kCapTile;
+    for (int base = 0; base < U; base += kCapThreads) {
+      const int i = base + tid;
+      const bool have = i < U;
+      int ji = 0;
+      double ki = 0.0;
+      if (have && !one_tile) {
+        ji = ul[i];
+        ki = cap_key<G>(mask, prob, sc, h0, ji);
       }
-      __syncthreads();
-      if (have) {
-        if (one_tile) {
-          ki = s_ent[i].key;
-          ji = s_ent[i].id;
-        }
-        // branch-free: every entry is read (one broadcast 16-byte LDS read)
-        // and counted with a select, so the reads of an unrolled group are
-        // all in flight together
+      long long S = 0;
+      for (int go = ga; go < gb; ++go) {
+        const int32_t* ulo = ulist + (size_t)go * sc;
+        const int Uo = ucount[go];
+        for (int t0 = 0; t0 < Uo; t0 += kCapTile) {
+          const int tn = min(kCapTile, Uo - t0);
+          __syncthreads();
+          for (int k = tid; k < tn; k += kCapThreads) {
+            const int j = ulo[t0 + k];
+            CapEnt e;
+            e.key = cap_key<G>(mask, prob, sc, go * G, j);
+            e.id = j;
+            e.len = clen[j];
+            s_ent[k] = e;
+          }
+          __syncthreads();
+          if (have) {
+            if (one_tile) {
+              ki = s_ent[i].key;
+              ji = s_ent[i].id;
+            }
+            // branch-free: every entry is read (one broadcast 16-byte LDS
+            // read) and counted with a select, so the reads of an unrolled
+            // group are all in flight together; candidates of a lower KV
+            // head win key ties, of a higher one lose them
+            const bool lower = go < g, same = go == g;
 #pragma unroll 8
-        for (int k = 0; k < tn; ++k) {
-          const CapEnt e = s_ent[k];
-          const bool before = (e.key > ki) | ((e.key == ki) & (e.id <= ji));
-          S += before ? e.len : 0;
+            for (int k = 0; k < tn; ++k) {
+              const CapEnt e = s_ent[k];
+              const bool before = (e.key > ki) |
+                                  ((e.key == ki) & (lower | (same & (e.id <= ji))));
+              S += before ? e.len : 0;
+            }
+          }
         }
       }
+      if (PHASE == kCapDecide) {
+        if (have) drop[(size_t)g * sc + i] = S > budget;
+      } else if (have && S > budget) {
+        atomicOr(&s_drop[i >> 5], 1u << (i & 31));
+      }
     }
-    if (have && S > budget) atomicOr(&s_drop[i >> 5], 1u << (i & 31));
+    if (PHASE == kCapDecide) return;
+  } else {
+    __syncthreads();
+    for (int i = tid; i < U; i += kCapThreads)
+      if (drop[(size_t)g * sc + i]) atomicOr(&s_drop[i >> 5], 1u << (i & 31));
   }
   __syncthreads();
 
@@ -196,13 +229,25 @@ size_t cap_budget_lds_bytes(int sc) { return (size_t)((sc + 31) / 32) * sizeof(u
 
 hipError_t launch_cap_budget(int sc, int hkv, int group, long long budget, const int32_t* clen,
                              const double* prob, uint8_t* mask, int32_t* list, int32_t* count,
-                             int32_t* ulist, int32_t* ucount, hipStream_t st) {
+                             int32_t* ulist, int32_t* ucount, uint8_t* drop, hipStream_t st) {
   if (sc <= 0 || hkv <= 0) return hipSuccess;
   const size_t lds = cap_budget_lds_bytes(sc);
+  // drop == NULL: each KV head's own budget (one launch); else one budget for
+  // the layer: the decisions, then their application
 #define SEKV_CAP(GG)                                                                           \
   case GG:                                                                                     \
-    hipLaunchKernelGGL(cap_budget_kernel<GG>, dim3(hkv), dim3(kCapThreads), lds, st, sc,       \
-                       budget, clen, prob, mask, list, count, ulist, ucount);                  \
+    if (!drop) {                                                                               \
+      hipLaunchKernelGGL((cap_budget_kernel<GG, kCapBoth>), dim3(hkv), dim3(kCapThreads), lds, \
+                         st, sc, hkv, budget, clen, prob, mask, list, count, ulist, ucount,    \
+                         drop);                                                                \
+    } else {                                                                                   \
+      hipLaunchKernelGGL((cap_budget_kernel<GG, kCapDecide>), dim3(hkv), dim3(kCapThreads),    \
+                         lds, st, sc, hkv, budget, clen, prob, mask, list, count, ulist,       \
+                         ucount, drop);                                                        \
+      hipLaunchKernelGGL((cap_budget_kernel<GG, kCapApply>), dim3(hkv), dim3(kCapThreads),     \
+                         lds, st, sc, hkv, budget, clen, prob, mask, list, count, ulist,       \
+                         ucount, drop);                                                        \
+    }                                                                                          \
     break;
   switch (group) {
     SEKV_CAP(1) SEKV_CAP(2) SEKV_CAP(3) SEKV_CAP(4) SEKV_CAP(5) SEKV_CAP(6) SEKV_CAP(7)

@@ -175,17 +175,30 @@ struct MergeScratch {
 template <int G>
 struct alignas(16) Smem {
   float qs[G][kHeadDim];           // query * 1/sqrt(d)
-  uint64_t m_off[kChunk];          // factor block of span j0 + i, relative to the pool
-  int m_n[kChunk], m_r[kChunk];    // its length and packed key and value ranks
   int bits[kChunk];                // heads of the group that zoom span j0 + i
-  int zl[kChunk];                  // chunk-local ids of zoomed spans
-  int nz;
   union {
     struct {                       // routing (dead once the gates are taken)
       float qu[G][kHeadDim];       // query as given
       double qt[G][kMaxRouteDim];  // P_h q_h
     } rt;
     WaveScratch<G> w[kWaves];      // written from the rows phase on
+  };
+};
+
+// Shared memory of the zoom kernel: the query, a batch of the workgroup's
+// zoomed spans (factor block, length, packed ranks, heads that zoom it), each
+// KV head's union size, and each wave's state / span scratch.
+constexpr int kZoomBatch = kZoomBatchMax;
+template <int G>
+struct alignas(16) ZSmem {
+  float qs[G][kHeadDim];
+  uint64_t m_off[kZoomBatch];
+  int m_n[kZoomBatch], m_r[kZoomBatch], bits[kZoomBatch];
+  int g, i, zg, lo, hi;            // this workgroup's KV head, index among its
+                                   // zoom workgroups, their count, span range
+  union {
+    int cnt[kMaxKvHeads];          // union size of each KV head (dead once shared out)
+    WaveScratch<G> w[kWaves];      // the waves' states and span scratch
   };
 };
 // Per wave: V_K of its next zoomed span, written by LDS DMA while the current
@@ -541,7 +554,7 @@ struct SpanRef {        // a zoomed span, the same on every lane of the wave
 };
 
 template <int G>
-__device__ __forceinline__ SpanRef span_ref(const Smem<G>& s, const float* pool, int jl) {
+__device__ __forceinline__ SpanRef span_ref(const ZSmem<G>& s, const float* pool, int jl) {
   SpanRef sp;
   jl = uniform(jl);
   sp.blk = pool + uniform64(s.m_off[jl]);
@@ -925,14 +938,15 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // ---------------------------------------------------------------------------
 static_assert(kChunk * kMaxGroup <= kThreads, "one gate per thread");
 template <int G> constexpr bool smem_fits() {
-  return sizeof(Smem<G>) + sizeof(Stage<G>) <= 80 * 1024 &&   // two workgroups per CU (160 KB)
+  return sizeof(Smem<G>) <= 40 * 1024 &&                          // layer kernel
+         sizeof(ZSmem<G>) + sizeof(Stage<G>) <= 80 * 1024 &&       // zoom kernel: two per CU
          sizeof(Smem<G>::rt) <= sizeof(Smem<G>::w) &&
          sizeof(ZoomScratchAny<G>) <= sizeof(float) * stage_floats<stage_rows<G>()>() &&
          stage_rows<G>() % 2 == 0 && stage_rows<G>() <= 32;
 }
 static_assert(smem_fits<1>() && smem_fits<2>() && smem_fits<3>() && smem_fits<4>() &&
               smem_fits<5>() && smem_fits<6>() && smem_fits<7>() && smem_fits<8>(),
-              "LDS layout of the layer kernel");
+              "LDS layout of the layer and zoom kernels");
 static_assert(kChunk <= 64, "a chunk's zoom sets are one wave ballot");
 
 // The ascending zoom lists of a KV head's query heads and its union, from the
@@ -1000,7 +1014,8 @@ __device__ __attribute__((always_inline)) void tail_merge(const LayerGeom& geo, 
                                                           int mode, int h, MergeScratch& mg) {
   const int tid = threadIdx.x;
   const int g = h / G, hl = h % G;
-  const int ns = (mode & kZoomSplit) ? geo.n_slots() : geo.n_work;
+  // the layer kernel's slots, then those of the zoom workgroups this KV head got
+  const int ns = geo.n_work + ((mode & kZoomSplit) ? a.zcount[g] : 0);
   const float* pg = a.part + (size_t)g * geo.n_slots() * G * kPartStride;
   constexpr int B = 16;
   const int dq = tid % kMergeQuads, stripe = tid / kMergeQuads;
@@ -1075,6 +1090,221 @@ __device__ __attribute__((always_inline)) void tail_merge(const LayerGeom& geo, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// The zoom kernel: every zoomed span of a layer, dealt to geo.z_total
+// workgroups in proportion to each KV head's union size, so a KV head whose
+// heads zoom many spans gets as many workgroups as its share of the work.
+//
+// Every workgroup reads the chunks' union bit masks of all KV heads (written by
+// the layer launch), counts each union U_g and takes the same decision: a KV
+// head with U_g > 0 gets Z_g = 1 + (its share of the z_total - n_nonempty
+// others, by cumulative integer rounding, so the shares add up exactly);
+// workgroup z belongs to the KV head g with B_g <= z < B_g + Z_g, B_g the sum
+// of the Z of the heads before it, and takes the spans [U_g i / Z_g,
+// U_g (i + 1) / Z_g) of g's ascending union, i = z - B_g.  Workgroup 0 also
+// records each Z_g for the tail's merge.  z_total is at least
+// Hkv S_c / kZoomBatch + Hkv, so a share never exceeds kZoomBatch spans and
+// their metadata fit LDS at once.  The 4 waves each run the software
+// pipeline of zoom_span32 over spans wid, wid + 4, ... of the share (spans
+// above rank 32 afterwards, through zoom_span), and the 4 wave states merge
+// into one partial per head of g, in slot n_work + i.
+// ---------------------------------------------------------------------------
+template <int G>
+__device__ __attribute__((always_inline)) void zoom_body(const LayerGeom& geo, const LayerArgs& a,
+                                                         int z) {
+  __shared__ ZSmem<G> s;
+  __shared__ Stage<G> stg;
+  constexpr int SR = stage_rows<G>();
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  float* const stage = stg.v[uniform(wid)];
+  const int hkv = geo.n_kv_heads, W = geo.n_work, nc = geo.n_chunks, scs = geo.sc_stride;
+  const int zt = geo.z_total;
+
+  // ---- union sizes of every KV head, and this workgroup's share -------------
+  for (int g = tid; g < hkv; g += kThreads) s.cnt[g] = 0;
+  __syncthreads();
+  for (int p = tid; p < hkv * nc; p += kThreads) {
+    const int g = p / nc, c = p % nc;
+    const int n = __popc(a.chunk_bits[((size_t)g * W + c) * kListWords + G]);
+    if (n) atomicAdd(&s.cnt[g], n);
+  }
+  if (tid == 0) s.g = -1;
+  __syncthreads();
+  if (wid == 0) {
+    // lane = KV head (64 at a time): totals, then each head's share of the
+    // workgroups by cumulative rounding (exact in float64: every product is
+    // far below 2^53 and the quotients far from the next integer)
+    int U = 0, nne = 0;
+    for (int g0 = 0; g0 < hkv; g0 += 64) {
+      const int c = g0 + lane < hkv ? s.cnt[g0 + lane] : 0;
+      U += __builtin_amdgcn_readlane(wave_incl_scan(c), 63);
+      nne += __popcll(__ballot(c > 0));
+    }
+    const double extra = (double)(zt - nne);   // z_total >= Hkv >= nne
+    int cum = 0, base = 0;
+    for (int g0 = 0; g0 < hkv; g0 += 64) {
+      const int g = g0 + lane;
+      const int c = g < hkv ? s.cnt[g] : 0;
+      const int incl = wave_incl_scan(c);
+      const double e0 = U ? floor(extra * (double)(cum + incl - c) / (double)U) : 0.0;
+      const double e1 = U ? floor(extra * (double)(cum + incl) / (double)U) : 0.0;
+      const int zg = (c > 0 ? 1 : 0) + (int)(e1 - e0);
+      const int zincl = wave_incl_scan(zg);
+      const int b = base + zincl - zg;   // first workgroup of head g
+      if (g < hkv) {
+        if (z == 0) a.zcount[g] = zg;
+        if (z >= b && z < b + zg) {
+          const int i = z - b;
+          s.g = g;
+          s.i = i;
+          s.zg = zg;
+          s.lo = (int)((long long)c * i / zg);
+          s.hi = (int)((long long)c * (i + 1) / zg);
+        }
+      }
+      cum += __builtin_amdgcn_readlane(incl, 63);
+      base += __builtin_amdgcn_readlane(zincl, 63);
+    }
+  }
+  __syncthreads();
+  const int g = s.g;
+  if (g < 0) return;   // uniform: no span for this workgroup
+  // z_total >= Hkv S_c / kZoomBatch + Hkv, so a share never exceeds one batch
+  const int lo = s.lo, nb = min(s.hi - s.lo, kZoomBatch), slot = W + s.i;
+
+  // ---- the group's queries, scaled by 1/sqrt(d) -----------------------------
+  const float scale = rsqrtf((float)kHeadDim);
+  for (int o = tid; o < G * kHeadDim; o += kThreads)
+    s.qs[o / kHeadDim][o % kHeadDim] = a.q[(size_t)g * G * kHeadDim + o] * scale;
+
+  // ---- spans lo .. lo + nb - 1 of g's union: wave 0 scans the chunks'
+  // popcounts, each lane writes its chunk's spans that fall in the range
+  if (wid == 0) {
+    int run = 0;
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+      const int c = c0 + lane;
+      uint32_t word[kListWords];
+#pragma unroll
+      for (int li = 0; li <= G; ++li)
+        word[li] = c < nc ? a.chunk_bits[((size_t)g * W + c) * kListWords + li] : 0u;
+      const int pop = __popc(word[G]);
+      const int incl = wave_incl_scan(pop);
+      int k = run + incl - pop;   // rank of this chunk's first span in the union
+      if (k < lo + nb && k + pop > lo) {
+        uint32_t bits = word[G];
+        while (bits) {
+          const int bb = __ffs(bits) - 1;
+          bits &= bits - 1;
+          if (k >= lo && k < lo + nb) {
+            unsigned hm = 0;
+#pragma unroll
+            for (int h = 0; h < G; ++h) hm |= ((word[h] >> bb) & 1u) << h;
+            s.m_n[k - lo] = c * kChunk + bb;   // the span id for now
+            s.bits[k - lo] = (int)hm;
+          }
+          ++k;
+        }
+      }
+      run += __builtin_amdgcn_readlane(incl, 63);
+    }
+  }
+  __syncthreads();
+  if (tid < nb) {
+    const int j = s.m_n[tid];
+    const size_t gj = (size_t)g * scs + j;
+    s.m_off[tid] = a.fac_off[gj] - a.off_base;
+    s.m_r[tid] = a.rank[gj];
+    s.m_n[tid] = a.clen[j];
+  }
+  __syncthreads();
+
+  float zm[G], zl[G], za[G][2];   // the wave's state (lane: dims 2 lane, 2 lane + 1)
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    zm[h] = -INFINITY;
+    zl[h] = 0.f;
+    za[h][0] = za[h][1] = 0.f;
+  }
+  const SpanRef zero{a.zero_block, 1, 1, 1, 0u};
+  // ---- the wave's spans u = wid, wid + kWaves, ... of rank <= 32, pipelined
+  auto next_small = [&](int u) {
+    while (u < nb && rank_max(s.m_r[u]) > 32) u += kWaves;
+    return uniform(u);
+  };
+  int u = next_small(wid);
+  if (u < nb) {
+    SpanRef cu = span_ref(s, a.pool, u);
+    stage_vk<SR>(cu.rk <= SR ? cu : zero, stage);
+    float4 ub[8];
+    prefetch_span(cu, ub);
+    for (;;) {
+      const int un = next_small(u + kWaves);
+      const bool has_nx = un < nb;
+      const SpanRef nx = span_ref(s, a.pool, min(un, nb - 1));
+      // stand-ins when there is no next span: this one again (its V_K only if
+      // it is staged, else the zeros)
+      const SpanRef nxp = has_nx ? nx : cu;
+      const SpanRef nxs = has_nx && nx.rk <= SR ? nx : (cu.rk <= SR ? cu : zero);
+      float (*scr)[kHeadDim] = s.w[wid].st.acc;
+      if (cu.rk <= 16 && cu.rv <= 16)
+        zoom_span32<G, SR, 16>(cu, nxp, nxs, ub, stage, scr, s.qs, zm, zl, za);
+      else
+        zoom_span32<G, SR, 32>(cu, nxp, nxs, ub, stage, scr, s.qs, zm, zl, za);
+      if (!has_nx) break;
+      cu = nx;
+      u = un;
+    }
+  }
+  // ---- then those of rank > 32, with the stage as scratch once its DMA is done
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  for (u = wid; u < nb; u += kWaves) {
+    if (rank_max(s.m_r[u]) <= 32) continue;
+    const SpanRef sp = span_ref(s, a.pool, u);
+    zoom_span<G>(sp.blk, sp.n, sp.rk, sp.rv, sp.hm, s.qs,
+                 *reinterpret_cast<ZoomScratchAny<G>*>(stage), zm, zl, za);
+  }
+  __syncthreads();   // every wave is done with its span scratch
+
+  // ---- the 4 wave states into one partial per head, slot n_work + i ---------
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    s.w[wid].st.acc[h][2 * lane] = za[h][0];
+    s.w[wid].st.acc[h][2 * lane + 1] = za[h][1];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s.w[wid].st.m[h] = zm[h];
+      s.w[wid].st.l[h] = zl[h];
+    }
+  }
+  __syncthreads();
+  float* dst = a.part + ((size_t)g * geo.n_slots() + slot) * G * kPartStride;
+  for (int o = tid; o < G * kHeadDim; o += kThreads) {
+    const int h = o / kHeadDim, d = o % kHeadDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) M = fmaxf(M, s.w[wv].st.m[h]);
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int wv = 0; wv < kWaves; ++wv) {
+        const float m1 = s.w[wv].st.m[h];
+        if (m1 != -INFINITY) {
+          const float wt = __expf(m1 - M);
+          L += s.w[wv].st.l[h] * wt;
+          A += s.w[wv].st.acc[h][d] * wt;
+        }
+      }
+    }
+    dst[(size_t)h * kPartStride + 4 + d] = A;
+    if (d == 0) {
+      dst[(size_t)h * kPartStride] = M;
+      dst[(size_t)h * kPartStride + 1] = L;
+    }
+  }
+}
+
 // One workgroup of a tail launch: x < Hq merges query head x, the others
 // write KV head x - Hq's lists.
 template <int G>
@@ -1089,7 +1319,9 @@ __device__ __attribute__((always_inline)) void layer_tail(const LayerGeom& geo, 
   }
 }
 
-// One layer of one sequence: workgroup `block` of its Hkv x n_work grid.
+// One layer of one sequence: workgroup `block` of its Hkv x n_work grid
+// routes its chunk of compressed spans and attends its full-resolution rows
+// and its chunk's coarse entries; the zoomed spans go to the zoom kernel.
 template <typename T, int G>
 __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
                                                           const LayerArgs& a, int mode,
@@ -1098,39 +1330,29 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
   constexpr int CLOADS = (kChunk / kWaves) / Ln::RPW;     // coarse entries: loads per wave
   constexpr int DLOADS = kRowBlock / Ln::RPW;             // full-resolution rows: loads per pass
   __shared__ Smem<G> s;
-  __shared__ Stage<G> stg;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  float* const stage = stg.v[uniform(wid)];   // this wave's stage, a scalar LDS address
   const int W = geo.n_work;
   const int g = block / W, w = block % W;
   const int sc = geo.n_compressed, D = geo.n_dense, dr = geo.route_dim;
+  const int scs = geo.sc_stride;   // the span arrays' stride (route buffers use sc)
   const int h0 = g * G;
   const int j0 = w * kChunk, nj = w < geo.n_chunks ? min(kChunk, sc - j0) : 0;
   const int d0 = w * geo.dense_rows, d1 = min(D, d0 + geo.dense_rows);
   const bool route = (mode & kRoute) != 0, dense = (mode & kDense) != 0;
-  const bool zoom = (mode & kZoom) != 0, attn = dense || zoom;
   const float scale = rsqrtf((float)kHeadDim);
 
-  // ---- everything this workgroup reads before its zoom decisions, issued up
-  // front: query, span metadata, routing projections, summaries, ln n,
-  // thresholds, then the full-resolution rows (first pass) and coarse entries.
-  // Query and metadata go to LDS only after every load is out, so no wait for
-  // them holds back the rest: the whole prologue is one round trip.
+  // ---- everything this workgroup reads, issued up front: query, routing
+  // projections, summaries, ln n, thresholds, then the full-resolution rows
+  // (first pass) and coarse entries.  The query goes to LDS only after every
+  // load is out, so no wait for it holds back the rest: the whole prologue is
+  // one round trip.
   constexpr int QPT = (G * kHeadDim + kThreads - 1) / kThreads;   // query floats per thread
   float qx[QPT];
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
     const int o = tid + i * kThreads;
     qx[i] = o < G * kHeadDim ? a.q[(size_t)h0 * kHeadDim + o] : 0.f;
-  }
-  unsigned long long m_off = 0;
-  int m_n = 0, m_r = 0;
-  if (zoom && tid < nj) {
-    const size_t gj = (size_t)g * sc + j0 + tid;
-    m_off = a.fac_off[gj];
-    m_n = a.clen[j0 + tid];
-    m_r = a.rank[gj];
   }
   const int nout = G * dr, part = tid & 7, orow = tid >> 3;
   float4 pv[4][4];
@@ -1152,7 +1374,7 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
     }
     if (gate) {
       const int j = j0 + jl_g, h = h0 + hl_g;
-      const uint4* sr = (const uint4*)((const T*)a.summ + ((size_t)h * sc + j) * dr);
+      const uint4* sr = (const uint4*)((const T*)a.summ + ((size_t)h * scs + j) * dr);
       if (sfast) {
 #pragma unroll
         for (int v = 0; v < kSumVec; ++v) sum[v] = sr[min(v, svec - 1)];
@@ -1161,8 +1383,8 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
       tau_f = a.tau[h];
     }
   }
-  const T* DK = (const T*)a.dense_k + (size_t)g * D * kHeadDim;
-  const T* DV = (const T*)a.dense_v + (size_t)g * D * kHeadDim;
+  const T* DK = (const T*)a.dense_k + (size_t)g * geo.dense_stride * kHeadDim;
+  const T* DV = (const T*)a.dense_v + (size_t)g * geo.dense_stride * kHeadDim;
   uint4 dk[DLOADS], dv[DLOADS];
   const int dr0 = d0 + wid * kRowBlock;
   if (dense) rows_load<T, DLOADS>(DK, DV, dr0, min(d1, dr0 + kRowBlock), dk, dv);
@@ -1171,8 +1393,8 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
   uint4 kr[CLOADS], vr[CLOADS];
   float cbias[CLOADS];   // ln n of each coarse entry (loaded with it)
   if (dense && nj > 0) {
-    const T* K = (const T*)a.kbar + (size_t)g * sc * kHeadDim;
-    const T* V = (const T*)a.vbar + (size_t)g * sc * kHeadDim;
+    const T* K = (const T*)a.kbar + (size_t)g * scs * kHeadDim;
+    const T* V = (const T*)a.vbar + (size_t)g * scs * kHeadDim;
     rows_load<T, CLOADS>(K, V, cr0, cr1, kr, vr);
 #pragma unroll
     for (int u = 0; u < CLOADS; ++u)
@@ -1187,14 +1409,6 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
     }
   }
   if (tid < kChunk) s.bits[tid] = 0;
-  if (zoom && tid < nj) {
-    // (an empty asm keeps the compiler from moving this arithmetic, and the
-    // wait for its load, up next to the load)
-    asm volatile("" : "+v"(m_off));
-    s.m_off[tid] = m_off - a.off_base;
-    s.m_n[tid] = m_n;
-    s.m_r[tid] = m_r;
-  }
   __syncthreads();
 
   // ---- routing ------------------------------------------------------------
@@ -1241,7 +1455,7 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
           }
         }
       } else {
-        const T* sr = (const T*)a.summ + ((size_t)h * sc + j) * dr;
+        const T* sr = (const T*)a.summ + ((size_t)h * scs + j) * dr;
         for (int i = 0; i < dr; ++i) x += s.rt.qt[hl][i] * (double)Store<T>::load(sr + i);
       }
       x += a.gamma * lnn_j;
@@ -1252,7 +1466,7 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
       if (a.prob) a.prob[(size_t)h * sc + j] = p;
       if (z) atomicOr(&s.bits[jl], 1 << hl);
     }
-  } else if (attn && nj > 0) {
+  } else if (dense && nj > 0) {
     for (int idx = tid; idx < nj * G; idx += kThreads) {
       const int jl = idx / G, hl = idx % G;
       if (a.mask[(size_t)(h0 + hl) * sc + j0 + jl]) atomicOr(&s.bits[jl], 1 << hl);
@@ -1260,54 +1474,27 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
   }
   __syncthreads();
 
-  // ---- zoom sets of the chunk: one wave ballot per list ---------------------
+  // ---- zoom sets of the chunk: one wave ballot per list (per head, then the
+  // union), read by the zoom kernel and by the tail's lists -----------------
   if (wid == 0 && nj > 0) {
     const int b = lane < nj ? s.bits[lane] : 0;
-    if (route) {
 #pragma unroll
-      for (int li = 0; li <= G; ++li) {
-        const bool z = li < G ? ((b >> li) & 1) != 0 : b != 0;
-        const unsigned long long bal = __ballot(z);
-        if (lane == 0) a.chunk_bits[((size_t)g * W + w) * kListWords + li] = (uint32_t)bal;
-      }
-    }
-    if (zoom) {
-      const bool z = b != 0;
+    for (int li = 0; li <= G; ++li) {
+      const bool z = li < G ? ((b >> li) & 1) != 0 : b != 0;
       const unsigned long long bal = __ballot(z);
-      if (z) s.zl[__popcll(bal & ((1ull << lane) - 1ull))] = lane;
-      if (lane == 0) s.nz = __popcll(bal);
+      if (lane == 0) a.chunk_bits[((size_t)g * W + w) * kListWords + li] = (uint32_t)bal;
     }
   }
-
-  // ---- each wave's first zoomed span (the wid-th of the chunk): its V_K
-  // moves into the wave's stage under the rest of the rows phase (issued once
-  // the first rows have arrived, so no wait for them also waits for it) ------
-  constexpr int SR = stage_rows<G>();
-  const SpanRef zero{a.zero_block, 1, 1, 1, 0u};
-  SpanRef first = zero;   // the wave's first zoomed span of rank <= 32
-  if (zoom && nj > 0) {
-    unsigned zb = (unsigned)__ballot(lane < nj && s.bits[lane] != 0);
-    for (int k = 0; k < wid; ++k) zb &= zb - 1u;   // the wid-th zoomed span on
-    while (zb != 0u) {
-      const int jl = __ffs(zb) - 1;
-      if (rank_max(s.m_r[jl]) <= 32) {
-        first = span_ref(s, a.pool, jl);
-        break;
-      }
-      for (int k = 0; k < kWaves; ++k) zb &= zb - 1u;   // the wave's next one
-    }
-  }
-  if (first.rk > SR) first = zero;
+  if (!dense) return;
 
   // ---- full-resolution rows and coarse entries: each wave's state ----------
-  if (dense) {
+  {
     QSlice<T, G> qv;
     qv.load(s.qs);
     RowState<T, G> rs;
     rs.init();
     const float nob[DLOADS] = {};
     rows_accumulate<T, G, DLOADS>(dk, dv, dr0, min(d1, dr0 + kRowBlock), qv, nob, nullptr, 0, rs);
-    stage_vk<SR>(first, stage);
     for (int p0 = d0 + kWaves * kRowBlock; p0 < d1; p0 += kWaves * kRowBlock) {
       const int r0 = p0 + wid * kRowBlock, r1 = min(d1, r0 + kRowBlock);
       rows_load<T, DLOADS>(DK, DV, r0, r1, dk, dv);
@@ -1316,108 +1503,34 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
     if (nj > 0) rows_accumulate<T, G, CLOADS>(kr, vr, cr0, cr1, qv, cbias, s.bits, j0, rs);
     rows_finish<T, G>(rs);
     rows_store<T, G>(rs, s.w[wid].st.acc, s.w[wid].st.m, s.w[wid].st.l);
-  } else {
-    stage_vk<SR>(first, stage);
   }
   __syncthreads();
 
-  // ---- zoomed spans: the wave's running state starts from its rows and
-  // coarse entries; spans u = wid, wid + kWaves, ... of the chunk's list ------
-  // (lane holds dims 2 lane, 2 lane + 1)
-  float zm[G], zl[G], za[G][2];
+  // ---- this workgroup's partial: slot w -------------------------------------
+  float* dst = a.part + ((size_t)g * geo.n_slots() + w) * G * kPartStride;
+  for (int o = tid; o < G * kHeadDim; o += kThreads) {
+    const int h = o / kHeadDim, d = o % kHeadDim;
+    float M = -INFINITY;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    zm[h] = dense ? s.w[wid].st.m[h] : -INFINITY;
-    zl[h] = dense ? s.w[wid].st.l[h] : 0.f;
-    za[h][0] = dense ? s.w[wid].st.acc[h][2 * lane] : 0.f;
-    za[h][1] = dense ? s.w[wid].st.acc[h][2 * lane + 1] : 0.f;
-  }
-  __builtin_amdgcn_wave_barrier();
-  if (zoom && nj > 0) {
-    const int nz = s.nz;
-    // the wave's spans u = wid, wid + kWaves, ... of rank <= 32, pipelined
-    auto next_small = [&](int u) {
-      while (u < nz && rank_max(s.m_r[s.zl[u]]) > 32) u += kWaves;
-      return uniform(u);
-    };
-    int u = next_small(wid);
-    if (u < nz) {
-      SpanRef cu = span_ref(s, a.pool, s.zl[u]);
-      float4 ub[8];
-      prefetch_span(cu, ub);
-      for (;;) {
-        const int un = next_small(u + kWaves);
-        const bool has_nx = un < nz;
-        const SpanRef nx = span_ref(s, a.pool, s.zl[min(un, nz - 1)]);
-        // stand-ins when there is no next span: this one again (its V_K only
-        // if it is staged, else the zeros)
-        const SpanRef nxp = has_nx ? nx : cu;
-        const SpanRef nxs = has_nx && nx.rk <= SR ? nx : (cu.rk <= SR ? cu : zero);
-        // the span's scratch: the wave's state area (idle while its spans run)
-        float (*scr)[kHeadDim] = s.w[wid].st.acc;
-        if (cu.rk <= 16 && cu.rv <= 16)
-          zoom_span32<G, SR, 16>(cu, nxp, nxs, ub, stage, scr, s.qs, zm, zl, za);
-        else
-          zoom_span32<G, SR, 32>(cu, nxp, nxs, ub, stage, scr, s.qs, zm, zl, za);
-        if (!has_nx) break;
-        cu = nx;
-        u = un;
-      }
-    }
-    // then those of rank > 32, with the stage as scratch once its DMA is done
-    for (u = wid; u < nz; u += kWaves) {
-      const int jl = uniform(s.zl[u]);
-      if (rank_max(s.m_r[jl]) <= 32) continue;
-      const SpanRef sp = span_ref(s, a.pool, jl);
-      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-      zoom_span<G>(sp.blk, sp.n, sp.rk, sp.rv, sp.hm, s.qs,
-                   *reinterpret_cast<ZoomScratchAny<G>*>(stage), zm, zl, za);
-    }
-  }
-
-  // ---- the wave's zoomed-span state over its (dead) zoom scratch ------------
-  if (attn) {
+    for (int wv = 0; wv < kWaves; ++wv) M = fmaxf(M, s.w[wv].st.m[h]);
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      s.w[wid].st.acc[h][2 * lane] = za[h][0];
-      s.w[wid].st.acc[h][2 * lane + 1] = za[h][1];
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        s.w[wid].st.m[h] = zm[h];
-        s.w[wid].st.l[h] = zl[h];
-      }
-    }
-    __syncthreads();
-    // ---- this workgroup's partial --------------------------------------------
-    const int slot = (mode & kZoomSplit) ? W + w : w;
-    float* dst = a.part + ((size_t)g * geo.n_slots() + slot) * G * kPartStride;
-    for (int o = tid; o < G * kHeadDim; o += kThreads) {
-      const int h = o / kHeadDim, d = o % kHeadDim;
-      float M = -INFINITY;
-#pragma unroll
-      for (int wv = 0; wv < kWaves; ++wv) M = fmaxf(M, s.w[wv].st.m[h]);
-      float L = 0.f, A = 0.f;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int wv = 0; wv < kWaves; ++wv) {
-          const float m1 = s.w[wv].st.m[h];
-          if (m1 != -INFINITY) {
-            const float wt = __expf(m1 - M);
-            L += s.w[wv].st.l[h] * wt;
-            A += s.w[wv].st.acc[h][d] * wt;
-          }
+      for (int wv = 0; wv < kWaves; ++wv) {
+        const float m1 = s.w[wv].st.m[h];
+        if (m1 != -INFINITY) {
+          const float wt = __expf(m1 - M);
+          L += s.w[wv].st.l[h] * wt;
+          A += s.w[wv].st.acc[h][d] * wt;
         }
       }
-      dst[(size_t)h * kPartStride + 4 + d] = A;
-      if (d == 0) {
-        dst[(size_t)h * kPartStride] = M;
-        dst[(size_t)h * kPartStride + 1] = L;
-      }
+    }
+    dst[(size_t)h * kPartStride + 4 + d] = A;
+    if (d == 0) {
+      dst[(size_t)h * kPartStride] = M;
+      dst[(size_t)h * kPartStride + 1] = L;
     }
   }
-
 }
 
 template <typename T, int G>
@@ -1455,6 +1568,57 @@ __global__ __launch_bounds__(kThreads) void layer_tail_batch_kernel(BatchLayerAr
   __shared__ MergeScratch mg;
   const int i = blockIdx.y;
   layer_tail<G>(b.geo[i], b.arg[i], mode, blockIdx.x, wc, mg);
+}
+
+// The zoomed spans of one layer (geo.z_total workgroups; grid.y: the sequence
+// of a batch, the extra workgroups of a shorter grid return at once).
+template <int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void zoom_kernel(LayerGeom geo, LayerArgs a) {
+  zoom_body<G>(geo, a, blockIdx.x);
+}
+
+template <int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void zoom_batch_kernel(BatchLayerArgs b) {
+  const int i = blockIdx.y;
+  if ((int)blockIdx.x >= b.geo[i].z_total) return;
+  zoom_body<G>(b.geo[i], b.arg[i], blockIdx.x);
+}
+
+hipError_t launch_zoom(const LayerGeom& g, const LayerArgs& a, hipStream_t st) {
+  if (g.n_compressed == 0) return hipSuccess;
+  const dim3 grid(g.z_total);
+#define SEKV_ZOOM(GG)                                                                       \
+  case GG:                                                                                  \
+    hipLaunchKernelGGL((zoom_kernel<GG>), grid, dim3(kThreads), 0, st, g, a);               \
+    break;
+  switch (g.group) {
+    SEKV_ZOOM(1) SEKV_ZOOM(2) SEKV_ZOOM(3) SEKV_ZOOM(4) SEKV_ZOOM(5) SEKV_ZOOM(6) SEKV_ZOOM(7)
+    SEKV_ZOOM(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef SEKV_ZOOM
+  return hipGetLastError();
+}
+
+hipError_t launch_zoom_batch(int group, const BatchLayerArgs& b, int batch, hipStream_t st) {
+  if (batch < 1 || batch > kMaxBatch) return hipErrorInvalidValue;
+  int nx = 0;
+  for (int i = 0; i < batch; ++i) nx = max(nx, b.geo[i].n_compressed ? b.geo[i].z_total : 0);
+  if (nx == 0) return hipSuccess;
+  const dim3 grid(nx, batch);
+#define SEKV_ZOOM(GG)                                                                       \
+  case GG:                                                                                  \
+    hipLaunchKernelGGL((zoom_batch_kernel<GG>), grid, dim3(kThreads), 0, st, b);            \
+    break;
+  switch (group) {
+    SEKV_ZOOM(1) SEKV_ZOOM(2) SEKV_ZOOM(3) SEKV_ZOOM(4) SEKV_ZOOM(5) SEKV_ZOOM(6) SEKV_ZOOM(7)
+    SEKV_ZOOM(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef SEKV_ZOOM
+  return hipGetLastError();
 }
 
 hipError_t launch_layer_tail(int mode, const LayerGeom& g, const LayerArgs& a, hipStream_t st) {
@@ -1559,14 +1723,14 @@ constexpr int kFetchSlots = 64;
 __global__ __launch_bounds__(256) void fetch_gather_kernel(
     const int32_t* __restrict__ ulist, const int32_t* __restrict__ ucount,
     const int32_t* __restrict__ clen, const int32_t* __restrict__ rank,
-    const uint64_t* __restrict__ fac_off, uint64_t layer_base, int sc,
+    const uint64_t* __restrict__ fac_off, uint64_t layer_base, int sc, int scs,
     const float* __restrict__ host, float* __restrict__ stage) {
   const int zs = blockIdx.x, g = blockIdx.y;
   const int nu = ucount[g];
   for (int u = zs; u < nu; u += kFetchSlots) {
     const int j = ulist[(size_t)g * sc + u];
-    const FactorView fv = FactorView::packed(rank[(size_t)g * sc + j], clen[j]);
-    const uint64_t off = fac_off[(size_t)g * sc + j];
+    const FactorView fv = FactorView::packed(rank[(size_t)g * scs + j], clen[j]);
+    const uint64_t off = fac_off[(size_t)g * scs + j];
     const uint4* src = (const uint4*)(host + off);
     uint4* dst = (uint4*)(stage + (off - layer_base));
     const int nvec = (int)(fv.block_floats() / 4);
@@ -1581,7 +1745,7 @@ hipError_t launch_fetch_gather(const LayerGeom& g, const int32_t* ulist, const i
   if (g.n_compressed == 0) return hipSuccess;
   hipLaunchKernelGGL(fetch_gather_kernel, dim3(kFetchSlots, g.n_kv_heads), dim3(256), 0, st,
                      ulist, ucount, clen, rank, fac_off, layer_base, g.n_compressed,
-                     host_pool_mapped, stage);
+                     g.sc_stride, host_pool_mapped, stage);
   return hipGetLastError();
 }
 

@@ -24,11 +24,15 @@ __global__ __launch_bounds__(kGateThreads) void gate_repack_kernel(
     const int32_t* __restrict__ old_rank, float* __restrict__ new_pool,
     const uint64_t* __restrict__ new_off, const int32_t* __restrict__ new_rank,
     const uint8_t* __restrict__ kept, const float* __restrict__ key_gates,
-    const float* __restrict__ value_gates, const int32_t* __restrict__ clen, int sc,
+    const float* __restrict__ value_gates, const int32_t* __restrict__ clen, int sc, int scs,
     int max_rank, uint64_t n_blocks) {
+  // block b = lg * scs + j of the tables; the gates are laid out [lg][sc][R]
   const uint64_t b = blockIdx.x;
   if (b >= n_blocks) return;
-  const int j = (int)(b % (uint64_t)sc);
+  const uint64_t lg = b / (uint64_t)scs;
+  const int j = (int)(b % (uint64_t)scs);
+  if (j >= sc) return;
+  const uint64_t gi = lg * (uint64_t)sc + j;
   const int n = clen[j];
   const FactorView fo = FactorView::packed(old_rank[b], n);
   const FactorView fn = FactorView::packed(new_rank[b], n);
@@ -36,7 +40,7 @@ __global__ __launch_bounds__(kGateThreads) void gate_repack_kernel(
   float* dst = new_pool + new_off[b];
   for (int kv = 0; kv < 2; ++kv) {
     const uint8_t* kp = kept + (b * 2 + kv) * (uint64_t)max_rank;
-    const float* gb = (kv ? value_gates : key_gates) + b * (uint64_t)max_rank;
+    const float* gb = (kv ? value_gates : key_gates) + gi * (uint64_t)max_rank;
     const int nr = fn.r(kv), nr4 = fn.r4(kv), or4 = fo.r4(kv);
     // V^T rows of the kept components
     for (int e = threadIdx.x; e < nr * kHeadDim; e += kGateThreads) {
@@ -59,12 +63,12 @@ __global__ __launch_bounds__(kGateThreads) void gate_repack_kernel(
 hipError_t launch_gate_repack(const float* old_pool, const uint64_t* old_off,
                               const int32_t* old_rank, float* new_pool, const uint64_t* new_off,
                               const int32_t* new_rank, const uint8_t* kept, const float* key_gates,
-                              const float* value_gates, const int32_t* clen, int sc, int max_rank,
-                              uint64_t n_blocks, hipStream_t st) {
+                              const float* value_gates, const int32_t* clen, int sc, int scs,
+                              int max_rank, uint64_t n_blocks, hipStream_t st) {
   if (n_blocks == 0 || sc == 0) return hipSuccess;
   hipLaunchKernelGGL(gate_repack_kernel, dim3((unsigned)n_blocks), dim3(kGateThreads), 0, st,
                      old_pool, old_off, old_rank, new_pool, new_off, new_rank, kept, key_gates,
-                     value_gates, clen, sc, max_rank, n_blocks);
+                     value_gates, clen, sc, scs, max_rank, n_blocks);
   return hipGetLastError();
 }
 

@@ -124,10 +124,13 @@ struct SegOut {          // all device, capacity N unless noted
 //   compressed spans [kChunk w, kChunk (w + 1)) (routing, coarse entries and
 //   the zoomed spans among them), and
 //   full-resolution rows [dense_rows w, dense_rows (w + 1)).
+// The zoomed spans of a layer run in a launch of their own, z_total
+// workgroups dealt to the KV heads in proportion to their union sizes.
 // Partial softmax states live in the workspace as
-//   part[Hkv][2 n_work][G][kPartStride] floats: m, l, -, -, acc[d]
-// slot w holds workgroup w's rows, coarse entries and zoomed spans, or, when
-// the zoomed spans run in a launch of their own, slot n_work + w holds those.
+//   part[Hkv][n_work + z_total][G][kPartStride] floats: m, l, -, -, acc[d]
+// slot w < n_work holds layer workgroup w's rows and coarse entries, slot
+// n_work + i the spans of the KV head's i-th zoom workgroup; zcount[g] (per
+// cache) records how many zoom workgroups KV head g got in the last launch.
 // ---------------------------------------------------------------------------
 constexpr int kWaves = 4;                 // waves per workgroup of the layer kernel
 constexpr int kThreads = kWaves * 64;
@@ -142,18 +145,27 @@ constexpr int kListWords = kMaxGroup + 1; // zoom bit masks per chunk: heads, th
 // loads and the compiler counts outstanding loads exactly.  It holds a factor
 // block of one token at rank 1 and a full V_K stage (32 rows of d floats).
 constexpr int kZeroBlockFloats = 32 * kHeadDim;
+constexpr int kMaxKvHeads = 256;          // KV heads of a layer, at most
+constexpr int kZoomWgMax = 512;           // zoom workgroups filling the GPU (two per CU)
+constexpr int kZoomBatchMax = 64;         // zoomed spans of one zoom workgroup, at most
 
 struct LayerGeom {
   int n_q_heads, n_kv_heads, group, route_dim;
   int n_dense, n_compressed;
+  int dense_stride;  // rows between the full-resolution sets of two KV heads (>= n_dense)
+  int sc_stride;     // entries between two (layer, head) rows of the span arrays (>= S_c)
   int n_chunks;      // ceil(S_c / kChunk)
   int n_work;        // workgroups per KV head: max(1, n_chunks, ceil(D / kMaxDenseRows))
   int dense_rows;    // full-resolution rows per workgroup, a multiple of kWaves * kRowBlock
-  __host__ __device__ int n_slots() const { return 2 * n_work; }
+  int z_total;       // zoom workgroups (see make_layer_geom)
+  __host__ __device__ int n_slots() const { return n_work + z_total; }
 };
 
-__host__ inline LayerGeom make_layer_geom(int hq, int hkv, int dr, int n_dense, int sc) {
+__host__ inline LayerGeom make_layer_geom(int hq, int hkv, int dr, int n_dense, int sc,
+                                          int dense_stride, int sc_stride) {
   LayerGeom g{};
+  g.dense_stride = dense_stride;
+  g.sc_stride = sc_stride;
   g.n_q_heads = hq;
   g.n_kv_heads = hkv;
   g.group = hq / hkv;
@@ -168,15 +180,23 @@ __host__ inline LayerGeom make_layer_geom(int hq, int hkv, int dr, int n_dense, 
   const int unit = kWaves * kRowBlock;
   const int rows = (n_dense + w - 1) / w;
   g.dense_rows = (rows + unit - 1) / unit * unit;
+  // zoom workgroups: enough to fill the GPU (at most kZoomWgMax unless more
+  // are needed), and never fewer than Hkv S_c / kZoomBatchMax + Hkv, so that
+  // no workgroup's share of a layer's zoomed spans exceeds kZoomBatchMax
+  int z = hkv * g.n_chunks;
+  if (z > kZoomWgMax) z = kZoomWgMax;
+  const long long need = ((long long)hkv * sc + kZoomBatchMax - 1) / kZoomBatchMax + hkv;
+  if (z < need) z = (int)need;
+  g.z_total = z;
   return g;
 }
 
 // What one launch of the layer kernel does (bit set).
 enum LayerMode : int {
   kRoute = 1,      // gate the chunk's spans: mask (+ prob) and the chunk's zoom bit masks
-  kDense = 2,      // attend the workgroup's full-resolution rows and coarse entries
-  kZoom = 4,       // attend the chunk's zoomed spans from their factors
-  kZoomSplit = 8,  // zoomed-span partials go to their own slots (separate launch)
+  kDense = 2,      // attend the workgroup's full-resolution rows and coarse entries (and
+                   // write the chunk's zoom bit masks from the mask if not routing)
+  kZoomSplit = 8,  // tail launch: merge the zoom kernel's slots too
   kMerge = 16,     // tail launch: merge each query head's partials into o
   kLists = 32,     // tail launch: write the ascending zoom lists and union
 };
@@ -194,8 +214,8 @@ struct LayerArgs {
   const void* kbar;        // [Hkv][S_c][d]
   const void* vbar;
   const int32_t* clen;     // [S_c]
-  const int32_t* rank;     // [Hkv][S_c] packed key and value ranks
-  const uint64_t* fac_off; // [Hkv][S_c] float offsets
+  const int32_t* rank;     // [Hkv][sc_stride] packed key and value ranks
+  const uint64_t* fac_off; // [Hkv][sc_stride] float offsets
   const float* pool;       // factor blocks, addressed as pool + (fac_off - off_base)
   uint64_t off_base;
   uint8_t* mask;           // [Hq][S_c] (written with kRoute, read otherwise)
@@ -207,6 +227,7 @@ struct LayerArgs {
   float* o;                // [Hq][d]
   float* part;             // workspace
   uint32_t* chunk_bits;    // [Hkv][n_work][kListWords] zoom bit masks of each chunk
+  int32_t* zcount;         // [Hkv] zoom workgroups of each KV head (written by the zoom kernel)
   const float* zero_block; // kZeroBlockFloats zeros
 };
 
@@ -225,15 +246,26 @@ hipError_t launch_segment(const float* s, int n, int window, double alpha, int m
                           const SegOut& o, hipStream_t st);
 hipError_t launch_log_len(const int32_t* clen, int sc, double* lnn64, float* lnn32,
                           hipStream_t st);
+// spans j0 .. j0 + n - 1; `stride` separates the (layer, head) rows of the
+// span arrays, n_tokens the rows of the K/V (or dense) source
 hipError_t launch_span_rank(const int32_t* rank_by_pos, const int32_t* cstart,
-                            const int32_t* clen, int n_tokens, int sc, int n_lg, int max_rank,
-                            int32_t* rank, hipStream_t st);
+                            const int32_t* clen, int n_tokens, int j0, int n, int stride,
+                            int n_lg, int max_rank, int32_t* rank, hipStream_t st);
 hipError_t launch_gather_dense(int bf16, const void* src, int n_tokens, const int32_t* pos,
-                               int n_dense, int n_lg, void* dst, hipStream_t st);
+                               int n_dense, int dst_stride, int n_lg, void* dst, hipStream_t st);
+// window append: per-row 32-bit gather, and removal of sorted row ranges
+// ([a, len] pairs, device int32) from [0, n_rows) of each of n_lg blocks of
+// stride rows (rows of elems_per_row elements of elem_bytes 4 or 16)
+hipError_t launch_gather_words(const uint32_t* src, int src_stride, const int32_t* pos, int n,
+                               int dst_stride, int n_lg, uint32_t* dst, hipStream_t st);
+hipError_t launch_compact_rows(void* base, int elem_bytes, int stride, int elems_per_row,
+                               int n_rows, int n_lg, const int32_t* ranges, int n_ranges,
+                               hipStream_t st);
 hipError_t launch_span_summarize(int bf16, const float* s, const void* k, const void* v,
                                  const float* w_route, int n_tokens, const int32_t* cstart,
-                                 const int32_t* clen, int sc, int n_layers, int hkv, int group,
-                                 int dr, void* kbar, void* vbar, void* summ, hipStream_t st);
+                                 const int32_t* clen, int j0, int n, int sc, int n_layers,
+                                 int hkv, int group, int dr, void* kbar, void* vbar, void* summ,
+                                 hipStream_t st);
 hipError_t launch_span_svd(int bf16, const void* x, int n_tokens, const int32_t* cstart,
                            const int32_t* clen, const int32_t* span_ids, int n_ids, int sc,
                            int n_lg, const int32_t* rank, const uint64_t* fac_off, float* pool,
@@ -259,14 +291,19 @@ hipError_t launch_layer_batch(int bf16, int mode, int group, const BatchLayerArg
 hipError_t launch_layer_tail(int mode, const LayerGeom& g, const LayerArgs& a, hipStream_t st);
 hipError_t launch_layer_tail_batch(int mode, int group, const BatchLayerArgs& b, int batch,
                                    hipStream_t st);
+// the zoomed spans of a layer, after a layer launch that wrote its chunk masks
+hipError_t launch_zoom(const LayerGeom& g, const LayerArgs& a, hipStream_t st);
+hipError_t launch_zoom_batch(int group, const BatchLayerArgs& b, int batch, hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st);
 // matched-budget cap of one layer's route output (in place); the kernel keeps
 // one bit per union entry in LDS, so S_c is limited to kCapMaxSpans
 constexpr int kCapMaxSpans = 1 << 19;
 size_t cap_budget_lds_bytes(int sc);
+// drop == NULL caps each KV head on its own; else drop [Hkv][S_c] bytes of
+// scratch and one budget for the whole layer
 hipError_t launch_cap_budget(int sc, int hkv, int group, long long budget, const int32_t* clen,
                              const double* prob, uint8_t* mask, int32_t* list, int32_t* count,
-                             int32_t* ulist, int32_t* ucount, hipStream_t st);
+                             int32_t* ulist, int32_t* ucount, uint8_t* drop, hipStream_t st);
 // HBM residency cache of host-tier factor blocks (two-choice: a block may sit
 // in either of two hashed sets, one slot per set).  A block's key is
 // (layer * Hkv + g) * S_c + j, below 2^kResKeyBits; a set's claim is
@@ -296,8 +333,8 @@ hipError_t launch_resident_fetch(const LayerGeom& g, int layer, const int32_t* u
 hipError_t launch_gate_repack(const float* old_pool, const uint64_t* old_off,
                               const int32_t* old_rank, float* new_pool, const uint64_t* new_off,
                               const int32_t* new_rank, const uint8_t* kept, const float* key_gates,
-                              const float* value_gates, const int32_t* clen, int sc, int max_rank,
-                              uint64_t n_blocks, hipStream_t st);
+                              const float* value_gates, const int32_t* clen, int sc, int scs,
+                              int max_rank, uint64_t n_blocks, hipStream_t st);
 hipError_t launch_fetch_gather(const LayerGeom& g, const int32_t* ulist, const int32_t* ucount,
                                const int32_t* clen, const int32_t* rank,
                                const uint64_t* fac_off, uint64_t layer_base,

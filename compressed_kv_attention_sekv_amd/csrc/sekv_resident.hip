@@ -57,14 +57,14 @@ __device__ __forceinline__ void res_sets(uint64_t key, uint64_t n_sets, uint64_t
 
 __global__ __launch_bounds__(256) void res_claim_kernel(
     const int32_t* __restrict__ ulist, const int32_t* __restrict__ ucount,
-    const int32_t* __restrict__ clen, const int32_t* __restrict__ rank, int sc, int layer,
-    int hkv, uint64_t slot_floats, uint64_t n_sets, uint64_t epoch,
+    const int32_t* __restrict__ clen, const int32_t* __restrict__ rank, int sc, int scs,
+    int layer, int hkv, uint64_t slot_floats, uint64_t n_sets, uint64_t epoch,
     const long long* __restrict__ tag, unsigned long long* __restrict__ claim) {
   const int g = blockIdx.y;
   const int nu = ucount[g];
   for (int u = blockIdx.x * 256 + threadIdx.x; u < nu; u += gridDim.x * 256) {
     const int j = ulist[(size_t)g * sc + u];
-    const FactorView fv = FactorView::packed(rank[(size_t)g * sc + j], clen[j]);
+    const FactorView fv = FactorView::packed(rank[(size_t)g * scs + j], clen[j]);
     if (fv.block_floats() > slot_floats) continue;
     const uint64_t key = ((uint64_t)layer * hkv + g) * (uint64_t)sc + j;
     uint64_t s1, s2;
@@ -78,7 +78,8 @@ __global__ __launch_bounds__(256) void res_claim_kernel(
 __global__ __launch_bounds__(256) void res_fetch_kernel(
     const int32_t* __restrict__ ulist, const int32_t* __restrict__ ucount,
     const int32_t* __restrict__ clen, const int32_t* __restrict__ rank,
-    const uint64_t* __restrict__ fac_off, uint64_t layer_base, int sc, int layer, int hkv,
+    const uint64_t* __restrict__ fac_off, uint64_t layer_base, int sc, int scs, int layer,
+    int hkv,
     uint64_t slot_floats, uint64_t n_sets, uint64_t epoch,
     const unsigned long long* __restrict__ claim, long long* __restrict__ tag,
     const float* __restrict__ host, float* __restrict__ arena, uint64_t slots_off,
@@ -87,9 +88,9 @@ __global__ __launch_bounds__(256) void res_fetch_kernel(
   const int nu = ucount[g];
   for (int u = blockIdx.x; u < nu; u += kResSlotsPerHead) {
     const int j = ulist[(size_t)g * sc + u];
-    const FactorView fv = FactorView::packed(rank[(size_t)g * sc + j], clen[j]);
+    const FactorView fv = FactorView::packed(rank[(size_t)g * scs + j], clen[j]);
     const uint64_t nfl = fv.block_floats();
-    const uint64_t hoff = fac_off[(size_t)g * sc + j];
+    const uint64_t hoff = fac_off[(size_t)g * scs + j];
     const uint64_t key = ((uint64_t)layer * hkv + g) * (uint64_t)sc + j;
     uint64_t dst_off = hoff - layer_base;   // the layer's staging (arena start)
     bool copy = true, hit = false, cached = false;
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(256) void res_fetch_kernel(
     // every lane has read the tag before it changes
     __syncthreads();
     if (threadIdx.x == 0) {
-      off_out[(size_t)g * sc + j] = dst_off;
+      off_out[(size_t)g * scs + j] = dst_off;
       if (cached && !hit) tag[set] = (long long)key;
       const unsigned long long bytes = (unsigned long long)fv.alg_bytes();
       atomicAdd(&stats[hit ? 0 : 1], 1ull);
@@ -141,12 +142,13 @@ hipError_t launch_resident_fetch(const LayerGeom& g, int layer, const int32_t* u
   const int sc = g.n_compressed, hkv = g.n_kv_heads;
   const int cx = (sc + 255) / 256;
   hipLaunchKernelGGL(res_claim_kernel, dim3(cx < 64 ? cx : 64, hkv), dim3(256), 0, st, ulist,
-                     ucount, clen, rank, sc, layer, hkv, rv.slot_floats, rv.n_sets, epoch,
-                     rv.tag, rv.claim);
+                     ucount, clen, rank, sc, g.sc_stride, layer, hkv, rv.slot_floats, rv.n_sets,
+                     epoch, rv.tag, rv.claim);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(res_fetch_kernel, dim3(kResSlotsPerHead, hkv), dim3(256), 0, st, ulist,
-                     ucount, clen, rank, fac_off, layer_base, sc, layer, hkv, rv.slot_floats,
+                     ucount, clen, rank, fac_off, layer_base, sc, g.sc_stride, layer, hkv,
+                     rv.slot_floats,
                      rv.n_sets, epoch, rv.claim, rv.tag, host_pool_mapped, rv.arena,
                      rv.slots_off, rv.off, rv.stats);
   return hipGetLastError();

@@ -79,7 +79,8 @@ typedef struct {
   int32_t factor_tier;    /* sekv_tier */
   uint64_t host_pool_cap_bytes;  /* host tier: refuse a pool larger than this (0 = no cap) */
   int32_t svd_mode;       /* sekv_svd_mode */
-  int32_t reserved;       /* must be 0 */
+  int32_t append_capacity; /* tokens sekv_append_tokens may add over the cache's life
+                              (device-tier factors only); 0 = the cache never grows */
 } sekv_config;
 
 typedef struct {
@@ -93,6 +94,9 @@ typedef struct {
   uint64_t resident_bytes;       /* dense rows, means, summaries, tables on the device */
   uint64_t factor_bytes;         /* sum over (layer, KV head, span) of 4 (rK + rV) (n + d + 1) */
   uint64_t factor_pool_bytes;    /* bytes allocated for the pool, padding included */
+  int32_t open_start, open_len;  /* retired tokens not yet closed into a span (appends) */
+  int32_t n_appended;            /* tokens added by sekv_append_tokens so far */
+  int32_t append_capacity;       /* as configured */
 } sekv_cache_info;
 
 /* Output of sekv_route for one layer; every buffer is device memory the
@@ -163,6 +167,42 @@ sekv_status sekv_cache_copy_group(const sekv_cache* cache, int32_t layer, int32_
 sekv_status sekv_cache_copy_factors(const sekv_cache* cache, int32_t layer, int32_t kv_head,
                                     int32_t span, int32_t kv, float* u, float* sigma, float* vt);
 
+/* Append decode tokens to the cache's local window and retire the tokens that
+ * leave it (SeKV paper Sec. 3.3: every decode step attends over the
+ * mixed-resolution memory; the summary page, sec. 2: the most recent `window`
+ * tokens stay at full resolution; how tokens leave the window is not stated).
+ * Reading: each appended token enters the window at full resolution; a token
+ * that leaves the window is compared with the build's threshold (the prompt's
+ * mean + alpha std, computed once): above it, it becomes an anchor;
+ * otherwise it joins the open run of retired tokens since the last retired
+ * anchor, which stays at full resolution until the next retired anchor closes
+ * it into a span.  A closed span of at least min_span_len tokens is
+ * compressed exactly as the build compresses spans (surprisal weights, coarse
+ * mean key and value, routing summaries, truncated SVD of its keys and of its
+ * values at the rank requested at its first token, exact SVD); a shorter one
+ * stays at full resolution.  Nothing the build or earlier appends made
+ * changes.
+ *   n_new >= 1 tokens, in order, following the cache's last token:
+ *   surprisal_dev: device float32 [n_new]
+ *   k_dev, v_dev:  device [L][Hkv][n_new][d] in kv_dtype
+ *   w_route_dev:   device float32 [L][Hq][dr][d], the summary projections of
+ *                  the build
+ *   rank_dev:      device int32 [L][Hkv][n_new], the rank requested for a span
+ *                  that starts at each new token, or NULL for max_rank.
+ * The span table, full-resolution set, compressed spans and decode geometry
+ * grow; S_c (and with it the route buffer sizes) and the decode workspace
+ * size may change: read them again (sekv_cache_info_get,
+ * sekv_decode_workspace_bytes) before the next decode call.  Synchronises
+ * `stream`; no decode call of this cache may be in flight.  Errors:
+ * SEKV_ERR_INVALID for NULL arguments, n_new < 1 or a non-finite surprisal
+ * (nothing changed); SEKV_ERR_UNSUPPORTED for a cache built without
+ * append_capacity (or with host-tier factors, where it must be 0);
+ * SEKV_ERR_NOMEM when n_appended + n_new exceeds append_capacity (nothing
+ * changed); after SEKV_ERR_HIP the cache must be destroyed. */
+sekv_status sekv_append_tokens(sekv_cache* cache, int32_t n_new, const float* surprisal_dev,
+                               const void* k_dev, const void* v_dev, const float* w_route_dev,
+                               const int32_t* rank_dev, hipStream_t stream);
+
 /* Route one layer (SeKV paper Sec. 3.2 gate and Sec. 3.3 Eq. 9), float64
  * throughout: q~_h = P_h q_h; x_j = q~_h . s_{h,j} + gamma ln n_j;
  * p_j = 1 / (1 + e^-x_j); span j is zoomed by head h iff p_j > tau_h.
@@ -201,8 +241,10 @@ sekv_status sekv_decode_attn(const sekv_cache* cache, int32_t layer, const float
  * Eq. 9 and the mixed-resolution softmax): the result is the same as
  * sekv_route followed by sekv_decode_attn with the same arguments, and `route`
  * receives the same mask, lists and counts (and prob, if non-NULL).  With
- * device-tier factors the layer is two kernel launches on `stream` (route and
- * attention in one pass, then the merge and lists); with host-tier factors it
+ * device-tier factors the layer is three kernel launches on `stream` (routing
+ * with the full-resolution rows and coarse entries; the zoomed spans, shared
+ * among the workgroups in proportion to each KV head's union; the merge and
+ * lists); with host-tier factors it
  * runs as sekv_route then sekv_decode_attn (fetch on `fetch_stream`).
  * Arguments as for those two calls. */
 sekv_status sekv_route_attn(const sekv_cache* cache, int32_t layer, const float* q_dev,
@@ -252,6 +294,22 @@ sekv_status sekv_route_attn_noalloc(const sekv_cache* cache, int32_t layer, cons
  * more than 2^19 compressed spans. */
 sekv_status sekv_cap_budget(const sekv_cache* cache, const sekv_route_out* route,
                             int64_t budget_tokens, hipStream_t stream);
+
+/* The same cap with one budget for the whole layer (SeKV paper Sec. 3.3
+ * defines the budget as the peak GPU-resident KV of a decoding step,
+ * reconstructed spans included; a step reaches that peak inside one layer,
+ * since a layer's reconstructed spans are needed only while it attends).  The
+ * candidates are the (KV head g, span j) pairs of every union of the layer,
+ * keyed as above, in one order: key descending, ties to the lower KV head,
+ * then the lower span id; the kept candidates are the longest prefix whose
+ * total length sum n_j (counted once per KV head that reconstructs j) is at
+ * most budget_tokens.  A kept (g, j) stays zoomed for the heads of g that
+ * selected it; a dropped one leaves their masks.  Two launches on `stream`
+ * (the decisions, then their application in place); arguments and errors as
+ * for sekv_cap_budget.  Uses the cache's per-layer decision scratch, so calls
+ * on one cache must not overlap. */
+sekv_status sekv_cap_budget_layer(const sekv_cache* cache, const sekv_route_out* route,
+                                  int64_t budget_tokens, hipStream_t stream);
 
 /* Soft-gated reconstruction (SeKV paper Sec. 3.2 low-rank paragraph, Eq. 8:
  * K^_j = U_j diag(g_j * sigma_j) V_j^T with per-component gates in [0, 1],

@@ -61,7 +61,7 @@ def _cfg(**kw):
     ("factor_tier", 3, "factor_tier"),
     ("alpha", float("nan"), "finite"),
     ("svd_mode", 2, "svd_mode"),
-    ("reserved", 1, "reserved"),
+    ("append_capacity", -1, "append_capacity"),
 ])
 def test_build_rejects_bad_config(L, field, value, msg):
     cfg = _cfg(**{field: value})
@@ -93,6 +93,7 @@ def test_calls_on_null_cache_are_rejected(L):
     assert L.sekv_decode_attn(None, 0, None, ctypes.byref(ro), None, None, 0, None,
                               None) == S.SEKV_ERR_INVALID
     assert L.sekv_cap_budget(None, ctypes.byref(ro), 0, None) == S.SEKV_ERR_INVALID
+    assert L.sekv_cap_budget_layer(None, ctypes.byref(ro), 0, None) == S.SEKV_ERR_INVALID
     assert L.sekv_set_residency(None, 1 << 20, 1 << 16) == S.SEKV_ERR_INVALID
     assert L.sekv_apply_gates(None, ctypes.c_void_p(8), ctypes.c_void_p(8), 0.5,
                               None) == S.SEKV_ERR_INVALID

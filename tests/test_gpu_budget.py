@@ -1,7 +1,9 @@
 """Parity of the matched-budget cap (SeKV paper Sec. 3.3, zoom-in decoding)
-through the C ABI: sekv_cap_budget against the oracle's cap_budget on the same
-gate values and masks, bit-exact (masks, per-head lists, unions), and the
-attention over the capped route against the oracle's mixed attention."""
+through the C ABI: sekv_cap_budget (per KV head) and sekv_cap_budget_layer
+(one budget and one order for the whole layer) against the oracle's
+cap_budget on the same gate values and masks, bit-exact (masks, per-head
+lists, unions), and the attention over the capped route against the oracle's
+mixed attention."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +11,7 @@ import torch
 import oracle as O
 import synth
 from tests.conftest import gpu_available
-from tests.parity import Inputs, OracleSide, log, make_cfg, rel_err, to64
+from tests.parity import Inputs, OracleSide, attn_err, log, make_cfg, rel_err, to64
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -48,6 +50,61 @@ def assert_route_equals(rb, ref: O.LayerRoute, hq: int, hkv: int):
     uc, ul = rb.union_count.cpu().numpy(), rb.union_list.cpu().numpy()
     for g in range(hkv):
         assert ul[g, :uc[g]].tolist() == ref.unions[g].tolist(), f"group {g}"
+
+
+@pytest.mark.parametrize("name,kw,zoom", [
+    ("llama3_8b_128k", dict(n_layers=1, n_tokens=20000), 0.3),
+    ("qwen25_14b_128k_b4", dict(n_layers=1, n_tokens=9000, batch=1), 0.5),
+    ("llama3_8b_128k", dict(n_layers=1, n_tokens=5000, n_q_heads=24, n_kv_heads=8), 0.2),
+])
+def test_layer_budget_cap_matches_oracle(S, name, kw, zoom):
+    """One budget for the layer: the kept (KV head, span) pairs are the longest
+    prefix of one order over every KV head's candidates (key descending, ties
+    to the lower KV head, then the lower span id)."""
+    wl = synth.workload(name, **kw)
+    hq, hkv = wl.n_q_heads, wl.n_kv_heads
+    log(f"[budget] layer scope {name} {kw} zoom={zoom}")
+    inp = Inputs(wl, 10)
+    cache = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    orc = OracleSide(inp, [0], wl.max_rank)
+    sc = cache.info.n_compressed
+    q = inp.query(0)[0].contiguous()
+    p = inp.p[0].contiguous()
+    # uneven zoom across KV heads: head 0 of every other KV head zooms 3x the share
+    prob = orc.route(0, to64(q), to64(p), np.full(hq, 2.0), wl.gamma).prob
+    g = wl.group
+    share = [min(0.9, zoom * (3.0 if (h // g) % 2 == 0 and h % g == 0 else 1.0)) for h in range(hq)]
+    tau = torch.tensor([float(np.quantile(prob[h], 1.0 - share[h])) for h in range(hq)],
+                       dtype=torch.float32).cuda()
+    base = S.RouteBuffers.allocate(cache, with_prob=True)
+    S.sekv_route(cache, 0, q, p, tau, base)
+    torch.cuda.synchronize()
+    uncapped = gpu_route_as_oracle(base, sc, hq, hkv)
+    n = orc.seg.span_len[orc.seg.cspan].astype(np.int64)
+    total = sum(int(n[u].sum()) for u in uncapped.unions)
+    assert total > 0
+    budgets = sorted({0, 1, total // 5, total // 2, total - 1, total, 10 ** 12})
+    ws = torch.empty(cache.workspace_bytes(), dtype=torch.uint8, device="cuda")
+    for budget in budgets:
+        rb = clone_route(S, base)
+        S.sekv_cap_budget(cache, rb, budget, scope="layer")
+        o = torch.zeros(hq, wl.head_dim, device="cuda")
+        S.sekv_decode_attn(cache, 0, q, rb, o, ws)
+        torch.cuda.synchronize()
+        ref = O.cap_budget(uncapped, orc.seg, hkv, budget, scope="layer")
+        assert_route_equals(rb, ref, hq, hkv)
+        assert torch.equal(rb.prob, base.prob)
+        kept = [int(n[u].sum()) for u in ref.unions]
+        assert sum(kept) <= budget
+        out = orc.decode(0, to64(q), ref)
+        worst = max(attn_err(to64(o)[h], out[h]) for h in range(hq))
+        log(f"[budget] layer budget={budget} kept tokens per group {kept} (total {total}) "
+            f"zoomed pairs {int(ref.mask.sum())} err={worst:.2e}")
+        assert worst <= TOL[wl.kv_dtype]
+        if budget >= total:
+            assert torch.equal(rb.mask, base.mask) and torch.equal(rb.count, base.count)
+        if budget == 0:
+            assert int(rb.count.sum()) == 0 and int(rb.union_count.sum()) == 0
 
 
 @pytest.mark.parametrize("name,kw,zoom", [
@@ -93,7 +150,12 @@ def test_budget_cap_matches_oracle(S, name, kw, zoom):
         kept = [int(n[u].sum()) for u in ref.unions]
         assert all(k <= budget for k in kept)
         out = orc.decode(0, to64(q), ref)
-        worst = max(rel_err(to64(o)[h], out[h]) for h in range(hq))
+        worst = max(attn_err(to64(o)[h], out[h]) for h in range(hq))
+        if hkv == 1:   # one KV head: the layer scope is the per-KV-head cap
+            rl = clone_route(S, base)
+            S.sekv_cap_budget(cache, rl, budget, scope="layer")
+            torch.cuda.synchronize()
+            assert torch.equal(rl.mask, rb.mask) and torch.equal(rl.union_count, rb.union_count)
         log(f"[budget] budget={budget} kept tokens per group {kept} (of {totals}) "
             f"zoomed pairs {int(ref.mask.sum())} err={worst:.2e}")
         assert worst <= TOL[wl.kv_dtype]

@@ -78,7 +78,7 @@ def check_layer(S, cache, orc, inp, layer, q, tau, gamma, tol):
     return n_tie, worst, route
 
 
-@pytest.mark.parametrize("seed", [1, 2, 3, 4])
+@pytest.mark.parametrize("seed", list(range(1, 17)))
 def test_tiny_workload_full_parity(S, seed):
     wl = synth.workload("tiny")
     log(f"[parity] tiny seed={seed} N={wl.n_tokens}")
@@ -443,6 +443,28 @@ def sampled_group_parity(S, wl, inp, cache, s64, seg, layer, kv_head, step, tag)
         f"rel err {worst:.2e}, zoom {route.mask.mean(axis=1).round(3).tolist()} ties "
         f"{int(tie.sum())} attention err {err:.2e}")
     assert err <= TOL["bf16"]
+
+
+@pytest.fixture(scope="module")
+def full_c2(S):
+    """The Llama-3.2-3B-shape workload at full size (28 layers, 24 query / 8 KV
+    heads, 32768 tokens, bf16), built once."""
+    wl = synth.workload("llama32_3b_32k")
+    seed = synth.default_seed(wl)
+    log("[parity] full size: drawing inputs and building the 32K cache")
+    inp = Inputs(wl, seed)
+    cache = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    s64 = to64(inp.s)
+    seg = O.segment(s64, wl.window, wl.alpha, wl.min_span_len)
+    return wl, inp, cache, s64, seg
+
+
+@pytest.mark.parametrize("layer,kv_head", [(0, 0), (13, 4), (27, 7), (20, 2)])
+def test_full_size_32k_sampled_parity(S, full_c2, layer, kv_head):
+    """Full-size Llama-3.2-3B shape (32K): sampled (layer, KV head) groups
+    against the oracle through the single-launch call."""
+    wl, inp, cache, s64, seg = full_c2
+    sampled_group_parity(S, wl, inp, cache, s64, seg, layer, kv_head, 3 + layer, "full size 32K")
 
 
 @pytest.mark.parametrize("layer,kv_head", [(0, 3), (31, 6), (12, 0), (20, 7), (7, 5), (27, 2)])
