@@ -44,10 +44,13 @@ def parse():
     ap.add_argument("--tier", choices=["device", "host"], default="device")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=3)
-    ap.add_argument("--cpu-configs", action="store_true",
-                    help="only time the CPU oracle (one pinned core) on every decode workload and "
-                         "print one JSON line; uses no GPU")
+    ap.add_argument("--cpu-layers", type=int, default=1,
+                    help="layers the CPU oracle decodes for cpu_baseline: 1 = the middle layer, "
+                         "3 = first, middle and last")
+    ap.add_argument("--cpu-configs", nargs="?", const="all", default=None,
+                    help="only time the CPU oracle (one pinned core) on the decode workloads "
+                         "(comma-separated names, default all) and print one JSON line; uses no "
+                         "GPU")
     ap.add_argument("--n-layers", type=int, default=None, help="override layer count (testing)")
     ap.add_argument("--n-tokens", type=int, default=None, help="override context (testing)")
     ap.add_argument("--batch", type=int, default=None,
@@ -60,6 +63,13 @@ def parse():
     ap.add_argument("--residency-gb", type=float, default=0.0,
                     help="host tier: HBM residency cache of factor blocks, in GB (0 = none)")
     ap.add_argument("--slot-kb", type=int, default=64, help="residency cache slot size, KiB")
+    ap.add_argument("--fetch", choices=["gather", "memcpy"], default="gather",
+                    help="host tier: factor fetch by the gather kernel, or one hipMemcpyAsync per "
+                         "run of union spans (the host waits for each layer's route)")
+    ap.add_argument("--trace-summary", default=None,
+                    help="summarise a rocprofv3 kernel trace CSV (per-kernel launches and mean "
+                         "duration; host tier: how much of each layer's factor fetch overlaps "
+                         "its full-resolution launch) and exit; uses no GPU")
     ap.add_argument("--query-corr", type=float, default=0.0,
                     help="AR(1) correlation of consecutive step queries (0 = independent)")
     ap.add_argument("--svd", choices=["exact", "randomized"], default="exact",
@@ -67,6 +77,11 @@ def parse():
     ap.add_argument("--gates", type=float, default=None,
                     help="soft-gate the factors after the build (Eq. 8) with synthetic gates, "
                          "dropping components whose gate is below this value")
+    ap.add_argument("--zoom-sweep", default=None,
+                    help="comma-separated zoom shares: one build, one JSON line per share")
+    ap.add_argument("--full-rank", action="store_true",
+                    help="build every span at full rank (rank cap d, every component kept); with "
+                         "--zoom-frac 1 the step is the dense-attention check")
     ap.add_argument("--zoom-frac", type=float, default=None,
                     help="share of spans every query head zooms, replacing the workload's own "
                          "shares (0 zooms nothing, 1 zooms every span)")
@@ -88,7 +103,7 @@ def counters_apply(args) -> bool:
     return (args.tier == "device" and args.budget is None and args.gates is None
             and args.query_corr == 0.0 and args.svd == "exact" and args.zoom_frac is None
             and args.batch is None and args.n_layers is None and args.n_tokens is None
-            and args.residency_gb == 0.0)
+            and args.residency_gb == 0.0 and not args.zoom_sweep and not args.full_rank)
 
 
 def read_traffic(workload: str):
@@ -106,6 +121,9 @@ def read_traffic(workload: str):
 
 def main():
     args = parse()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.cpu_configs:
         cpu_configs(args)
         return
@@ -147,6 +165,8 @@ def main():
 
     # ---- inputs, resident in HBM, and one cache per sequence ---------------------
     w, p = synth.route_weights(wl, seed, device=dev)
+    if args.full_rank:
+        wl = wl.with_(max_rank=d)
     cfg = S.make_config(L, Hq, Hkv, head_dim=d, route_dim=wl.route_dim, window=wl.window,
                         max_rank=wl.max_rank, min_span_len=wl.min_span_len, alpha=wl.alpha,
                         gamma=wl.gamma, kv_dtype=wl.kv_dtype, factor_tier=args.tier,
@@ -156,6 +176,8 @@ def main():
         t0 = time.time()
         s_b, spike_b = synth.surprisal(wl, seed, seq=b, device=dev)
         k, v, ranks_b = synth.kv_cache(wl, seed, spike_b, seq=b, device=dev)
+        if args.full_rank:
+            ranks_b = torch.full_like(ranks_b, d)
         torch.cuda.synchronize()
         log(f"sequence {b}: inputs drawn in {time.time() - t0:.1f}s: K/V "
             f"{2 * k.numel() * k.element_size() / 1e9:.1f} GB")
@@ -179,6 +201,8 @@ def main():
                                args.gates)
             log(f"sequence {b}: gates applied in {time.time() - t0:.2f}s, factor bytes "
                 f"{fb / 1e9:.2f} -> {c.info.factor_bytes / 1e9:.2f} GB")
+        if args.tier == "host" and args.fetch != "gather":
+            c.set_fetch_mode(args.fetch)
         caches.append(c)
         if b == 0:
             s, spike, ranks = s_b, spike_b, ranks_b   # the CPU baseline's sample
@@ -189,305 +213,369 @@ def main():
     info = cache.info
     sc = info.n_compressed
 
-    # ---- thresholds: calibrated on the library's own gate values (sequence 0;
-    # thresholds belong to the model, so every sequence uses them) -------------
-    if args.zoom_frac is not None:
-        # one share for every (layer, head), whatever the workload's own mode
-        targets = torch.full((L, Hq), float(args.zoom_frac), dtype=torch.float64)
-    elif wl.tau_mode == "uniform":
-        targets = None
-    else:
-        targets = synth.zoom_targets(wl, seed)
-    if targets is None:
-        tau = synth.tau_uniform(wl, seed, device=dev)
-    else:
-        cq = synth.calibration_queries(wl, seed, 16, device=dev)
-        tau = torch.empty(L, Hq, dtype=torch.float32, device=dev)
-        rb = S.RouteBuffers.allocate(cache, with_prob=True)
-        big = torch.full((Hq,), 2.0, device=dev)
-        for layer in range(L):
-            probs = []
-            for i in range(cq.shape[0]):
-                S.sekv_route(cache, layer, cq[i, layer].contiguous(), p[layer].contiguous(), big, rb)
-                probs.append(rb.prob.clone())
-            allp = torch.cat(probs, dim=1)
-            # a share of 0 zooms nothing (p <= 1 is never above 1), 1 zooms all
-            tau[layer] = torch.stack([
-                torch.tensor(1.0, device=dev) if float(targets[layer, h]) <= 0.0 else
-                torch.tensor(-1.0, device=dev) if float(targets[layer, h]) >= 1.0 else
-                torch.quantile(allp[h], 1.0 - float(targets[layer, h])).float()
-                for h in range(Hq)]).float()
-        torch.cuda.synchronize()
-
-    # ---- per-step buffers ----------------------------------------------------------
-    n_q = args.steps + args.warmup
-    if args.query_corr:
-        qs = torch.stack([synth.correlated_queries(wl, seed, n_q, args.query_corr, seq=b,
-                                                   device=dev) for b in range(B)], dim=1)
-    else:
-        qs = torch.stack([torch.stack([synth.queries(wl, seed, i, seq=b, device=dev)
-                                       for b in range(B)]) for i in range(n_q)])
-    # qs: [T][B][L][Hq][d]
-    if args.residency_gb > 0:
-        cache.set_residency(int(args.residency_gb * 1e9), args.slot_kb * 1024)
-    q_cur = torch.empty(B, L, Hq, d, device=dev)
-    p_c = [p[l].contiguous() for l in range(L)]
-    tau_c = [tau[l].contiguous() for l in range(L)]
-    capped = args.budget is not None
-    routes = [[S.RouteBuffers.allocate(c, with_prob=capped) for _ in range(L)]
-              for c in caches]   # [B][L]
-    outs = torch.zeros(B, L, Hq, d, device=dev)
-    wss = [torch.empty(c.workspace_bytes(), dtype=torch.uint8, device=dev) for c in caches]
-    side = torch.cuda.Stream() if args.tier == "host" else None
-
-    def layer_call(layer):
-        if capped:
-            S.sekv_route(cache, layer, q_cur[0, layer], p_c[layer], tau_c[layer], routes[0][layer])
-            S.sekv_cap_budget(cache, routes[0][layer], args.budget)
-            S.sekv_decode_attn(cache, layer, q_cur[0, layer], routes[0][layer], outs[0, layer],
-                               wss[0], fetch_stream=side)
-        elif B == 1:
-            S.sekv_route_attn(cache, layer, q_cur[0, layer], p_c[layer], tau_c[layer],
-                              routes[0][layer], outs[0, layer], wss[0], fetch_stream=side)
+    def measure(zoom_arg):
+        """Calibrate the thresholds for a zoom share (None: the workload's own
+        shares), time the steps and account their bytes; returns the JSON line."""
+        # ---- thresholds: calibrated on the library's own gate values (sequence 0;
+        # thresholds belong to the model, so every sequence uses them) -------------
+        if zoom_arg is not None:
+            # one share for every (layer, head), whatever the workload's own mode
+            targets = torch.full((L, Hq), float(zoom_arg), dtype=torch.float64)
+        elif wl.tau_mode == "uniform":
+            targets = None
         else:
-            S.sekv_route_attn_batch(caches, layer, [q_cur[b, layer] for b in range(B)],
-                                    p_c[layer], tau_c[layer], [r[layer] for r in routes],
-                                    [outs[b, layer] for b in range(B)], wss)
-
-    def step():
-        for layer in range(L):
-            layer_call(layer)
-
-    graph = None
-    if not args.no_graph and args.tier == "device":
-        q_cur.copy_(qs[0])
-        step()
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        torch.cuda.synchronize()
-
-    def run(i):
-        q_cur.copy_(qs[i])
-        if graph is not None:
-            graph.replay()
+            targets = synth.zoom_targets(wl, seed)
+        if targets is None:
+            tau = synth.tau_uniform(wl, seed, device=dev)
         else:
+            cq = synth.calibration_queries(wl, seed, 16, device=dev)
+            tau = torch.empty(L, Hq, dtype=torch.float32, device=dev)
+            rb = S.RouteBuffers.allocate(cache, with_prob=True)
+            big = torch.full((Hq,), 2.0, device=dev)
+            for layer in range(L):
+                probs = []
+                for i in range(cq.shape[0]):
+                    S.sekv_route(cache, layer, cq[i, layer].contiguous(), p[layer].contiguous(), big, rb)
+                    probs.append(rb.prob.clone())
+                allp = torch.cat(probs, dim=1)
+                # a share of 0 zooms nothing (p <= 1 is never above 1), 1 zooms all
+                tau[layer] = torch.stack([
+                    torch.tensor(1.0, device=dev) if float(targets[layer, h]) <= 0.0 else
+                    torch.tensor(-1.0, device=dev) if float(targets[layer, h]) >= 1.0 else
+                    torch.quantile(allp[h], 1.0 - float(targets[layer, h])).float()
+                    for h in range(Hq)]).float()
+            torch.cuda.synchronize()
+
+        # ---- per-step buffers ----------------------------------------------------------
+        n_q = args.steps + args.warmup
+        if args.query_corr:
+            qs = torch.stack([synth.correlated_queries(wl, seed, n_q, args.query_corr, seq=b,
+                                                       device=dev) for b in range(B)], dim=1)
+        else:
+            qs = torch.stack([torch.stack([synth.queries(wl, seed, i, seq=b, device=dev)
+                                           for b in range(B)]) for i in range(n_q)])
+        # qs: [T][B][L][Hq][d]
+        if args.residency_gb > 0:
+            cache.set_residency(int(args.residency_gb * 1e9), args.slot_kb * 1024)
+        q_cur = torch.empty(B, L, Hq, d, device=dev)
+        p_c = [p[l].contiguous() for l in range(L)]
+        tau_c = [tau[l].contiguous() for l in range(L)]
+        capped = args.budget is not None
+        routes = [[S.RouteBuffers.allocate(c, with_prob=capped) for _ in range(L)]
+                  for c in caches]   # [B][L]
+        outs = torch.zeros(B, L, Hq, d, device=dev)
+        wss = [torch.empty(c.workspace_bytes(), dtype=torch.uint8, device=dev) for c in caches]
+        side = torch.cuda.Stream() if args.tier == "host" else None
+
+        def layer_call(layer):
+            if capped:
+                S.sekv_route(cache, layer, q_cur[0, layer], p_c[layer], tau_c[layer], routes[0][layer])
+                S.sekv_cap_budget(cache, routes[0][layer], args.budget)
+                S.sekv_decode_attn(cache, layer, q_cur[0, layer], routes[0][layer], outs[0, layer],
+                                   wss[0], fetch_stream=side)
+            elif B == 1:
+                S.sekv_route_attn(cache, layer, q_cur[0, layer], p_c[layer], tau_c[layer],
+                                  routes[0][layer], outs[0, layer], wss[0], fetch_stream=side)
+            else:
+                S.sekv_route_attn_batch(caches, layer, [q_cur[b, layer] for b in range(B)],
+                                        p_c[layer], tau_c[layer], [r[layer] for r in routes],
+                                        [outs[b, layer] for b in range(B)], wss)
+
+        def step():
+            for layer in range(L):
+                layer_call(layer)
+
+        graph = None
+        if not args.no_graph and args.tier == "device":
+            q_cur.copy_(qs[0])
             step()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            torch.cuda.synchronize()
 
-    for i in range(args.warmup):
-        run(i)
-    torch.cuda.synchronize()
+        def run(i):
+            q_cur.copy_(qs[i])
+            if graph is not None:
+                graph.replay()
+            else:
+                step()
 
-    # ---- timed region ----------------------------------------------------------
-    if args.residency_gb > 0:
-        cache.residency_stats(reset=True)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.time()
-    ev0.record()
-    for i in range(args.warmup, n_q):
-        run(i)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.time() - wall0
-    total_ms = ev0.elapsed_time(ev1)
-    ms_per_step = total_ms / args.steps
-    log(f"{args.steps} steps in {total_ms:.1f} ms (wall {wall * 1e3:.1f} ms): {ms_per_step:.4f} ms/step")
-    res_stats = cache.residency_stats(reset=True) if args.residency_gb > 0 else None
-    if res_stats:
-        log(f"residency: {res_stats['hit_blocks']} blocks from HBM, {res_stats['fetched_blocks']} "
-            f"over the host link ({res_stats['fetched_bytes'] / args.steps / 1e9:.3f} GB/step)")
+        for i in range(args.warmup):
+            run(i)
+        torch.cuda.synchronize()
 
-    # ---- algorithmic bytes of the timed steps ----------------------------------
-    # per sequence: the resident bytes every layer launch reads, and the factor
-    # bytes 4 (rK + rV) (n + d + 1) of each (layer, KV head, span) for the zoom part
-    eb = 2 if wl.kv_dtype == "bf16" else 4
-    span_bytes, resident_layer = [], 0
-    for c in caches:
-        sp = c.spans()
-        clen = sp["span_len"][sp["cspan"].long()].to(torch.float64)
-        rank_tab = torch.stack([torch.stack([sum(c.group_data(l, g)[3:5]) for g in range(Hkv)])
-                                for l in range(L)]).to(torch.float64)  # [L][Hkv][Sc] rK + rV
-        span_bytes.append((4.0 * rank_tab * (clen + d + 1)).to(dev))
-        D_b, sc_b = c.info.n_dense, c.info.n_compressed
-        resident_layer += (Hkv * (2 * d * eb * D_b + 2 * d * eb * sc_b) +
-                           Hq * wl.route_dim * eb * sc_b + Hq * (wl.route_dim * d + d + 1) * 4 +
-                           Hq * d * 4 + 4 * sc_b)
-
-    zoom_bytes = torch.zeros(args.steps, L, dtype=torch.float64, device=dev)
-    zoom_frac = torch.zeros(L, Hq, dtype=torch.float64, device=dev)
-    union_frac = torch.zeros(L, Hkv, dtype=torch.float64, device=dev)
-    for si, i in enumerate(range(args.warmup, n_q)):
-        q_cur.copy_(qs[i])
-        for layer in range(L):
-            layer_call(layer)
-            for b, c in enumerate(caches):
-                rb = routes[b][layer]
-                sc_b = c.info.n_compressed
-                if sc_b == 0:
-                    continue
-                ar = torch.arange(sc_b, device=dev)
-                valid = ar.unsqueeze(0) < rb.union_count.unsqueeze(1)           # [Hkv][Sc]
-                ids = torch.where(valid, rb.union_list.long(),
-                                  torch.zeros_like(rb.union_list.long()))
-                zb = torch.gather(span_bytes[b][layer], 1, ids) * valid
-                zoom_bytes[si, layer] += zb.sum()
-                zoom_frac[layer] += rb.count.double() / (sc_b * B)
-                union_frac[layer] += rb.union_count.double() / (sc_b * B)
-    torch.cuda.synchronize()
-    zoom_frac /= args.steps
-    union_frac /= args.steps
-    zb_step = zoom_bytes.sum(1)                       # [steps]
-    bytes_step = float(zb_step.mean()) + L * resident_layer
-    step_gbs = bytes_step / (ms_per_step * 1e-3) / 1e9
-    log(f"bytes/step {bytes_step / 1e9:.3f} GB (zoom {float(zb_step.mean()) / 1e9:.3f} GB): "
-        f"{step_gbs:.0f} GB/s = {step_gbs / HBM_PEAK_GBS:.3f} of peak")
-
-    # ---- mean launch of the layer kernel, live, from the timed region ----------
-    # The graph replays launch the 32 layer kernels back to back on one stream
-    # (no host gaps: in a kernel trace the step's span equals the sum of its
-    # launches), so the HIP events around the timed region over its steps x L
-    # launches give the kernel's mean duration (plus one small query copy per
-    # step).  Algorithmic bytes: the timed steps' zoomed-span factors per launch
-    # plus the resident bytes every launch reads.
-    attn_us_mean = total_ms * 1e3 / (args.steps * L)   # with --budget: the layer's 3 launches
-    attn_bytes_meas = float(zoom_bytes.mean()) + resident_layer
-    attn_gbs = attn_bytes_meas / (attn_us_mean * 1e-6) / 1e9
-    log(f"layer launch: {attn_us_mean:.2f} us avg, {attn_bytes_meas / 1e6:.2f} MB algorithmic "
-        f"-> {attn_gbs:.0f} GB/s")
-
-    # ---- reference probes: device copy and pinned host->device copy ------------
-    x = torch.empty(512 * 1024 * 1024, dtype=torch.float32, device=dev)   # 2 GiB
-    y = torch.empty_like(x)
-    y.copy_(x)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
-        y.copy_(x)
-    e1.record()
-    torch.cuda.synchronize()
-    copy_gbs = 5 * 2 * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    # read-only stream: row sums over the same 2 GiB (4096-float rows; writes
-    # 0.02% of what it reads), the fastest read-only torch op on this GPU
-    acc = x.view(-1, 4096).sum(dim=1)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(5):
-        acc = x.view(-1, 4096).sum(dim=1)
-    e1.record()
-    torch.cuda.synchronize()
-    read_gbs = 5 * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del x, y, acc
-    hpin = torch.empty(64 * 1024 * 1024, dtype=torch.float32, pin_memory=True)   # 256 MiB
-    hd = torch.empty(hpin.shape, dtype=torch.float32, device=dev)
-    hd.copy_(hpin, non_blocking=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(4):
-        hd.copy_(hpin, non_blocking=True)
-    e1.record()
-    torch.cuda.synchronize()
-    h2d_gbs = 4 * hpin.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del hpin, hd
-    log(f"probes: device copy {copy_gbs:.0f} GB/s (read+write), read-only {read_gbs:.0f} GB/s, "
-        f"pinned H2D {h2d_gbs:.1f} GB/s")
-
-    host_link = None
-    if args.tier == "host":
-        # bytes that crossed the link: every union block, or with the residency
-        # cache only the blocks it did not hold
-        link_bytes = (res_stats["fetched_bytes"] / args.steps if res_stats
-                      else float(zb_step.mean()))
-        link_gbs = link_bytes / (ms_per_step * 1e-3) / 1e9
-        host_link = {"gbs": link_gbs, "bytes_per_step": link_bytes,
-                     "frac_of_measured_h2d": link_gbs / h2d_gbs,
-                     "frac_of_pcie5_x16": link_gbs / PCIE_GBS}
+        # ---- timed region ----------------------------------------------------------
+        if args.residency_gb > 0:
+            cache.residency_stats(reset=True)
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.time()
+        ev0.record()
+        for i in range(args.warmup, n_q):
+            run(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.time() - wall0
+        total_ms = ev0.elapsed_time(ev1)
+        ms_per_step = total_ms / args.steps
+        log(f"{args.steps} steps in {total_ms:.1f} ms (wall {wall * 1e3:.1f} ms): {ms_per_step:.4f} ms/step")
+        res_stats = cache.residency_stats(reset=True) if args.residency_gb > 0 else None
         if res_stats:
-            tot = res_stats["hit_blocks"] + res_stats["fetched_blocks"]
-            host_link["residency"] = {
-                "capacity_gb": args.residency_gb, "slot_bytes": res_stats["slot_bytes"],
-                "sets": res_stats["sets"],
-                "hit_rate_blocks": res_stats["hit_blocks"] / tot if tot else None,
-                "hit_bytes_per_step": res_stats["hit_bytes"] / args.steps}
+            log(f"residency: {res_stats['hit_blocks']} blocks from HBM, {res_stats['fetched_blocks']} "
+                f"over the host link ({res_stats['fetched_bytes'] / args.steps / 1e9:.3f} GB/step)")
 
-    # ---- CPU oracle baseline on a bounded sample --------------------------------
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, seed, s, spike, w, p, tau, qs[:, 0], args, ranks, B)
+        # ---- algorithmic bytes of the timed steps ----------------------------------
+        # per sequence: the resident bytes every layer launch reads, and the factor
+        # bytes 4 (rK + rV) (n + d + 1) of each (layer, KV head, span) for the zoom part
+        eb = 2 if wl.kv_dtype == "bf16" else 4
+        span_bytes, resident_layer = [], 0
+        for c in caches:
+            sp = c.spans()
+            clen = sp["span_len"][sp["cspan"].long()].to(torch.float64)
+            rank_tab = torch.stack([torch.stack([sum(c.group_data(l, g)[3:5]) for g in range(Hkv)])
+                                    for l in range(L)]).to(torch.float64)  # [L][Hkv][Sc] rK + rV
+            span_bytes.append((4.0 * rank_tab * (clen + d + 1)).to(dev))
+            D_b, sc_b = c.info.n_dense, c.info.n_compressed
+            resident_layer += (Hkv * (2 * d * eb * D_b + 2 * d * eb * sc_b) +
+                               Hq * wl.route_dim * eb * sc_b + Hq * (wl.route_dim * d + d + 1) * 4 +
+                               Hq * d * 4 + 4 * sc_b)
 
-    traffic = read_traffic(wl.name) if counters_apply(args) else None
-    result = {
-        "metric": METRIC,
-        "value": 1e3 / ms_per_step,
-        "unit": "steps/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": wl.kv_dtype,
-        "data": "synthetic",
-        "config": {
-            "workload": wl.name, "n_layers": L, "n_q_heads": Hq, "n_kv_heads": Hkv,
-            "head_dim": d, "context": wl.n_tokens, "batch": B, "kv_dtype": wl.kv_dtype,
-            "factor_dtype": "f32", "factor_tier": args.tier, "window": wl.window,
-            "max_rank": wl.max_rank, "route_dim": wl.route_dim, "graph": graph is not None,
-            "budget_tokens": args.budget, "query_corr": args.query_corr,
-            "gate_eps": args.gates, "svd": args.svd,
-            "zoom": ("skewed" if wl.tau_mode == "skewed" and args.zoom_frac is None else
-                     (f"{float(targets[0, 0]):g} per head" if targets is not None
-                      else "uniform tau")),
-        },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": attn_gbs,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": attn_gbs / HBM_PEAK_GBS,
-            "traffic": traffic,
-            "kernel": ("sekv::layer_kernel + sekv::layer_tail_kernel, twice, and "
-                       "sekv::cap_budget_kernel (sekv_route, sekv_cap_budget, sekv_decode_attn: "
-                       "one layer, capped)" if capped else
-                       "host tier: sekv::layer_kernel + sekv::layer_tail_kernel (route, lists), "
-                       "the factor fetch (fetch_gather_kernel, or res_claim_kernel + "
-                       "res_fetch_kernel with a residency cache), sekv::layer_kernel twice (rows "
-                       "and coarse entries; zoomed spans) and sekv::layer_tail_kernel (merge)"
-                       if args.tier == "host" else
-                       "sekv::layer_kernel + sekv::layer_tail_kernel (sekv_route_attn, one "
-                       "layer: route + attention, then merge + lists)"
-                       if B == 1 else
-                       f"sekv::layer_batch_kernel + sekv::layer_tail_batch_kernel "
-                       f"(sekv_route_attn_batch, one layer of {B} sequences)"),
-            "algorithmic_bytes_per_launch": attn_bytes_meas,
-            "avg_launch_us": attn_us_mean,
-            "avg_launch_from": "HIP events around the timed region / (steps x layers); "
-                               "a layer is every launch named under kernel",
-            "frac_of_measured_read": attn_gbs / read_gbs,
-        },
-        "cpu_baseline": cpu,
-        "step_hbm": {"bytes_per_step": bytes_step, "gbs": step_gbs, "frac": step_gbs / HBM_PEAK_GBS,
-                     "measured_copy_gbs": copy_gbs, "measured_read_gbs": read_gbs},
-        "host_link": host_link,
-        "measured_h2d_gbs": h2d_gbs,
-        "cache": {"n_spans": info.n_spans, "n_compressed": sc, "n_anchors": info.n_anchors,
-                  "n_dense": info.n_dense, "factor_pool_gb": info.factor_pool_bytes / 1e9,
-                  "resident_gb": info.resident_bytes / 1e9, "build_s": build_s,
-                  "zoom_frac_per_head_mean": float(zoom_frac.mean()),
-                  "union_frac_per_group_mean": float(union_frac.mean()),
-                  "zoom_bytes_per_step_gb": float(zb_step.mean()) / 1e9,
-                  # the GPU KV budget of a step: what is resident plus the factors
-                  # of the spans zoomed in it, against the full-resolution K/V
-                  "kv_budget_frac": (sum(c.info.resident_bytes for c in caches) +
-                                     float(zb_step.mean())) /
-                                    (B * L * Hkv * wl.n_tokens * d * 2 * eb),
-                  "tokens_per_s": B * 1e3 / ms_per_step},
-    }
-    print(json.dumps(result), flush=True)
+        # the zoomed spans' bytes, from the union lists of the timed steps' queries
+        # (the first 128 of them: the union fractions vary little between steps,
+        # and re-running every step of a long batched run layer by layer would
+        # take minutes)
+        acct = min(args.steps, 128)
+        zoom_bytes = torch.zeros(acct, L, dtype=torch.float64, device=dev)
+        zoom_frac = torch.zeros(L, Hq, dtype=torch.float64, device=dev)
+        union_frac = torch.zeros(L, Hkv, dtype=torch.float64, device=dev)
+        for si, i in enumerate(range(args.warmup, args.warmup + acct)):
+            q_cur.copy_(qs[i])
+            for layer in range(L):
+                layer_call(layer)
+                for b, c in enumerate(caches):
+                    rb = routes[b][layer]
+                    sc_b = c.info.n_compressed
+                    if sc_b == 0:
+                        continue
+                    ar = torch.arange(sc_b, device=dev)
+                    valid = ar.unsqueeze(0) < rb.union_count.unsqueeze(1)           # [Hkv][Sc]
+                    ids = torch.where(valid, rb.union_list.long(),
+                                      torch.zeros_like(rb.union_list.long()))
+                    zb = torch.gather(span_bytes[b][layer], 1, ids) * valid
+                    zoom_bytes[si, layer] += zb.sum()
+                    zoom_frac[layer] += rb.count.double() / (sc_b * B)
+                    union_frac[layer] += rb.union_count.double() / (sc_b * B)
+        torch.cuda.synchronize()
+        zoom_frac /= acct
+        union_frac /= acct
+        zb_step = zoom_bytes.sum(1)                       # [steps]
+        bytes_step = float(zb_step.mean()) + L * resident_layer
+        step_gbs = bytes_step / (ms_per_step * 1e-3) / 1e9
+        log(f"bytes/step {bytes_step / 1e9:.3f} GB (zoom {float(zb_step.mean()) / 1e9:.3f} GB): "
+            f"{step_gbs:.0f} GB/s = {step_gbs / HBM_PEAK_GBS:.3f} of peak")
+
+        # ---- mean launch of the layer kernel, live, from the timed region ----------
+        # The graph replays launch the 32 layer kernels back to back on one stream
+        # (no host gaps: in a kernel trace the step's span equals the sum of its
+        # launches), so the HIP events around the timed region over its steps x L
+        # launches give the kernel's mean duration (plus one small query copy per
+        # step).  Algorithmic bytes: the timed steps' zoomed-span factors per launch
+        # plus the resident bytes every launch reads.
+        attn_us_mean = total_ms * 1e3 / (args.steps * L)   # with --budget: the layer's 3 launches
+        attn_bytes_meas = float(zoom_bytes.mean()) + resident_layer
+        attn_gbs = attn_bytes_meas / (attn_us_mean * 1e-6) / 1e9
+        log(f"layer launch: {attn_us_mean:.2f} us avg, {attn_bytes_meas / 1e6:.2f} MB algorithmic "
+            f"-> {attn_gbs:.0f} GB/s")
+
+        # ---- reference probes: device copy and pinned host->device copy ------------
+        x = torch.empty(512 * 1024 * 1024, dtype=torch.float32, device=dev)   # 2 GiB
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            y.copy_(x)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_gbs = 5 * 2 * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        # read-only stream: row sums over the same 2 GiB (4096-float rows; writes
+        # 0.02% of what it reads), the fastest read-only torch op on this GPU
+        acc = x.view(-1, 4096).sum(dim=1)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            acc = x.view(-1, 4096).sum(dim=1)
+        e1.record()
+        torch.cuda.synchronize()
+        read_gbs = 5 * x.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del x, y, acc
+        hpin = torch.empty(64 * 1024 * 1024, dtype=torch.float32, pin_memory=True)   # 256 MiB
+        hd = torch.empty(hpin.shape, dtype=torch.float32, device=dev)
+        hd.copy_(hpin, non_blocking=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(4):
+            hd.copy_(hpin, non_blocking=True)
+        e1.record()
+        torch.cuda.synchronize()
+        h2d_gbs = 4 * hpin.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del hpin, hd
+        log(f"probes: device copy {copy_gbs:.0f} GB/s (read+write), read-only {read_gbs:.0f} GB/s, "
+            f"pinned H2D {h2d_gbs:.1f} GB/s")
+
+        host_link = None
+        if args.tier == "host":
+            # bytes that crossed the link: every union block, or with the residency
+            # cache only the blocks it did not hold
+            link_bytes = (res_stats["fetched_bytes"] / args.steps if res_stats
+                          else float(zb_step.mean()))
+            link_gbs = link_bytes / (ms_per_step * 1e-3) / 1e9
+            host_link = {"gbs": link_gbs, "bytes_per_step": link_bytes,
+                         "frac_of_measured_h2d": link_gbs / h2d_gbs,
+                         "frac_of_pcie5_x16": link_gbs / PCIE_GBS}
+            if res_stats:
+                tot = res_stats["hit_blocks"] + res_stats["fetched_blocks"]
+                host_link["residency"] = {
+                    "capacity_gb": args.residency_gb, "slot_bytes": res_stats["slot_bytes"],
+                    "sets": res_stats["sets"],
+                    "hit_rate_blocks": res_stats["hit_blocks"] / tot if tot else None,
+                    "hit_bytes_per_step": res_stats["hit_bytes"] / args.steps}
+
+        # ---- CPU oracle baseline on a bounded sample --------------------------------
+        cpu = None
+        if not args.no_cpu_baseline:
+            cpu = cpu_baseline(wl, seed, s, spike, w, p, tau, qs[:, 0], args, ranks, B)
+
+        traffic = read_traffic(wl.name) if counters_apply(args) else None
+        result = {
+            "metric": METRIC,
+            "value": 1e3 / ms_per_step,
+            "unit": "steps/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": ms_per_step,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": wl.kv_dtype,
+            "data": "synthetic",
+            "config": {
+                "workload": wl.name, "n_layers": L, "n_q_heads": Hq, "n_kv_heads": Hkv,
+                "head_dim": d, "context": wl.n_tokens, "batch": B, "kv_dtype": wl.kv_dtype,
+                "factor_dtype": "f32", "factor_tier": args.tier, "window": wl.window,
+                "max_rank": wl.max_rank, "route_dim": wl.route_dim, "graph": graph is not None,
+                "budget_tokens": args.budget, "query_corr": args.query_corr,
+                "gate_eps": args.gates, "svd": args.svd,
+                "fetch": args.fetch if args.tier == "host" else None,
+                "zoom": ("skewed" if wl.tau_mode == "skewed" and zoom_arg is None else
+                         (f"{float(targets[0, 0]):g} per head" if targets is not None
+                          else "uniform tau")),
+            },
+            "roofline": {
+                "bound": "hbm",
+                "achieved": attn_gbs,
+                "peak": HBM_PEAK_GBS,
+                "unit": "GB/s",
+                "frac": attn_gbs / HBM_PEAK_GBS,
+                "traffic": traffic,
+                "kernel": ("sekv::layer_kernel + sekv::layer_tail_kernel, twice, and "
+                           "sekv::cap_budget_kernel (sekv_route, sekv_cap_budget, sekv_decode_attn: "
+                           "one layer, capped)" if capped else
+                           "host tier: sekv::layer_kernel + sekv::layer_tail_kernel (route, lists), "
+                           "the factor fetch (fetch_gather_kernel, or res_claim_kernel + "
+                           "res_fetch_kernel with a residency cache), sekv::layer_kernel twice (rows "
+                           "and coarse entries; zoomed spans) and sekv::layer_tail_kernel (merge)"
+                           if args.tier == "host" else
+                           "sekv::layer_kernel + sekv::layer_tail_kernel (sekv_route_attn, one "
+                           "layer: route + attention, then merge + lists)"
+                           if B == 1 else
+                           f"sekv::layer_batch_kernel + sekv::layer_tail_batch_kernel "
+                           f"(sekv_route_attn_batch, one layer of {B} sequences)"),
+                "algorithmic_bytes_per_launch": attn_bytes_meas,
+                "avg_launch_us": attn_us_mean,
+                "avg_launch_from": "HIP events around the timed region / (steps x layers); "
+                                   "a layer is every launch named under kernel",
+                "frac_of_measured_read": attn_gbs / read_gbs,
+            },
+            "cpu_baseline": cpu,
+            "step_hbm": {"bytes_per_step": bytes_step, "gbs": step_gbs, "frac": step_gbs / HBM_PEAK_GBS,
+                         "measured_copy_gbs": copy_gbs, "measured_read_gbs": read_gbs},
+            "host_link": host_link,
+            "measured_h2d_gbs": h2d_gbs,
+            "cache": {"n_spans": info.n_spans, "n_compressed": sc, "n_anchors": info.n_anchors,
+                      "n_dense": info.n_dense, "factor_pool_gb": info.factor_pool_bytes / 1e9,
+                      "resident_gb": info.resident_bytes / 1e9, "build_s": build_s,
+                      "zoom_frac_per_head_mean": float(zoom_frac.mean()),
+                      "union_frac_per_group_mean": float(union_frac.mean()),
+                      "zoom_bytes_per_step_gb": float(zb_step.mean()) / 1e9,
+                      # the GPU KV budget of a step: what is resident plus the factors
+                      # of the spans zoomed in it, against the full-resolution K/V
+                      "kv_budget_frac": (sum(c.info.resident_bytes for c in caches) +
+                                         float(zb_step.mean())) /
+                                        (B * L * Hkv * wl.n_tokens * d * 2 * eb),
+                      "tokens_per_s": B * 1e3 / ms_per_step},
+        }
+        return result
+
+    if args.zoom_sweep:
+        for zf in [float(x) for x in args.zoom_sweep.split(",")]:
+            print(json.dumps(measure(zf)), flush=True)
+    else:
+        print(json.dumps(measure(args.zoom_frac)), flush=True)
+
+
+def trace_summary(path: str) -> None:
+    """Per-kernel launches and mean duration of a rocprofv3 kernel trace CSV,
+    the gaps between consecutive decode launches, and for host-tier traces
+    the overlap of each layer's factor fetch (fetch_gather_kernel) with the
+    full-resolution launch that runs beside it on the other stream: the time
+    both run, over the fetch's own time and over the shorter of the two (1 =
+    the shorter one hides entirely under the other).  Prints one JSON line."""
+    import csv
+    import statistics
+    with open(path) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+
+    def span(r):
+        return int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+
+    def short(name):
+        return name.split("(")[0].replace("void ", "").strip()
+
+    per = {}
+    for r in rows:
+        a, b = span(r)
+        per.setdefault(short(r["Kernel_Name"]), []).append((b - a) / 1e3)
+    kernels = {k: {"launches": len(v), "mean_us": statistics.mean(v),
+                   "median_us": statistics.median(v), "total_us": sum(v)}
+               for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1]))}
+    decode = [r for r in rows if any(k in r["Kernel_Name"] for k in
+                                     ("layer_kernel", "zoom_kernel", "layer_tail", "fetch_gather"))]
+    gaps = [(span(b)[0] - span(a)[1]) / 1e3 for a, b in zip(decode, decode[1:])
+            if span(b)[0] >= span(a)[1]]
+    out = {"trace": os.path.basename(path), "kernels": kernels,
+           "decode_gap_us_median": statistics.median(gaps) if gaps else None}
+    # host tier: each fetch against the layer launch that starts closest to it
+    fetch = [r for r in rows if "fetch_gather_kernel" in r["Kernel_Name"]]
+    layer = [r for r in rows if "layer_kernel" in r["Kernel_Name"]]
+    if fetch and layer:
+        fracs = []
+        for fr in fetch:
+            f0, f1 = span(fr)
+            lr = min(layer, key=lambda r: abs(span(r)[0] - f0))
+            l0, l1 = span(lr)
+            both = max(0, min(f1, l1) - max(f0, l0))
+            fracs.append((both / max(f1 - f0, 1), both / max(min(f1 - f0, l1 - l0), 1)))
+        out["fetch_overlap"] = {
+            "fetches": len(fracs),
+            "of_fetch_time_mean": statistics.mean(f for f, _ in fracs),
+            "of_shorter_launch_mean": statistics.mean(g for _, g in fracs)}
+    print(json.dumps(out), flush=True)
 
 
 def host_info() -> dict:
@@ -546,7 +634,7 @@ def oracle_cache(wl, seg, sv, seed, spike, w, layers, device):
     return groups
 
 
-def time_oracle_decode(wl, seg, groups, p, tau, qs, layers, budget_s=10.0, max_steps=40):
+def time_oracle_decode(wl, seg, groups, p, tau, qs, layers, budget_s=12.0, max_steps=200):
     """Route + attention of the given layers, every query head, over fresh step
     queries until about ``budget_s`` of work; returns (seconds per layer, steps)."""
     import oracle as O
@@ -578,7 +666,7 @@ def cpu_baseline(wl, seed, s, spike, w, p, tau, qs, args, ranks, batch=1):
     import oracle as O
 
     L = wl.n_layers
-    layers = sorted({0, L // 2, L - 1}) if args.cpu_layers >= 3 else list(range(args.cpu_layers))
+    layers = sorted({0, L // 2, L - 1}) if args.cpu_layers >= 3 else [L // 2]
     with one_core() as pin:
         t0 = time.time()
         sv = s.detach().cpu().double().numpy()
@@ -613,12 +701,14 @@ def cpu_configs(args):
     import synth
 
     results = []
-    for name, n_layers_timed in (("tiny", 1), ("llama32_3b_32k", 3), ("llama3_8b_128k", 3),
-                                 ("qwen25_14b_128k_b4", 3)):
+    names = ["tiny", "llama32_3b_32k", "llama3_8b_128k", "qwen25_14b_128k_b4"]
+    if args.cpu_configs != "all":
+        names = [n for n in args.cpu_configs.split(",") if n]
+    for name in names:
         wl = synth.workload(name)
         seed = synth.default_seed(wl)
         L = wl.n_layers
-        layers = [0] if L == 1 else sorted({0, L // 2, L - 1})[:n_layers_timed]
+        layers = [L // 2]   # one layer's oracle cache keeps the untimed setup to minutes
         t0 = time.time()
         s, spike = synth.surprisal(wl, seed)
         w, p = synth.route_weights(wl, seed)
