@@ -20,17 +20,18 @@ __all__ = [
     "make_config", "Cache", "RouteBuffers", "sekv_segment", "sekv_build_spans", "sekv_route",
     "sekv_decode_attn", "sekv_route_attn", "sekv_decode_attn_batch", "sekv_route_attn_batch",
     "sekv_cap_budget", "sekv_cap_budget_layer", "sekv_decode_workspace_bytes",
-    "sekv_append_tokens",
+    "sekv_append_tokens", "sekv_test_fail_fetch",
     "EXPORTED_SYMBOLS",
     "sekv_set_residency", "sekv_residency_stats", "sekv_apply_gates", "SEKV_MAX_BATCH",
     "SEKV_F32", "SEKV_BF16", "SEKV_TIER_DEVICE", "SEKV_TIER_HOST_PINNED",
     "SEKV_SVD_EXACT", "SEKV_SVD_RANDOMIZED", "sekv_route_attn_noalloc",
-    "SEKV_NOALLOC_SCRATCH_BYTES",
+    "SEKV_NOALLOC_SCRATCH_BYTES", "SEKV_FETCH_GATHER", "SEKV_FETCH_MEMCPY",
 ]
 
 SEKV_OK, SEKV_ERR_INVALID, SEKV_ERR_NOMEM, SEKV_ERR_HIP, SEKV_ERR_UNSUPPORTED = range(5)
 SEKV_F32, SEKV_BF16 = 0, 1
 SEKV_TIER_DEVICE, SEKV_TIER_HOST_PINNED = 0, 1
+SEKV_FETCH_GATHER, SEKV_FETCH_MEMCPY = 0, 1
 SEKV_SVD_EXACT, SEKV_SVD_RANDOMIZED = 0, 1
 SEKV_MAX_BATCH = 8
 SEKV_NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024
@@ -42,6 +43,7 @@ EXPORTED_SYMBOLS = (
     "sekv_decode_attn_batch", "sekv_route_attn_batch", "sekv_cap_budget", "sekv_set_residency",
     "sekv_residency_stats", "sekv_apply_gates", "sekv_cache_destroy", "sekv_last_error",
     "sekv_route_attn_noalloc", "sekv_cap_budget_layer", "sekv_append_tokens",
+    "sekv_test_fail_fetch", "sekv_set_fetch_mode",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -133,6 +135,8 @@ def lib() -> ctypes.CDLL:
         "sekv_set_residency": (I32, [P, U64, U64]),
         "sekv_apply_gates": (I32, [P, P, P, ctypes.c_float, P]),
         "sekv_residency_stats": (I32, [P, ctypes.POINTER(U64), I32]),
+        "sekv_test_fail_fetch": (I32, [I32]),
+        "sekv_set_fetch_mode": (I32, [P, I32]),
         "sekv_cache_destroy": (None, [P]),
         "sekv_last_error": (ctypes.c_char_p, []),
     }
@@ -287,6 +291,14 @@ class Cache:
         host-tier cache's factor blocks."""
         _check(lib().sekv_set_residency(self.handle, int(capacity_bytes), int(slot_bytes)))
 
+    def set_fetch_mode(self, mode: str) -> None:
+        """Host tier: "gather" (one kernel, default) or "memcpy" (hipMemcpyAsync
+        per run of union spans) for the factor fetch."""
+        modes = {"gather": SEKV_FETCH_GATHER, "memcpy": SEKV_FETCH_MEMCPY}
+        if mode not in modes:
+            raise ValueError(f"fetch mode must be one of {sorted(modes)}")
+        _check(lib().sekv_set_fetch_mode(self.handle, modes[mode]))
+
     def residency_stats(self, reset: bool = False) -> dict:
         out = (ctypes.c_uint64 * 6)()
         _check(lib().sekv_residency_stats(self.handle, out, 1 if reset else 0))
@@ -318,6 +330,11 @@ def sekv_build_spans(cfg: SekvConfig, surprisal: torch.Tensor, k: torch.Tensor, 
                                   _ptr(w_route), _ptr(rank_by_pos), _stream(stream),
                                   ctypes.byref(h)))
     return Cache(h, cfg)
+
+
+def sekv_test_fail_fetch(n: int) -> None:
+    """Test hook: the next ``n`` host-tier factor fetches fail (SekvError)."""
+    _check(lib().sekv_test_fail_fetch(int(n)))
 
 
 def sekv_append_tokens(cache: Cache, surprisal: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

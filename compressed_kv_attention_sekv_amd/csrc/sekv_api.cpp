@@ -7,9 +7,12 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <memory>
 #include <mutex>
@@ -24,6 +27,26 @@ namespace {
 
 thread_local std::string g_err;
 
+// SEKV_LOG=1 in the environment: one line per build, append, error and
+// configuration change on stderr (read once, at the first message)
+bool log_on() {
+  static const bool on = [] {
+    const char* v = std::getenv("SEKV_LOG");
+    return v && *v && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+void slog(const char* fmt, ...) {
+  if (!log_on()) return;
+  char buf[640];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "[sekv] %s\n", buf);
+}
+
 sekv_status fail(sekv_status st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -31,7 +54,15 @@ sekv_status fail(sekv_status st, const char* fmt, ...) {
   vsnprintf(buf, sizeof(buf), fmt, ap);
   va_end(ap);
   g_err = buf;
+  slog("error %d: %s", (int)st, buf);
   return st;
+}
+
+// sekv_test_fail_fetch: host-tier factor fetches still to fail on purpose
+std::atomic<int> g_fail_fetch{0};
+
+double ms_since(std::chrono::steady_clock::time_point t0) {
+  return std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
 }
 
 #define SEKV_HIP(expr)                                                                        \
@@ -162,6 +193,9 @@ struct sekv_cache {
   uint64_t factor_bytes = 0, pool_floats = 0;
   float* pool_dev = nullptr;      // device tier
   float* pool_host = nullptr;     // host tier (pinned, mapped)
+  int fetch_mode = SEKV_FETCH_GATHER;  // host tier: how the union blocks reach staging
+  std::vector<int32_t> h_ulist;   // memcpy fetch: the route's union lists, on the host
+  std::vector<int32_t> h_ucount;
   float* pool_host_dev = nullptr; // device view of pool_host
   float* stage = nullptr;         // host tier: device staging for one layer
   uint64_t stage_floats = 0;
@@ -456,12 +490,18 @@ sekv_status sekv_build_spans(const sekv_config* cfg, int32_t n_tokens, const flo
   if (!surprisal_dev || !k_dev || !v_dev || !w_route_dev)
     return fail(SEKV_ERR_INVALID, "surprisal, keys, values and w_route must be non-NULL");
   std::unique_ptr<sekv_cache> c;
+  const auto t0 = std::chrono::steady_clock::now();
   r = build_impl(cfg, n_tokens, surprisal_dev, k_dev, v_dev, w_route_dev, rank_by_pos_dev, stream,
                  c);
   if (r) {
     (void)hipStreamSynchronize(stream);  // nothing queued may outlive the freed buffers
     return r;
   }
+  slog("build: %d tokens, %d layers x %d KV heads: %d anchors, %d spans (%d compressed), %d "
+       "full-resolution rows; factor pool %.3f GB (%s tier, %s SVD), %.1f ms",
+       n_tokens, cfg->n_layers, cfg->n_kv_heads, c->n_anchors, c->n_spans, c->sc, c->n_dense,
+       (double)c->pool_floats * 4e-9, cfg->factor_tier == SEKV_TIER_DEVICE ? "device" : "host",
+       cfg->svd_mode == SEKV_SVD_EXACT ? "exact" : "randomized", ms_since(t0));
   *out = c.release();
   return SEKV_OK;
 }
@@ -673,6 +713,29 @@ static sekv_status append_impl(sekv_cache* c, int n_new, const float* s_new, con
   c->n_tokens = N;
   c->n_appended += n_new;
   c->geom = make_layer_geom(Hq, Hkv, dr, D, c->sc, ds, scs);
+  slog("append: %d tokens (%d of %d appended), %d retired: %d anchors and %d spans (%d "
+       "compressed) closed, open run %d; %d full-resolution rows", n_new, c->n_appended,
+       cfg.append_capacity, r_new - r_old, (int)new_anchors.size(), (int)closed.size(), nc,
+       c->open_len, D);
+  return SEKV_OK;
+}
+
+sekv_status sekv_set_fetch_mode(sekv_cache* c, int32_t mode) {
+  if (!c) return fail(SEKV_ERR_INVALID, "cache is NULL");
+  if (mode != SEKV_FETCH_GATHER && mode != SEKV_FETCH_MEMCPY)
+    return fail(SEKV_ERR_INVALID, "fetch mode must be SEKV_FETCH_GATHER or SEKV_FETCH_MEMCPY");
+  if (c->cfg.factor_tier != SEKV_TIER_HOST_PINNED)
+    return fail(SEKV_ERR_INVALID, "the fetch mode is a host-tier setting; this cache keeps its "
+                "factors in HBM");
+  c->fetch_mode = mode;
+  slog("fetch mode: %s", mode == SEKV_FETCH_GATHER ? "gather kernel" : "hipMemcpyAsync per run");
+  return SEKV_OK;
+}
+
+sekv_status sekv_test_fail_fetch(int32_t n) {
+  if (n < 0) return fail(SEKV_ERR_INVALID, "n must be >= 0 (got %d)", n);
+  g_fail_fetch.store(n);
+  slog("test hook: the next %d host-tier factor fetches fail", n);
   return SEKV_OK;
 }
 
@@ -889,6 +952,10 @@ static sekv_status attn_impl(const sekv_cache* c, int32_t layer, const float* q_
   // host tier: the zoomed spans' factors are gathered into device staging on
   // the fetch stream while full-resolution rows and coarse entries are
   // attended on `stream`; the zoomed spans and the merge follow the fetch
+  for (int n = g_fail_fetch.load(); n > 0;)
+    if (g_fail_fetch.compare_exchange_weak(n, n - 1))
+      return fail(SEKV_ERR_HIP, "factor fetch of layer %d failed (injected by sekv_test_fail_fetch)",
+                  layer);
   const size_t lg0 = (size_t)layer * c->cfg.n_kv_heads;
   hipStream_t fst = fetch_stream ? fetch_stream : stream;
   if (fst != stream) {
@@ -912,6 +979,38 @@ static sekv_status attn_impl(const sekv_cache* c, int32_t layer, const float* q_
     az.pool = c->res.arena;
     az.fac_off = c->res.off;
     az.off_base = 0;
+  } else if (c->fetch_mode == SEKV_FETCH_MEMCPY) {
+    // one hipMemcpyAsync per run of consecutive union spans (their blocks
+    // are adjacent in the pool); the union lists must reach the host first,
+    // so the host waits for the route
+    sekv_cache* cm = const_cast<sekv_cache*>(c);
+    const int Hkv = c->cfg.n_kv_heads, sc = c->sc;
+    cm->h_ucount.resize(Hkv);
+    cm->h_ulist.resize((size_t)Hkv * sc);
+    SEKV_HIP(hipMemcpyAsync(cm->h_ucount.data(), route->union_count, (size_t)Hkv * 4,
+                            hipMemcpyDeviceToHost, fst));
+    SEKV_HIP(hipMemcpyAsync(cm->h_ulist.data(), route->union_list, (size_t)Hkv * sc * 4,
+                            hipMemcpyDeviceToHost, fst));
+    SEKV_HIP(hipStreamSynchronize(fst));
+    const uint64_t base = c->layer_base[layer];
+    for (int g = 0; g < Hkv; ++g) {
+      const int n = std::min(std::max(cm->h_ucount[g], 0), sc);
+      const size_t row = (lg0 + g) * (size_t)c->scs;
+      for (int k = 0; k < n;) {
+        const int j0 = cm->h_ulist[(size_t)g * sc + k];
+        if (j0 < 0 || j0 >= sc) return fail(SEKV_ERR_INVALID, "union list entry %d out of range", j0);
+        int j1 = j0 + 1;   // the run j0 .. j1 - 1
+        while (k + (j1 - j0) < n && cm->h_ulist[(size_t)g * sc + k + (j1 - j0)] == j1 && j1 < sc)
+          ++j1;
+        const uint64_t o0 = c->h_fac_off[row + j0];
+        const uint64_t o1 = o0 + (uint64_t)FactorView::packed(c->h_rank[row + j1 - 1],
+                                                               c->h_clen[j1 - 1]).block_floats() +
+                            (c->h_fac_off[row + j1 - 1] - o0);
+        SEKV_HIP(hipMemcpyAsync(c->stage + (o0 - base), c->pool_host + o0, (size_t)(o1 - o0) * 4,
+                                hipMemcpyHostToDevice, fst));
+        k += j1 - j0;
+      }
+    }
   } else {
     SEKV_HIP(launch_fetch_gather(c->geom, route->union_list, route->union_count, c->clen,
                                  c->rank + lg0 * c->scs, c->fac_off + lg0 * c->scs,

@@ -64,6 +64,10 @@ typedef enum { SEKV_SVD_EXACT = 0, SEKV_SVD_RANDOMIZED = 1 } sekv_svd_mode;
  * fetched asynchronously for selected spans) */
 typedef enum { SEKV_TIER_DEVICE = 0, SEKV_TIER_HOST_PINNED = 1 } sekv_tier;
 
+/* how a host-tier decode call moves the zoomed spans' factor blocks to HBM
+ * staging (see sekv_set_fetch_mode) */
+typedef enum { SEKV_FETCH_GATHER = 0, SEKV_FETCH_MEMCPY = 1 } sekv_fetch_mode;
+
 typedef struct {
   int32_t n_layers;
   int32_t n_q_heads;
@@ -392,6 +396,26 @@ sekv_status sekv_decode_attn_batch(const sekv_cache* const* caches, int32_t batc
                                    const float* const* q_devs, const sekv_route_out* routes,
                                    float* const* o_devs, void* const* ws_devs,
                                    const size_t* ws_bytes, hipStream_t stream);
+
+/* Fetch of a host-tier cache's factor blocks (SeKV paper Sec. 3.2: bases on
+ * the CPU, fetched for the selected spans; the summary page asks that the
+ * fetch be asynchronous).  SEKV_FETCH_GATHER (default): one kernel on the
+ * fetch stream reads the union spans' blocks from mapped pinned memory, driven
+ * by the route's union lists on the device, so the host never waits.
+ * SEKV_FETCH_MEMCPY: the union lists are copied to the host (the call waits
+ * for the route), then one hipMemcpyAsync per run of consecutive union spans
+ * moves their blocks on the fetch stream.  Outputs are the same bit for bit.
+ * Applies to later calls; a residency cache (sekv_set_residency) takes
+ * precedence.  Errors: SEKV_ERR_INVALID for a NULL or device-tier cache or an
+ * unknown mode. */
+sekv_status sekv_set_fetch_mode(sekv_cache* cache, int32_t mode);
+
+/* Test hook for the failure path of the host-tier factor fetch (the link the
+ * SeKV paper Sec. 3.2 fetches factors over): the next n host-tier fetches
+ * (sekv_decode_attn, or the attention half of sekv_route_attn) fail with
+ * SEKV_ERR_HIP before anything of theirs is queued, and the cache stays
+ * usable.  n = 0 cancels.  Process-wide; SEKV_ERR_INVALID for n < 0. */
+sekv_status sekv_test_fail_fetch(int32_t n);
 
 void sekv_cache_destroy(sekv_cache* cache);
 

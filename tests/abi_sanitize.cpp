@@ -95,6 +95,7 @@ int main() {
   CHECK(sekv_cap_budget(nullptr, &ro, 0, nullptr) == SEKV_ERR_INVALID);
   CHECK(sekv_cap_budget_layer(nullptr, &ro, 0, nullptr) == SEKV_ERR_INVALID);
   CHECK(sekv_set_residency(nullptr, 1 << 20, 1 << 16) == SEKV_ERR_INVALID);
+  CHECK(sekv_set_fetch_mode(nullptr, SEKV_FETCH_MEMCPY) == SEKV_ERR_INVALID);
   CHECK(sekv_apply_gates(nullptr, F, F, 0.5f, nullptr) == SEKV_ERR_INVALID);
   CHECK(sekv_append_tokens(nullptr, 1, F, P, P, F, nullptr, nullptr) == SEKV_ERR_INVALID);
   uint64_t stats[6];
@@ -133,6 +134,11 @@ int main() {
         SEKV_ERR_INVALID);
   CHECK(sekv_decode_attn_batch(caches, 2, 0, qs, ros, os, wss, sizes, nullptr) ==
         SEKV_ERR_INVALID);
+
+  // the fetch-failure test hook: arguments only (nothing fetches here)
+  CHECK(sekv_test_fail_fetch(-1) == SEKV_ERR_INVALID);
+  CHECK(sekv_test_fail_fetch(2) == SEKV_OK);
+  CHECK(sekv_test_fail_fetch(0) == SEKV_OK);
 
   // a long message is truncated, never overrun
   CHECK(std::strlen(sekv_last_error()) < 4096);

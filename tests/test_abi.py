@@ -95,6 +95,7 @@ def test_calls_on_null_cache_are_rejected(L):
     assert L.sekv_cap_budget(None, ctypes.byref(ro), 0, None) == S.SEKV_ERR_INVALID
     assert L.sekv_cap_budget_layer(None, ctypes.byref(ro), 0, None) == S.SEKV_ERR_INVALID
     assert L.sekv_set_residency(None, 1 << 20, 1 << 16) == S.SEKV_ERR_INVALID
+    assert L.sekv_set_fetch_mode(None, S.SEKV_FETCH_MEMCPY) == S.SEKV_ERR_INVALID
     assert L.sekv_apply_gates(None, ctypes.c_void_p(8), ctypes.c_void_p(8), 0.5,
                               None) == S.SEKV_ERR_INVALID
     out6 = (ctypes.c_uint64 * 6)()
@@ -103,6 +104,12 @@ def test_calls_on_null_cache_are_rejected(L):
     info = S.SekvCacheInfo()
     assert L.sekv_cache_info_get(None, ctypes.byref(info)) == S.SEKV_ERR_INVALID
     L.sekv_cache_destroy(None)  # no-op
+
+
+def test_fetch_failure_hook_arguments(L):
+    assert L.sekv_test_fail_fetch(-1) == S.SEKV_ERR_INVALID
+    assert b"n must be" in L.sekv_last_error()
+    assert L.sekv_test_fail_fetch(0) == S.SEKV_OK
 
 
 def test_batch_calls_reject_bad_arguments(L):

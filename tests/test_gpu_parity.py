@@ -346,6 +346,82 @@ def test_host_tier_matches_oracle_and_device_tier(S):
             assert err <= 1e-6
 
 
+def test_host_tier_fetch_failure_leaves_cache_usable(S):
+    """A failing host-tier fetch (forced by the library's test hook) makes the
+    call fail with the HIP status before anything of its attention is queued;
+    the next calls on the same cache give the outputs of a call that never
+    failed, bit for bit."""
+    wl = synth.workload("llama3_8b_128k", n_layers=1, n_tokens=6000)
+    log("[parity] host tier fetch failure")
+    inp = Inputs(wl, 5)
+    host = S.sekv_build_spans(make_cfg(S, wl, tier="host"), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    tau = torch.full((wl.n_q_heads,), 0.6, device="cuda")
+    q = inp.query(0)[0]
+    p = inp.p[0].contiguous()
+    ws = torch.empty(host.workspace_bytes(), dtype=torch.uint8, device="cuda")
+
+    def call(fused):
+        rb = S.RouteBuffers.allocate(host)
+        o = torch.zeros(wl.n_q_heads, wl.head_dim, device="cuda")
+        if fused:
+            S.sekv_route_attn(host, 0, q, p, tau, rb, o, ws)
+        else:
+            S.sekv_route(host, 0, q, p, tau, rb)
+            S.sekv_decode_attn(host, 0, q, rb, o, ws)
+        torch.cuda.synchronize()
+        return rb, o
+
+    rb0, o0 = call(True)
+    assert int(rb0.union_count.sum()) > 0
+    for fused in (True, False):
+        S.sekv_test_fail_fetch(1)
+        with pytest.raises(S.SekvError, match="injected"):
+            call(fused)
+        rb, o = call(fused)
+        assert torch.equal(rb.mask, rb0.mask) and torch.equal(o, o0)
+    S.sekv_test_fail_fetch(0)
+
+
+def test_host_tier_memcpy_fetch_equals_gather(S):
+    """The hipMemcpyAsync-per-run fetch moves the same blocks as the gather
+    kernel: routes and outputs bit-identical, with and without a fetch stream,
+    over both call paths; device-tier caches refuse the setting."""
+    wl = synth.workload("llama3_8b_128k", n_layers=2, n_tokens=7000)
+    log("[parity] host tier memcpy fetch")
+    inp = Inputs(wl, 6)
+    host = S.sekv_build_spans(make_cfg(S, wl, tier="host"), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    tau = torch.full((wl.n_q_heads,), 0.65, device="cuda")
+    side = torch.cuda.Stream()
+    ws = torch.empty(host.workspace_bytes(), dtype=torch.uint8, device="cuda")
+
+    def call(layer, fused, fst):
+        q = inp.query(2)[layer]
+        p = inp.p[layer].contiguous()
+        rb = S.RouteBuffers.allocate(host)
+        o = torch.zeros(wl.n_q_heads, wl.head_dim, device="cuda")
+        if fused:
+            S.sekv_route_attn(host, layer, q, p, tau, rb, o, ws, fetch_stream=fst)
+        else:
+            S.sekv_route(host, layer, q, p, tau, rb)
+            S.sekv_decode_attn(host, layer, q, rb, o, ws, fetch_stream=fst)
+        torch.cuda.synchronize()
+        return rb, o
+
+    for layer in range(2):
+        for fused, fst in ((True, side), (False, None)):
+            host.set_fetch_mode("gather")
+            rb0, o0 = call(layer, fused, fst)
+            host.set_fetch_mode("memcpy")
+            rb1, o1 = call(layer, fused, fst)
+            assert int(rb0.union_count.sum()) > 0
+            assert torch.equal(rb0.union_list, rb1.union_list)
+            assert torch.equal(o0, o1)
+    host.set_fetch_mode("gather")
+    dev = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    with pytest.raises(S.SekvError, match="host-tier"):
+        dev.set_fetch_mode("memcpy")
+
+
 def test_many_chunks_merge_parity(S):
     """Thousands of short spans, so a KV head has more than 128 chunks and the
     tail's merge runs more than one round of slot loads per thread (three with
