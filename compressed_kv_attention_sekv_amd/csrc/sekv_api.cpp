@@ -943,10 +943,16 @@ static sekv_status attn_impl(const sekv_cache* c, int32_t layer, const float* q_
                              hipStream_t stream, hipStream_t fetch_stream) {
   const LayerArgs a = layer_args(c, layer, q_dev, nullptr, nullptr, route, o_dev, ws_dev);
   const int sc = c->sc;
-  if (c->cfg.factor_tier == SEKV_TIER_DEVICE || sc == 0) {
+  if (sc == 0) {
     SEKV_HIP(launch_layer(c->bf16(), kDense, c->geom, a, stream));
-    SEKV_HIP(launch_zoom(c->geom, a, stream));
-    SEKV_HIP(launch_layer_tail(kMerge | (sc ? kZoomSplit : 0), c->geom, a, stream));
+    SEKV_HIP(launch_layer_tail(kMerge, c->geom, a, stream));
+    return SEKV_OK;
+  }
+  if (c->cfg.factor_tier == SEKV_TIER_DEVICE) {
+    // the chunk masks from the given mask, then as sekv_route_attn after its route
+    SEKV_HIP(launch_layer(c->bf16(), kMaskBits, c->geom, a, stream));
+    SEKV_HIP(launch_attend(c->bf16(), kDense, c->geom, a, stream));
+    SEKV_HIP(launch_layer_tail(kMerge | kZoomSplit, c->geom, a, stream));
     return SEKV_OK;
   }
   // host tier: the zoomed spans' factors are gathered into device staging on
@@ -1060,9 +1066,11 @@ sekv_status sekv_route_attn(const sekv_cache* c, int32_t layer, const float* q_d
     if ((r = sekv_route(c, layer, q_dev, proj_dev, tau_dev, route, stream))) return r;
     return attn_impl(c, layer, q_dev, route, o_dev, ws_dev, stream, fetch_stream);
   }
+  // route; then rows, coarse entries and zoomed spans side by side; then the
+  // merge and lists
   const LayerArgs a = layer_args(c, layer, q_dev, proj_dev, tau_dev, route, o_dev, ws_dev);
-  SEKV_HIP(launch_layer(c->bf16(), kRoute | kDense, c->geom, a, stream));
-  SEKV_HIP(launch_zoom(c->geom, a, stream));
+  SEKV_HIP(launch_layer(c->bf16(), kRoute, c->geom, a, stream));
+  SEKV_HIP(launch_attend(c->bf16(), kDense, c->geom, a, stream));
   SEKV_HIP(launch_layer_tail(kMerge | kLists | kZoomSplit, c->geom, a, stream));
   return SEKV_OK;
 }
@@ -1377,11 +1385,14 @@ static sekv_status batch_impl(const sekv_cache* const* caches, int32_t batch, in
     ++nb;
   }
   if (nb > 0) {
-    const int mode = with_route ? (kRoute | kDense) : kDense;
+    // as the single calls: route (or the chunk masks of the given routes), then
+    // zoomed spans beside rows and coarse entries, then merge (and lists)
+    const int first = with_route ? kRoute : kMaskBits;
     const int tail = (with_route ? (kMerge | kLists) : kMerge) | kZoomSplit;
-    SEKV_HIP(launch_layer_batch(caches[0]->bf16(), mode, caches[0]->geom.group, b, nb, stream));
-    SEKV_HIP(launch_zoom_batch(caches[0]->geom.group, b, nb, stream));
-    SEKV_HIP(launch_layer_tail_batch(tail, caches[0]->geom.group, b, nb, stream));
+    const int grp = caches[0]->geom.group;
+    SEKV_HIP(launch_layer_batch(caches[0]->bf16(), first, grp, b, nb, stream));
+    SEKV_HIP(launch_attend_batch(caches[0]->bf16(), kDense, grp, b, nb, stream));
+    SEKV_HIP(launch_layer_tail_batch(tail, grp, b, nb, stream));
   }
   return SEKV_OK;
 }

@@ -1111,9 +1111,7 @@ __device__ __attribute__((always_inline)) void tail_merge(const LayerGeom& geo, 
 // ---------------------------------------------------------------------------
 template <int G>
 __device__ __attribute__((always_inline)) void zoom_body(const LayerGeom& geo, const LayerArgs& a,
-                                                         int z) {
-  __shared__ ZSmem<G> s;
-  __shared__ Stage<G> stg;
+                                                         int z, ZSmem<G>& s, Stage<G>& stg) {
   constexpr int SR = stage_rows<G>();
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   float* const stage = stg.v[uniform(wid)];
@@ -1325,11 +1323,10 @@ __device__ __attribute__((always_inline)) void layer_tail(const LayerGeom& geo, 
 template <typename T, int G>
 __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
                                                           const LayerArgs& a, int mode,
-                                                          int block) {
+                                                          int block, Smem<G>& s) {
   using Ln = Lanes<T>;
   constexpr int CLOADS = (kChunk / kWaves) / Ln::RPW;     // coarse entries: loads per wave
   constexpr int DLOADS = kRowBlock / Ln::RPW;             // full-resolution rows: loads per pass
-  __shared__ Smem<G> s;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int W = geo.n_work;
@@ -1466,7 +1463,7 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
       if (a.prob) a.prob[(size_t)h * sc + j] = p;
       if (z) atomicOr(&s.bits[jl], 1 << hl);
     }
-  } else if (dense && nj > 0) {
+  } else if ((dense || (mode & kMaskBits)) && nj > 0) {
     for (int idx = tid; idx < nj * G; idx += kThreads) {
       const int jl = idx / G, hl = idx % G;
       if (a.mask[(size_t)(h0 + hl) * sc + j0 + jl]) atomicOr(&s.bits[jl], 1 << hl);
@@ -1476,7 +1473,7 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
 
   // ---- zoom sets of the chunk: one wave ballot per list (per head, then the
   // union), read by the zoom kernel and by the tail's lists -----------------
-  if (wid == 0 && nj > 0) {
+  if (wid == 0 && nj > 0 && !(mode & kKeepBits)) {
     const int b = lane < nj ? s.bits[lane] : 0;
 #pragma unroll
     for (int li = 0; li <= G; ++li) {
@@ -1536,7 +1533,8 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
 template <typename T, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void layer_kernel(LayerGeom geo, LayerArgs a, int mode) {
-  layer_body<T, G>(geo, a, mode, blockIdx.x);
+  __shared__ Smem<G> s;
+  layer_body<T, G>(geo, a, mode, blockIdx.x, s);
 }
 
 // A batch of sequences, one cache each: blockIdx.y is the sequence; each runs
@@ -1546,7 +1544,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void layer_batch_kernel(BatchLayerArgs b, int mode) {
   const int i = blockIdx.y;
   if ((int)blockIdx.x >= b.geo[i].n_kv_heads * b.geo[i].n_work) return;
-  layer_body<T, G>(b.geo[i], b.arg[i], mode, blockIdx.x);
+  __shared__ Smem<G> s;
+  layer_body<T, G>(b.geo[i], b.arg[i], mode, blockIdx.x, s);
 }
 
 // The merge and lists of one layer in a launch of their own: one workgroup
@@ -1570,20 +1569,63 @@ __global__ __launch_bounds__(kThreads) void layer_tail_batch_kernel(BatchLayerAr
   layer_tail<G>(b.geo[i], b.arg[i], mode, blockIdx.x, wc, mg);
 }
 
-// The zoomed spans of one layer (geo.z_total workgroups; grid.y: the sequence
-// of a batch, the extra workgroups of a shorter grid return at once).
+// The zoomed spans of one layer on their own (geo.z_total workgroups): the
+// host tier's, after its rows launch and the factor fetch.
 template <int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void zoom_kernel(LayerGeom geo, LayerArgs a) {
-  zoom_body<G>(geo, a, blockIdx.x);
+  __shared__ ZSmem<G> s;
+  __shared__ Stage<G> stg;
+  zoom_body<G>(geo, a, blockIdx.x, s, stg);
 }
 
+// The full-resolution rows, coarse entries and zoomed spans of a layer whose
+// route is already out (chunk masks written by a route-only layer launch):
+// the first geo.z_total workgroups (launch_attend passes z_attend there)
+// attend the zoomed spans, the next Hkv x n_work rows and coarse entries (the
+// chunk masks stay as the route wrote them).  Neither kind waits for the
+// other, so the zoomed spans are attended while the rows are, not after them;
+// the zoom workgroups, the longer ones, are dispatched first.
 template <int G>
+struct ZoomLds {
+  ZSmem<G> z;
+  Stage<G> st;
+};
+template <int G>
+union AttendLds {
+  Smem<G> l;
+  ZoomLds<G> zz;
+};
+template <typename T, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void zoom_batch_kernel(BatchLayerArgs b) {
+void attend_kernel(LayerGeom geo, LayerArgs a, int mode) {
+  __shared__ AttendLds<G> u;
+  const int nz = geo.n_compressed ? geo.z_total : 0;
+  if ((int)blockIdx.x < nz)
+    zoom_body<G>(geo, a, blockIdx.x, u.zz.z, u.zz.st);
+  else
+    layer_body<T, G>(geo, a, mode | kKeepBits, (int)blockIdx.x - nz, u.l);
+}
+static_assert(sizeof(AttendLds<4>) <= 80 * 1024 && sizeof(AttendLds<5>) <= 80 * 1024,
+              "two attend workgroups per CU");
+
+// A batch of sequences (grid.y), each with its own z_attend zoom workgroups
+// and Hkv x n_work row workgroups; the rest of grid.x returns at once.
+template <typename T, int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attend_batch_kernel(BatchLayerArgs b, int mode) {
+  __shared__ AttendLds<G> u;
   const int i = blockIdx.y;
-  if ((int)blockIdx.x >= b.geo[i].z_total) return;
-  zoom_body<G>(b.geo[i], b.arg[i], blockIdx.x);
+  LayerGeom geo = b.geo[i];
+  const int nz = geo.n_compressed ? geo.z_attend : 0;
+  const int nr = geo.n_kv_heads * geo.n_work;
+  const int x = blockIdx.x;
+  if (x >= nz + nr) return;
+  geo.z_total = geo.z_attend;
+  if (x < nz)
+    zoom_body<G>(geo, b.arg[i], x, u.zz.z, u.zz.st);
+  else
+    layer_body<T, G>(geo, b.arg[i], mode | kKeepBits, x - nz, u.l);
 }
 
 hipError_t launch_zoom(const LayerGeom& g, const LayerArgs& a, hipStream_t st) {
@@ -1594,25 +1636,6 @@ hipError_t launch_zoom(const LayerGeom& g, const LayerArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((zoom_kernel<GG>), grid, dim3(kThreads), 0, st, g, a);               \
     break;
   switch (g.group) {
-    SEKV_ZOOM(1) SEKV_ZOOM(2) SEKV_ZOOM(3) SEKV_ZOOM(4) SEKV_ZOOM(5) SEKV_ZOOM(6) SEKV_ZOOM(7)
-    SEKV_ZOOM(8)
-    default: return hipErrorInvalidValue;
-  }
-#undef SEKV_ZOOM
-  return hipGetLastError();
-}
-
-hipError_t launch_zoom_batch(int group, const BatchLayerArgs& b, int batch, hipStream_t st) {
-  if (batch < 1 || batch > kMaxBatch) return hipErrorInvalidValue;
-  int nx = 0;
-  for (int i = 0; i < batch; ++i) nx = max(nx, b.geo[i].n_compressed ? b.geo[i].z_total : 0);
-  if (nx == 0) return hipSuccess;
-  const dim3 grid(nx, batch);
-#define SEKV_ZOOM(GG)                                                                       \
-  case GG:                                                                                  \
-    hipLaunchKernelGGL((zoom_batch_kernel<GG>), grid, dim3(kThreads), 0, st, b);            \
-    break;
-  switch (group) {
     SEKV_ZOOM(1) SEKV_ZOOM(2) SEKV_ZOOM(3) SEKV_ZOOM(4) SEKV_ZOOM(5) SEKV_ZOOM(6) SEKV_ZOOM(7)
     SEKV_ZOOM(8)
     default: return hipErrorInvalidValue;
@@ -1676,6 +1699,56 @@ hipError_t launch_layer_batch(int bf16, int mode, int group, const BatchLayerArg
     default: return hipErrorInvalidValue;
   }
 #undef SEKV_LAYER
+  return hipGetLastError();
+}
+
+hipError_t launch_attend(int bf16, int mode, const LayerGeom& g, const LayerArgs& a,
+                         hipStream_t st) {
+  if (mode != kDense) return hipErrorInvalidValue;
+  LayerGeom ga = g;   // the zoom shares over z_attend workgroups (their count is
+  ga.z_total = g.z_attend;   // recorded for the merge, within the z_total slots)
+  const dim3 grid(ga.n_work * ga.n_kv_heads + (ga.n_compressed ? ga.z_total : 0));
+#define SEKV_ATTEND(GG)                                                                      \
+  case GG:                                                                                   \
+    if (bf16)                                                                                \
+      hipLaunchKernelGGL((attend_kernel<uint16_t, GG>), grid, dim3(kThreads), 0, st, ga, a,  \
+                         mode);                                                              \
+    else                                                                                     \
+      hipLaunchKernelGGL((attend_kernel<float, GG>), grid, dim3(kThreads), 0, st, ga, a,     \
+                         mode);                                                              \
+    break;
+  switch (g.group) {
+    SEKV_ATTEND(1) SEKV_ATTEND(2) SEKV_ATTEND(3) SEKV_ATTEND(4) SEKV_ATTEND(5) SEKV_ATTEND(6)
+    SEKV_ATTEND(7) SEKV_ATTEND(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef SEKV_ATTEND
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_batch(int bf16, int mode, int group, const BatchLayerArgs& b, int batch,
+                               hipStream_t st) {
+  if (mode != kDense || batch < 1 || batch > kMaxBatch) return hipErrorInvalidValue;
+  int nx = 0;
+  for (int i = 0; i < batch; ++i)
+    nx = max(nx, b.geo[i].n_kv_heads * b.geo[i].n_work +
+                     (b.geo[i].n_compressed ? b.geo[i].z_attend : 0));
+  const dim3 grid(nx, batch);
+#define SEKV_ATTEND(GG)                                                                      \
+  case GG:                                                                                   \
+    if (bf16)                                                                                \
+      hipLaunchKernelGGL((attend_batch_kernel<uint16_t, GG>), grid, dim3(kThreads), 0, st, b, \
+                         mode);                                                              \
+    else                                                                                     \
+      hipLaunchKernelGGL((attend_batch_kernel<float, GG>), grid, dim3(kThreads), 0, st, b,   \
+                         mode);                                                              \
+    break;
+  switch (group) {
+    SEKV_ATTEND(1) SEKV_ATTEND(2) SEKV_ATTEND(3) SEKV_ATTEND(4) SEKV_ATTEND(5) SEKV_ATTEND(6)
+    SEKV_ATTEND(7) SEKV_ATTEND(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef SEKV_ATTEND
   return hipGetLastError();
 }
 

@@ -147,6 +147,8 @@ constexpr int kListWords = kMaxGroup + 1; // zoom bit masks per chunk: heads, th
 constexpr int kZeroBlockFloats = 32 * kHeadDim;
 constexpr int kMaxKvHeads = 256;          // KV heads of a layer, at most
 constexpr int kZoomWgMax = 512;           // zoom workgroups filling the GPU (two per CU)
+constexpr int kAttendZoomWgs = 256;       // zoom workgroups beside the rows: one per CU of
+                                          // MI355X (two ~80 KB workgroups fit a CU)
 constexpr int kZoomBatchMax = 64;         // zoomed spans of one zoom workgroup, at most
 
 struct LayerGeom {
@@ -158,7 +160,10 @@ struct LayerGeom {
   int n_work;        // workgroups per KV head: max(1, n_chunks, ceil(D / kMaxDenseRows))
   int dense_rows;    // full-resolution rows per workgroup, a multiple of kWaves * kRowBlock
   int z_total;       // zoom workgroups (see make_layer_geom)
-  __host__ __device__ int n_slots() const { return n_work + z_total; }
+  int z_attend;      // zoom workgroups of launch_attend (<= z_total)
+  int z_slots;       // zoom partial slots per KV head: z_total as built (launch_attend
+                     // deals the spans to fewer workgroups, into the same slots)
+  __host__ __device__ int n_slots() const { return n_work + z_slots; }
 };
 
 __host__ inline LayerGeom make_layer_geom(int hq, int hkv, int dr, int n_dense, int sc,
@@ -188,6 +193,15 @@ __host__ inline LayerGeom make_layer_geom(int hq, int hkv, int dr, int n_dense, 
   const long long need = ((long long)hkv * sc + kZoomBatchMax - 1) / kZoomBatchMax + hkv;
   if (z < need) z = (int)need;
   g.z_total = z;
+  g.z_slots = z;
+  // beside the rows in one launch (launch_attend): one zoom workgroup per CU,
+  // the other slot of each CU taking row workgroups (measured at 128K: 188,
+  // 256, 320 and 512 zoom workgroups gave 37.1, 35.7, 36.4 and 37.0 us per
+  // layer), within the same bounds
+  long long za = kAttendZoomWgs;
+  if (za < need) za = need;
+  if (za > z) za = z;
+  g.z_attend = (int)za;
   return g;
 }
 
@@ -199,6 +213,8 @@ enum LayerMode : int {
   kZoomSplit = 8,  // tail launch: merge the zoom kernel's slots too
   kMerge = 16,     // tail launch: merge each query head's partials into o
   kLists = 32,     // tail launch: write the ascending zoom lists and union
+  kKeepBits = 64,  // with kDense: leave the chunk masks a route launch wrote
+  kMaskBits = 128, // alone: write the chunk masks from a given route's mask
 };
 
 struct LayerArgs {
@@ -293,7 +309,12 @@ hipError_t launch_layer_tail_batch(int mode, int group, const BatchLayerArgs& b,
                                    hipStream_t st);
 // the zoomed spans of a layer, after a layer launch that wrote its chunk masks
 hipError_t launch_zoom(const LayerGeom& g, const LayerArgs& a, hipStream_t st);
-hipError_t launch_zoom_batch(int group, const BatchLayerArgs& b, int batch, hipStream_t st);
+// rows, coarse entries (mode kDense) and the zoomed spans of a layer in one
+// launch, after a route-only layer launch (which wrote mask and chunk masks)
+hipError_t launch_attend(int bf16, int mode, const LayerGeom& g, const LayerArgs& a,
+                         hipStream_t st);
+hipError_t launch_attend_batch(int bf16, int mode, int group, const BatchLayerArgs& b, int batch,
+                               hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st);
 // matched-budget cap of one layer's route output (in place); the kernel keeps
 // one bit per union entry in LDS, so S_c is limited to kCapMaxSpans

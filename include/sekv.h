@@ -245,10 +245,10 @@ sekv_status sekv_decode_attn(const sekv_cache* cache, int32_t layer, const float
  * Eq. 9 and the mixed-resolution softmax): the result is the same as
  * sekv_route followed by sekv_decode_attn with the same arguments, and `route`
  * receives the same mask, lists and counts (and prob, if non-NULL).  With
- * device-tier factors the layer is three kernel launches on `stream` (routing
- * with the full-resolution rows and coarse entries; the zoomed spans, shared
- * among the workgroups in proportion to each KV head's union; the merge and
- * lists); with host-tier factors it
+ * device-tier factors the layer is three kernel launches on `stream`: the
+ * route; then the zoomed spans (shared among workgroups in proportion to each
+ * KV head's union) side by side with the full-resolution rows and coarse
+ * entries; then the merge and lists.  With host-tier factors it
  * runs as sekv_route then sekv_decode_attn (fetch on `fetch_stream`).
  * Arguments as for those two calls. */
 sekv_status sekv_route_attn(const sekv_cache* cache, int32_t layer, const float* q_dev,
