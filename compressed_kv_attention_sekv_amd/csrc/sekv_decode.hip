@@ -1595,16 +1595,21 @@ template <int G>
 union AttendLds {
   Smem<G> l;
   ZoomLds<G> zz;
+  int wc[kListWords][kWaves];
 };
 template <typename T, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attend_kernel(LayerGeom geo, LayerArgs a, int mode) {
   __shared__ AttendLds<G> u;
   const int nz = geo.n_compressed ? geo.z_total : 0;
-  if ((int)blockIdx.x < nz)
-    zoom_body<G>(geo, a, blockIdx.x, u.zz.z, u.zz.st);
-  else
-    layer_body<T, G>(geo, a, mode | kKeepBits, (int)blockIdx.x - nz, u.l);
+  const int nr = geo.n_kv_heads * geo.n_work;
+  const int x = blockIdx.x;
+  if (x < nz)
+    zoom_body<G>(geo, a, x, u.zz.z, u.zz.st);
+  else if (x < nz + nr)
+    layer_body<T, G>(geo, a, (mode & ~kLists) | kKeepBits, x - nz, u.l);
+  else if (mode & kLists)   // the lists need only the route's chunk masks
+    tail_lists<G>(geo, a, x - nz - nr, u.wc);
 }
 static_assert(sizeof(AttendLds<4>) <= 80 * 1024 && sizeof(AttendLds<5>) <= 80 * 1024,
               "two attend workgroups per CU");
@@ -1620,12 +1625,15 @@ void attend_batch_kernel(BatchLayerArgs b, int mode) {
   const int nz = geo.n_compressed ? geo.z_attend : 0;
   const int nr = geo.n_kv_heads * geo.n_work;
   const int x = blockIdx.x;
-  if (x >= nz + nr) return;
+  const int nl = (mode & kLists) ? geo.n_kv_heads : 0;
+  if (x >= nz + nr + nl) return;
   geo.z_total = geo.z_attend;
   if (x < nz)
     zoom_body<G>(geo, b.arg[i], x, u.zz.z, u.zz.st);
+  else if (x < nz + nr)
+    layer_body<T, G>(geo, b.arg[i], (mode & ~kLists) | kKeepBits, x - nz, u.l);
   else
-    layer_body<T, G>(geo, b.arg[i], mode | kKeepBits, x - nz, u.l);
+    tail_lists<G>(geo, b.arg[i], x - nz - nr, u.wc);
 }
 
 hipError_t launch_zoom(const LayerGeom& g, const LayerArgs& a, hipStream_t st) {
@@ -1645,7 +1653,7 @@ hipError_t launch_zoom(const LayerGeom& g, const LayerArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_layer_tail(int mode, const LayerGeom& g, const LayerArgs& a, hipStream_t st) {
-  const dim3 grid(g.n_kv_heads * (g.group + 1));
+  const dim3 grid(g.n_kv_heads * g.group + ((mode & kLists) ? g.n_kv_heads : 0));
 #define SEKV_TAIL(GG)                                                                          \
   case GG:                                                                                     \
     hipLaunchKernelGGL((layer_tail_kernel<GG>), grid, dim3(kThreads), 0, st, g, a, mode);     \
@@ -1663,7 +1671,8 @@ hipError_t launch_layer_tail_batch(int mode, int group, const BatchLayerArgs& b,
                                    hipStream_t st) {
   if (batch < 1 || batch > kMaxBatch) return hipErrorInvalidValue;
   int nx = 0;
-  for (int i = 0; i < batch; ++i) nx = max(nx, b.geo[i].n_kv_heads * (group + 1));
+  for (int i = 0; i < batch; ++i)
+    nx = max(nx, b.geo[i].n_kv_heads * group + ((mode & kLists) ? b.geo[i].n_kv_heads : 0));
   const dim3 grid(nx, batch);
 #define SEKV_TAIL(GG)                                                                          \
   case GG:                                                                                     \
@@ -1704,10 +1713,11 @@ hipError_t launch_layer_batch(int bf16, int mode, int group, const BatchLayerArg
 
 hipError_t launch_attend(int bf16, int mode, const LayerGeom& g, const LayerArgs& a,
                          hipStream_t st) {
-  if (mode != kDense) return hipErrorInvalidValue;
+  if ((mode & ~kLists) != kDense) return hipErrorInvalidValue;
   LayerGeom ga = g;   // the zoom shares over z_attend workgroups (their count is
   ga.z_total = g.z_attend;   // recorded for the merge, within the z_total slots)
-  const dim3 grid(ga.n_work * ga.n_kv_heads + (ga.n_compressed ? ga.z_total : 0));
+  const dim3 grid(ga.n_work * ga.n_kv_heads + (ga.n_compressed ? ga.z_total : 0) +
+                  ((mode & kLists) ? ga.n_kv_heads : 0));
 #define SEKV_ATTEND(GG)                                                                      \
   case GG:                                                                                   \
     if (bf16)                                                                                \
@@ -1728,11 +1738,12 @@ hipError_t launch_attend(int bf16, int mode, const LayerGeom& g, const LayerArgs
 
 hipError_t launch_attend_batch(int bf16, int mode, int group, const BatchLayerArgs& b, int batch,
                                hipStream_t st) {
-  if (mode != kDense || batch < 1 || batch > kMaxBatch) return hipErrorInvalidValue;
+  if ((mode & ~kLists) != kDense || batch < 1 || batch > kMaxBatch) return hipErrorInvalidValue;
   int nx = 0;
   for (int i = 0; i < batch; ++i)
     nx = max(nx, b.geo[i].n_kv_heads * b.geo[i].n_work +
-                     (b.geo[i].n_compressed ? b.geo[i].z_attend : 0));
+                     (b.geo[i].n_compressed ? b.geo[i].z_attend : 0) +
+                     ((mode & kLists) ? b.geo[i].n_kv_heads : 0));
   const dim3 grid(nx, batch);
 #define SEKV_ATTEND(GG)                                                                      \
   case GG:                                                                                   \
