@@ -7,11 +7,12 @@ Llama-3-8B workload at 128K context (32 layers, 32 query / 8 KV heads, d 128,
 bf16 K/V, spans of ~80 tokens, rank cap 32, window 512, 10% of heads zoom ~20%
 of spans and the rest ~1%), resident in HBM before timing starts.
 
-Prints ONE JSON line.  ``value`` is decode steps/s of the whole job.
-``roofline`` covers a layer, the step's only work: the layer kernel (route and
-attention) and its tail launch (merge and lists); algorithmic bytes per layer /
-average layer time from HIP events recorded on the launch stream.  ``cpu_baseline`` times the
-CPU oracle on a bounded sample.
+Prints ONE JSON line (one per share with --zoom-sweep).  ``value`` is decode
+steps/s of the whole job.  ``roofline`` covers a layer, the step's only work:
+the layer kernel (routing, full-resolution rows, coarse entries), the zoom
+kernel (zoomed spans) and the tail launch (merge and lists); algorithmic bytes
+per layer / average layer time from HIP events recorded on the launch stream.
+``cpu_baseline`` times the CPU oracle, pinned to one core, on a bounded sample.
 """
 from __future__ import annotations
 
@@ -66,6 +67,11 @@ def parse():
     ap.add_argument("--fetch", choices=["gather", "memcpy"], default="gather",
                     help="host tier: factor fetch by the gather kernel, or one hipMemcpyAsync per "
                          "run of union spans (the host waits for each layer's route)")
+    ap.add_argument("--write-traffic", nargs=3, default=None,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "ALG_BYTES"),
+                    help="from the counter CSVs of a FETCH_SIZE and a WRITE_SIZE rocprofv3 pass "
+                         "over the default step and its algorithmic bytes per layer, write the "
+                         "traffic file roofline.traffic reads; uses no GPU")
     ap.add_argument("--trace-summary", default=None,
                     help="summarise a rocprofv3 kernel trace CSV (per-kernel launches and mean "
                          "duration; host tier: how much of each layer's factor fetch overlaps "
@@ -106,6 +112,74 @@ def counters_apply(args) -> bool:
             and args.residency_gb == 0.0 and not args.zoom_sweep and not args.full_rank)
 
 
+LAYER_KERNELS = ("route_kernel", "attend_kernel", "layer_tail_kernel")   # a device-tier layer
+
+
+def counter_means(path: str, last: int = 64) -> dict:
+    """Mean of each counter per kernel over its last `last` dispatches, from a
+    rocprofv3 --pmc counter collection CSV: {kernel: {counter: mean}}."""
+    import csv
+    import statistics
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            k = (r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+                 .replace("void ", "").strip())
+            did = int(r.get("Dispatch_Id") or r.get("Correlation_Id"))
+            per.setdefault(k, {}).setdefault(r["Counter_Name"], {})[did] = float(r["Counter_Value"])
+    out = {}
+    for k, cs in per.items():
+        out[k] = {}
+        for c, byd in cs.items():
+            vals = [byd[i] for i in sorted(byd)[-last:]]
+            out[k][c] = statistics.mean(vals)
+            out[k]["dispatches"] = len(vals)
+    return out
+
+
+def write_traffic(workload: str, fetch_csv: str, write_csv: str, alg_bytes: str) -> None:
+    """HBM bytes per layer (its layer, zoom and tail launches) from FETCH_SIZE
+    and WRITE_SIZE in KiB per dispatch, each scaled by what it reads for the
+    device-copy probe of this script (a 2 GiB torch copy_, dispatched as
+    __amd_rocclr_copyBuffer), into profiles/traffic_layer_kernel_<workload>.json
+    with the hash of the kernel sources it was taken on."""
+    import statistics
+    fm, wm = counter_means(fetch_csv, last=1 << 30), counter_means(write_csv, last=1 << 30)
+
+    def per_layer(m, counter):
+        return sum(v[counter] for k, v in m.items() if any(n in k for n in LAYER_KERNELS)
+                   and counter in v)
+
+    def copy_kib(path, counter):
+        import csv
+        with open(path) as f:
+            vals = [float(r["Counter_Value"]) for r in csv.DictReader(f)
+                    if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        return statistics.median(sorted(vals)[-6:])
+
+    fm64, wm64 = counter_means(fetch_csv), counter_means(write_csv)
+    fetch_raw, write_raw = per_layer(fm64, "FETCH_SIZE"), per_layer(wm64, "WRITE_SIZE")
+    moved_kib = 2 * 1024 * 1024   # the probe copies 2 GiB each way
+    cf, cw = copy_kib(fetch_csv, "FETCH_SIZE"), copy_kib(write_csv, "WRITE_SIZE")
+    fs, ws = moved_kib / cf, moved_kib / cw
+    fb, wb = fetch_raw * 1024 * fs, write_raw * 1024 * ws
+    out = {"workload": workload,
+           "kernel": "sekv::route_kernel + sekv::attend_kernel + sekv::layer_tail_kernel (one layer)",
+           "kernel_source_hash": kernel_source_hash(), "bytes_per_launch": fb + wb,
+           "fetch_bytes": fb, "write_bytes": wb, "fetch_KiB_raw": fetch_raw,
+           "write_KiB_raw": write_raw, "fetch_scale": fs, "write_scale": ws,
+           "copy_probe_fetch_KiB": cf, "copy_probe_write_KiB": cw,
+           "algorithmic_bytes_per_launch_same_steps": float(alg_bytes),
+           "per_kernel_KiB": {k: {"FETCH_SIZE": fm64[k].get("FETCH_SIZE"),
+                                  "WRITE_SIZE": wm64.get(k, {}).get("WRITE_SIZE")}
+                              for k in fm64 if any(n in k for n in LAYER_KERNELS)},
+           "launches_averaged": 64}
+    path = os.path.join(ROOT, "profiles", f"traffic_layer_kernel_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out), flush=True)
+
+
 def read_traffic(workload: str):
     """HBM traffic per attention launch from committed rocprofv3 --pmc
     summaries, only if they were taken on the current kernel sources."""
@@ -123,6 +197,9 @@ def main():
     args = parse()
     if args.trace_summary:
         trace_summary(args.trace_summary)
+        return
+    if args.write_traffic:
+        write_traffic(args.workload, *args.write_traffic)
         return
     if args.cpu_configs:
         cpu_configs(args)
@@ -483,19 +560,23 @@ def main():
                 "unit": "GB/s",
                 "frac": attn_gbs / HBM_PEAK_GBS,
                 "traffic": traffic,
-                "kernel": ("sekv::layer_kernel + sekv::layer_tail_kernel, twice, and "
-                           "sekv::cap_budget_kernel (sekv_route, sekv_cap_budget, sekv_decode_attn: "
-                           "one layer, capped)" if capped else
-                           "host tier: sekv::layer_kernel + sekv::layer_tail_kernel (route, lists), "
-                           "the factor fetch (fetch_gather_kernel, or res_claim_kernel + "
-                           "res_fetch_kernel with a residency cache), sekv::layer_kernel twice (rows "
-                           "and coarse entries; zoomed spans) and sekv::layer_tail_kernel (merge)"
+                "kernel": ("sekv_route (sekv::route_kernel + sekv::layer_tail_kernel), "
+                           "sekv_cap_budget (sekv::cap_budget_kernel), sekv_decode_attn "
+                           "(sekv::layer_kernel for the chunk masks + sekv::attend_kernel + "
+                           "sekv::layer_tail_kernel): one layer, capped" if capped else
+                           "host tier: sekv::route_kernel + sekv::layer_tail_kernel (route, lists), "
+                           "the factor fetch (fetch_gather_kernel, one hipMemcpyAsync per run of "
+                           "union spans, or res_claim_kernel + res_fetch_kernel with a residency "
+                           "cache), sekv::layer_kernel (rows and coarse entries), sekv::zoom_kernel "
+                           "(zoomed spans) and sekv::layer_tail_kernel (merge)"
                            if args.tier == "host" else
-                           "sekv::layer_kernel + sekv::layer_tail_kernel (sekv_route_attn, one "
-                           "layer: route + attention, then merge + lists)"
+                           "sekv::route_kernel + sekv::attend_kernel + sekv::layer_tail_kernel "
+                           "(sekv_route_attn, one layer: the route, then the zoomed spans beside "
+                           "the full-resolution rows, coarse entries and lists, then the merge)"
                            if B == 1 else
-                           f"sekv::layer_batch_kernel + sekv::layer_tail_batch_kernel "
-                           f"(sekv_route_attn_batch, one layer of {B} sequences)"),
+                           f"sekv::route_batch_kernel + sekv::attend_batch_kernel + "
+                           f"sekv::layer_tail_batch_kernel (sekv_route_attn_batch, one layer of "
+                           f"{B} sequences)"),
                 "algorithmic_bytes_per_launch": attn_bytes_meas,
                 "avg_launch_us": attn_us_mean,
                 "avg_launch_from": "HIP events around the timed region / (steps x layers); "
@@ -539,23 +620,34 @@ def trace_summary(path: str) -> None:
     import csv
     import statistics
     with open(path) as f:
+        head = f.readline()
+    if "Counter_Name" in head:   # a counter collection: per-kernel means instead
+        print(json.dumps({"counters": counter_means(path)}), flush=True)
+        return
+    with open(path) as f:
         rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
 
     def span(r):
         return int(r["Start_Timestamp"]), int(r["End_Timestamp"])
 
     def short(name):
+        name = name.replace("(anonymous namespace)::", "")
         return name.split("(")[0].replace("void ", "").strip()
 
     per = {}
     for r in rows:
         a, b = span(r)
         per.setdefault(short(r["Kernel_Name"]), []).append((b - a) / 1e3)
+    # the last 640 launches of a kernel: the byte-count pass over the last 20
+    # steps x 32 layers of a default run (the same work as the timed steps,
+    # launched one by one), free of the calibration's route-only launches
     kernels = {k: {"launches": len(v), "mean_us": statistics.mean(v),
-                   "median_us": statistics.median(v), "total_us": sum(v)}
+                   "median_us": statistics.median(v), "total_us": sum(v),
+                   "last640_mean_us": statistics.mean(v[-640:])}
                for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1]))}
     decode = [r for r in rows if any(k in r["Kernel_Name"] for k in
-                                     ("layer_kernel", "zoom_kernel", "layer_tail", "fetch_gather"))]
+                                     ("route_kernel", "attend_kernel", "layer_kernel", "zoom_kernel",
+                                      "layer_tail", "fetch_gather"))]
     gaps = [(span(b)[0] - span(a)[1]) / 1e3 for a, b in zip(decode, decode[1:])
             if span(b)[0] >= span(a)[1]]
     out = {"trace": os.path.basename(path), "kernels": kernels,
@@ -731,7 +823,7 @@ def cpu_configs(args):
                 for h in range(wl.n_q_heads):
                     f = float(targets[layer, h])
                     tau[layer, h] = float(np.quantile(probs[h], 1.0 - f)) if f > 0 else 1.0
-        qs = torch.stack([synth.queries(wl, seed, i) for i in range(40)])
+        qs = torch.stack([synth.queries(wl, seed, i) for i in range(400)])
         setup_s = time.time() - t0
         with one_core() as pin:
             per_layer, n_steps, dt = time_oracle_decode(wl, seg, groups, p, tau, qs, layers)

@@ -926,7 +926,7 @@ sekv_status sekv_route(const sekv_cache* c, int32_t layer, const float* q_dev,
     return SEKV_OK;
   }
   const LayerArgs a = layer_args(c, layer, q_dev, proj_dev, tau_dev, out, nullptr, nullptr);
-  SEKV_HIP(launch_layer(c->bf16(), kRoute, c->geom, a, stream));
+  SEKV_HIP(launch_route(c->bf16(), c->geom, a, stream));
   SEKV_HIP(launch_layer_tail(kLists, c->geom, a, stream));
   return SEKV_OK;
 }
@@ -1069,7 +1069,7 @@ sekv_status sekv_route_attn(const sekv_cache* c, int32_t layer, const float* q_d
   // route; then rows, coarse entries and zoomed spans side by side; then the
   // merge and lists
   const LayerArgs a = layer_args(c, layer, q_dev, proj_dev, tau_dev, route, o_dev, ws_dev);
-  SEKV_HIP(launch_layer(c->bf16(), kRoute, c->geom, a, stream));
+  SEKV_HIP(launch_route(c->bf16(), c->geom, a, stream));
   SEKV_HIP(launch_attend(c->bf16(), kDense | kLists, c->geom, a, stream));
   SEKV_HIP(launch_layer_tail(kMerge | kZoomSplit, c->geom, a, stream));
   return SEKV_OK;
@@ -1387,9 +1387,11 @@ static sekv_status batch_impl(const sekv_cache* const* caches, int32_t batch, in
   if (nb > 0) {
     // as the single calls: route (or the chunk masks of the given routes), then
     // zoomed spans beside rows and coarse entries, then merge (and lists)
-    const int first = with_route ? kRoute : kMaskBits;
     const int grp = caches[0]->geom.group;
-    SEKV_HIP(launch_layer_batch(caches[0]->bf16(), first, grp, b, nb, stream));
+    if (with_route)
+      SEKV_HIP(launch_route_batch(caches[0]->bf16(), grp, b, nb, stream));
+    else
+      SEKV_HIP(launch_layer_batch(caches[0]->bf16(), kMaskBits, grp, b, nb, stream));
     SEKV_HIP(launch_attend_batch(caches[0]->bf16(), kDense | (with_route ? kLists : 0), grp, b,
                                  nb, stream));
     SEKV_HIP(launch_layer_tail_batch(kMerge | kZoomSplit, grp, b, nb, stream));

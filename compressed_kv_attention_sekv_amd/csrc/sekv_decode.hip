@@ -1317,9 +1317,12 @@ __device__ __attribute__((always_inline)) void layer_tail(const LayerGeom& geo, 
   }
 }
 
-// One layer of one sequence: workgroup `block` of its Hkv x n_work grid
-// routes its chunk of compressed spans and attends its full-resolution rows
-// and its chunk's coarse entries; the zoomed spans go to the zoom kernel.
+// The full-resolution rows and coarse entries of one layer of one sequence
+// (mode kDense): workgroup `block` of its Hkv x n_work grid attends its slice
+// of the rows and its chunk's coarse entries (those its heads did not zoom,
+// read from the route's mask), one partial per head into slot w; it also
+// writes the chunk's zoom masks from the mask unless kKeepBits.  Mode
+// kMaskBits alone only writes those masks.
 template <typename T, int G>
 __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
                                                           const LayerArgs& a, int mode,
@@ -1331,54 +1334,23 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int W = geo.n_work;
   const int g = block / W, w = block % W;
-  const int sc = geo.n_compressed, D = geo.n_dense, dr = geo.route_dim;
+  const int sc = geo.n_compressed, D = geo.n_dense;
   const int scs = geo.sc_stride;   // the span arrays' stride (route buffers use sc)
   const int h0 = g * G;
   const int j0 = w * kChunk, nj = w < geo.n_chunks ? min(kChunk, sc - j0) : 0;
   const int d0 = w * geo.dense_rows, d1 = min(D, d0 + geo.dense_rows);
-  const bool route = (mode & kRoute) != 0, dense = (mode & kDense) != 0;
+  const bool dense = (mode & kDense) != 0;
   const float scale = rsqrtf((float)kHeadDim);
 
-  // ---- everything this workgroup reads, issued up front: query, routing
-  // projections, summaries, ln n, thresholds, then the full-resolution rows
-  // (first pass) and coarse entries.  The query goes to LDS only after every
-  // load is out, so no wait for it holds back the rest: the whole prologue is
-  // one round trip.
+  // ---- everything this workgroup reads, issued up front: query, the
+  // full-resolution rows (first pass) and the coarse entries.  The query goes
+  // to LDS only after every load is out, so the prologue is one round trip.
   constexpr int QPT = (G * kHeadDim + kThreads - 1) / kThreads;   // query floats per thread
   float qx[QPT];
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
     const int o = tid + i * kThreads;
     qx[i] = o < G * kHeadDim ? a.q[(size_t)h0 * kHeadDim + o] : 0.f;
-  }
-  const int nout = G * dr, part = tid & 7, orow = tid >> 3;
-  float4 pv[4][4];
-  constexpr int kSumVec = 4;                       // up to 64 bytes of summary per (span, head)
-  const int svec = (dr * (int)sizeof(T)) % 16 == 0 ? dr * (int)sizeof(T) / 16 : 0;
-  const bool sfast = svec > 0 && svec <= kSumVec;
-  uint4 sum[kSumVec];
-  const int jl_g = tid / G, hl_g = tid % G;        // this thread's (span, head) of the gate
-  const bool gate = route && tid < nj * G;
-  double lnn_j = 0.0;   // used only after the barrier, so no wait is forced here
-  float tau_f = 0.f;
-  if (route && nj > 0) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int o = min(orow + 32 * k, nout - 1);   // rows past nout are never used
-      const float* pr = a.proj + ((size_t)h0 * dr + o) * kHeadDim + part * 4;
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) pv[k][c4] = *(const float4*)(pr + 32 * c4);
-    }
-    if (gate) {
-      const int j = j0 + jl_g, h = h0 + hl_g;
-      const uint4* sr = (const uint4*)((const T*)a.summ + ((size_t)h * scs + j) * dr);
-      if (sfast) {
-#pragma unroll
-        for (int v = 0; v < kSumVec; ++v) sum[v] = sr[min(v, svec - 1)];
-      }
-      lnn_j = a.lnn64[j];
-      tau_f = a.tau[h];
-    }
   }
   const T* DK = (const T*)a.dense_k + (size_t)g * geo.dense_stride * kHeadDim;
   const T* DV = (const T*)a.dense_v + (size_t)g * geo.dense_stride * kHeadDim;
@@ -1400,70 +1372,13 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
 #pragma unroll
   for (int i = 0; i < QPT; ++i) {
     const int o = tid + i * kThreads;
-    if (o < G * kHeadDim) {
-      s.rt.qu[o / kHeadDim][o % kHeadDim] = qx[i];
-      s.qs[o / kHeadDim][o % kHeadDim] = qx[i] * scale;
-    }
+    if (o < G * kHeadDim) s.qs[o / kHeadDim][o % kHeadDim] = qx[i] * scale;
   }
   if (tid < kChunk) s.bits[tid] = 0;
   __syncthreads();
 
-  // ---- routing ------------------------------------------------------------
-  if (route && nj > 0) {
-    // q~_h = P_h q_h (float64): 8 lanes per output, 16 dims per lane, lane
-    // `part` takes dims 32 c + 4 part .. + 3, so each load is a 128-byte run
-    for (int k0 = 0; k0 < nout; k0 += 128) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int o = k0 + orow + 32 * k;
-        if (k0 > 0 && o < nout) {
-          const float* pr = a.proj + ((size_t)h0 * dr + o) * kHeadDim + part * 4;
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) pv[k][c4] = *(const float4*)(pr + 32 * c4);
-        }
-        double acc = 0.0;
-        if (o < nout) {
-          const float* qh = &s.rt.qu[o / dr][part * 4];
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4) {
-            const float4 x = pv[k][c4];
-            const float* qc = qh + 32 * c4;
-            acc += (double)x.x * (double)qc[0] + (double)x.y * (double)qc[1] +
-                   (double)x.z * (double)qc[2] + (double)x.w * (double)qc[3];
-          }
-        }
-        acc = group_sum<8>(acc);
-        if (part == 0 && o < nout) s.rt.qt[o / dr][o % dr] = acc;
-      }
-    }
-    __syncthreads();
-    // gate: x = q~ . s_j + gamma ln n_j; p = sigmoid(x); zoom iff p > tau_h
-    if (gate) {
-      const int jl = jl_g, hl = hl_g, j = j0 + jl, h = h0 + hl;
-      double x = 0.0;
-      if (sfast) {
-#pragma unroll
-        for (int v = 0; v < kSumVec; ++v) {
-          if (v < svec) {
-            float f[Ln::EPL];
-            unpack16(sum[v], f, T());
-#pragma unroll
-            for (int e = 0; e < Ln::EPL; ++e) x += s.rt.qt[hl][v * Ln::EPL + e] * (double)f[e];
-          }
-        }
-      } else {
-        const T* sr = (const T*)a.summ + ((size_t)h * scs + j) * dr;
-        for (int i = 0; i < dr; ++i) x += s.rt.qt[hl][i] * (double)Store<T>::load(sr + i);
-      }
-      x += a.gamma * lnn_j;
-      const double p = 1.0 / (1.0 + exp(-x));
-      asm volatile("" : "+v"(tau_f));   // its widening stays here, not next to its load
-      const bool z = p > (double)tau_f;
-      a.mask[(size_t)h * sc + j] = (uint8_t)z;
-      if (a.prob) a.prob[(size_t)h * sc + j] = p;
-      if (z) atomicOr(&s.bits[jl], 1 << hl);
-    }
-  } else if ((dense || (mode & kMaskBits)) && nj > 0) {
+  // ---- the heads of the group that zoom each span of the chunk (from the mask)
+  if (nj > 0) {
     for (int idx = tid; idx < nj * G; idx += kThreads) {
       const int jl = idx / G, hl = idx % G;
       if (a.mask[(size_t)(h0 + hl) * sc + j0 + jl]) atomicOr(&s.bits[jl], 1 << hl);
@@ -1529,6 +1444,167 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
     }
   }
 }
+
+// The route of one layer on its own (sekv_route, and the first launch of
+// sekv_route_attn): workgroup b of KV head g = b / R gates the spans of
+// chunks RC r .. RC (r + 1) - 1, r = b % R, R = ceil(n_chunks / RC) route
+// workgroups per KV head.  With RC chunks per workgroup the group's projected
+// queries (G x dr outputs over P's 64 KB at G = 4, dr = 32) are formed once
+// per RC chunks: launch_route takes RC = 1 while the grid fits the GPU's
+// resident workgroups and RC = kRouteChunks beyond (batches of long
+// contexts), where fewer, fuller workgroups and 1 / RC of the projection
+// reads pay.  Per chunk: mask and gate values of every (head, span), then one
+// ballot per list into the chunk's zoom masks, as the layer kernel writes them.
+template <typename T, int G, int RC>
+__device__ __attribute__((always_inline)) void route_body(const LayerGeom& geo, const LayerArgs& a,
+                                                          int block, Smem<G>& s) {
+  using Ln = Lanes<T>;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int W = geo.n_work, nc = geo.n_chunks, sc = geo.n_compressed, dr = geo.route_dim;
+  const int scs = geo.sc_stride;
+  const int nrw = (nc + RC - 1) / RC;
+  const int g = block / nrw, c0 = (block % nrw) * RC;
+  const int h0 = g * G;
+
+  // ---- all loads up front: query, projections, each chunk's summaries, ln n
+  constexpr int QPT = (G * kHeadDim + kThreads - 1) / kThreads;
+  float qx[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int o = tid + i * kThreads;
+    qx[i] = o < G * kHeadDim ? a.q[(size_t)h0 * kHeadDim + o] : 0.f;
+  }
+  const int nout = G * dr, part = tid & 7, orow = tid >> 3;
+  float4 pv[4][4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int o = min(orow + 32 * k, nout - 1);   // rows past nout are never used
+    const float* pr = a.proj + ((size_t)h0 * dr + o) * kHeadDim + part * 4;
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) pv[k][c4] = *(const float4*)(pr + 32 * c4);
+  }
+  constexpr int kSumVec = 4;
+  const int svec = (dr * (int)sizeof(T)) % 16 == 0 ? dr * (int)sizeof(T) / 16 : 0;
+  const bool sfast = svec > 0 && svec <= kSumVec;
+  const int jl = tid / G, hl = tid % G, h = h0 + hl;   // this thread's (span, head) of a chunk
+  uint4 sum[RC][kSumVec];
+  double lnn[RC];
+  int nj[RC];
+#pragma unroll
+  for (int cc = 0; cc < RC; ++cc) {
+    const int c = c0 + cc, j = c * kChunk + jl;
+    nj[cc] = c < nc ? min(kChunk, sc - c * kChunk) : 0;
+    lnn[cc] = 0.0;
+    if (tid < nj[cc] * G) {
+      if (sfast) {
+        const uint4* sr = (const uint4*)((const T*)a.summ + ((size_t)h * scs + j) * dr);
+#pragma unroll
+        for (int v = 0; v < kSumVec; ++v) sum[cc][v] = sr[min(v, svec - 1)];
+      }
+      lnn[cc] = a.lnn64[j];
+    }
+  }
+  float tau_f = tid < kChunk * G ? a.tau[h] : 0.f;
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int o = tid + i * kThreads;
+    if (o < G * kHeadDim) s.rt.qu[o / kHeadDim][o % kHeadDim] = qx[i];
+  }
+  if (tid < kChunk) s.bits[tid] = 0;
+  __syncthreads();
+
+  // ---- q~_h = P_h q_h (float64), as the layer kernel forms it
+  for (int k0 = 0; k0 < nout; k0 += 128) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int o = k0 + orow + 32 * k;
+      if (k0 > 0 && o < nout) {
+        const float* pr = a.proj + ((size_t)h0 * dr + o) * kHeadDim + part * 4;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) pv[k][c4] = *(const float4*)(pr + 32 * c4);
+      }
+      double acc = 0.0;
+      if (o < nout) {
+        const float* qh = &s.rt.qu[o / dr][part * 4];
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const float4 x = pv[k][c4];
+          const float* qc = qh + 32 * c4;
+          acc += (double)x.x * (double)qc[0] + (double)x.y * (double)qc[1] +
+                 (double)x.z * (double)qc[2] + (double)x.w * (double)qc[3];
+        }
+      }
+      acc = group_sum<8>(acc);
+      if (part == 0 && o < nout) s.rt.qt[o / dr][o % dr] = acc;
+    }
+  }
+  __syncthreads();
+
+  // ---- each chunk: gates, then its zoom masks (one ballot per list)
+  asm volatile("" : "+v"(tau_f));   // its widening stays here, not next to its load
+  const double tau_d = (double)tau_f;
+#pragma unroll
+  for (int cc = 0; cc < RC; ++cc) {
+    const int c = c0 + cc;
+    if (c >= nc) break;   // uniform
+    if (tid < nj[cc] * G) {
+      const int j = c * kChunk + jl;
+      double x = 0.0;
+      if (sfast) {
+#pragma unroll
+        for (int v = 0; v < kSumVec; ++v) {
+          if (v < svec) {
+            float f[Ln::EPL];
+            unpack16(sum[cc][v], f, T());
+#pragma unroll
+            for (int e = 0; e < Ln::EPL; ++e) x += s.rt.qt[hl][v * Ln::EPL + e] * (double)f[e];
+          }
+        }
+      } else {
+        const T* sr = (const T*)a.summ + ((size_t)h * scs + j) * dr;
+        for (int i = 0; i < dr; ++i) x += s.rt.qt[hl][i] * (double)Store<T>::load(sr + i);
+      }
+      x += a.gamma * lnn[cc];
+      const double p = 1.0 / (1.0 + exp(-x));
+      const bool z = p > tau_d;
+      a.mask[(size_t)h * sc + j] = (uint8_t)z;
+      if (a.prob) a.prob[(size_t)h * sc + j] = p;
+      if (z) atomicOr(&s.bits[jl], 1 << hl);
+    }
+    __syncthreads();
+    if (wid == 0) {
+      const int b = lane < nj[cc] ? s.bits[lane] : 0;
+#pragma unroll
+      for (int li = 0; li <= G; ++li) {
+        const bool z = li < G ? ((b >> li) & 1) != 0 : b != 0;
+        const unsigned long long bal = __ballot(z);
+        if (lane == 0) a.chunk_bits[((size_t)g * W + c) * kListWords + li] = (uint32_t)bal;
+      }
+      if (lane < kChunk) s.bits[lane] = 0;   // wave 0 alone reads and clears them
+    }
+    __syncthreads();
+  }
+}
+
+template <typename T, int G, int RC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void route_kernel(LayerGeom geo, LayerArgs a) {
+  __shared__ Smem<G> s;
+  route_body<T, G, RC>(geo, a, blockIdx.x, s);
+}
+
+template <typename T, int G, int RC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void route_batch_kernel(BatchLayerArgs b) {
+  const int i = blockIdx.y;
+  const int nc = b.geo[i].n_chunks;
+  if ((int)blockIdx.x >= b.geo[i].n_kv_heads * ((nc + RC - 1) / RC)) return;
+  __shared__ Smem<G> s;
+  route_body<T, G, RC>(b.geo[i], b.arg[i], blockIdx.x, s);
+}
+
+// chunks per route workgroup for a launch of `wgs1` workgroups at one chunk each
+inline int route_chunks(long long wgs1) { return wgs1 <= 2LL * 256 ? 1 : kRouteChunks; }
 
 template <typename T, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
@@ -1760,6 +1836,67 @@ hipError_t launch_attend_batch(int bf16, int mode, int group, const BatchLayerAr
     default: return hipErrorInvalidValue;
   }
 #undef SEKV_ATTEND
+  return hipGetLastError();
+}
+
+hipError_t launch_route(int bf16, const LayerGeom& g, const LayerArgs& a, hipStream_t st) {
+  if (g.n_compressed == 0) return hipSuccess;
+  const int rc = route_chunks((long long)g.n_kv_heads * g.n_chunks);
+  const dim3 grid(g.n_kv_heads * ((g.n_chunks + rc - 1) / rc));
+#define SEKV_ROUTE_RC(TT, GG)                                                                \
+  if (rc == 1)                                                                               \
+    hipLaunchKernelGGL((route_kernel<TT, GG, 1>), grid, dim3(kThreads), 0, st, g, a);        \
+  else                                                                                       \
+    hipLaunchKernelGGL((route_kernel<TT, GG, kRouteChunks>), grid, dim3(kThreads), 0, st, g, a);
+#define SEKV_ROUTE(GG)                                                                       \
+  case GG:                                                                                   \
+    if (bf16) {                                                                              \
+      SEKV_ROUTE_RC(uint16_t, GG)                                                            \
+    } else {                                                                                 \
+      SEKV_ROUTE_RC(float, GG)                                                               \
+    }                                                                                        \
+    break;
+  switch (g.group) {
+    SEKV_ROUTE(1) SEKV_ROUTE(2) SEKV_ROUTE(3) SEKV_ROUTE(4) SEKV_ROUTE(5) SEKV_ROUTE(6)
+    SEKV_ROUTE(7) SEKV_ROUTE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef SEKV_ROUTE
+#undef SEKV_ROUTE_RC
+  return hipGetLastError();
+}
+
+hipError_t launch_route_batch(int bf16, int group, const BatchLayerArgs& b, int batch,
+                              hipStream_t st) {
+  if (batch < 1 || batch > kMaxBatch) return hipErrorInvalidValue;
+  long long wgs1 = 0;
+  for (int i = 0; i < batch; ++i) wgs1 += (long long)b.geo[i].n_kv_heads * b.geo[i].n_chunks;
+  const int rc = route_chunks(wgs1);
+  int nx = 0;
+  for (int i = 0; i < batch; ++i)
+    nx = max(nx, b.geo[i].n_kv_heads * ((b.geo[i].n_chunks + rc - 1) / rc));
+  if (nx == 0) return hipSuccess;
+  const dim3 grid(nx, batch);
+#define SEKV_ROUTE_RC(TT, GG)                                                                \
+  if (rc == 1)                                                                               \
+    hipLaunchKernelGGL((route_batch_kernel<TT, GG, 1>), grid, dim3(kThreads), 0, st, b);     \
+  else                                                                                       \
+    hipLaunchKernelGGL((route_batch_kernel<TT, GG, kRouteChunks>), grid, dim3(kThreads), 0, st, b);
+#define SEKV_ROUTE(GG)                                                                       \
+  case GG:                                                                                   \
+    if (bf16) {                                                                              \
+      SEKV_ROUTE_RC(uint16_t, GG)                                                            \
+    } else {                                                                                 \
+      SEKV_ROUTE_RC(float, GG)                                                               \
+    }                                                                                        \
+    break;
+  switch (group) {
+    SEKV_ROUTE(1) SEKV_ROUTE(2) SEKV_ROUTE(3) SEKV_ROUTE(4) SEKV_ROUTE(5) SEKV_ROUTE(6)
+    SEKV_ROUTE(7) SEKV_ROUTE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef SEKV_ROUTE
+#undef SEKV_ROUTE_RC
   return hipGetLastError();
 }
 

@@ -150,6 +150,7 @@ constexpr int kZoomWgMax = 512;           // zoom workgroups filling the GPU (tw
 constexpr int kAttendZoomWgs = 256;       // zoom workgroups beside the rows: one per CU of
                                           // MI355X (two ~80 KB workgroups fit a CU)
 constexpr int kZoomBatchMax = 64;         // zoomed spans of one zoom workgroup, at most
+constexpr int kRouteChunks = 4;           // chunks per route workgroup when one each is too many
 
 struct LayerGeom {
   int n_q_heads, n_kv_heads, group, route_dim;
@@ -207,14 +208,13 @@ __host__ inline LayerGeom make_layer_geom(int hq, int hkv, int dr, int n_dense, 
 
 // What one launch of the layer kernel does (bit set).
 enum LayerMode : int {
-  kRoute = 1,      // gate the chunk's spans: mask (+ prob) and the chunk's zoom bit masks
-  kDense = 2,      // attend the workgroup's full-resolution rows and coarse entries (and
-                   // write the chunk's zoom bit masks from the mask if not routing)
-  kZoomSplit = 8,  // tail launch: merge the zoom kernel's slots too
+  kDense = 2,      // layer launch: attend the workgroup's full-resolution rows and coarse
+                   // entries (and write the chunk's zoom masks from the mask)
+  kZoomSplit = 8,  // tail launch: merge the zoom workgroups' slots too
   kMerge = 16,     // tail launch: merge each query head's partials into o
-  kLists = 32,     // tail launch: write the ascending zoom lists and union
-  kKeepBits = 64,  // with kDense: leave the chunk masks a route launch wrote
-  kMaskBits = 128, // alone: write the chunk masks from a given route's mask
+  kLists = 32,     // tail or attend launch: write the ascending zoom lists and union
+  kKeepBits = 64,  // with kDense: leave the chunk masks the route launch wrote
+  kMaskBits = 128, // layer launch, alone: write the chunk masks from a given route's mask
 };
 
 struct LayerArgs {
@@ -234,7 +234,7 @@ struct LayerArgs {
   const uint64_t* fac_off; // [Hkv][sc_stride] float offsets
   const float* pool;       // factor blocks, addressed as pool + (fac_off - off_base)
   uint64_t off_base;
-  uint8_t* mask;           // [Hq][S_c] (written with kRoute, read otherwise)
+  uint8_t* mask;           // [Hq][S_c] (written by the route launch, read otherwise)
   double* prob;            // [Hq][S_c] or NULL
   int32_t* list;           // [Hq][S_c]
   int32_t* count;          // [Hq]
@@ -300,6 +300,11 @@ hipError_t launch_span_rsvd(int bf16, const void* x, int n_tokens, const int32_t
 
 hipError_t launch_layer(int bf16, int mode, const LayerGeom& g, const LayerArgs& a,
                         hipStream_t st);
+// the route of a layer alone (mask, gate values, chunk masks): one chunk per
+// workgroup, or kRouteChunks when that many workgroups would not all be resident
+hipError_t launch_route(int bf16, const LayerGeom& g, const LayerArgs& a, hipStream_t st);
+hipError_t launch_route_batch(int bf16, int group, const BatchLayerArgs& b, int batch,
+                              hipStream_t st);
 hipError_t launch_layer_batch(int bf16, int mode, int group, const BatchLayerArgs& b, int batch,
                               hipStream_t st);
 // the merge and lists of a layer (kMerge, kLists, kZoomSplit bits of mode) in a
