@@ -179,7 +179,8 @@ struct alignas(16) Smem {
   union {
     struct {                       // routing (dead once the gates are taken)
       float qu[G][kHeadDim];       // query as given
-      double qt[G][kMaxRouteDim];  // P_h q_h
+      double qt[G][kMaxRouteDim + 1];  // P_h q_h (rows padded: the gates of G heads read
+                                       // G rows at once, on different LDS banks)
     } rt;
     WaveScratch<G> w[kWaves];      // written from the rows phase on
   };
@@ -399,11 +400,11 @@ __device__ __attribute__((always_inline)) void zoom_span(const float* __restrict
 #pragma unroll
       for (int h = 0; h < G; ++h) pa[h] = 0.f;
       if (i < rk) {
-        const float4* row = (const float4*)(vk + (size_t)i * kHeadDim + part * 16);
+        const float* row = vk + (size_t)i * kHeadDim + part * 4;
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
-          const float4 x = row[c4];
-          const int d0 = part * 16 + c4 * 4;
+          const float4 x = *(const float4*)(row + 32 * c4);
+          const int d0 = part * 4 + c4 * 32;
 #pragma unroll
           for (int h = 0; h < G; ++h)
             pa[h] += x.x * qs[h][d0] + x.y * qs[h][d0 + 1] + x.z * qs[h][d0 + 2] +
@@ -715,9 +716,10 @@ __device__ __forceinline__ void reduce_scatter(float p, const float4 (&u)[RC / 4
 // receives the V_K of `nxs` (the next span, or a stand-in when it has none of
 // the kind).
 //
-//  (A) b_h[i] = sigma_K[i] (V_K q_h)[i]: lane (part, ci) sums 16 dims of rows
-//      ci + 8 p; b goes to the wave's scratch scr[h][0..32), which (B) reads
-//      broadcast.
+//  (A) b_h[i] = sigma_K[i] (V_K q_h)[i]: lane (part, ci) sums dims 4 part + 32 c
+//      .. + 3, c < 4, of rows ci + 8 p (eight lanes read 128 contiguous bytes,
+//      free of LDS bank conflicts); b goes to the wave's scratch scr[h][0..32),
+//      which (B) reads broadcast.
 //  (B) e[t] = U_K[t] . b_h with lane = token t, then the online softmax.
 //  (C) c_h[i] = sum_t p_h[t] U_V[t][i]: each lane multiplies its token's row,
 //      and a reduce-scatter over the 64 lanes leaves components 4 g .. 4 g + 3
@@ -741,7 +743,7 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
   const int rk4 = fv.r4(0), rv4 = fv.r4(1), nqk = rk4 / 4;
   const float* vk = cu.blk + fv.vt(0);
   const float* vv = cu.blk + fv.vt(1);
-  const int part = lane & 7, ci = lane >> 3;   // (A): component ci + 8 p, dims 16 part ..
+  const int part = lane & 7, ci = lane >> 3;   // (A): component ci + 8 p, dims 4 part + 32 c
   const int half = lane >> 5, dq = lane & 31;  // (D): rows 2 k + half, dims 4 dq ..
   const int cg = lane / GL;                    // after (C): components 4 cg ..
   const bool staged = SR >= 32 || rk <= SR;    // always, when the stage holds 32 rows
@@ -762,7 +764,7 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
       const int i = min(ci + 8 * p, rk - 1);
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4)
-        va[p][c4] = *(const float4*)(vk + (size_t)i * kHeadDim + part * 16 + c4 * 4);
+        va[p][c4] = *(const float4*)(vk + (size_t)i * kHeadDim + part * 4 + c4 * 32);
     }
     // entries clamped to each matrix's r4 (as the stage copy is)
     const float* sk = cu.blk + fv.sigma(0);
@@ -798,8 +800,8 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
           const float4 x =
-              staged ? *(const float4*)(stage + i * kHeadDim + part * 16 + c4 * 4) : va[p][c4];
-          const float4 qv = *(const float4*)&qs[h][part * 16 + c4 * 4];
+              staged ? *(const float4*)(stage + i * kHeadDim + part * 4 + c4 * 32) : va[p][c4];
+          const float4 qv = *(const float4*)&qs[h][part * 4 + c4 * 32];
           acc += x.x * qv.x + x.y * qv.y + x.z * qv.z + x.w * qv.w;
         }
         acc = group_sum<8>(acc);
@@ -1446,14 +1448,12 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
 }
 
 // The route of one layer on its own (sekv_route, and the first launch of
-// sekv_route_attn): workgroup b of KV head g = b / R gates the spans of
-// chunks RC r .. RC (r + 1) - 1, r = b % R, R = ceil(n_chunks / RC) route
-// workgroups per KV head.  With RC chunks per workgroup the group's projected
-// queries (G x dr outputs over P's 64 KB at G = 4, dr = 32) are formed once
-// per RC chunks: launch_route takes RC = 1 while the grid fits the GPU's
-// resident workgroups and RC = kRouteChunks beyond (batches of long
-// contexts), where fewer, fuller workgroups and 1 / RC of the projection
-// reads pay.  Per chunk: mask and gate values of every (head, span), then one
+// sekv_route_attn): workgroup b of KV head g = b mod Hkv gates the spans of
+// chunks RC r .. RC (r + 1) - 1, r = b / Hkv.  With RC chunks per workgroup
+// the group's projected queries (G x dr outputs over P's 64 KB at G = 4,
+// dr = 32) are formed once per RC chunks; launch_route takes RC = 1 for grids
+// up to one workgroup per CU, 2 up to two, kRouteChunks beyond (batches of
+// long contexts), where fewer, fuller workgroups pay.  Per chunk: mask and gate values of every (head, span), then one
 // ballot per list into the chunk's zoom masks, as the layer kernel writes them.
 template <typename T, int G, int RC>
 __device__ __attribute__((always_inline)) void route_body(const LayerGeom& geo, const LayerArgs& a,
@@ -1462,8 +1462,10 @@ __device__ __attribute__((always_inline)) void route_body(const LayerGeom& geo, 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int W = geo.n_work, nc = geo.n_chunks, sc = geo.n_compressed, dr = geo.route_dim;
   const int scs = geo.sc_stride;
-  const int nrw = (nc + RC - 1) / RC;
-  const int g = block / nrw, c0 = (block % nrw) * RC;
+  // consecutive workgroups take consecutive KV heads: the dispatcher deals
+  // workgroups to the XCDs round robin, so with Hkv a multiple of the XCD
+  // count each XCD's L2 fetches the projections of its own KV heads only
+  const int g = block % geo.n_kv_heads, c0 = (block / geo.n_kv_heads) * RC;
   const int h0 = g * G;
 
   // ---- all loads up front: query, projections, each chunk's summaries, ln n
@@ -1604,7 +1606,7 @@ void route_batch_kernel(BatchLayerArgs b) {
 }
 
 // chunks per route workgroup for a launch of `wgs1` workgroups at one chunk each
-inline int route_chunks(long long wgs1) { return wgs1 <= 2LL * 256 ? 1 : kRouteChunks; }
+inline int route_chunks(long long wgs1) { return wgs1 <= 256 ? 1 : (wgs1 <= 512 ? 2 : kRouteChunks); }
 
 template <typename T, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
@@ -1846,6 +1848,8 @@ hipError_t launch_route(int bf16, const LayerGeom& g, const LayerArgs& a, hipStr
 #define SEKV_ROUTE_RC(TT, GG)                                                                \
   if (rc == 1)                                                                               \
     hipLaunchKernelGGL((route_kernel<TT, GG, 1>), grid, dim3(kThreads), 0, st, g, a);        \
+  else if (rc == 2)                                                                          \
+    hipLaunchKernelGGL((route_kernel<TT, GG, 2>), grid, dim3(kThreads), 0, st, g, a);        \
   else                                                                                       \
     hipLaunchKernelGGL((route_kernel<TT, GG, kRouteChunks>), grid, dim3(kThreads), 0, st, g, a);
 #define SEKV_ROUTE(GG)                                                                       \
@@ -1880,6 +1884,8 @@ hipError_t launch_route_batch(int bf16, int group, const BatchLayerArgs& b, int 
 #define SEKV_ROUTE_RC(TT, GG)                                                                \
   if (rc == 1)                                                                               \
     hipLaunchKernelGGL((route_batch_kernel<TT, GG, 1>), grid, dim3(kThreads), 0, st, b);     \
+  else if (rc == 2)                                                                          \
+    hipLaunchKernelGGL((route_batch_kernel<TT, GG, 2>), grid, dim3(kThreads), 0, st, b);     \
   else                                                                                       \
     hipLaunchKernelGGL((route_batch_kernel<TT, GG, kRouteChunks>), grid, dim3(kThreads), 0, st, b);
 #define SEKV_ROUTE(GG)                                                                       \

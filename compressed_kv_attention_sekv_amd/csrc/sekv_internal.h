@@ -150,7 +150,7 @@ constexpr int kZoomWgMax = 512;           // zoom workgroups filling the GPU (tw
 constexpr int kAttendZoomWgs = 256;       // zoom workgroups beside the rows: one per CU of
                                           // MI355X (two ~80 KB workgroups fit a CU)
 constexpr int kZoomBatchMax = 64;         // zoomed spans of one zoom workgroup, at most
-constexpr int kRouteChunks = 4;           // chunks per route workgroup when one each is too many
+constexpr int kRouteChunks = 4;           // chunks per route workgroup for the largest grids
 
 struct LayerGeom {
   int n_q_heads, n_kv_heads, group, route_dim;
@@ -300,8 +300,8 @@ hipError_t launch_span_rsvd(int bf16, const void* x, int n_tokens, const int32_t
 
 hipError_t launch_layer(int bf16, int mode, const LayerGeom& g, const LayerArgs& a,
                         hipStream_t st);
-// the route of a layer alone (mask, gate values, chunk masks): one chunk per
-// workgroup, or kRouteChunks when that many workgroups would not all be resident
+// the route of a layer alone (mask, gate values, chunk masks): 1, 2 or
+// kRouteChunks chunks per workgroup as the grid grows
 hipError_t launch_route(int bf16, const LayerGeom& g, const LayerArgs& a, hipStream_t st);
 hipError_t launch_route_batch(int bf16, int group, const BatchLayerArgs& b, int batch,
                               hipStream_t st);
