@@ -498,8 +498,8 @@ def sekv_route_attn_batch(caches: Sequence[Cache], layer: int, qs: Sequence[torc
                           proj: torch.Tensor, tau: torch.Tensor, routes: Sequence[RouteBuffers],
                           os_: Sequence[torch.Tensor], workspaces: Sequence[torch.Tensor],
                           stream=None) -> None:
-    """Route and attend one layer of several sequences (one cache each): one layer launch
-    and one tail launch for all of them."""
+    """Route and attend one layer of several sequences (one cache each): one route launch,
+    one attend launch and one tail launch for all of them."""
     _need(proj, "proj", torch.float32)
     _need(tau, "tau", torch.float32)
     cs, qp, rs, op, wp, wb = _batch_arrays(caches, qs, routes, os_, workspaces)
@@ -510,8 +510,8 @@ def sekv_route_attn_batch(caches: Sequence[Cache], layer: int, qs: Sequence[torc
 def sekv_decode_attn_batch(caches: Sequence[Cache], layer: int, qs: Sequence[torch.Tensor],
                            routes: Sequence[RouteBuffers], os_: Sequence[torch.Tensor],
                            workspaces: Sequence[torch.Tensor], stream=None) -> None:
-    """Attend one layer of several sequences (routes given): one layer launch and one
-    tail launch."""
+    """Attend one layer of several sequences (routes given): one chunk-mask launch, one
+    attend launch and one tail launch."""
     cs, qp, rs, op, wp, wb = _batch_arrays(caches, qs, routes, os_, workspaces)
     _check(lib().sekv_decode_attn_batch(cs, len(caches), layer, qp, rs, op, wp, wb,
                                         _stream(stream)))

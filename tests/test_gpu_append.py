@@ -166,3 +166,40 @@ def test_append_errors_change_nothing(S):
         assert torch.equal(before[key], after[key]), key
     S.sekv_append_tokens(cache, *one(N0 + 10, 6))
     assert cache.info.n_appended == 16
+
+
+def test_appended_caches_in_batched_and_noalloc_calls(S):
+    """Caches grown by different appends keep working through the batched
+    call (bit-identical to the single calls) and the allocation-free call
+    (bit-identical to the workspace call)."""
+    wl = workload(n_layers=1)
+    log("[append] batched and allocation-free calls after appends")
+    caches, inps = [], []
+    for seed, steps in ((41, (1,) * 20 + (250, 130)), (42, (120, 3, 47, 230)), (43, (400,))):
+        inp = Inputs(wl, seed)
+        caches.append(build_and_append(S, wl, inp, capacity=512, steps=steps))
+        inps.append(inp)
+    p = inps[0].p[0].contiguous()
+    tau = torch.full((wl.n_q_heads,), 0.7, device="cuda")
+    qs = [inp.query(3)[0].contiguous() for inp in inps]
+    single = []
+    for c, q in zip(caches, qs):
+        rb = S.RouteBuffers.allocate(c)
+        o = torch.zeros(wl.n_q_heads, wl.head_dim, device="cuda")
+        ws = torch.empty(c.workspace_bytes(), dtype=torch.uint8, device="cuda")
+        S.sekv_route_attn(c, 0, q, p, tau, rb, o, ws)
+        single.append((rb, o))
+    rbs = [S.RouteBuffers.allocate(c) for c in caches]
+    outs = [torch.zeros(wl.n_q_heads, wl.head_dim, device="cuda") for _ in caches]
+    wss = [torch.empty(c.workspace_bytes(), dtype=torch.uint8, device="cuda") for c in caches]
+    S.sekv_route_attn_batch(caches, 0, qs, p, tau, rbs, outs, wss)
+    torch.cuda.synchronize()
+    for (rb, o), rbb, ob in zip(single, rbs, outs):
+        assert torch.equal(rb.mask, rbb.mask) and torch.equal(o, ob)
+    for c, q, (rb, o) in zip(caches, qs, single):
+        rbn = S.RouteBuffers.allocate(c)
+        on = torch.zeros_like(o)
+        S.sekv_route_attn_noalloc(c, 0, q, p, tau, rbn, on)
+        torch.cuda.synchronize()
+        assert torch.equal(rb.mask, rbn.mask) and torch.equal(o, on)
+    log(f"[append] spans after appends: {[c.info.n_compressed for c in caches]}")
