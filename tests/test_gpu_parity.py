@@ -456,6 +456,43 @@ def test_many_chunks_merge_parity(S):
     assert err <= 1e-6
 
 
+@pytest.mark.parametrize("n_tokens,chunks_per_wg", [(20000, 2), (40000, 4)])
+def test_route_chunks_per_workgroup(S, n_tokens, chunks_per_wg):
+    """The route launch gates 1, 2 or 4 chunks of 32 spans per workgroup as
+    Hkv x chunks grows past one and two workgroups per CU: 4 KV heads of
+    short spans reach the 2- and 4-chunk launches.  Routes and outputs of
+    every head against the oracle; the batched call (whose route launch
+    counts the chunks of all its sequences) bit-identical to single calls."""
+    wl = synth.workload("tiny", n_tokens=n_tokens, min_span_len=1, n_q_heads=8, n_kv_heads=4)
+    log(f"[parity] route chunks per workgroup: N={n_tokens}, 4 KV heads")
+    inp = Inputs(wl, 7)
+    cache = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    wgs1 = wl.n_kv_heads * -(-cache.info.n_compressed // 32)
+    assert (wgs1 > 512) == (chunks_per_wg == 4) and (256 < wgs1 <= 512) == (chunks_per_wg == 2)
+    orc = OracleSide(inp, [0], wl.max_rank)
+    tau = synth.tau_uniform(wl, 7, device="cuda")[0].contiguous()
+    q = inp.query(0)[0]
+    n_tie, worst, route = check_layer(S, cache, orc, inp, 0, q, tau, wl.gamma, TOL["f32"])
+    log(f"[parity] route chunks: spans={cache.info.n_compressed} chunk workgroups={wgs1} "
+        f"zoomed={int(route.mask.sum())} ties={n_tie} err={worst:.2e}")
+    assert int(route.mask.sum()) > 0
+    # two sequences through the batched call: its route launch sees both
+    inp2 = Inputs(wl, 8)
+    cache2 = S.sekv_build_spans(make_cfg(S, wl), inp2.s, inp2.k, inp2.v, inp2.w, inp2.ranks)
+    q2 = inp2.query(0)[0]
+    p = inp.p[0].contiguous()
+    single = [run_gpu_layer(S, c, 0, qq, p, tau) for c, qq in ((cache, q), (cache2, q2))]
+    rbs = [S.RouteBuffers.allocate(c, with_prob=True) for c in (cache, cache2)]
+    outs = [torch.zeros(wl.n_q_heads, wl.head_dim, device="cuda") for _ in range(2)]
+    wss = [torch.empty(c.workspace_bytes(), dtype=torch.uint8, device="cuda") for c in (cache, cache2)]
+    S.sekv_route_attn_batch([cache, cache2], 0, [q.contiguous(), q2.contiguous()], p, tau, rbs,
+                            outs, wss)
+    torch.cuda.synchronize()
+    for (rb, o), rbb, ob in zip(single, rbs, outs):
+        assert torch.equal(rb.mask, rbb.mask) and torch.equal(rb.prob, rbb.prob)
+        assert torch.equal(rb.list, rbb.list) and torch.equal(o, ob)
+
+
 @pytest.fixture(scope="module")
 def full_c3(S):
     """The Llama-3-8B-shape workload at full size (32 layers, 131072 tokens,
