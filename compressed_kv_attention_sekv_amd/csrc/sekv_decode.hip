@@ -659,52 +659,21 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Sum over the 64 lanes of p * u[i] for the RC components i of u (u[q] holds
-// components 4 q .. 4 q + 3 of the lane's row), left as components 4 g + k
-// (k < 4) in out[k] of the lanes GL g .. GL g + GL - 1, GL = 256 / RC: the
-// halves of the wave swap RC / 2 components, rows RC / 4, then (RC 32) lanes
-// 8 apart 4 and each group of 8 lanes sums, or (RC 16) each row sums.
+// Rows t0 .. t0 + 63 of U_V (n rows of r4 floats) in the layout of (C):
+// lane = (component group cg, token group tg), lane = cg TG + tg with TG =
+// 64 / (RC / 4); x[k] holds components 4 cg .. 4 cg + 3 of token
+// t0 + k TG + tg, k < RC / 4 (rows clamped to the span, component groups to
+// r4).  For each k the wave reads TG consecutive rows whole: one contiguous
+// piece of memory.
 template <int RC>
-__device__ __forceinline__ void reduce_scatter(float p, const float4 (&u)[RC / 4], float (&out)[4]) {
-  static_assert(RC == 16 || RC == 32, "rank class");
-  constexpr int H = RC / 2;
+__device__ __forceinline__ void load_uv_tile(const float* u, int n, int r4, int t0,
+                                             float4 (&x)[RC / 4]) {
+  constexpr int CG = RC / 4, TG = 64 / CG;
   const int lane = threadIdx.x & 63;
-  // lanes 0..31 keep the first RC / 2 components, lanes 32..63 the others
-  // (each product formed where it is swapped)
-  float y[H];
+  const int cg = min(lane / TG, r4 / 4 - 1), tg = lane % TG;
 #pragma unroll
-  for (int q = 0; q < RC / 8; ++q) {
-    const float lo[4] = {p * u[q].x, p * u[q].y, p * u[q].z, p * u[q].w};
-    const float4 uh = u[q + RC / 8];
-    const float hi[4] = {p * uh.x, p * uh.y, p * uh.z, p * uh.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo[k]), __float_as_uint(hi[k]),
-                                                      false, false);
-      y[4 * q + k] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
-    }
-  }
-  // even rows keep the first half of theirs, odd rows the second
-  float z[H / 2];
-#pragma unroll
-  for (int i = 0; i < H / 2; ++i) {
-    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(y[i]),
-                                                    __float_as_uint(y[i + H / 2]), false, false);
-    z[i] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
-  }
-  if constexpr (RC == 32) {
-    // lanes 0..7 of a row keep the first 4 of their 8, lanes 8..15 the last 4
-    const bool hi8 = (lane & 8) != 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float keep = hi8 ? z[k + 4] : z[k];
-      const float send = hi8 ? z[k] : z[k + 4];
-      out[k] = group_sum<8>(keep + dpp<kDppRor8>(send));
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) out[k] = group_sum<16>(z[k]);
-  }
+  for (int k = 0; k < CG; ++k)
+    x[k] = *(const float4*)(u + (size_t)min(t0 + k * TG + tg, n - 1) * r4 + 4 * cg);
 }
 
 // One span of the pipeline, for key and value ranks up to RC (16 or 32):
@@ -721,9 +690,12 @@ __device__ __forceinline__ void reduce_scatter(float p, const float4 (&u)[RC / 4
 //      free of LDS bank conflicts); b goes to the wave's scratch scr[h][0..32),
 //      which (B) reads broadcast.
 //  (B) e[t] = U_K[t] . b_h with lane = token t, then the online softmax.
-//  (C) c_h[i] = sum_t p_h[t] U_V[t][i]: each lane multiplies its token's row,
-//      and a reduce-scatter over the 64 lanes leaves components 4 g .. 4 g + 3
-//      in lanes GL g .. GL g + GL - 1.
+//  (C) c_h[i] = sum_t p_h[t] U_V[t][i]: p goes through the wave's scratch
+//      to lane (cg, tg), which keeps components 4 cg .. 4 cg + 3 of the sum
+//      over its RC / 4 tokens of each block (rescaled with the softmax);
+//      once per span the GL token groups are added, which leaves components
+//      4 g .. 4 g + 3 in lanes GL g .. GL g + GL - 1.  The softmax sum l
+//      likewise stays a per-lane partial until then.
 //  (D) a_h = V_V^T (sigma_V c_h) with sigma_V c_h read out as scalars; lane
 //      (half, dq) sums rows 2 k + half of dims 4 dq .. 4 dq + 3, the two
 //      halves of the wave are added, and scr[h] turns the result into the
@@ -745,12 +717,13 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
   const float* vv = cu.blk + fv.vt(1);
   const int part = lane & 7, ci = lane >> 3;   // (A): component ci + 8 p, dims 4 part + 32 c
   const int half = lane >> 5, dq = lane & 31;  // (D): rows 2 k + half, dims 4 dq ..
-  const int cg = lane / GL;                    // after (C): components 4 cg ..
+  const int cg = lane / GL;                    // (C): components 4 cg .. 4 cg + 3
+  const int tg = lane % GL;                    // (C): tokens tg, tg + GL, ... of a block
   const bool staged = SR >= 32 || rk <= SR;    // always, when the stage holds 32 rows
 
   // this span's own loads, needed last: the first rows of U_V, all of V_V
   float4 uc[UQ];
-  load_u_tile<UQ>(cu.blk + fv.u(1), n, rv4, 0, uc);
+  load_uv_tile<RC>(cu.blk + fv.u(1), n, rv4, 0, uc);
   float4 vd[VK];
 #pragma unroll
   for (int k = 0; k < VK; ++k)
@@ -842,20 +815,48 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
   };
   // online softmax and (C) from the rows in uc
   auto accumulate = [&](const float (&e)[G]) {
+    float corr[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+      corr[h] = 1.f;
       if (!((hm >> h) & 1u)) continue;
       const float mx = wave_max(e[h]);
       const float mn = fmaxf(ms[h], mx);
-      const float corr = (ms[h] == -INFINITY) ? 0.f : __expf(ms[h] - mn);
+      corr[h] = (ms[h] == -INFINITY) ? 0.f : __expf(ms[h] - mn);
       const float p = (e[h] == -INFINITY) ? 0.f : __expf(e[h] - mn);
-      ls[h] = ls[h] * corr + wave_sum(p);
+      ls[h] = ls[h] * corr[h] + p;   // the lane's part of l
       ms[h] = mn;
-      float c4[4];
-      reduce_scatter<RC>(p, uc, c4);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) cacc[h][k] = cacc[h][k] * corr + c4[k];
+      // token `lane` to lane (tg, k) = (lane mod GL, lane / GL), k-th of its tokens
+      scr[h][64 + (lane % GL) * (RC / 4) + lane / GL] = p;
     }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (!((hm >> h) & 1u)) continue;
+      float pk[RC / 4];
+#pragma unroll
+      for (int q = 0; q < RC / 16; ++q) {
+        const float4 v = *(const float4*)&scr[h][64 + tg * (RC / 4) + 4 * q];
+        pk[4 * q] = v.x;
+        pk[4 * q + 1] = v.y;
+        pk[4 * q + 2] = v.z;
+        pk[4 * q + 3] = v.w;
+      }
+      float c0 = cacc[h][0] * corr[h], c1 = cacc[h][1] * corr[h];
+      float c2 = cacc[h][2] * corr[h], c3 = cacc[h][3] * corr[h];
+#pragma unroll
+      for (int k = 0; k < RC / 4; ++k) {
+        c0 += pk[k] * uc[k].x;
+        c1 += pk[k] * uc[k].y;
+        c2 += pk[k] * uc[k].z;
+        c3 += pk[k] * uc[k].w;
+      }
+      cacc[h][0] = c0;
+      cacc[h][1] = c1;
+      cacc[h][2] = c2;
+      cacc[h][3] = c3;
+    }
+    __builtin_amdgcn_wave_barrier();
   };
   // every 64 tokens but the last: the next 64 rows of U_K and U_V follow
   // (the same loads on every pass, so the compiler's waits stay exact)
@@ -868,7 +869,7 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
     issue_fence();
     accumulate(e);
     issue_fence();
-    load_u_tile<UQ>(cu.blk + fv.u(1), n, rv4, t0 + 64, uc);
+    load_uv_tile<RC>(cu.blk + fv.u(1), n, rv4, t0 + 64, uc);
     issue_fence();
   }
   // the last 64: then what the next span needs first
@@ -879,6 +880,15 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
     prefetch_span(nxp, ub);
     issue_fence();
     accumulate(e);
+  }
+
+  // the token groups' parts of c_h, and the lanes' parts of l
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if (!((hm >> h) & 1u)) continue;
+    ls[h] = wave_sum(ls[h]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cacc[h][k] = group_sum<GL>(cacc[h][k]);
   }
 
   // (D) a_h[dim] = sum_i V_V[i][dim] (sigma_V c_h)[i]; rows past rV hold a
