@@ -96,16 +96,31 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
   return ((uint64_t)hi << 32) | lo;
 }
+// A float as an int of the same order (for every value but NaN): the sign
+// bit stays, the other bits of a negative value are flipped.  A max taken on
+// these keys is the float max, with neither operand canonicalised, and the
+// DPP move folds into the integer max.  The map is its own inverse.
+__device__ __forceinline__ int fkey(float x) {
+  const int i = __float_as_int(x);
+  return i ^ ((i >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ float funkey(int k) { return __int_as_float(fkey(__int_as_float(k))); }
+template <int CTRL>
+__device__ __forceinline__ int kmax_dpp(int k) {
+  // the patterns used stay inside a row, so no lane reads out of bounds
+  return max(k, __builtin_amdgcn_mov_dpp(k, CTRL, 0xF, 0xF, true));
+}
 // wave-wide max / sum, the total on every lane
 __device__ __forceinline__ float wave_max(float x) {
-  x = fmaxf(x, dpp<kDppXor1>(x));
-  x = fmaxf(x, dpp<kDppXor2>(x));
-  x = fmaxf(x, dpp<kDppHalfMirror>(x));
-  x = fmaxf(x, dpp<kDppMirror>(x));
-  Pair p = pair_xor<16>(x);
-  x = fmaxf(p.lo, p.hi);
-  p = pair_xor<32>(x);
-  return fmaxf(p.lo, p.hi);
+  int k = fkey(x);
+  k = kmax_dpp<kDppXor1>(k);
+  k = kmax_dpp<kDppXor2>(k);
+  k = kmax_dpp<kDppHalfMirror>(k);
+  k = kmax_dpp<kDppMirror>(k);
+  auto r = __builtin_amdgcn_permlane16_swap((uint32_t)k, (uint32_t)k, false, false);
+  k = max((int)r[0], (int)r[1]);
+  r = __builtin_amdgcn_permlane32_swap((uint32_t)k, (uint32_t)k, false, false);
+  return funkey(max((int)r[0], (int)r[1]));
 }
 __device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
 // weights of two online-softmax states under their common max; -inf = empty
@@ -712,7 +727,7 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
   const int n = cu.n, rk = cu.rk, rv = cu.rv;
   const unsigned hm = cu.hm;
   const FactorView fv(rk, rv, n);
-  const int rk4 = fv.r4(0), rv4 = fv.r4(1), nqk = rk4 / 4;
+  const int rk4 = fv.r4(0), rv4 = fv.r4(1);
   const float* vk = cu.blk + fv.vt(0);
   const float* vv = cu.blk + fv.vt(1);
   const int part = lane & 7, ci = lane >> 3;   // (A): component ci + 8 p, dims 4 part + 32 c
@@ -808,7 +823,7 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
 #pragma unroll
       for (int q = 0; q < UQ; ++q) {
         const float4 b = *(const float4*)&scr[h][4 * q];   // the same address on every lane
-        if (q < nqk) acc += ub[q].x * b.x + ub[q].y * b.y + ub[q].z * b.z + ub[q].w * b.w;
+        if (q < rk4 / 4) acc += ub[q].x * b.x + ub[q].y * b.y + ub[q].z * b.z + ub[q].w * b.w;
       }
       if (lane < tn) e[h] = acc;
     }
@@ -820,10 +835,12 @@ __device__ __attribute__((always_inline)) void zoom_span32(const SpanRef& cu, co
     for (int h = 0; h < G; ++h) {
       corr[h] = 1.f;
       if (!((hm >> h) & 1u)) continue;
+      // every block has a token, so mx and mn are finite, and the empty
+      // state (ms = -inf) and the lanes past the span (e = -inf) get exp(-inf) = 0
       const float mx = wave_max(e[h]);
       const float mn = fmaxf(ms[h], mx);
-      corr[h] = (ms[h] == -INFINITY) ? 0.f : __expf(ms[h] - mn);
-      const float p = (e[h] == -INFINITY) ? 0.f : __expf(e[h] - mn);
+      corr[h] = __expf(ms[h] - mn);
+      const float p = __expf(e[h] - mn);
       ls[h] = ls[h] * corr[h] + p;   // the lane's part of l
       ms[h] = mn;
       // token `lane` to lane (tg, k) = (lane mod GL, lane / GL), k-th of its tokens
