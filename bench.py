@@ -72,6 +72,12 @@ def parse():
                     help="from the counter CSVs of a FETCH_SIZE and a WRITE_SIZE rocprofv3 pass "
                          "over the default step and its algorithmic bytes per layer, write the "
                          "traffic file roofline.traffic reads; uses no GPU")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-workgroup time stamps of each layer's route, attend and tail "
+                         "launches (one sequence, device tier; needs the diagnostic library: "
+                         "python -m compressed_kv_attention_sekv_amd.build --timeline, loaded "
+                         "with SEKV_LIBRARY=compressed_kv_attention_sekv_amd/libsekv_timeline.so); "
+                         "prints a JSON summary instead of the bench line")
     ap.add_argument("--trace-summary", default=None,
                     help="summarise a rocprofv3 kernel trace CSV (per-kernel launches and mean "
                          "duration; host tier: how much of each layer's factor fetch overlaps "
@@ -322,6 +328,9 @@ def main():
                     torch.quantile(allp[h], 1.0 - float(targets[layer, h])).float()
                     for h in range(Hq)]).float()
             torch.cuda.synchronize()
+
+        if args.timeline:
+            return timeline_summary(S, cache, wl, seed, p, tau, dev)
 
         # ---- per-step buffers ----------------------------------------------------------
         n_q = args.steps + args.warmup
@@ -608,6 +617,96 @@ def main():
             print(json.dumps(measure(zf)), flush=True)
     else:
         print(json.dumps(measure(args.zoom_frac)), flush=True)
+
+
+def timeline_summary(S, cache, wl, seed, p, tau, dev) -> dict:
+    """Time stamps of one step: for each layer, sekv_route_attn runs twice and
+    the second run's stamps are read (route, attend and tail workgroups, in
+    microseconds from the route's first workgroup).  Returns the means over
+    the layers of each phase; `layers` holds each layer's figures."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    import synth
+
+    lib = S.lib()
+    if not hasattr(lib, "sekv_timeline_read"):
+        print("--timeline needs the time-stamped library: build it with python -m "
+              "compressed_kv_attention_sekv_amd.build --timeline and load it with "
+              "SEKV_LIBRARY=compressed_kv_attention_sekv_amd/libsekv_timeline.so", file=sys.stderr)
+        sys.exit(2)
+    lib.sekv_timeline_read.restype = ctypes.c_int
+    lib.sekv_timeline_read.argtypes = [ctypes.c_void_p] * 3
+    lib.sekv_timeline_clear.restype = ctypes.c_int
+    if wl.batch != 1 or cache.cfg.factor_tier != S.SEKV_TIER_DEVICE:
+        print("--timeline takes one sequence with device-tier factors", file=sys.stderr)
+        sys.exit(2)
+    slots = 16
+    tr, ta, tt = (np.zeros(4096 * slots, dtype=np.uint64) for _ in range(3))
+    L, Hq, d = wl.n_layers, wl.n_q_heads, wl.head_dim
+    q = synth.queries(wl, seed, 3, device=dev)
+    o = torch.zeros(Hq, d, device=dev)
+    ws = torch.empty(cache.workspace_bytes(), dtype=torch.uint8, device=dev)
+    layers = []
+    for layer in range(L):
+        rb = S.RouteBuffers.allocate(cache)
+        call = (cache, layer, q[layer].contiguous(), p[layer].contiguous(),
+                tau[layer].contiguous(), rb, o, ws)
+        S.sekv_route_attn(*call)
+        torch.cuda.synchronize()
+        if lib.sekv_timeline_clear() != 0:
+            raise RuntimeError("sekv_timeline_clear failed")
+        S.sekv_route_attn(*call)
+        torch.cuda.synchronize()
+        if lib.sekv_timeline_read(tr.ctypes.data, ta.ctypes.data, tt.ctypes.data) != 0:
+            raise RuntimeError("sekv_timeline_read failed")
+        r, a, t = (x.reshape(-1, slots).astype(np.int64) for x in (tr, ta, tt))
+        r, a, t = r[r[:, 0] > 0], a[a[:, 0] > 0], t[t[:, 0] > 0]
+        base = r[:, 0].min()
+
+        def us(x):
+            return (x - base) / 100.0   # the stamps count a 100 MHz clock
+
+        z, rows = a[a[:, 1] == 0], a[a[:, 1] == 1]
+        zw = z[z[:, 10] > 0]   # zoom workgroups that got a share
+        wave_end = us(zw[:, 6:10]).max(axis=1)
+        first = us(a[:, 0]).min()
+        rec = {
+            "route_end": float(us(r[:, 1]).max()),
+            "route_query": float((us(r[:, 4]) - us(r[:, 0])).mean()),
+            "route_projection": float((us(r[:, 2]) - us(r[:, 4])).mean()),
+            "route_first_chunk_gates": float((us(r[:, 3]) - us(r[:, 2])).mean()),
+            "route_rest": float((us(r[:, 1]) - us(r[:, 3])).mean()),
+            "attend_start": first,
+            "zoom_allocation": float((us(zw[:, 3]) - us(zw[:, 0])).mean()),
+            "zoom_lookup": float((us(zw[:, 4]) - us(zw[:, 3])).mean()),
+            "zoom_metadata": float((us(zw[:, 5]) - us(zw[:, 4])).mean()),
+            "zoom_pipeline_mean": float((wave_end - us(zw[:, 5])).mean()),
+            "zoom_pipeline_max": float((wave_end - us(zw[:, 5])).max()),
+            "zoom_wave_spread": float((us(zw[:, 6:10]).max(axis=1) -
+                                       us(zw[:, 6:10]).min(axis=1)).mean()),
+            "zoom_merge": float((us(zw[:, 2]) - wave_end).mean()),
+            "zoom_end_max": float(us(zw[:, 2]).max()),
+            "rows_prologue": float((us(rows[:, 3]) - us(rows[:, 0])).mean()),
+            "rows_compute": float((us(rows[:, 4]) - us(rows[:, 3])).mean()),
+            "rows_write": float((us(rows[:, 2]) - us(rows[:, 4])).mean()),
+            "rows_late": int((us(rows[:, 0]) > first + 2.0).sum()),
+            "rows_end_max": float(us(rows[:, 2]).max()),
+            "attend_end": float(us(a[:, 2]).max()),
+            "zoom_last": bool(us(zw[:, 2]).max() >= us(a[:, 2]).max()),
+            "tail_start": float(us(t[:, 0]).min()),
+            "tail_end": float(us(t[:, 1]).max()),
+            "tail_workgroup": float((us(t[:, 1]) - us(t[:, 0])).mean()),
+        }
+        layers.append(rec)
+        log(f"timeline layer {layer}: route ends {rec['route_end']:.2f}, attend "
+            f"{rec['attend_start']:.2f}-{rec['attend_end']:.2f}, tail ends {rec['tail_end']:.2f} us")
+    summary = {k: float(np.mean([x[k] for x in layers])) for k in layers[0]}
+    return {"timeline": "microseconds from the route launch's first workgroup, means over the "
+                        f"{L} layers of one step (second of two runs of each layer)",
+            "workload": wl.name, "summary": summary, "layers": layers}
 
 
 def trace_summary(path: str) -> None:

@@ -1,6 +1,7 @@
-// Decode-step kernels of the SeKV cache (gfx950): one launch per layer routes
-// every compressed span and attends over the four sources of the mixed-
-// resolution memory; a small second launch merges the partial softmax states.
+// Decode-step kernels of the SeKV cache (gfx950).  A layer is three launches:
+// the route gates every compressed span; the attend launch attends the zoomed
+// spans beside the full-resolution rows and coarse entries; a small tail
+// merges the partial softmax states.
 //
 // SeKV paper Sec. 3.2 (query projected into the routing space; independent
 // sigmoid gate with a gamma ln n size prior) and Sec. 3.3 (Eq. 9 zoom decision
@@ -8,29 +9,66 @@
 // from their low-rank factors (Eq. 8 with hard gates), and one coarse entry per
 // other span whose scaled score gets + ln n_j).
 //
-// Work split, per KV head g: n_work workgroups of 4 waves.  Workgroup w
-//   - projects the group's queries into routing space (float64), gates the
-//     compressed spans [32 w, 32 w + 32) and writes their zoom mask;
-//   - streams its slice of the full-resolution rows (window, anchors,
-//     short-span tokens) with 16-byte loads shared by the G query heads;
-//   - attends the coarse entries of its spans that a head did not zoom;
-//   - attends each zoomed span straight from its factors, one wave per span:
+// Per KV head g:
+//   - route: each workgroup projects the group's queries into routing space
+//     (float64), gates chunks of 32 compressed spans and writes their zoom mask
+//     and one bit mask per list (per head, and their union) for each chunk;
+//   - attend: zoom workgroups share out the union's spans and attend each one
+//     straight from its factors, one wave per span:
 //       b_h = sigma_K * (V_K^T q_h) / sqrt(d);  e_{h,t} = U_K[t] . b_h;
 //       c_h = U_V^T p_h;  acc_h += V_V^T (sigma_V * c_h)
-//     so the factors are read once for all heads and no token row is formed.
-// Each workgroup writes one partial (m, l, acc) per head and its chunk's zoom
-// bit masks.  A second, small launch merges the partials into o (one workgroup
-// per query head) and writes the ascending zoom lists from the bit masks (one
-// per KV head): the kernel boundary between the two makes every workgroup's stores visible, so
-// no workgroup waits on another and no agent-scope fence (an L2 write-back or
-// invalidation, which stalls the other KV heads' workgroups still streaming
-// factors through that L2) sits inside the layer kernel.
+//     so the factors are read once for all heads and no token row is formed;
+//     row workgroups stream a slice of the full-resolution rows (window,
+//     anchors, short-span tokens) with 16-byte loads shared by the G query
+//     heads, and the coarse entries of a chunk that a head did not zoom;
+//     list workgroups write the ascending zoom lists from the bit masks;
+//   - tail: one workgroup per query head merges the partial (m, l, acc) of
+//     every attend workgroup of its KV head into o.
+// The kernel boundaries make every workgroup's stores visible to the next
+// launch, so no workgroup waits on another and no agent-scope fence (an L2
+// write-back or invalidation, which stalls the workgroups still streaming
+// factors through that L2) sits inside a launch.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
 #include "sekv_internal.h"
 
 namespace sekv {
+
+// ---------------------------------------------------------------------------
+// Time stamps of a diagnostic build (compiled with SEKV_TIMELINE, into its own
+// library): workgroups of the route, attend and tail launches record
+// s_memrealtime (a 100 MHz clock) at fixed points of their work into device
+// tables that sekv_timeline_read copies out; one table row per workgroup.
+// The product build compiles every stamp away.
+//   route:  0 start, 1 end, 2 projections done, 3 first chunk gated, 4 query in LDS
+//   attend: 0 start, 1 kind (0 zoom, 1 rows, 2 lists), 2 end;
+//           zoom: 3 allocated, 4 spans found, 5 metadata, 6..9 each wave's
+//           pipeline done, 10 KV head + 1 (0: no share), 11 spans in the share;
+//           rows: 3 prologue done, 4 rows and coarse entries done
+//   tail:   0 start, 1 end
+// ---------------------------------------------------------------------------
+#ifdef SEKV_TIMELINE
+constexpr int kTlWgs = 4096, kTlSlots = 16;
+__device__ unsigned long long g_tl_route[kTlWgs * kTlSlots];
+__device__ unsigned long long g_tl_attend[kTlWgs * kTlSlots];
+__device__ unsigned long long g_tl_tail[kTlWgs * kTlSlots];
+#define SEKV_NOW() __builtin_amdgcn_s_memrealtime()
+#define SEKV_TL(table, slot, value)                                               \
+  do {                                                                            \
+    if (threadIdx.x == 0 && blockIdx.x < kTlWgs && blockIdx.y == 0)               \
+      table[blockIdx.x * kTlSlots + (slot)] = (unsigned long long)(value);         \
+  } while (0)
+#define SEKV_TL_WAVE(table, slot, value)                                          \
+  do {                                                                            \
+    if ((threadIdx.x & 63) == 0 && blockIdx.x < kTlWgs && blockIdx.y == 0)        \
+      table[blockIdx.x * kTlSlots + (slot) + (threadIdx.x >> 6)] =                \
+          (unsigned long long)(value);                                            \
+  } while (0)
+#else
+#define SEKV_TL(table, slot, value) ((void)0)
+#define SEKV_TL_WAVE(table, slot, value) ((void)0)
+#endif
 
 // ---------------------------------------------------------------------------
 // small helpers
@@ -1194,7 +1232,9 @@ __device__ __attribute__((always_inline)) void zoom_body(const LayerGeom& geo, c
     }
   }
   __syncthreads();
+  SEKV_TL(g_tl_attend, 3, SEKV_NOW());
   const int g = s.g;
+  SEKV_TL(g_tl_attend, 10, g + 1);
   if (g < 0) return;   // uniform: no span for this workgroup
   // z_total >= Hkv S_c / kZoomBatch + Hkv, so a share never exceeds one batch
   const int lo = s.lo, nb = min(s.hi - s.lo, kZoomBatch), slot = W + s.i;
@@ -1236,6 +1276,8 @@ __device__ __attribute__((always_inline)) void zoom_body(const LayerGeom& geo, c
     }
   }
   __syncthreads();
+  SEKV_TL(g_tl_attend, 4, SEKV_NOW());
+  SEKV_TL(g_tl_attend, 11, nb);
   if (tid < nb) {
     const int j = s.m_n[tid];
     const size_t gj = (size_t)g * scs + j;
@@ -1244,6 +1286,7 @@ __device__ __attribute__((always_inline)) void zoom_body(const LayerGeom& geo, c
     s.m_n[tid] = a.clen[j];
   }
   __syncthreads();
+  SEKV_TL(g_tl_attend, 5, SEKV_NOW());
 
   float zm[G], zl[G], za[G][2];   // the wave's state (lane: dims 2 lane, 2 lane + 1)
 #pragma unroll
@@ -1284,6 +1327,7 @@ __device__ __attribute__((always_inline)) void zoom_body(const LayerGeom& geo, c
   }
   // ---- then those of rank > 32, with the stage as scratch once its DMA is done
   __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  SEKV_TL_WAVE(g_tl_attend, 6, SEKV_NOW());
   for (u = wid; u < nb; u += kWaves) {
     if (rank_max(s.m_r[u]) <= 32) continue;
     const SpanRef sp = span_ref(s, a.pool, u);
@@ -1414,6 +1458,7 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
     }
   }
   __syncthreads();
+  if (mode & kKeepBits) SEKV_TL(g_tl_attend, 3, SEKV_NOW());
 
   // ---- zoom sets of the chunk: one wave ballot per list (per head, then the
   // union), read by the zoom kernel and by the tail's lists -----------------
@@ -1446,6 +1491,7 @@ __device__ __attribute__((always_inline)) void layer_body(const LayerGeom& geo,
     rows_store<T, G>(rs, s.w[wid].st.acc, s.w[wid].st.m, s.w[wid].st.l);
   }
   __syncthreads();
+  if (mode & kKeepBits) SEKV_TL(g_tl_attend, 4, SEKV_NOW());
 
   // ---- this workgroup's partial: slot w -------------------------------------
   float* dst = a.part + ((size_t)g * geo.n_slots() + w) * G * kPartStride;
@@ -1541,6 +1587,7 @@ __device__ __attribute__((always_inline)) void route_body(const LayerGeom& geo, 
   }
   if (tid < kChunk) s.bits[tid] = 0;
   __syncthreads();
+  SEKV_TL(g_tl_route, 4, SEKV_NOW());
 
   // ---- q~_h = P_h q_h (float64), as the layer kernel forms it
   for (int k0 = 0; k0 < nout; k0 += 128) {
@@ -1569,6 +1616,7 @@ __device__ __attribute__((always_inline)) void route_body(const LayerGeom& geo, 
   }
   __syncthreads();
 
+  SEKV_TL(g_tl_route, 2, SEKV_NOW());
   // ---- each chunk: gates, then its zoom masks (one ballot per list)
   asm volatile("" : "+v"(tau_f));   // its widening stays here, not next to its load
   const double tau_d = (double)tau_f;
@@ -1601,6 +1649,7 @@ __device__ __attribute__((always_inline)) void route_body(const LayerGeom& geo, 
       if (z) atomicOr(&s.bits[jl], 1 << hl);
     }
     __syncthreads();
+    if (cc == 0) SEKV_TL(g_tl_route, 3, SEKV_NOW());
     if (wid == 0) {
       const int b = lane < nj[cc] ? s.bits[lane] : 0;
 #pragma unroll
@@ -1619,7 +1668,9 @@ template <typename T, int G, int RC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void route_kernel(LayerGeom geo, LayerArgs a) {
   __shared__ Smem<G> s;
+  SEKV_TL(g_tl_route, 0, SEKV_NOW());
   route_body<T, G, RC>(geo, a, blockIdx.x, s);
+  SEKV_TL(g_tl_route, 1, SEKV_NOW());
 }
 
 template <typename T, int G, int RC>
@@ -1663,7 +1714,9 @@ __global__ __launch_bounds__(kThreads) void layer_tail_kernel(LayerGeom geo, Lay
                                                               int mode) {
   __shared__ int wc[kListWords][kWaves];
   __shared__ MergeScratch mg;
+  SEKV_TL(g_tl_tail, 0, SEKV_NOW());
   layer_tail<G>(geo, a, mode, blockIdx.x, wc, mg);
+  SEKV_TL(g_tl_tail, 1, SEKV_NOW());
 }
 
 template <int G>
@@ -1706,15 +1759,18 @@ template <typename T, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attend_kernel(LayerGeom geo, LayerArgs a, int mode) {
   __shared__ AttendLds<G> u;
+  SEKV_TL(g_tl_attend, 0, SEKV_NOW());
   const int nz = geo.n_compressed ? geo.z_total : 0;
   const int nr = geo.n_kv_heads * geo.n_work;
   const int x = blockIdx.x;
+  SEKV_TL(g_tl_attend, 1, x < nz ? 0 : (x < nz + nr ? 1 : 2));
   if (x < nz)
     zoom_body<G>(geo, a, x, u.zz.z, u.zz.st);
   else if (x < nz + nr)
     layer_body<T, G>(geo, a, (mode & ~kLists) | kKeepBits, x - nz, u.l);
   else if (mode & kLists)   // the lists need only the route's chunk masks
     tail_lists<G>(geo, a, x - nz - nr, u.wc);
+  SEKV_TL(g_tl_attend, 2, SEKV_NOW());
 }
 static_assert(sizeof(AttendLds<4>) <= 80 * 1024 && sizeof(AttendLds<5>) <= 80 * 1024,
               "two attend workgroups per CU");
@@ -2004,3 +2060,25 @@ hipError_t launch_fetch_gather(const LayerGeom& g, const int32_t* ulist, const i
 }
 
 }  // namespace sekv
+
+#ifdef SEKV_TIMELINE
+// The diagnostic build's stamp tables (each kTlWgs x kTlSlots entries of
+// 64 bits, in workgroup order) copied to host memory, or zeroed.  Returns a
+// hipError_t.  Not part of the product library's ABI.
+extern "C" int sekv_timeline_read(unsigned long long* route, unsigned long long* attend,
+                                  unsigned long long* tail) {
+  hipError_t e = hipMemcpyFromSymbol(route, HIP_SYMBOL(sekv::g_tl_route), sizeof(sekv::g_tl_route));
+  if (e == hipSuccess)
+    e = hipMemcpyFromSymbol(attend, HIP_SYMBOL(sekv::g_tl_attend), sizeof(sekv::g_tl_attend));
+  if (e == hipSuccess)
+    e = hipMemcpyFromSymbol(tail, HIP_SYMBOL(sekv::g_tl_tail), sizeof(sekv::g_tl_tail));
+  return (int)e;
+}
+extern "C" int sekv_timeline_clear() {
+  static unsigned long long zeros[sekv::kTlWgs * sekv::kTlSlots];
+  hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(sekv::g_tl_route), zeros, sizeof(zeros));
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(sekv::g_tl_attend), zeros, sizeof(zeros));
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(sekv::g_tl_tail), zeros, sizeof(zeros));
+  return (int)e;
+}
+#endif
