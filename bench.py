@@ -59,8 +59,11 @@ def parse():
                          "through the batched calls, one layer launch and one tail launch for "
                          "all sequences")
     ap.add_argument("--budget", type=int, default=None,
-                    help="matched-budget cap in tokens per KV head and layer: each layer runs "
-                         "sekv_route (gate values kept), sekv_cap_budget, sekv_decode_attn")
+                    help="matched-budget cap in tokens per KV head and layer (or per layer, "
+                         "with --budget-scope layer): each layer runs sekv_route (gate values "
+                         "kept), sekv_cap_budget, sekv_decode_attn")
+    ap.add_argument("--budget-scope", choices=["kv_head", "layer"], default="kv_head",
+                    help="the budget covers each KV head of a layer, or the whole layer")
     ap.add_argument("--residency-gb", type=float, default=0.0,
                     help="host tier: HBM residency cache of factor blocks, in GB (0 = none)")
     ap.add_argument("--slot-kb", type=int, default=64, help="residency cache slot size, KiB")
@@ -78,6 +81,9 @@ def parse():
                          "python -m compressed_kv_attention_sekv_amd.build --timeline, loaded "
                          "with SEKV_LIBRARY=compressed_kv_attention_sekv_amd/libsekv_timeline.so); "
                          "prints a JSON summary instead of the bench line")
+    ap.add_argument("--trace-last", type=int, default=640,
+                    help="with --trace-summary: the per-kernel statistics of each kernel's last "
+                         "this many launches (default 640: 20 steps x 32 layers)")
     ap.add_argument("--trace-summary", default=None,
                     help="summarise a rocprofv3 kernel trace CSV (per-kernel launches and mean "
                          "duration; host tier: how much of each layer's factor fetch overlaps "
@@ -202,7 +208,7 @@ def read_traffic(workload: str):
 def main():
     args = parse()
     if args.trace_summary:
-        trace_summary(args.trace_summary)
+        trace_summary(args.trace_summary, args.trace_last)
         return
     if args.write_traffic:
         write_traffic(args.workload, *args.write_traffic)
@@ -356,7 +362,7 @@ def main():
         def layer_call(layer):
             if capped:
                 S.sekv_route(cache, layer, q_cur[0, layer], p_c[layer], tau_c[layer], routes[0][layer])
-                S.sekv_cap_budget(cache, routes[0][layer], args.budget)
+                S.sekv_cap_budget(cache, routes[0][layer], args.budget, scope=args.budget_scope)
                 S.sekv_decode_attn(cache, layer, q_cur[0, layer], routes[0][layer], outs[0, layer],
                                    wss[0], fetch_stream=side)
             elif B == 1:
@@ -555,7 +561,9 @@ def main():
                 "head_dim": d, "context": wl.n_tokens, "batch": B, "kv_dtype": wl.kv_dtype,
                 "factor_dtype": "f32", "factor_tier": args.tier, "window": wl.window,
                 "max_rank": wl.max_rank, "route_dim": wl.route_dim, "graph": graph is not None,
-                "budget_tokens": args.budget, "query_corr": args.query_corr,
+                "budget_tokens": args.budget,
+                "budget_scope": args.budget_scope if args.budget is not None else None,
+                "query_corr": args.query_corr,
                 "gate_eps": args.gates, "svd": args.svd,
                 "fetch": args.fetch if args.tier == "host" else None,
                 "zoom": ("skewed" if wl.tau_mode == "skewed" and zoom_arg is None else
@@ -709,7 +717,7 @@ def timeline_summary(S, cache, wl, seed, p, tau, dev) -> dict:
             "workload": wl.name, "summary": summary, "layers": layers}
 
 
-def trace_summary(path: str) -> None:
+def trace_summary(path: str, last: int = 640) -> None:
     """Per-kernel launches and mean duration of a rocprofv3 kernel trace CSV,
     the gaps between consecutive decode launches, and for host-tier traces
     the overlap of each layer's factor fetch (fetch_gather_kernel) with the
@@ -737,12 +745,15 @@ def trace_summary(path: str) -> None:
     for r in rows:
         a, b = span(r)
         per.setdefault(short(r["Kernel_Name"]), []).append((b - a) / 1e3)
-    # the last 640 launches of a kernel: the byte-count pass over the last 20
-    # steps x 32 layers of a default run (the same work as the timed steps,
-    # launched one by one), free of the calibration's route-only launches
+    # the last `last` launches of a kernel (640: the byte-count pass over the
+    # last 20 steps x 32 layers of a default run, the same work as the timed
+    # steps launched one by one, free of the calibration's route-only launches)
     kernels = {k: {"launches": len(v), "mean_us": statistics.mean(v),
                    "median_us": statistics.median(v), "total_us": sum(v),
-                   "last640_mean_us": statistics.mean(v[-640:])}
+                   "last": min(last, len(v)),
+                   "last_mean_us": statistics.mean(v[-last:]),
+                   "last_median_us": statistics.median(v[-last:]),
+                   "last_min_us": min(v[-last:]), "last_max_us": max(v[-last:])}
                for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1]))}
     decode = [r for r in rows if any(k in r["Kernel_Name"] for k in
                                      ("route_kernel", "attend_kernel", "layer_kernel", "zoom_kernel",

@@ -14,10 +14,13 @@
 // candidates of every KV head (ties to the lower KV head, then the lower span
 // id), whose kept prefix bounds the total the layer reconstructs.
 //
-// One workgroup of 512 threads per KV head.  The order is never materialised:
-// each candidate's inclusive prefix length is a sum over the candidates that
-// precede it, counted against LDS tiles of (key, id, length), so the decisions
-// do not depend on any sort and are deterministic.  Then one pass over the
+// One workgroup of 512 threads per KV head (the layer scope's decisions: up
+// to 8 per KV head, each taking a share of its candidates).  The order is
+// never materialised: each candidate's inclusive prefix length is a sum over
+// the candidates that precede it, counted against LDS tiles of (key, id,
+// length); when the candidates fit one tile, each candidate's sum is split
+// over several threads so that every thread counts.  The sums are integers,
+// so the decisions do not depend on any sort or order and are deterministic.  Then one pass over the
 // union clears the dropped spans from the masks and compacts the union and
 // every head's list at once (a head's new list is the kept union filtered by
 // its mask bit), in place and stably, with ballot scans.  Every gather is
@@ -31,7 +34,7 @@ namespace {
 
 constexpr int kCapThreads = 512;
 constexpr int kCapWaves = kCapThreads / 64;
-constexpr int kCapTile = 2048;
+constexpr int kCapTile = 4096;
 
 // largest gate value among the heads [h0, h0 + G) that zoomed span j (gate
 // values are probabilities, so -1 marks "none"); all 2 G loads go out at once
@@ -87,7 +90,7 @@ __device__ __forceinline__ void cap_scan(const int (&flag)[NF], int (&pos)[NF], 
 // one candidate in LDS: a single 16-byte read per comparison
 struct alignas(16) CapEnt {
   double key;
-  int id;
+  int id;   // span id; in the layer-wide single tile, KV head x S_c + span id
   int len;
 };
 
@@ -105,6 +108,8 @@ __global__ __launch_bounds__(kCapThreads) void cap_budget_kernel(
     int32_t* ucount, uint8_t* __restrict__ drop) {
   __shared__ CapEnt s_ent[kCapTile];
   __shared__ int s_wave[G + 1][kCapWaves];
+  __shared__ int s_upre[kMaxKvHeads + 1];   // layer scope: candidates of the KV heads before
+  __shared__ long long s_part[kCapThreads]; // layer scope: parts of the candidates' sums
   extern __shared__ uint32_t s_drop[];  // one bit per union position
 
   const int g = blockIdx.x, tid = threadIdx.x;
@@ -117,15 +122,121 @@ __global__ __launch_bounds__(kCapThreads) void cap_budget_kernel(
   //    id asc) order, over this KV head's candidates or over every KV head's
   //    (layer scope); with a single tile of its own candidates a candidate's
   //    own key comes from it
-  if (PHASE != kCapApply) {
+  if (PHASE == kCapDecide) {
+    // layer scope: the KV heads' candidate counts and their running sum
+    if (tid < 64) {
+      int run = 0;
+      for (int g0 = 0; g0 < hkv; g0 += 64) {
+        int v = g0 + tid < hkv ? ucount[g0 + tid] : 0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int u = __shfl_up(v, o, 64);
+          if (tid >= o) v += u;
+        }
+        if (g0 + tid < hkv) s_upre[g0 + tid + 1] = run + v;
+        run += __shfl(v, 63, 64);
+      }
+      if (tid == 0) s_upre[0] = 0;
+    }
+    __syncthreads();
+  }
+  // layer scope with every KV head's candidates in one tile: they are
+  // gathered in one pass (two round trips in all, instead of two per KV
+  // head), and a candidate's place among equal keys is its KV head x S_c + id
+  if (PHASE == kCapDecide && s_upre[hkv] <= kCapTile && (long long)hkv * sc < (1ll << 31)) {
+    const int Ut = s_upre[hkv];
+    for (int k = tid; k < Ut; k += kCapThreads) {
+      int lo = 0, hi = hkv;   // the KV head of candidate k: s_upre[go] <= k < s_upre[go + 1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_upre[mid] <= k) lo = mid; else hi = mid;
+      }
+      const int j = ulist[(size_t)lo * sc + (k - s_upre[lo])];
+      CapEnt e;
+      e.key = cap_key<G>(mask, prob, sc, lo * G, j);
+      e.id = lo * sc + j;
+      e.len = clen[j];
+      s_ent[k] = e;
+    }
+    __syncthreads();
+    // workgroup y of the KV head decides its candidates [i0, i1); each
+    // candidate's sum over the tile is split into P parts, one per thread,
+    // so that every thread counts
+    const int i0 = (int)((long long)U * blockIdx.y / gridDim.y);
+    const int i1 = (int)((long long)U * (blockIdx.y + 1) / gridDim.y);
+    const int nloc = i1 - i0;
+    const int cpb = min(kCapThreads, max(64, (nloc + 63) & ~63));   // candidates per pass
+    const int P = kCapThreads / cpb;                                 // parts per candidate
+    const int p = tid / cpb, il = tid % cpb;
+    const int k0 = (int)((long long)Ut * p / P), k1 = (int)((long long)Ut * (p + 1) / P);
+    for (int b0 = 0; b0 < nloc; b0 += cpb) {
+      const bool mine = p < P && b0 + il < nloc;
+      long long S = 0;
+      if (mine) {
+        const CapEnt me = s_ent[s_upre[g] + i0 + b0 + il];
+#pragma unroll 8
+        for (int k = k0; k < k1; ++k) {
+          const CapEnt e = s_ent[k];
+          const bool before = (e.key > me.key) | ((e.key == me.key) & (e.id <= me.id));
+          S += before ? e.len : 0;
+        }
+      }
+      s_part[tid] = S;
+      __syncthreads();
+      if (mine && p == 0) {
+        for (int q = 1; q < P; ++q) S += s_part[q * cpb + il];
+        drop[(size_t)g * sc + i0 + b0 + il] = S > budget;
+      }
+      __syncthreads();
+    }
+    return;
+  }
+  if (PHASE == kCapDecide && blockIdx.y > 0) return;   // the tiled path runs in y = 0
+  if (PHASE == kCapBoth && U <= kCapTile) {
+    // one KV head's candidates in one tile: each candidate's sum over it split
+    // into P parts, one per thread, so that every thread counts
+    for (int k = tid; k < U; k += kCapThreads) {
+      const int j = ul[k];
+      CapEnt e;
+      e.key = cap_key<G>(mask, prob, sc, h0, j);
+      e.id = j;
+      e.len = clen[j];
+      s_ent[k] = e;
+    }
+    __syncthreads();
+    const int cpb = min(kCapThreads, max(64, (U + 63) & ~63));   // candidates per pass
+    const int P = kCapThreads / cpb;                              // parts per candidate
+    const int p = tid / cpb, il = tid % cpb;
+    const int k0 = (int)((long long)U * p / P), k1 = (int)((long long)U * (p + 1) / P);
+    for (int b0 = 0; b0 < U; b0 += cpb) {
+      const bool mine = p < P && b0 + il < U;
+      long long S = 0;
+      if (mine) {
+        const CapEnt me = s_ent[b0 + il];
+#pragma unroll 8
+        for (int k = k0; k < k1; ++k) {
+          const CapEnt e = s_ent[k];
+          const bool before = (e.key > me.key) | ((e.key == me.key) & (e.id <= me.id));
+          S += before ? e.len : 0;
+        }
+      }
+      s_part[tid] = S;
+      __syncthreads();
+      if (mine && p == 0) {
+        for (int q = 1; q < P; ++q) S += s_part[q * cpb + il];
+        const int i = b0 + il;
+        if (S > budget) atomicOr(&s_drop[i >> 5], 1u << (i & 31));
+      }
+      __syncthreads();
+    }
+  } else if (PHASE != kCapApply) {
     const int ga = PHASE == kCapDecide ? 0 : g, gb = PHASE == kCapDecide ? hkv : g + 1;
-    const bool one_tile = PHASE == kCapBoth && U <= kCapTile;
     for (int base = 0; base < U; base += kCapThreads) {
       const int i = base + tid;
       const bool have = i < U;
       int ji = 0;
       double ki = 0.0;
-      if (have && !one_tile) {
+      if (have) {
         ji = ul[i];
         ki = cap_key<G>(mask, prob, sc, h0, ji);
       }
@@ -146,10 +257,6 @@ __global__ __launch_bounds__(kCapThreads) void cap_budget_kernel(
           }
           __syncthreads();
           if (have) {
-            if (one_tile) {
-              ki = s_ent[i].key;
-              ji = s_ent[i].id;
-            }
             // branch-free: every entry is read (one broadcast 16-byte LDS
             // read) and counted with a select, so the reads of an unrolled
             // group are all in flight together; candidates of a lower KV
@@ -232,6 +339,8 @@ hipError_t launch_cap_budget(int sc, int hkv, int group, long long budget, const
                              int32_t* ulist, int32_t* ucount, uint8_t* drop, hipStream_t st) {
   if (sc <= 0 || hkv <= 0) return hipSuccess;
   const size_t lds = cap_budget_lds_bytes(sc);
+  // layer scope: each KV head's decisions over qd workgroups (about 256 in all)
+  const int qd = max(1, min(8, 256 / hkv));
   // drop == NULL: each KV head's own budget (one launch); else one budget for
   // the layer: the decisions, then their application
 #define SEKV_CAP(GG)                                                                           \
@@ -241,7 +350,7 @@ hipError_t launch_cap_budget(int sc, int hkv, int group, long long budget, const
                          st, sc, hkv, budget, clen, prob, mask, list, count, ulist, ucount,    \
                          drop);                                                                \
     } else {                                                                                   \
-      hipLaunchKernelGGL((cap_budget_kernel<GG, kCapDecide>), dim3(hkv), dim3(kCapThreads),    \
+      hipLaunchKernelGGL((cap_budget_kernel<GG, kCapDecide>), dim3(hkv, qd), dim3(kCapThreads), \
                          lds, st, sc, hkv, budget, clen, prob, mask, list, count, ulist,       \
                          ucount, drop);                                                        \
       hipLaunchKernelGGL((cap_budget_kernel<GG, kCapApply>), dim3(hkv), dim3(kCapThreads),     \

@@ -221,8 +221,9 @@ def test_budget_cap_rejects_bad_arguments(S):
 
 def test_budget_cap_large_union(S):
     """A union of thousands of spans (short spans, every span zoomed), so the
-    cap runs its multi-tile comparison and multi-block compaction: masks,
-    lists and unions bit-exact against the oracle's cap on the GPU's gates."""
+    cap runs its multi-tile comparison and multi-block compaction, per KV head
+    and for the layer: masks, lists and unions bit-exact against the oracle's
+    cap on the GPU's gates."""
     wl = synth.workload("tiny", n_tokens=40000, min_span_len=1)
     hq, hkv = wl.n_q_heads, wl.n_kv_heads
     inp = Inputs(wl, 4)
@@ -250,4 +251,9 @@ def test_budget_cap_large_union(S):
         torch.cuda.synchronize()
         ref = O.cap_budget(uncapped, seg, hkv, budget)
         assert_route_equals(rb, ref, hq, hkv)
+        # the layer scope over more candidates than one LDS tile holds
+        rl = clone_route(S, base)
+        S.sekv_cap_budget(cache, rl, budget, scope="layer")
+        torch.cuda.synchronize()
+        assert_route_equals(rl, O.cap_budget(uncapped, seg, hkv, budget, scope="layer"), hq, hkv)
         log(f"[budget] budget={budget}: kept {ref.unions[0].size} of {sc} spans")
