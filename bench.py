@@ -162,18 +162,23 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, alg_bytes: str)
         return sum(v[counter] for k, v in m.items() if any(n in k for n in LAYER_KERNELS)
                    and counter in v)
 
-    def copy_kib(path, counter):
+    def probe_kib(path, counter, names, top):
         import csv
         with open(path) as f:
             vals = [float(r["Counter_Value"]) for r in csv.DictReader(f)
-                    if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == counter]
-        return statistics.median(sorted(vals)[-6:])
+                    if all(n in r["Kernel_Name"] for n in names) and r["Counter_Name"] == counter]
+        return statistics.median(sorted(vals)[-top:]) if vals else None
+
+    def copy_kib(path, counter):
+        return probe_kib(path, counter, ("copyBuffer",), 6)
 
     fm64, wm64 = counter_means(fetch_csv), counter_means(write_csv)
     fetch_raw, write_raw = per_layer(fm64, "FETCH_SIZE"), per_layer(wm64, "WRITE_SIZE")
     moved_kib = 2 * 1024 * 1024   # the probe copies 2 GiB each way
     cf, cw = copy_kib(fetch_csv, "FETCH_SIZE"), copy_kib(write_csv, "WRITE_SIZE")
     fs, ws = moved_kib / cf, moved_kib / cw
+    rf = probe_kib(fetch_csv, "FETCH_SIZE", ("reduce_kernel", "ReduceOp<float",
+                                             "sum_functor<float, float, float>"), 5)
     fb, wb = fetch_raw * 1024 * fs, write_raw * 1024 * ws
     out = {"workload": workload,
            "kernel": "sekv::route_kernel + sekv::attend_kernel + sekv::layer_tail_kernel (one layer)",
@@ -181,6 +186,10 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, alg_bytes: str)
            "fetch_bytes": fb, "write_bytes": wb, "fetch_KiB_raw": fetch_raw,
            "write_KiB_raw": write_raw, "fetch_scale": fs, "write_scale": ws,
            "copy_probe_fetch_KiB": cf, "copy_probe_write_KiB": cw,
+           # a second point for the fetch scale: the read-only probe's row sums
+           # over the same 2 GiB (a float sum reduction that reads 2 GiB, writes 2 MiB)
+           "read_probe_fetch_KiB": rf,
+           "read_probe_fetch_scale": moved_kib / rf if rf else None,
            "algorithmic_bytes_per_launch_same_steps": float(alg_bytes),
            "per_kernel_KiB": {k: {"FETCH_SIZE": fm64[k].get("FETCH_SIZE"),
                                   "WRITE_SIZE": wm64.get(k, {}).get("WRITE_SIZE")}
