@@ -107,6 +107,47 @@ def test_layer_budget_cap_matches_oracle(S, name, kw, zoom):
             assert int(rb.count.sum()) == 0 and int(rb.union_count.sum()) == 0
 
 
+@pytest.mark.parametrize("hq,hkv", [(64, 64), (256, 128)])
+def test_layer_budget_cap_many_kv_heads(S, hq, hkv):
+    """The layer scope with 64 and 128 KV heads, whose decisions are spread
+    over 4 and 2 workgroups per KV head (8 up to 32 KV heads), each taking a
+    share of its KV head's candidates: masks, per-head lists and unions
+    against the oracle's cap on the GPU's own route, at budgets across the
+    range (the attention over capped routes is checked above)."""
+    wl = synth.workload("tiny", n_q_heads=hq, n_kv_heads=hkv, n_tokens=2048)
+    log(f"[budget] layer scope, {hq}/{hkv} heads")
+    inp = Inputs(wl, 14)
+    cache = S.sekv_build_spans(make_cfg(S, wl), inp.s, inp.k, inp.v, inp.w, inp.ranks)
+    orc = OracleSide(inp, [0], wl.max_rank, with_factors=False)
+    sc = cache.info.n_compressed
+    assert sc > 0
+    q = inp.query(0)[0].contiguous()
+    p = inp.p[0].contiguous()
+    prob = orc.route(0, to64(q), to64(p), np.full(hq, 2.0), wl.gamma).prob
+    g = wl.group
+    # uneven zoom: every third KV head's heads zoom 40% of the spans, the rest 10%
+    share = [0.4 if (h // g) % 3 == 0 else 0.1 for h in range(hq)]
+    tau = torch.tensor([float(np.quantile(prob[h], 1.0 - share[h])) for h in range(hq)],
+                       dtype=torch.float32).cuda()
+    base = S.RouteBuffers.allocate(cache, with_prob=True)
+    S.sekv_route(cache, 0, q, p, tau, base)
+    torch.cuda.synchronize()
+    uncapped = gpu_route_as_oracle(base, sc, hq, hkv)
+    n = orc.seg.span_len[orc.seg.cspan].astype(np.int64)
+    total = sum(int(n[u].sum()) for u in uncapped.unions)
+    assert total > 0
+    for budget in sorted({0, total // 7, total // 3, total - 1, total}):
+        rb = clone_route(S, base)
+        S.sekv_cap_budget(cache, rb, budget, scope="layer")
+        torch.cuda.synchronize()
+        ref = O.cap_budget(uncapped, orc.seg, hkv, budget, scope="layer")
+        assert_route_equals(rb, ref, hq, hkv)
+        kept = sum(int(n[u].sum()) for u in ref.unions)
+        assert kept <= budget
+        log(f"[budget] {hkv} KV heads, layer budget={budget}: kept {kept} of {total} tokens, "
+            f"zoomed pairs {int(ref.mask.sum())}")
+
+
 @pytest.mark.parametrize("name,kw,zoom", [
     ("tiny", dict(), None),
     ("llama3_8b_128k", dict(n_layers=1, n_tokens=20000), 0.3),
