@@ -592,12 +592,13 @@ def test_full_size_sampled_parity(S, full_c3, layer, kv_head):
 @pytest.mark.parametrize("name,hq,hkv", [
     ("llama3_8b_128k", 4, 4), ("llama3_8b_128k", 8, 4), ("llama3_8b_128k", 6, 2),
     ("llama3_8b_128k", 12, 2), ("llama3_8b_128k", 16, 2),
-    ("tiny", 2, 2), ("tiny", 4, 2), ("tiny", 8, 1)])
+    ("tiny", 2, 2), ("tiny", 4, 2), ("tiny", 8, 1), ("tiny", 256, 128)])
 def test_group_sizes(S, name, hq, hkv):
     """Query heads per KV head G = 1, 2, 3, 6 and 8 with bf16 K/V and G = 1, 2
     and 8 with float32 K/V (the kernels are instantiated for every G up to 8
-    and both storage types): route and attention against the oracle, both
-    call paths bit-identical, and the budget cap on the same route."""
+    and both storage types), and 128 KV heads (the zoom workgroups' shares
+    are taken 64 KV heads at a time): route and attention against the oracle,
+    both call paths bit-identical, and the budget cap on the same route."""
     kw = dict(n_layers=1, n_tokens=5000) if name != "tiny" else {}
     wl = synth.workload(name, n_q_heads=hq, n_kv_heads=hkv, **kw)
     log(f"[parity] group size G={hq // hkv} ({hq}/{hkv} heads)")
