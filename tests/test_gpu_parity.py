@@ -609,7 +609,8 @@ def test_group_sizes(S, name, hq, hkv):
     and 8 with float32 K/V (the kernels are instantiated for every G up to 8
     and both storage types), and 128 KV heads (the zoom workgroups' shares
     are taken 64 KV heads at a time): route and attention against the oracle,
-    both call paths bit-identical, and the budget cap on the same route."""
+    both call paths bit-identical, and the budget cap in both scopes on the
+    same route."""
     kw = dict(n_layers=1, n_tokens=5000) if name != "tiny" else {}
     wl = synth.workload(name, n_q_heads=hq, n_kv_heads=hkv, **kw)
     log(f"[parity] group size G={hq // hkv} ({hq}/{hkv} heads)")
@@ -639,8 +640,21 @@ def test_group_sizes(S, name, hq, hkv):
         assert rb.union_list[k, :int(rb.union_count[k])].cpu().tolist() == ref.unions[k].tolist()
     for h in range(hq):
         assert rb.list[h, :int(rb.count[h])].cpu().tolist() == ref.lists[h].tolist()
+    # one budget for the layer: half of every KV head's union tokens together
+    lbudget = sum(int(n[u].sum()) for u in uncapped.unions) // 2
+    rl, _ = run_gpu_layer(S, cache, 0, q, inp.p[0], tau)
+    S.sekv_cap_budget(cache, rl, lbudget, scope="layer")
+    torch.cuda.synchronize()
+    lref = O.cap_budget(uncapped, orc.seg, hkv, lbudget, scope="layer")
+    assert np.array_equal(rl.mask.cpu().numpy().astype(bool)[:, :cache.info.n_compressed],
+                          lref.mask)
+    for k in range(hkv):
+        assert rl.union_list[k, :int(rl.union_count[k])].cpu().tolist() == lref.unions[k].tolist()
+    for h in range(hq):
+        assert rl.list[h, :int(rl.count[h])].cpu().tolist() == lref.lists[h].tolist()
     log(f"[parity] G={g}: zoom={route.mask.mean():.3f} ties={n_tie} err={worst:.2e} "
-        f"budget={budget} capped pairs={int(ref.mask.sum())}")
+        f"budget={budget} capped pairs={int(ref.mask.sum())}, layer budget={lbudget} "
+        f"capped pairs={int(lref.mask.sum())}")
 
 
 @pytest.mark.parametrize("case", ["route_dim_7", "route_dim_64_bf16", "no_window_unit_spans",
