@@ -33,6 +33,7 @@ def rsvd_cfg(S, wl):
 @pytest.mark.parametrize("name,kw", [
     ("llama3_8b_128k", dict(n_layers=2, n_tokens=16384 + 77)),
     ("llama32_3b_32k", dict(n_layers=1, n_tokens=8192 + 5)),
+    ("llama3_8b_128k", dict(n_layers=1, n_tokens=16384 + 77, kv_dtype="f32")),
 ])
 def test_randomized_svd_bounds_and_attention(S, name, kw):
     wl = synth.workload(name, **kw)
