@@ -1,7 +1,8 @@
 """bench.py measures one GPU: asked for more it exits with status 2 and says so,
 before touching the GPU.  It reports the committed HBM traffic counters only
 for the configuration they were taken on, and it turns counter files into
-those figures by the copy probe's scale."""
+those figures by the copy probe's scale; its trace reader gives the per-kernel
+figures of the profiles."""
 import importlib.util
 import os
 import subprocess
@@ -84,3 +85,44 @@ def test_write_traffic_scales_counters_by_the_probes(tmp_path, monkeypatch):
     assert abs(out["write_bytes"] - write_kib * 1024 * 1.0) < 1e-6
     assert abs(out["bytes_per_launch"] - (out["fetch_bytes"] + out["write_bytes"])) < 1e-6
     assert out["kernel_source_hash"] == h
+
+
+def test_trace_summary_means_gaps_and_fetch_overlap(tmp_path, capsys):
+    """The kernel-trace reader behind the profiles: per-kernel means over the
+    last launches, the median gap between consecutive decode launches, and a
+    host-tier fetch's overlap with the layer launch beside it.  A synthetic
+    trace with known timestamps (nanoseconds)."""
+    import csv
+    import json
+    spec = importlib.util.spec_from_file_location("bench_trace_mod", os.path.join(ROOT, "bench.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    rows, t = [], 0
+    route = "void sekv::route_kernel<unsigned short, 4, 2>(sekv::LayerGeom, sekv::LayerArgs)"
+    attend = "void sekv::attend_kernel<unsigned short, 4>(sekv::LayerGeom, sekv::LayerArgs, int)"
+    for i, dur in enumerate((7000, 8000, 9000)):   # three layers: route, 1 us gap, attend
+        rows.append((route, t, t + dur))
+        t += dur + 1000
+        rows.append((attend, t, t + 2 * dur))
+        t += 2 * dur + 1000
+    fetch = "void sekv::fetch_gather_kernel(int, int)"
+    layer = "void sekv::layer_kernel<unsigned short, 4>(sekv::LayerGeom, sekv::LayerArgs, int)"
+    rows.append((layer, t, t + 10000))               # a host-tier pair: the fetch runs
+    rows.append((fetch, t + 6000, t + 14000))        # 4 of its 8 us beside the layer launch
+    path = tmp_path / "run_kernel_trace.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for name, a, e in rows:
+            w.writerow({"Kernel_Name": name, "Start_Timestamp": a, "End_Timestamp": e})
+    b.trace_summary(str(path), last=2)
+    out = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    k = out["kernels"]["sekv::route_kernel<unsigned short, 4, 2>"]
+    assert k["launches"] == 3 and k["mean_us"] == 8.0 and k["last_mean_us"] == 8.5
+    assert k["last_min_us"] == 8.0 and k["last_max_us"] == 9.0
+    a = out["kernels"]["sekv::attend_kernel<unsigned short, 4>"]
+    assert a["last_mean_us"] == 17.0 and a["total_us"] == 48.0
+    assert out["decode_gap_us_median"] == 1.0
+    ov = out["fetch_overlap"]
+    assert ov["fetches"] == 1 and ov["of_fetch_time_mean"] == 0.5
+    assert ov["of_shorter_launch_mean"] == 0.5
