@@ -84,6 +84,10 @@ def parse():
     ap.add_argument("--trace-last", type=int, default=640,
                     help="with --trace-summary: the per-kernel statistics of each kernel's last "
                          "this many launches (default 640: 20 steps x 32 layers)")
+    ap.add_argument("--trace-skip", type=int, default=0,
+                    help="with --trace-summary: leave out each kernel's last this many launches "
+                         "before taking the last --trace-last (640 with the defaults: the timed, "
+                         "graph-replayed steps instead of the byte count's launches after them)")
     ap.add_argument("--trace-summary", default=None,
                     help="summarise a rocprofv3 kernel trace CSV (per-kernel launches and mean "
                          "duration; host tier: how much of each layer's factor fetch overlaps "
@@ -217,7 +221,7 @@ def read_traffic(workload: str):
 def main():
     args = parse()
     if args.trace_summary:
-        trace_summary(args.trace_summary, args.trace_last)
+        trace_summary(args.trace_summary, args.trace_last, args.trace_skip)
         return
     if args.write_traffic:
         write_traffic(args.workload, *args.write_traffic)
@@ -726,7 +730,7 @@ def timeline_summary(S, cache, wl, seed, p, tau, dev) -> dict:
             "workload": wl.name, "summary": summary, "layers": layers}
 
 
-def trace_summary(path: str, last: int = 640) -> None:
+def trace_summary(path: str, last: int = 640, skip: int = 0) -> None:
     """Per-kernel launches and mean duration of a rocprofv3 kernel trace CSV,
     the gaps between consecutive decode launches, and for host-tier traces
     the overlap of each layer's factor fetch (fetch_gather_kernel) with the
@@ -754,15 +758,23 @@ def trace_summary(path: str, last: int = 640) -> None:
     for r in rows:
         a, b = span(r)
         per.setdefault(short(r["Kernel_Name"]), []).append((b - a) / 1e3)
-    # the last `last` launches of a kernel (640: the byte-count pass over the
-    # last 20 steps x 32 layers of a default run, the same work as the timed
-    # steps launched one by one, free of the calibration's route-only launches)
+    # the last `last` launches of a kernel before its final `skip` (640 and 0
+    # in a default run: the byte-count pass over 20 steps x 32 layers, the
+    # timed steps' work launched one layer at a time; 640 and 640: the timed
+    # steps themselves, graph-replayed; both free of the calibration's
+    # route-only launches)
+    def kept(v):
+        return skip if 0 < skip < len(v) else 0
+
+    def window(v):
+        return v[:len(v) - kept(v)][-last:]
+
     kernels = {k: {"launches": len(v), "mean_us": statistics.mean(v),
                    "median_us": statistics.median(v), "total_us": sum(v),
-                   "last": min(last, len(v)),
-                   "last_mean_us": statistics.mean(v[-last:]),
-                   "last_median_us": statistics.median(v[-last:]),
-                   "last_min_us": min(v[-last:]), "last_max_us": max(v[-last:])}
+                   "last": len(window(v)), "skipped": kept(v),
+                   "last_mean_us": statistics.mean(window(v)),
+                   "last_median_us": statistics.median(window(v)),
+                   "last_min_us": min(window(v)), "last_max_us": max(window(v))}
                for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1]))}
     decode = [r for r in rows if any(k in r["Kernel_Name"] for k in
                                      ("route_kernel", "attend_kernel", "layer_kernel", "zoom_kernel",

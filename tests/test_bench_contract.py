@@ -126,3 +126,8 @@ def test_trace_summary_means_gaps_and_fetch_overlap(tmp_path, capsys):
     ov = out["fetch_overlap"]
     assert ov["fetches"] == 1 and ov["of_fetch_time_mean"] == 0.5
     assert ov["of_shorter_launch_mean"] == 0.5
+    # the window before the last launch: the first two routes
+    b.trace_summary(str(path), last=2, skip=1)
+    out = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    k = out["kernels"]["sekv::route_kernel<unsigned short, 4, 2>"]
+    assert k["skipped"] == 1 and k["last"] == 2 and k["last_mean_us"] == 7.5
